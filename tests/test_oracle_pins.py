@@ -1,0 +1,395 @@
+"""Pins of the CPU oracle against things other than itself: a hand-worked example,
+library routines, brute force on tiny inputs, closed forms, invariants and finite
+differences.  CPU only."""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+from combine_expert_ffn_amd.inputs import WORKLOADS, make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "tiny_hand_worked.json")
+
+
+def _sig(z):
+    return 1.0 / (1.0 + math.exp(-z))
+
+
+def _ev(expr):
+    return float(eval(expr, {"__builtins__": {}}, {"s": _sig}))
+
+
+def _evs(a):
+    if isinstance(a, list):
+        return np.array([_evs(v) for v in a], dtype=np.float64)
+    return _ev(a)
+
+
+def _rand(shape, rng, scale=1.0):
+    return rng.standard_normal(shape) * scale
+
+
+# ----------------------------------------------------------------------------
+# hand-worked example
+# ----------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def test_golden_k1_forward_backward(golden):
+    g = golden["inputs"]
+    x, W_r = np.array(g["x"]), np.array(g["W_r"])
+    W_gu, W_down, dout = np.array(g["W_gu"]), np.array(g["W_down"]), np.array(g["dout"])
+    ex = golden["k1"]
+    f = O.layer_forward(x, 1, 0, 2, W_gu, W_down, W_r=W_r, tile_m=4, prec="f64")
+    assert f["idx"].tolist() == ex["idx"]
+    np.testing.assert_allclose(f["gates"], _evs(ex["gates"]), rtol=0, atol=1e-15)
+    assert f["counts"].tolist() == ex["counts"]
+    assert f["offsets"].tolist() == ex["offsets"]
+    assert f["row_of_pair"].tolist() == ex["row_of_pair"]
+    np.testing.assert_allclose(f["out"], _evs(ex["out"]), rtol=1e-14, atol=1e-15)
+    b = O.layer_backward(f, x, dout, W_gu, W_down, W_r=W_r, prec="f64")
+    np.testing.assert_allclose(b["dx"], _evs(ex["dx"]), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(b["dW_down"], _evs(ex["dW_down"]), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(b["dW_gu"], _evs(ex["dW_gu"]), rtol=1e-14, atol=1e-15)
+
+
+def test_golden_k2_forward_router_grads(golden):
+    g = golden["inputs"]
+    x, W_r = np.array(g["x"]), np.array(g["W_r"])
+    W_gu, W_down, dout = np.array(g["W_gu"]), np.array(g["W_down"]), np.array(g["dout"])
+    ex = golden["k2"]
+    f = O.layer_forward(x, 2, 0, 2, W_gu, W_down, W_r=W_r, tile_m=4, prec="f64")
+    assert f["idx"].tolist() == ex["idx"]
+    np.testing.assert_allclose(f["gates"], _evs(ex["gates"]), rtol=1e-15, atol=1e-15)
+    assert f["counts"].tolist() == ex["counts"]
+    assert f["offsets"].tolist() == ex["offsets"]
+    assert f["row_of_pair"].tolist() == ex["row_of_pair"]
+    assert f["pair_of_row"].tolist() == ex["pair_of_row"]
+    np.testing.assert_allclose(f["out"], _evs(ex["out"]), rtol=1e-14, atol=1e-15)
+    b = O.layer_backward(f, x, dout, W_gu, W_down, W_r=W_r, prec="f64")
+    np.testing.assert_allclose(b["dgates"], _evs(ex["dgates"]), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(b["dlogits"], _evs(ex["dlogits"]), rtol=1e-13, atol=1e-15)
+
+
+def test_golden_k2_window(golden):
+    g = golden["inputs"]
+    x, W_r = np.array(g["x"]), np.array(g["W_r"])
+    W_gu, W_down = np.array(g["W_gu"]), np.array(g["W_down"])
+    ex = golden["k2_window_expert1_only"]
+    f = O.layer_forward(x, 2, ex["e_lo"], ex["E_l"], W_gu[1:2], W_down[1:2], W_r=W_r,
+                        tile_m=4, prec="f64")
+    assert f["counts"].tolist() == ex["counts"]
+    assert f["offsets"].tolist() == ex["offsets"]
+    assert f["row_of_pair"].tolist() == ex["row_of_pair"]
+    assert f["pair_of_row"].tolist() == ex["pair_of_row"]
+    np.testing.assert_allclose(f["out"], _evs(ex["out"]), rtol=1e-14, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------
+# rounding: library routine (torch's RNE cast)
+# ----------------------------------------------------------------------------
+def test_round_bf16_matches_torch_cast():
+    import torch
+
+    rng = np.random.default_rng(1)
+    v = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000),
+        np.array([0.0, -0.0, 1.0, -1.0, 3.0e38, 1e-40, -1e-40]),
+    ]).astype(np.float32)
+    # exact ties: bf16 value + half an ulp, odd and even kept lsb
+    base = np.array([1.0, 1.0078125, 2.0, 2.015625, -1.0078125], np.float32)
+    u = base.view(np.uint32) | np.uint32(0x8000)
+    v = np.concatenate([v, u.view(np.float32)])
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float32).numpy().astype(np.float64)
+    got = O.round_bf16(v)
+    assert np.array_equal(got.view(np.uint64), ref.view(np.uint64))
+
+
+# ----------------------------------------------------------------------------
+# routing: brute force and closed forms
+# ----------------------------------------------------------------------------
+def test_logits_match_elementwise_sum():
+    rng = np.random.default_rng(2)
+    x, W, b = _rand((7, 5), rng), _rand((5, 4), rng), _rand(4, rng)
+    l = O.router_logits(x, W, b, prec="f64")
+    for t in range(7):
+        for e in range(4):
+            ref = math.fsum(x[t, c] * W[c, e] for c in range(5)) + b[e]
+            assert abs(l[t, e] - ref) < 1e-13
+
+
+def test_topk_brute_force_sort_and_ties():
+    rng = np.random.default_rng(3)
+    l = np.round(rng.standard_normal((200, 9)), 1)   # rounding forces many ties
+    for K in (1, 3, 9):
+        idx, gates = O.topk_route(l, K, prec="f64")
+        for t in range(200):
+            order = sorted(range(9), key=lambda e: (-l[t, e], e))[:K]
+            assert idx[t].tolist() == order
+            ex = [math.exp(l[t, e] - l[t, order[0]]) for e in order]
+            s = math.fsum(ex)
+            np.testing.assert_allclose(gates[t], [v / s for v in ex], rtol=1e-14)
+        np.testing.assert_allclose(gates.sum(1), 1.0, rtol=1e-14)
+
+
+def test_topk_k1_is_argmax_gate_one_and_k_e_is_permutation():
+    rng = np.random.default_rng(4)
+    l = rng.standard_normal((100, 8))
+    idx, g = O.topk_route(l, 1, prec="f32")
+    assert np.array_equal(idx[:, 0], np.argmax(l, axis=1))
+    assert np.all(g == 1.0)
+    idx, g = O.topk_route(l, 8, prec="f32")
+    assert np.all(np.sort(idx, axis=1) == np.arange(8)[None, :])
+    soft = np.exp(l) / np.exp(l).sum(1, keepdims=True)          # K = E: plain softmax
+    np.testing.assert_allclose(g, np.take_along_axis(soft, idx.astype(np.int64), 1),
+                               rtol=1e-6)
+
+
+def test_force_balance_closed_form_counts():
+    w = WORKLOADS["ep16_rank_bf16"]
+    idx = O.force_balance_idx(w.T, w.K, w.E)
+    assert np.array_equal(np.bincount(idx.reshape(-1), minlength=w.E),
+                          np.full(w.E, w.T * w.K // w.E))
+    for t in (0, 1, 4095):
+        assert sorted(idx[t].tolist()) == list(range(8))  # distinct per token (K <= E)
+    plan = O.dispatch_plan(idx[:512], 0, 8, 256)
+    assert plan["counts"].tolist() == [512] * 8
+
+
+# ----------------------------------------------------------------------------
+# dispatch plan: invariants and library routine (bincount, stable argsort)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("e_lo,E_l", [(0, 16), (3, 5), (15, 1), (0, 1)])
+def test_plan_invariants(e_lo, E_l):
+    rng = np.random.default_rng(5 + e_lo)
+    T, K, E = 300, 4, 16
+    # distinct experts per token, skewed toward low ids
+    idx = np.stack([rng.choice(E, K, replace=False, p=np.arange(E, 0, -1) / 136.0)
+                    for _ in range(T)]).astype(np.int32)
+    p = O.dispatch_plan(idx, e_lo, E_l, tile_m=32)
+    flat = idx.reshape(-1)
+    local = (flat >= e_lo) & (flat < e_lo + E_l)
+    N = int(local.sum())
+    assert np.array_equal(p["counts"], np.bincount(flat[local] - e_lo, minlength=E_l))
+    assert p["offsets"][0] == 0 and p["offsets"][-1] == N
+    rop = p["row_of_pair"].reshape(-1)
+    assert np.all(rop[~local] == -1)
+    assert np.array_equal(np.sort(rop[local]), np.arange(N))           # bijection
+    pr = p["pair_of_row"]
+    assert np.array_equal(rop[pr[:N]], np.arange(N))                    # inverse
+    assert np.all(pr[N:] == -1)
+    # stable: equals a stable argsort of the local ids
+    order = np.nonzero(local)[0][np.argsort(flat[local], kind="stable")]
+    assert np.array_equal(pr[:N], order)
+    for j in range(E_l):                                                 # tokens increase
+        seg = pr[p["offsets"][j]:p["offsets"][j + 1]] // K
+        assert np.all(np.diff(seg) > 0)
+    np.testing.assert_array_equal(p["tile_offsets"],
+                                  np.concatenate([[0], np.cumsum(-(-p["counts"] // 32))]))
+
+
+def test_plan_empty_and_degenerate():
+    p = O.dispatch_plan(np.zeros((0, 2), np.int32), 0, 4, 256)
+    assert p["counts"].tolist() == [0] * 4 and p["offsets"].tolist() == [0] * 5
+    idx = np.full((5, 2), 7, np.int32)
+    idx[:, 1] = 6
+    p = O.dispatch_plan(idx, 0, 4, 256)       # nothing local
+    assert p["offsets"][-1] == 0 and np.all(p["row_of_pair"] == -1)
+
+
+def test_permute_copy_and_unpermute_identity():
+    rng = np.random.default_rng(6)
+    T, K, E, d = 50, 3, 6, 8
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+    x = rng.standard_normal((T, d))
+    p = O.dispatch_plan(idx, 1, 4, 16)
+    N = int(p["offsets"][-1])
+    xp = O.permute(x, p["pair_of_row"], K, N)
+    for r in range(N):
+        assert np.array_equal(xp[r], x[p["pair_of_row"][r] // K])
+    back = O.dispatch_bwd(xp, p["row_of_pair"], prec="f64")
+    nloc = (p["row_of_pair"] >= 0).sum(1)
+    assert np.array_equal(back, x * nloc[:, None])
+
+
+# ----------------------------------------------------------------------------
+# FFN + combine: brute-force per-token definition with no permutation
+# ----------------------------------------------------------------------------
+def _brute_layer(x, idx, gates, e_lo, E_l, W_gu, W_down):
+    T, d = x.shape
+    F = W_gu.shape[1] // 2
+    out = np.zeros((T, d))
+    for t in range(T):
+        for k in range(idx.shape[1]):
+            e = int(idx[t, k])
+            if not (e_lo <= e < e_lo + E_l):
+                continue
+            j = e - e_lo
+            y = np.zeros(d)
+            for f in range(F):
+                gv = math.fsum(W_gu[j, f, c] * x[t, c] for c in range(d))
+                uv = math.fsum(W_gu[j, F + f, c] * x[t, c] for c in range(d))
+                av = gv / (1.0 + math.exp(-gv)) * uv
+                y += W_down[j, :, f] * av
+            out[t] += gates[t, k] * y
+    return out
+
+
+def test_ffn_combine_match_brute_force():
+    rng = np.random.default_rng(7)
+    T, d, F, E, K, e_lo, E_l = 24, 6, 5, 6, 3, 1, 4
+    x = rng.standard_normal((T, d))
+    W_r = rng.standard_normal((d, E))
+    W_gu = rng.standard_normal((E_l, 2 * F, d)) * 0.5
+    W_down = rng.standard_normal((E_l, d, F)) * 0.5
+    f = O.layer_forward(x, K, e_lo, E_l, W_gu, W_down, W_r=W_r, tile_m=4, prec="f64")
+    ref = _brute_layer(x, f["idx"], f["gates"], e_lo, E_l, W_gu, W_down)
+    np.testing.assert_allclose(f["out"], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_identity_experts_combine_gives_gate_weighted_x():
+    rng = np.random.default_rng(8)
+    T, d, E, K = 40, 8, 5, 2
+    x = rng.standard_normal((T, d))
+    l = rng.standard_normal((T, E))
+    idx, gates = O.topk_route(l, K, prec="f64")
+    p = O.dispatch_plan(idx, 0, E, 8)
+    N = int(p["offsets"][-1])
+    xp = O.permute(x, p["pair_of_row"], K, N)
+    out = O.combine(xp, gates, p["row_of_pair"], prec="f64")   # y_p := xp
+    np.testing.assert_allclose(out, x, rtol=1e-14, atol=1e-14)  # gates sum to 1
+    p = O.dispatch_plan(idx, 1, 2, 8)                            # partial window
+    N = int(p["offsets"][-1])
+    xp = O.permute(x, p["pair_of_row"], K, N)
+    out = O.combine(xp, gates, p["row_of_pair"], prec="f64")
+    loc = (p["row_of_pair"] >= 0)
+    np.testing.assert_allclose(out, x * (gates * loc).sum(1, keepdims=True), rtol=1e-14,
+                               atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# gradients: central finite differences in float64
+# ----------------------------------------------------------------------------
+def _loss(x, W_r, W_gu, W_down, dout, K, e_lo, E_l):
+    f = O.layer_forward(x, K, e_lo, E_l, W_gu, W_down, W_r=W_r, tile_m=4, prec="f64")
+    return float(np.sum(f["out"] * dout)), f["idx"]
+
+
+def test_finite_differences_full_layer():
+    rng = np.random.default_rng(9)
+    T, d, F, E, K, e_lo, E_l = 6, 5, 3, 4, 2, 1, 2
+    x = rng.standard_normal((T, d))
+    W_r = rng.standard_normal((d, E))
+    W_gu = rng.standard_normal((E_l, 2 * F, d))
+    W_down = rng.standard_normal((E_l, d, F))
+    dout = rng.standard_normal((T, d))
+    f = O.layer_forward(x, K, e_lo, E_l, W_gu, W_down, W_r=W_r, tile_m=4, prec="f64")
+    assert 0 < f["N"] < T * K
+    b = O.layer_backward(f, x, dout, W_gu, W_down, W_r=W_r, prec="f64")
+    h = 1e-6
+    grads = {"x": b["dx"], "W_r": b["dW_r"], "W_gu": b["dW_gu"], "W_down": b["dW_down"]}
+    params = {"x": x, "W_r": W_r, "W_gu": W_gu, "W_down": W_down}
+    checked = 0
+    for name, P in params.items():
+        for i in np.ndindex(P.shape):
+            old = P[i]
+            P[i] = old + h
+            lp, ip = _loss(params["x"], params["W_r"], params["W_gu"], params["W_down"],
+                           dout, K, e_lo, E_l)
+            P[i] = old - h
+            lm, im = _loss(params["x"], params["W_r"], params["W_gu"], params["W_down"],
+                           dout, K, e_lo, E_l)
+            P[i] = old
+            if not (np.array_equal(ip, f["idx"]) and np.array_equal(im, f["idx"])):
+                continue
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - grads[name][i]) <= 1e-6 * max(1.0, abs(fd)), (name, i)
+            checked += 1
+    assert checked > 0.9 * sum(p.size for p in params.values())
+
+
+def test_finite_differences_gates_and_logits():
+    rng = np.random.default_rng(10)
+    T, d, F, E, K = 5, 4, 3, 3, 2
+    x = rng.standard_normal((T, d))
+    W_gu = rng.standard_normal((E, 2 * F, d))
+    W_down = rng.standard_normal((E, d, F))
+    dout = rng.standard_normal((T, d))
+    logits = rng.standard_normal((T, E))
+    f = O.layer_forward(x, K, 0, E, W_gu, W_down, logits=logits, tile_m=4, prec="f64")
+    b = O.layer_backward(f, x, dout, W_gu, W_down, W_r=None, prec="f64")
+    h = 1e-6
+    for i in np.ndindex(logits.shape):
+        lp_, lm_ = logits.copy(), logits.copy()
+        lp_[i] += h
+        lm_[i] -= h
+        fp = O.layer_forward(x, K, 0, E, W_gu, W_down, logits=lp_, tile_m=4, prec="f64")
+        fm = O.layer_forward(x, K, 0, E, W_gu, W_down, logits=lm_, tile_m=4, prec="f64")
+        fd = (np.sum(fp["out"] * dout) - np.sum(fm["out"] * dout)) / (2 * h)
+        assert abs(fd - b["dlogits"][i]) <= 1e-6 * max(1.0, abs(fd))
+    # dgates: forced balance with gates as inputs
+    gates = rng.random((T, K)) + 0.1
+    f = O.layer_forward(x, K, 0, E, W_gu, W_down, E=E, force_balance=True, gates=gates,
+                        tile_m=4, prec="f64")
+    b = O.layer_backward(f, x, dout, W_gu, W_down, differentiate_router=False, prec="f64")
+    for i in np.ndindex(gates.shape):
+        gp, gm = gates.copy(), gates.copy()
+        gp[i] += h
+        gm[i] -= h
+        fp = O.layer_forward(x, K, 0, E, W_gu, W_down, E=E, force_balance=True, gates=gp,
+                             tile_m=4, prec="f64")
+        fm = O.layer_forward(x, K, 0, E, W_gu, W_down, E=E, force_balance=True, gates=gm,
+                             tile_m=4, prec="f64")
+        fd = (np.sum(fp["out"] * dout) - np.sum(fm["out"] * dout)) / (2 * h)
+        assert abs(fd - b["dgates"][i]) <= 1e-6 * max(1.0, abs(fd))
+
+
+def test_wgrad_accumulation_is_additive():
+    rng = np.random.default_rng(11)
+    E_l, d, F = 3, 6, 4
+    offs_a = np.array([0, 5, 5, 9])
+    offs_b = np.array([0, 2, 6, 7])
+    mk = lambda n: (rng.standard_normal((n, d)), rng.standard_normal((n, F)),
+                    rng.standard_normal((n, 2 * F)), rng.standard_normal((n, d)))
+    A, B = mk(9), mk(7)
+    gA = O.ffn_wgrad(*A, offs_a, prec="f64")
+    gAB = O.ffn_wgrad(*B, offs_b, dW_gu_prev=gA[0], dW_down_prev=gA[1], prec="f64")
+    # union: each expert's rows of A followed by its rows of B
+    U = [np.concatenate([np.concatenate([A[i][offs_a[j]:offs_a[j + 1]],
+                                         B[i][offs_b[j]:offs_b[j + 1]]])
+                         for j in range(E_l)]) for i in range(4)]
+    offs_u = np.concatenate([[0], np.cumsum(np.diff(offs_a) + np.diff(offs_b))])
+    gU = O.ffn_wgrad(*U, offs_u, prec="f64")
+    assert U[0].shape[0] == 16
+    np.testing.assert_allclose(gAB[0], gU[0], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(gAB[1], gU[1], rtol=1e-13, atol=1e-13)
+    z = O.ffn_wgrad(*[v[:0] for v in A], np.zeros(E_l + 1, int), prec="f64")
+    assert np.all(z[0] == 0) and np.all(z[1] == 0)        # empty experts -> 0
+
+
+def test_bf16_oracle_within_tolerance_of_f64_oracle():
+    w = WORKLOADS["tiny_f32"]
+    inp = make_inputs(w, seed=0)
+    args = dict(W_r=inp["W_r"], tile_m=256)
+    x = O.round_bf16(inp["x"])
+    Wr = O.round_bf16(inp["W_r"])
+    Wgu, Wd, dout = O.round_bf16(inp["W_gu"]), O.round_bf16(inp["W_down"]), O.round_bf16(inp["dout"])
+    args["W_r"] = Wr
+    f64 = O.layer_forward(x, w.K, 0, w.E, Wgu, Wd, prec="f64", **args)
+    b16 = O.layer_forward(x, w.K, 0, w.E, Wgu, Wd, prec="bf16", **args)
+    same = np.all(f64["idx"] == b16["idx"], axis=1)
+    assert same.mean() > 0.99
+    tol = lambda ref: 2e-2 * np.maximum(1.0, np.abs(ref))
+    assert np.all(np.abs(b16["out"][same] - f64["out"][same]) <= tol(f64["out"][same]))
+    g64 = O.layer_backward(f64, x, dout, Wgu, Wd, W_r=Wr, prec="f64")
+    g16 = O.layer_backward(b16, x, dout, Wgu, Wd, W_r=Wr, prec="bf16")
+    if same.all():
+        for k in ("dx", "dW_gu", "dW_down", "dW_r"):
+            assert np.all(np.abs(g16[k] - g64[k]) <= tol(g64[k])), k
