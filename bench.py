@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of one GPU's share of the MoE expert-parallel layer (MI355X).
+
+One step = the 1F1B two-micro-batch step of the expert-parallel overlap pages
+(1F1B note page 2, "MoE 1F1B overlap"): the forward of one micro-batch and the
+backward (dgrad, then wgrad deferred past the other's expert GEMMs) of the other,
+on two streams, so that every step passes T tokens through the whole layer
+forward and backward.  Throughput = T / step time (tokens/s).  Inputs are
+synthetic (seeded), resident in HBM before the timed region.
+
+Prints ONE JSON line on stdout; diagnostics go to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "MoE layer fwd+bwd tokens/s on 1 MI355X; grouped-GEMM MFMA util %; dispatch HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+
+GEMM_KERNELS = ("ffn_gate_up", "ffn_down", "dgrad_act", "dgrad_in", "wgrad")
+
+
+def err(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(w, N, T_loc):
+    """Per-launch algorithmic work: flops for the GEMMs, HBM bytes for the
+    permute kernels (one pass over each operand, no re-reads)."""
+    d, F, T, K, E = w.d, w.F, w.T, w.K, w.E
+    b = 2 if w.dtype == "bf16" else 4
+    return {
+        "ffn_gate_up": ("flop", 2.0 * N * d * 2 * F),
+        "ffn_down": ("flop", 2.0 * N * F * d),
+        "dgrad_act": ("flop", 2.0 * N * d * F),
+        "dgrad_in": ("flop", 2.0 * N * 2 * F * d),
+        "wgrad": ("flop", 6.0 * N * d * F),
+        "router": ("flop", 2.0 * T * d * E),
+        # x rows of tokens with a local expert + row map -> N rows
+        "permute": ("byte", T_loc * d * b + 4.0 * T * K + N * d * b),
+        # y_p rows + gates + row map -> out
+        "combine": ("byte", N * d * b + 8.0 * T * K + T * d * b),
+        # dout + y_p rows + gates + map -> dy_p rows + dgates
+        "combine_bwd": ("byte", T * d * b + 2.0 * N * d * b + 12.0 * T * K),
+        # dx_p rows + map -> dx
+        "dispatch_bwd": ("byte", N * d * b + 4.0 * T * K + T * d * b),
+    }
+
+
+def cpu_oracle_baseline(w, inp, target_s=10.0):
+    """The oracle as it stands, timed on this host on the first Ts tokens of the
+    workload (full weights), one forward + backward; Ts grown until the run
+    takes about target_s seconds."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    fb = w.route == "force_balance"
+    X = {k: (None if v is None else np.asarray(v, np.float64)) for k, v in inp.items()}
+
+    def run(Ts):
+        t0 = time.perf_counter()
+        f = O.layer_forward(X["x"][:Ts], w.K, w.e_lo, w.E_l, X["W_gu"], X["W_down"],
+                            W_r=X["W_r"], bias=X["bias"], E=w.E, force_balance=fb,
+                            gates=None if X["gates"] is None else X["gates"][:Ts],
+                            prec=w.dtype)
+        O.layer_backward(f, X["x"][:Ts], X["dout"][:Ts], X["W_gu"], X["W_down"], W_r=X["W_r"],
+                         differentiate_router=not fb, prec=w.dtype)
+        return time.perf_counter() - t0
+
+    Ts = min(w.T, 64)
+    el = run(Ts)
+    while el < target_s / 4 and Ts < w.T:
+        Ts = min(w.T, max(Ts * 2, int(Ts * target_s / max(el, 1e-3))))
+        el = run(Ts)
+    return {"value": Ts / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {Ts} of {w.T} tokens of {w.name}, full weights, one forward+backward "
+                      f"(float64 numpy, bf16 rounding points), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="ep16_rank_bf16")
+    ap.add_argument("--tokens", type=int, default=None, help="override T of the workload")
+    ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
+    ap.add_argument("--no-serial", action="store_true", help="skip the serialized comparison")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        err("bench.py: this build is single-GPU only (one GPU's share of the expert-parallel "
+            "layer); runs on more than one GPU are not supported.")
+        sys.exit(2)
+
+    import torch
+    import combine_expert_ffn_amd as M
+    from combine_expert_ffn_amd.inputs import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        err("bench.py: no GPU visible")
+        sys.exit(1)
+    M.lib()  # fails loudly if libmoe.so is not built
+    w = WORKLOADS[args.workload]
+    if args.tokens:
+        w = w.with_tokens(args.tokens)
+    err(f"[bench] workload {w.name}: T={w.T} d={w.d} F={w.F} E={w.E} E_l={w.E_l} K={w.K} "
+        f"{w.dtype} route={w.route}")
+    inp = make_inputs(w, seed=0, microbatches=2)
+    s = M.shape_of(w)
+    D = lambda a: torch.from_numpy(a).to("cuda", torch.bfloat16 if w.dtype == "bf16" else torch.float32)
+    F32 = lambda a: torch.from_numpy(a).to("cuda")
+    topk = w.route == "topk"
+    mode = M.MOE_ROUTE_TOPK if topk else M.MOE_ROUTE_FORCE_BALANCE
+    W_gu, W_down = D(inp["W_gu"]), D(inp["W_down"])
+    W_r = D(inp["W_r"]) if topk else None
+    bias = F32(inp["bias"]) if inp["bias"] is not None else None
+    dW_gu = torch.zeros(w.E_l, 2 * w.F, w.d, dtype=torch.float32, device="cuda")
+    dW_down = torch.zeros(w.E_l, w.d, w.F, dtype=torch.float32, device="cuda")
+    dW_r = torch.zeros(w.d, w.E, dtype=torch.float32, device="cuda") if topk else None
+    ws = torch.empty(M.moe_step_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    mbs = [M.MicroBatch(s, x=D(inp["x"]), dout=D(inp["dout"]),
+                        gates=None if topk else F32(inp["gates"])),
+           M.MicroBatch(s, x=D(inp["x_b"]), dout=D(inp["dout_b"]),
+                        gates=None if topk else F32(inp["gates_b"]))]
+    s0 = torch.cuda.current_stream()
+    s1 = torch.cuda.Stream()
+
+    def step(fwd, bwd, flags):
+        st = M.make_step(s, mode, W_gu, W_down, dW_gu, dW_down, ws, fwd=fwd, bwd=bwd, W_r=W_r,
+                         bias=bias, dW_r=dW_r, accumulate=M.MOE_ACCUM_DW)
+        M.moe_overlap_step(st, s0, s1, flags)
+
+    def run_loop(n, flags, i0):
+        for i in range(i0, i0 + n):
+            step(mbs[(i + 1) % 2], mbs[i % 2], flags)
+        return i0 + n
+
+    step(mbs[0], None, 0)  # prime: micro-batch 0 forwarded
+    i = run_loop(args.warmup, 0, 0)
+    torch.cuda.synchronize()
+    counts = [mbs[k].counts.cpu() for k in range(2)]
+    N = int(counts[0].sum())
+    T_loc = int((mbs[0].row_of_pair >= 0).any(dim=1).sum())
+
+    # ---- timed region: overlapped 1F1B steps, kernel events on their own streams
+    M.moe_timing_reset()
+    M.moe_timing_enable(64 * args.steps)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(s0)
+    i = run_loop(args.steps, 0, i)
+    ev1.record(s0)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    M.moe_timing_disable()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    kern = M.moe_timing_report()
+    err(f"[bench] overlapped: {ms_step:.4f} ms/step (wall {1e3 * wall / args.steps:.4f})")
+
+    # ---- serialized comparison (same calls, one stream, forward then backward)
+    ms_serial = None
+    if not args.no_serial:
+        i = run_loop(args.warmup, M.MOE_STEP_SERIALIZE, i)
+        torch.cuda.synchronize()
+        ev0.record(s0)
+        i = run_loop(args.steps, M.MOE_STEP_SERIALIZE, i)
+        ev1.record(s0)
+        torch.cuda.synchronize()
+        ms_serial = ev0.elapsed_time(ev1) / args.steps
+        err(f"[bench] serialized: {ms_serial:.4f} ms/step -> overlap x{ms_serial / ms_step:.3f}")
+
+    nonfinite = int(sum((~torch.isfinite(t.float())).sum().item()
+                        for mb in mbs for t in (mb.out, mb.dx)))
+
+    # ---- per-kernel achieved rates from the live kernel events
+    work = algorithmic(w, N, T_loc)
+    kernels = {}
+    for name, (tot_ms, n) in sorted(kern.items(), key=lambda kv: -kv[1][0]):
+        avg_s = tot_ms / 1e3 / max(n, 1)
+        ent = {"avg_us": round(avg_s * 1e6, 2), "launches_per_step": round(n / args.steps, 3),
+               "ms_per_step": round(tot_ms / args.steps, 4)}
+        if name in work:
+            kind, amount = work[name]
+            if kind == "flop":
+                ach = amount / avg_s / 1e12
+                ent.update(achieved=round(ach, 1), unit="TFLOP/s",
+                           frac=round(ach / PEAK_BF16_TFLOPS, 4))
+            else:
+                ach = amount / avg_s / 1e9
+                ent.update(achieved=round(ach, 1), unit="GB/s", frac=round(ach / PEAK_HBM_GBS, 4))
+        kernels[name] = ent
+        err(f"  {name:14s} {ent}")
+
+    gemm = [k for k in GEMM_KERNELS if k in kern]
+    dom = max(gemm, key=lambda k: kern[k][0])
+    dom_avg_s = kern[dom][0] / 1e3 / kern[dom][1]
+    dom_ach = work[dom][1] / dom_avg_s / 1e12
+    gemm_flops = sum(work[k][1] * kern[k][1] for k in gemm)
+    gemm_s = sum(kern[k][0] / 1e3 for k in gemm)
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(dom_ach, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dom_ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": None,
+                "algorithmic_per_launch": f"{work[dom][1]:.4g} flop",
+                "avg_launch_us": round(dom_avg_s * 1e6, 2)}
+    disp = kernels.get("permute", {})
+
+    tokens_per_s = w.T / (ms_step / 1e3)
+    cpu = None
+    if args.cpu_baseline == "on":
+        cpu = cpu_oracle_baseline(w, inp)
+        err(f"[bench] cpu oracle: {cpu}")
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "F": w.F, "E": w.E, "e_lo": w.e_lo,
+                   "E_l": w.E_l, "K": w.K, "routing": w.route, "N_rows": N,
+                   "step": "1F1B: forward of one micro-batch + backward of the other, "
+                           "two streams, wgrad deferred"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "grouped_gemm_mfma_util": round(gemm_flops / gemm_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "dispatch_hbm_gbs": disp.get("achieved"),
+        "serialized_ms_per_step": None if ms_serial is None else round(ms_serial, 4),
+        "overlap_speedup": None if ms_serial is None else round(ms_serial / ms_step, 4),
+        "kernels": kernels,
+        "nonfinite_outputs": nonfinite,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

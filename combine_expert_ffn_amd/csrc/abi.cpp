@@ -1,0 +1,600 @@
+// libmoe C ABI: host-side validation, launch sequencing and the two-stream
+// two-micro-batch step.  Every entry point validates all of its arguments
+// before the first launch, so a rejected call writes nothing.
+#include "moe_internal.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+namespace moe {
+
+static thread_local char g_err[512] = "";
+
+int set_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// kernel timing
+// ---------------------------------------------------------------------------
+struct TimingState {
+  std::mutex mu;
+  bool on = false;
+  int cap = 0;
+  int used = 0;
+  std::vector<hipEvent_t> ev;  // 2 per record
+  std::vector<const char*> name;
+};
+static TimingState g_timing;
+
+KernelTimer::KernelTimer(const char* nm, hipStream_t st) : stream(st) {
+  if (!__atomic_load_n(&g_timing.on, __ATOMIC_ACQUIRE)) return;
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  if (!g_timing.on || g_timing.used >= g_timing.cap) return;
+  slot = g_timing.used++;
+  g_timing.name[slot] = nm;
+  if (hipEventRecord(g_timing.ev[2 * slot], st) != hipSuccess) slot = -1;
+}
+
+void KernelTimer::stop() {
+  if (slot >= 0) (void)hipEventRecord(g_timing.ev[2 * slot + 1], stream);
+  slot = -1;
+}
+
+static int validate_shape(const moe_shape* s) {
+  if (!s) return set_error(MOE_ERR_NULL, "shape is NULL");
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16)
+    return set_error(MOE_ERR_DTYPE, "dtype %d is neither MOE_F32 nor MOE_BF16", s->dtype);
+  if (s->reserved != 0) return set_error(MOE_ERR_ARG, "shape.reserved must be 0");
+  if (s->T < 0) return set_error(MOE_ERR_SHAPE, "T = %lld < 0", (long long)s->T);
+  if (s->E < 1 || s->E > 512)
+    return set_error(MOE_ERR_SHAPE, "E = %lld outside [1, 512]", (long long)s->E);
+  if (s->K < 1 || s->K > 16 || s->K > s->E)
+    return set_error(MOE_ERR_SHAPE, "K = %lld outside [1, min(E, 16)]", (long long)s->K);
+  if (s->E_l < 1 || s->E_l > 256 || s->e_lo < 0 || s->e_lo + s->E_l > s->E)
+    return set_error(MOE_ERR_SHAPE, "local window [%lld, %lld) invalid for E = %lld",
+                     (long long)s->e_lo, (long long)(s->e_lo + s->E_l), (long long)s->E);
+  if (s->d < 64 || s->d > 16384 || s->d % 64)
+    return set_error(MOE_ERR_SHAPE, "d = %lld must be a multiple of 64 in [64, 16384]",
+                     (long long)s->d);
+  if (s->F < 64 || s->F > 16384 || s->F % 64)
+    return set_error(MOE_ERR_SHAPE, "F = %lld must be a multiple of 64 in [64, 16384]",
+                     (long long)s->F);
+  if (s->T * s->K >= (1LL << 31) || s->T * s->E >= (1LL << 31))
+    return set_error(MOE_ERR_SHAPE, "T*K and T*E must be < 2^31");
+  return MOE_OK;
+}
+
+#define REQUIRE(p)                                                               \
+  do {                                                                           \
+    if (!(p)) return set_error(MOE_ERR_NULL, "%s: %s is NULL", __func__, #p);    \
+  } while (0)
+
+static size_t ws_one(const moe_shape* s) {
+  size_t b = ws_plan_bytes(s);
+  if (ws_wrt_bytes(s) > b) b = ws_wrt_bytes(s);
+  if (ws_router_partial_bytes(s) > b) b = ws_router_partial_bytes(s);
+  return b < 256 ? 256 : b;
+}
+
+static int need_ws(const char* fn, size_t have, size_t need) {
+  if (have < need)
+    return set_error(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu required", fn, have,
+                     need);
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// unvalidated bodies (arguments checked by the callers)
+// ---------------------------------------------------------------------------
+static int do_route(const moe_shape* s, int mode, const void* x, const void* W_r,
+                    const float* bias, float* logits, int32_t* idx, float* gates, void* ws,
+                    hipStream_t st) {
+  int rc;
+  if (mode == MOE_ROUTE_FORCE_BALANCE) return launch_force_balance(s, idx, st);
+  if (mode == MOE_ROUTE_TOPK) {
+    if (s->dtype == MOE_BF16 && s->T > 0) {
+      if ((rc = launch_transpose_wr(s, W_r, ws, st))) return rc;
+    }
+    if ((rc = launch_router_logits(s, x, W_r, ws, bias, logits, st))) return rc;
+  }
+  return launch_topk(s, logits, idx, gates, st);
+}
+
+static int do_dispatch(const moe_shape* s, const void* x, const int32_t* idx, int32_t* counts,
+                       int32_t* offsets, int32_t* row_of_pair, int32_t* pair_of_row,
+                       int32_t* tile_offsets, void* xp, void* ws, hipStream_t st) {
+  int rc = launch_plan(s, idx, counts, offsets, row_of_pair, pair_of_row, tile_offsets, ws, st);
+  if (rc) return rc;
+  return launch_permute(s, x, row_of_pair, xp, st);
+}
+
+static int do_dispatch_bwd(const moe_shape* s, const void* dxp, const int32_t* row_of_pair,
+                           const int32_t* idx, const float* dlogits, const void* W_r, void* dx,
+                           bool accumulate, void* ws, hipStream_t st) {
+  if (dlogits && s->T > 0) {
+    int rc = launch_transpose_wr(s, W_r, ws, st);
+    if (rc) return rc;
+  }
+  return launch_dispatch_bwd(s, dxp, row_of_pair, idx, dlogits, ws, dx, accumulate, st);
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_shape* s) {
+  if (validate_shape(s)) return 0;
+  return ws_one(s);
+}
+
+size_t moe_step_workspace_bytes(const moe_shape* s) {
+  if (validate_shape(s)) return 0;
+  return 2 * ws_one(s);
+}
+
+int moe_tile_m(void) { return kTileM; }
+
+const char* moe_last_error(void) { return g_err; }
+
+int moe_version(void) { return 100; }
+
+int moe_timing_enable(int max_records) {
+  if (max_records < 1) return set_error(MOE_ERR_SHAPE, "moe_timing_enable: max_records < 1");
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  while ((int)g_timing.name.size() < max_records) {
+    hipEvent_t a, b;
+    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess)
+      return set_error(MOE_ERR_HIP, "moe_timing_enable: hipEventCreate failed");
+    g_timing.ev.push_back(a);
+    g_timing.ev.push_back(b);
+    g_timing.name.push_back(nullptr);
+  }
+  g_timing.cap = max_records;
+  __atomic_store_n(&g_timing.on, true, __ATOMIC_RELEASE);
+  return MOE_OK;
+}
+
+int moe_timing_disable(void) {
+  __atomic_store_n(&g_timing.on, false, __ATOMIC_RELEASE);
+  return MOE_OK;
+}
+
+int moe_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.used = 0;
+  return MOE_OK;
+}
+
+int moe_timing_report(int i, char* name, size_t name_len, double* total_ms, int* launches) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  std::vector<const char*> names;
+  for (int r = 0; r < g_timing.used; ++r) {
+    bool seen = false;
+    for (const char* n : names) seen |= (strcmp(n, g_timing.name[r]) == 0);
+    if (!seen) names.push_back(g_timing.name[r]);
+  }
+  if (i < 0 || i >= (int)names.size()) return (int)names.size();
+  double tot = 0.0;
+  int cnt = 0;
+  for (int r = 0; r < g_timing.used; ++r) {
+    if (strcmp(g_timing.name[r], names[i]) != 0) continue;
+    float ms = 0.f;
+    if (hipEventSynchronize(g_timing.ev[2 * r + 1]) != hipSuccess ||
+        hipEventElapsedTime(&ms, g_timing.ev[2 * r], g_timing.ev[2 * r + 1]) != hipSuccess)
+      return set_error(MOE_ERR_HIP, "moe_timing_report: event query failed");
+    tot += ms;
+    ++cnt;
+  }
+  if (name && name_len) {
+    snprintf(name, name_len, "%s", names[i]);
+  }
+  if (total_ms) *total_ms = tot;
+  if (launches) *launches = cnt;
+  return (int)names.size();
+}
+
+int moe_route(const moe_shape* s, int mode, const void* x, const void* W_r, const float* bias,
+              float* logits, int32_t* idx, float* gates, void* ws, size_t ws_bytes,
+              hipStream_t stream) {
+  g_err[0] = 0;
+  if (int rc = validate_shape(s)) return rc;
+  REQUIRE(idx);
+  switch (mode) {
+    case MOE_ROUTE_TOPK:
+      REQUIRE(x);
+      REQUIRE(W_r);
+      REQUIRE(logits);
+      REQUIRE(gates);
+      if (s->dtype == MOE_BF16) {
+        REQUIRE(ws);
+        if (int rc = need_ws(__func__, ws_bytes, ws_wrt_bytes(s))) return rc;
+      }
+      break;
+    case MOE_ROUTE_TOPK_FROM_LOGITS:
+      REQUIRE(logits);
+      REQUIRE(gates);
+      break;
+    case MOE_ROUTE_FORCE_BALANCE:
+      break;
+    default:
+      return set_error(MOE_ERR_ARG, "moe_route: unknown mode %d", mode);
+  }
+  return do_route(s, mode, x, W_r, bias, logits, idx, gates, ws, stream);
+}
+
+int moe_dispatch(const moe_shape* s, const void* x, const int32_t* idx, int32_t* counts,
+                 int32_t* offsets, int32_t* row_of_pair, int32_t* pair_of_row,
+                 int32_t* tile_offsets, void* xp, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  if (int rc = validate_shape(s)) return rc;
+  REQUIRE(x);
+  REQUIRE(idx);
+  REQUIRE(counts);
+  REQUIRE(offsets);
+  REQUIRE(row_of_pair);
+  REQUIRE(pair_of_row);
+  REQUIRE(tile_offsets);
+  REQUIRE(xp);
+  REQUIRE(ws);
+  if (int rc = need_ws(__func__, ws_bytes, ws_plan_bytes(s))) return rc;
+  return do_dispatch(s, x, idx, counts, offsets, row_of_pair, pair_of_row, tile_offsets, xp, ws,
+                     stream);
+}
+
+int moe_expert_ffn_fwd(const moe_shape* s, const void* xp, const int32_t* offsets,
+                       const int32_t* tile_offsets, const void* W_gu, const void* W_down,
+                       void* h, void* a, void* yp, hipStream_t stream) {
+  g_err[0] = 0;
+  if (int rc = validate_shape(s)) return rc;
+  REQUIRE(xp);
+  REQUIRE(offsets);
+  REQUIRE(tile_offsets);
+  REQUIRE(W_gu);
+  REQUIRE(W_down);
+  REQUIRE(h);
+  REQUIRE(a);
+  REQUIRE(yp);
+  return launch_ffn_fwd(s, xp, offsets, tile_offsets, W_gu, W_down, h, a, yp, stream);
+}
+
+int moe_combine(const moe_shape* s, const void* yp, const float* gates,
+                const int32_t* row_of_pair, void* out, hipStream_t stream) {
+  g_err[0] = 0;
+  if (int rc = validate_shape(s)) return rc;
+  REQUIRE(yp);
+  REQUIRE(gates);
+  REQUIRE(row_of_pair);
+  REQUIRE(out);
+  return launch_combine(s, yp, gates, row_of_pair, out, stream);
+}
+
+int moe_combine_bwd(const moe_shape* s, const void* dout, const void* yp, const float* gates,
+                    const int32_t* row_of_pair, void* dyp, float* dgates, hipStream_t stream) {
+  g_err[0] = 0;
+  if (int rc = validate_shape(s)) return rc;
+  REQUIRE(dout);
+  REQUIRE(yp);
+  REQUIRE(gates);
+  REQUIRE(row_of_pair);
+  REQUIRE(dyp);
+  REQUIRE(dgates);
+  return launch_combine_bwd(s, dout, yp, gates, row_of_pair, dyp, dgates, stream);
+}
+
+int moe_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h, const int32_t* offsets,
+                  const int32_t* tile_offsets, const void* W_gu, const void* W_down, void* dh,
+                  void* dxp, hipStream_t stream) {
+  g_err[0] = 0;
+  if (int rc = validate_shape(s)) return rc;
+  REQUIRE(dyp);
+  REQUIRE(h);
+  REQUIRE(offsets);
+  REQUIRE(tile_offsets);
+  REQUIRE(W_gu);
+  REQUIRE(W_down);
+  REQUIRE(dh);
+  REQUIRE(dxp);
+  return launch_ffn_dgrad(s, dyp, h, offsets, tile_offsets, W_gu, W_down, dh, dxp, stream);
+}
+
+int moe_ffn_wgrad(const moe_shape* s, const void* xp, const void* a, const void* dh,
+                  const void* dyp, const int32_t* offsets, float* dW_gu, float* dW_down,
+                  int accumulate, hipStream_t stream) {
+  g_err[0] = 0;
+  if (int rc = validate_shape(s)) return rc;
+  REQUIRE(xp);
+  REQUIRE(a);
+  REQUIRE(dh);
+  REQUIRE(dyp);
+  REQUIRE(offsets);
+  REQUIRE(dW_gu);
+  REQUIRE(dW_down);
+  if (accumulate & ~(MOE_ACCUM_DX | MOE_ACCUM_DW))
+    return set_error(MOE_ERR_ARG, "moe_ffn_wgrad: unknown accumulate bits 0x%x", accumulate);
+  return launch_ffn_wgrad(s, xp, a, dh, dyp, offsets, dW_gu, dW_down,
+                          (accumulate & MOE_ACCUM_DW) != 0, stream);
+}
+
+int moe_route_bwd(const moe_shape* s, int mode, const float* dgates, const float* gates,
+                  const int32_t* idx, const void* x, float* dlogits, float* dW_r, int accumulate,
+                  void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  if (int rc = validate_shape(s)) return rc;
+  if (mode == MOE_ROUTE_FORCE_BALANCE)
+    return set_error(MOE_ERR_UNSUPPORTED,
+                     "moe_route_bwd: forced-balance gates are inputs; their gradient is dgates");
+  if (mode != MOE_ROUTE_TOPK && mode != MOE_ROUTE_TOPK_FROM_LOGITS)
+    return set_error(MOE_ERR_ARG, "moe_route_bwd: unknown mode %d", mode);
+  REQUIRE(dgates);
+  REQUIRE(gates);
+  REQUIRE(idx);
+  REQUIRE(dlogits);
+  if (accumulate & ~(MOE_ACCUM_DX | MOE_ACCUM_DW))
+    return set_error(MOE_ERR_ARG, "moe_route_bwd: unknown accumulate bits 0x%x", accumulate);
+  const bool with_dw = x && dW_r;
+  if (with_dw) {
+    REQUIRE(ws);
+    if (int rc = need_ws(__func__, ws_bytes, ws_router_partial_bytes(s))) return rc;
+  }
+  return launch_route_bwd(s, dgates, gates, idx, with_dw ? x : nullptr, dlogits,
+                          with_dw ? dW_r : nullptr, (accumulate & MOE_ACCUM_DW) != 0, ws, stream);
+}
+
+int moe_dispatch_bwd(const moe_shape* s, const void* dxp, const int32_t* row_of_pair,
+                     const int32_t* idx, const float* dlogits, const void* W_r, void* dx,
+                     int accumulate, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  if (int rc = validate_shape(s)) return rc;
+  REQUIRE(dxp);
+  REQUIRE(row_of_pair);
+  REQUIRE(dx);
+  if (accumulate & ~(MOE_ACCUM_DX | MOE_ACCUM_DW))
+    return set_error(MOE_ERR_ARG, "moe_dispatch_bwd: unknown accumulate bits 0x%x", accumulate);
+  if (dlogits) {
+    REQUIRE(idx);
+    REQUIRE(W_r);
+    REQUIRE(ws);
+    if (int rc = need_ws(__func__, ws_bytes, ws_wrt_bytes(s))) return rc;
+  }
+  return do_dispatch_bwd(s, dxp, row_of_pair, idx, dlogits, W_r, dx,
+                         (accumulate & MOE_ACCUM_DX) != 0, ws, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// two-micro-batch step
+// ---------------------------------------------------------------------------
+namespace moe {
+
+struct StepEvents {
+  hipEvent_t start, cb, route, dgrad, disp, fwd, end;
+};
+
+// One event set per (host thread, device); events are only recorded and waited
+// on inside one call, so reuse by the next call of the same thread is safe.
+static int step_events(StepEvents** out) {
+  static thread_local std::vector<StepEvents*> sets;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return set_error(MOE_ERR_HIP, "hipGetDevice failed");
+  if ((int)sets.size() <= dev) sets.resize(dev + 1, nullptr);
+  if (!sets[dev]) {
+    StepEvents* e = new StepEvents();
+    hipEvent_t* all[] = {&e->start, &e->cb, &e->route, &e->dgrad, &e->disp, &e->fwd, &e->end};
+    for (hipEvent_t* p : all)
+      if (hipEventCreateWithFlags(p, hipEventDisableTiming) != hipSuccess)
+        return set_error(MOE_ERR_HIP, "hipEventCreateWithFlags failed");
+    sets[dev] = e;
+  }
+  *out = sets[dev];
+  return MOE_OK;
+}
+
+static int validate_mb_fwd(const moe_mb* m, int mode) {
+  REQUIRE(m->x);
+  REQUIRE(m->idx);
+  REQUIRE(m->counts);
+  REQUIRE(m->offsets);
+  REQUIRE(m->row_of_pair);
+  REQUIRE(m->pair_of_row);
+  REQUIRE(m->tile_offsets);
+  REQUIRE(m->xp);
+  REQUIRE(m->h);
+  REQUIRE(m->a);
+  REQUIRE(m->yp);
+  REQUIRE(m->out);
+  REQUIRE(m->gates);
+  if (mode != MOE_ROUTE_FORCE_BALANCE) REQUIRE(m->logits);
+  return MOE_OK;
+}
+
+static int validate_mb_bwd(const moe_mb* m, int mode) {
+  REQUIRE(m->idx);
+  REQUIRE(m->gates);
+  REQUIRE(m->offsets);
+  REQUIRE(m->tile_offsets);
+  REQUIRE(m->row_of_pair);
+  REQUIRE(m->xp);
+  REQUIRE(m->h);
+  REQUIRE(m->a);
+  REQUIRE(m->yp);
+  REQUIRE(m->dout);
+  REQUIRE(m->dyp);
+  REQUIRE(m->dgates);
+  REQUIRE(m->dh);
+  REQUIRE(m->dxp);
+  REQUIRE(m->dx);
+  if (mode != MOE_ROUTE_FORCE_BALANCE) REQUIRE(m->dlogits);
+  return MOE_OK;
+}
+
+#define TRY(call)                 \
+  do {                            \
+    if (int rc_ = (call)) return rc_; \
+  } while (0)
+#define HIPTRY(call)                                                               \
+  do {                                                                             \
+    if ((call) != hipSuccess) return set_error(MOE_ERR_HIP, "%s failed", #call);   \
+  } while (0)
+
+struct StepCtx {
+  const moe_step* st;
+  const moe_shape* s;
+  void* wsA;
+  void* wsB;
+  bool router;  // TOPK mode: router weights are differentiated
+};
+
+static int fwd_route(const StepCtx& c, const moe_mb* A, hipStream_t q) {
+  return do_route(c.s, c.st->route_mode, A->x, c.st->W_r, c.st->bias, A->logits, A->idx,
+                  A->gates, c.wsA, q);
+}
+static int fwd_dispatch(const StepCtx& c, const moe_mb* A, hipStream_t q) {
+  return do_dispatch(c.s, A->x, A->idx, A->counts, A->offsets, A->row_of_pair, A->pair_of_row,
+                     A->tile_offsets, A->xp, c.wsA, q);
+}
+static int fwd_ffn(const StepCtx& c, const moe_mb* A, hipStream_t q) {
+  return launch_ffn_fwd(c.s, A->xp, A->offsets, A->tile_offsets, c.st->W_gu, c.st->W_down, A->h,
+                        A->a, A->yp, q);
+}
+static int fwd_combine(const StepCtx& c, const moe_mb* A, hipStream_t q) {
+  return launch_combine(c.s, A->yp, A->gates, A->row_of_pair, A->out, q);
+}
+static int bwd_combine(const StepCtx& c, const moe_mb* B, hipStream_t q) {
+  return launch_combine_bwd(c.s, B->dout, B->yp, B->gates, B->row_of_pair, B->dyp, B->dgates, q);
+}
+static int bwd_route(const StepCtx& c, const moe_mb* B, hipStream_t q) {
+  if (c.st->route_mode == MOE_ROUTE_FORCE_BALANCE) return MOE_OK;
+  const bool with_dw = c.router && c.st->dW_r;
+  return launch_route_bwd(c.s, B->dgates, B->gates, B->idx, with_dw ? B->x : nullptr, B->dlogits,
+                          with_dw ? c.st->dW_r : nullptr,
+                          (c.st->accumulate & MOE_ACCUM_DW) != 0, c.wsB, q);
+}
+static int bwd_dgrad(const StepCtx& c, const moe_mb* B, hipStream_t q) {
+  return launch_ffn_dgrad(c.s, B->dyp, B->h, B->offsets, B->tile_offsets, c.st->W_gu,
+                          c.st->W_down, B->dh, B->dxp, q);
+}
+static int bwd_dispatch(const StepCtx& c, const moe_mb* B, hipStream_t q) {
+  return do_dispatch_bwd(c.s, B->dxp, B->row_of_pair, B->idx, c.router ? B->dlogits : nullptr,
+                         c.st->W_r, B->dx, false, c.wsB, q);
+}
+static int bwd_wgrad(const StepCtx& c, const moe_mb* B, hipStream_t q) {
+  return launch_ffn_wgrad(c.s, B->xp, B->a, B->dh, B->dyp, B->offsets, c.st->dW_gu,
+                          c.st->dW_down, (c.st->accumulate & MOE_ACCUM_DW) != 0, q);
+}
+
+}  // namespace moe
+
+extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t s1, int flags) {
+  g_err[0] = 0;
+  REQUIRE(st);
+  const moe_shape* s = &st->shape;
+  if (int rc = validate_shape(s)) return rc;
+  if (flags & ~(MOE_STEP_SERIALIZE | MOE_STEP_EAGER_WGRAD))
+    return set_error(MOE_ERR_ARG, "moe_overlap_step: unknown flags 0x%x", flags);
+  const int mode = st->route_mode;
+  if (mode != MOE_ROUTE_TOPK && mode != MOE_ROUTE_TOPK_FROM_LOGITS &&
+      mode != MOE_ROUTE_FORCE_BALANCE)
+    return set_error(MOE_ERR_ARG, "moe_overlap_step: unknown route mode %d", mode);
+  if (st->accumulate & ~(MOE_ACCUM_DX | MOE_ACCUM_DW))
+    return set_error(MOE_ERR_ARG, "moe_overlap_step: unknown accumulate bits 0x%x",
+                     st->accumulate);
+  REQUIRE(st->W_gu);
+  REQUIRE(st->W_down);
+  if (mode == MOE_ROUTE_TOPK) REQUIRE(st->W_r);
+  const moe_mb* A = st->fwd;
+  const moe_mb* B = st->bwd;
+  if (A) TRY(validate_mb_fwd(A, mode));
+  if (B) {
+    TRY(validate_mb_bwd(B, mode));
+    REQUIRE(st->dW_gu);
+    REQUIRE(st->dW_down);
+    if (mode == MOE_ROUTE_TOPK && st->dW_r) REQUIRE(B->x);
+  }
+  if (A && B && A == B)
+    return set_error(MOE_ERR_ARG, "moe_overlap_step: fwd and bwd micro-batches must differ");
+  REQUIRE(st->ws);
+  const size_t one = ws_one(s);
+  if (int rc = need_ws(__func__, st->ws_bytes, 2 * one)) return rc;
+
+  StepCtx c{st, s, st->ws, (char*)st->ws + one, mode == MOE_ROUTE_TOPK};
+  const bool serial = (flags & MOE_STEP_SERIALIZE) || s0 == s1;
+  const bool eager = (flags & MOE_STEP_EAGER_WGRAD) != 0;
+
+  if (serial) {  // the forward-then-backward order of a non-overlapped layer
+    if (A) {
+      TRY(fwd_route(c, A, s0));
+      TRY(fwd_dispatch(c, A, s0));
+      TRY(fwd_ffn(c, A, s0));
+      TRY(fwd_combine(c, A, s0));
+    }
+    if (B) {
+      TRY(bwd_combine(c, B, s0));
+      TRY(bwd_route(c, B, s0));
+      TRY(bwd_dgrad(c, B, s0));
+      if (eager) TRY(bwd_wgrad(c, B, s0));
+      TRY(bwd_dispatch(c, B, s0));
+      if (!eager) TRY(bwd_wgrad(c, B, s0));
+    }
+    return MOE_OK;
+  }
+
+  StepEvents* ev = nullptr;
+  TRY(step_events(&ev));
+  // s1 starts after everything already queued on s0
+  HIPTRY(hipEventRecord(ev->start, s0));
+  HIPTRY(hipStreamWaitEvent(s1, ev->start, 0));
+  if (B) {
+    TRY(bwd_combine(c, B, s1));
+    HIPTRY(hipEventRecord(ev->cb, s1));
+  }
+  if (A) {
+    TRY(fwd_route(c, A, s0));
+    HIPTRY(hipEventRecord(ev->route, s0));
+  }
+  if (B) {
+    HIPTRY(hipStreamWaitEvent(s0, ev->cb, 0));
+    TRY(bwd_route(c, B, s0));
+    TRY(bwd_dgrad(c, B, s0));
+    HIPTRY(hipEventRecord(ev->dgrad, s0));
+    if (eager) TRY(bwd_wgrad(c, B, s0));
+  }
+  if (A) {
+    HIPTRY(hipStreamWaitEvent(s1, ev->route, 0));
+    TRY(fwd_dispatch(c, A, s1));
+    HIPTRY(hipEventRecord(ev->disp, s1));
+    HIPTRY(hipStreamWaitEvent(s0, ev->disp, 0));
+    TRY(fwd_ffn(c, A, s0));
+    HIPTRY(hipEventRecord(ev->fwd, s0));
+  }
+  if (B) {
+    HIPTRY(hipStreamWaitEvent(s1, ev->dgrad, 0));
+    TRY(bwd_dispatch(c, B, s1));
+    if (!eager) TRY(bwd_wgrad(c, B, s0));  // deferred past A's expert GEMMs
+  }
+  if (A) {
+    HIPTRY(hipStreamWaitEvent(s1, ev->fwd, 0));
+    TRY(fwd_combine(c, A, s1));
+  }
+  // s0 ends after everything the step issued on s1
+  HIPTRY(hipEventRecord(ev->end, s1));
+  HIPTRY(hipStreamWaitEvent(s0, ev->end, 0));
+  return MOE_OK;
+}

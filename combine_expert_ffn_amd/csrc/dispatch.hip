@@ -1,0 +1,466 @@
+// Dispatch (token -> expert-grouped rows) and combine (rows -> tokens, gate
+// weighted), forward and backward: the local halves of the token all-to-all
+// that the expert-parallel overlap pages hide behind the expert FFN (skill card
+// page 1, "What it is"; 1F1B note page 2, backward chain "combine.backward",
+// "dispatch.backward").
+//
+// The plan is a deterministic stable counting sort of the (token, slot) pairs
+// by local expert: per-block LDS histograms, one exclusive scan over
+// (expert, block), then an in-block stable rank from wave ballots + popcounts
+// and a per-wave LDS prefix.  No global atomics decide positions, so the maps
+// are bit-identical run to run.
+//
+// The copies are token-major: one wave per token reads the token's row once
+// and writes (or gathers) its K rows with 16-byte accesses.
+#include "moe_internal.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// plan step 1: per-block histogram of local expert ids.
+// blockcnt[j * NB + b] = number of pairs of block b with local id j.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void plan_hist_kernel(const int32_t* __restrict__ idx,
+                                                        long npairs, int e_lo, int E_l, int NB,
+                                                        int32_t* __restrict__ blockcnt) {
+  __shared__ int cnt[256];
+  const int b = blockIdx.x;
+  for (int j = threadIdx.x; j < E_l; j += 256) cnt[j] = 0;
+  __syncthreads();
+  const long p0 = (long)b * kPlanChunk;
+  const long p1 = min(npairs, p0 + kPlanChunk);
+  for (long p = p0 + threadIdx.x; p < p1; p += 256) {
+    const int j = idx[p] - e_lo;
+    if (j >= 0 && j < E_l) atomicAdd(&cnt[j], 1);
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < E_l; j += 256) blockcnt[(size_t)j * NB + b] = cnt[j];
+}
+
+// ---------------------------------------------------------------------------
+// plan step 2: one block.  Exclusive scan of blockcnt in (expert, block) order
+// -> blockbase; counts, offsets and tile_offsets.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void plan_scan_kernel(const int32_t* __restrict__ blockcnt,
+                                                         int32_t* __restrict__ blockbase,
+                                                         int E_l, int NB,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ tile_offsets) {
+  __shared__ int part[1024];
+  const int n = E_l * NB;
+  const int tid = threadIdx.x;
+  const int per = (n + 1023) / 1024;
+  const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
+  int s = 0;
+  for (int i = i0; i < i1; ++i) s += blockcnt[i];
+  part[tid] = s;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over the 1024 partial sums
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - s;  // exclusive prefix of this thread's segment
+  for (int i = i0; i < i1; ++i) {
+    blockbase[i] = run;
+    run += blockcnt[i];
+  }
+  __syncthreads();
+  const int total = part[1023];
+  // offsets[j] = blockbase[j*NB] (start of expert j's segment); offsets[E_l] = N
+  for (int j = tid; j <= E_l; j += 1024) {
+    int off;
+    if (j == E_l) off = total;
+    else if (NB == 0) off = 0;
+    else off = blockbase[(size_t)j * NB];
+    offsets[j] = off;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int j = 0; j < E_l; ++j) {
+      const int c = offsets[j + 1] - offsets[j];
+      counts[j] = c;
+      if (tile_offsets) tile_offsets[j] = acc;
+      acc += (c + kTileM - 1) / kTileM;
+    }
+    if (tile_offsets) tile_offsets[E_l] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// plan step 3: stable in-block rank -> row_of_pair, pair_of_row.
+// Rounds of 256 pairs; within a wave, pairs with the same expert are ranked by
+// ballot + popcount (one pass per distinct expert present in the wave); across
+// waves by a per-wave count prefix in LDS; across rounds by a running count.
+// Also writes -1 into pair_of_row rows [N, cap) of this block's range.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void plan_rank_kernel(const int32_t* __restrict__ idx,
+                                                        long npairs, int e_lo, int E_l, int NB,
+                                                        const int32_t* __restrict__ blockbase,
+                                                        const int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ row_of_pair,
+                                                        int32_t* __restrict__ pair_of_row) {
+  __shared__ int running[256];
+  __shared__ int wcnt[4][256];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int j = tid; j < E_l; j += 256) {
+    running[j] = blockbase[(size_t)j * NB + b];
+    wcnt[0][j] = wcnt[1][j] = wcnt[2][j] = wcnt[3][j] = 0;
+  }
+  __syncthreads();
+  const long p0 = (long)b * kPlanChunk;
+  const long p1 = min(npairs, p0 + kPlanChunk);
+  const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (long base = p0; base < p1; base += 256) {
+    const long p = base + tid;
+    int j = -1;
+    if (p < p1) {
+      const int jj = idx[p] - e_lo;
+      if (jj >= 0 && jj < E_l) j = jj;
+    }
+    unsigned long long active = __ballot(j >= 0);
+    int myrank = 0;
+    while (active) {  // wave-uniform loop: one pass per distinct expert in the wave
+      const int leader = __ffsll((long long)active) - 1;
+      const int jl = __shfl(j, leader, 64);
+      const unsigned long long m = __ballot(j == jl);
+      if (j == jl) myrank = __popcll(m & lt_mask);
+      if (lane == leader) wcnt[w][jl] = __popcll(m);
+      active &= ~m;
+    }
+    __syncthreads();
+    if (p < p1) {
+      if (j >= 0) {
+        int row = running[j] + myrank;
+        for (int ww = 0; ww < w; ++ww) row += wcnt[ww][j];
+        row_of_pair[p] = row;
+        if (row < npairs) pair_of_row[row] = (int32_t)p;
+      } else {
+        row_of_pair[p] = -1;
+      }
+    }
+    __syncthreads();
+    for (int jj = tid; jj < E_l; jj += 256) {
+      running[jj] += wcnt[0][jj] + wcnt[1][jj] + wcnt[2][jj] + wcnt[3][jj];
+      wcnt[0][jj] = wcnt[1][jj] = wcnt[2][jj] = wcnt[3][jj] = 0;
+    }
+    __syncthreads();
+  }
+  // rows [N, cap) of this block's row range get -1
+  const long N = offsets[E_l];
+  const long r0 = max(N, p0);
+  for (long r = r0 + tid; r < min(npairs, p0 + (long)kPlanChunk); r += 256) pair_of_row[r] = -1;
+}
+
+int launch_plan(const moe_shape* s, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                int32_t* row_of_pair, int32_t* pair_of_row, int32_t* tile_offsets, void* ws,
+                hipStream_t st) {
+  const long npairs = s->T * s->K;
+  const int NB = (int)cdiv(npairs, kPlanChunk);
+  int32_t* blockcnt = (int32_t*)ws;
+  int32_t* blockbase = blockcnt + (size_t)s->E_l * NB;
+  int rc;
+  if (NB > 0) {
+    MOE_LAUNCH("plan_hist", st,
+               plan_hist_kernel<<<NB, 256, 0, st>>>(idx, npairs, (int)s->e_lo, (int)s->E_l, NB, blockcnt));
+    if ((rc = check_launch("plan histogram"))) return rc;
+  }
+  MOE_LAUNCH("plan_scan", st,
+             plan_scan_kernel<<<1, 1024, 0, st>>>(blockcnt, blockbase, (int)s->E_l, NB, counts, offsets,
+                                       tile_offsets));
+  if ((rc = check_launch("plan scan"))) return rc;
+  if (NB > 0) {
+    MOE_LAUNCH("plan_rank", st,
+               plan_rank_kernel<<<NB, 256, 0, st>>>(idx, npairs, (int)s->e_lo, (int)s->E_l, NB, blockbase,
+                                         offsets, row_of_pair, pair_of_row));
+    if ((rc = check_launch("plan rank"))) return rc;
+  }
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// permute: xp[row_of_pair[t*K+k]] = x[t].  One wave per token, 16-byte chunks;
+// the token row is read once and written to each of its local rows.
+// ---------------------------------------------------------------------------
+template <int MAXC>
+__global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ x,
+                                                      const int32_t* __restrict__ row_of_pair,
+                                                      uint4* __restrict__ xp, int T, int K,
+                                                      int nch) {
+  const int t = (int)(((long)blockIdx.x * 256 + threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  const uint4* src = x + (size_t)t * nch;
+  for (int c0 = 0; c0 < nch; c0 += 64 * MAXC) {
+    uint4 v[MAXC];
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int c = c0 + lane + 64 * i;
+      if (c < nch) v[i] = src[c];
+    }
+    for (int k = 0; k < K; ++k) {
+      const int r = row_of_pair[(size_t)t * K + k];
+      if (r < 0 || r >= T * K) continue;
+      uint4* dst = xp + (size_t)r * nch;
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) {
+        const int c = c0 + lane + 64 * i;
+        if (c < nch) dst[c] = v[i];
+      }
+    }
+  }
+}
+
+static inline int row_chunks(const moe_shape* s) {
+  return (int)(s->d * (s->dtype == MOE_BF16 ? 2 : 4) / 16);
+}
+
+int launch_permute(const moe_shape* s, const void* x, const int32_t* row_of_pair, void* xp,
+                   hipStream_t st) {
+  if (s->T == 0) return MOE_OK;
+  MOE_LAUNCH("permute", st,
+             permute_kernel<4><<<(unsigned)cdiv(s->T, 4), 256, 0, st>>>(
+      (const uint4*)x, row_of_pair, (uint4*)xp, (int)s->T, (int)s->K, row_chunks(s)));
+  return check_launch("permute");
+}
+
+// ---------------------------------------------------------------------------
+// combine: out[t] = sum_k gates[t,k] * yp[row(t,k)] over local k ascending,
+// float32 accumulation, one rounding.  One wave per token.
+// ---------------------------------------------------------------------------
+template <typename T, int MAXC>
+__global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ yp,
+                                                      const float* __restrict__ gates,
+                                                      const int32_t* __restrict__ row_of_pair,
+                                                      uint4* __restrict__ out, int T_, int K,
+                                                      int nch) {
+  constexpr int CN = Chunk<T>::N;
+  const int t = (int)(((long)blockIdx.x * 256 + threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T_) return;
+  for (int c0 = 0; c0 < nch; c0 += 64 * MAXC) {
+    float acc[MAXC][CN];
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i)
+#pragma unroll
+      for (int q = 0; q < CN; ++q) acc[i][q] = 0.f;
+    for (int k = 0; k < K; ++k) {
+      const int r = row_of_pair[(size_t)t * K + k];
+      if (r < 0 || r >= T_ * K) continue;
+      const float g = gates[(size_t)t * K + k];
+      const uint4* src = yp + (size_t)r * nch;
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) {
+        const int c = c0 + lane + 64 * i;
+        if (c < nch) {
+          float f[CN];
+          Chunk<T>::unpack(src[c], f);
+#pragma unroll
+          for (int q = 0; q < CN; ++q) acc[i][q] = fmaf(g, f[q], acc[i][q]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int c = c0 + lane + 64 * i;
+      if (c < nch) out[(size_t)t * nch + c] = Chunk<T>::pack(acc[i]);
+    }
+  }
+}
+
+int launch_combine(const moe_shape* s, const void* yp, const float* gates,
+                   const int32_t* row_of_pair, void* out, hipStream_t st) {
+  if (s->T == 0) return MOE_OK;
+  const unsigned grid = (unsigned)cdiv(s->T, 4);
+  if (s->dtype == MOE_BF16)
+    MOE_LAUNCH("combine", st,
+               combine_kernel<uint16_t, 4><<<grid, 256, 0, st>>>((const uint4*)yp, gates, row_of_pair,
+                                                      (uint4*)out, (int)s->T, (int)s->K,
+                                                      row_chunks(s)));
+  else
+    MOE_LAUNCH("combine", st,
+               combine_kernel<float, 4><<<grid, 256, 0, st>>>((const uint4*)yp, gates, row_of_pair,
+                                                   (uint4*)out, (int)s->T, (int)s->K,
+                                                   row_chunks(s)));
+  return check_launch("combine");
+}
+
+// ---------------------------------------------------------------------------
+// combine backward: dyp[r] = g * dout[t]; dgates[t,k] = <dout[t], yp[r]>.
+// One wave per token; dout row held in registers.
+// ---------------------------------------------------------------------------
+template <typename T, int MAXC>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restrict__ dout,
+                                                          const uint4* __restrict__ yp,
+                                                          const float* __restrict__ gates,
+                                                          const int32_t* __restrict__ row_of_pair,
+                                                          uint4* __restrict__ dyp,
+                                                          float* __restrict__ dgates, int T_,
+                                                          int K, int nch) {
+  constexpr int CN = Chunk<T>::N;
+  const int t = (int)(((long)blockIdx.x * 256 + threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T_) return;
+  // nch <= 64 * MAXC is guaranteed by the launcher (whole row in registers)
+  float dv[MAXC][CN];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      Chunk<T>::unpack(dout[(size_t)t * nch + c], dv[i]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < CN; ++q) dv[i][q] = 0.f;
+    }
+  }
+  for (int k = 0; k < K; ++k) {
+    const int r = row_of_pair[(size_t)t * K + k];
+    if (r < 0 || r >= T_ * K) {
+      if (lane == 0) dgates[(size_t)t * K + k] = 0.f;
+      continue;
+    }
+    const float g = gates[(size_t)t * K + k];
+    float dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nch) {
+        float y[CN], o[CN];
+        Chunk<T>::unpack(yp[(size_t)r * nch + c], y);
+#pragma unroll
+        for (int q = 0; q < CN; ++q) {
+          dot = fmaf(dv[i][q], y[q], dot);
+          o[q] = g * dv[i][q];
+        }
+        dyp[(size_t)r * nch + c] = Chunk<T>::pack(o);
+      }
+    }
+    dot = wave_sum(dot);
+    if (lane == 0) dgates[(size_t)t * K + k] = dot;
+  }
+}
+
+int launch_combine_bwd(const moe_shape* s, const void* dout, const void* yp, const float* gates,
+                       const int32_t* row_of_pair, void* dyp, float* dgates, hipStream_t st) {
+  if (s->T == 0) return MOE_OK;
+  const unsigned grid = (unsigned)cdiv(s->T, 4);
+  const int nch = row_chunks(s);
+  // d <= 16384: bf16 rows <= 2048 chunks, f32 rows <= 4096 chunks
+  if (s->dtype == MOE_BF16) {
+    if (nch <= 256)
+      MOE_LAUNCH("combine_bwd", st,
+                 combine_bwd_kernel<uint16_t, 4><<<grid, 256, 0, st>>>(
+          (const uint4*)dout, (const uint4*)yp, gates, row_of_pair, (uint4*)dyp, dgates,
+          (int)s->T, (int)s->K, nch));
+    else
+      MOE_LAUNCH("combine_bwd", st,
+                 combine_bwd_kernel<uint16_t, 32><<<grid, 256, 0, st>>>(
+          (const uint4*)dout, (const uint4*)yp, gates, row_of_pair, (uint4*)dyp, dgates,
+          (int)s->T, (int)s->K, nch));
+  } else {
+    if (nch <= 256)
+      MOE_LAUNCH("combine_bwd", st,
+                 combine_bwd_kernel<float, 4><<<grid, 256, 0, st>>>(
+          (const uint4*)dout, (const uint4*)yp, gates, row_of_pair, (uint4*)dyp, dgates,
+          (int)s->T, (int)s->K, nch));
+    else
+      MOE_LAUNCH("combine_bwd", st,
+                 combine_bwd_kernel<float, 64><<<grid, 256, 0, st>>>(
+          (const uint4*)dout, (const uint4*)yp, gates, row_of_pair, (uint4*)dyp, dgates,
+          (int)s->T, (int)s->K, nch));
+  }
+  return check_launch("combine bwd");
+}
+
+// ---------------------------------------------------------------------------
+// dispatch backward: dx[t] = [dx[t]] + sum_k dxp[row(t,k)]
+//                            [+ sum_k dlogits[t, e_k] * W_rT[e_k]]   (e_k = idx[t,k])
+// float32 accumulation, one rounding.  One wave per token.
+// ---------------------------------------------------------------------------
+template <typename T, int MAXC>
+__global__ __launch_bounds__(256) void dispatch_bwd_kernel(
+    const uint4* __restrict__ dxp, const int32_t* __restrict__ row_of_pair,
+    const int32_t* __restrict__ idx, const float* __restrict__ dlogits,
+    const uint4* __restrict__ W_rT, uint4* __restrict__ dx, int T_, int K, int E, int nch,
+    int accumulate) {
+  constexpr int CN = Chunk<T>::N;
+  const int t = (int)(((long)blockIdx.x * 256 + threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T_) return;
+  for (int c0 = 0; c0 < nch; c0 += 64 * MAXC) {
+    float acc[MAXC][CN];
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int c = c0 + lane + 64 * i;
+      if (accumulate && c < nch) {
+        Chunk<T>::unpack(dx[(size_t)t * nch + c], acc[i]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < CN; ++q) acc[i][q] = 0.f;
+      }
+    }
+    for (int k = 0; k < K; ++k) {
+      const int r = row_of_pair[(size_t)t * K + k];
+      if (r < 0 || r >= T_ * K) continue;
+      const uint4* src = dxp + (size_t)r * nch;
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) {
+        const int c = c0 + lane + 64 * i;
+        if (c < nch) {
+          float f[CN];
+          Chunk<T>::unpack(src[c], f);
+#pragma unroll
+          for (int q = 0; q < CN; ++q) acc[i][q] += f[q];
+        }
+      }
+    }
+    if (dlogits) {
+      for (int k = 0; k < K; ++k) {
+        const int e = idx[(size_t)t * K + k];
+        if (e < 0 || e >= E) continue;
+        const float gl = dlogits[(size_t)t * E + e];
+        const uint4* wr = W_rT + (size_t)e * nch;
+#pragma unroll
+        for (int i = 0; i < MAXC; ++i) {
+          const int c = c0 + lane + 64 * i;
+          if (c < nch) {
+            float f[CN];
+            Chunk<T>::unpack(wr[c], f);
+#pragma unroll
+            for (int q = 0; q < CN; ++q) acc[i][q] = fmaf(gl, f[q], acc[i][q]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int c = c0 + lane + 64 * i;
+      if (c < nch) dx[(size_t)t * nch + c] = Chunk<T>::pack(acc[i]);
+    }
+  }
+}
+
+int launch_dispatch_bwd(const moe_shape* s, const void* dxp, const int32_t* row_of_pair,
+                        const int32_t* idx, const float* dlogits, const void* W_rT, void* dx,
+                        bool accumulate, hipStream_t st) {
+  if (s->T == 0) return MOE_OK;
+  const unsigned grid = (unsigned)cdiv(s->T, 4);
+  if (s->dtype == MOE_BF16)
+    MOE_LAUNCH("dispatch_bwd", st,
+               dispatch_bwd_kernel<uint16_t, 4><<<grid, 256, 0, st>>>(
+        (const uint4*)dxp, row_of_pair, idx, dlogits, (const uint4*)W_rT, (uint4*)dx, (int)s->T,
+        (int)s->K, (int)s->E, row_chunks(s), accumulate ? 1 : 0));
+  else
+    MOE_LAUNCH("dispatch_bwd", st,
+               dispatch_bwd_kernel<float, 4><<<grid, 256, 0, st>>>(
+        (const uint4*)dxp, row_of_pair, idx, dlogits, (const uint4*)W_rT, (uint4*)dx, (int)s->T,
+        (int)s->K, (int)s->E, row_chunks(s), accumulate ? 1 : 0));
+  return check_launch("dispatch bwd");
+}
+
+}  // namespace moe

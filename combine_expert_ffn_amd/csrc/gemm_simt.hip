@@ -1,0 +1,189 @@
+// Expert GEMMs in float32: one thread per output element, float32
+// accumulation in k order.  This is the float32 mode of the library (small
+// layers, exact-to-1e-5 checks); bf16 layers use the matrix-core kernels in
+// gemm_mfma.hip.  Same formulas as there: SwiGLU expert FFN forward, its
+// activation gradient (D) and weight gradient (W) (1F1B note page 2, "MoE 1F1B
+// overlap").
+#include "moe_internal.h"
+
+namespace moe {
+
+// Local expert owning permuted row `row` (offsets non-decreasing, row < offsets[E_l]).
+__device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offsets, int E_l,
+                                             int row) {
+  int lo = 0, hi = E_l;  // offsets[lo] <= row < offsets[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (offsets[mid] <= row) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256) void f32_gate_up_kernel(const float* __restrict__ xp,
+                                                          const int32_t* __restrict__ offsets,
+                                                          const float* __restrict__ W_gu,
+                                                          float* __restrict__ h,
+                                                          float* __restrict__ a, long cap,
+                                                          int E_l, int d, int F) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= cap * F) return;
+  const int row = (int)(i / F), j = (int)(i % F);
+  if (row >= offsets[E_l]) return;
+  const int e = expert_of_row(offsets, E_l, row);
+  const float* xr = xp + (size_t)row * d;
+  const float* wg = W_gu + ((size_t)e * 2 * F + j) * d;
+  const float* wu = W_gu + ((size_t)e * 2 * F + F + j) * d;
+  float g = 0.f, u = 0.f;
+  for (int c = 0; c < d; ++c) {
+    g = fmaf(xr[c], wg[c], g);
+    u = fmaf(xr[c], wu[c], u);
+  }
+  h[(size_t)row * 2 * F + j] = g;
+  h[(size_t)row * 2 * F + F + j] = u;
+  a[(size_t)row * F + j] = silu_f(g) * u;
+}
+
+__global__ __launch_bounds__(256) void f32_down_kernel(const float* __restrict__ a,
+                                                       const int32_t* __restrict__ offsets,
+                                                       const float* __restrict__ W_down,
+                                                       float* __restrict__ yp, long cap, int E_l,
+                                                       int d, int F) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= cap * d) return;
+  const int row = (int)(i / d), c = (int)(i % d);
+  if (row >= offsets[E_l]) return;
+  const int e = expert_of_row(offsets, E_l, row);
+  const float* ar = a + (size_t)row * F;
+  const float* w = W_down + ((size_t)e * d + c) * F;
+  float y = 0.f;
+  for (int f = 0; f < F; ++f) y = fmaf(ar[f], w[f], y);
+  yp[(size_t)row * d + c] = y;
+}
+
+__global__ __launch_bounds__(256) void f32_dgrad_act_kernel(
+    const float* __restrict__ dyp, const float* __restrict__ hbuf,
+    const int32_t* __restrict__ offsets, const float* __restrict__ W_down,
+    float* __restrict__ dh, long cap, int E_l, int d, int F) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= cap * F) return;
+  const int row = (int)(i / F), j = (int)(i % F);
+  if (row >= offsets[E_l]) return;
+  const int e = expert_of_row(offsets, E_l, row);
+  const float* dy = dyp + (size_t)row * d;
+  const float* w = W_down + (size_t)e * d * F + j;
+  float da = 0.f;
+  for (int c = 0; c < d; ++c) da = fmaf(dy[c], w[(size_t)c * F], da);
+  const float g = hbuf[(size_t)row * 2 * F + j];
+  const float u = hbuf[(size_t)row * 2 * F + F + j];
+  const float s = sigmoid_f(g);
+  dh[(size_t)row * 2 * F + j] = da * u * s * (1.0f + g * (1.0f - s));
+  dh[(size_t)row * 2 * F + F + j] = da * g * s;
+}
+
+__global__ __launch_bounds__(256) void f32_dgrad_in_kernel(const float* __restrict__ dh,
+                                                           const int32_t* __restrict__ offsets,
+                                                           const float* __restrict__ W_gu,
+                                                           float* __restrict__ dxp, long cap,
+                                                           int E_l, int d, int F) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= cap * d) return;
+  const int row = (int)(i / d), c = (int)(i % d);
+  if (row >= offsets[E_l]) return;
+  const int e = expert_of_row(offsets, E_l, row);
+  const float* g = dh + (size_t)row * 2 * F;
+  const float* w = W_gu + (size_t)e * 2 * F * d + c;
+  float acc = 0.f;
+  for (int m = 0; m < 2 * F; ++m) acc = fmaf(g[m], w[(size_t)m * d], acc);
+  dxp[(size_t)row * d + c] = acc;
+}
+
+// dW_down[e][i][f] = sum_r dyp[r][i] a[r][f]; dW_gu[e][m][c] = sum_r dh[r][m] xp[r][c]
+__global__ __launch_bounds__(256) void f32_wgrad_kernel(
+    const float* __restrict__ xp, const float* __restrict__ a, const float* __restrict__ dh,
+    const float* __restrict__ dyp, const int32_t* __restrict__ offsets,
+    float* __restrict__ dW_gu, float* __restrict__ dW_down, int E_l, int d, int F,
+    int accumulate) {
+  const long per_e = (long)d * F + 2L * F * d;
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= per_e * E_l) return;
+  const int e = (int)(i / per_e);
+  long q = i % per_e;
+  const int r0 = offsets[e], r1 = offsets[e + 1];
+  float acc = 0.f;
+  float* o;
+  if (q < (long)d * F) {
+    const int ii = (int)(q / F), f = (int)(q % F);
+    for (int r = r0; r < r1; ++r) acc = fmaf(dyp[(size_t)r * d + ii], a[(size_t)r * F + f], acc);
+    o = dW_down + (size_t)e * d * F + q;
+  } else {
+    q -= (long)d * F;
+    const int m = (int)(q / d), c = (int)(q % d);
+    for (int r = r0; r < r1; ++r)
+      acc = fmaf(dh[(size_t)r * 2 * F + m], xp[(size_t)r * d + c], acc);
+    o = dW_gu + (size_t)e * 2 * F * d + q;
+  }
+  *o = accumulate ? *o + acc : acc;
+}
+
+int launch_ffn_fwd_bf16(const moe_shape* s, const void* xp, const int32_t* offsets,
+                        const int32_t* tile_offsets, const void* W_gu, const void* W_down,
+                        void* h, void* a, void* yp, hipStream_t st);
+int launch_ffn_dgrad_bf16(const moe_shape* s, const void* dyp, const void* h,
+                          const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
+                          const void* W_down, void* dh, void* dxp, hipStream_t st);
+int launch_ffn_wgrad_bf16(const moe_shape* s, const void* xp, const void* a, const void* dh,
+                          const void* dyp, const int32_t* offsets, float* dW_gu, float* dW_down,
+                          bool accumulate, hipStream_t st);
+
+int launch_ffn_fwd(const moe_shape* s, const void* xp, const int32_t* offsets,
+                   const int32_t* tile_offsets, const void* W_gu, const void* W_down, void* h,
+                   void* a, void* yp, hipStream_t st) {
+  if (s->T == 0) return MOE_OK;
+  if (s->dtype == MOE_BF16)
+    return launch_ffn_fwd_bf16(s, xp, offsets, tile_offsets, W_gu, W_down, h, a, yp, st);
+  const long cap = s->T * s->K;
+  const int d = (int)s->d, F = (int)s->F, E_l = (int)s->E_l;
+  MOE_LAUNCH("f32_gate_up", st,
+             f32_gate_up_kernel<<<(unsigned)cdiv(cap * F, 256), 256, 0, st>>>(
+      (const float*)xp, offsets, (const float*)W_gu, (float*)h, (float*)a, cap, E_l, d, F));
+  if (int rc = check_launch("f32 expert GEMM1")) return rc;
+  MOE_LAUNCH("f32_down", st,
+             f32_down_kernel<<<(unsigned)cdiv(cap * d, 256), 256, 0, st>>>(
+      (const float*)a, offsets, (const float*)W_down, (float*)yp, cap, E_l, d, F));
+  return check_launch("f32 expert GEMM2");
+}
+
+int launch_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h, const int32_t* offsets,
+                     const int32_t* tile_offsets, const void* W_gu, const void* W_down, void* dh,
+                     void* dxp, hipStream_t st) {
+  if (s->T == 0) return MOE_OK;
+  if (s->dtype == MOE_BF16)
+    return launch_ffn_dgrad_bf16(s, dyp, h, offsets, tile_offsets, W_gu, W_down, dh, dxp, st);
+  const long cap = s->T * s->K;
+  const int d = (int)s->d, F = (int)s->F, E_l = (int)s->E_l;
+  MOE_LAUNCH("f32_dgrad_act", st,
+             f32_dgrad_act_kernel<<<(unsigned)cdiv(cap * F, 256), 256, 0, st>>>(
+      (const float*)dyp, (const float*)h, offsets, (const float*)W_down, (float*)dh, cap, E_l, d,
+      F));
+  if (int rc = check_launch("f32 dgrad (activation)")) return rc;
+  MOE_LAUNCH("f32_dgrad_in", st,
+             f32_dgrad_in_kernel<<<(unsigned)cdiv(cap * d, 256), 256, 0, st>>>(
+      (const float*)dh, offsets, (const float*)W_gu, (float*)dxp, cap, E_l, d, F));
+  return check_launch("f32 dgrad (input)");
+}
+
+int launch_ffn_wgrad(const moe_shape* s, const void* xp, const void* a, const void* dh,
+                     const void* dyp, const int32_t* offsets, float* dW_gu, float* dW_down,
+                     bool accumulate, hipStream_t st) {
+  if (s->dtype == MOE_BF16)
+    return launch_ffn_wgrad_bf16(s, xp, a, dh, dyp, offsets, dW_gu, dW_down, accumulate, st);
+  const long n = s->E_l * (s->d * s->F + 2 * s->F * s->d);
+  MOE_LAUNCH("f32_wgrad", st,
+             f32_wgrad_kernel<<<(unsigned)cdiv(n, 256), 256, 0, st>>>(
+      (const float*)xp, (const float*)a, (const float*)dh, (const float*)dyp, offsets, dW_gu,
+      dW_down, (int)s->E_l, (int)s->d, (int)s->F, accumulate ? 1 : 0));
+  return check_launch("f32 wgrad");
+}
+
+}  // namespace moe

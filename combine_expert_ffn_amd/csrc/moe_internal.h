@@ -1,0 +1,171 @@
+// Internal declarations shared by the libmoe HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// element types: bf16 is kept as raw 16-bit patterns
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf2f(uint16_t v) {
+  return __uint_as_float(((uint32_t)v) << 16);
+}
+// float32 -> bfloat16, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+template <typename T> struct Elt;
+template <> struct Elt<float> {
+  static __device__ __forceinline__ float ld(const float* p) { return *p; }
+  static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
+};
+template <> struct Elt<uint16_t> {
+  static __device__ __forceinline__ float ld(const uint16_t* p) { return bf2f(*p); }
+  static __device__ __forceinline__ void st(uint16_t* p, float v) { *p = f2bf(v); }
+};
+
+// Unpack a 16-byte chunk into floats (8 bf16 or 4 f32).
+template <typename T> struct Chunk;
+template <> struct Chunk<uint16_t> {
+  static constexpr int N = 8;
+  static __device__ __forceinline__ void unpack(const uint4& v, float* f) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ uint4 pack(const float* f) {
+    uint4 r;
+    r.x = pack_bf2(f[0], f[1]);
+    r.y = pack_bf2(f[2], f[3]);
+    r.z = pack_bf2(f[4], f[5]);
+    r.w = pack_bf2(f[6], f[7]);
+    return r;
+  }
+};
+template <> struct Chunk<float> {
+  static constexpr int N = 4;
+  static __device__ __forceinline__ void unpack(const uint4& v, float* f) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+  static __device__ __forceinline__ uint4 pack(const float* f) {
+    uint4 r;
+    r.x = __float_as_uint(f[0]);
+    r.y = __float_as_uint(f[1]);
+    r.z = __float_as_uint(f[2]);
+    r.w = __float_as_uint(f[3]);
+    return r;
+  }
+};
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
+__device__ __forceinline__ float sigmoid_f(float g) { return 1.0f / (1.0f + expf(-g)); }
+
+// Wave-wide float sum (wave64).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// host-side helpers (defined in abi.cpp)
+// ---------------------------------------------------------------------------
+int set_error(int code, const char* fmt, ...);
+int check_launch(const char* what);
+
+// Brackets one kernel launch with timing events while moe_timing is enabled.
+// `name` must outlive the process (a string literal).
+struct KernelTimer {
+  int slot = -1;
+  hipStream_t stream;
+  KernelTimer(const char* name, hipStream_t st);
+  void stop();
+  ~KernelTimer() { stop(); }
+};
+#define MOE_LAUNCH(name, st, ...)          \
+  do {                                     \
+    ::moe::KernelTimer kt_(name, st);      \
+    __VA_ARGS__;                           \
+    kt_.stop();                            \
+  } while (0)
+
+// Rows per M-tile of the bf16 grouped GEMMs (tile_offsets are in these units).
+constexpr int kTileM = 256;
+// Pairs per block of the dispatch-plan kernels.
+constexpr int kPlanChunk = 2048;
+// Tokens per partial of the router weight-gradient reduction.
+constexpr int kRouterChunk = 1024;
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Workspace layout pieces (bytes).
+inline size_t ws_plan_bytes(const moe_shape* s) {
+  int64_t nb = cdiv(s->T * s->K, kPlanChunk);
+  return align_up((size_t)(2 * s->E_l * nb) * sizeof(int32_t), 256);
+}
+inline size_t ws_wrt_bytes(const moe_shape* s) {
+  size_t es = s->dtype == MOE_BF16 ? 2 : 4;
+  return align_up((size_t)(s->E * s->d) * es, 256);
+}
+inline size_t ws_router_partial_bytes(const moe_shape* s) {
+  int64_t nc = cdiv(s->T, kRouterChunk);
+  return align_up((size_t)(nc * s->d * s->E) * sizeof(float), 256);
+}
+
+// ---------------------------------------------------------------------------
+// launchers (each returns MOE_OK or MOE_ERR_HIP)
+// ---------------------------------------------------------------------------
+// routing
+int launch_transpose_wr(const moe_shape* s, const void* W_r, void* W_rT, hipStream_t st);
+int launch_router_logits(const moe_shape* s, const void* x, const void* W_r,
+                         const void* W_rT, const float* bias, float* logits, hipStream_t st);
+int launch_topk(const moe_shape* s, const float* logits, int32_t* idx, float* gates,
+                hipStream_t st);
+int launch_force_balance(const moe_shape* s, int32_t* idx, hipStream_t st);
+int launch_route_bwd(const moe_shape* s, const float* dgates, const float* gates,
+                     const int32_t* idx, const void* x, float* dlogits, float* dW_r,
+                     bool accumulate, void* ws, hipStream_t st);
+// dispatch / combine
+int launch_plan(const moe_shape* s, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                int32_t* row_of_pair, int32_t* pair_of_row, int32_t* tile_offsets, void* ws,
+                hipStream_t st);
+int launch_permute(const moe_shape* s, const void* x, const int32_t* row_of_pair, void* xp,
+                   hipStream_t st);
+int launch_combine(const moe_shape* s, const void* yp, const float* gates,
+                   const int32_t* row_of_pair, void* out, hipStream_t st);
+int launch_combine_bwd(const moe_shape* s, const void* dout, const void* yp, const float* gates,
+                       const int32_t* row_of_pair, void* dyp, float* dgates, hipStream_t st);
+int launch_dispatch_bwd(const moe_shape* s, const void* dxp, const int32_t* row_of_pair,
+                        const int32_t* idx, const float* dlogits, const void* W_rT, void* dx,
+                        bool accumulate, hipStream_t st);
+// expert GEMMs
+int launch_ffn_fwd(const moe_shape* s, const void* xp, const int32_t* offsets,
+                   const int32_t* tile_offsets, const void* W_gu, const void* W_down, void* h,
+                   void* a, void* yp, hipStream_t st);
+int launch_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h, const int32_t* offsets,
+                     const int32_t* tile_offsets, const void* W_gu, const void* W_down, void* dh,
+                     void* dxp, hipStream_t st);
+int launch_ffn_wgrad(const moe_shape* s, const void* xp, const void* a, const void* dh,
+                     const void* dyp, const int32_t* offsets, float* dW_gu, float* dW_down,
+                     bool accumulate, hipStream_t st);
+
+}  // namespace moe

@@ -90,11 +90,12 @@ def _to_dtype(a: np.ndarray, dtype: str) -> np.ndarray:
     return torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
 
 
-def make_inputs(w: Workload, seed: int = 0) -> dict:
+def make_inputs(w: Workload, seed: int = 0, microbatches: int | None = None) -> dict:
     """All inputs of one workload as float32 numpy arrays (values representable
     in ``w.dtype``).  Keys: x, W_r (None for forced balance), bias (or None),
     W_gu [E_l,2F,d], W_down [E_l,d,F], dout, gates (forced balance only), and
-    x_b, dout_b for a second micro-batch."""
+    x_b, dout_b (, gates_b) for a second micro-batch."""
+    microbatches = w.microbatches if microbatches is None else microbatches
     rng = np.random.Generator(np.random.PCG64(seed))
     out = {}
     out["x"] = _to_dtype(_normal(rng, (w.T, w.d), 1.0), w.dtype)
@@ -116,9 +117,12 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
         out["gates"] = (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
     else:
         out["gates"] = None
-    if w.microbatches > 1:
+    if microbatches > 1:
         out["x_b"] = _to_dtype(_normal(rng, (w.T, w.d), 1.0), w.dtype)
         out["dout_b"] = _to_dtype(_normal(rng, (w.T, w.d), 1.0), w.dtype)
+        if w.route == "force_balance":
+            e = rng.standard_exponential((w.T, w.K))
+            out["gates_b"] = (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
     return out
 
 
@@ -132,7 +136,7 @@ def to_device(arrays: dict, dtype: str, device="cuda"):
     for k, v in arrays.items():
         if v is None:
             res[k] = None
-        elif k in ("gates", "bias"):
+        elif k in ("gates", "gates_b", "bias"):
             res[k] = torch.from_numpy(np.ascontiguousarray(v)).to(device)
         else:
             res[k] = torch.from_numpy(np.ascontiguousarray(v)).to(device=device, dtype=tdt)

@@ -1,0 +1,312 @@
+/*
+ * moe.h - C ABI of libmoe: one GPU's share of a Mixture-of-Experts
+ * expert-parallel layer on AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the one the expert-parallel overlap pages describe: tokens are
+ * dispatched to their experts, each expert runs its FFN, and the results are
+ * combined back per token (skill card page 1, "What it is"); the backward pass
+ * runs combine -> expert MLP -> dispatch, with the MLP's activation gradient (D)
+ * computed before its weight gradient (W) so the latter can be deferred (1F1B
+ * note page 2, "MoE 1F1B overlap" and the backward chain under "how the 8 ops
+ * are split"; skill card page 1, delay_wgrad_compute).  Two micro-batches run
+ * on two streams so that one's dispatch/combine overlaps the other's expert
+ * GEMMs (page 2, "MoE 1F1B overlap": two streams + two micro-batches).
+ * The pages leave the routing function and FFN type open; this library uses
+ * top-K softmax routing (or forced balance, page 1 "HybridEP benchmark":
+ * "Routing: force balance") and SwiGLU experts.
+ *
+ * Conventions (all entry points):
+ *  - Pointers are DEVICE pointers unless stated otherwise; the caller owns
+ *    every buffer.  The library allocates no device memory: scratch space is
+ *    the caller's `ws` of at least moe_workspace_bytes() bytes.
+ *  - Every call validates its arguments on the host before any launch.  On a
+ *    validation failure it returns a negative MOE_ERR_* code, launches
+ *    nothing and writes nothing; moe_last_error() then describes the problem.
+ *  - Every call is asynchronous on the given stream and never synchronises the
+ *    device.  Buffers must stay alive until that stream's work completes (the
+ *    free-input hazard the 1F1B note reports under "TP=1 bug", page 2).
+ *  - Activations ("data" tensors) are in shape->dtype (MOE_BF16 or MOE_F32).
+ *    Logits, gates, gate gradients, logit gradients and weight gradients are
+ *    always float32; indices and maps are int32.  Layouts are row-major.
+ *  - Results are deterministic: the same inputs give bit-identical outputs,
+ *    whatever the stream schedule.
+ *  - HIP launch failures return MOE_ERR_HIP.  There is no silent fallback.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define MOE_OK               0
+#define MOE_ERR_NULL        -1   /* a required pointer is NULL                 */
+#define MOE_ERR_SHAPE       -2   /* a size is outside the supported range      */
+#define MOE_ERR_DTYPE       -3   /* dtype is not MOE_F32 / MOE_BF16            */
+#define MOE_ERR_WORKSPACE   -4   /* workspace smaller than required            */
+#define MOE_ERR_HIP         -5   /* a HIP runtime call or launch failed        */
+#define MOE_ERR_UNSUPPORTED -6   /* mode / flag combination not supported      */
+#define MOE_ERR_ARG         -7   /* unknown mode or flag value                 */
+
+/* ---- data types ---------------------------------------------------------- */
+#define MOE_F32   0
+#define MOE_BF16  1
+
+/* ---- routing modes ------------------------------------------------------- */
+/* Top-K over router logits = x . W_r (+ bias); gates = softmax over the K
+ * selected logits (= softmax over all E renormalised over the selected). */
+#define MOE_ROUTE_TOPK              0
+/* Top-K over caller-given logits (same selection and gates). */
+#define MOE_ROUTE_TOPK_FROM_LOGITS  1
+/* Forced balance: slot k of token t goes to expert (t*K + k) mod E; the gates
+ * are caller-given inputs and are not touched. */
+#define MOE_ROUTE_FORCE_BALANCE     2
+
+/* ---- accumulate bits ------------------------------------------------------ */
+#define MOE_ACCUM_DX  1   /* moe_dispatch_bwd: add into dx instead of overwrite */
+#define MOE_ACCUM_DW  2   /* moe_ffn_wgrad / moe_route_bwd: add into weight grads */
+
+/* ---- moe_overlap_step flags ------------------------------------------------ */
+#define MOE_STEP_SERIALIZE   1  /* everything on s_compute, forward then backward */
+#define MOE_STEP_EAGER_WGRAD 2  /* wgrad right after dgrad (not after the other
+                                   micro-batch's forward GEMMs)                   */
+
+/*
+ * Layer shape.  T tokens of hidden size d; E experts routed over, of which the
+ * local window [e_lo, e_lo + E_l) lives on this GPU; K experts per token; F is
+ * the expert FFN width.  Supported: T >= 0, T*K < 2^31, 1 <= K <= min(E, 16),
+ * 1 <= E <= 512, 1 <= E_l <= 256, 0 <= e_lo, e_lo + E_l <= E,
+ * d and F multiples of 64 in [64, 16384].  reserved must be 0.
+ * N (rows dispatched to the local window) is at most cap = T*K; it is only
+ * known on the device (offsets[E_l]), so row buffers are sized to cap.
+ */
+typedef struct moe_shape {
+  int64_t T, d, F, E, e_lo, E_l, K;
+  int32_t dtype;
+  int32_t reserved;
+} moe_shape;
+
+/* Bytes of workspace any single call below needs for this shape. */
+size_t moe_workspace_bytes(const moe_shape* s);
+/* Bytes of workspace moe_overlap_step needs (two micro-batches in flight). */
+size_t moe_step_workspace_bytes(const moe_shape* s);
+/* Rows per M-tile of the grouped GEMMs; tile_offsets are counted in these. */
+int moe_tile_m(void);
+/* Thread-local description of the last error (empty string if none). */
+const char* moe_last_error(void);
+/* Library version (major*10000 + minor*100 + patch). */
+int moe_version(void);
+
+/*
+ * moe_route - routing (router scores, top-K selection, gates).
+ *   x      [T,d] dtype        (MOE_ROUTE_TOPK only)
+ *   W_r    [d,E] dtype        (MOE_ROUTE_TOPK only)
+ *   bias   [E] f32 or NULL    (MOE_ROUTE_TOPK only; added to the logits, so it
+ *                              affects selection and gates)
+ *   logits [T,E] f32          written (TOPK), read (TOPK_FROM_LOGITS), unused
+ *                              (FORCE_BALANCE, may be NULL)
+ *   idx    [T,K] i32 written  selected experts, descending logit, ties -> lower
+ *                              expert index
+ *   gates  [T,K] f32          written (TOPK modes); caller input (FORCE_BALANCE,
+ *                              may be NULL)
+ *   ws/ws_bytes               workspace (TOPK)
+ * Logits must be finite.
+ */
+int moe_route(const moe_shape* s, int mode, const void* x, const void* W_r,
+              const float* bias, float* logits, int32_t* idx, float* gates,
+              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_dispatch - dispatch plan and permute (the local half of the token
+ * all-to-all of page 1, "What it is").  A stable counting sort of the
+ * (token, slot) pairs whose expert is local, in (t, k) order:
+ *   idx          [T,K] i32 in   from moe_route
+ *   counts       [E_l] i32 out  rows per local expert
+ *   offsets      [E_l+1] i32 out exclusive prefix sum; offsets[E_l] = N
+ *   row_of_pair  [T*K] i32 out  row of pair t*K+k, or -1 if its expert is not local
+ *   pair_of_row  [T*K] i32 out  inverse map on rows [0,N); -1 on rows [N, T*K)
+ *   tile_offsets [E_l+1] i32 out exclusive prefix sum of ceil(counts/moe_tile_m())
+ *   x            [T,d] dtype in
+ *   xp           [T*K,d] dtype out  xp[row_of_pair[t*K+k]] = x[t] (exact copy);
+ *                                   rows >= N untouched
+ */
+int moe_dispatch(const moe_shape* s, const void* x, const int32_t* idx,
+                 int32_t* counts, int32_t* offsets, int32_t* row_of_pair,
+                 int32_t* pair_of_row, int32_t* tile_offsets, void* xp,
+                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_expert_ffn_fwd - per local expert j (rows [offsets[j], offsets[j+1])):
+ *   [g,u] = xp . W_gu[j]^T,  a = silu(g) * u,  y_p = a . W_down[j]^T
+ *   xp [T*K,d], W_gu [E_l,2F,d] (rows [0,F) gate, [F,2F) up), W_down [E_l,d,F]
+ *   h  [T*K,2F] out (g and u, saved for the backward), a [T*K,F] out,
+ *   yp [T*K,d] out.  All dtype.  a is computed from g, u before rounding.
+ *   offsets, tile_offsets from moe_dispatch.  Rows >= N are untouched.
+ */
+int moe_expert_ffn_fwd(const moe_shape* s, const void* xp, const int32_t* offsets,
+                       const int32_t* tile_offsets, const void* W_gu,
+                       const void* W_down, void* h, void* a, void* yp,
+                       hipStream_t stream);
+
+/*
+ * moe_combine - unpermute and gate-weighted sum (page 1, "What it is":
+ * combine).  out[t] = sum over local slots k, ascending, of
+ * gates[t,k] * yp[row_of_pair[t*K+k]], accumulated in float32; a token with no
+ * local slot gets 0.   yp [T*K,d], gates [T,K] f32, out [T,d].
+ */
+int moe_combine(const moe_shape* s, const void* yp, const float* gates,
+                const int32_t* row_of_pair, void* out, hipStream_t stream);
+
+/*
+ * moe_combine_bwd - backward of combine (page 2, backward chain: combine's
+ * backward first).  For each local pair (t,k) with row r:
+ *   dyp[r] = gates[t,k] * dout[t];  dgates[t,k] = <dout[t], yp[r]> (f32)
+ * dgates is 0 for non-local pairs.  dout [T,d], dyp [T*K,d] (rows >= N untouched).
+ */
+int moe_combine_bwd(const moe_shape* s, const void* dout, const void* yp,
+                    const float* gates, const int32_t* row_of_pair, void* dyp,
+                    float* dgates, hipStream_t stream);
+
+/*
+ * moe_ffn_dgrad - the D of the W/D split (page 2, "MoE 1F1B overlap"): the
+ * expert FFN's activation gradient, per local expert j:
+ *   da = dyp . W_down[j];  with g, u from h and s = sigmoid(g):
+ *   dg = da*u*s*(1 + g*(1-s)),  du = da*g*s;  dh = [dg, du];  dxp = dh . W_gu[j]
+ *   dh [T*K,2F] out, dxp [T*K,d] out (dtype).
+ */
+int moe_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h,
+                  const int32_t* offsets, const int32_t* tile_offsets,
+                  const void* W_gu, const void* W_down, void* dh, void* dxp,
+                  hipStream_t stream);
+
+/*
+ * moe_ffn_wgrad - the W of the W/D split, deferrable (page 1,
+ * delay_wgrad_compute).  Reduced over each expert's rows:
+ *   dW_down[j] = sum_r dyp[r] (outer) a[r]   [E_l,d,F] f32
+ *   dW_gu[j]   = sum_r dh[r]  (outer) xp[r]  [E_l,2F,d] f32
+ * accumulate & MOE_ACCUM_DW: add to the existing values (gradient
+ * accumulation); otherwise overwrite (an expert with no rows gets 0).
+ */
+int moe_ffn_wgrad(const moe_shape* s, const void* xp, const void* a,
+                  const void* dh, const void* dyp, const int32_t* offsets,
+                  float* dW_gu, float* dW_down, int accumulate, hipStream_t stream);
+
+/*
+ * moe_route_bwd - backward of the top-K softmax gates and of the router
+ * product (TOPK modes; returns MOE_ERR_UNSUPPORTED for FORCE_BALANCE, whose
+ * gates are inputs with gradient dgates).
+ *   dlogits[t, idx[t,j]] = g_j * (dg_j - sum_k g_k dg_k); other logits 0.  [T,E] f32
+ *   dW_r = x^T . dlogits  [d,E] f32 (skipped when x or dW_r is NULL; with
+ *   accumulate & MOE_ACCUM_DW added to the existing value)
+ */
+int moe_route_bwd(const moe_shape* s, int mode, const float* dgates,
+                  const float* gates, const int32_t* idx, const void* x,
+                  float* dlogits, float* dW_r, int accumulate, void* ws,
+                  size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_dispatch_bwd - backward of dispatch (page 2, backward chain:
+ * dispatch's backward after the MLP's):
+ *   dx[t] = [dx[t] if accumulate & MOE_ACCUM_DX] + sum over local k of dxp[row(t,k)]
+ *           [+ sum_k dlogits[t, idx[t,k]] * W_r[:, idx[t,k]]  if dlogits != NULL]
+ * rounded once.  The router term is the input gradient of x . W_r; only the
+ * K selected logits of a token have nonzero gradient.  idx and W_r are
+ * required when dlogits is given.  dx [T,d] dtype.
+ */
+int moe_dispatch_bwd(const moe_shape* s, const void* dxp,
+                     const int32_t* row_of_pair, const int32_t* idx,
+                     const float* dlogits, const void* W_r, void* dx,
+                     int accumulate, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- two-micro-batch step ------------------------------------------------ */
+/* One micro-batch's buffers (sizes as in the calls above). */
+typedef struct moe_mb {
+  /* forward */
+  const void* x;
+  float* logits;
+  int32_t* idx;
+  float* gates;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* row_of_pair;
+  int32_t* pair_of_row;
+  int32_t* tile_offsets;
+  void* xp;
+  void* h;
+  void* a;
+  void* yp;
+  void* out;
+  /* backward */
+  const void* dout;
+  void* dyp;
+  float* dgates;
+  float* dlogits;
+  void* dh;
+  void* dxp;
+  void* dx;
+} moe_mb;
+
+typedef struct moe_step {
+  moe_shape shape;
+  int32_t route_mode;     /* MOE_ROUTE_* */
+  int32_t accumulate;     /* MOE_ACCUM_DW: add weight grads into dW_* */
+  const void* W_r;        /* [d,E] (TOPK) */
+  const float* bias;      /* [E] or NULL */
+  const void* W_gu;       /* [E_l,2F,d] */
+  const void* W_down;     /* [E_l,d,F] */
+  float* dW_r;            /* [d,E] or NULL */
+  float* dW_gu;           /* [E_l,2F,d] */
+  float* dW_down;         /* [E_l,d,F] */
+  const moe_mb* fwd;      /* micro-batch forwarded in this step, or NULL */
+  const moe_mb* bwd;      /* micro-batch back-propagated in this step (its
+                             forward buffers hold its forward results), or NULL */
+  void* ws;               /* >= moe_step_workspace_bytes(&shape) */
+  size_t ws_bytes;
+} moe_step;
+
+/*
+ * moe_overlap_step - forward of micro-batch `fwd` and backward of micro-batch
+ * `bwd` in one step (1F1B note page 2, "MoE 1F1B overlap": two streams and two
+ * micro-batches, D before W).  The expert GEMMs and routing run on s_compute;
+ * the HBM-bound dispatch/combine kernels run on s_copy, ordered by events:
+ *   s_copy:    B.combine_bwd | A.dispatch | B.dispatch_bwd | A.combine
+ *   s_compute: A.route, B.route_bwd, B.dgrad, A.ffn_fwd, B.wgrad (deferred)
+ * On return, work on s_compute depends on everything the step issued, so a
+ * caller that waits for s_compute sees all results.  Results are bit-identical
+ * to MOE_STEP_SERIALIZE (all calls on s_compute in forward-then-backward order).
+ * s_copy may equal s_compute (then the step is serialized).
+ */
+int moe_overlap_step(const moe_step* st, hipStream_t s_compute, hipStream_t s_copy,
+                     int flags);
+
+/* ---- kernel timing -------------------------------------------------------- */
+/*
+ * Opt-in kernel timing for measurement.  While enabled, every kernel the
+ * library launches is bracketed by two timing events recorded on the stream
+ * it is launched on (so the measured interval is that kernel's execution on
+ * its own stream, including any slowdown from work running beside it).
+ *   moe_timing_enable(max_records): start recording (up to max_records launches;
+ *     further launches are not timed).  Creates the events on first use.
+ *     Returns MOE_OK, MOE_ERR_SHAPE (max_records < 1) or MOE_ERR_HIP.
+ *   moe_timing_disable(): stop recording (records are kept).
+ *   moe_timing_reset(): drop all records.
+ *   moe_timing_report(i, name, name_len, total_ms, launches): waits for the
+ *     recorded events, then returns the number of distinct kernels recorded
+ *     and, for 0 <= i < that number, the i-th kernel's name (copied into
+ *     name[name_len]), total milliseconds and launch count.  Negative on error.
+ * Timing is process-wide; record and report from one host thread.
+ */
+int moe_timing_enable(int max_records);
+int moe_timing_disable(void);
+int moe_timing_reset(void);
+int moe_timing_report(int i, char* name, size_t name_len, double* total_ms, int* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,137 @@
+"""The C-ABI library loads, exports every symbol include/moe.h declares, and
+rejects bad arguments on the host before any launch.  CPU only: no call here
+reaches a kernel launch."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import combine_expert_ffn_amd as M
+from combine_expert_ffn_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "moe.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("moe_route", "moe_dispatch", "moe_expert_ffn_fwd", "moe_combine", "moe_ffn_dgrad",
+              "moe_ffn_wgrad", "moe_overlap_step", "moe_combine_bwd", "moe_dispatch_bwd",
+              "moe_route_bwd", "moe_workspace_bytes", "moe_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = C.CDLL(_lib.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), f"{n} declared in moe.h but not exported"
+    assert set(_declared()) == set(_lib.SIGNATURES), "binding signatures out of sync with moe.h"
+
+
+def test_struct_layouts_match_header():
+    assert C.sizeof(_lib.MoeShape) == 7 * 8 + 2 * 4
+    assert C.sizeof(_lib.MoeMB) == len(_lib.MB_FIELDS) * 8
+    # shape + 2 ints + 7 pointers + 2 mb pointers + ws + ws_bytes
+    assert C.sizeof(_lib.MoeStep) == C.sizeof(_lib.MoeShape) + 8 + 7 * 8 + 2 * 8 + 8 + 8
+
+
+def _shape(**kw):
+    base = dict(T=64, d=128, F=128, E=8, e_lo=0, E_l=8, K=2, dtype="bf16")
+    base.update(kw)
+    return M.make_shape(**base)
+
+
+FAKE = C.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), M.MOE_ERR_DTYPE),
+    (dict(d=100), M.MOE_ERR_SHAPE),
+    (dict(d=32), M.MOE_ERR_SHAPE),
+    (dict(F=96), M.MOE_ERR_SHAPE),
+    (dict(K=9), M.MOE_ERR_SHAPE),
+    (dict(K=0), M.MOE_ERR_SHAPE),
+    (dict(K=17, E=32, E_l=8), M.MOE_ERR_SHAPE),
+    (dict(E=600, E_l=8), M.MOE_ERR_SHAPE),
+    (dict(e_lo=4, E_l=8), M.MOE_ERR_SHAPE),
+    (dict(E_l=0), M.MOE_ERR_SHAPE),
+    (dict(T=-1), M.MOE_ERR_SHAPE),
+    (dict(T=1 << 28, K=8), M.MOE_ERR_SHAPE),
+])
+def test_shape_validation(kw, code):
+    s = _shape(**kw)
+    rc = M.lib().moe_combine(C.byref(s), FAKE, FAKE, FAKE, FAKE, None)
+    assert rc == code
+    assert M.lib().moe_last_error()
+    assert M.moe_workspace_bytes(s) == 0
+
+
+def test_null_pointers_rejected():
+    s = _shape()
+    L = M.lib()
+    assert L.moe_combine(C.byref(s), None, FAKE, FAKE, FAKE, None) == M.MOE_ERR_NULL
+    assert b"yp" in L.moe_last_error()
+    assert L.moe_combine(None, FAKE, FAKE, FAKE, FAKE, None) == M.MOE_ERR_NULL
+    assert L.moe_expert_ffn_fwd(C.byref(s), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                None) == M.MOE_ERR_NULL
+    assert L.moe_ffn_dgrad(C.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                           None) == M.MOE_ERR_NULL
+    assert L.moe_ffn_wgrad(C.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                           None) == M.MOE_ERR_NULL
+    # TOPK routing needs x, W_r, logits, gates
+    assert L.moe_route(C.byref(s), M.MOE_ROUTE_TOPK, None, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                       1 << 20, None) == M.MOE_ERR_NULL
+    # the router term of dispatch_bwd needs idx and W_r
+    assert L.moe_dispatch_bwd(C.byref(s), FAKE, FAKE, None, FAKE, FAKE, FAKE, 0, FAKE, 1 << 20,
+                              None) == M.MOE_ERR_NULL
+
+
+def test_workspace_size_checked():
+    s = _shape(T=4096, K=8)
+    need = M.moe_workspace_bytes(s)
+    assert need >= 256
+    L = M.lib()
+    rc = L.moe_dispatch(C.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None)
+    assert rc == M.MOE_ERR_WORKSPACE
+    rc = L.moe_route(C.byref(s), M.MOE_ROUTE_TOPK, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 16,
+                     None)
+    assert rc == M.MOE_ERR_WORKSPACE
+    assert M.moe_step_workspace_bytes(s) == 2 * need
+
+
+def test_modes_and_flags_rejected():
+    s = _shape()
+    L = M.lib()
+    assert L.moe_route(C.byref(s), 9, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                       None) == M.MOE_ERR_ARG
+    assert L.moe_route_bwd(C.byref(s), M.MOE_ROUTE_FORCE_BALANCE, FAKE, FAKE, FAKE, None, FAKE,
+                           None, 0, None, 0, None) == M.MOE_ERR_UNSUPPORTED
+    assert L.moe_ffn_wgrad(C.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8,
+                           None) == M.MOE_ERR_ARG
+    st = _lib.MoeStep()
+    st.shape = s
+    st.route_mode = M.MOE_ROUTE_FORCE_BALANCE
+    assert L.moe_overlap_step(C.byref(st), None, None, 64) == M.MOE_ERR_ARG
+    st.route_mode = 5
+    assert L.moe_overlap_step(C.byref(st), None, None, 0) == M.MOE_ERR_ARG
+    st.route_mode = M.MOE_ROUTE_FORCE_BALANCE
+    assert L.moe_overlap_step(C.byref(st), None, None, 0) == M.MOE_ERR_NULL   # no weights
+    assert L.moe_overlap_step(None, None, None, 0) == M.MOE_ERR_NULL
+
+
+def test_step_rejects_small_workspace_and_same_microbatch():
+    s = _shape()
+    mb = _lib.MoeMB(*([0x1000] * len(_lib.MB_FIELDS)))
+    st = _lib.MoeStep(s, M.MOE_ROUTE_FORCE_BALANCE, 0, None, None, 0x1000, 0x1000, None, 0x1000,
+                      0x1000, C.pointer(mb), C.pointer(mb), 0x1000, 1 << 30)
+    assert M.lib().moe_overlap_step(C.byref(st), None, None, 0) == M.MOE_ERR_ARG
+    st.bwd = None
+    st.ws_bytes = 8
+    assert M.lib().moe_overlap_step(C.byref(st), None, None, 0) == M.MOE_ERR_WORKSPACE

@@ -1,0 +1,227 @@
+"""Full-size workloads on the GPU, in the launch configuration the benchmark times
+(moe_overlap_step on two streams), checked against the oracle on sampled
+outputs: the oracle recomputes sampled rows / tokens / weight-gradient entries
+from the GPU's inputs to that stage.  Maps and indices are checked in full.
+Also: overlapped == serialized == eager-wgrad, bit for bit (the pages' "loss
+trajectory unchanged by overlap" criterion, skill card page 1, success criteria)."""
+
+import numpy as np
+import pytest
+import torch
+
+import combine_expert_ffn_amd as M
+import oracle as O
+from combine_expert_ffn_amd.inputs import WORKLOADS, make_inputs
+from moe_harness import TAU, close, dev, exact, host, log, topk_gap
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    M.lib()
+
+
+class Net:
+    """Device weights and gradient buffers of one workload."""
+
+    def __init__(self, w, inp):
+        D = lambda a: dev(a, w.dtype)
+        self.w = w
+        self.s = M.shape_of(w)
+        self.topk = w.route == "topk"
+        self.mode = M.MOE_ROUTE_TOPK if self.topk else M.MOE_ROUTE_FORCE_BALANCE
+        self.W_gu, self.W_down = D(inp["W_gu"]), D(inp["W_down"])
+        self.W_r = D(inp["W_r"]) if self.topk else None
+        self.bias = dev(inp["bias"], "f32x") if inp["bias"] is not None else None
+        self.dW_gu = torch.empty(w.E_l, 2 * w.F, w.d, dtype=torch.float32, device="cuda")
+        self.dW_down = torch.empty(w.E_l, w.d, w.F, dtype=torch.float32, device="cuda")
+        self.dW_r = torch.empty(w.d, w.E, dtype=torch.float32, device="cuda") if self.topk else None
+        self.ws = torch.empty(M.moe_step_workspace_bytes(self.s), dtype=torch.uint8, device="cuda")
+
+    def mb(self, x, dout, gates=None):
+        D = lambda a: dev(a, self.w.dtype)
+        return M.MicroBatch(self.s, x=D(x), dout=D(dout),
+                            gates=None if gates is None else dev(gates, "f32x"))
+
+    def step(self, fwd, bwd, s0, s1, flags, accumulate=0):
+        st = M.make_step(self.s, self.mode, self.W_gu, self.W_down, self.dW_gu, self.dW_down,
+                         self.ws, fwd=fwd, bwd=bwd, W_r=self.W_r, bias=self.bias,
+                         dW_r=self.dW_r, accumulate=accumulate)
+        M.moe_overlap_step(st, s0, s1, flags)
+
+
+def _rows(t, idx):
+    return host(t[torch.from_numpy(np.asarray(idx, np.int64)).cuda()])
+
+
+def sampled_check(w, inp, A, net, rng, nrows=192, ntok=96, wgrad_prev=None):
+    """Check micro-batch A (forward and backward done) against the oracle on samples."""
+    prec, tau = w.dtype, TAU[w.dtype]
+    K = w.K
+    x64 = np.asarray(inp["x"], np.float64)
+    # ---- routing: in full
+    if net.topk:
+        ref_l = O.router_logits(x64, np.asarray(inp["W_r"], np.float64), inp["bias"], prec)
+        gl = host(A.logits)
+        close("logits", gl, ref_l, tau)
+        i_o, g_o = O.topk_route(gl, K, prec)
+        exact("idx vs oracle top-k of the GPU logits", host(A.idx), i_o)
+        close("gates", host(A.gates), g_o, tau)
+        i_ref, _ = O.topk_route(ref_l, K, prec)
+        diff = np.any(i_o != i_ref, axis=1)
+        assert np.all(topk_gap(ref_l, K)[diff] < 1e-4), "selection differs without a near tie"
+        log(f"  routing: {diff.sum()} of {w.T} tokens differ from oracle-logit routing (near ties)")
+    else:
+        exact("idx", host(A.idx), O.force_balance_idx(w.T, K, w.E))
+    idx = host(A.idx)
+    gates = host(A.gates)
+    # ---- plan: in full
+    plan = O.dispatch_plan(idx, w.e_lo, w.E_l, M.moe_tile_m())
+    for k in ("counts", "offsets", "tile_offsets", "row_of_pair", "pair_of_row"):
+        exact(k, host(getattr(A, k)), plan[k])
+    offsets = plan["offsets"]
+    N = int(offsets[-1])
+    log(f"  plan: N={N} rows, counts min {plan['counts'].min()} max {plan['counts'].max()}")
+    # ---- sampled rows: permute, FFN forward, dgrad
+    rows = np.sort(rng.choice(N, min(nrows, N), replace=False))
+    exact("xp rows", _rows(A.xp, rows), x64[plan["pair_of_row"][rows] // K])
+    xp_s, h_s, a_s, y_s = (_rows(getattr(A, k), rows) for k in ("xp", "h", "a", "yp"))
+    dyp_s, dh_s, dxp_s = (_rows(getattr(A, k), rows) for k in ("dyp", "dh", "dxp"))
+    e_of = np.searchsorted(offsets, rows, side="right") - 1
+    for j in np.unique(e_of):
+        sel = e_of == j
+        o = np.array([0, sel.sum()])
+        Wg = np.asarray(inp["W_gu"][j:j + 1], np.float64)
+        Wd = np.asarray(inp["W_down"][j:j + 1], np.float64)
+        hh, aa, yy = O.expert_ffn_fwd(xp_s[sel], o, Wg, Wd, prec)
+        close(f"h (expert {j})", h_s[sel], hh, tau)
+        close(f"a (expert {j})", a_s[sel], aa, tau)
+        close(f"yp (expert {j})", y_s[sel], yy, tau)
+        dh_r, dxp_r = O.ffn_dgrad(dyp_s[sel], h_s[sel], o, Wg, Wd, prec)
+        close(f"dh (expert {j})", dh_s[sel], dh_r, tau)
+        close(f"dxp (expert {j})", dxp_s[sel], dxp_r, tau)
+    # ---- sampled tokens: combine, combine bwd, router bwd, dispatch bwd
+    toks = np.sort(rng.choice(w.T, min(ntok, w.T), replace=False))
+    rop = plan["row_of_pair"][toks]
+    loc = np.unique(rop[rop >= 0])
+    remap = {r: i for i, r in enumerate(loc)}
+    rop_l = np.vectorize(lambda r: remap.get(r, -1))(rop) if rop.size else rop
+    yp_l = _rows(A.yp, loc)
+    dout = np.asarray(inp["dout"], np.float64)[toks]
+    close("out", _rows(A.out, toks), O.combine(yp_l, gates[toks], rop_l, prec), tau)
+    dyp_l, dg_l = O.combine_bwd(dout, yp_l, gates[toks], rop_l, len(loc), prec)
+    close("dyp (token rows)", _rows(A.dyp, loc), dyp_l, tau)
+    dgates = host(A.dgates)
+    close("dgates", dgates[toks], dg_l, tau)
+    dl_t = None
+    if net.topk:
+        dl_t, _ = O.route_bwd(dgates[toks], gates[toks], idx[toks], None, w.E, prec=prec)
+        close("dlogits", _rows(A.dlogits, toks), dl_t, tau)
+        if wgrad_prev is None:
+            cols = np.sort(rng.choice(w.d, 16, replace=False))
+            _, dwr = O.route_bwd(dgates, gates, idx, x64[:, cols], w.E, prec=prec)
+            close("dW_r (columns)", host(net.dW_r)[cols], dwr, tau)
+        dl_t = _rows(A.dlogits, toks)
+    dxp_l = _rows(A.dxp, loc)
+    W_r64 = np.asarray(inp["W_r"], np.float64) if net.topk else None
+    close("dx", _rows(A.dx, toks), O.dispatch_bwd(dxp_l, rop_l, dl_t, W_r64, None, prec), tau)
+    # ---- sampled weight-gradient entries
+    if wgrad_prev is None:
+        nz = np.nonzero(plan["counts"])[0]
+        experts = np.unique(np.concatenate([
+            nz[[np.argmax(plan["counts"][nz]), np.argmin(plan["counts"][nz])]],
+            rng.choice(nz, min(2, nz.size), replace=False)]))
+        for j in experts:
+            r0, r1 = int(offsets[j]), int(offsets[j + 1])
+            I = np.sort(rng.choice(w.d, 8, replace=False))
+            Fc = np.sort(rng.choice(w.F, 8, replace=False))
+            Mc = np.sort(rng.choice(2 * w.F, 8, replace=False))
+            Cc = np.sort(rng.choice(w.d, 8, replace=False))
+            sl = lambda t, c: host(t[r0:r1][:, torch.from_numpy(c).cuda()])
+            gu, dn = O.ffn_wgrad(sl(A.xp, Cc), sl(A.a, Fc), sl(A.dh, Mc), sl(A.dyp, I),
+                                 np.array([0, r1 - r0]), prec=prec)
+            close(f"dW_gu (expert {j})", host(net.dW_gu[j])[np.ix_(Mc, Cc)], gu[0], tau)
+            close(f"dW_down (expert {j})", host(net.dW_down[j])[np.ix_(I, Fc)], dn[0], tau)
+
+
+@pytest.mark.parametrize("name,T", [("ep16_rank_bf16", None), ("ep8_rank_zipf_bf16", None),
+                                    ("ep1_128exp_bf16", 16384)])
+def test_fullsize_sampled(name, T):
+    w = WORKLOADS[name] if T is None else WORKLOADS[name].with_tokens(T)
+    log(f"[full size] {name}: T={w.T} d={w.d} F={w.F} E={w.E} E_l={w.E_l} K={w.K}")
+    inp = make_inputs(w, seed=0)
+    net = Net(w, inp)
+    A = net.mb(inp["x"], inp["dout"], inp["gates"])
+    s0 = torch.cuda.current_stream()
+    s1 = torch.cuda.Stream()
+    net.step(A, None, s0, s1, 0)
+    net.step(None, A, s0, s1, 0)
+    torch.cuda.synchronize()
+    sampled_check(w, inp, A, net, np.random.default_rng(1))
+    log(f"[full size] {name}: ok")
+
+
+def test_overlap_equals_serialized_two_microbatch():
+    w = WORKLOADS["two_microbatch_bf16"]
+    log(f"[overlap] two micro-batches T={w.T} d={w.d} F={w.F} E={w.E} K={w.K}")
+    inp = make_inputs(w, seed=0)
+    net = Net(w, inp)
+    s0 = torch.cuda.current_stream()
+    s1 = torch.cuda.Stream()
+    results = {}
+    for tag, flags, copy in (("serial", M.MOE_STEP_SERIALIZE, s0), ("overlap", 0, s1),
+                             ("eager", M.MOE_STEP_EAGER_WGRAD, s1)):
+        A = net.mb(inp["x"], inp["dout"])
+        B = net.mb(inp["x_b"], inp["dout_b"])
+        net.step(A, None, s0, copy, flags)
+        net.step(B, A, s0, copy, flags)                        # A's grads overwrite
+        net.step(None, B, s0, copy, flags, M.MOE_ACCUM_DW)     # B's grads accumulate
+        torch.cuda.synchronize()
+        results[tag] = dict(A=A, B=B, dW_gu=net.dW_gu.clone(), dW_down=net.dW_down.clone(),
+                            dW_r=net.dW_r.clone())
+    ref = results["serial"]
+    for tag in ("overlap", "eager"):
+        r = results[tag]
+        for mbn in ("A", "B"):
+            for k in ("idx", "gates", "row_of_pair", "out", "dgates", "dlogits", "dx", "yp"):
+                assert torch.equal(getattr(r[mbn], k), getattr(ref[mbn], k)), (tag, mbn, k)
+        for k in ("dW_gu", "dW_down", "dW_r"):
+            assert torch.equal(r[k], ref[k]), (tag, k)
+    log("[overlap] overlapped and eager-wgrad steps bit-identical to serialized")
+    # oracle on samples of micro-batch A (weight grads hold A + B)
+    r = results["overlap"]
+    A, B = r["A"], r["B"]
+    net.dW_gu.copy_(r["dW_gu"])
+    net.dW_down.copy_(r["dW_down"])
+    net.dW_r.copy_(r["dW_r"])
+    rng = np.random.default_rng(2)
+    sampled_check(w, inp, A, net, rng, wgrad_prev=True)
+    # weight gradients: sum over both micro-batches, sampled entries
+    prec, tau = w.dtype, TAU[w.dtype]
+    cols = np.sort(rng.choice(w.d, 16, replace=False))
+    prev = None
+    for mb, xk in ((A, "x"), (B, "x_b")):
+        _, prev = O.route_bwd(host(mb.dgates), host(mb.gates), host(mb.idx),
+                              np.asarray(inp[xk], np.float64)[:, cols], w.E, dW_r_prev=prev,
+                              prec=prec)
+    close("dW_r A+B (columns)", host(net.dW_r)[cols], prev, tau)
+    for j in (0, 5):
+        I = np.sort(rng.choice(w.d, 8, replace=False))
+        Fc = np.sort(rng.choice(w.F, 8, replace=False))
+        Mc = np.sort(rng.choice(2 * w.F, 8, replace=False))
+        Cc = np.sort(rng.choice(w.d, 8, replace=False))
+        prev = None
+        for mb in (A, B):
+            off = host(mb.offsets)
+            r0, r1 = int(off[j]), int(off[j + 1])
+            sl = lambda t, c: host(t[r0:r1][:, torch.from_numpy(c).cuda()])
+            gu, dn = O.ffn_wgrad(sl(mb.xp, Cc), sl(mb.a, Fc), sl(mb.dh, Mc), sl(mb.dyp, I),
+                                 np.array([0, r1 - r0]),
+                                 dW_gu_prev=None if prev is None else prev[0],
+                                 dW_down_prev=None if prev is None else prev[1], prec=prec)
+            prev = (gu, dn)
+        close(f"dW_gu A+B (expert {j})", host(net.dW_gu[j])[np.ix_(Mc, Cc)], prev[0][0], tau)
+        close(f"dW_down A+B (expert {j})", host(net.dW_down[j])[np.ix_(I, Fc)], prev[1][0], tau)
