@@ -95,7 +95,6 @@ def main():
     ap.add_argument("--workload", default="ep16_rank_bf16")
     ap.add_argument("--tokens", type=int, default=None, help="override T of the workload")
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
-    ap.add_argument("--no-serial", action="store_true", help="skip the serialized comparison")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -154,9 +153,7 @@ def main():
     N = int(counts[0].sum())
     T_loc = int((mbs[0].row_of_pair >= 0).any(dim=1).sum())
 
-    # ---- timed region: overlapped 1F1B steps, kernel events on their own streams
-    M.moe_timing_reset()
-    M.moe_timing_enable(64 * args.steps)
+    # ---- timed region 1: overlapped 1F1B steps (the product schedule) -> value
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -165,22 +162,25 @@ def main():
     ev1.record(s0)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    M.moe_timing_disable()
     ms_step = ev0.elapsed_time(ev1) / args.steps
-    kern = M.moe_timing_report()
     err(f"[bench] overlapped: {ms_step:.4f} ms/step (wall {1e3 * wall / args.steps:.4f})")
 
-    # ---- serialized comparison (same calls, one stream, forward then backward)
-    ms_serial = None
-    if not args.no_serial:
-        i = run_loop(args.warmup, M.MOE_STEP_SERIALIZE, i)
-        torch.cuda.synchronize()
-        ev0.record(s0)
-        i = run_loop(args.steps, M.MOE_STEP_SERIALIZE, i)
-        ev1.record(s0)
-        torch.cuda.synchronize()
-        ms_serial = ev0.elapsed_time(ev1) / args.steps
-        err(f"[bench] serialized: {ms_serial:.4f} ms/step -> overlap x{ms_serial / ms_step:.3f}")
+    # ---- timed region 2: the same steps serialized on one stream, with every
+    # kernel bracketed by HIP events on its stream (no concurrency, so each
+    # kernel's interval is its own execution)
+    i = run_loop(args.warmup, M.MOE_STEP_SERIALIZE, i)
+    M.moe_timing_reset()
+    M.moe_timing_enable(64 * args.steps)
+    torch.cuda.synchronize()
+    ev0.record(s0)
+    i = run_loop(args.steps, M.MOE_STEP_SERIALIZE, i)
+    ev1.record(s0)
+    torch.cuda.synchronize()
+    M.moe_timing_disable()
+    ms_serial = ev0.elapsed_time(ev1) / args.steps
+    kern = M.moe_timing_report()
+    err(f"[bench] serialized (kernel events on): {ms_serial:.4f} ms/step -> overlap "
+        f"x{ms_serial / ms_step:.3f}")
 
     nonfinite = int(sum((~torch.isfinite(t.float())).sum().item()
                         for mb in mbs for t in (mb.out, mb.dx)))

@@ -98,9 +98,10 @@ def moe_combine_bwd(s, dout, yp, gates, row_of_pair, dyp, dgates, stream=None):
                                 _p(dyp), _p(dgates), _stream(stream)))
 
 
-def moe_ffn_dgrad(s, dyp, h, offsets, tile_offsets, W_gu, W_down, dh, dxp, stream=None):
+def moe_ffn_dgrad(s, dyp, h, offsets, tile_offsets, W_gu, W_down, dh, dxp, ws, stream=None):
+    wp, wb = _ws(ws)
     check(lib().moe_ffn_dgrad(C.byref(s), _p(dyp), _p(h), _p(offsets), _p(tile_offsets),
-                              _p(W_gu), _p(W_down), _p(dh), _p(dxp), _stream(stream)))
+                              _p(W_gu), _p(W_down), _p(dh), _p(dxp), wp, wb, _stream(stream)))
 
 
 def moe_ffn_wgrad(s, xp, a, dh, dyp, offsets, dW_gu, dW_down, accumulate=0, stream=None):

@@ -69,7 +69,7 @@ SIGNATURES = {
     "moe_expert_ffn_fwd": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_combine": (C.c_int, [_SP, _P, _P, _P, _P, _P]),
     "moe_combine_bwd": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P]),
-    "moe_ffn_dgrad": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_ffn_dgrad": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "moe_ffn_wgrad": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, C.c_int, _P]),
     "moe_route_bwd": (C.c_int, [_SP, C.c_int, _P, _P, _P, _P, _P, _P, C.c_int, _P, C.c_size_t,
                                 _P]),

@@ -88,6 +88,7 @@ static size_t ws_one(const moe_shape* s) {
   size_t b = ws_plan_bytes(s);
   if (ws_wrt_bytes(s) > b) b = ws_wrt_bytes(s);
   if (ws_router_partial_bytes(s) > b) b = ws_router_partial_bytes(s);
+  if (ws_wT_bytes(s) > b) b = ws_wT_bytes(s);
   return b < 256 ? 256 : b;
 }
 
@@ -300,7 +301,7 @@ int moe_combine_bwd(const moe_shape* s, const void* dout, const void* yp, const 
 
 int moe_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h, const int32_t* offsets,
                   const int32_t* tile_offsets, const void* W_gu, const void* W_down, void* dh,
-                  void* dxp, hipStream_t stream) {
+                  void* dxp, void* ws, size_t ws_bytes, hipStream_t stream) {
   g_err[0] = 0;
   if (int rc = validate_shape(s)) return rc;
   REQUIRE(dyp);
@@ -311,7 +312,11 @@ int moe_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h, const int3
   REQUIRE(W_down);
   REQUIRE(dh);
   REQUIRE(dxp);
-  return launch_ffn_dgrad(s, dyp, h, offsets, tile_offsets, W_gu, W_down, dh, dxp, stream);
+  if (s->dtype == MOE_BF16) {
+    REQUIRE(ws);
+    if (int rc = need_ws(__func__, ws_bytes, ws_wT_bytes(s))) return rc;
+  }
+  return launch_ffn_dgrad(s, dyp, h, offsets, tile_offsets, W_gu, W_down, dh, dxp, ws, stream);
 }
 
 int moe_ffn_wgrad(const moe_shape* s, const void* xp, const void* a, const void* dh,
@@ -489,7 +494,7 @@ static int bwd_route(const StepCtx& c, const moe_mb* B, hipStream_t q) {
 }
 static int bwd_dgrad(const StepCtx& c, const moe_mb* B, hipStream_t q) {
   return launch_ffn_dgrad(c.s, B->dyp, B->h, B->offsets, B->tile_offsets, c.st->W_gu,
-                          c.st->W_down, B->dh, B->dxp, q);
+                          c.st->W_down, B->dh, B->dxp, c.wsB, q);
 }
 static int bwd_dispatch(const StepCtx& c, const moe_mb* B, hipStream_t q) {
   return do_dispatch_bwd(c.s, B->dxp, B->row_of_pair, B->idx, c.router ? B->dlogits : nullptr,

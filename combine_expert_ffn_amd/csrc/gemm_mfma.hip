@@ -6,18 +6,29 @@
 // W) as the 1F1B note describes (page 2, "MoE 1F1B overlap").
 //
 // Structure shared by every kernel here:
-//  * block tile BM x BN, K step 64, operands staged through LDS in two stages
-//    (global -> registers for step k+1 while the matrix cores work on step k);
+//  * persistent grid (one block per CU); the tiles are split into eight
+//    contiguous ranges, one per XCD (the hardware places block b on XCD b % 8),
+//    so the tiles running together on an XCD share A rows and expert weights
+//    in its L2, and the ranges stay balanced whatever the device-side tile count;
+//  * block tile 256 x 256, K step 64, 8 waves (2 per SIMD), each owning a
+//    128 x 64 piece as 4 x 2 MFMA 32x32 tiles;
+//  * two LDS stages fed through registers: the loads for step k+1 are issued
+//    at the start of step k and written to LDS in its third quarter;
 //  * LDS tiles are [rows][64] bf16 with the 16-byte chunk index XOR-swizzled
-//    by the row so that the matrix-core fragment reads hit distinct banks;
-//  * an operand that is contiguous along K is copied 16 bytes at a time; an
-//    operand contiguous along M/N (weights in dgrad, activations in wgrad) is
-//    read as 8 (k) x 4 (m) blocks and transposed in registers on its way to LDS;
-//  * the block id is remapped so that consecutive tiles (same expert, same
-//    rows) land on the same XCD and share its L2.
+//    by the row, so matrix-core fragment reads are free of bank conflicts;
+//  * the MFMA fragments of the next 16-wide k slice are read while the current
+//    slice's MFMAs run, and the instruction order (MFMA / LDS read / global
+//    load / LDS write) is fixed with scheduling group barriers so the matrix
+//    pipe is fed continuously;
+//  * loads are branch free: rows or columns outside the matrix read a valid
+//    clamped address (their results are discarded, or replaced by zero where
+//    they would enter a sum);
+//  * an operand contiguous along K is copied 16 bytes at a time; an operand
+//    contiguous along M/N (both operands of wgrad) is read as 8 (k) x 4 (m)
+//    blocks and transposed in registers on its way to LDS.  dgrad reads its
+//    weights from K-contiguous transposed copies made at the start of the call.
 // Row-grouped GEMMs (fwd, dgrad) take their (expert, M-tile) from the dispatch
-// plan's tile_offsets (tiles of kTileM rows); the grid is sized for the worst
-// case on the host and surplus blocks exit.
+// plan's tile_offsets (tiles of kTileM rows).
 #include "moe_internal.h"
 
 namespace moe {
@@ -28,26 +39,23 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int BK = 64;
 
+// scheduling group masks (instruction classes)
+constexpr int SG_MFMA = 0x008, SG_VMEM_R = 0x020, SG_DS_R = 0x100, SG_DS_W = 0x200;
+#define SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+
 // Element offset of 16-byte chunk `ch` (0..7) of row `row` of an LDS tile.
 __device__ __forceinline__ int lds_off(int row, int ch) {
   const int s = (row & 7) ^ ((row >> 3) & 1);
   return row * BK + ((ch ^ s) << 3);
 }
 
-// Hardware places block b on XCD b % 8.  Map so that each XCD works on a
-// contiguous range of logical tile ids.
-__device__ __forceinline__ int xcd_remap(int bid, int nb) {
-  const int q = nb >> 3, r = nb & 7;
-  const int xcd = bid & 7, lid = bid >> 3;
-  return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + lid;
-}
-
 // Operand contiguous along K: R rows x 64 k per stage, 16-byte chunks.
-// row_ptr(r) gives the address of element k = 0 of tile row r, or nullptr for
-// a row outside the matrix (loaded as zeros).  K must be a multiple of 64.
+// row_ptr(r) gives a valid address of element k = 0 of tile row r (rows
+// outside the matrix are clamped by the caller).  K is a multiple of 64.
 template <int R, int NT>
 struct LoadK {
   static constexpr int CH = R * 8 / NT;
+  static constexpr int NLOAD = CH, NSTORE = CH;
   static_assert(CH >= 1 && (R * 8) % NT == 0, "tile/threads mismatch");
   const uint16_t* src[CH];
   int dst[CH];
@@ -57,15 +65,13 @@ struct LoadK {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int q = c * NT + tid, row = q >> 3, ch = q & 7;
-      const uint16_t* p = row_ptr(row);
-      src[c] = p ? p + ch * 8 : nullptr;
+      src[c] = row_ptr(row) + ch * 8;
       dst[c] = lds_off(row, ch);
     }
   }
   __device__ __forceinline__ void load(int k0, int /*k_end*/) {
 #pragma unroll
-    for (int c = 0; c < CH; ++c)
-      v[c] = src[c] ? *(const uint4*)(src[c] + k0) : make_uint4(0u, 0u, 0u, 0u);
+    for (int c = 0; c < CH; ++c) v[c] = *(const uint4*)(src[c] + k0);
   }
   __device__ __forceinline__ void store(uint16_t* lds) const {
 #pragma unroll
@@ -73,27 +79,31 @@ struct LoadK {
   }
 };
 
-// Operand contiguous along M/N: element (k, col) at col_ptr(col)[k * ld].
+// Operand contiguous along M/N: element (k, col) at base[k * ld + col].
 // Each unit is 8 consecutive k x 4 consecutive columns, transposed in
-// registers into four 16-byte K-chunks.  col_ptr(c) is nullptr for a group of
-// 4 columns outside the matrix; rows k >= k_end load as zeros.
+// registers into four 16-byte K-chunks.  col_ok(c) tells whether the group of
+// 4 columns starting at c is inside the matrix; outside groups and rows
+// k >= k_end contribute zeros (their loads read a clamped valid address).
 template <int R, int NT>
 struct LoadMN {
   static constexpr int U = 2 * R / NT;
+  static constexpr int NLOAD = 8 * U, NSTORE = 4 * U;
   static_assert(U >= 1 && (2 * R) % NT == 0, "tile/threads mismatch");
   const uint16_t* src[U];
+  bool ok[U];
   int kg[U];
   int dst_row[U];
   long ld;
   uint2 v[U][8];
-  template <class ColPtr>
-  __device__ __forceinline__ void init(ColPtr col_ptr, long ld_, int tid) {
+  template <class ColPtr, class ColOk>
+  __device__ __forceinline__ void init(ColPtr col_ptr, ColOk col_ok, long ld_, int tid) {
     ld = ld_;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int q = u * NT + tid, mg = q % (R / 4);
       kg[u] = q / (R / 4);
       dst_row[u] = mg * 4;
+      ok[u] = col_ok(mg * 4);
       src[u] = col_ptr(mg * 4);
     }
   }
@@ -103,8 +113,9 @@ struct LoadMN {
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         const int k = k0 + kg[u] * 8 + kk;
-        v[u][kk] = (src[u] && k < k_end) ? *(const uint2*)(src[u] + (long)k * ld)
-                                          : make_uint2(0u, 0u);
+        const uint2 w = *(const uint2*)(src[u] + (long)min(k, k_end - 1) * ld);
+        const bool take = ok[u] && k < k_end;
+        v[u][kk] = make_uint2(take ? w.x : 0u, take ? w.y : 0u);
       }
   }
   __device__ __forceinline__ void store(uint16_t* lds) const {
@@ -137,6 +148,7 @@ struct Tile {
   static constexpr int LDS_ELEMS = 2 * (BM + BN) * BK;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
 };
+using T256 = Tile<256, 256, 2, 4>;
 
 // Output element held by accumulator register r of 32x32 tile (i, j) in this
 // lane: row = wave_row0 + i*32 + out_row(lane, r), col = wave_col0 + j*32 + lane%32.
@@ -144,8 +156,48 @@ __device__ __forceinline__ int out_row(int lane, int r) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
-// Two-stage LDS main loop over k in [k_begin, k_end), steps of 64.
-template <class TL, class LA, class LB>
+template <class TL>
+struct Frags {
+  bf16x8_t a[TL::TM], b[TL::TN];
+};
+
+template <class TL>
+__device__ __forceinline__ void read_frags(Frags<TL>& f, const uint16_t* A, const uint16_t* B,
+                                           int kk, int wm, int wn, int lane) {
+  const int fr = lane & 31, ch = kk * 2 + (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < TL::TM; ++i)
+    f.a[i] = *(const bf16x8_t*)(A + lds_off(wm * TL::WTM + i * 32 + fr, ch));
+#pragma unroll
+  for (int j = 0; j < TL::TN; ++j)
+    f.b[j] = *(const bf16x8_t*)(B + lds_off(wn * TL::WTN + j * 32 + fr, ch));
+}
+
+template <class TL>
+__device__ __forceinline__ void mfmas(const Frags<TL>& f, f32x16_t (&acc)[TL::TM][TL::TN]) {
+#pragma unroll
+  for (int i = 0; i < TL::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::TN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+// One 16-wide k slice: NM MFMAs, each followed by up to one LDS read, one
+// global load and one LDS write (while those remain).
+template <int NM, int NR, int NV, int NW>
+__device__ __forceinline__ void sched_slice() {
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    SCHED_GROUP(SG_MFMA, 1);
+    if (i < NR) SCHED_GROUP(SG_DS_R, 1);
+    if (i < NV) SCHED_GROUP(SG_VMEM_R, 1);
+    if (i < NW) SCHED_GROUP(SG_DS_W, 1);
+  }
+}
+
+// Two-stage LDS main loop over k in [k_begin, k_end), steps of 64.  The last
+// step reloads its own stage (harmless) so the loop body has no branches.
+template <class TL, class LA, class LB, bool SCHED = true>
 __device__ __forceinline__ void mainloop(LA& la, LB& lb, int k_begin, int k_end,
                                          uint16_t* smem, f32x16_t (&acc)[TL::TM][TL::TN]) {
   uint16_t* const sA0 = smem;
@@ -154,7 +206,6 @@ __device__ __forceinline__ void mainloop(LA& la, LB& lb, int k_begin, int k_end,
   uint16_t* const sB1 = sB0 + TL::BN * BK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / TL::WGN, wn = wave % TL::WGN;
-  const int fr = lane & 31, fk = lane >> 5;
 #pragma unroll
   for (int i = 0; i < TL::TM; ++i)
 #pragma unroll
@@ -163,263 +214,245 @@ __device__ __forceinline__ void mainloop(LA& la, LB& lb, int k_begin, int k_end,
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   const int nk = (k_end - k_begin + BK - 1) / BK;
   if (nk <= 0) return;  // block-uniform
+  constexpr int NM = TL::TM * TL::TN, NR = TL::TM + TL::TN;
+  constexpr int NV = LA::NLOAD + LB::NLOAD, NW = LA::NSTORE + LB::NSTORE;
   la.load(k_begin, k_end);
   lb.load(k_begin, k_end);
   la.store(sA0);
   lb.store(sB0);
   __syncthreads();
+  Frags<TL> f0, f1;
+  read_frags<TL>(f0, sA0, sB0, 0, wm, wn, lane);
   for (int kt = 0; kt < nk; ++kt) {
     const bool odd = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      la.load(k_begin + (kt + 1) * BK, k_end);
-      lb.load(k_begin + (kt + 1) * BK, k_end);
-    }
     const uint16_t* A = odd ? sA1 : sA0;
     const uint16_t* B = odd ? sB1 : sB0;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t a[TL::TM], b[TL::TN];
-#pragma unroll
-      for (int i = 0; i < TL::TM; ++i)
-        a[i] = *(const bf16x8_t*)(A + lds_off(wm * TL::WTM + i * 32 + fr, kk * 2 + fk));
-#pragma unroll
-      for (int j = 0; j < TL::TN; ++j)
-        b[j] = *(const bf16x8_t*)(B + lds_off(wn * TL::WTN + j * 32 + fr, kk * 2 + fk));
-#pragma unroll
-      for (int i = 0; i < TL::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TL::TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      la.store(odd ? sA0 : sA1);
-      lb.store(odd ? sB0 : sB1);
-    }
+    uint16_t* An = odd ? sA0 : sA1;
+    uint16_t* Bn = odd ? sB0 : sB1;
+    const int kn = k_begin + (kt + 1 < nk ? kt + 1 : kt) * BK;
+    la.load(kn, k_end);
+    lb.load(kn, k_end);
+    read_frags<TL>(f1, A, B, 1, wm, wn, lane);
+    mfmas<TL>(f0, acc);
+    if constexpr (SCHED) sched_slice<NM, NR, NV, 0>();
+    read_frags<TL>(f0, A, B, 2, wm, wn, lane);
+    mfmas<TL>(f1, acc);
+    if constexpr (SCHED) sched_slice<NM, NR, 0, 0>();
+    read_frags<TL>(f1, A, B, 3, wm, wn, lane);
+    mfmas<TL>(f0, acc);
+    la.store(An);
+    lb.store(Bn);
+    if constexpr (SCHED) sched_slice<NM, NR, 0, NW>();
+    mfmas<TL>(f1, acc);
     __syncthreads();
+    read_frags<TL>(f0, An, Bn, 0, wm, wn, lane);
   }
+  __syncthreads();  // LDS free for the caller's next tile
 }
 
-struct RowTile {
-  int e, m0, m_end;
+// Persistent schedule: the blocks form G = min(8, grid) groups by block % G
+// (with G = 8 a group is one XCD); group g owns tiles [g*total/G, (g+1)*total/G),
+// handed out to its blocks round robin.  Every group has at least one block,
+// so every tile is processed.
+struct Sched {
+  int t, end, step;
+  __device__ __forceinline__ explicit Sched(int total) {
+    const int nb = gridDim.x, G = nb < 8 ? nb : 8;
+    const int g = blockIdx.x % G, slot = blockIdx.x / G;
+    t = (int)((long)total * g / G) + slot;
+    end = (int)((long)total * (g + 1) / G);
+    step = (nb - g + G - 1) / G;
+  }
 };
 
-// (expert, first row, row end) of M-tile mt; false (block-uniform) past the last tile.
-__device__ __forceinline__ bool row_tile(const int32_t* __restrict__ offsets,
-                                         const int32_t* __restrict__ tile_offsets, int E_l,
-                                         int mt, int* s_to, int* s_off, RowTile& rt) {
-  for (int j = threadIdx.x; j <= E_l; j += blockDim.x) {
-    s_to[j] = tile_offsets[j];
-    s_off[j] = offsets[j];
-  }
-  __syncthreads();
-  if (mt >= s_to[E_l]) return false;
+// (expert, first row, row end) of M-tile mt from LDS copies of tile_offsets/offsets.
+__device__ __forceinline__ void row_tile(const int* s_to, const int* s_off, int E_l, int mt,
+                                         int& e, int& m0, int& m_end) {
   int lo = 0, hi = E_l;  // s_to[lo] <= mt < s_to[hi]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (s_to[mid] <= mt) lo = mid;
     else hi = mid;
   }
-  rt.e = lo;
-  rt.m0 = s_off[lo] + (mt - s_to[lo]) * kTileM;
-  rt.m_end = s_off[lo + 1];
-  return true;
+  e = lo;
+  m0 = s_off[lo] + (mt - s_to[lo]) * kTileM;
+  m_end = s_off[lo + 1];
 }
 
 // ---------------------------------------------------------------------------
-// forward GEMM1: [g, u] = xp . W_gu[e]^T with the SwiGLU epilogue.
-// The B tile pairs gate and up rows: wave wn's 64 tile rows are 32 gate rows
-// j and the 32 up rows F + j of the same j, so each lane holds g and u of the
-// same output element.
+// Row-grouped GEMM (forward and dgrad): M tiles follow the dispatch plan, N
+// tiles are fixed.  Op supplies the loaders, the K extent and the epilogue.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WGM, int WGN>
-__global__ __launch_bounds__(64 * WGM * WGN) void ffn_gate_up_kernel(
-    const uint16_t* __restrict__ xp, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ tile_offsets, const uint16_t* __restrict__ W_gu,
-    uint16_t* __restrict__ h, uint16_t* __restrict__ a, int E_l, int d, int F, int n_tiles) {
-  using TL = Tile<BM, BN, WGM, WGN>;
-  static_assert(BM == kTileM, "row tiles come from the dispatch plan");
-  static_assert(TL::WTN == 64, "each wave pairs 32 gate with 32 up columns");
+template <class TL, class Op>
+__global__ __launch_bounds__(TL::NT) void row_grouped_kernel(Op op,
+                                                             const int32_t* __restrict__ offsets,
+                                                             const int32_t* __restrict__ tile_offsets,
+                                                             int E_l, int n_tiles) {
+  static_assert(TL::BM == kTileM, "row tiles come from the dispatch plan");
   __shared__ __attribute__((aligned(16))) uint16_t smem[TL::LDS_ELEMS];
   __shared__ int s_to[257], s_off[257];
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int mt = lid / n_tiles, nt = lid % n_tiles;
-  RowTile rt;
-  if (!row_tile(offsets, tile_offsets, E_l, mt, s_to, s_off, rt)) return;
-  const int tid = threadIdx.x;
-  const int jb = nt * (BN / 2);
-  const uint16_t* Wg = W_gu + (size_t)rt.e * 2 * F * d;
-  LoadK<BM, TL::NT> la;
-  LoadK<BN, TL::NT> lb;
-  la.init([&](int r) -> const uint16_t* {
-    const int row = rt.m0 + r;
-    return row < rt.m_end ? xp + (size_t)row * d : nullptr;
-  }, tid);
-  lb.init([&](int n) -> const uint16_t* {
-    const int j = jb + (n >> 6) * 32 + (n & 31);
-    return j < F ? Wg + (size_t)(((n >> 5) & 1) * F + j) * d : nullptr;
-  }, tid);
-  f32x16_t acc[TL::TM][TL::TN];
-  mainloop<TL>(la, lb, 0, d, smem, acc);
-  const int lane = tid & 63, wave = tid >> 6, wm = wave / WGN, wn = wave % WGN;
-  const int j = jb + wn * 32 + (lane & 31);
-  if (j >= F) return;
-#pragma unroll
-  for (int i = 0; i < TL::TM; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = rt.m0 + wm * TL::WTM + i * 32 + out_row(lane, r);
-      if (row < rt.m_end) {
-        const float g = acc[i][0][r], u = acc[i][1][r];
-        h[(size_t)row * 2 * F + j] = f2bf(g);
-        h[(size_t)row * 2 * F + F + j] = f2bf(u);
-        a[(size_t)row * F + j] = f2bf(silu_f(g) * u);
-      }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// forward GEMM2: y_p = a . W_down[e]^T   (A: a rows, K = F; B: W_down rows, K = F)
-// ---------------------------------------------------------------------------
-template <int BM, int BN, int WGM, int WGN>
-__global__ __launch_bounds__(64 * WGM * WGN) void ffn_down_kernel(
-    const uint16_t* __restrict__ a, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ tile_offsets, const uint16_t* __restrict__ W_down,
-    uint16_t* __restrict__ yp, int E_l, int d, int F, int n_tiles) {
-  using TL = Tile<BM, BN, WGM, WGN>;
-  static_assert(BM == kTileM, "row tiles come from the dispatch plan");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[TL::LDS_ELEMS];
-  __shared__ int s_to[257], s_off[257];
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int mt = lid / n_tiles, nt = lid % n_tiles;
-  RowTile rt;
-  if (!row_tile(offsets, tile_offsets, E_l, mt, s_to, s_off, rt)) return;
-  const int tid = threadIdx.x;
-  const int nb = nt * BN;
-  const uint16_t* Wd = W_down + (size_t)rt.e * d * F;
-  LoadK<BM, TL::NT> la;
-  LoadK<BN, TL::NT> lb;
-  la.init([&](int r) -> const uint16_t* {
-    const int row = rt.m0 + r;
-    return row < rt.m_end ? a + (size_t)row * F : nullptr;
-  }, tid);
-  lb.init([&](int n) -> const uint16_t* {
-    return nb + n < d ? Wd + (size_t)(nb + n) * F : nullptr;
-  }, tid);
-  f32x16_t acc[TL::TM][TL::TN];
-  mainloop<TL>(la, lb, 0, F, smem, acc);
-  const int lane = tid & 63, wave = tid >> 6, wm = wave / WGN, wn = wave % WGN;
-#pragma unroll
-  for (int j = 0; j < TL::TN; ++j) {
-    const int col = nb + wn * TL::WTN + j * 32 + (lane & 31);
-    if (col >= d) continue;
-#pragma unroll
-    for (int i = 0; i < TL::TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = rt.m0 + wm * TL::WTM + i * 32 + out_row(lane, r);
-        if (row < rt.m_end) yp[(size_t)row * d + col] = f2bf(acc[i][j][r]);
-      }
+  for (int j = threadIdx.x; j <= E_l; j += blockDim.x) {
+    s_to[j] = tile_offsets[j];
+    s_off[j] = offsets[j];
+  }
+  __syncthreads();
+  for (Sched sc(s_to[E_l] * n_tiles); sc.t < sc.end; sc.t += sc.step) {
+    int e, m0, m_end;
+    row_tile(s_to, s_off, E_l, sc.t / n_tiles, e, m0, m_end);
+    op.template run<TL>(e, m0, m_end, sc.t % n_tiles, smem);
   }
 }
 
-// ---------------------------------------------------------------------------
-// dgrad GEMM A: da = dy_p . W_down[e]  (A: dy_p rows, K = d; B: W_down[e] as
-// [K = d][N = F], contiguous along N) with the SwiGLU backward epilogue.
-// ---------------------------------------------------------------------------
-template <int BM, int BN, int WGM, int WGN>
-__global__ __launch_bounds__(64 * WGM * WGN) void dgrad_act_kernel(
-    const uint16_t* __restrict__ dyp, const uint16_t* __restrict__ hbuf,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_offsets,
-    const uint16_t* __restrict__ W_down, uint16_t* __restrict__ dh, int E_l, int d, int F,
-    int n_tiles) {
-  using TL = Tile<BM, BN, WGM, WGN>;
-  static_assert(BM == kTileM, "row tiles come from the dispatch plan");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[TL::LDS_ELEMS];
-  __shared__ int s_to[257], s_off[257];
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int mt = lid / n_tiles, nt = lid % n_tiles;
-  RowTile rt;
-  if (!row_tile(offsets, tile_offsets, E_l, mt, s_to, s_off, rt)) return;
-  const int tid = threadIdx.x;
-  const int nb = nt * BN;
-  const uint16_t* Wd = W_down + (size_t)rt.e * d * F;
-  LoadK<BM, TL::NT> la;
-  LoadMN<BN, TL::NT> lb;
-  la.init([&](int r) -> const uint16_t* {
-    const int row = rt.m0 + r;
-    return row < rt.m_end ? dyp + (size_t)row * d : nullptr;
-  }, tid);
-  lb.init([&](int c) -> const uint16_t* { return nb + c < F ? Wd + nb + c : nullptr; },
-          (long)F, tid);
-  f32x16_t acc[TL::TM][TL::TN];
-  mainloop<TL>(la, lb, 0, d, smem, acc);
-  const int lane = tid & 63, wave = tid >> 6, wm = wave / WGN, wn = wave % WGN;
-#pragma unroll
-  for (int j = 0; j < TL::TN; ++j) {
-    const int col = nb + wn * TL::WTN + j * 32 + (lane & 31);
-    if (col >= F) continue;
+// forward GEMM1: [g, u] = xp . W_gu[e]^T with the SwiGLU epilogue.  The B tile
+// pairs gate and up rows: wave wn's 64 tile rows are 32 gate rows j and the 32
+// up rows F + j of the same j, so each lane holds g and u of one output.
+struct GateUpOp {
+  const uint16_t* xp;
+  const uint16_t* W_gu;
+  uint16_t* h;
+  uint16_t* a;
+  int d, F;
+  template <class TL>
+  __device__ __forceinline__ void run(int e, int m0, int m_end, int nt, uint16_t* smem) const {
+    static_assert(TL::WTN == 64, "each wave pairs 32 gate with 32 up columns");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / TL::WGN, wn = wave % TL::WGN;
+    const int jb = nt * (TL::BN / 2);
+    const uint16_t* Wg = W_gu + (size_t)e * 2 * F * d;
+    LoadK<TL::BM, TL::NT> la;
+    LoadK<TL::BN, TL::NT> lb;
+    la.init([&](int r) { return xp + (size_t)min(m0 + r, m_end - 1) * d; }, tid);
+    lb.init([&](int n) {
+      const int j = min(jb + (n >> 6) * 32 + (n & 31), F - 1);
+      return Wg + (size_t)(((n >> 5) & 1) * F + j) * d;
+    }, tid);
+    f32x16_t acc[TL::TM][TL::TN];
+    mainloop<TL>(la, lb, 0, d, smem, acc);
+    const int j = jb + wn * 32 + (lane & 31);
+    if (j >= F) return;
 #pragma unroll
     for (int i = 0; i < TL::TM; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = rt.m0 + wm * TL::WTM + i * 32 + out_row(lane, r);
-        if (row < rt.m_end) {
-          const float da = acc[i][j][r];
-          const float g = bf2f(hbuf[(size_t)row * 2 * F + col]);
-          const float u = bf2f(hbuf[(size_t)row * 2 * F + F + col]);
-          const float s = sigmoid_f(g);
-          dh[(size_t)row * 2 * F + col] = f2bf(da * u * s * (1.0f + g * (1.0f - s)));
-          dh[(size_t)row * 2 * F + F + col] = f2bf(da * g * s);
+        const int row = m0 + wm * TL::WTM + i * 32 + out_row(lane, r);
+        if (row < m_end) {
+          const float g = acc[i][0][r], u = acc[i][1][r];
+          h[(size_t)row * 2 * F + j] = f2bf(g);
+          h[(size_t)row * 2 * F + F + j] = f2bf(u);
+          a[(size_t)row * F + j] = f2bf(silu_f(g) * u);
         }
       }
   }
-}
+};
 
-// ---------------------------------------------------------------------------
-// dgrad GEMM B: dxp = dh . W_gu[e]  (A: dh rows, K = 2F; B: W_gu[e] as
-// [K = 2F][N = d], contiguous along N)
-// ---------------------------------------------------------------------------
-template <int BM, int BN, int WGM, int WGN>
-__global__ __launch_bounds__(64 * WGM * WGN) void dgrad_in_kernel(
-    const uint16_t* __restrict__ dh, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ tile_offsets, const uint16_t* __restrict__ W_gu,
-    uint16_t* __restrict__ dxp, int E_l, int d, int F, int n_tiles) {
-  using TL = Tile<BM, BN, WGM, WGN>;
-  static_assert(BM == kTileM, "row tiles come from the dispatch plan");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[TL::LDS_ELEMS];
-  __shared__ int s_to[257], s_off[257];
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int mt = lid / n_tiles, nt = lid % n_tiles;
-  RowTile rt;
-  if (!row_tile(offsets, tile_offsets, E_l, mt, s_to, s_off, rt)) return;
-  const int tid = threadIdx.x;
-  const int nb = nt * BN;
-  const uint16_t* Wg = W_gu + (size_t)rt.e * 2 * F * d;
-  LoadK<BM, TL::NT> la;
-  LoadMN<BN, TL::NT> lb;
-  la.init([&](int r) -> const uint16_t* {
-    const int row = rt.m0 + r;
-    return row < rt.m_end ? dh + (size_t)row * 2 * F : nullptr;
-  }, tid);
-  lb.init([&](int c) -> const uint16_t* { return nb + c < d ? Wg + nb + c : nullptr; },
-          (long)d, tid);
-  f32x16_t acc[TL::TM][TL::TN];
-  mainloop<TL>(la, lb, 0, 2 * F, smem, acc);
-  const int lane = tid & 63, wave = tid >> 6, wm = wave / WGN, wn = wave % WGN;
+// forward GEMM2: y_p = a . W_down[e]^T  (A: a rows, K = F; B: W_down rows, K = F)
+struct DownOp {
+  const uint16_t* a;
+  const uint16_t* W_down;
+  uint16_t* yp;
+  int d, F;
+  template <class TL>
+  __device__ __forceinline__ void run(int e, int m0, int m_end, int nt, uint16_t* smem) const {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / TL::WGN, wn = wave % TL::WGN;
+    const int nb = nt * TL::BN;
+    const uint16_t* Wd = W_down + (size_t)e * d * F;
+    LoadK<TL::BM, TL::NT> la;
+    LoadK<TL::BN, TL::NT> lb;
+    la.init([&](int r) { return a + (size_t)min(m0 + r, m_end - 1) * F; }, tid);
+    lb.init([&](int n) { return Wd + (size_t)min(nb + n, d - 1) * F; }, tid);
+    f32x16_t acc[TL::TM][TL::TN];
+    mainloop<TL>(la, lb, 0, F, smem, acc);
 #pragma unroll
-  for (int j = 0; j < TL::TN; ++j) {
-    const int col = nb + wn * TL::WTN + j * 32 + (lane & 31);
-    if (col >= d) continue;
+    for (int j = 0; j < TL::TN; ++j) {
+      const int col = nb + wn * TL::WTN + j * 32 + (lane & 31);
+      if (col >= d) continue;
 #pragma unroll
-    for (int i = 0; i < TL::TM; ++i)
+      for (int i = 0; i < TL::TM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = rt.m0 + wm * TL::WTM + i * 32 + out_row(lane, r);
-        if (row < rt.m_end) dxp[(size_t)row * d + col] = f2bf(acc[i][j][r]);
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * TL::WTM + i * 32 + out_row(lane, r);
+          if (row < m_end) yp[(size_t)row * d + col] = f2bf(acc[i][j][r]);
+        }
+    }
   }
-}
+};
+
+// dgrad GEMM A: da = dy_p . W_down[e]  (A: dy_p rows, K = d; B: W_down[e]
+// transposed, W_downT[e] [F][d], K-contiguous) with the SwiGLU backward epilogue.
+struct DgradActOp {
+  const uint16_t* dyp;
+  const uint16_t* hbuf;
+  const uint16_t* W_downT;
+  uint16_t* dh;
+  int d, F;
+  template <class TL>
+  __device__ __forceinline__ void run(int e, int m0, int m_end, int nt, uint16_t* smem) const {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / TL::WGN, wn = wave % TL::WGN;
+    const int nb = nt * TL::BN;
+    const uint16_t* WdT = W_downT + (size_t)e * F * d;
+    LoadK<TL::BM, TL::NT> la;
+    LoadK<TL::BN, TL::NT> lb;
+    la.init([&](int r) { return dyp + (size_t)min(m0 + r, m_end - 1) * d; }, tid);
+    lb.init([&](int n) { return WdT + (size_t)min(nb + n, F - 1) * d; }, tid);
+    f32x16_t acc[TL::TM][TL::TN];
+    mainloop<TL>(la, lb, 0, d, smem, acc);
+#pragma unroll
+    for (int j = 0; j < TL::TN; ++j) {
+      const int col = nb + wn * TL::WTN + j * 32 + (lane & 31);
+      if (col >= F) continue;
+#pragma unroll
+      for (int i = 0; i < TL::TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * TL::WTM + i * 32 + out_row(lane, r);
+          if (row < m_end) {
+            const float da = acc[i][j][r];
+            const float g = bf2f(hbuf[(size_t)row * 2 * F + col]);
+            const float u = bf2f(hbuf[(size_t)row * 2 * F + F + col]);
+            const float s = sigmoid_f(g);
+            dh[(size_t)row * 2 * F + col] = f2bf(da * u * s * (1.0f + g * (1.0f - s)));
+            dh[(size_t)row * 2 * F + F + col] = f2bf(da * g * s);
+          }
+        }
+    }
+  }
+};
+
+// dgrad GEMM B: dxp = dh . W_gu[e]  (A: dh rows, K = 2F; B: W_gu[e]
+// transposed, W_guT[e] [d][2F], K-contiguous)
+struct DgradInOp {
+  const uint16_t* dh;
+  const uint16_t* W_guT;
+  uint16_t* dxp;
+  int d, F;
+  template <class TL>
+  __device__ __forceinline__ void run(int e, int m0, int m_end, int nt, uint16_t* smem) const {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / TL::WGN, wn = wave % TL::WGN;
+    const int nb = nt * TL::BN;
+    const uint16_t* WgT = W_guT + (size_t)e * d * 2 * F;
+    LoadK<TL::BM, TL::NT> la;
+    LoadK<TL::BN, TL::NT> lb;
+    la.init([&](int r) { return dh + (size_t)min(m0 + r, m_end - 1) * 2 * F; }, tid);
+    lb.init([&](int n) { return WgT + (size_t)min(nb + n, d - 1) * 2 * F; }, tid);
+    f32x16_t acc[TL::TM][TL::TN];
+    mainloop<TL>(la, lb, 0, 2 * F, smem, acc);
+#pragma unroll
+    for (int j = 0; j < TL::TN; ++j) {
+      const int col = nb + wn * TL::WTN + j * 32 + (lane & 31);
+      if (col >= d) continue;
+#pragma unroll
+      for (int i = 0; i < TL::TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * TL::WTM + i * 32 + out_row(lane, r);
+          if (row < m_end) dxp[(size_t)row * d + col] = f2bf(acc[i][j][r]);
+        }
+    }
+  }
+};
 
 // ---------------------------------------------------------------------------
 // wgrad: per local expert e over its rows [offsets[e], offsets[e+1]):
@@ -428,66 +461,66 @@ __global__ __launch_bounds__(64 * WGM * WGN) void dgrad_in_kernel(
 // Both operands are contiguous along M/N (reduction over rows).  One launch
 // covers both products of every expert; tiles of one expert are consecutive.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WGM, int WGN>
-__global__ __launch_bounds__(64 * WGM * WGN) void wgrad_kernel(
+template <class TL>
+__global__ __launch_bounds__(TL::NT) void wgrad_kernel(
     const uint16_t* __restrict__ xp, const uint16_t* __restrict__ abuf,
     const uint16_t* __restrict__ dh, const uint16_t* __restrict__ dyp,
     const int32_t* __restrict__ offsets, float* __restrict__ dW_gu,
-    float* __restrict__ dW_down, int d, int F, int accumulate) {
-  using TL = Tile<BM, BN, WGM, WGN>;
+    float* __restrict__ dW_down, int E_l, int d, int F, int accumulate) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[TL::LDS_ELEMS];
-  const int tdm = (d + BM - 1) / BM, tdn = (F + BN - 1) / BN;
-  const int tgm = (2 * F + BM - 1) / BM, tgn = (d + BN - 1) / BN;
+  const int tdm = (d + TL::BM - 1) / TL::BM, tdn = (F + TL::BN - 1) / TL::BN;
+  const int tgm = (2 * F + TL::BM - 1) / TL::BM, tgn = (d + TL::BN - 1) / TL::BN;
   const int per_e = tdm * tdn + tgm * tgn;
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int e = lid / per_e;
-  int t = lid % per_e;
-  const int r0 = offsets[e], r1 = offsets[e + 1];
-  const uint16_t *Asrc, *Bsrc;
-  int M, N, m0, n0;
-  float* out;
-  if (t < tdm * tdn) {
-    Asrc = dyp;
-    Bsrc = abuf;
-    M = d;
-    N = F;
-    m0 = (t / tdn) * BM;
-    n0 = (t % tdn) * BN;
-    out = dW_down + (size_t)e * d * F;
-  } else {
-    t -= tdm * tdn;
-    Asrc = dh;
-    Bsrc = xp;
-    M = 2 * F;
-    N = d;
-    m0 = (t / tgn) * BM;
-    n0 = (t % tgn) * BN;
-    out = dW_gu + (size_t)e * 2 * F * d;
-  }
-  const int tid = threadIdx.x;
-  LoadMN<BM, TL::NT> la;
-  LoadMN<BN, TL::NT> lb;
-  la.init([&](int c) -> const uint16_t* { return m0 + c < M ? Asrc + m0 + c : nullptr; },
-          (long)M, tid);
-  lb.init([&](int c) -> const uint16_t* { return n0 + c < N ? Bsrc + n0 + c : nullptr; },
-          (long)N, tid);
-  f32x16_t acc[TL::TM][TL::TN];
-  mainloop<TL>(la, lb, r0, r1, smem, acc);
-  const int lane = tid & 63, wave = tid >> 6, wm = wave / WGN, wn = wave % WGN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / TL::WGN, wn = wave % TL::WGN;
+  for (Sched sc(E_l * per_e); sc.t < sc.end; sc.t += sc.step) {
+    const int e = sc.t / per_e;
+    int t = sc.t % per_e;
+    const int r0 = offsets[e], r1 = offsets[e + 1];
+    const uint16_t *Asrc, *Bsrc;
+    int M, N, m0, n0;
+    float* out;
+    if (t < tdm * tdn) {
+      Asrc = dyp;
+      Bsrc = abuf;
+      M = d;
+      N = F;
+      m0 = (t / tdn) * TL::BM;
+      n0 = (t % tdn) * TL::BN;
+      out = dW_down + (size_t)e * d * F;
+    } else {
+      t -= tdm * tdn;
+      Asrc = dh;
+      Bsrc = xp;
+      M = 2 * F;
+      N = d;
+      m0 = (t / tgn) * TL::BM;
+      n0 = (t % tgn) * TL::BN;
+      out = dW_gu + (size_t)e * 2 * F * d;
+    }
+    LoadMN<TL::BM, TL::NT> la;
+    LoadMN<TL::BN, TL::NT> lb;
+    la.init([&](int c) { return Asrc + min(m0 + c, M - 4); }, [&](int c) { return m0 + c < M; },
+            (long)M, tid);
+    lb.init([&](int c) { return Bsrc + min(n0 + c, N - 4); }, [&](int c) { return n0 + c < N; },
+            (long)N, tid);
+    f32x16_t acc[TL::TM][TL::TN];
+    mainloop<TL, decltype(la), decltype(lb), false>(la, lb, r0, r1, smem, acc);
 #pragma unroll
-  for (int j = 0; j < TL::TN; ++j) {
-    const int col = n0 + wn * TL::WTN + j * 32 + (lane & 31);
-    if (col >= N) continue;
+    for (int j = 0; j < TL::TN; ++j) {
+      const int col = n0 + wn * TL::WTN + j * 32 + (lane & 31);
+      if (col >= N) continue;
 #pragma unroll
-    for (int i = 0; i < TL::TM; ++i)
+      for (int i = 0; i < TL::TM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * TL::WTM + i * 32 + out_row(lane, r);
-        if (row < M) {
-          float* o = out + (size_t)row * N + col;
-          *o = accumulate ? *o + acc[i][j][r] : acc[i][j][r];
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * TL::WTM + i * 32 + out_row(lane, r);
+          if (row < M) {
+            float* o = out + (size_t)row * N + col;
+            *o = accumulate ? *o + acc[i][j][r] : acc[i][j][r];
+          }
         }
-      }
+    }
   }
 }
 
@@ -495,39 +528,65 @@ __global__ __launch_bounds__(64 * WGM * WGN) void wgrad_kernel(
 // router logits: l = x . W_r + bias with W_r given transposed (W_rT [E][d]),
 // float32 output.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WGM, int WGN>
-__global__ __launch_bounds__(64 * WGM * WGN) void router_kernel(
+template <class TL>
+__global__ __launch_bounds__(TL::NT) void router_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W_rT,
     const float* __restrict__ bias, float* __restrict__ logits, int T, int d, int E,
-    int n_tiles) {
-  using TL = Tile<BM, BN, WGM, WGN>;
+    int n_tiles, int m_tiles) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[TL::LDS_ELEMS];
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int m0 = (lid / n_tiles) * BM, n0 = (lid % n_tiles) * BN;
-  const int tid = threadIdx.x;
-  LoadK<BM, TL::NT> la;
-  LoadK<BN, TL::NT> lb;
-  la.init([&](int r) -> const uint16_t* {
-    return m0 + r < T ? x + (size_t)(m0 + r) * d : nullptr;
-  }, tid);
-  lb.init([&](int n) -> const uint16_t* {
-    return n0 + n < E ? W_rT + (size_t)(n0 + n) * d : nullptr;
-  }, tid);
-  f32x16_t acc[TL::TM][TL::TN];
-  mainloop<TL>(la, lb, 0, d, smem, acc);
-  const int lane = tid & 63, wave = tid >> 6, wm = wave / WGN, wn = wave % WGN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / TL::WGN, wn = wave % TL::WGN;
+  for (Sched sc(m_tiles * n_tiles); sc.t < sc.end; sc.t += sc.step) {
+    const int m0 = (sc.t / n_tiles) * TL::BM, n0 = (sc.t % n_tiles) * TL::BN;
+    LoadK<TL::BM, TL::NT> la;
+    LoadK<TL::BN, TL::NT> lb;
+    la.init([&](int r) { return x + (size_t)min(m0 + r, T - 1) * d; }, tid);
+    lb.init([&](int n) { return W_rT + (size_t)min(n0 + n, E - 1) * d; }, tid);
+    f32x16_t acc[TL::TM][TL::TN];
+    mainloop<TL>(la, lb, 0, d, smem, acc);
 #pragma unroll
-  for (int j = 0; j < TL::TN; ++j) {
-    const int col = n0 + wn * TL::WTN + j * 32 + (lane & 31);
-    if (col >= E) continue;
-    const float b = bias ? bias[col] : 0.f;
+    for (int j = 0; j < TL::TN; ++j) {
+      const int col = n0 + wn * TL::WTN + j * 32 + (lane & 31);
+      if (col >= E) continue;
+      const float b = bias ? bias[col] : 0.f;
 #pragma unroll
-    for (int i = 0; i < TL::TM; ++i)
+      for (int i = 0; i < TL::TM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * TL::WTM + i * 32 + out_row(lane, r);
-        if (row < T) logits[(size_t)row * E + col] = acc[i][j][r] + b;
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * TL::WTM + i * 32 + out_row(lane, r);
+          if (row < T) logits[(size_t)row * E + col] = acc[i][j][r] + b;
+        }
+    }
+  }
+}
+
+// out[b] = in[b]^T for a batch of R x C bf16 matrices (R, C multiples of 64):
+// 64 x 64 tiles through LDS, 16-byte global accesses on both sides.
+__global__ __launch_bounds__(256) void transpose_batched_kernel(const uint16_t* __restrict__ in,
+                                                                uint16_t* __restrict__ out, int R,
+                                                                int C) {
+  __shared__ uint16_t t[64][64 + 2];
+  const size_t mat = (size_t)blockIdx.z * R * C;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  for (int q = threadIdx.x; q < 512; q += 256) {
+    const int rr = q >> 3, cc = (q & 7) * 8;
+    const uint4 v = *(const uint4*)(in + mat + (size_t)(r0 + rr) * C + c0 + cc);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      t[rr][cc + 2 * i] = (uint16_t)(w[i] & 0xffffu);
+      t[rr][cc + 2 * i + 1] = (uint16_t)(w[i] >> 16);
+    }
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < 512; q += 256) {
+    const int cc = q >> 3, rr = (q & 7) * 8;
+    uint4 v;
+    v.x = t[rr + 0][cc] | ((uint32_t)t[rr + 1][cc] << 16);
+    v.y = t[rr + 2][cc] | ((uint32_t)t[rr + 3][cc] << 16);
+    v.z = t[rr + 4][cc] | ((uint32_t)t[rr + 5][cc] << 16);
+    v.w = t[rr + 6][cc] | ((uint32_t)t[rr + 7][cc] << 16);
+    *(uint4*)(out + mat + (size_t)(c0 + cc) * R + r0 + rr) = v;
   }
 }
 
@@ -535,6 +594,34 @@ __global__ __launch_bounds__(64 * WGM * WGN) void router_kernel(
 inline int max_row_tiles(const moe_shape* s) {
   const int64_t cap = s->T * s->K;
   return (int)((cap + s->E_l * (int64_t)(kTileM - 1)) / kTileM);
+}
+
+// Persistent grid: one block per CU of the current device (at most `tiles`).
+inline int persistent_grid(long tiles) {
+  static int ncu[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (ncu[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    ncu[dev] = n;
+  }
+  return (int)(tiles < ncu[dev] ? (tiles > 0 ? tiles : 1) : ncu[dev]);
+}
+
+template <class TL = T256, class Op>
+int launch_row_grouped(const char* name, const moe_shape* s, const Op& op,
+                       const int32_t* offsets, const int32_t* tile_offsets, int n_tiles,
+                       hipStream_t st) {
+  const long tiles = (long)max_row_tiles(s) * n_tiles;
+  if (tiles == 0) return MOE_OK;
+  const int grid = persistent_grid(tiles);
+  MOE_LAUNCH(name, st,
+             row_grouped_kernel<TL, Op><<<grid, TL::NT, 0, st>>>(
+                 op, offsets, tile_offsets, (int)s->E_l, n_tiles));
+  return check_launch(name);
 }
 
 }  // namespace
@@ -545,72 +632,64 @@ inline int max_row_tiles(const moe_shape* s) {
 int launch_ffn_fwd_bf16(const moe_shape* s, const void* xp, const int32_t* offsets,
                         const int32_t* tile_offsets, const void* W_gu, const void* W_down,
                         void* h, void* a, void* yp, hipStream_t st) {
-  const int d = (int)s->d, F = (int)s->F, E_l = (int)s->E_l;
-  const int mt = max_row_tiles(s);
-  if (mt == 0) return MOE_OK;
-  {
-    const int nt = (F + 127) / 128;
-    MOE_LAUNCH("ffn_gate_up", st,
-               ffn_gate_up_kernel<256, 256, 2, 4><<<mt * nt, 512, 0, st>>>(
-        (const uint16_t*)xp, offsets, tile_offsets, (const uint16_t*)W_gu, (uint16_t*)h,
-        (uint16_t*)a, E_l, d, F, nt));
-    if (int rc = check_launch("expert GEMM1 (gate/up + SwiGLU)")) return rc;
-  }
-  {
-    const int nt = (d + 255) / 256;
-    MOE_LAUNCH("ffn_down", st,
-               ffn_down_kernel<256, 256, 2, 4><<<mt * nt, 512, 0, st>>>(
-        (const uint16_t*)a, offsets, tile_offsets, (const uint16_t*)W_down, (uint16_t*)yp, E_l,
-        d, F, nt));
-    if (int rc = check_launch("expert GEMM2 (down)")) return rc;
-  }
-  return MOE_OK;
+  const int d = (int)s->d, F = (int)s->F;
+  GateUpOp g{(const uint16_t*)xp, (const uint16_t*)W_gu, (uint16_t*)h, (uint16_t*)a, d, F};
+  if (int rc = launch_row_grouped("ffn_gate_up", s, g, offsets, tile_offsets,
+                                  (F + T256::BN / 2 - 1) / (T256::BN / 2), st))
+    return rc;
+  DownOp dn{(const uint16_t*)a, (const uint16_t*)W_down, (uint16_t*)yp, d, F};
+  return launch_row_grouped("ffn_down", s, dn, offsets, tile_offsets,
+                            (d + T256::BN - 1) / T256::BN, st);
 }
 
 int launch_ffn_dgrad_bf16(const moe_shape* s, const void* dyp, const void* h,
                           const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
-                          const void* W_down, void* dh, void* dxp, hipStream_t st) {
+                          const void* W_down, void* dh, void* dxp, void* ws, hipStream_t st) {
   const int d = (int)s->d, F = (int)s->F, E_l = (int)s->E_l;
-  const int mt = max_row_tiles(s);
-  if (mt == 0) return MOE_OK;
-  {
-    const int nt = (F + 255) / 256;
-    MOE_LAUNCH("dgrad_act", st,
-               dgrad_act_kernel<256, 256, 2, 4><<<mt * nt, 512, 0, st>>>(
-        (const uint16_t*)dyp, (const uint16_t*)h, offsets, tile_offsets,
-        (const uint16_t*)W_down, (uint16_t*)dh, E_l, d, F, nt));
-    if (int rc = check_launch("dgrad GEMM (activation)")) return rc;
-  }
-  {
-    const int nt = (d + 255) / 256;
-    MOE_LAUNCH("dgrad_in", st,
-               dgrad_in_kernel<256, 256, 2, 4><<<mt * nt, 512, 0, st>>>(
-        (const uint16_t*)dh, offsets, tile_offsets, (const uint16_t*)W_gu, (uint16_t*)dxp, E_l,
-        d, F, nt));
-    if (int rc = check_launch("dgrad GEMM (input)")) return rc;
-  }
-  return MOE_OK;
+  // K-contiguous copies of the weights: W_downT[e] = W_down[e]^T [F][d],
+  // W_guT[e] = W_gu[e]^T [d][2F]
+  uint16_t* W_downT = (uint16_t*)ws;
+  uint16_t* W_guT = (uint16_t*)((char*)ws + ws_wT_down_bytes(s));
+  MOE_LAUNCH("transpose_w", st,
+             transpose_batched_kernel<<<dim3(F / 64, d / 64, E_l), 256, 0, st>>>(
+                 (const uint16_t*)W_down, W_downT, d, F));
+  if (int rc = check_launch("transpose W_down")) return rc;
+  MOE_LAUNCH("transpose_w", st,
+             transpose_batched_kernel<<<dim3(d / 64, 2 * F / 64, E_l), 256, 0, st>>>(
+                 (const uint16_t*)W_gu, W_guT, 2 * F, d));
+  if (int rc = check_launch("transpose W_gu")) return rc;
+  DgradActOp da{(const uint16_t*)dyp, (const uint16_t*)h, W_downT, (uint16_t*)dh, d, F};
+  if (int rc = launch_row_grouped("dgrad_act", s, da, offsets, tile_offsets,
+                                  (F + T256::BN - 1) / T256::BN, st))
+    return rc;
+  DgradInOp di{(const uint16_t*)dh, W_guT, (uint16_t*)dxp, d, F};
+  return launch_row_grouped("dgrad_in", s, di, offsets, tile_offsets,
+                            (d + T256::BN - 1) / T256::BN, st);
 }
 
 int launch_ffn_wgrad_bf16(const moe_shape* s, const void* xp, const void* a, const void* dh,
                           const void* dyp, const int32_t* offsets, float* dW_gu, float* dW_down,
                           bool accumulate, hipStream_t st) {
   const int d = (int)s->d, F = (int)s->F, E_l = (int)s->E_l;
-  const int per_e = ((d + 255) / 256) * ((F + 255) / 256) + ((2 * F + 255) / 256) * ((d + 255) / 256);
+  const long per_e = (long)((d + 255) / 256) * ((F + 255) / 256) +
+                     (long)((2 * F + 255) / 256) * ((d + 255) / 256);
+  const int grid = persistent_grid(E_l * per_e);
   MOE_LAUNCH("wgrad", st,
-             wgrad_kernel<256, 256, 2, 4><<<E_l * per_e, 512, 0, st>>>(
-      (const uint16_t*)xp, (const uint16_t*)a, (const uint16_t*)dh, (const uint16_t*)dyp, offsets,
-      dW_gu, dW_down, d, F, accumulate ? 1 : 0));
+             wgrad_kernel<T256><<<grid, T256::NT, 0, st>>>(
+                 (const uint16_t*)xp, (const uint16_t*)a, (const uint16_t*)dh,
+                 (const uint16_t*)dyp, offsets, dW_gu, dW_down, E_l, d, F, accumulate ? 1 : 0));
   return check_launch("wgrad GEMM");
 }
 
 int launch_router_logits_bf16(const moe_shape* s, const void* x, const void* W_rT,
                               const float* bias, float* logits, hipStream_t st) {
+  using TR = Tile<128, 128, 2, 2>;
   const int T = (int)s->T, d = (int)s->d, E = (int)s->E;
-  const int nt = (E + 127) / 128, mt = (T + 127) / 128;
+  const int nt = (E + TR::BN - 1) / TR::BN, mt = (T + TR::BM - 1) / TR::BM;
+  const int grid = persistent_grid((long)mt * nt);
   MOE_LAUNCH("router", st,
-             router_kernel<128, 128, 2, 2><<<mt * nt, 256, 0, st>>>(
-      (const uint16_t*)x, (const uint16_t*)W_rT, bias, logits, T, d, E, nt));
+             router_kernel<TR><<<grid, TR::NT, 0, st>>>((const uint16_t*)x, (const uint16_t*)W_rT,
+                                                        bias, logits, T, d, E, nt, mt));
   return check_launch("router GEMM");
 }
 

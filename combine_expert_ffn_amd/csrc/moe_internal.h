@@ -130,6 +130,15 @@ inline size_t ws_router_partial_bytes(const moe_shape* s) {
   int64_t nc = cdiv(s->T, kRouterChunk);
   return align_up((size_t)(nc * s->d * s->E) * sizeof(float), 256);
 }
+// Transposed expert weights for the bf16 dgrad: W_downT [E_l][F][d] then
+// W_guT [E_l][d][2F] (bf16).  The float32 dgrad needs none.
+inline size_t ws_wT_down_bytes(const moe_shape* s) {
+  return s->dtype == MOE_BF16 ? align_up((size_t)(s->E_l * s->F * s->d) * 2, 256) : 0;
+}
+inline size_t ws_wT_bytes(const moe_shape* s) {
+  return s->dtype == MOE_BF16 ? ws_wT_down_bytes(s) + align_up((size_t)(s->E_l * 2 * s->F * s->d) * 2, 256)
+                              : 0;
+}
 
 // ---------------------------------------------------------------------------
 // launchers (each returns MOE_OK or MOE_ERR_HIP)
@@ -163,7 +172,7 @@ int launch_ffn_fwd(const moe_shape* s, const void* xp, const int32_t* offsets,
                    void* a, void* yp, hipStream_t st);
 int launch_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h, const int32_t* offsets,
                      const int32_t* tile_offsets, const void* W_gu, const void* W_down, void* dh,
-                     void* dxp, hipStream_t st);
+                     void* dxp, void* ws, hipStream_t st);
 int launch_ffn_wgrad(const moe_shape* s, const void* xp, const void* a, const void* dh,
                      const void* dyp, const int32_t* offsets, float* dW_gu, float* dW_down,
                      bool accumulate, hipStream_t st);

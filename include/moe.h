@@ -178,11 +178,13 @@ int moe_combine_bwd(const moe_shape* s, const void* dout, const void* yp,
  *   da = dyp . W_down[j];  with g, u from h and s = sigmoid(g):
  *   dg = da*u*s*(1 + g*(1-s)),  du = da*g*s;  dh = [dg, du];  dxp = dh . W_gu[j]
  *   dh [T*K,2F] out, dxp [T*K,d] out (dtype).
+ *   ws/ws_bytes: workspace (bf16: the call stores transposed copies of W_down
+ *   and W_gu there, so both products read K-contiguous operands).
  */
 int moe_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h,
                   const int32_t* offsets, const int32_t* tile_offsets,
                   const void* W_gu, const void* W_down, void* dh, void* dxp,
-                  hipStream_t stream);
+                  void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * moe_ffn_wgrad - the W of the W/D split, deferrable (page 1,

@@ -82,7 +82,9 @@ def test_null_pointers_rejected():
     assert L.moe_expert_ffn_fwd(C.byref(s), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
                                 None) == M.MOE_ERR_NULL
     assert L.moe_ffn_dgrad(C.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
-                           None) == M.MOE_ERR_NULL
+                           FAKE, 1 << 30, None) == M.MOE_ERR_NULL
+    assert L.moe_ffn_dgrad(C.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                           FAKE, 16, None) == M.MOE_ERR_WORKSPACE
     assert L.moe_ffn_wgrad(C.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
                            None) == M.MOE_ERR_NULL
     # TOPK routing needs x, W_r, logits, gates

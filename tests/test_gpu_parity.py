@@ -155,7 +155,7 @@ def test_stage_parity(name):
     # ---- dgrad (oracle dy_p, h)
     dyp_r = D(_pad(refb["dyp"], cap))
     h_r = D(_pad(ref["h"], cap))
-    M.moe_ffn_dgrad(s, dyp_r, h_r, mb.offsets, mb.tile_offsets, W_gu, W_down, mb.dh, mb.dxp)
+    M.moe_ffn_dgrad(s, dyp_r, h_r, mb.offsets, mb.tile_offsets, W_gu, W_down, mb.dh, mb.dxp, ws)
     close("dh", host(mb.dh)[:N], refb["dh"], tau)
     close("dxp", host(mb.dxp)[:N], refb["dxp"], tau)
 
