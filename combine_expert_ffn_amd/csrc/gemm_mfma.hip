@@ -23,10 +23,10 @@
 //  * loads are branch free: rows or columns outside the matrix read a valid
 //    clamped address (their results are discarded, or replaced by zero where
 //    they would enter a sum);
-//  * an operand contiguous along K is copied 16 bytes at a time; an operand
-//    contiguous along M/N (both operands of wgrad) is read as 8 (k) x 4 (m)
-//    blocks and transposed in registers on its way to LDS.  dgrad reads its
-//    weights from K-contiguous transposed copies made at the start of the call.
+//  * operands contiguous along K are copied 16 bytes at a time; dgrad reads
+//    its weights from K-contiguous transposed copies made at the start of the
+//    call; wgrad, whose operands are contiguous along M/N, stages natural-layout
+//    tiles in LDS and transposes on the fragment read (see wgrad_kernel).
 // Row-grouped GEMMs (fwd, dgrad) take their (expert, M-tile) from the dispatch
 // plan's tile_offsets (tiles of kTileM rows).
 #include "moe_internal.h"
@@ -76,66 +76,6 @@ struct LoadK {
   __device__ __forceinline__ void store(uint16_t* lds) const {
 #pragma unroll
     for (int c = 0; c < CH; ++c) *(uint4*)(lds + dst[c]) = v[c];
-  }
-};
-
-// Operand contiguous along M/N: element (k, col) at base[k * ld + col].
-// Each unit is 8 consecutive k x 4 consecutive columns, transposed in
-// registers into four 16-byte K-chunks.  col_ok(c) tells whether the group of
-// 4 columns starting at c is inside the matrix; outside groups and rows
-// k >= k_end contribute zeros (their loads read a clamped valid address).
-template <int R, int NT>
-struct LoadMN {
-  static constexpr int U = 2 * R / NT;
-  static constexpr int NLOAD = 8 * U, NSTORE = 4 * U;
-  static_assert(U >= 1 && (2 * R) % NT == 0, "tile/threads mismatch");
-  const uint16_t* src[U];
-  bool ok[U];
-  int kg[U];
-  int dst_row[U];
-  long ld;
-  uint2 v[U][8];
-  template <class ColPtr, class ColOk>
-  __device__ __forceinline__ void init(ColPtr col_ptr, ColOk col_ok, long ld_, int tid) {
-    ld = ld_;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int q = u * NT + tid, mg = q % (R / 4);
-      kg[u] = q / (R / 4);
-      dst_row[u] = mg * 4;
-      ok[u] = col_ok(mg * 4);
-      src[u] = col_ptr(mg * 4);
-    }
-  }
-  __device__ __forceinline__ void load(int k0, int k_end) {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const int k = k0 + kg[u] * 8 + kk;
-        const uint2 w = *(const uint2*)(src[u] + (long)min(k, k_end - 1) * ld);
-        const bool take = ok[u] && k < k_end;
-        v[u][kk] = make_uint2(take ? w.x : 0u, take ? w.y : 0u);
-      }
-  }
-  __device__ __forceinline__ void store(uint16_t* lds) const {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t e[8];
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const uint32_t w = (i < 2) ? v[u][kk].x : v[u][kk].y;
-          e[kk] = (i & 1) ? (w >> 16) : (w & 0xffffu);
-        }
-        uint4 o;
-        o.x = e[0] | (e[1] << 16);
-        o.y = e[2] | (e[3] << 16);
-        o.z = e[4] | (e[5] << 16);
-        o.w = e[6] | (e[7] << 16);
-        *(uint4*)(lds + lds_off(dst_row[u] + i, kg[u])) = o;
-      }
   }
 };
 
@@ -458,21 +398,80 @@ struct DgradInOp {
 // wgrad: per local expert e over its rows [offsets[e], offsets[e+1]):
 //   dW_down[e] (d x F)  = dy_p^T . a      (A: dy_p, M = d;  B: a,  N = F)
 //   dW_gu[e]   (2F x d) = dh^T   . xp     (A: dh,   M = 2F; B: xp, N = d)
-// Both operands are contiguous along M/N (reduction over rows).  One launch
-// covers both products of every expert; tiles of one expert are consecutive.
+// Both operands are contiguous along M/N (the reduction runs over rows), so
+// each 64-row stage is copied straight into LDS in its natural [k][col]
+// layout (16-byte global loads, one 1 KiB LDS block per wave instruction)
+// and the MFMA operands, 8 consecutive k of one column per lane, are
+// assembled from two LDS transpose reads (ds_read_b64_tr_b16): within each
+// group of 16 lanes, lane s addresses row k0 + s/4 at columns c0 + 4*(s%4),
+// and lane t receives rows k0..k0+3 of column c0 + t.  Rows past the expert's
+// end and columns past the matrix read a zero row instead, so no masking is
+// needed.  One launch covers both products of every expert.
 // ---------------------------------------------------------------------------
-template <class TL>
-__global__ __launch_bounds__(TL::NT) void wgrad_kernel(
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+__device__ uint16_t g_zero_row[256];  // zero-initialised device memory
+
+constexpr int WG_ROWB = 256 * 2;  // bytes per LDS tile row (256 columns)
+
+// Physical 32-byte chunk of logical chunk c in tile row k: rows k..k+3 of a
+// transpose read land in distinct bank groups.
+__device__ __forceinline__ int wg_swz(int k) { return ((k & 3) << 1) | ((k >> 2) & 1); }
+__device__ __forceinline__ int wg_byte(int k, int col) {
+  return k * WG_ROWB + ((((col >> 4) ^ wg_swz(k)) & 15) << 5) + ((col & 15) << 1);
+}
+
+// Direct global -> LDS loader of a [64 k][256 col] tile.
+template <int NW>
+struct LoadKM {
+  static constexpr int PER = BK / 2 / NW;  // wave instructions per stage
+  const uint16_t* base;
+  long ld;
+  int M, m0, lane, w;
+  __device__ __forceinline__ void issue(uint8_t* lds, int k0, int k_end) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int blk = i * NW + w;
+      const int kr = blk * 2 + (lane >> 5);
+      const int s = lane & 31;
+      const int col = (((s >> 1) ^ wg_swz(kr)) & 15) * 16 + (s & 1) * 8;
+      const int k = k0 + kr;
+      const bool ok = (k < k_end) && (m0 + col < M);
+      const uint16_t* src = ok ? base + (long)k * ld + m0 + col : g_zero_row + col;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(lds + blk * 1024), 16, 0, 0);
+    }
+  }
+};
+
+// MFMA 32x32x16 operand for tile columns [cb, cb + 32) and k slice kk.
+__device__ __forceinline__ bf16x8_t frag_tr(const uint8_t* lds, int cb, int kk, int lane) {
+  const int g = lane >> 4, t = lane & 15;
+  const int col = cb + ((g & 1) << 4) + ((t & 3) << 2);
+  const int kr = kk * 16 + ((g >> 1) << 3) + (t >> 2);
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lds + wg_byte(kr, col)));
+  const i16x4_t hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lds + wg_byte(kr + 4, col)));
+  const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// 256 x 256 output tiles, 8 waves (2 x 4), wave tile 128 x 64.
+__global__ __launch_bounds__(512) void wgrad_kernel(
     const uint16_t* __restrict__ xp, const uint16_t* __restrict__ abuf,
     const uint16_t* __restrict__ dh, const uint16_t* __restrict__ dyp,
     const int32_t* __restrict__ offsets, float* __restrict__ dW_gu,
     float* __restrict__ dW_down, int E_l, int d, int F, int accumulate) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[TL::LDS_ELEMS];
-  const int tdm = (d + TL::BM - 1) / TL::BM, tdn = (F + TL::BN - 1) / TL::BN;
-  const int tgm = (2 * F + TL::BM - 1) / TL::BM, tgn = (d + TL::BN - 1) / TL::BN;
+  constexpr int NW = 8, WGN = 4, WTM = 128, WTN = 64, TM = 4, TN = 2;
+  constexpr int STAGE = 2 * BK * WG_ROWB;  // A + B tiles
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  const int tdm = (d + 255) / 256, tdn = (F + 255) / 256;
+  const int tgm = (2 * F + 255) / 256, tgn = (d + 255) / 256;
   const int per_e = tdm * tdn + tgm * tgn;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / TL::WGN, wn = wave % TL::WGN;
+  const int wm = wave / WGN, wn = wave % WGN;
   for (Sched sc(E_l * per_e); sc.t < sc.end; sc.t += sc.step) {
     const int e = sc.t / per_e;
     int t = sc.t % per_e;
@@ -485,8 +484,8 @@ __global__ __launch_bounds__(TL::NT) void wgrad_kernel(
       Bsrc = abuf;
       M = d;
       N = F;
-      m0 = (t / tdn) * TL::BM;
-      n0 = (t % tdn) * TL::BN;
+      m0 = (t / tdn) * 256;
+      n0 = (t % tdn) * 256;
       out = dW_down + (size_t)e * d * F;
     } else {
       t -= tdm * tdn;
@@ -494,27 +493,58 @@ __global__ __launch_bounds__(TL::NT) void wgrad_kernel(
       Bsrc = xp;
       M = 2 * F;
       N = d;
-      m0 = (t / tgn) * TL::BM;
-      n0 = (t % tgn) * TL::BN;
+      m0 = (t / tgn) * 256;
+      n0 = (t % tgn) * 256;
       out = dW_gu + (size_t)e * 2 * F * d;
     }
-    LoadMN<TL::BM, TL::NT> la;
-    LoadMN<TL::BN, TL::NT> lb;
-    la.init([&](int c) { return Asrc + min(m0 + c, M - 4); }, [&](int c) { return m0 + c < M; },
-            (long)M, tid);
-    lb.init([&](int c) { return Bsrc + min(n0 + c, N - 4); }, [&](int c) { return n0 + c < N; },
-            (long)N, tid);
-    f32x16_t acc[TL::TM][TL::TN];
-    mainloop<TL, decltype(la), decltype(lb), false>(la, lb, r0, r1, smem, acc);
+    const LoadKM<NW> la{Asrc, (long)M, M, m0, lane, wave};
+    const LoadKM<NW> lb{Bsrc, (long)N, N, n0, lane, wave};
+    f32x16_t acc[TM][TN];
 #pragma unroll
-    for (int j = 0; j < TL::TN; ++j) {
-      const int col = n0 + wn * TL::WTN + j * 32 + (lane & 31);
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    const int nk = (r1 - r0 + BK - 1) / BK;
+    if (nk > 0) {  // block-uniform
+      la.issue(smem, r0, r1);
+      lb.issue(smem + BK * WG_ROWB, r0, r1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      for (int kt = 0; kt < nk; ++kt) {
+        uint8_t* cur = smem + (kt & 1) * STAGE;
+        uint8_t* nxt = smem + ((kt + 1) & 1) * STAGE;
+        if (kt + 1 < nk) {
+          la.issue(nxt, r0 + (kt + 1) * BK, r1);
+          lb.issue(nxt + BK * WG_ROWB, r0 + (kt + 1) * BK, r1);
+        }
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+          bf16x8_t a[TM], b[TN];
+#pragma unroll
+          for (int i = 0; i < TM; ++i) a[i] = frag_tr(cur, wm * WTM + i * 32, kk, lane);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) b[j] = frag_tr(cur + BK * WG_ROWB, wn * WTN + j * 32, kk, lane);
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn * WTN + j * 32 + (lane & 31);
       if (col >= N) continue;
 #pragma unroll
-      for (int i = 0; i < TL::TM; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * TL::WTM + i * 32 + out_row(lane, r);
+          const int row = m0 + wm * WTM + i * 32 + out_row(lane, r);
           if (row < M) {
             float* o = out + (size_t)row * N + col;
             *o = accumulate ? *o + acc[i][j][r] : acc[i][j][r];
@@ -675,7 +705,7 @@ int launch_ffn_wgrad_bf16(const moe_shape* s, const void* xp, const void* a, con
                      (long)((2 * F + 255) / 256) * ((d + 255) / 256);
   const int grid = persistent_grid(E_l * per_e);
   MOE_LAUNCH("wgrad", st,
-             wgrad_kernel<T256><<<grid, T256::NT, 0, st>>>(
+             wgrad_kernel<<<grid, 512, 0, st>>>(
                  (const uint16_t*)xp, (const uint16_t*)a, (const uint16_t*)dh,
                  (const uint16_t*)dyp, offsets, dW_gu, dW_down, E_l, d, F, accumulate ? 1 : 0));
   return check_launch("wgrad GEMM");
