@@ -11,9 +11,10 @@ expert FFN, optionally with the expert weight gradient computed later) and the
 1F1B EP-overlap note (page 2, "MoE 1F1B overlap": the MLP backward split into
 activation gradient D before weight gradient W; "how the 8 ops are split": the
 backward chain combine -> mlp -> dispatch).  The pages do not spell out the
-routing function, the FFN type or the permutation order; the readings adopted
-for those (top-k softmax routing, SwiGLU experts, a stable counting-sort
-permutation) are listed with every other reading in the design doc.
+routing function, the FFN type or the permutation order; this oracle takes
+top-k softmax routing (gates renormalised over the chosen experts), SwiGLU
+experts and a stable counting-sort permutation (pairs in token-major order
+within each expert) as the plainest readings.
 
 Every function is numpy in float64.  Precision modes:
 
