@@ -24,6 +24,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
 
 GEMM_KERNELS = ("ffn_gate_up", "ffn_down", "dgrad_act", "dgrad_in", "wgrad")
+COPY_PROBE_BYTES = 1 << 30
+TRAFFIC_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
 
 
 def err(*a):
@@ -51,6 +53,42 @@ def algorithmic(w, N, T_loc):
         # dx_p rows + map -> dx
         "dispatch_bwd": ("byte", N * d * b + 4.0 * T * K + T * d * b),
     }
+
+
+KERNEL_SOURCE = {k: "gemm_mfma.hip" for k in GEMM_KERNELS}
+KERNEL_SOURCE.update({k: "dispatch.hip" for k in ("permute", "combine", "combine_bwd",
+                                                  "dispatch_bwd")})
+
+
+def kernel_source_hash(name):
+    """sha256 of the source that defines kernel `name` and the shared header."""
+    import hashlib
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "combine_expert_ffn_amd",
+                        "csrc")
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCE[name], "moe_internal.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload):
+    """Per-launch HBM bytes of each kernel from the committed counter summary
+    (rocprofv3 FETCH_SIZE and WRITE_SIZE, scaled by the copy probe), keeping
+    only kernels whose source is unchanged since the counters were taken."""
+    import re
+    path = os.path.join(TRAFFIC_DIR, f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return {}
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), flags=re.S)
+    if not m:
+        return {}
+    rec = json.loads(m.group(1))
+    out = {}
+    for name, ent in rec.get("kernels", {}).items():
+        if name in KERNEL_SOURCE and ent.get("source_sha256") == kernel_source_hash(name):
+            out[name] = ent["hbm_bytes_per_launch"]
+    return out
 
 
 def cpu_oracle_baseline(w, inp, target_s=10.0):
@@ -101,6 +139,10 @@ def main():
     ap.add_argument("--workload", default="ep16_rank_bf16")
     ap.add_argument("--tokens", type=int, default=None, help="override T of the workload")
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="run a few serialized steps and a copy probe of known size, print no "
+                         "JSON line: the program to run under rocprofv3 --pmc FETCH_SIZE / "
+                         "WRITE_SIZE for the per-kernel HBM traffic")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -153,6 +195,19 @@ def main():
         return i0 + n
 
     step(mbs[0], None, 0)  # prime: micro-batch 0 forwarded
+    if args.counter_pass:
+        run_loop(args.steps, M.MOE_STEP_SERIALIZE, 0)
+        # copy probe: a plain elementwise pass (negation) that reads and writes
+        # COPY_PROBE_BYTES each, larger than the last-level cache, so the
+        # counters' reading for it calibrates bytes per counted KiB
+        src = torch.ones(COPY_PROBE_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        err(f"[bench] counter pass done: {args.steps} serialized steps, 3 copy probes of "
+            f"{COPY_PROBE_BYTES} bytes")
+        return
     i = run_loop(args.warmup, 0, 0)
     torch.cuda.synchronize()
     counts = [mbs[k].counts.cpu() for k in range(2)]
@@ -193,6 +248,7 @@ def main():
 
     # ---- per-kernel achieved rates from the live kernel events
     work = algorithmic(w, N, T_loc)
+    traffic = stored_traffic(w.name) if args.tokens is None else {}
     kernels = {}
     for name, (tot_ms, n) in sorted(kern.items(), key=lambda kv: -kv[1][0]):
         avg_s = tot_ms / 1e3 / max(n, 1)
@@ -207,6 +263,8 @@ def main():
             else:
                 ach = amount / avg_s / 1e9
                 ent.update(achieved=round(ach, 1), unit="GB/s", frac=round(ach / PEAK_HBM_GBS, 4))
+        if name in traffic:
+            ent["traffic"] = traffic[name]
         kernels[name] = ent
         err(f"  {name:14s} {ent}")
 
@@ -218,7 +276,7 @@ def main():
     gemm_s = sum(kern[k][0] / 1e3 for k in gemm)
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(dom_ach, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dom_ach / PEAK_BF16_TFLOPS, 4),
-                "traffic": None,
+                "traffic": traffic.get(dom),
                 "algorithmic_per_launch": f"{work[dom][1]:.4g} flop",
                 "avg_launch_us": round(dom_avg_s * 1e6, 2)}
     disp = kernels.get("permute", {})
