@@ -96,6 +96,45 @@ __device__ __forceinline__ int out_row(int lane, int r) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
+// Epilogue staging: the 32 x 64 accumulator block acc[i][0..1] of a wave is
+// written to the wave's own LDS area, row-major with EP_LD floats per row, so
+// that each lane can then read 32 consecutive columns of one row (lane l:
+// row l/2, columns 32*(l%2)..+32).  The epilogues' global accesses become
+// 16-byte and contiguous along rows.  The LDS must be free (the main loop ends
+// with a barrier); the caller synchronises before the next tile writes it.
+// LDS operations of one wave complete in order, so a lane may read what other
+// lanes of its wave wrote just before.
+constexpr int EP_LD = 68;  // 64 + 4: the row-run reads are free of bank conflicts
+template <class TL>
+__device__ __forceinline__ const float* stage_rows(const f32x16_t (&acc)[TL::TM][TL::TN], int i,
+                                                   uint16_t* smem, int wave, int lane) {
+  static_assert(TL::TN == 2, "a staged block is 64 columns wide");
+  static_assert(TL::NT / 64 * 32 * EP_LD * 4 <= TL::LDS_ELEMS * 2, "staging exceeds the LDS");
+  float* reg = reinterpret_cast<float*>(smem) + wave * 32 * EP_LD;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) reg[out_row(lane, r) * EP_LD + j * 32 + (lane & 31)] = acc[i][j][r];
+  return reg + (lane >> 1) * EP_LD + (lane & 1) * 32;
+}
+
+// Eight consecutive staged floats.
+__device__ __forceinline__ void ld8(const float* p, float* f) {
+  const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+// Store a staged 32-column run as bf16 (four 16-byte stores).
+__device__ __forceinline__ void store_run32(const float* src, uint16_t* dst) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float f[8];
+    ld8(src + q * 8, f);
+    *(uint4*)(dst + q * 8) = Chunk<uint16_t>::pack(f);
+  }
+}
+
 template <class TL>
 struct Frags {
   bf16x8_t a[TL::TM], b[TL::TN];
@@ -240,6 +279,7 @@ __global__ __launch_bounds__(TL::NT) void row_grouped_kernel(Op op,
     int e, m0, m_end;
     row_tile(s_to, s_off, E_l, sc.t / n_tiles, e, m0, m_end);
     op.template run<TL>(e, m0, m_end, sc.t % n_tiles, smem);
+    __syncthreads();  // epilogue staging done before the next tile's loads land in LDS
   }
 }
 
@@ -268,20 +308,29 @@ struct GateUpOp {
     }, tid);
     f32x16_t acc[TL::TM][TL::TN];
     mainloop<TL>(la, lb, 0, d, smem, acc);
-    const int j = jb + wn * 32 + (lane & 31);
-    if (j >= F) return;
+    // staged row: columns 0..31 gate, 32..63 up of outputs jb + wn*32 + c;
+    // this lane writes the 16 outputs j0..j0+15 of its row
+    const int half = lane & 1, j0 = jb + wn * 32 + half * 16;
+    const bool col_ok = j0 < F;  // F is a multiple of 64
 #pragma unroll
-    for (int i = 0; i < TL::TM; ++i)
+    for (int i = 0; i < TL::TM; ++i) {
+      const int rt = wm * TL::WTM + i * 32 + (lane >> 1);
+      const float* src = stage_rows<TL>(acc, i, smem, wave, lane) - half * 16;
+      if (col_ok && m0 + rt < m_end) {
+        const size_t row = (size_t)(m0 + rt);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * TL::WTM + i * 32 + out_row(lane, r);
-        if (row < m_end) {
-          const float g = acc[i][0][r], u = acc[i][1][r];
-          h[(size_t)row * 2 * F + j] = f2bf(g);
-          h[(size_t)row * 2 * F + F + j] = f2bf(u);
-          a[(size_t)row * F + j] = f2bf(silu_f(g) * u);
+        for (int q = 0; q < 2; ++q) {
+          float g[8], u[8], av[8];
+          ld8(src + q * 8, g);
+          ld8(src + 32 + q * 8, u);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) av[t] = silu_f(g[t]) * u[t];
+          *(uint4*)(h + row * 2 * F + j0 + q * 8) = Chunk<uint16_t>::pack(g);
+          *(uint4*)(h + row * 2 * F + F + j0 + q * 8) = Chunk<uint16_t>::pack(u);
+          *(uint4*)(a + row * F + j0 + q * 8) = Chunk<uint16_t>::pack(av);
         }
       }
+    }
   }
 };
 
@@ -303,17 +352,13 @@ struct DownOp {
     lb.init([&](int n) { return Wd + (size_t)min(nb + n, d - 1) * F; }, tid);
     f32x16_t acc[TL::TM][TL::TN];
     mainloop<TL>(la, lb, 0, F, smem, acc);
+    const int c0 = nb + wn * TL::WTN + (lane & 1) * 32;
+    const bool col_ok = c0 < d;  // d is a multiple of 64
 #pragma unroll
-    for (int j = 0; j < TL::TN; ++j) {
-      const int col = nb + wn * TL::WTN + j * 32 + (lane & 31);
-      if (col >= d) continue;
-#pragma unroll
-      for (int i = 0; i < TL::TM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * TL::WTM + i * 32 + out_row(lane, r);
-          if (row < m_end) yp[(size_t)row * d + col] = f2bf(acc[i][j][r]);
-        }
+    for (int i = 0; i < TL::TM; ++i) {
+      const int rt = wm * TL::WTM + i * 32 + (lane >> 1);
+      const float* src = stage_rows<TL>(acc, i, smem, wave, lane);
+      if (col_ok && m0 + rt < m_end) store_run32(src, yp + (size_t)(m0 + rt) * d + c0);
     }
   }
 };
@@ -338,24 +383,41 @@ struct DgradActOp {
     lb.init([&](int n) { return WdT + (size_t)min(nb + n, F - 1) * d; }, tid);
     f32x16_t acc[TL::TM][TL::TN];
     mainloop<TL>(la, lb, 0, d, smem, acc);
+    // h runs of this lane's row are loaded (16 bytes at a time, row clamped
+    // to a valid one) before the block is staged, so their latency overlaps
+    // the staging
+    const int c0 = nb + wn * TL::WTN + (lane & 1) * 32;
+    const bool col_ok = c0 < F;  // F is a multiple of 64
+    const int cc = col_ok ? c0 : F - 32;
 #pragma unroll
-    for (int j = 0; j < TL::TN; ++j) {
-      const int col = nb + wn * TL::WTN + j * 32 + (lane & 31);
-      if (col >= F) continue;
+    for (int i = 0; i < TL::TM; ++i) {
+      const int rt = wm * TL::WTM + i * 32 + (lane >> 1);
+      const size_t rowc = (size_t)min(m0 + rt, m_end - 1);
+      uint4 gv[4], uv[4];
 #pragma unroll
-      for (int i = 0; i < TL::TM; ++i)
+      for (int q = 0; q < 4; ++q) {
+        gv[q] = *(const uint4*)(hbuf + rowc * 2 * F + cc + q * 8);
+        uv[q] = *(const uint4*)(hbuf + rowc * 2 * F + F + cc + q * 8);
+      }
+      const float* src = stage_rows<TL>(acc, i, smem, wave, lane);
+      if (col_ok && m0 + rt < m_end) {
+        const size_t row = (size_t)(m0 + rt);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * TL::WTM + i * 32 + out_row(lane, r);
-          if (row < m_end) {
-            const float da = acc[i][j][r];
-            const float g = bf2f(hbuf[(size_t)row * 2 * F + col]);
-            const float u = bf2f(hbuf[(size_t)row * 2 * F + F + col]);
-            const float s = sigmoid_f(g);
-            dh[(size_t)row * 2 * F + col] = f2bf(da * u * s * (1.0f + g * (1.0f - s)));
-            dh[(size_t)row * 2 * F + F + col] = f2bf(da * g * s);
+        for (int q = 0; q < 4; ++q) {
+          float da[8], g[8], u[8], dg[8], du[8];
+          ld8(src + q * 8, da);
+          Chunk<uint16_t>::unpack(gv[q], g);
+          Chunk<uint16_t>::unpack(uv[q], u);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const float sg = sigmoid_f(g[t]);
+            dg[t] = da[t] * u[t] * sg * (1.0f + g[t] * (1.0f - sg));
+            du[t] = da[t] * g[t] * sg;
           }
+          *(uint4*)(dh + row * 2 * F + c0 + q * 8) = Chunk<uint16_t>::pack(dg);
+          *(uint4*)(dh + row * 2 * F + F + c0 + q * 8) = Chunk<uint16_t>::pack(du);
         }
+      }
     }
   }
 };
@@ -379,17 +441,13 @@ struct DgradInOp {
     lb.init([&](int n) { return WgT + (size_t)min(nb + n, d - 1) * 2 * F; }, tid);
     f32x16_t acc[TL::TM][TL::TN];
     mainloop<TL>(la, lb, 0, 2 * F, smem, acc);
+    const int c0 = nb + wn * TL::WTN + (lane & 1) * 32;
+    const bool col_ok = c0 < d;  // d is a multiple of 64
 #pragma unroll
-    for (int j = 0; j < TL::TN; ++j) {
-      const int col = nb + wn * TL::WTN + j * 32 + (lane & 31);
-      if (col >= d) continue;
-#pragma unroll
-      for (int i = 0; i < TL::TM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * TL::WTM + i * 32 + out_row(lane, r);
-          if (row < m_end) dxp[(size_t)row * d + col] = f2bf(acc[i][j][r]);
-        }
+    for (int i = 0; i < TL::TM; ++i) {
+      const int rt = wm * TL::WTM + i * 32 + (lane >> 1);
+      const float* src = stage_rows<TL>(acc, i, smem, wave, lane);
+      if (col_ok && m0 + rt < m_end) store_run32(src, dxp + (size_t)(m0 + rt) * d + c0);
     }
   }
 };
@@ -536,20 +594,30 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
         __syncthreads();
       }
     }
+    // With accumulate, the 16 previous values of a 32x32 piece are loaded
+    // together (clamped, always valid addresses) before the first store, so
+    // each piece waits for memory once.
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int col = n0 + wn * WTN + j * 32 + (lane & 31);
-      if (col >= N) continue;
+      const bool col_ok = col < N;
+      const int colc = col_ok ? col : N - 1;
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i) {
+        const int rb = m0 + wm * WTM + i * 32;
+        float prev[16];
+        if (accumulate) {  // uniform
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            prev[r] = out[(size_t)min(rb + out_row(lane, r), M - 1) * N + colc];
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * WTM + i * 32 + out_row(lane, r);
-          if (row < M) {
-            float* o = out + (size_t)row * N + col;
-            *o = accumulate ? *o + acc[i][j][r] : acc[i][j][r];
-          }
+          const int row = rb + out_row(lane, r);
+          if (col_ok && row < M)
+            out[(size_t)row * N + col] = accumulate ? prev[r] + acc[i][j][r] : acc[i][j][r];
         }
+      }
     }
   }
 }
