@@ -96,25 +96,26 @@ __device__ __forceinline__ int out_row(int lane, int r) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
-// Epilogue staging: the 32 x 64 accumulator block acc[i][0..1] of a wave is
-// written to the wave's own LDS area, row-major with EP_LD floats per row, so
-// that each lane can then read 32 consecutive columns of one row (lane l:
-// row l/2, columns 32*(l%2)..+32).  The epilogues' global accesses become
-// 16-byte and contiguous along rows.  The LDS must be free (the main loop ends
-// with a barrier); the caller synchronises before the next tile writes it.
-// LDS operations of one wave complete in order, so a lane may read what other
-// lanes of its wave wrote just before.
+// Epilogue staging: the 32 x 64 accumulator block acc[i][2p], acc[i][2p+1]
+// of a wave is written to the wave's own LDS area, row-major with EP_LD floats
+// per row, so that each lane can then read 32 consecutive columns of one row
+// (lane l: row l/2, columns 32*(l%2)..+32 of the block).  The epilogues'
+// global accesses become 16-byte and contiguous along rows.  The LDS must be
+// free (the main loop ends with a barrier); the caller synchronises before the
+// next tile writes it.  LDS operations of one wave complete in order, so a
+// lane may read what other lanes of its wave wrote just before.
 constexpr int EP_LD = 68;  // 64 + 4: the row-run reads are free of bank conflicts
 template <class TL>
 __device__ __forceinline__ const float* stage_rows(const f32x16_t (&acc)[TL::TM][TL::TN], int i,
-                                                   uint16_t* smem, int wave, int lane) {
-  static_assert(TL::TN == 2, "a staged block is 64 columns wide");
+                                                   int p, uint16_t* smem, int wave, int lane) {
+  static_assert(TL::TN % 2 == 0, "staged blocks are 64 columns wide");
   static_assert(TL::NT / 64 * 32 * EP_LD * 4 <= TL::LDS_ELEMS * 2, "staging exceeds the LDS");
   float* reg = reinterpret_cast<float*>(smem) + wave * 32 * EP_LD;
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) reg[out_row(lane, r) * EP_LD + j * 32 + (lane & 31)] = acc[i][j][r];
+    for (int r = 0; r < 16; ++r)
+      reg[out_row(lane, r) * EP_LD + j * 32 + (lane & 31)] = acc[i][2 * p + j][r];
   return reg + (lane >> 1) * EP_LD + (lane & 1) * 32;
 }
 
@@ -284,8 +285,9 @@ __global__ __launch_bounds__(TL::NT) void row_grouped_kernel(Op op,
 }
 
 // forward GEMM1: [g, u] = xp . W_gu[e]^T with the SwiGLU epilogue.  The B tile
-// pairs gate and up rows: wave wn's 64 tile rows are 32 gate rows j and the 32
-// up rows F + j of the same j, so each lane holds g and u of one output.
+// pairs gate and up rows: every 64 tile rows are 32 gate rows j and the 32 up
+// rows F + j of the same j, so a staged 64-column block holds g and u of 32
+// outputs.
 struct GateUpOp {
   const uint16_t* xp;
   const uint16_t* W_gu;
@@ -294,7 +296,6 @@ struct GateUpOp {
   int d, F;
   template <class TL>
   __device__ __forceinline__ void run(int e, int m0, int m_end, int nt, uint16_t* smem) const {
-    static_assert(TL::WTN == 64, "each wave pairs 32 gate with 32 up columns");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / TL::WGN, wn = wave % TL::WGN;
     const int jb = nt * (TL::BN / 2);
@@ -308,26 +309,30 @@ struct GateUpOp {
     }, tid);
     f32x16_t acc[TL::TM][TL::TN];
     mainloop<TL>(la, lb, 0, d, smem, acc);
-    // staged row: columns 0..31 gate, 32..63 up of outputs jb + wn*32 + c;
-    // this lane writes the 16 outputs j0..j0+15 of its row
-    const int half = lane & 1, j0 = jb + wn * 32 + half * 16;
-    const bool col_ok = j0 < F;  // F is a multiple of 64
+    // staged block p: columns 0..31 gate, 32..63 up of outputs
+    // jb + (wn*TN/2 + p)*32 + c; this lane writes 16 outputs of its row
+    const int half = lane & 1;
 #pragma unroll
-    for (int i = 0; i < TL::TM; ++i) {
-      const int rt = wm * TL::WTM + i * 32 + (lane >> 1);
-      const float* src = stage_rows<TL>(acc, i, smem, wave, lane) - half * 16;
-      if (col_ok && m0 + rt < m_end) {
-        const size_t row = (size_t)(m0 + rt);
+    for (int p = 0; p < TL::TN / 2; ++p) {
+      const int j0 = jb + (wn * (TL::TN / 2) + p) * 32 + half * 16;
+      const bool col_ok = j0 < F;  // F is a multiple of 64
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          float g[8], u[8], av[8];
-          ld8(src + q * 8, g);
-          ld8(src + 32 + q * 8, u);
+      for (int i = 0; i < TL::TM; ++i) {
+        const int rt = wm * TL::WTM + i * 32 + (lane >> 1);
+        const float* src = stage_rows<TL>(acc, i, p, smem, wave, lane) - half * 16;
+        if (col_ok && m0 + rt < m_end) {
+          const size_t row = (size_t)(m0 + rt);
 #pragma unroll
-          for (int t = 0; t < 8; ++t) av[t] = silu_f(g[t]) * u[t];
-          *(uint4*)(h + row * 2 * F + j0 + q * 8) = Chunk<uint16_t>::pack(g);
-          *(uint4*)(h + row * 2 * F + F + j0 + q * 8) = Chunk<uint16_t>::pack(u);
-          *(uint4*)(a + row * F + j0 + q * 8) = Chunk<uint16_t>::pack(av);
+          for (int q = 0; q < 2; ++q) {
+            float g[8], u[8], av[8];
+            ld8(src + q * 8, g);
+            ld8(src + 32 + q * 8, u);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) av[t] = silu_f(g[t]) * u[t];
+            *(uint4*)(h + row * 2 * F + j0 + q * 8) = Chunk<uint16_t>::pack(g);
+            *(uint4*)(h + row * 2 * F + F + j0 + q * 8) = Chunk<uint16_t>::pack(u);
+            *(uint4*)(a + row * F + j0 + q * 8) = Chunk<uint16_t>::pack(av);
+          }
         }
       }
     }
@@ -352,13 +357,16 @@ struct DownOp {
     lb.init([&](int n) { return Wd + (size_t)min(nb + n, d - 1) * F; }, tid);
     f32x16_t acc[TL::TM][TL::TN];
     mainloop<TL>(la, lb, 0, F, smem, acc);
-    const int c0 = nb + wn * TL::WTN + (lane & 1) * 32;
-    const bool col_ok = c0 < d;  // d is a multiple of 64
 #pragma unroll
-    for (int i = 0; i < TL::TM; ++i) {
-      const int rt = wm * TL::WTM + i * 32 + (lane >> 1);
-      const float* src = stage_rows<TL>(acc, i, smem, wave, lane);
-      if (col_ok && m0 + rt < m_end) store_run32(src, yp + (size_t)(m0 + rt) * d + c0);
+    for (int p = 0; p < TL::TN / 2; ++p) {
+      const int c0 = nb + wn * TL::WTN + p * 64 + (lane & 1) * 32;
+      const bool col_ok = c0 < d;  // d is a multiple of 64
+#pragma unroll
+      for (int i = 0; i < TL::TM; ++i) {
+        const int rt = wm * TL::WTM + i * 32 + (lane >> 1);
+        const float* src = stage_rows<TL>(acc, i, p, smem, wave, lane);
+        if (col_ok && m0 + rt < m_end) store_run32(src, yp + (size_t)(m0 + rt) * d + c0);
+      }
     }
   }
 };
@@ -386,36 +394,39 @@ struct DgradActOp {
     // h runs of this lane's row are loaded (16 bytes at a time, row clamped
     // to a valid one) before the block is staged, so their latency overlaps
     // the staging
-    const int c0 = nb + wn * TL::WTN + (lane & 1) * 32;
-    const bool col_ok = c0 < F;  // F is a multiple of 64
-    const int cc = col_ok ? c0 : F - 32;
 #pragma unroll
-    for (int i = 0; i < TL::TM; ++i) {
-      const int rt = wm * TL::WTM + i * 32 + (lane >> 1);
-      const size_t rowc = (size_t)min(m0 + rt, m_end - 1);
-      uint4 gv[4], uv[4];
+    for (int p = 0; p < TL::TN / 2; ++p) {
+      const int c0 = nb + wn * TL::WTN + p * 64 + (lane & 1) * 32;
+      const bool col_ok = c0 < F;  // F is a multiple of 64
+      const int cc = col_ok ? c0 : F - 32;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        gv[q] = *(const uint4*)(hbuf + rowc * 2 * F + cc + q * 8);
-        uv[q] = *(const uint4*)(hbuf + rowc * 2 * F + F + cc + q * 8);
-      }
-      const float* src = stage_rows<TL>(acc, i, smem, wave, lane);
-      if (col_ok && m0 + rt < m_end) {
-        const size_t row = (size_t)(m0 + rt);
+      for (int i = 0; i < TL::TM; ++i) {
+        const int rt = wm * TL::WTM + i * 32 + (lane >> 1);
+        const size_t rowc = (size_t)min(m0 + rt, m_end - 1);
+        uint4 gv[4], uv[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          float da[8], g[8], u[8], dg[8], du[8];
-          ld8(src + q * 8, da);
-          Chunk<uint16_t>::unpack(gv[q], g);
-          Chunk<uint16_t>::unpack(uv[q], u);
+          gv[q] = *(const uint4*)(hbuf + rowc * 2 * F + cc + q * 8);
+          uv[q] = *(const uint4*)(hbuf + rowc * 2 * F + F + cc + q * 8);
+        }
+        const float* src = stage_rows<TL>(acc, i, p, smem, wave, lane);
+        if (col_ok && m0 + rt < m_end) {
+          const size_t row = (size_t)(m0 + rt);
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const float sg = sigmoid_f(g[t]);
-            dg[t] = da[t] * u[t] * sg * (1.0f + g[t] * (1.0f - sg));
-            du[t] = da[t] * g[t] * sg;
+          for (int q = 0; q < 4; ++q) {
+            float da[8], g[8], u[8], dg[8], du[8];
+            ld8(src + q * 8, da);
+            Chunk<uint16_t>::unpack(gv[q], g);
+            Chunk<uint16_t>::unpack(uv[q], u);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+              const float sg = sigmoid_f(g[t]);
+              dg[t] = da[t] * u[t] * sg * (1.0f + g[t] * (1.0f - sg));
+              du[t] = da[t] * g[t] * sg;
+            }
+            *(uint4*)(dh + row * 2 * F + c0 + q * 8) = Chunk<uint16_t>::pack(dg);
+            *(uint4*)(dh + row * 2 * F + F + c0 + q * 8) = Chunk<uint16_t>::pack(du);
           }
-          *(uint4*)(dh + row * 2 * F + c0 + q * 8) = Chunk<uint16_t>::pack(dg);
-          *(uint4*)(dh + row * 2 * F + F + c0 + q * 8) = Chunk<uint16_t>::pack(du);
         }
       }
     }
@@ -441,13 +452,16 @@ struct DgradInOp {
     lb.init([&](int n) { return WgT + (size_t)min(nb + n, d - 1) * 2 * F; }, tid);
     f32x16_t acc[TL::TM][TL::TN];
     mainloop<TL>(la, lb, 0, 2 * F, smem, acc);
-    const int c0 = nb + wn * TL::WTN + (lane & 1) * 32;
-    const bool col_ok = c0 < d;  // d is a multiple of 64
 #pragma unroll
-    for (int i = 0; i < TL::TM; ++i) {
-      const int rt = wm * TL::WTM + i * 32 + (lane >> 1);
-      const float* src = stage_rows<TL>(acc, i, smem, wave, lane);
-      if (col_ok && m0 + rt < m_end) store_run32(src, dxp + (size_t)(m0 + rt) * d + c0);
+    for (int p = 0; p < TL::TN / 2; ++p) {
+      const int c0 = nb + wn * TL::WTN + p * 64 + (lane & 1) * 32;
+      const bool col_ok = c0 < d;  // d is a multiple of 64
+#pragma unroll
+      for (int i = 0; i < TL::TM; ++i) {
+        const int rt = wm * TL::WTM + i * 32 + (lane >> 1);
+        const float* src = stage_rows<TL>(acc, i, p, smem, wave, lane);
+        if (col_ok && m0 + rt < m_end) store_run32(src, dxp + (size_t)(m0 + rt) * d + c0);
+      }
     }
   }
 };
