@@ -17,9 +17,9 @@
 //  * LDS tiles are [rows][64] bf16 with the 16-byte chunk index XOR-swizzled
 //    by the row, so matrix-core fragment reads are free of bank conflicts;
 //  * the MFMA fragments of the next 16-wide k slice are read while the current
-//    slice's MFMAs run, and the instruction order (MFMA / LDS read / global
-//    load / LDS write) is fixed with scheduling group barriers so the matrix
-//    pipe is fed continuously;
+//    slice's MFMAs run (across the stage barrier too), and the instruction
+//    order (MFMA / LDS read / global load / LDS write) is fixed with
+//    scheduling group barriers so the matrix pipe is fed continuously;
 //  * loads are branch free: rows or columns outside the matrix read a valid
 //    clamped address (their results are discarded, or replaced by zero where
 //    they would enter a sum);
@@ -141,16 +141,18 @@ struct Frags {
   bf16x8_t a[TL::TM], b[TL::TN];
 };
 
+// B fragments first: the first MFMA of a slice needs a[0] and b[0], so with
+// B read first it waits for the third read instead of the fifth.
 template <class TL>
 __device__ __forceinline__ void read_frags(Frags<TL>& f, const uint16_t* A, const uint16_t* B,
                                            int kk, int wm, int wn, int lane) {
   const int fr = lane & 31, ch = kk * 2 + (lane >> 5);
 #pragma unroll
-  for (int i = 0; i < TL::TM; ++i)
-    f.a[i] = *(const bf16x8_t*)(A + lds_off(wm * TL::WTM + i * 32 + fr, ch));
-#pragma unroll
   for (int j = 0; j < TL::TN; ++j)
     f.b[j] = *(const bf16x8_t*)(B + lds_off(wn * TL::WTN + j * 32 + fr, ch));
+#pragma unroll
+  for (int i = 0; i < TL::TM; ++i)
+    f.a[i] = *(const bf16x8_t*)(A + lds_off(wm * TL::WTM + i * 32 + fr, ch));
 }
 
 template <class TL>
@@ -162,14 +164,16 @@ __device__ __forceinline__ void mfmas(const Frags<TL>& f, f32x16_t (&acc)[TL::TM
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
-// One 16-wide k slice: NM MFMAs, each followed by up to one LDS read, one
+// One 16-wide k slice: NM MFMAs, each followed by up to two LDS reads (the
+// next slice's fragments are all in flight after the first NR/2 MFMAs), one
 // global load and one LDS write (while those remain).
 template <int NM, int NR, int NV, int NW>
 __device__ __forceinline__ void sched_slice() {
 #pragma unroll
   for (int i = 0; i < NM; ++i) {
     SCHED_GROUP(SG_MFMA, 1);
-    if (i < NR) SCHED_GROUP(SG_DS_R, 1);
+    if (2 * i < NR) SCHED_GROUP(SG_DS_R, 1);
+    if (2 * i + 1 < NR) SCHED_GROUP(SG_DS_R, 1);
     if (i < NV) SCHED_GROUP(SG_VMEM_R, 1);
     if (i < NW) SCHED_GROUP(SG_DS_W, 1);
   }
@@ -223,9 +227,12 @@ __device__ __forceinline__ void mainloop(LA& la, LB& lb, int k_begin, int k_end,
     la.store(An);
     lb.store(Bn);
     if constexpr (SCHED) sched_slice<NM, NR, 0, NW>();
-    mfmas<TL>(f1, acc);
+    // the next stage is complete once every wave passes the barrier; its
+    // first fragments are read while the last slice's MFMAs run
     __syncthreads();
     read_frags<TL>(f0, An, Bn, 0, wm, wn, lane);
+    mfmas<TL>(f1, acc);
+    if constexpr (SCHED) sched_slice<NM, NR, 0, 0>();
   }
   __syncthreads();  // LDS free for the caller's next tile
 }
