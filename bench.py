@@ -139,6 +139,10 @@ def main():
     ap.add_argument("--workload", default="ep16_rank_bf16")
     ap.add_argument("--tokens", type=int, default=None, help="override T of the workload")
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
+    ap.add_argument("--overlapped-only", action="store_true",
+                    help="run only the warm-up and the overlapped steps and print no JSON line: "
+                         "the program to trace with rocprofv3 --kernel-trace for the overlap of "
+                         "the two streams' kernels")
     ap.add_argument("--counter-pass", action="store_true",
                     help="run a few serialized steps and a copy probe of known size, print no "
                          "JSON line: the program to run under rocprofv3 --pmc FETCH_SIZE / "
@@ -225,6 +229,8 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = ev0.elapsed_time(ev1) / args.steps
     err(f"[bench] overlapped: {ms_step:.4f} ms/step (wall {1e3 * wall / args.steps:.4f})")
+    if args.overlapped_only:
+        return
 
     # ---- timed region 2: the same steps serialized on one stream, with every
     # kernel bracketed by HIP events on its stream (no concurrency, so each

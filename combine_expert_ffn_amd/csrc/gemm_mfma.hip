@@ -537,6 +537,13 @@ __device__ __forceinline__ bf16x8_t frag_tr(const uint8_t* lds, int cb, int kk, 
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// A wave-uniform 64-bit value moved to scalar registers.
+__device__ __forceinline__ long long uniform64(long long v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(unsigned long long)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long long)v >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
 // 256 x 256 output tiles, 8 waves (2 x 4), wave tile 128 x 64.
 __global__ __launch_bounds__(512) void wgrad_kernel(
     const uint16_t* __restrict__ xp, const uint16_t* __restrict__ abuf,
@@ -546,14 +553,53 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
   constexpr int NW = 8, WGN = 4, WTM = 128, WTN = 64, TM = 4, TN = 2;
   constexpr int STAGE = 2 * BK * WG_ROWB;  // A + B tiles
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  __shared__ long long s_it[257];  // first k-step of each expert's tiles; s_it[E_l] = W
   const int tdm = (d + 255) / 256, tdn = (F + 255) / 256;
   const int tgm = (2 * F + 255) / 256, tgn = (d + 255) / 256;
   const int per_e = tdm * tdn + tgm * tgn;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
-  for (Sched sc(E_l * per_e); sc.t < sc.end; sc.t += sc.step) {
-    const int e = sc.t / per_e;
-    int t = sc.t % per_e;
+  // Work-balanced schedule: a tile costs nk_e = max(1, ceil(rows_e / 64))
+  // k-steps (experts' row counts differ) and the W steps of all tiles are laid
+  // out tile-major.  XCD g (the hardware places block b on XCD b % 8) takes
+  // the tiles whose first step falls in [W*g/8, W*(g+1)/8), so the XCDs get
+  // equal work, and its blocks take those tiles round robin, so the tiles
+  // running together share operand rows in the XCD's L2.
+  if (tid == 0) {
+    long long acc_it = 0;
+    for (int e = 0; e < E_l; ++e) {
+      s_it[e] = acc_it;
+      const int nk = (offsets[e + 1] - offsets[e] + BK - 1) / BK;
+      acc_it += (long long)per_e * (nk > 0 ? nk : 1);
+    }
+    s_it[E_l] = acc_it;
+  }
+  __syncthreads();
+  const int G = gridDim.x, NG = G % 8 == 0 ? 8 : 1;
+  const int grp = blockIdx.x % NG, slot = blockIdx.x / NG, nslots = G / NG;
+  const long long W = uniform64(s_it[E_l]);
+  const long long lo = W * grp / NG, hi = W * (grp + 1) / NG;
+  long long gt0;  // first tile (expert-major index) starting at or after lo
+  {
+    int a = 0, b = E_l;  // s_it[a] <= lo < s_it[b]
+    while (b - a > 1) {
+      const int mid = (a + b) >> 1;
+      if (s_it[mid] <= lo) a = mid;
+      else b = mid;
+    }
+    a = __builtin_amdgcn_readfirstlane(a);
+    const long long it0 = uniform64(s_it[a]);
+    const long long nk0 = (uniform64(s_it[a + 1]) - it0) / per_e;
+    gt0 = (long long)a * per_e + (lo - it0 + nk0 - 1) / nk0;
+  }
+  for (long long gt = gt0 + slot; gt < (long long)E_l * per_e; gt += nslots) {
+    const int e = (int)(gt / per_e);
+    int t = (int)(gt % per_e);
+    {
+      const long long it0 = uniform64(s_it[e]);
+      const long long nk_e = (uniform64(s_it[e + 1]) - it0) / per_e;
+      if (it0 + t * nk_e >= hi) break;  // uniform
+    }
     const int r0 = offsets[e], r1 = offsets[e + 1];
     const uint16_t *Asrc, *Bsrc;
     int M, N, m0, n0;
