@@ -112,7 +112,7 @@ constexpr int kTileM = 256;
 // Pairs per block of the dispatch-plan kernels.
 constexpr int kPlanChunk = 2048;
 // Tokens per partial of the router weight-gradient reduction.
-constexpr int kRouterChunk = 1024;
+constexpr int kRouterChunk = 256;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -195,23 +195,27 @@ __global__ __launch_bounds__(256) void dlogits_kernel(const float* __restrict__ 
 }
 
 // dW_r partials: block = 64 columns c x 64 experts e over one chunk of tokens.
-// partial[chunk][c][e] = sum_{t in chunk} x[t][c] * dlogits[t][e].
+// partial[chunk][c][e] = sum_{t in chunk} x[t][c] * dlogits[t][e].  Each
+// thread owns a 4 x 4 piece (columns 4*(tid%16).., experts 4*(tid/16)..), so
+// a 32-token slab staged in LDS feeds 16 FMAs per two 16-byte LDS reads.
 template <typename T>
 __global__ __launch_bounds__(256) void dwr_partial_kernel(const T* __restrict__ x,
                                                           const float* __restrict__ dl,
                                                           float* __restrict__ partial, int T_,
                                                           int d, int E) {
-  __shared__ float xs[32][65];
-  __shared__ float ds[32][65];
+  __shared__ __attribute__((aligned(16))) float xs[32][68];
+  __shared__ __attribute__((aligned(16))) float ds[32][68];
   const int c0 = blockIdx.x * 64, e0 = blockIdx.z * 64;
   const int chunk = blockIdx.y;
   const int t_begin = chunk * kRouterChunk;
   const int t_end = min(T_, t_begin + kRouterChunk);
   const int tid = threadIdx.x;
-  const int c = tid & 63, eg = (tid >> 6) * 16;
-  float acc[16];
+  const int ci = (tid & 15) * 4, ei = (tid >> 4) * 4;
+  float acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
   for (int t0 = t_begin; t0 < t_end; t0 += 32) {
     for (int i = tid; i < 32 * 64; i += 256) {
       const int tt = i >> 6, cc = i & 63;
@@ -220,19 +224,26 @@ __global__ __launch_bounds__(256) void dwr_partial_kernel(const T* __restrict__ 
       ds[tt][cc] = (t < t_end && e0 + cc < E) ? dl[(size_t)t * E + e0 + cc] : 0.f;
     }
     __syncthreads();
-#pragma unroll 4
+#pragma unroll 8
     for (int tt = 0; tt < 32; ++tt) {
-      const float xv = xs[tt][c];
+      const float4 xv = *(const float4*)&xs[tt][ci];
+      const float4 dv = *(const float4*)&ds[tt][ei];
+      const float xa[4] = {xv.x, xv.y, xv.z, xv.w};
+      const float da[4] = {dv.x, dv.y, dv.z, dv.w};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = fmaf(xv, ds[tt][eg + i], acc[i]);
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(xa[i], da[j], acc[i][j]);
     }
     __syncthreads();
   }
-  if (c0 + c < d) {
-    float* out = partial + ((size_t)chunk * d + c0 + c) * E;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (e0 + eg + i < E) out[e0 + eg + i] = acc[i];
+  for (int i = 0; i < 4; ++i) {
+    if (c0 + ci + i >= d) continue;
+    float* out = partial + ((size_t)chunk * d + c0 + ci + i) * E + e0 + ei;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (e0 + ei + j < E) out[j] = acc[i][j];
   }
 }
 
