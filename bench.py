@@ -143,6 +143,10 @@ def main():
                     help="run only the warm-up and the overlapped steps and print no JSON line: "
                          "the program to trace with rocprofv3 --kernel-trace for the overlap of "
                          "the two streams' kernels")
+    ap.add_argument("--serialized-only", action="store_true",
+                    help="skip the overlapped steps and print no JSON line: the program to trace "
+                         "with rocprofv3 --kernel-trace for per-kernel durations comparable to the "
+                         "bench's event timings (taken on the serialized steps)")
     ap.add_argument("--counter-pass", action="store_true",
                     help="run a few serialized steps and a copy probe of known size, print no "
                          "JSON line: the program to run under rocprofv3 --pmc FETCH_SIZE / "
@@ -218,6 +222,11 @@ def main():
     N = int(counts[0].sum())
     T_loc = int((mbs[0].row_of_pair >= 0).any(dim=1).sum())
 
+    if args.serialized_only:
+        i = run_loop(args.warmup + args.steps, M.MOE_STEP_SERIALIZE, i)
+        torch.cuda.synchronize()
+        err(f"[bench] serialized-only pass done: {args.warmup + args.steps} steps")
+        return
     # ---- timed region 1: overlapped 1F1B steps (the product schedule) -> value
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
