@@ -41,6 +41,12 @@ SMALL = {
     # the largest supported hidden size
     "wide_bf16": Workload("wide_bf16", T=24, d=16384, F=64, E=4, e_lo=0, E_l=4, K=2,
                           dtype="bf16", route="topk"),
+    # the largest supported FFN width
+    "wide_ffn_bf16": Workload("wide_ffn_bf16", T=40, d=64, F=16384, E=2, e_lo=0, E_l=2, K=2,
+                              dtype="bf16", route="topk"),
+    # the largest router (E = 512, K = 16) with the largest window (256 experts)
+    "max_router_bf16": Workload("max_router_bf16", T=200, d=128, F=64, E=512, e_lo=128,
+                                E_l=256, K=16, dtype="bf16", route="topk"),
 }
 
 
@@ -213,7 +219,7 @@ def _layer_step(w, inp, flags=0, s_copy=None):
 
 
 @pytest.mark.parametrize("name", ["tiny_f32", "fb_ragged_bf16", "zipf_window_bf16",
-                                  "many_experts_bf16", "mid_window_bf16"])
+                                  "many_experts_bf16", "mid_window_bf16", "max_router_bf16"])
 def test_chain_parity(name):
     w = SMALL[name]
     log(f"[chain parity] {name}")
