@@ -282,6 +282,10 @@ typedef struct moe_step {
  * caller that waits for s_compute sees all results.  Results are bit-identical
  * to MOE_STEP_SERIALIZE (all calls on s_compute in forward-then-backward order).
  * s_copy may equal s_compute (then the step is serialized).
+ * The step only launches kernels and records/waits on events (s_copy forks
+ * from and joins back to s_compute), so it may be captured into a HIP graph
+ * on s_compute and replayed; it issues no memset, copy, allocation or
+ * synchronisation.
  */
 int moe_overlap_step(const moe_step* st, hipStream_t s_compute, hipStream_t s_copy,
                      int flags);
