@@ -88,7 +88,7 @@ static size_t ws_one(const moe_shape* s) {
   size_t b = ws_plan_bytes(s);
   if (ws_wrt_bytes(s) > b) b = ws_wrt_bytes(s);
   if (ws_router_partial_bytes(s) > b) b = ws_router_partial_bytes(s);
-  if (ws_wT_bytes(s) > b) b = ws_wT_bytes(s);
+  if (ws_wT_offset(s) + ws_wT_bytes(s) > b) b = ws_wT_offset(s) + ws_wT_bytes(s);
   return b < 256 ? 256 : b;
 }
 
@@ -314,9 +314,10 @@ int moe_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h, const int3
   REQUIRE(dxp);
   if (s->dtype == MOE_BF16) {
     REQUIRE(ws);
-    if (int rc = need_ws(__func__, ws_bytes, ws_wT_bytes(s))) return rc;
+    if (int rc = need_ws(__func__, ws_bytes, ws_wT_offset(s) + ws_wT_bytes(s))) return rc;
   }
-  return launch_ffn_dgrad(s, dyp, h, offsets, tile_offsets, W_gu, W_down, dh, dxp, ws, stream);
+  return launch_ffn_dgrad(s, dyp, h, offsets, tile_offsets, W_gu, W_down, dh, dxp, ws, false,
+                          stream);
 }
 
 int moe_ffn_wgrad(const moe_shape* s, const void* xp, const void* a, const void* dh,
@@ -492,9 +493,12 @@ static int bwd_route(const StepCtx& c, const moe_mb* B, hipStream_t q) {
                           with_dw ? c.st->dW_r : nullptr,
                           (c.st->accumulate & MOE_ACCUM_DW) != 0, c.wsB, q);
 }
-static int bwd_dgrad(const StepCtx& c, const moe_mb* B, hipStream_t q) {
+static int bwd_dgrad_weights(const StepCtx& c, hipStream_t q) {
+  return launch_dgrad_weights(c.s, c.st->W_gu, c.st->W_down, c.wsB, q);
+}
+static int bwd_dgrad(const StepCtx& c, const moe_mb* B, bool weights_ready, hipStream_t q) {
   return launch_ffn_dgrad(c.s, B->dyp, B->h, B->offsets, B->tile_offsets, c.st->W_gu,
-                          c.st->W_down, B->dh, B->dxp, c.wsB, q);
+                          c.st->W_down, B->dh, B->dxp, c.wsB, weights_ready, q);
 }
 static int bwd_dispatch(const StepCtx& c, const moe_mb* B, hipStream_t q) {
   return do_dispatch_bwd(c.s, B->dxp, B->row_of_pair, B->idx, c.router ? B->dlogits : nullptr,
@@ -553,7 +557,7 @@ extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t 
     if (B) {
       TRY(bwd_combine(c, B, s0));
       TRY(bwd_route(c, B, s0));
-      TRY(bwd_dgrad(c, B, s0));
+      TRY(bwd_dgrad(c, B, false, s0));
       if (eager) TRY(bwd_wgrad(c, B, s0));
       TRY(bwd_dispatch(c, B, s0));
       if (!eager) TRY(bwd_wgrad(c, B, s0));
@@ -575,9 +579,12 @@ extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t 
     HIPTRY(hipEventRecord(ev->route, s0));
   }
   if (B) {
+    // the dgrad's weight copies need nothing from this step: made on s0 while
+    // s1 runs B's combine backward
+    TRY(bwd_dgrad_weights(c, s0));
     HIPTRY(hipStreamWaitEvent(s0, ev->cb, 0));
     TRY(bwd_route(c, B, s0));
-    TRY(bwd_dgrad(c, B, s0));
+    TRY(bwd_dgrad(c, B, true, s0));
     HIPTRY(hipEventRecord(ev->dgrad, s0));
     if (eager) TRY(bwd_wgrad(c, B, s0));
   }

@@ -807,14 +807,13 @@ int launch_ffn_fwd_bf16(const moe_shape* s, const void* xp, const int32_t* offse
                             (d + T256::BN - 1) / T256::BN, st);
 }
 
-int launch_ffn_dgrad_bf16(const moe_shape* s, const void* dyp, const void* h,
-                          const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
-                          const void* W_down, void* dh, void* dxp, void* ws, hipStream_t st) {
+int launch_dgrad_weights_bf16(const moe_shape* s, const void* W_gu, const void* W_down,
+                              void* ws, hipStream_t st) {
   const int d = (int)s->d, F = (int)s->F, E_l = (int)s->E_l;
   // K-contiguous copies of the weights: W_downT[e] = W_down[e]^T [F][d],
   // W_guT[e] = W_gu[e]^T [d][2F]
-  uint16_t* W_downT = (uint16_t*)ws;
-  uint16_t* W_guT = (uint16_t*)((char*)ws + ws_wT_down_bytes(s));
+  uint16_t* W_downT = (uint16_t*)((char*)ws + ws_wT_offset(s));
+  uint16_t* W_guT = (uint16_t*)((char*)W_downT + ws_wT_down_bytes(s));
   MOE_LAUNCH("transpose_w", st,
              transpose_batched_kernel<<<dim3(F / 64, d / 64, E_l), 256, 0, st>>>(
                  (const uint16_t*)W_down, W_downT, d, F));
@@ -822,7 +821,18 @@ int launch_ffn_dgrad_bf16(const moe_shape* s, const void* dyp, const void* h,
   MOE_LAUNCH("transpose_w", st,
              transpose_batched_kernel<<<dim3(d / 64, 2 * F / 64, E_l), 256, 0, st>>>(
                  (const uint16_t*)W_gu, W_guT, 2 * F, d));
-  if (int rc = check_launch("transpose W_gu")) return rc;
+  return check_launch("transpose W_gu");
+}
+
+int launch_ffn_dgrad_bf16(const moe_shape* s, const void* dyp, const void* h,
+                          const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
+                          const void* W_down, void* dh, void* dxp, void* ws, bool weights_ready,
+                          hipStream_t st) {
+  const int d = (int)s->d, F = (int)s->F;
+  if (!weights_ready)
+    if (int rc = launch_dgrad_weights_bf16(s, W_gu, W_down, ws, st)) return rc;
+  const uint16_t* W_downT = (const uint16_t*)((char*)ws + ws_wT_offset(s));
+  const uint16_t* W_guT = (const uint16_t*)((const char*)W_downT + ws_wT_down_bytes(s));
   DgradActOp da{(const uint16_t*)dyp, (const uint16_t*)h, W_downT, (uint16_t*)dh, d, F};
   if (int rc = launch_row_grouped("dgrad_act", s, da, offsets, tile_offsets,
                                   (F + T256::BN - 1) / T256::BN, st))

@@ -129,9 +129,12 @@ __global__ __launch_bounds__(256) void f32_wgrad_kernel(
 int launch_ffn_fwd_bf16(const moe_shape* s, const void* xp, const int32_t* offsets,
                         const int32_t* tile_offsets, const void* W_gu, const void* W_down,
                         void* h, void* a, void* yp, hipStream_t st);
+int launch_dgrad_weights_bf16(const moe_shape* s, const void* W_gu, const void* W_down,
+                              void* ws, hipStream_t st);
 int launch_ffn_dgrad_bf16(const moe_shape* s, const void* dyp, const void* h,
                           const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
-                          const void* W_down, void* dh, void* dxp, void* ws, hipStream_t st);
+                          const void* W_down, void* dh, void* dxp, void* ws, bool weights_ready,
+                          hipStream_t st);
 int launch_ffn_wgrad_bf16(const moe_shape* s, const void* xp, const void* a, const void* dh,
                           const void* dyp, const int32_t* offsets, float* dW_gu, float* dW_down,
                           bool accumulate, hipStream_t st);
@@ -154,12 +157,19 @@ int launch_ffn_fwd(const moe_shape* s, const void* xp, const int32_t* offsets,
   return check_launch("f32 expert GEMM2");
 }
 
+int launch_dgrad_weights(const moe_shape* s, const void* W_gu, const void* W_down, void* ws,
+                         hipStream_t st) {
+  if (s->T == 0 || s->dtype != MOE_BF16) return MOE_OK;
+  return launch_dgrad_weights_bf16(s, W_gu, W_down, ws, st);
+}
+
 int launch_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h, const int32_t* offsets,
                      const int32_t* tile_offsets, const void* W_gu, const void* W_down, void* dh,
-                     void* dxp, void* ws, hipStream_t st) {
+                     void* dxp, void* ws, bool weights_ready, hipStream_t st) {
   if (s->T == 0) return MOE_OK;
   if (s->dtype == MOE_BF16)
-    return launch_ffn_dgrad_bf16(s, dyp, h, offsets, tile_offsets, W_gu, W_down, dh, dxp, ws, st);
+    return launch_ffn_dgrad_bf16(s, dyp, h, offsets, tile_offsets, W_gu, W_down, dh, dxp, ws,
+                                 weights_ready, st);
   const long cap = s->T * s->K;
   const int d = (int)s->d, F = (int)s->F, E_l = (int)s->E_l;
   MOE_LAUNCH("f32_dgrad_act", st,

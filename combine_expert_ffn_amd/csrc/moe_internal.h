@@ -131,7 +131,16 @@ inline size_t ws_router_partial_bytes(const moe_shape* s) {
   return align_up((size_t)(nc * s->d * s->E) * sizeof(float), 256);
 }
 // Transposed expert weights for the bf16 dgrad: W_downT [E_l][F][d] then
-// W_guT [E_l][d][2F] (bf16).  The float32 dgrad needs none.
+// W_guT [E_l][d][2F] (bf16).  The float32 dgrad needs none.  They sit after
+// the regions of the plan, the transposed router weights and the router
+// gradient partials, so a step can write them while the same micro-batch's
+// router backward still uses its partials.
+inline size_t ws_wT_offset(const moe_shape* s) {
+  size_t b = ws_plan_bytes(s);
+  if (ws_wrt_bytes(s) > b) b = ws_wrt_bytes(s);
+  if (ws_router_partial_bytes(s) > b) b = ws_router_partial_bytes(s);
+  return align_up(b, 256);
+}
 inline size_t ws_wT_down_bytes(const moe_shape* s) {
   return s->dtype == MOE_BF16 ? align_up((size_t)(s->E_l * s->F * s->d) * 2, 256) : 0;
 }
@@ -170,9 +179,15 @@ int launch_dispatch_bwd(const moe_shape* s, const void* dxp, const int32_t* row_
 int launch_ffn_fwd(const moe_shape* s, const void* xp, const int32_t* offsets,
                    const int32_t* tile_offsets, const void* W_gu, const void* W_down, void* h,
                    void* a, void* yp, hipStream_t st);
+// The bf16 dgrad's transposed weight copies (into ws at ws_wT_offset); a
+// no-op in float32.
+int launch_dgrad_weights(const moe_shape* s, const void* W_gu, const void* W_down, void* ws,
+                         hipStream_t st);
+// weights_ready: launch_dgrad_weights already ran on this ws (ordered before
+// this call), so the copies are not made again.
 int launch_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h, const int32_t* offsets,
                      const int32_t* tile_offsets, const void* W_gu, const void* W_down, void* dh,
-                     void* dxp, void* ws, hipStream_t st);
+                     void* dxp, void* ws, bool weights_ready, hipStream_t st);
 int launch_ffn_wgrad(const moe_shape* s, const void* xp, const void* a, const void* dh,
                      const void* dyp, const int32_t* offsets, float* dW_gu, float* dW_down,
                      bool accumulate, hipStream_t st);
