@@ -503,7 +503,8 @@ __device__ __forceinline__ int wg_byte(int k, int col) {
   return k * WG_ROWB + ((((col >> 4) ^ wg_swz(k)) & 15) << 5) + ((col & 15) << 1);
 }
 
-// Direct global -> LDS loader of a [64 k][256 col] tile.
+// Direct global -> LDS loader of a [64 k][256 col] tile (16 bytes per lane;
+// a wave instruction fills one contiguous 1 KiB block of LDS, addressed by m0).
 template <int NW>
 struct LoadKM {
   static constexpr int PER = BK / 2 / NW;  // wave instructions per stage
@@ -520,7 +521,17 @@ struct LoadKM {
       const int k = k0 + kr;
       const bool ok = (k < k_end) && (m0 + col < M);
       const uint16_t* src = ok ? base + (long)k * ld + m0 + col : g_zero_row + col;
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(lds + blk * 1024), 16, 0, 0);
+      // Issued by inline assembly: with the builtin the compiler treats these
+      // LDS writes as possibly aliasing every later LDS read and waits for the
+      // next stage's loads before reading the current stage, which serialises
+      // the prefetch.  Completion is awaited explicitly (vmcnt) before the
+      // barrier that publishes the stage.
+      const uint32_t m0v =
+          __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)(lds + blk * 1024));
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                   :
+                   : "v"(src), "s"(m0v)
+                   : "memory", "m0");
     }
   }
 };
