@@ -166,7 +166,8 @@ __device__ __forceinline__ void mfmas(const Frags<TL>& f, f32x16_t (&acc)[TL::TM
 
 // One 16-wide k slice: NM MFMAs, each followed by up to two LDS reads (the
 // next slice's fragments are all in flight after the first NR/2 MFMAs), one
-// global load and one LDS write (while those remain).
+// LDS write and one global load (while those remain; a chunk's load reuses
+// the registers its LDS write has just read).
 template <int NM, int NR, int NV, int NW>
 __device__ __forceinline__ void sched_slice() {
 #pragma unroll
@@ -174,13 +175,16 @@ __device__ __forceinline__ void sched_slice() {
     SCHED_GROUP(SG_MFMA, 1);
     if (2 * i < NR) SCHED_GROUP(SG_DS_R, 1);
     if (2 * i + 1 < NR) SCHED_GROUP(SG_DS_R, 1);
-    if (i < NV) SCHED_GROUP(SG_VMEM_R, 1);
     if (i < NW) SCHED_GROUP(SG_DS_W, 1);
+    if (i < NV) SCHED_GROUP(SG_VMEM_R, 1);
   }
 }
 
-// Two-stage LDS main loop over k in [k_begin, k_end), steps of 64.  The last
-// step reloads its own stage (harmless) so the loop body has no branches.
+// Two-stage LDS main loop over k in [k_begin, k_end), steps of 64.  The
+// registers hold the stage after the one being written to LDS: in step kt,
+// stage kt+1 goes from registers to LDS and the loads of stage kt+2 are issued
+// right behind it, so a load has four k slices to arrive.  Loads past the last
+// stage re-read it (harmless), so the loop body has no branches.
 template <class TL, class LA, class LB, bool SCHED = true>
 __device__ __forceinline__ void mainloop(LA& la, LB& lb, int k_begin, int k_end,
                                          uint16_t* smem, f32x16_t (&acc)[TL::TM][TL::TN]) {
@@ -204,6 +208,11 @@ __device__ __forceinline__ void mainloop(LA& la, LB& lb, int k_begin, int k_end,
   lb.load(k_begin, k_end);
   la.store(sA0);
   lb.store(sB0);
+  {
+    const int k1 = k_begin + (nk > 1 ? 1 : 0) * BK;
+    la.load(k1, k_end);
+    lb.load(k1, k_end);
+  }
   __syncthreads();
   Frags<TL> f0, f1;
   read_frags<TL>(f0, sA0, sB0, 0, wm, wn, lane);
@@ -213,12 +222,10 @@ __device__ __forceinline__ void mainloop(LA& la, LB& lb, int k_begin, int k_end,
     const uint16_t* B = odd ? sB1 : sB0;
     uint16_t* An = odd ? sA0 : sA1;
     uint16_t* Bn = odd ? sB0 : sB1;
-    const int kn = k_begin + (kt + 1 < nk ? kt + 1 : kt) * BK;
-    la.load(kn, k_end);
-    lb.load(kn, k_end);
+    const int kn2 = k_begin + (kt + 2 < nk ? kt + 2 : nk - 1) * BK;
     read_frags<TL>(f1, A, B, 1, wm, wn, lane);
     mfmas<TL>(f0, acc);
-    if constexpr (SCHED) sched_slice<NM, NR, NV, 0>();
+    if constexpr (SCHED) sched_slice<NM, NR, 0, 0>();
     read_frags<TL>(f0, A, B, 2, wm, wn, lane);
     mfmas<TL>(f1, acc);
     if constexpr (SCHED) sched_slice<NM, NR, 0, 0>();
@@ -226,7 +233,9 @@ __device__ __forceinline__ void mainloop(LA& la, LB& lb, int k_begin, int k_end,
     mfmas<TL>(f0, acc);
     la.store(An);
     lb.store(Bn);
-    if constexpr (SCHED) sched_slice<NM, NR, 0, NW>();
+    la.load(kn2, k_end);
+    lb.load(kn2, k_end);
+    if constexpr (SCHED) sched_slice<NM, NR, NV, NW>();
     // the next stage is complete once every wave passes the barrier; its
     // first fragments are read while the last slice's MFMAs run
     __syncthreads();
