@@ -31,6 +31,7 @@ MOE_ACCUM_DW = 2
 
 MOE_STEP_SERIALIZE = 1
 MOE_STEP_EAGER_WGRAD = 2
+MOE_STEP_SKIP_WGRAD = 4
 
 
 class MoeShape(C.Structure):

@@ -516,7 +516,7 @@ extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t 
   REQUIRE(st);
   const moe_shape* s = &st->shape;
   if (int rc = validate_shape(s)) return rc;
-  if (flags & ~(MOE_STEP_SERIALIZE | MOE_STEP_EAGER_WGRAD))
+  if (flags & ~(MOE_STEP_SERIALIZE | MOE_STEP_EAGER_WGRAD | MOE_STEP_SKIP_WGRAD))
     return set_error(MOE_ERR_ARG, "moe_overlap_step: unknown flags 0x%x", flags);
   const int mode = st->route_mode;
   if (mode != MOE_ROUTE_TOPK && mode != MOE_ROUTE_TOPK_FROM_LOGITS &&
@@ -546,6 +546,9 @@ extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t 
   StepCtx c{st, s, st->ws, (char*)st->ws + one, mode == MOE_ROUTE_TOPK};
   const bool serial = (flags & MOE_STEP_SERIALIZE) || s0 == s1;
   const bool eager = (flags & MOE_STEP_EAGER_WGRAD) != 0;
+  const bool skip_w = (flags & MOE_STEP_SKIP_WGRAD) != 0;
+  if (eager && skip_w)
+    return set_error(MOE_ERR_ARG, "moe_overlap_step: EAGER_WGRAD and SKIP_WGRAD exclude each other");
 
   if (serial) {  // the forward-then-backward order of a non-overlapped layer
     if (A) {
@@ -560,7 +563,7 @@ extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t 
       TRY(bwd_dgrad(c, B, false, s0));
       if (eager) TRY(bwd_wgrad(c, B, s0));
       TRY(bwd_dispatch(c, B, s0));
-      if (!eager) TRY(bwd_wgrad(c, B, s0));
+      if (!eager && !skip_w) TRY(bwd_wgrad(c, B, s0));
     }
     return MOE_OK;
   }
@@ -599,7 +602,7 @@ extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t 
   if (B) {
     HIPTRY(hipStreamWaitEvent(s1, ev->dgrad, 0));
     TRY(bwd_dispatch(c, B, s1));
-    if (!eager) TRY(bwd_wgrad(c, B, s0));  // deferred past A's expert GEMMs
+    if (!eager && !skip_w) TRY(bwd_wgrad(c, B, s0));  // deferred past A's expert GEMMs
   }
   if (A) {
     HIPTRY(hipStreamWaitEvent(s1, ev->fwd, 0));

@@ -75,6 +75,11 @@ extern "C" {
 #define MOE_STEP_SERIALIZE   1  /* everything on s_compute, forward then backward */
 #define MOE_STEP_EAGER_WGRAD 2  /* wgrad right after dgrad (not after the other
                                    micro-batch's forward GEMMs)                   */
+#define MOE_STEP_SKIP_WGRAD  4  /* leave the backward micro-batch's wgrad out: the
+                                   caller issues moe_ffn_wgrad later (e.g. while the
+                                   next layer's forward runs, page 1
+                                   delay_wgrad_compute); its inputs (xp, a, dh,
+                                   dyp, offsets of `bwd`) must then stay intact   */
 
 /*
  * Layer shape.  T tokens of hidden size d; E experts routed over, of which the

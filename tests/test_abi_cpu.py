@@ -137,3 +137,10 @@ def test_step_rejects_small_workspace_and_same_microbatch():
     st.bwd = None
     st.ws_bytes = 8
     assert M.lib().moe_overlap_step(C.byref(st), None, None, 0) == M.MOE_ERR_WORKSPACE
+    # eager and skipped wgrad exclude each other
+    mb2 = _lib.MoeMB(*([0x2000] * len(_lib.MB_FIELDS)))
+    st.bwd = C.pointer(mb2)
+    st.ws_bytes = 1 << 40
+    flags = M.MOE_STEP_EAGER_WGRAD | M.MOE_STEP_SKIP_WGRAD
+    assert M.lib().moe_overlap_step(C.byref(st), None, None, flags) == M.MOE_ERR_ARG
+    assert b"exclude" in M.lib().moe_last_error()

@@ -172,25 +172,36 @@ def test_overlap_equals_serialized_two_microbatch():
     s0 = torch.cuda.current_stream()
     s1 = torch.cuda.Stream()
     results = {}
+    def late_wgrad(mb, acc):  # the wgrad a SKIP_WGRAD step leaves to the caller
+        M.moe_ffn_wgrad(net.s, mb.xp, mb.a, mb.dh, mb.dyp, mb.offsets, net.dW_gu, net.dW_down,
+                        acc, s0)
+
     for tag, flags, copy in (("serial", M.MOE_STEP_SERIALIZE, s0), ("overlap", 0, s1),
-                             ("eager", M.MOE_STEP_EAGER_WGRAD, s1)):
+                             ("eager", M.MOE_STEP_EAGER_WGRAD, s1),
+                             ("skip", M.MOE_STEP_SKIP_WGRAD, s1)):
+        skip = flags == M.MOE_STEP_SKIP_WGRAD
         A = net.mb(inp["x"], inp["dout"])
         B = net.mb(inp["x_b"], inp["dout_b"])
         net.step(A, None, s0, copy, flags)
         net.step(B, A, s0, copy, flags)                        # A's grads overwrite
+        if skip:
+            late_wgrad(A, 0)
         net.step(None, B, s0, copy, flags, M.MOE_ACCUM_DW)     # B's grads accumulate
+        if skip:
+            late_wgrad(B, M.MOE_ACCUM_DW)
         torch.cuda.synchronize()
         results[tag] = dict(A=A, B=B, dW_gu=net.dW_gu.clone(), dW_down=net.dW_down.clone(),
                             dW_r=net.dW_r.clone())
     ref = results["serial"]
-    for tag in ("overlap", "eager"):
+    for tag in ("overlap", "eager", "skip"):
         r = results[tag]
         for mbn in ("A", "B"):
             for k in ("idx", "gates", "row_of_pair", "out", "dgates", "dlogits", "dx", "yp"):
                 assert torch.equal(getattr(r[mbn], k), getattr(ref[mbn], k)), (tag, mbn, k)
         for k in ("dW_gu", "dW_down", "dW_r"):
             assert torch.equal(r[k], ref[k]), (tag, k)
-    log("[overlap] overlapped and eager-wgrad steps bit-identical to serialized")
+    log("[overlap] overlapped, eager-wgrad and caller-deferred-wgrad steps bit-identical to "
+        "serialized")
     # oracle on samples of micro-batch A (weight grads hold A + B)
     r = results["overlap"]
     A, B = r["A"], r["B"]
