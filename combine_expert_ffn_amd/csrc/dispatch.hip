@@ -184,29 +184,73 @@ int launch_plan(const moe_shape* s, const int32_t* idx, int32_t* counts, int32_t
 }
 
 // ---------------------------------------------------------------------------
-// permute: xp[row_of_pair[t*K+k]] = x[t].  One wave per token, 16-byte chunks;
-// the token row is read once and written to each of its local rows.
+// Token-major kernels (permute, combine and their backwards): one wave per
+// token, lane l handles the 16-byte chunks l, l+64, ... of a row.  Row lengths
+// are multiples of 8 chunks but not always of 64, so loads use a clamped
+// (always valid) chunk index and only the stores are predicated: with no
+// branch between them, a row's loads, and those of the next row, are in
+// flight together instead of one at a time.
+// ---------------------------------------------------------------------------
+
+// The token's local rows: lane k (< K) holds row_of_pair[t*K + k]; the valid
+// slots form a wave-uniform bit mask, walked in ascending slot order, and a
+// slot's row is read from its lane, so everything stays in scalar registers.
+struct LocalRows {
+  uint64_t mask;
+  int rk;
+  __device__ __forceinline__ void load(const int32_t* __restrict__ row_of_pair, int t, int K,
+                                       int nrows, int lane) {
+    rk = lane < K ? row_of_pair[(size_t)t * K + lane] : -1;
+    mask = __ballot(rk >= 0 && rk < nrows);
+  }
+  __device__ __forceinline__ bool empty() const { return mask == 0; }
+  // next valid slot (ascending); the mask must not be empty
+  __device__ __forceinline__ int next() {
+    const int k = __ffsll((unsigned long long)mask) - 1;
+    mask &= mask - 1;
+    return k;
+  }
+  __device__ __forceinline__ int row(int k) const { return __builtin_amdgcn_readlane(rk, k); }
+};
+
+// Keep a loaded chunk in registers where it was loaded: without this the
+// compiler may move a side-effect-free load next to each of its uses (into a
+// conditional block or a loop), where its latency is no longer overlapped.
+__device__ __forceinline__ void pin(uint4& v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+
+__device__ __forceinline__ int uniform_token(int lane_tid_base) {
+  return __builtin_amdgcn_readfirstlane(lane_tid_base);
+}
+
+// ---------------------------------------------------------------------------
+// permute: xp[row_of_pair[t*K+k]] = x[t].  The token row is read once and
+// written to each of its local rows.
 // ---------------------------------------------------------------------------
 template <int MAXC>
 __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ x,
                                                       const int32_t* __restrict__ row_of_pair,
                                                       uint4* __restrict__ xp, int T, int K,
                                                       int nch) {
-  const int t = (int)(((long)blockIdx.x * 256 + threadIdx.x) >> 6);
+  const int t = uniform_token((int)(((long)blockIdx.x * 256 + threadIdx.x) >> 6));
   const int lane = threadIdx.x & 63;
   if (t >= T) return;
   const uint4* src = x + (size_t)t * nch;
+  LocalRows lr0;
+  lr0.load(row_of_pair, t, K, T * K, lane);
   for (int c0 = 0; c0 < nch; c0 += 64 * MAXC) {
     uint4 v[MAXC];
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
       const int c = c0 + lane + 64 * i;
-      if (c < nch) v[i] = src[c];
+      v[i] = src[c < nch ? c : nch - 1];
     }
-    for (int k = 0; k < K; ++k) {
-      const int r = row_of_pair[(size_t)t * K + k];
-      if (r < 0 || r >= T * K) continue;
-      uint4* dst = xp + (size_t)r * nch;
+    // (otherwise the loads are re-issued for every destination row)
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) pin(v[i]);
+    for (LocalRows lr = lr0; !lr.empty();) {
+      uint4* dst = xp + (size_t)lr.row(lr.next()) * nch;
 #pragma unroll
       for (int i = 0; i < MAXC; ++i) {
         const int c = c0 + lane + 64 * i;
@@ -240,28 +284,58 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
                                                       uint4* __restrict__ out, int T_, int K,
                                                       int nch) {
   constexpr int CN = Chunk<T>::N;
-  const int t = (int)(((long)blockIdx.x * 256 + threadIdx.x) >> 6);
+  const int t = uniform_token((int)(((long)blockIdx.x * 256 + threadIdx.x) >> 6));
   const int lane = threadIdx.x & 63;
   if (t >= T_) return;
+  LocalRows lr0;
+  lr0.load(row_of_pair, t, K, T_ * K, lane);
   for (int c0 = 0; c0 < nch; c0 += 64 * MAXC) {
+    int cc[MAXC];
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int c = c0 + lane + 64 * i;
+      cc[i] = c < nch ? c : nch - 1;
+    }
     float acc[MAXC][CN];
 #pragma unroll
     for (int i = 0; i < MAXC; ++i)
 #pragma unroll
       for (int q = 0; q < CN; ++q) acc[i][q] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int r = row_of_pair[(size_t)t * K + k];
-      if (r < 0 || r >= T_ * K) continue;
-      const float g = gates[(size_t)t * K + k];
-      const uint4* src = yp + (size_t)r * nch;
+    // two rows per pass: both rows' loads are issued before the first FMA;
+    // the sum still runs over the rows in ascending slot order
+    LocalRows lr = lr0;
+    while (!lr.empty()) {
+      const int k0 = lr.next();
+      const bool two = !lr.empty();
+      const int k1 = two ? lr.next() : k0;
+      const uint4* s0 = yp + (size_t)lr.row(k0) * nch;
+      const uint4* s1 = yp + (size_t)lr.row(k1) * nch;
+      uint4 v0[MAXC], v1[MAXC];
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) v0[i] = s0[cc[i]];
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) v1[i] = s1[cc[i]];
 #pragma unroll
       for (int i = 0; i < MAXC; ++i) {
-        const int c = c0 + lane + 64 * i;
-        if (c < nch) {
-          float f[CN];
-          Chunk<T>::unpack(src[c], f);
+        pin(v0[i]);
+        pin(v1[i]);
+      }
+      const float g0 = gates[(size_t)t * K + k0];
+      const float g1 = gates[(size_t)t * K + k1];
 #pragma unroll
-          for (int q = 0; q < CN; ++q) acc[i][q] = fmaf(g, f[q], acc[i][q]);
+      for (int i = 0; i < MAXC; ++i) {
+        float f[CN];
+        Chunk<T>::unpack(v0[i], f);
+#pragma unroll
+        for (int q = 0; q < CN; ++q) acc[i][q] = fmaf(g0, f[q], acc[i][q]);
+      }
+      if (two) {
+#pragma unroll
+        for (int i = 0; i < MAXC; ++i) {
+          float f[CN];
+          Chunk<T>::unpack(v1[i], f);
+#pragma unroll
+          for (int q = 0; q < CN; ++q) acc[i][q] = fmaf(g1, f[q], acc[i][q]);
         }
       }
     }
@@ -303,21 +377,28 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
                                                           float* __restrict__ dgates, int T_,
                                                           int K, int nch) {
   constexpr int CN = Chunk<T>::N;
-  const int t = (int)(((long)blockIdx.x * 256 + threadIdx.x) >> 6);
+  const int t = uniform_token((int)(((long)blockIdx.x * 256 + threadIdx.x) >> 6));
   const int lane = threadIdx.x & 63;
   if (t >= T_) return;
-  // nch <= 64 * MAXC is guaranteed by the launcher (whole row in registers)
+  // nch <= 64 * MAXC is guaranteed by the launcher (whole dout row in registers)
   float dv[MAXC][CN];
+  {
+    uint4 raw[MAXC];
 #pragma unroll
-  for (int i = 0; i < MAXC; ++i) {
-    const int c = lane + 64 * i;
-    if (c < nch) {
-      Chunk<T>::unpack(dout[(size_t)t * nch + c], dv[i]);
-    } else {
+    for (int i = 0; i < MAXC; ++i) {
+      const int c = lane + 64 * i;
+      raw[i] = dout[(size_t)t * nch + (c < nch ? c : nch - 1)];
+    }
 #pragma unroll
-      for (int q = 0; q < CN; ++q) dv[i][q] = 0.f;
+    for (int i = 0; i < MAXC; ++i) {
+      if constexpr (MAXC <= 4) pin(raw[i]);
+      Chunk<T>::unpack(raw[i], dv[i]);
     }
   }
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i)
+#pragma unroll
+    for (int q = 0; q < CN; ++q) dv[i][q] = lane + 64 * i < nch ? dv[i][q] : 0.f;
   for (int k = 0; k < K; ++k) {
     const int r = row_of_pair[(size_t)t * K + k];
     if (r < 0 || r >= T_ * K) {
@@ -326,18 +407,46 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
     }
     const float g = gates[(size_t)t * K + k];
     float dot = 0.f;
+    if constexpr (MAXC <= 4) {
+      // the row's chunks are loaded together (clamped indices), then used in
+      // chunk order
+      uint4 yv[MAXC];
 #pragma unroll
-    for (int i = 0; i < MAXC; ++i) {
-      const int c = lane + 64 * i;
-      if (c < nch) {
-        float y[CN], o[CN];
-        Chunk<T>::unpack(yp[(size_t)r * nch + c], y);
+      for (int i = 0; i < MAXC; ++i) {
+        const int c = lane + 64 * i;
+        yv[i] = yp[(size_t)r * nch + (c < nch ? c : nch - 1)];
+      }
 #pragma unroll
-        for (int q = 0; q < CN; ++q) {
-          dot = fmaf(dv[i][q], y[q], dot);
-          o[q] = g * dv[i][q];
+      for (int i = 0; i < MAXC; ++i) pin(yv[i]);
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nch) {
+          float y[CN], o[CN];
+          Chunk<T>::unpack(yv[i], y);
+#pragma unroll
+          for (int q = 0; q < CN; ++q) {
+            dot = fmaf(dv[i][q], y[q], dot);
+            o[q] = g * dv[i][q];
+          }
+          dyp[(size_t)r * nch + c] = Chunk<T>::pack(o);
         }
-        dyp[(size_t)r * nch + c] = Chunk<T>::pack(o);
+      }
+    } else {
+      // wide rows: the dout row already fills the registers
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nch) {
+          float y[CN], o[CN];
+          Chunk<T>::unpack(yp[(size_t)r * nch + c], y);
+#pragma unroll
+          for (int q = 0; q < CN; ++q) {
+            dot = fmaf(dv[i][q], y[q], dot);
+            o[q] = g * dv[i][q];
+          }
+          dyp[(size_t)r * nch + c] = Chunk<T>::pack(o);
+        }
       }
     }
     dot = wave_sum(dot);
@@ -389,31 +498,58 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(
     const uint4* __restrict__ W_rT, uint4* __restrict__ dx, int T_, int K, int E, int nch,
     int accumulate) {
   constexpr int CN = Chunk<T>::N;
-  const int t = (int)(((long)blockIdx.x * 256 + threadIdx.x) >> 6);
+  const int t = uniform_token((int)(((long)blockIdx.x * 256 + threadIdx.x) >> 6));
   const int lane = threadIdx.x & 63;
   if (t >= T_) return;
+  LocalRows lr0;
+  lr0.load(row_of_pair, t, K, T_ * K, lane);
   for (int c0 = 0; c0 < nch; c0 += 64 * MAXC) {
-    float acc[MAXC][CN];
+    int cc[MAXC];
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
       const int c = c0 + lane + 64 * i;
-      if (accumulate && c < nch) {
-        Chunk<T>::unpack(dx[(size_t)t * nch + c], acc[i]);
+      cc[i] = c < nch ? c : nch - 1;
+    }
+    float acc[MAXC][CN];
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      if (accumulate) {  // uniform
+        Chunk<T>::unpack(dx[(size_t)t * nch + cc[i]], acc[i]);
       } else {
 #pragma unroll
         for (int q = 0; q < CN; ++q) acc[i][q] = 0.f;
       }
     }
-    for (int k = 0; k < K; ++k) {
-      const int r = row_of_pair[(size_t)t * K + k];
-      if (r < 0 || r >= T_ * K) continue;
-      const uint4* src = dxp + (size_t)r * nch;
+    // two rows per pass, summed in ascending slot order
+    LocalRows lr = lr0;
+    while (!lr.empty()) {
+      const int k0 = lr.next();
+      const bool two = !lr.empty();
+      const int k1 = two ? lr.next() : k0;
+      const uint4* s0 = dxp + (size_t)lr.row(k0) * nch;
+      const uint4* s1 = dxp + (size_t)lr.row(k1) * nch;
+      uint4 v0[MAXC], v1[MAXC];
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) v0[i] = s0[cc[i]];
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) v1[i] = s1[cc[i]];
 #pragma unroll
       for (int i = 0; i < MAXC; ++i) {
-        const int c = c0 + lane + 64 * i;
-        if (c < nch) {
+        pin(v0[i]);
+        pin(v1[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) {
+        float f[CN];
+        Chunk<T>::unpack(v0[i], f);
+#pragma unroll
+        for (int q = 0; q < CN; ++q) acc[i][q] += f[q];
+      }
+      if (two) {
+#pragma unroll
+        for (int i = 0; i < MAXC; ++i) {
           float f[CN];
-          Chunk<T>::unpack(src[c], f);
+          Chunk<T>::unpack(v1[i], f);
 #pragma unroll
           for (int q = 0; q < CN; ++q) acc[i][q] += f[q];
         }
@@ -425,15 +561,15 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(
         if (e < 0 || e >= E) continue;
         const float gl = dlogits[(size_t)t * E + e];
         const uint4* wr = W_rT + (size_t)e * nch;
+        uint4 wv[MAXC];
+#pragma unroll
+        for (int i = 0; i < MAXC; ++i) wv[i] = wr[cc[i]];
 #pragma unroll
         for (int i = 0; i < MAXC; ++i) {
-          const int c = c0 + lane + 64 * i;
-          if (c < nch) {
-            float f[CN];
-            Chunk<T>::unpack(wr[c], f);
+          float f[CN];
+          Chunk<T>::unpack(wv[i], f);
 #pragma unroll
-            for (int q = 0; q < CN; ++q) acc[i][q] = fmaf(gl, f[q], acc[i][q]);
-          }
+          for (int q = 0; q < CN; ++q) acc[i][q] = fmaf(gl, f[q], acc[i][q]);
         }
       }
     }
