@@ -35,6 +35,7 @@ namespace moe {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int BK = 64;
@@ -49,33 +50,45 @@ __device__ __forceinline__ int lds_off(int row, int ch) {
   return row * BK + ((ch ^ s) << 3);
 }
 
-// Operand contiguous along K: R rows x 64 k per stage, 16-byte chunks.
-// row_ptr(r) gives a valid address of element k = 0 of tile row r (rows
-// outside the matrix are clamped by the caller).  K is a multiple of 64.
+// Operand contiguous along K: R rows x 64 k per stage, 16-byte chunks, read
+// with buffer loads: the operand base is a wave-uniform buffer resource
+// (scalar registers), each chunk a 32-bit byte offset in one vector register,
+// and the k position the scalar offset.  row_off(r) gives the element offset
+// from the base of element k = 0 of tile row r (rows outside the matrix are
+// clamped by the caller to valid ones); offsets stay below 2^31 bytes.  K is
+// a multiple of 64.
 template <int R, int NT>
 struct LoadK {
   static constexpr int CH = R * 8 / NT;
   static constexpr int NLOAD = CH, NSTORE = CH;
   static_assert(CH >= 1 && (R * 8) % NT == 0, "tile/threads mismatch");
-  const uint16_t* src[CH];
-  int dst[CH];
-  uint4 v[CH];
-  template <class RowPtr>
-  __device__ __forceinline__ void init(RowPtr row_ptr, int tid) {
+  // Chunk c of this thread is row c*NT/8 + tid/8, chunk tid%8; with NT a
+  // multiple of 128 the swizzle of those rows does not depend on c, so the
+  // LDS offsets are one register plus constants.
+  static_assert(NT % 128 == 0, "LDS offsets assume NT % 128 == 0");
+  static constexpr int DSTEP = NT / 8 * BK;
+  u32x4_t v[CH];  // the stage in flight
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t off[CH];  // bytes
+  int dst0;
+  template <class RowOff>
+  __device__ __forceinline__ void init(const uint16_t* base, RowOff row_off, int tid) {
+    // raw buffer (stride 0); the records limit is never reached: every
+    // offset is a valid element of the operand
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7fffffff, 0x00020000);
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int q = c * NT + tid, row = q >> 3, ch = q & 7;
-      src[c] = row_ptr(row) + ch * 8;
-      dst[c] = lds_off(row, ch);
-    }
+    for (int c = 0; c < CH; ++c)
+      off[c] = (uint32_t)row_off(c * (NT / 8) + (tid >> 3)) * 2u + (uint32_t)(tid & 7) * 16u;
+    dst0 = lds_off(tid >> 3, tid & 7);
   }
   __device__ __forceinline__ void load(int k0, int /*k_end*/) {
 #pragma unroll
-    for (int c = 0; c < CH; ++c) v[c] = *(const uint4*)(src[c] + k0);
+    for (int c = 0; c < CH; ++c)
+      v[c] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off[c], k0 * 2, 0);
   }
   __device__ __forceinline__ void store(uint16_t* lds) const {
 #pragma unroll
-    for (int c = 0; c < CH; ++c) *(uint4*)(lds + dst[c]) = v[c];
+    for (int c = 0; c < CH; ++c) *(u32x4_t*)(lds + dst0 + c * DSTEP) = v[c];
   }
 };
 
@@ -98,13 +111,14 @@ __device__ __forceinline__ int out_row(int lane, int r) {
 
 // Epilogue staging: the 32 x 64 accumulator block acc[i][2p], acc[i][2p+1]
 // of a wave is written to the wave's own LDS area, row-major with EP_LD floats
-// per row, so that each lane can then read 32 consecutive columns of one row
-// (lane l: row l/2, columns 32*(l%2)..+32 of the block).  The epilogues'
-// global accesses become 16-byte and contiguous along rows.  The LDS must be
-// free (the main loop ends with a barrier); the caller synchronises before the
-// next tile writes it.  LDS operations of one wave complete in order, so a
-// lane may read what other lanes of its wave wrote just before.
-constexpr int EP_LD = 68;  // 64 + 4: the row-run reads are free of bank conflicts
+// per row, and read back by rows, so that the epilogues' global accesses are
+// 16 bytes per lane and whole rows per group of lanes: in pass q (0..3) lane l
+// takes row 8q + l/8, columns 8(l%8)..+8, and one store instruction writes
+// eight 128-byte rows.  The LDS must be free (the main loop ends with a
+// barrier); the caller synchronises before the next tile writes it.  LDS
+// operations of one wave complete in order, so a lane may read what other
+// lanes of its wave wrote just before.
+constexpr int EP_LD = 68;  // 64 + 4 floats per staged row
 template <class TL>
 __device__ __forceinline__ const float* stage_rows(const f32x16_t (&acc)[TL::TM][TL::TN], int i,
                                                    int p, uint16_t* smem, int wave, int lane) {
@@ -116,7 +130,7 @@ __device__ __forceinline__ const float* stage_rows(const f32x16_t (&acc)[TL::TM]
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       reg[out_row(lane, r) * EP_LD + j * 32 + (lane & 31)] = acc[i][2 * p + j][r];
-  return reg + (lane >> 1) * EP_LD + (lane & 1) * 32;
+  return reg;
 }
 
 // Eight consecutive staged floats.
@@ -126,13 +140,21 @@ __device__ __forceinline__ void ld8(const float* p, float* f) {
   f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
-// Store a staged 32-column run as bf16 (four 16-byte stores).
-__device__ __forceinline__ void store_run32(const float* src, uint16_t* dst) {
+// Staged row of pass q for this lane, and its 8-column chunk.
+__device__ __forceinline__ int st_row(int q, int lane) { return q * 8 + (lane >> 3); }
+__device__ __forceinline__ int st_col(int lane) { return (lane & 7) * 8; }
+
+// Store a staged 32 x 64 block as bf16 rows: out_row0 points at column 0 of
+// the block's first row, ld is the row stride, rows at or past n_rows are
+// skipped.
+__device__ __forceinline__ void store_block(const float* blk, uint16_t* out_row0, size_t ld,
+                                            int n_rows, int lane) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
+    const int r = st_row(q, lane), c = st_col(lane);
     float f[8];
-    ld8(src + q * 8, f);
-    *(uint4*)(dst + q * 8) = Chunk<uint16_t>::pack(f);
+    ld8(blk + r * EP_LD + c, f);
+    if (r < n_rows) *(uint4*)(out_row0 + r * ld + c) = Chunk<uint16_t>::pack(f);
   }
 }
 
@@ -180,40 +202,46 @@ __device__ __forceinline__ void sched_slice() {
   }
 }
 
-// Two-stage LDS main loop over k in [k_begin, k_end), steps of 64.  The
-// registers hold the stage after the one being written to LDS: in step kt,
-// stage kt+1 goes from registers to LDS and the loads of stage kt+2 are issued
-// right behind it, so a load has four k slices to arrive.  Loads past the last
-// stage re-read it (harmless), so the loop body has no branches.
+// Wave position inside the block tile.  The wave index is moved to a scalar
+// register and the lane index is recomputed where it is needed (from the exec
+// mask count, made opaque to the optimiser), so addresses derived from it are
+// computed next to their use instead of being hoisted out of the tile loop
+// and held in vector registers across the main loop.
+struct WavePos {
+  int lane, wave, wm, wn;
+  template <class TL>
+  __device__ __forceinline__ static WavePos of() {
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    int l = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(l));
+    return {l, w, w / TL::WGN, w % TL::WGN};
+  }
+};
+
+// Two-stage LDS main loop, steps of 64 k from k_begin, once stage 0 is in LDS
+// buffer 0 (published by a barrier) and the loads of stage 1 are in the
+// loaders' registers.  The registers hold the stage after the one being
+// written to LDS: in step kt, stage kt+1 goes from registers to LDS and the
+// loads of stage kt+2 are issued right behind it, so a load has four k slices
+// to arrive.  Loads past the last stage re-read it (harmless), so the loop
+// body has no branches.  Ends with a barrier: the LDS is free on return.
 template <class TL, class LA, class LB, bool SCHED = true>
-__device__ __forceinline__ void mainloop(LA& la, LB& lb, int k_begin, int k_end,
-                                         uint16_t* smem, f32x16_t (&acc)[TL::TM][TL::TN]) {
+__device__ __forceinline__ void mainloop_steps(LA& la, LB& lb, int k_begin, int nk,
+                                               uint16_t* smem, f32x16_t (&acc)[TL::TM][TL::TN]) {
   uint16_t* const sA0 = smem;
   uint16_t* const sA1 = smem + TL::BM * BK;
   uint16_t* const sB0 = smem + 2 * TL::BM * BK;
   uint16_t* const sB1 = sB0 + TL::BN * BK;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / TL::WGN, wn = wave % TL::WGN;
+  const WavePos w = WavePos::of<TL>();
+  const int lane = w.lane, wm = w.wm, wn = w.wn;
 #pragma unroll
   for (int i = 0; i < TL::TM; ++i)
 #pragma unroll
     for (int j = 0; j < TL::TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  const int nk = (k_end - k_begin + BK - 1) / BK;
-  if (nk <= 0) return;  // block-uniform
   constexpr int NM = TL::TM * TL::TN, NR = TL::TM + TL::TN;
   constexpr int NV = LA::NLOAD + LB::NLOAD, NW = LA::NSTORE + LB::NSTORE;
-  la.load(k_begin, k_end);
-  lb.load(k_begin, k_end);
-  la.store(sA0);
-  lb.store(sB0);
-  {
-    const int k1 = k_begin + (nk > 1 ? 1 : 0) * BK;
-    la.load(k1, k_end);
-    lb.load(k1, k_end);
-  }
-  __syncthreads();
   Frags<TL> f0, f1;
   read_frags<TL>(f0, sA0, sB0, 0, wm, wn, lane);
   for (int kt = 0; kt < nk; ++kt) {
@@ -233,8 +261,8 @@ __device__ __forceinline__ void mainloop(LA& la, LB& lb, int k_begin, int k_end,
     mfmas<TL>(f0, acc);
     la.store(An);
     lb.store(Bn);
-    la.load(kn2, k_end);
-    lb.load(kn2, k_end);
+    la.load(kn2, 0);
+    lb.load(kn2, 0);
     if constexpr (SCHED) sched_slice<NM, NR, NV, NW>();
     // the next stage is complete once every wave passes the barrier; its
     // first fragments are read while the last slice's MFMAs run
@@ -243,7 +271,34 @@ __device__ __forceinline__ void mainloop(LA& la, LB& lb, int k_begin, int k_end,
     mfmas<TL>(f1, acc);
     if constexpr (SCHED) sched_slice<NM, NR, 0, 0>();
   }
-  __syncthreads();  // LDS free for the caller's next tile
+  __syncthreads();  // LDS free for the caller's epilogue / next tile
+}
+
+// The whole main loop over k in [k_begin, k_end) (a multiple of 64 long)
+// for a tile whose loaders are initialised: stage 0 to LDS, stage 1 to
+// registers, then the steps.
+template <class TL, class LA, class LB>
+__device__ __forceinline__ void mainloop(LA& la, LB& lb, int k_begin, int k_end,
+                                         uint16_t* smem, f32x16_t (&acc)[TL::TM][TL::TN]) {
+  const int nk = (k_end - k_begin + BK - 1) / BK;
+  if (nk <= 0) {  // block-uniform
+#pragma unroll
+    for (int i = 0; i < TL::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TL::TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    return;
+  }
+  la.load(k_begin, k_end);
+  lb.load(k_begin, k_end);
+  la.store(smem);
+  lb.store(smem + 2 * TL::BM * BK);
+  const int k1 = k_begin + (nk > 1 ? 1 : 0) * BK;
+  la.load(k1, k_end);
+  lb.load(k1, k_end);
+  __syncthreads();
+  mainloop_steps<TL>(la, lb, k_begin, nk, smem, acc);
 }
 
 // Persistent schedule: the blocks form G = min(8, grid) groups by block % G
@@ -274,10 +329,23 @@ __device__ __forceinline__ void row_tile(const int* s_to, const int* s_off, int 
   m0 = s_off[lo] + (mt - s_to[lo]) * kTileM;
   m_end = s_off[lo + 1];
 }
+// The same, moved to scalar registers (the values are block-uniform), so the
+// operand bases built from them are scalar.
+__device__ __forceinline__ void uniform_row_tile(const int* s_to, const int* s_off, int E_l,
+                                                 int mt, int& e, int& m0, int& m_end) {
+  row_tile(s_to, s_off, E_l, mt, e, m0, m_end);
+  e = __builtin_amdgcn_readfirstlane(e);
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  m_end = __builtin_amdgcn_readfirstlane(m_end);
+}
 
 // ---------------------------------------------------------------------------
 // Row-grouped GEMM (forward and dgrad): M tiles follow the dispatch plan, N
-// tiles are fixed.  Op supplies the loaders, the K extent and the epilogue.
+// tiles are fixed.  Op supplies the loaders (init), the K extent (k_len) and
+// the epilogue.  Tiles are software-pipelined across the persistent loop: the
+// first two stages of the next tile are loaded before the epilogue of the
+// current one issues its stores, so the next main loop does not wait for
+// those stores to complete (the vector memory counter retires in order).
 // ---------------------------------------------------------------------------
 template <class TL, class Op>
 __global__ __launch_bounds__(TL::NT) void row_grouped_kernel(Op op,
@@ -292,13 +360,42 @@ __global__ __launch_bounds__(TL::NT) void row_grouped_kernel(Op op,
     s_off[j] = offsets[j];
   }
   __syncthreads();
-  for (Sched sc(s_to[E_l] * n_tiles); sc.t < sc.end; sc.t += sc.step) {
-    int e, m0, m_end;
-    row_tile(s_to, s_off, E_l, sc.t / n_tiles, e, m0, m_end);
-    op.template run<TL>(e, m0, m_end, sc.t % n_tiles, smem);
-    __syncthreads();  // epilogue staging done before the next tile's loads land in LDS
+  Sched sc(s_to[E_l] * n_tiles);
+  if (sc.t >= sc.end) return;  // block-uniform
+  const int tid = threadIdx.x;
+  const int nk = (op.k_len() + BK - 1) / BK;  // >= 1: K is a positive multiple of 64
+  const int k1 = (nk > 1 ? 1 : 0) * BK;
+  LoadK<TL::BM, TL::NT> la;
+  LoadK<TL::BN, TL::NT> lb;
+  int e, m0, m_end, nt = sc.t % n_tiles;
+  uniform_row_tile(s_to, s_off, E_l, sc.t / n_tiles, e, m0, m_end);
+  op.template init<TL>(e, m0, m_end, nt, la, lb, tid);
+  la.load(0, 0);
+  lb.load(0, 0);
+  for (;;) {
+    la.store(smem);
+    lb.store(smem + 2 * TL::BM * BK);
+    la.load(k1, 0);
+    lb.load(k1, 0);
+    __syncthreads();
+    f32x16_t acc[TL::TM][TL::TN];
+    mainloop_steps<TL>(la, lb, 0, nk, smem, acc);
+    const int ce = e, cm0 = m0, cm_end = m_end, cnt = nt;
+    sc.t += sc.step;
+    const bool more = sc.t < sc.end;  // block-uniform
+    if (more) {
+      nt = sc.t % n_tiles;
+      uniform_row_tile(s_to, s_off, E_l, sc.t / n_tiles, e, m0, m_end);
+      op.template init<TL>(e, m0, m_end, nt, la, lb, tid);
+      la.load(0, 0);
+      lb.load(0, 0);
+    }
+    op.template epilogue<TL>(acc, ce, cm0, cm_end, cnt, smem);
+    __syncthreads();  // epilogue staging done before the next tile's stage 0 lands in LDS
+    if (!more) break;
   }
 }
+
 
 // forward GEMM1: [g, u] = xp . W_gu[e]^T with the SwiGLU epilogue.  The B tile
 // pairs gate and up rows: every 64 tile rows are 32 gate rows j and the 32 up
@@ -310,44 +407,47 @@ struct GateUpOp {
   uint16_t* h;
   uint16_t* a;
   int d, F;
-  template <class TL>
-  __device__ __forceinline__ void run(int e, int m0, int m_end, int nt, uint16_t* smem) const {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / TL::WGN, wn = wave % TL::WGN;
+  __device__ __forceinline__ int k_len() const { return d; }
+  template <class TL, class LA, class LB>
+  __device__ __forceinline__ void init(int e, int m0, int m_end, int nt, LA& la, LB& lb,
+                                       int tid) const {
     const int jb = nt * (TL::BN / 2);
     const uint16_t* Wg = W_gu + (size_t)e * 2 * F * d;
-    LoadK<TL::BM, TL::NT> la;
-    LoadK<TL::BN, TL::NT> lb;
-    la.init([&](int r) { return xp + (size_t)min(m0 + r, m_end - 1) * d; }, tid);
-    lb.init([&](int n) {
+    la.init(xp + (size_t)m0 * d, [&](int r) { return (min(m0 + r, m_end - 1) - m0) * d; }, tid);
+    lb.init(Wg, [&](int n) {
       const int j = min(jb + (n >> 6) * 32 + (n & 31), F - 1);
-      return Wg + (size_t)(((n >> 5) & 1) * F + j) * d;
+      return (((n >> 5) & 1) * F + j) * d;
     }, tid);
-    f32x16_t acc[TL::TM][TL::TN];
-    mainloop<TL>(la, lb, 0, d, smem, acc);
-    // staged block p: columns 0..31 gate, 32..63 up of outputs
-    // jb + (wn*TN/2 + p)*32 + c; this lane writes 16 outputs of its row
-    const int half = lane & 1;
+  }
+  // staged block p: columns 0..31 gate, 32..63 up of the 32 outputs starting
+  // at jb + (wn*TN/2 + p)*32; in pass q a lane takes row 16q + l/4 and
+  // outputs 8(l%4)..+8 (four lanes cover a row's 64 bytes of each output)
+  template <class TL>
+  __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TL::TM][TL::TN], int e, int m0,
+                                           int m_end, int nt, uint16_t* smem) const {
+    const WavePos w = WavePos::of<TL>();
+    const int jb = nt * (TL::BN / 2);
 #pragma unroll
     for (int p = 0; p < TL::TN / 2; ++p) {
-      const int j0 = jb + (wn * (TL::TN / 2) + p) * 32 + half * 16;
+      const int j0 = jb + (w.wn * (TL::TN / 2) + p) * 32 + (w.lane & 3) * 8;
       const bool col_ok = j0 < F;  // F is a multiple of 64
 #pragma unroll
       for (int i = 0; i < TL::TM; ++i) {
-        const int rt = wm * TL::WTM + i * 32 + (lane >> 1);
-        const float* src = stage_rows<TL>(acc, i, p, smem, wave, lane) - half * 16;
-        if (col_ok && m0 + rt < m_end) {
-          const size_t row = (size_t)(m0 + rt);
+        const float* blk = stage_rows<TL>(acc, i, p, smem, w.wave, w.lane);
+        const int rb = m0 + w.wm * TL::WTM + i * 32;
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            float g[8], u[8], av[8];
-            ld8(src + q * 8, g);
-            ld8(src + 32 + q * 8, u);
+        for (int q = 0; q < 2; ++q) {
+          const int r = q * 16 + (w.lane >> 2);
+          float g[8], u[8], av[8];
+          ld8(blk + r * EP_LD + (w.lane & 3) * 8, g);
+          ld8(blk + r * EP_LD + 32 + (w.lane & 3) * 8, u);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) av[t] = silu_f(g[t]) * u[t];
-            *(uint4*)(h + row * 2 * F + j0 + q * 8) = Chunk<uint16_t>::pack(g);
-            *(uint4*)(h + row * 2 * F + F + j0 + q * 8) = Chunk<uint16_t>::pack(u);
-            *(uint4*)(a + row * F + j0 + q * 8) = Chunk<uint16_t>::pack(av);
+          for (int t = 0; t < 8; ++t) av[t] = silu_f(g[t]) * u[t];
+          if (col_ok && rb + r < m_end) {
+            const size_t row = (size_t)(rb + r);
+            *(uint4*)(h + row * 2 * F + j0) = Chunk<uint16_t>::pack(g);
+            *(uint4*)(h + row * 2 * F + F + j0) = Chunk<uint16_t>::pack(u);
+            *(uint4*)(a + row * F + j0) = Chunk<uint16_t>::pack(av);
           }
         }
       }
@@ -361,27 +461,28 @@ struct DownOp {
   const uint16_t* W_down;
   uint16_t* yp;
   int d, F;
-  template <class TL>
-  __device__ __forceinline__ void run(int e, int m0, int m_end, int nt, uint16_t* smem) const {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / TL::WGN, wn = wave % TL::WGN;
+  __device__ __forceinline__ int k_len() const { return F; }
+  template <class TL, class LA, class LB>
+  __device__ __forceinline__ void init(int e, int m0, int m_end, int nt, LA& la, LB& lb,
+                                       int tid) const {
     const int nb = nt * TL::BN;
     const uint16_t* Wd = W_down + (size_t)e * d * F;
-    LoadK<TL::BM, TL::NT> la;
-    LoadK<TL::BN, TL::NT> lb;
-    la.init([&](int r) { return a + (size_t)min(m0 + r, m_end - 1) * F; }, tid);
-    lb.init([&](int n) { return Wd + (size_t)min(nb + n, d - 1) * F; }, tid);
-    f32x16_t acc[TL::TM][TL::TN];
-    mainloop<TL>(la, lb, 0, F, smem, acc);
+    la.init(a + (size_t)m0 * F, [&](int r) { return (min(m0 + r, m_end - 1) - m0) * F; }, tid);
+    lb.init(Wd, [&](int n) { return min(nb + n, d - 1) * F; }, tid);
+  }
+  template <class TL>
+  __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TL::TM][TL::TN], int e, int m0,
+                                           int m_end, int nt, uint16_t* smem) const {
+    const WavePos w = WavePos::of<TL>();
 #pragma unroll
     for (int p = 0; p < TL::TN / 2; ++p) {
-      const int c0 = nb + wn * TL::WTN + p * 64 + (lane & 1) * 32;
-      const bool col_ok = c0 < d;  // d is a multiple of 64
+      const int cb = nt * TL::BN + w.wn * TL::WTN + p * 64;
+      if (cb >= d) continue;  // d is a multiple of 64; wave-uniform
 #pragma unroll
       for (int i = 0; i < TL::TM; ++i) {
-        const int rt = wm * TL::WTM + i * 32 + (lane >> 1);
-        const float* src = stage_rows<TL>(acc, i, p, smem, wave, lane);
-        if (col_ok && m0 + rt < m_end) store_run32(src, yp + (size_t)(m0 + rt) * d + c0);
+        const int rb = m0 + w.wm * TL::WTM + i * 32;
+        const float* blk = stage_rows<TL>(acc, i, p, smem, w.wave, w.lane);
+        store_block(blk, yp + (size_t)rb * d + cb, (size_t)d, m_end - rb, w.lane);
       }
     }
   }
@@ -395,53 +496,55 @@ struct DgradActOp {
   const uint16_t* W_downT;
   uint16_t* dh;
   int d, F;
-  template <class TL>
-  __device__ __forceinline__ void run(int e, int m0, int m_end, int nt, uint16_t* smem) const {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / TL::WGN, wn = wave % TL::WGN;
+  __device__ __forceinline__ int k_len() const { return d; }
+  template <class TL, class LA, class LB>
+  __device__ __forceinline__ void init(int e, int m0, int m_end, int nt, LA& la, LB& lb,
+                                       int tid) const {
     const int nb = nt * TL::BN;
     const uint16_t* WdT = W_downT + (size_t)e * F * d;
-    LoadK<TL::BM, TL::NT> la;
-    LoadK<TL::BN, TL::NT> lb;
-    la.init([&](int r) { return dyp + (size_t)min(m0 + r, m_end - 1) * d; }, tid);
-    lb.init([&](int n) { return WdT + (size_t)min(nb + n, F - 1) * d; }, tid);
-    f32x16_t acc[TL::TM][TL::TN];
-    mainloop<TL>(la, lb, 0, d, smem, acc);
-    // h runs of this lane's row are loaded (16 bytes at a time, row clamped
-    // to a valid one) before the block is staged, so their latency overlaps
-    // the staging
+    la.init(dyp + (size_t)m0 * d, [&](int r) { return (min(m0 + r, m_end - 1) - m0) * d; }, tid);
+    lb.init(WdT, [&](int n) { return min(nb + n, F - 1) * d; }, tid);
+  }
+  // The h chunks of this lane's rows are loaded (16 bytes each, rows clamped
+  // to valid ones) before the block is staged, so their latency overlaps the
+  // staging.
+  template <class TL>
+  __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TL::TM][TL::TN], int e, int m0,
+                                           int m_end, int nt, uint16_t* smem) const {
+    const WavePos w = WavePos::of<TL>();
+    const int c = st_col(w.lane);
 #pragma unroll
     for (int p = 0; p < TL::TN / 2; ++p) {
-      const int c0 = nb + wn * TL::WTN + p * 64 + (lane & 1) * 32;
-      const bool col_ok = c0 < F;  // F is a multiple of 64
-      const int cc = col_ok ? c0 : F - 32;
+      const int cb = nt * TL::BN + w.wn * TL::WTN + p * 64;
+      if (cb >= F) continue;  // F is a multiple of 64; wave-uniform
 #pragma unroll
       for (int i = 0; i < TL::TM; ++i) {
-        const int rt = wm * TL::WTM + i * 32 + (lane >> 1);
-        const size_t rowc = (size_t)min(m0 + rt, m_end - 1);
+        const int rb = m0 + w.wm * TL::WTM + i * 32;
         uint4 gv[4], uv[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          gv[q] = *(const uint4*)(hbuf + rowc * 2 * F + cc + q * 8);
-          uv[q] = *(const uint4*)(hbuf + rowc * 2 * F + F + cc + q * 8);
+          const size_t rowc = (size_t)min(rb + st_row(q, w.lane), m_end - 1);
+          gv[q] = *(const uint4*)(hbuf + rowc * 2 * F + cb + c);
+          uv[q] = *(const uint4*)(hbuf + rowc * 2 * F + F + cb + c);
         }
-        const float* src = stage_rows<TL>(acc, i, p, smem, wave, lane);
-        if (col_ok && m0 + rt < m_end) {
-          const size_t row = (size_t)(m0 + rt);
+        const float* blk = stage_rows<TL>(acc, i, p, smem, w.wave, w.lane);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float da[8], g[8], u[8], dg[8], du[8];
-            ld8(src + q * 8, da);
-            Chunk<uint16_t>::unpack(gv[q], g);
-            Chunk<uint16_t>::unpack(uv[q], u);
+        for (int q = 0; q < 4; ++q) {
+          const int r = st_row(q, w.lane);
+          float da[8], g[8], u[8], dg[8], du[8];
+          ld8(blk + r * EP_LD + c, da);
+          Chunk<uint16_t>::unpack(gv[q], g);
+          Chunk<uint16_t>::unpack(uv[q], u);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-              const float sg = sigmoid_f(g[t]);
-              dg[t] = da[t] * u[t] * sg * (1.0f + g[t] * (1.0f - sg));
-              du[t] = da[t] * g[t] * sg;
-            }
-            *(uint4*)(dh + row * 2 * F + c0 + q * 8) = Chunk<uint16_t>::pack(dg);
-            *(uint4*)(dh + row * 2 * F + F + c0 + q * 8) = Chunk<uint16_t>::pack(du);
+          for (int t = 0; t < 8; ++t) {
+            const float sg = sigmoid_f(g[t]);
+            dg[t] = da[t] * u[t] * sg * (1.0f + g[t] * (1.0f - sg));
+            du[t] = da[t] * g[t] * sg;
+          }
+          if (rb + r < m_end) {
+            const size_t row = (size_t)(rb + r);
+            *(uint4*)(dh + row * 2 * F + cb + c) = Chunk<uint16_t>::pack(dg);
+            *(uint4*)(dh + row * 2 * F + F + cb + c) = Chunk<uint16_t>::pack(du);
           }
         }
       }
@@ -456,27 +559,29 @@ struct DgradInOp {
   const uint16_t* W_guT;
   uint16_t* dxp;
   int d, F;
-  template <class TL>
-  __device__ __forceinline__ void run(int e, int m0, int m_end, int nt, uint16_t* smem) const {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / TL::WGN, wn = wave % TL::WGN;
+  __device__ __forceinline__ int k_len() const { return 2 * F; }
+  template <class TL, class LA, class LB>
+  __device__ __forceinline__ void init(int e, int m0, int m_end, int nt, LA& la, LB& lb,
+                                       int tid) const {
     const int nb = nt * TL::BN;
     const uint16_t* WgT = W_guT + (size_t)e * d * 2 * F;
-    LoadK<TL::BM, TL::NT> la;
-    LoadK<TL::BN, TL::NT> lb;
-    la.init([&](int r) { return dh + (size_t)min(m0 + r, m_end - 1) * 2 * F; }, tid);
-    lb.init([&](int n) { return WgT + (size_t)min(nb + n, d - 1) * 2 * F; }, tid);
-    f32x16_t acc[TL::TM][TL::TN];
-    mainloop<TL>(la, lb, 0, 2 * F, smem, acc);
+    la.init(dh + (size_t)m0 * 2 * F, [&](int r) { return (min(m0 + r, m_end - 1) - m0) * 2 * F; },
+            tid);
+    lb.init(WgT, [&](int n) { return min(nb + n, d - 1) * 2 * F; }, tid);
+  }
+  template <class TL>
+  __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TL::TM][TL::TN], int e, int m0,
+                                           int m_end, int nt, uint16_t* smem) const {
+    const WavePos w = WavePos::of<TL>();
 #pragma unroll
     for (int p = 0; p < TL::TN / 2; ++p) {
-      const int c0 = nb + wn * TL::WTN + p * 64 + (lane & 1) * 32;
-      const bool col_ok = c0 < d;  // d is a multiple of 64
+      const int cb = nt * TL::BN + w.wn * TL::WTN + p * 64;
+      if (cb >= d) continue;  // d is a multiple of 64; wave-uniform
 #pragma unroll
       for (int i = 0; i < TL::TM; ++i) {
-        const int rt = wm * TL::WTM + i * 32 + (lane >> 1);
-        const float* src = stage_rows<TL>(acc, i, p, smem, wave, lane);
-        if (col_ok && m0 + rt < m_end) store_run32(src, dxp + (size_t)(m0 + rt) * d + c0);
+        const int rb = m0 + w.wm * TL::WTM + i * 32;
+        const float* blk = stage_rows<TL>(acc, i, p, smem, w.wave, w.lane);
+        store_block(blk, dxp + (size_t)rb * d + cb, (size_t)d, m_end - rb, w.lane);
       }
     }
   }
@@ -725,8 +830,8 @@ __global__ __launch_bounds__(TL::NT) void router_kernel(
     const int m0 = (sc.t / n_tiles) * TL::BM, n0 = (sc.t % n_tiles) * TL::BN;
     LoadK<TL::BM, TL::NT> la;
     LoadK<TL::BN, TL::NT> lb;
-    la.init([&](int r) { return x + (size_t)min(m0 + r, T - 1) * d; }, tid);
-    lb.init([&](int n) { return W_rT + (size_t)min(n0 + n, E - 1) * d; }, tid);
+    la.init(x + (size_t)m0 * d, [&](int r) { return (min(m0 + r, T - 1) - m0) * d; }, tid);
+    lb.init(W_rT + (size_t)n0 * d, [&](int n) { return (min(n0 + n, E - 1) - n0) * d; }, tid);
     f32x16_t acc[TL::TM][TL::TN];
     mainloop<TL>(la, lb, 0, d, smem, acc);
 #pragma unroll
