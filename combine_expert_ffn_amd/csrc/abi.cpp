@@ -573,40 +573,22 @@ extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t 
   // s1 starts after everything already queued on s0
   HIPTRY(hipEventRecord(ev->start, s0));
   HIPTRY(hipStreamWaitEvent(s1, ev->start, 0));
-  if (B) {
-    TRY(bwd_combine(c, B, s1));
-    HIPTRY(hipEventRecord(ev->cb, s1));
-  }
-  if (A) {
-    TRY(fwd_route(c, A, s0));
-    HIPTRY(hipEventRecord(ev->route, s0));
-  }
-  if (B) {
-    // the dgrad's weight copies need nothing from this step: made on s0 while
-    // s1 runs B's combine backward
-    TRY(bwd_dgrad_weights(c, s0));
-    HIPTRY(hipStreamWaitEvent(s0, ev->cb, 0));
-    TRY(bwd_route(c, B, s0));
-    TRY(bwd_dgrad(c, B, true, s0));
-    HIPTRY(hipEventRecord(ev->dgrad, s0));
-    if (eager) TRY(bwd_wgrad(c, B, s0));
-  }
-  if (A) {
-    HIPTRY(hipStreamWaitEvent(s1, ev->route, 0));
+  // The micro-batches share no buffers (each has its own half of the
+  // workspace), so each runs in order on its own stream and the hardware
+  // interleaves the two streams' kernels.
+  if (A) {  // the forward micro-batch, start to end on s1
+    TRY(fwd_route(c, A, s1));
     TRY(fwd_dispatch(c, A, s1));
-    HIPTRY(hipEventRecord(ev->disp, s1));
-    HIPTRY(hipStreamWaitEvent(s0, ev->disp, 0));
-    TRY(fwd_ffn(c, A, s0));
-    HIPTRY(hipEventRecord(ev->fwd, s0));
-  }
-  if (B) {
-    HIPTRY(hipStreamWaitEvent(s1, ev->dgrad, 0));
-    TRY(bwd_dispatch(c, B, s1));
-    if (!eager && !skip_w) TRY(bwd_wgrad(c, B, s0));  // deferred past A's expert GEMMs
-  }
-  if (A) {
-    HIPTRY(hipStreamWaitEvent(s1, ev->fwd, 0));
+    TRY(fwd_ffn(c, A, s1));
     TRY(fwd_combine(c, A, s1));
+  }
+  if (B) {  // the backward micro-batch on s0
+    TRY(bwd_combine(c, B, s0));
+    TRY(bwd_route(c, B, s0));
+    TRY(bwd_dgrad(c, B, false, s0));
+    if (eager) TRY(bwd_wgrad(c, B, s0));
+    TRY(bwd_dispatch(c, B, s0));
+    if (!eager && !skip_w) TRY(bwd_wgrad(c, B, s0));
   }
   // s0 ends after everything the step issued on s1
   HIPTRY(hipEventRecord(ev->end, s1));

@@ -279,10 +279,13 @@ typedef struct moe_step {
 /*
  * moe_overlap_step - forward of micro-batch `fwd` and backward of micro-batch
  * `bwd` in one step (1F1B note page 2, "MoE 1F1B overlap": two streams and two
- * micro-batches, D before W).  The expert GEMMs and routing run on s_compute;
- * the HBM-bound dispatch/combine kernels run on s_copy, ordered by events:
- *   s_copy:    B.combine_bwd | A.dispatch | B.dispatch_bwd | A.combine
- *   s_compute: A.route, B.route_bwd, B.dgrad, A.ffn_fwd, B.wgrad (deferred)
+ * micro-batches, D before W).  The two micro-batches share no buffers, so each
+ * runs start to end on its own stream and the GPU interleaves their kernels
+ * (one micro-batch's permutes beside the other's expert GEMMs, and each GEMM's
+ * last partial wave of tiles beside the other stream's work):
+ *   s_copy:    A.route, A.dispatch, A.ffn_fwd, A.combine
+ *   s_compute: B.combine_bwd, B.route_bwd, B.dgrad, B.dispatch_bwd,
+ *              B.wgrad (deferred: last, unless MOE_STEP_EAGER_WGRAD)
  * On return, work on s_compute depends on everything the step issued, so a
  * caller that waits for s_compute sees all results.  Results are bit-identical
  * to MOE_STEP_SERIALIZE (all calls on s_compute in forward-then-backward order).
