@@ -142,6 +142,9 @@ def main():
     ap.add_argument("--graph", choices=("on", "off"), default="on",
                     help="time the overlapped steps as replays of a HIP graph that holds two "
                          "steps (on) or as eager launches (off)")
+    ap.add_argument("--fused-permute", choices=("on", "off"), default="off",
+                    help="fuse the permute into the expert GEMMs (MOE_STEP_FUSED_PERMUTE): GEMM1 "
+                         "and wgrad read the token rows of x through the dispatch plan, no xp")
     ap.add_argument("--overlapped-only", action="store_true",
                     help="run only the warm-up and the overlapped steps and print no JSON line: "
                          "the program to trace with rocprofv3 --kernel-trace for the overlap of "
@@ -188,17 +191,19 @@ def main():
     dW_down = torch.zeros(w.E_l, w.d, w.F, dtype=torch.float32, device="cuda")
     dW_r = torch.zeros(w.d, w.E, dtype=torch.float32, device="cuda") if topk else None
     ws = torch.empty(M.moe_step_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    fused = args.fused_permute == "on"
+    FUSED = M.MOE_STEP_FUSED_PERMUTE if fused else 0
     mbs = [M.MicroBatch(s, x=D(inp["x"]), dout=D(inp["dout"]),
-                        gates=None if topk else F32(inp["gates"])),
+                        gates=None if topk else F32(inp["gates"]), fused=fused),
            M.MicroBatch(s, x=D(inp["x_b"]), dout=D(inp["dout_b"]),
-                        gates=None if topk else F32(inp["gates_b"]))]
+                        gates=None if topk else F32(inp["gates_b"]), fused=fused)]
     s0 = torch.cuda.current_stream()
     s1 = torch.cuda.Stream()
 
     def step(fwd, bwd, flags):
         st = M.make_step(s, mode, W_gu, W_down, dW_gu, dW_down, ws, fwd=fwd, bwd=bwd, W_r=W_r,
                          bias=bias, dW_r=dW_r, accumulate=M.MOE_ACCUM_DW)
-        M.moe_overlap_step(st, s0, s1, flags)
+        M.moe_overlap_step(st, s0, s1, flags | FUSED)
 
     def run_loop(n, flags, i0):
         for i in range(i0, i0 + n):
@@ -260,7 +265,7 @@ def main():
                 st = M.make_step(s, mode, W_gu, W_down, dW_gu, dW_down, ws, fwd=mbs[(j + 1) % 2],
                                  bwd=mbs[j % 2], W_r=W_r, bias=bias, dW_r=dW_r,
                                  accumulate=M.MOE_ACCUM_DW)
-                M.moe_overlap_step(st, c0, s1, 0)
+                M.moe_overlap_step(st, c0, s1, FUSED)
                 sts.append(st)
         i += 2
         for _ in range(max(1, args.warmup // 2)):
@@ -333,7 +338,10 @@ def main():
                 "traffic": traffic.get(dom),
                 "algorithmic_per_launch": f"{work[dom][1]:.4g} flop",
                 "avg_launch_us": round(dom_avg_s * 1e6, 2)}
-    disp = kernels.get("permute", {})
+    # the dispatch kernel; with the fused permute there is none (GEMM1 gathers x),
+    # and the forward's remaining permute-class kernel, combine, is reported
+    disp_kernel = "combine" if fused else "permute"
+    disp = kernels.get(disp_kernel, {})
 
     tokens_per_s = w.T / (ms_step / 1e3)
     cpu = None
@@ -357,11 +365,13 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d": w.d, "F": w.F, "E": w.E, "e_lo": w.e_lo,
                    "E_l": w.E_l, "K": w.K, "routing": w.route, "N_rows": N,
                    "step": "1F1B: forward of one micro-batch + backward of the other, "
-                           "two streams, wgrad deferred", "launch": launch},
+                           "two streams, wgrad deferred", "launch": launch,
+                   "permute": "fused into GEMM1 and wgrad" if fused else "separate kernel"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "grouped_gemm_mfma_util": round(gemm_flops / gemm_s / 1e12 / PEAK_BF16_TFLOPS, 4),
         "dispatch_hbm_gbs": disp.get("achieved"),
+        "dispatch_hbm_kernel": disp_kernel,
         "eager_overlapped_ms_per_step": round(ms_eager, 4),
         "serialized_ms_per_step": None if ms_serial is None else round(ms_serial, 4),
         "overlap_speedup": None if ms_serial is None else round(ms_serial / ms_eager, 4),

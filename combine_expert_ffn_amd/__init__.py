@@ -16,7 +16,7 @@ from ._lib import (  # noqa: F401
     MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MOE_ERR_HIP,
     MOE_ERR_UNSUPPORTED, MOE_ERR_ARG, MOE_F32, MOE_BF16, MOE_ROUTE_TOPK,
     MOE_ROUTE_TOPK_FROM_LOGITS, MOE_ROUTE_FORCE_BALANCE, MOE_ACCUM_DX, MOE_ACCUM_DW,
-    MOE_STEP_SERIALIZE, MOE_STEP_EAGER_WGRAD, MOE_STEP_SKIP_WGRAD,
+    MOE_STEP_SERIALIZE, MOE_STEP_EAGER_WGRAD, MOE_STEP_SKIP_WGRAD, MOE_STEP_FUSED_PERMUTE,
 )
 
 
@@ -88,6 +88,13 @@ def moe_expert_ffn_fwd(s, xp, offsets, tile_offsets, W_gu, W_down, h, a, yp, str
                                    _p(W_down), _p(h), _p(a), _p(yp), _stream(stream)))
 
 
+def moe_expert_ffn_fwd_gather(s, x, pair_of_row, offsets, tile_offsets, W_gu, W_down, h, a, yp,
+                              stream=None):
+    check(lib().moe_expert_ffn_fwd_gather(C.byref(s), _p(x), _p(pair_of_row), _p(offsets),
+                                          _p(tile_offsets), _p(W_gu), _p(W_down), _p(h), _p(a),
+                                          _p(yp), _stream(stream)))
+
+
 def moe_combine(s, yp, gates, row_of_pair, out, stream=None):
     check(lib().moe_combine(C.byref(s), _p(yp), _p(gates), _p(row_of_pair), _p(out),
                             _stream(stream)))
@@ -107,6 +114,13 @@ def moe_ffn_dgrad(s, dyp, h, offsets, tile_offsets, W_gu, W_down, dh, dxp, ws, s
 def moe_ffn_wgrad(s, xp, a, dh, dyp, offsets, dW_gu, dW_down, accumulate=0, stream=None):
     check(lib().moe_ffn_wgrad(C.byref(s), _p(xp), _p(a), _p(dh), _p(dyp), _p(offsets),
                               _p(dW_gu), _p(dW_down), int(accumulate), _stream(stream)))
+
+
+def moe_ffn_wgrad_gather(s, x, pair_of_row, a, dh, dyp, offsets, dW_gu, dW_down, accumulate=0,
+                         stream=None):
+    check(lib().moe_ffn_wgrad_gather(C.byref(s), _p(x), _p(pair_of_row), _p(a), _p(dh), _p(dyp),
+                                     _p(offsets), _p(dW_gu), _p(dW_down), int(accumulate),
+                                     _stream(stream)))
 
 
 def moe_route_bwd(s, mode, dgates, gates, idx, x, dlogits, dW_r, accumulate, ws, stream=None):
@@ -158,9 +172,11 @@ def moe_timing_report() -> dict:
 # buffer plumbing (torch allocations only)
 # ---------------------------------------------------------------------------
 class MicroBatch:
-    """Device buffers of one micro-batch for shape ``s`` (sizes per include/moe.h)."""
+    """Device buffers of one micro-batch for shape ``s`` (sizes per include/moe.h).
+    With ``fused=True`` (steps run with MOE_STEP_FUSED_PERMUTE) no xp is allocated."""
 
-    def __init__(self, s: MoeShape, device="cuda", x=None, dout=None, gates=None, logits=None):
+    def __init__(self, s: MoeShape, device="cuda", x=None, dout=None, gates=None, logits=None,
+                 fused=False):
         import numpy as np
         import torch
 
@@ -180,7 +196,7 @@ class MicroBatch:
         self.row_of_pair = e(T, K, dtype=i32)
         self.pair_of_row = e(cap, dtype=i32)
         self.tile_offsets = e(E_l + 1, dtype=i32)
-        self.xp = e(cap, d)
+        self.xp = None if fused else e(cap, d)
         self.h = e(cap, 2 * F)
         self.a = e(cap, F)
         self.yp = e(cap, d)

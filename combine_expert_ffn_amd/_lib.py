@@ -32,6 +32,7 @@ MOE_ACCUM_DW = 2
 MOE_STEP_SERIALIZE = 1
 MOE_STEP_EAGER_WGRAD = 2
 MOE_STEP_SKIP_WGRAD = 4
+MOE_STEP_FUSED_PERMUTE = 8
 
 
 class MoeShape(C.Structure):
@@ -68,10 +69,12 @@ SIGNATURES = {
     "moe_route": (C.c_int, [_SP, C.c_int, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "moe_dispatch": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "moe_expert_ffn_fwd": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_expert_ffn_fwd_gather": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_combine": (C.c_int, [_SP, _P, _P, _P, _P, _P]),
     "moe_combine_bwd": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P]),
     "moe_ffn_dgrad": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "moe_ffn_wgrad": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, C.c_int, _P]),
+    "moe_ffn_wgrad_gather": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, C.c_int, _P]),
     "moe_route_bwd": (C.c_int, [_SP, C.c_int, _P, _P, _P, _P, _P, _P, C.c_int, _P, C.c_size_t,
                                 _P]),
     "moe_dispatch_bwd": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, C.c_int, _P, C.c_size_t, _P]),

@@ -116,12 +116,22 @@ static int do_route(const moe_shape* s, int mode, const void* x, const void* W_r
   return launch_topk(s, logits, idx, gates, st);
 }
 
+// xp == NULL: the plan only (fused permute)
 static int do_dispatch(const moe_shape* s, const void* x, const int32_t* idx, int32_t* counts,
                        int32_t* offsets, int32_t* row_of_pair, int32_t* pair_of_row,
                        int32_t* tile_offsets, void* xp, void* ws, hipStream_t st) {
   int rc = launch_plan(s, idx, counts, offsets, row_of_pair, pair_of_row, tile_offsets, ws, st);
-  if (rc) return rc;
+  if (rc || !xp) return rc;
   return launch_permute(s, x, row_of_pair, xp, st);
+}
+
+// The fused permute addresses x with 32-bit byte offsets.
+static int check_gather_x(const moe_shape* s, const char* fn) {
+  const int64_t es = s->dtype == MOE_BF16 ? 2 : 4;
+  if (s->T * s->d * es >= (1LL << 31))
+    return set_error(MOE_ERR_SHAPE, "%s: x is %lld bytes, the fused permute needs < 2^31", fn,
+                     (long long)(s->T * s->d * es));
+  return MOE_OK;
 }
 
 static int do_dispatch_bwd(const moe_shape* s, const void* dxp, const int32_t* row_of_pair,
@@ -245,14 +255,13 @@ int moe_dispatch(const moe_shape* s, const void* x, const int32_t* idx, int32_t*
                  int32_t* tile_offsets, void* xp, void* ws, size_t ws_bytes, hipStream_t stream) {
   g_err[0] = 0;
   if (int rc = validate_shape(s)) return rc;
-  REQUIRE(x);
+  if (xp) REQUIRE(x);
   REQUIRE(idx);
   REQUIRE(counts);
   REQUIRE(offsets);
   REQUIRE(row_of_pair);
   REQUIRE(pair_of_row);
   REQUIRE(tile_offsets);
-  REQUIRE(xp);
   REQUIRE(ws);
   if (int rc = need_ws(__func__, ws_bytes, ws_plan_bytes(s))) return rc;
   return do_dispatch(s, x, idx, counts, offsets, row_of_pair, pair_of_row, tile_offsets, xp, ws,
@@ -272,7 +281,27 @@ int moe_expert_ffn_fwd(const moe_shape* s, const void* xp, const int32_t* offset
   REQUIRE(h);
   REQUIRE(a);
   REQUIRE(yp);
-  return launch_ffn_fwd(s, xp, offsets, tile_offsets, W_gu, W_down, h, a, yp, stream);
+  return launch_ffn_fwd(s, xp, nullptr, offsets, tile_offsets, W_gu, W_down, h, a, yp, stream);
+}
+
+int moe_expert_ffn_fwd_gather(const moe_shape* s, const void* x, const int32_t* pair_of_row,
+                              const int32_t* offsets, const int32_t* tile_offsets,
+                              const void* W_gu, const void* W_down, void* h, void* a, void* yp,
+                              hipStream_t stream) {
+  g_err[0] = 0;
+  if (int rc = validate_shape(s)) return rc;
+  REQUIRE(x);
+  REQUIRE(pair_of_row);
+  REQUIRE(offsets);
+  REQUIRE(tile_offsets);
+  REQUIRE(W_gu);
+  REQUIRE(W_down);
+  REQUIRE(h);
+  REQUIRE(a);
+  REQUIRE(yp);
+  if (int rc = check_gather_x(s, __func__)) return rc;
+  return launch_ffn_fwd(s, x, pair_of_row, offsets, tile_offsets, W_gu, W_down, h, a, yp,
+                        stream);
 }
 
 int moe_combine(const moe_shape* s, const void* yp, const float* gates,
@@ -334,7 +363,28 @@ int moe_ffn_wgrad(const moe_shape* s, const void* xp, const void* a, const void*
   REQUIRE(dW_down);
   if (accumulate & ~(MOE_ACCUM_DX | MOE_ACCUM_DW))
     return set_error(MOE_ERR_ARG, "moe_ffn_wgrad: unknown accumulate bits 0x%x", accumulate);
-  return launch_ffn_wgrad(s, xp, a, dh, dyp, offsets, dW_gu, dW_down,
+  return launch_ffn_wgrad(s, xp, nullptr, a, dh, dyp, offsets, dW_gu, dW_down,
+                          (accumulate & MOE_ACCUM_DW) != 0, stream);
+}
+
+int moe_ffn_wgrad_gather(const moe_shape* s, const void* x, const int32_t* pair_of_row,
+                         const void* a, const void* dh, const void* dyp, const int32_t* offsets,
+                         float* dW_gu, float* dW_down, int accumulate, hipStream_t stream) {
+  g_err[0] = 0;
+  if (int rc = validate_shape(s)) return rc;
+  REQUIRE(x);
+  REQUIRE(pair_of_row);
+  REQUIRE(a);
+  REQUIRE(dh);
+  REQUIRE(dyp);
+  REQUIRE(offsets);
+  REQUIRE(dW_gu);
+  REQUIRE(dW_down);
+  if (accumulate & ~(MOE_ACCUM_DX | MOE_ACCUM_DW))
+    return set_error(MOE_ERR_ARG, "moe_ffn_wgrad_gather: unknown accumulate bits 0x%x",
+                     accumulate);
+  if (int rc = check_gather_x(s, __func__)) return rc;
+  return launch_ffn_wgrad(s, x, pair_of_row, a, dh, dyp, offsets, dW_gu, dW_down,
                           (accumulate & MOE_ACCUM_DW) != 0, stream);
 }
 
@@ -413,7 +463,7 @@ static int step_events(StepEvents** out) {
   return MOE_OK;
 }
 
-static int validate_mb_fwd(const moe_mb* m, int mode) {
+static int validate_mb_fwd(const moe_mb* m, int mode, bool fused) {
   REQUIRE(m->x);
   REQUIRE(m->idx);
   REQUIRE(m->counts);
@@ -421,7 +471,7 @@ static int validate_mb_fwd(const moe_mb* m, int mode) {
   REQUIRE(m->row_of_pair);
   REQUIRE(m->pair_of_row);
   REQUIRE(m->tile_offsets);
-  REQUIRE(m->xp);
+  if (!fused) REQUIRE(m->xp);
   REQUIRE(m->h);
   REQUIRE(m->a);
   REQUIRE(m->yp);
@@ -431,13 +481,18 @@ static int validate_mb_fwd(const moe_mb* m, int mode) {
   return MOE_OK;
 }
 
-static int validate_mb_bwd(const moe_mb* m, int mode) {
+static int validate_mb_bwd(const moe_mb* m, int mode, bool fused) {
   REQUIRE(m->idx);
   REQUIRE(m->gates);
   REQUIRE(m->offsets);
   REQUIRE(m->tile_offsets);
   REQUIRE(m->row_of_pair);
-  REQUIRE(m->xp);
+  if (fused) {
+    REQUIRE(m->x);
+    REQUIRE(m->pair_of_row);
+  } else {
+    REQUIRE(m->xp);
+  }
   REQUIRE(m->h);
   REQUIRE(m->a);
   REQUIRE(m->yp);
@@ -466,6 +521,7 @@ struct StepCtx {
   void* wsA;
   void* wsB;
   bool router;  // TOPK mode: router weights are differentiated
+  bool fused;   // fused permute: no xp, GEMM1 / wgrad gather from x
 };
 
 static int fwd_route(const StepCtx& c, const moe_mb* A, hipStream_t q) {
@@ -474,11 +530,12 @@ static int fwd_route(const StepCtx& c, const moe_mb* A, hipStream_t q) {
 }
 static int fwd_dispatch(const StepCtx& c, const moe_mb* A, hipStream_t q) {
   return do_dispatch(c.s, A->x, A->idx, A->counts, A->offsets, A->row_of_pair, A->pair_of_row,
-                     A->tile_offsets, A->xp, c.wsA, q);
+                     A->tile_offsets, c.fused ? nullptr : A->xp, c.wsA, q);
 }
 static int fwd_ffn(const StepCtx& c, const moe_mb* A, hipStream_t q) {
-  return launch_ffn_fwd(c.s, A->xp, A->offsets, A->tile_offsets, c.st->W_gu, c.st->W_down, A->h,
-                        A->a, A->yp, q);
+  return launch_ffn_fwd(c.s, c.fused ? A->x : A->xp, c.fused ? A->pair_of_row : nullptr,
+                        A->offsets, A->tile_offsets, c.st->W_gu, c.st->W_down, A->h, A->a,
+                        A->yp, q);
 }
 static int fwd_combine(const StepCtx& c, const moe_mb* A, hipStream_t q) {
   return launch_combine(c.s, A->yp, A->gates, A->row_of_pair, A->out, q);
@@ -505,7 +562,8 @@ static int bwd_dispatch(const StepCtx& c, const moe_mb* B, hipStream_t q) {
                          c.st->W_r, B->dx, false, c.wsB, q);
 }
 static int bwd_wgrad(const StepCtx& c, const moe_mb* B, hipStream_t q) {
-  return launch_ffn_wgrad(c.s, B->xp, B->a, B->dh, B->dyp, B->offsets, c.st->dW_gu,
+  return launch_ffn_wgrad(c.s, c.fused ? B->x : B->xp, c.fused ? B->pair_of_row : nullptr,
+                          B->a, B->dh, B->dyp, B->offsets, c.st->dW_gu,
                           c.st->dW_down, (c.st->accumulate & MOE_ACCUM_DW) != 0, q);
 }
 
@@ -516,7 +574,8 @@ extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t 
   REQUIRE(st);
   const moe_shape* s = &st->shape;
   if (int rc = validate_shape(s)) return rc;
-  if (flags & ~(MOE_STEP_SERIALIZE | MOE_STEP_EAGER_WGRAD | MOE_STEP_SKIP_WGRAD))
+  if (flags & ~(MOE_STEP_SERIALIZE | MOE_STEP_EAGER_WGRAD | MOE_STEP_SKIP_WGRAD |
+                MOE_STEP_FUSED_PERMUTE))
     return set_error(MOE_ERR_ARG, "moe_overlap_step: unknown flags 0x%x", flags);
   const int mode = st->route_mode;
   if (mode != MOE_ROUTE_TOPK && mode != MOE_ROUTE_TOPK_FROM_LOGITS &&
@@ -530,9 +589,11 @@ extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t 
   if (mode == MOE_ROUTE_TOPK) REQUIRE(st->W_r);
   const moe_mb* A = st->fwd;
   const moe_mb* B = st->bwd;
-  if (A) TRY(validate_mb_fwd(A, mode));
+  const bool fused = (flags & MOE_STEP_FUSED_PERMUTE) != 0;
+  if (fused) TRY(check_gather_x(s, "moe_overlap_step"));
+  if (A) TRY(validate_mb_fwd(A, mode, fused));
   if (B) {
-    TRY(validate_mb_bwd(B, mode));
+    TRY(validate_mb_bwd(B, mode, fused));
     REQUIRE(st->dW_gu);
     REQUIRE(st->dW_down);
     if (mode == MOE_ROUTE_TOPK && st->dW_r) REQUIRE(B->x);
@@ -543,7 +604,7 @@ extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t 
   const size_t one = ws_one(s);
   if (int rc = need_ws(__func__, st->ws_bytes, 2 * one)) return rc;
 
-  StepCtx c{st, s, st->ws, (char*)st->ws + one, mode == MOE_ROUTE_TOPK};
+  StepCtx c{st, s, st->ws, (char*)st->ws + one, mode == MOE_ROUTE_TOPK, fused};
   const bool serial = (flags & MOE_STEP_SERIALIZE) || s0 == s1;
   const bool eager = (flags & MOE_STEP_EAGER_WGRAD) != 0;
   const bool skip_w = (flags & MOE_STEP_SKIP_WGRAD) != 0;

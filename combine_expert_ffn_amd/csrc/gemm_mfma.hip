@@ -401,19 +401,29 @@ __global__ __launch_bounds__(TL::NT) void row_grouped_kernel(Op op,
 // pairs gate and up rows: every 64 tile rows are 32 gate rows j and the 32 up
 // rows F + j of the same j, so a staged 64-column block holds g and u of 32
 // outputs.
+//
+// With xrows set, the permute is fused into the A loads: xp is the token
+// matrix x [T][d] and dispatched row r reads token xrows[r] / K (xrows is the
+// dispatch plan's pair_of_row), so the permuted copy of x is never written.
 struct GateUpOp {
   const uint16_t* xp;
   const uint16_t* W_gu;
   uint16_t* h;
   uint16_t* a;
   int d, F;
+  const int32_t* xrows;
+  int K;
   __device__ __forceinline__ int k_len() const { return d; }
   template <class TL, class LA, class LB>
   __device__ __forceinline__ void init(int e, int m0, int m_end, int nt, LA& la, LB& lb,
                                        int tid) const {
     const int jb = nt * (TL::BN / 2);
     const uint16_t* Wg = W_gu + (size_t)e * 2 * F * d;
-    la.init(xp + (size_t)m0 * d, [&](int r) { return (min(m0 + r, m_end - 1) - m0) * d; }, tid);
+    if (xrows)  // block-uniform
+      la.init(xp, [&](int r) { return xrows[min(m0 + r, m_end - 1)] / K * d; }, tid);
+    else
+      la.init(xp + (size_t)m0 * d, [&](int r) { return (min(m0 + r, m_end - 1) - m0) * d; },
+              tid);
     lb.init(Wg, [&](int n) {
       const int j = min(jb + (n >> 6) * 32 + (n & 31), F - 1);
       return (((n >> 5) & 1) * F + j) * d;
@@ -619,21 +629,25 @@ __device__ __forceinline__ int wg_byte(int k, int col) {
 
 // Direct global -> LDS loader of a [64 k][256 col] tile (16 bytes per lane;
 // a wave instruction fills one contiguous 1 KiB block of LDS, addressed by m0).
+// With tok set (an LDS array of the stage's 64 source rows, -1 past the
+// expert's end), k-row kr of the stage is read from row tok[kr] of base: the
+// gathered operand of the fused permute.
 template <int NW>
 struct LoadKM {
   static constexpr int PER = BK / 2 / NW;  // wave instructions per stage
   const uint16_t* base;
   long ld;
   int M, m0, lane, w;
-  __device__ __forceinline__ void issue(uint8_t* lds, int k0, int k_end) const {
+  __device__ __forceinline__ void issue(uint8_t* lds, int k0, int k_end,
+                                        const int* tok = nullptr) const {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int blk = i * NW + w;
       const int kr = blk * 2 + (lane >> 5);
       const int s = lane & 31;
       const int col = (((s >> 1) ^ wg_swz(kr)) & 15) * 16 + (s & 1) * 8;
-      const int k = k0 + kr;
-      const bool ok = (k < k_end) && (m0 + col < M);
+      const int k = tok ? tok[kr] : k0 + kr;
+      const bool ok = (tok ? k >= 0 : k < k_end) && (m0 + col < M);
       const uint16_t* src = ok ? base + (long)k * ld + m0 + col : g_zero_row + col;
       // Issued by inline assembly: with the builtin the compiler treats these
       // LDS writes as possibly aliasing every later LDS read and waits for the
@@ -670,15 +684,22 @@ __device__ __forceinline__ long long uniform64(long long v) {
 }
 
 // 256 x 256 output tiles, 8 waves (2 x 4), wave tile 128 x 64.
+//
+// With xrows set (the fused permute), xp is the token matrix x [T][d] and the
+// dW_gu tiles read dispatched row r from token xrows[r] / K: the token rows of
+// stage k are looked up one stage ahead into an LDS list (s_tok, double
+// buffered), from which the next stage's loads take their addresses.
 __global__ __launch_bounds__(512) void wgrad_kernel(
-    const uint16_t* __restrict__ xp, const uint16_t* __restrict__ abuf,
-    const uint16_t* __restrict__ dh, const uint16_t* __restrict__ dyp,
-    const int32_t* __restrict__ offsets, float* __restrict__ dW_gu,
-    float* __restrict__ dW_down, int E_l, int d, int F, int accumulate) {
+    const uint16_t* __restrict__ xp, const int32_t* __restrict__ xrows, int K,
+    const uint16_t* __restrict__ abuf, const uint16_t* __restrict__ dh,
+    const uint16_t* __restrict__ dyp, const int32_t* __restrict__ offsets,
+    float* __restrict__ dW_gu, float* __restrict__ dW_down, int E_l, int d, int F,
+    int accumulate) {
   constexpr int NW = 8, WGN = 4, WTM = 128, WTN = 64, TM = 4, TN = 2;
   constexpr int STAGE = 2 * BK * WG_ROWB;  // A + B tiles
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
   __shared__ long long s_it[257];  // first k-step of each expert's tiles; s_it[E_l] = W
+  __shared__ int s_tok[2][BK];     // source token rows of the next two stages (fused permute)
   const int tdm = (d + 255) / 256, tdn = (F + 255) / 256;
   const int tgm = (2 * F + 255) / 256, tgn = (d + 255) / 256;
   const int per_e = tdm * tdn + tgm * tgn;
@@ -729,6 +750,7 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
     const uint16_t *Asrc, *Bsrc;
     int M, N, m0, n0;
     float* out;
+    bool gat = false;  // block-uniform
     if (t < tdm * tdn) {
       Asrc = dyp;
       Bsrc = abuf;
@@ -741,6 +763,7 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
       t -= tdm * tdn;
       Asrc = dh;
       Bsrc = xp;
+      gat = xrows != nullptr;
       M = 2 * F;
       N = d;
       m0 = (t / tgn) * 256;
@@ -757,9 +780,18 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     const int nk = (r1 - r0 + BK - 1) / BK;
+    // source token of dispatched row r (-1 past the expert's end)
+    auto token = [&](int r) { return r < r1 ? xrows[r] / K : -1; };
     if (nk > 0) {  // block-uniform
+      if (gat) {
+        if (tid < BK) {
+          s_tok[0][tid] = token(r0 + tid);
+          s_tok[1][tid] = token(r0 + BK + tid);
+        }
+        __syncthreads();
+      }
       la.issue(smem, r0, r1);
-      lb.issue(smem + BK * WG_ROWB, r0, r1);
+      lb.issue(smem + BK * WG_ROWB, r0, r1, gat ? s_tok[0] : nullptr);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       for (int kt = 0; kt < nk; ++kt) {
@@ -767,8 +799,14 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
         uint8_t* nxt = smem + ((kt + 1) & 1) * STAGE;
         if (kt + 1 < nk) {
           la.issue(nxt, r0 + (kt + 1) * BK, r1);
-          lb.issue(nxt + BK * WG_ROWB, r0 + (kt + 1) * BK, r1);
+          lb.issue(nxt + BK * WG_ROWB, r0 + (kt + 1) * BK, r1,
+                   gat ? s_tok[(kt + 1) & 1] : nullptr);
         }
+        // token rows of stage kt + 2, stored into the list stage kt used
+        // (its last reader, the issue of stage kt, is behind the previous
+        // barrier)
+        int tk = -1;
+        if (gat && tid < BK) tk = token(r0 + (kt + 2) * BK + tid);
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
           bf16x8_t a[TM], b[TN];
@@ -783,6 +821,7 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (gat && tid < BK) s_tok[kt & 1][tid] = tk;
         __syncthreads();
       }
     }
@@ -919,11 +958,12 @@ int launch_row_grouped(const char* name, const moe_shape* s, const Op& op,
 // ---------------------------------------------------------------------------
 // launchers (bf16)
 // ---------------------------------------------------------------------------
-int launch_ffn_fwd_bf16(const moe_shape* s, const void* xp, const int32_t* offsets,
-                        const int32_t* tile_offsets, const void* W_gu, const void* W_down,
-                        void* h, void* a, void* yp, hipStream_t st) {
+int launch_ffn_fwd_bf16(const moe_shape* s, const void* xp, const int32_t* xrows,
+                        const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
+                        const void* W_down, void* h, void* a, void* yp, hipStream_t st) {
   const int d = (int)s->d, F = (int)s->F;
-  GateUpOp g{(const uint16_t*)xp, (const uint16_t*)W_gu, (uint16_t*)h, (uint16_t*)a, d, F};
+  GateUpOp g{(const uint16_t*)xp, (const uint16_t*)W_gu, (uint16_t*)h, (uint16_t*)a, d, F,
+             xrows, (int)s->K};
   if (int rc = launch_row_grouped("ffn_gate_up", s, g, offsets, tile_offsets,
                                   (F + T256::BN / 2 - 1) / (T256::BN / 2), st))
     return rc;
@@ -967,16 +1007,17 @@ int launch_ffn_dgrad_bf16(const moe_shape* s, const void* dyp, const void* h,
                             (d + T256::BN - 1) / T256::BN, st);
 }
 
-int launch_ffn_wgrad_bf16(const moe_shape* s, const void* xp, const void* a, const void* dh,
-                          const void* dyp, const int32_t* offsets, float* dW_gu, float* dW_down,
-                          bool accumulate, hipStream_t st) {
+int launch_ffn_wgrad_bf16(const moe_shape* s, const void* xp, const int32_t* xrows,
+                          const void* a, const void* dh, const void* dyp,
+                          const int32_t* offsets, float* dW_gu, float* dW_down, bool accumulate,
+                          hipStream_t st) {
   const int d = (int)s->d, F = (int)s->F, E_l = (int)s->E_l;
   const long per_e = (long)((d + 255) / 256) * ((F + 255) / 256) +
                      (long)((2 * F + 255) / 256) * ((d + 255) / 256);
   const int grid = persistent_grid(E_l * per_e);
   MOE_LAUNCH("wgrad", st,
              wgrad_kernel<<<grid, 512, 0, st>>>(
-                 (const uint16_t*)xp, (const uint16_t*)a, (const uint16_t*)dh,
+                 (const uint16_t*)xp, xrows, (int)s->K, (const uint16_t*)a, (const uint16_t*)dh,
                  (const uint16_t*)dyp, offsets, dW_gu, dW_down, E_l, d, F, accumulate ? 1 : 0));
   return check_launch("wgrad GEMM");
 }

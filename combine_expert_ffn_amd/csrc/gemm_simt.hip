@@ -20,7 +20,11 @@ __device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offsets
   return lo;
 }
 
+// xrows: null, or pair_of_row for the fused permute (xp is then x and row r
+// reads token xrows[r] / K).
 __global__ __launch_bounds__(256) void f32_gate_up_kernel(const float* __restrict__ xp,
+                                                          const int32_t* __restrict__ xrows,
+                                                          int K,
                                                           const int32_t* __restrict__ offsets,
                                                           const float* __restrict__ W_gu,
                                                           float* __restrict__ h,
@@ -31,7 +35,7 @@ __global__ __launch_bounds__(256) void f32_gate_up_kernel(const float* __restric
   const int row = (int)(i / F), j = (int)(i % F);
   if (row >= offsets[E_l]) return;
   const int e = expert_of_row(offsets, E_l, row);
-  const float* xr = xp + (size_t)row * d;
+  const float* xr = xp + (size_t)(xrows ? xrows[row] / K : row) * d;
   const float* wg = W_gu + ((size_t)e * 2 * F + j) * d;
   const float* wu = W_gu + ((size_t)e * 2 * F + F + j) * d;
   float g = 0.f, u = 0.f;
@@ -100,7 +104,8 @@ __global__ __launch_bounds__(256) void f32_dgrad_in_kernel(const float* __restri
 
 // dW_down[e][i][f] = sum_r dyp[r][i] a[r][f]; dW_gu[e][m][c] = sum_r dh[r][m] xp[r][c]
 __global__ __launch_bounds__(256) void f32_wgrad_kernel(
-    const float* __restrict__ xp, const float* __restrict__ a, const float* __restrict__ dh,
+    const float* __restrict__ xp, const int32_t* __restrict__ xrows, int K,
+    const float* __restrict__ a, const float* __restrict__ dh,
     const float* __restrict__ dyp, const int32_t* __restrict__ offsets,
     float* __restrict__ dW_gu, float* __restrict__ dW_down, int E_l, int d, int F,
     int accumulate) {
@@ -120,36 +125,37 @@ __global__ __launch_bounds__(256) void f32_wgrad_kernel(
     q -= (long)d * F;
     const int m = (int)(q / d), c = (int)(q % d);
     for (int r = r0; r < r1; ++r)
-      acc = fmaf(dh[(size_t)r * 2 * F + m], xp[(size_t)r * d + c], acc);
+      acc = fmaf(dh[(size_t)r * 2 * F + m], xp[(size_t)(xrows ? xrows[r] / K : r) * d + c], acc);
     o = dW_gu + (size_t)e * 2 * F * d + q;
   }
   *o = accumulate ? *o + acc : acc;
 }
 
-int launch_ffn_fwd_bf16(const moe_shape* s, const void* xp, const int32_t* offsets,
-                        const int32_t* tile_offsets, const void* W_gu, const void* W_down,
-                        void* h, void* a, void* yp, hipStream_t st);
+int launch_ffn_fwd_bf16(const moe_shape* s, const void* xp, const int32_t* xrows,
+                        const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
+                        const void* W_down, void* h, void* a, void* yp, hipStream_t st);
 int launch_dgrad_weights_bf16(const moe_shape* s, const void* W_gu, const void* W_down,
                               void* ws, hipStream_t st);
 int launch_ffn_dgrad_bf16(const moe_shape* s, const void* dyp, const void* h,
                           const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
                           const void* W_down, void* dh, void* dxp, void* ws, bool weights_ready,
                           hipStream_t st);
-int launch_ffn_wgrad_bf16(const moe_shape* s, const void* xp, const void* a, const void* dh,
-                          const void* dyp, const int32_t* offsets, float* dW_gu, float* dW_down,
-                          bool accumulate, hipStream_t st);
+int launch_ffn_wgrad_bf16(const moe_shape* s, const void* xp, const int32_t* xrows,
+                          const void* a, const void* dh, const void* dyp,
+                          const int32_t* offsets, float* dW_gu, float* dW_down, bool accumulate,
+                          hipStream_t st);
 
-int launch_ffn_fwd(const moe_shape* s, const void* xp, const int32_t* offsets,
-                   const int32_t* tile_offsets, const void* W_gu, const void* W_down, void* h,
-                   void* a, void* yp, hipStream_t st) {
+int launch_ffn_fwd(const moe_shape* s, const void* xp, const int32_t* xrows,
+                   const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
+                   const void* W_down, void* h, void* a, void* yp, hipStream_t st) {
   if (s->T == 0) return MOE_OK;
   if (s->dtype == MOE_BF16)
-    return launch_ffn_fwd_bf16(s, xp, offsets, tile_offsets, W_gu, W_down, h, a, yp, st);
+    return launch_ffn_fwd_bf16(s, xp, xrows, offsets, tile_offsets, W_gu, W_down, h, a, yp, st);
   const long cap = s->T * s->K;
   const int d = (int)s->d, F = (int)s->F, E_l = (int)s->E_l;
   MOE_LAUNCH("f32_gate_up", st,
              f32_gate_up_kernel<<<(unsigned)cdiv(cap * F, 256), 256, 0, st>>>(
-      (const float*)xp, offsets, (const float*)W_gu, (float*)h, (float*)a, cap, E_l, d, F));
+      (const float*)xp, xrows, (int)s->K, offsets, (const float*)W_gu, (float*)h, (float*)a, cap, E_l, d, F));
   if (int rc = check_launch("f32 expert GEMM1")) return rc;
   MOE_LAUNCH("f32_down", st,
              f32_down_kernel<<<(unsigned)cdiv(cap * d, 256), 256, 0, st>>>(
@@ -183,15 +189,16 @@ int launch_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h, const i
   return check_launch("f32 dgrad (input)");
 }
 
-int launch_ffn_wgrad(const moe_shape* s, const void* xp, const void* a, const void* dh,
-                     const void* dyp, const int32_t* offsets, float* dW_gu, float* dW_down,
-                     bool accumulate, hipStream_t st) {
+int launch_ffn_wgrad(const moe_shape* s, const void* xp, const int32_t* xrows, const void* a,
+                     const void* dh, const void* dyp, const int32_t* offsets, float* dW_gu,
+                     float* dW_down, bool accumulate, hipStream_t st) {
   if (s->dtype == MOE_BF16)
-    return launch_ffn_wgrad_bf16(s, xp, a, dh, dyp, offsets, dW_gu, dW_down, accumulate, st);
+    return launch_ffn_wgrad_bf16(s, xp, xrows, a, dh, dyp, offsets, dW_gu, dW_down, accumulate,
+                                 st);
   const long n = s->E_l * (s->d * s->F + 2 * s->F * s->d);
   MOE_LAUNCH("f32_wgrad", st,
              f32_wgrad_kernel<<<(unsigned)cdiv(n, 256), 256, 0, st>>>(
-      (const float*)xp, (const float*)a, (const float*)dh, (const float*)dyp, offsets, dW_gu,
+      (const float*)xp, xrows, (int)s->K, (const float*)a, (const float*)dh, (const float*)dyp, offsets, dW_gu,
       dW_down, (int)s->E_l, (int)s->d, (int)s->F, accumulate ? 1 : 0));
   return check_launch("f32 wgrad");
 }

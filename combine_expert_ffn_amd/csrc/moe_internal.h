@@ -175,10 +175,12 @@ int launch_combine_bwd(const moe_shape* s, const void* dout, const void* yp, con
 int launch_dispatch_bwd(const moe_shape* s, const void* dxp, const int32_t* row_of_pair,
                         const int32_t* idx, const float* dlogits, const void* W_rT, void* dx,
                         bool accumulate, hipStream_t st);
-// expert GEMMs
-int launch_ffn_fwd(const moe_shape* s, const void* xp, const int32_t* offsets,
-                   const int32_t* tile_offsets, const void* W_gu, const void* W_down, void* h,
-                   void* a, void* yp, hipStream_t st);
+// expert GEMMs.  xrows: null, or the plan's pair_of_row for the fused permute,
+// in which case xp is the token matrix x and dispatched row r of the GEMM1 (and
+// wgrad dW_gu) operand is token xrows[r] / K.
+int launch_ffn_fwd(const moe_shape* s, const void* xp, const int32_t* xrows,
+                   const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
+                   const void* W_down, void* h, void* a, void* yp, hipStream_t st);
 // The bf16 dgrad's transposed weight copies (into ws at ws_wT_offset); a
 // no-op in float32.
 int launch_dgrad_weights(const moe_shape* s, const void* W_gu, const void* W_down, void* ws,
@@ -188,8 +190,8 @@ int launch_dgrad_weights(const moe_shape* s, const void* W_gu, const void* W_dow
 int launch_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h, const int32_t* offsets,
                      const int32_t* tile_offsets, const void* W_gu, const void* W_down, void* dh,
                      void* dxp, void* ws, bool weights_ready, hipStream_t st);
-int launch_ffn_wgrad(const moe_shape* s, const void* xp, const void* a, const void* dh,
-                     const void* dyp, const int32_t* offsets, float* dW_gu, float* dW_down,
-                     bool accumulate, hipStream_t st);
+int launch_ffn_wgrad(const moe_shape* s, const void* xp, const int32_t* xrows, const void* a,
+                     const void* dh, const void* dyp, const int32_t* offsets, float* dW_gu,
+                     float* dW_down, bool accumulate, hipStream_t st);
 
 }  // namespace moe

@@ -80,6 +80,13 @@ extern "C" {
                                    next layer's forward runs, page 1
                                    delay_wgrad_compute); its inputs (xp, a, dh,
                                    dyp, offsets of `bwd`) must then stay intact   */
+#define MOE_STEP_FUSED_PERMUTE 8 /* fuse the permute into the expert GEMMs: the
+                                   forward dispatch writes no xp, GEMM1 and the
+                                   dW_gu part of wgrad read the token rows of x
+                                   through pair_of_row (page 1 names the fused
+                                   permute, moe_permute_fusion); xp of both
+                                   micro-batches may be NULL, and `bwd` needs x
+                                   and pair_of_row                                */
 
 /*
  * Layer shape.  T tokens of hidden size d; E experts routed over, of which the
@@ -138,7 +145,9 @@ int moe_route(const moe_shape* s, int mode, const void* x, const void* W_r,
  *   tile_offsets [E_l+1] i32 out exclusive prefix sum of ceil(counts/moe_tile_m())
  *   x            [T,d] dtype in
  *   xp           [T*K,d] dtype out  xp[row_of_pair[t*K+k]] = x[t] (exact copy);
- *                                   rows >= N untouched
+ *                                   rows >= N untouched.  NULL: the plan only
+ *                                   (for the fused-permute calls below; x may
+ *                                   then be NULL too)
  */
 int moe_dispatch(const moe_shape* s, const void* x, const int32_t* idx,
                  int32_t* counts, int32_t* offsets, int32_t* row_of_pair,
@@ -157,6 +166,20 @@ int moe_expert_ffn_fwd(const moe_shape* s, const void* xp, const int32_t* offset
                        const int32_t* tile_offsets, const void* W_gu,
                        const void* W_down, void* h, void* a, void* yp,
                        hipStream_t stream);
+
+/*
+ * moe_expert_ffn_fwd_gather - moe_expert_ffn_fwd with the permute fused into
+ * GEMM1's operand loads (page 1 lists the fused permute, moe_permute_fusion,
+ * among the options): row r of the product reads token pair_of_row[r] / K of
+ * x [T,d] directly, so xp is never materialised.  Results are identical to
+ * moe_dispatch (with xp) followed by moe_expert_ffn_fwd.  pair_of_row from
+ * moe_dispatch; x must stay below 2^31 bytes.
+ */
+int moe_expert_ffn_fwd_gather(const moe_shape* s, const void* x,
+                              const int32_t* pair_of_row, const int32_t* offsets,
+                              const int32_t* tile_offsets, const void* W_gu,
+                              const void* W_down, void* h, void* a, void* yp,
+                              hipStream_t stream);
 
 /*
  * moe_combine - unpermute and gate-weighted sum (page 1, "What it is":
@@ -202,6 +225,17 @@ int moe_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h,
 int moe_ffn_wgrad(const moe_shape* s, const void* xp, const void* a,
                   const void* dh, const void* dyp, const int32_t* offsets,
                   float* dW_gu, float* dW_down, int accumulate, hipStream_t stream);
+
+/*
+ * moe_ffn_wgrad_gather - moe_ffn_wgrad with the fused permute: dW_gu reads
+ * row r of its xp operand as token pair_of_row[r] / K of x [T,d].  Results
+ * are identical to moe_ffn_wgrad on the materialised xp.  x must stay below
+ * 2^31 bytes.
+ */
+int moe_ffn_wgrad_gather(const moe_shape* s, const void* x, const int32_t* pair_of_row,
+                         const void* a, const void* dh, const void* dyp,
+                         const int32_t* offsets, float* dW_gu, float* dW_down,
+                         int accumulate, hipStream_t stream);
 
 /*
  * moe_route_bwd - backward of the top-K softmax gates and of the router

@@ -95,6 +95,37 @@ def test_null_pointers_rejected():
                               None) == M.MOE_ERR_NULL
 
 
+def test_fused_permute_validation():
+    L = M.lib()
+    s = _shape()
+    # NULL gather map / x
+    assert L.moe_expert_ffn_fwd_gather(C.byref(s), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       FAKE, FAKE, None) == M.MOE_ERR_NULL
+    assert L.moe_ffn_wgrad_gather(C.byref(s), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0,
+                                  None) == M.MOE_ERR_NULL
+    assert L.moe_ffn_wgrad_gather(C.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8,
+                                  None) == M.MOE_ERR_ARG
+    # x beyond the 32-bit offsets of the gathered loads
+    big = _shape(T=1 << 17, d=16384, K=2)
+    assert L.moe_expert_ffn_fwd_gather(C.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       FAKE, FAKE, None) == M.MOE_ERR_SHAPE
+    assert b"2^31" in L.moe_last_error()
+    # plan-only dispatch needs no x and no xp, but still its plan outputs
+    assert L.moe_dispatch(C.byref(s), None, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE,
+                          1 << 20, None) == M.MOE_ERR_NULL
+    # a fused step needs x and pair_of_row in the backward micro-batch, not xp
+    fields = {n: 0x1000 for n in _lib.MB_FIELDS}
+    fields["xp"] = 0
+    fields["pair_of_row"] = 0
+    mb = _lib.MoeMB(*[fields[n] for n in _lib.MB_FIELDS])
+    st = _lib.MoeStep(s, M.MOE_ROUTE_FORCE_BALANCE, 0, None, None, 0x1000, 0x1000, None, 0x1000,
+                      0x1000, None, C.pointer(mb), 0x1000, 1 << 40)
+    assert L.moe_overlap_step(C.byref(st), None, None, M.MOE_STEP_FUSED_PERMUTE) == M.MOE_ERR_NULL
+    assert b"pair_of_row" in L.moe_last_error()
+    assert L.moe_overlap_step(C.byref(st), None, None, 0) == M.MOE_ERR_NULL  # unfused needs xp
+    assert b"xp" in L.moe_last_error()
+
+
 def test_workspace_size_checked():
     s = _shape(T=4096, K=8)
     need = M.moe_workspace_bytes(s)

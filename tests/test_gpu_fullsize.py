@@ -41,10 +41,10 @@ class Net:
         self.dW_r = torch.empty(w.d, w.E, dtype=torch.float32, device="cuda") if self.topk else None
         self.ws = torch.empty(M.moe_step_workspace_bytes(self.s), dtype=torch.uint8, device="cuda")
 
-    def mb(self, x, dout, gates=None):
+    def mb(self, x, dout, gates=None, fused=False):
         D = lambda a: dev(a, self.w.dtype)
         return M.MicroBatch(self.s, x=D(x), dout=D(dout),
-                            gates=None if gates is None else dev(gates, "f32x"))
+                            gates=None if gates is None else dev(gates, "f32x"), fused=fused)
 
     def step(self, fwd, bwd, s0, s1, flags, accumulate=0):
         st = M.make_step(self.s, self.mode, self.W_gu, self.W_down, self.dW_gu, self.dW_down,
@@ -176,12 +176,14 @@ def test_overlap_equals_serialized_two_microbatch():
         M.moe_ffn_wgrad(net.s, mb.xp, mb.a, mb.dh, mb.dyp, mb.offsets, net.dW_gu, net.dW_down,
                         acc, s0)
 
+    fp = M.MOE_STEP_FUSED_PERMUTE
     for tag, flags, copy in (("serial", M.MOE_STEP_SERIALIZE, s0), ("overlap", 0, s1),
                              ("eager", M.MOE_STEP_EAGER_WGRAD, s1),
-                             ("skip", M.MOE_STEP_SKIP_WGRAD, s1)):
+                             ("skip", M.MOE_STEP_SKIP_WGRAD, s1),
+                             ("fused", fp, s1), ("fused_serial", fp | M.MOE_STEP_SERIALIZE, s0)):
         skip = flags == M.MOE_STEP_SKIP_WGRAD
-        A = net.mb(inp["x"], inp["dout"])
-        B = net.mb(inp["x_b"], inp["dout_b"])
+        A = net.mb(inp["x"], inp["dout"], fused=bool(flags & fp))
+        B = net.mb(inp["x_b"], inp["dout_b"], fused=bool(flags & fp))
         net.step(A, None, s0, copy, flags)
         net.step(B, A, s0, copy, flags)                        # A's grads overwrite
         if skip:
@@ -193,15 +195,15 @@ def test_overlap_equals_serialized_two_microbatch():
         results[tag] = dict(A=A, B=B, dW_gu=net.dW_gu.clone(), dW_down=net.dW_down.clone(),
                             dW_r=net.dW_r.clone())
     ref = results["serial"]
-    for tag in ("overlap", "eager", "skip"):
+    for tag in ("overlap", "eager", "skip", "fused", "fused_serial"):
         r = results[tag]
         for mbn in ("A", "B"):
             for k in ("idx", "gates", "row_of_pair", "out", "dgates", "dlogits", "dx", "yp"):
                 assert torch.equal(getattr(r[mbn], k), getattr(ref[mbn], k)), (tag, mbn, k)
         for k in ("dW_gu", "dW_down", "dW_r"):
             assert torch.equal(r[k], ref[k]), (tag, k)
-    log("[overlap] overlapped, eager-wgrad and caller-deferred-wgrad steps bit-identical to "
-        "serialized")
+    log("[overlap] overlapped, eager-wgrad, caller-deferred-wgrad and fused-permute steps "
+        "bit-identical to serialized")
     # oracle on samples of micro-batch A (weight grads hold A + B)
     r = results["overlap"]
     A, B = r["A"], r["B"]

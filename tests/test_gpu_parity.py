@@ -131,11 +131,24 @@ def test_stage_parity(name):
     exact("pair_of_row", host(mb.pair_of_row), ref["pair_of_row"])
     exact("xp", host(mb.xp)[:N], ref["xp"])
 
+    # plan only (the fused permute's dispatch): the same plan, no xp
+    fz = M.MicroBatch(s, fused=True)
+    M.moe_dispatch(s, None, idx_r, fz.counts, fz.offsets, fz.row_of_pair, fz.pair_of_row,
+                   fz.tile_offsets, None, ws)
+    for k in ("counts", "offsets", "tile_offsets", "row_of_pair", "pair_of_row"):
+        assert torch.equal(getattr(fz, k), getattr(mb, k)), f"plan-only dispatch: {k}"
+
     # ---- expert FFN forward
     M.moe_expert_ffn_fwd(s, mb.xp, mb.offsets, mb.tile_offsets, W_gu, W_down, mb.h, mb.a, mb.yp)
     close("h", host(mb.h)[:N], ref["h"], tau)
     close("a", host(mb.a)[:N], ref["a"], tau)
     close("yp", host(mb.yp)[:N], ref["yp"], tau)
+    # fused permute: GEMM1 gathers the token rows of x itself; same arithmetic,
+    # so the same bits as on the materialised xp
+    M.moe_expert_ffn_fwd_gather(s, x, fz.pair_of_row, fz.offsets, fz.tile_offsets, W_gu, W_down,
+                                fz.h, fz.a, fz.yp)
+    for k in ("h", "a", "yp"):
+        exact(f"{k} (fused permute)", host(getattr(fz, k))[:N], host(getattr(mb, k))[:N])
 
     # ---- combine (oracle y_p)
     yp_r = D(_pad(ref["yp"], cap))
@@ -187,6 +200,12 @@ def test_stage_parity(name):
     M.moe_ffn_wgrad(s, mb.xp, a_r, dh_r, dyp_r, mb.offsets, dW_gu, dW_down, M.MOE_ACCUM_DW)
     exact("dW_gu accumulate = 2x", host(dW_gu), 2 * host(first[0]))
     exact("dW_down accumulate = 2x", host(dW_down), 2 * host(first[1]))
+    # fused permute: dW_gu gathers its xp rows from x
+    gW_gu = torch.full_like(dW_gu, 7.0)
+    gW_down = torch.full_like(dW_down, 7.0)
+    M.moe_ffn_wgrad_gather(s, x, fz.pair_of_row, a_r, dh_r, dyp_r, fz.offsets, gW_gu, gW_down, 0)
+    exact("dW_gu (fused permute)", host(gW_gu), host(first[0]))
+    exact("dW_down (fused permute)", host(gW_down), host(first[1]))
     torch.cuda.synchronize()
     log(f"[stage parity] {name}: ok (N={N})")
 
@@ -197,7 +216,8 @@ def _layer_step(w, inp, flags=0, s_copy=None):
     D = lambda a: dev(a, w.dtype)
     topk = w.route == "topk"
     A = M.MicroBatch(s, x=D(inp["x"]), dout=D(inp["dout"]),
-                     gates=None if topk else dev(inp["gates"], "f32x"))
+                     gates=None if topk else dev(inp["gates"], "f32x"),
+                     fused=bool(flags & M.MOE_STEP_FUSED_PERMUTE))
     W_gu, W_down = D(inp["W_gu"]), D(inp["W_down"])
     W_r = D(inp["W_r"]) if topk else None
     bias = dev(inp["bias"], "f32x") if inp["bias"] is not None else None
@@ -218,15 +238,16 @@ def _layer_step(w, inp, flags=0, s_copy=None):
     return A, dict(dW_gu=dW_gu, dW_down=dW_down, dW_r=dW_r)
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["", "fused_permute"])
 @pytest.mark.parametrize("name", ["tiny_f32", "fb_ragged_bf16", "zipf_window_bf16",
                                   "many_experts_bf16", "mid_window_bf16", "max_router_bf16"])
-def test_chain_parity(name):
+def test_chain_parity(name, fused):
     w = SMALL[name]
-    log(f"[chain parity] {name}")
+    log(f"[chain parity] {name}{' fused permute' if fused else ''}")
     prec, tau = w.dtype, TAU[w.dtype]
     inp = make_inputs(w, seed=0)
     X, ref, refb = _oracle(w, inp, prec)
-    A, g = _layer_step(w, inp)
+    A, g = _layer_step(w, inp, M.MOE_STEP_FUSED_PERMUTE if fused else 0)
     if w.route == "topk":
         close("logits", host(A.logits), ref["logits"], tau)
         gi = host(A.idx)
@@ -237,7 +258,8 @@ def test_chain_parity(name):
             pytest.skip(f"{diff.sum()} near-tie tokens select differently; stage test covers them")
     N = ref["N"]
     exact("row_of_pair", host(A.row_of_pair), ref["row_of_pair"])
-    exact("xp", host(A.xp)[:N], ref["xp"])
+    if not fused:
+        exact("xp", host(A.xp)[:N], ref["xp"])
     for k in ("h", "a", "yp"):
         close(k, host(getattr(A, k))[:N], ref[k], tau)
     close("out", host(A.out), ref["out"], tau)
@@ -335,6 +357,36 @@ def test_deterministic_repeat():
         assert torch.equal(getattr(A1, k), getattr(A2, k)), k
     for k in g1:
         assert torch.equal(g1[k], g2[k]), k
+
+
+def test_wgrad_gather_scattered_tokens():
+    """Fused-permute wgrad with dispatched rows drawn from tokens in a random
+    order (every row a different token, some tokens repeated across experts):
+    bit-identical to moe_ffn_wgrad on the explicitly gathered xp."""
+    counts = (300, 0, 577, 65, 1)
+    d, F, K = 192, 64, 3
+    E_l = len(counts)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    N = int(off[-1])
+    T = (N + K - 1) // K + 5
+    s = M.make_shape(T, d, F, E_l, 0, E_l, K, "bf16")
+    rng = np.random.default_rng(11)
+    pairs = rng.permutation(T * K)[:N]             # pair t*K + k of each row
+    x_h = rng.standard_normal((T, d))
+    x = dev(x_h, "bf16")
+    xp = dev(x_h[pairs // K], "bf16")
+    a = dev(0.3 * rng.standard_normal((N, F)), "bf16")
+    dh = dev(0.5 * rng.standard_normal((N, 2 * F)), "bf16")
+    dyp = dev(0.1 * rng.standard_normal((N, d)), "bf16")
+    offsets = dev(off, "i32")
+    por = dev(np.concatenate([pairs, -np.ones(T * K - N)]), "i32")
+    log(f"[wgrad gather] counts={counts} T={T} K={K}")
+    ref = [torch.full((E_l, 2 * F, d), 5.0, device="cuda"), torch.full((E_l, d, F), 5.0, device="cuda")]
+    got = [torch.full_like(ref[0], 5.0), torch.full_like(ref[1], 5.0)]
+    M.moe_ffn_wgrad(s, xp, a, dh, dyp, offsets, ref[0], ref[1], 0)
+    M.moe_ffn_wgrad_gather(s, x, por, a, dh, dyp, offsets, got[0], got[1], 0)
+    torch.cuda.synchronize()
+    assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1])
 
 
 @pytest.mark.parametrize("counts", [(700, 0, 1313), (64, 1, 4095, 257, 0, 129)])
