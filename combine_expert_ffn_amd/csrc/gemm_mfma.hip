@@ -12,14 +12,16 @@
 //    in its L2, and the ranges stay balanced whatever the device-side tile count;
 //  * block tile 256 x 256, K step 64, 8 waves (2 per SIMD), each owning a
 //    128 x 64 piece as 4 x 2 MFMA 32x32 tiles;
-//  * two LDS stages fed through registers: the loads for step k+1 are issued
-//    at the start of step k and written to LDS in its third quarter;
+//  * two LDS stages fed through registers: the register stage is written to
+//    the free LDS buffer over the first three k slices of a step, each chunk's
+//    store followed by the load of the same chunk two stages ahead;
 //  * LDS tiles are [rows][64] bf16 with the 16-byte chunk index XOR-swizzled
 //    by the row, so matrix-core fragment reads are free of bank conflicts;
 //  * the MFMA fragments of the next 16-wide k slice are read while the current
 //    slice's MFMAs run (across the stage barrier too), and the instruction
-//    order (MFMA / LDS read / global load / LDS write) is fixed with
-//    scheduling group barriers so the matrix pipe is fed continuously;
+//    order (MFMA / LDS read / LDS write / global load) is fixed per slice with
+//    scheduling group barriers, the slices fenced from each other, so the
+//    matrix pipe is fed continuously;
 //  * loads are branch free: rows or columns outside the matrix read a valid
 //    clamped address (their results are discarded, or replaced by zero where
 //    they would enter a sum);
@@ -89,6 +91,12 @@ struct LoadK {
   __device__ __forceinline__ void store(uint16_t* lds) const {
 #pragma unroll
     for (int c = 0; c < CH; ++c) *(u32x4_t*)(lds + dst0 + c * DSTEP) = v[c];
+  }
+  __device__ __forceinline__ void load_c(int c, int k0) {
+    v[c] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off[c], k0 * 2, 0);
+  }
+  __device__ __forceinline__ void store_c(int c, uint16_t* lds) const {
+    *(u32x4_t*)(lds + dst0 + c * DSTEP) = v[c];
   }
 };
 
@@ -186,22 +194,6 @@ __device__ __forceinline__ void mfmas(const Frags<TL>& f, f32x16_t (&acc)[TL::TM
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
-// One 16-wide k slice: NM MFMAs, each followed by up to two LDS reads (the
-// next slice's fragments are all in flight after the first NR/2 MFMAs), one
-// LDS write and one global load (while those remain; a chunk's load reuses
-// the registers its LDS write has just read).
-template <int NM, int NR, int NV, int NW>
-__device__ __forceinline__ void sched_slice() {
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    SCHED_GROUP(SG_MFMA, 1);
-    if (2 * i < NR) SCHED_GROUP(SG_DS_R, 1);
-    if (2 * i + 1 < NR) SCHED_GROUP(SG_DS_R, 1);
-    if (i < NW) SCHED_GROUP(SG_DS_W, 1);
-    if (i < NV) SCHED_GROUP(SG_VMEM_R, 1);
-  }
-}
-
 // Wave position inside the block tile.  The wave index is moved to a scalar
 // register and the lane index is recomputed where it is needed (from the exec
 // mask count, made opaque to the optimiser), so addresses derived from it are
@@ -225,6 +217,39 @@ struct WavePos {
 // loads of stage kt+2 are issued right behind it, so a load has four k slices
 // to arrive.  Loads past the last stage re-read it (harmless), so the loop
 // body has no branches.  Ends with a barrier: the LDS is free on return.
+// One k slice with W chunk stores and V chunk loads: each MFMA is followed by
+// up to two LDS reads of the next slice; once the reads are all issued, each
+// MFMA is followed by one store and one load (reads first, so the next
+// slice's MFMAs do not wait behind the stores in the in-order LDS counter).
+template <int NM, int NR, int W, int V>
+__device__ __forceinline__ void sched_slice_wv() {
+  constexpr int RM = (NR + 1) / 2;  // MFMAs that carry reads
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    SCHED_GROUP(SG_MFMA, 1);
+    if (2 * i < NR) SCHED_GROUP(SG_DS_R, 1);
+    if (2 * i + 1 < NR) SCHED_GROUP(SG_DS_R, 1);
+    if (i >= RM && i - RM < W) SCHED_GROUP(SG_DS_W, 1);
+    if (i >= RM && i - RM < V) SCHED_GROUP(SG_VMEM_R, 1);
+  }
+}
+
+// Store chunks [Q0, Q1) of the register stage (A chunks first, then B) to
+// LDS, each followed by the load of the same chunk of the stage after.
+template <int Q0, int Q1, class LA, class LB>
+__device__ __forceinline__ void store_load(LA& la, LB& lb, uint16_t* An, uint16_t* Bn, int kn) {
+#pragma unroll
+  for (int q = Q0; q < Q1; ++q) {
+    if (q < LA::CH) {
+      la.store_c(q, An);
+      la.load_c(q, kn);
+    } else {
+      lb.store_c(q - LA::CH, Bn);
+      lb.load_c(q - LA::CH, kn);
+    }
+  }
+}
+
 template <class TL, class LA, class LB, bool SCHED = true>
 __device__ __forceinline__ void mainloop_steps(LA& la, LB& lb, int k_begin, int nk,
                                                uint16_t* smem, f32x16_t (&acc)[TL::TM][TL::TN]) {
@@ -241,7 +266,8 @@ __device__ __forceinline__ void mainloop_steps(LA& la, LB& lb, int k_begin, int 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   constexpr int NM = TL::TM * TL::TN, NR = TL::TM + TL::TN;
-  constexpr int NV = LA::NLOAD + LB::NLOAD, NW = LA::NSTORE + LB::NSTORE;
+  constexpr int NQ = LA::CH + LB::CH;  // chunks per stage, spread over slices 0..2
+  constexpr int Q1 = NQ / 3, Q2 = 2 * NQ / 3;
   Frags<TL> f0, f1;
   read_frags<TL>(f0, sA0, sB0, 0, wm, wn, lane);
   for (int kt = 0; kt < nk; ++kt) {
@@ -251,25 +277,32 @@ __device__ __forceinline__ void mainloop_steps(LA& la, LB& lb, int k_begin, int 
     uint16_t* An = odd ? sA0 : sA1;
     uint16_t* Bn = odd ? sB0 : sB1;
     const int kn2 = k_begin + (kt + 2 < nk ? kt + 2 : nk - 1) * BK;
+    // slice 0; the other buffer's last readers passed the previous barrier,
+    // so the stage in registers can go to it from here on
     read_frags<TL>(f1, A, B, 1, wm, wn, lane);
     mfmas<TL>(f0, acc);
-    if constexpr (SCHED) sched_slice<NM, NR, 0, 0>();
+    store_load<0, Q1>(la, lb, An, Bn, kn2);
+    if constexpr (SCHED) sched_slice_wv<NM, NR, Q1, Q1>();
+    __builtin_amdgcn_sched_barrier(0);
+    // slice 1
     read_frags<TL>(f0, A, B, 2, wm, wn, lane);
     mfmas<TL>(f1, acc);
-    if constexpr (SCHED) sched_slice<NM, NR, 0, 0>();
+    store_load<Q1, Q2>(la, lb, An, Bn, kn2);
+    if constexpr (SCHED) sched_slice_wv<NM, NR, Q2 - Q1, Q2 - Q1>();
+    __builtin_amdgcn_sched_barrier(0);
+    // slice 2
     read_frags<TL>(f1, A, B, 3, wm, wn, lane);
     mfmas<TL>(f0, acc);
-    la.store(An);
-    lb.store(Bn);
-    la.load(kn2, 0);
-    lb.load(kn2, 0);
-    if constexpr (SCHED) sched_slice<NM, NR, NV, NW>();
+    store_load<Q2, NQ>(la, lb, An, Bn, kn2);
+    if constexpr (SCHED) sched_slice_wv<NM, NR, NQ - Q2, NQ - Q2>();
+    __builtin_amdgcn_sched_barrier(0);
     // the next stage is complete once every wave passes the barrier; its
     // first fragments are read while the last slice's MFMAs run
     __syncthreads();
     read_frags<TL>(f0, An, Bn, 0, wm, wn, lane);
     mfmas<TL>(f1, acc);
-    if constexpr (SCHED) sched_slice<NM, NR, 0, 0>();
+    if constexpr (SCHED) sched_slice_wv<NM, NR, 0, 0>();
+    __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();  // LDS free for the caller's epilogue / next tile
 }
@@ -638,6 +671,7 @@ struct LoadKM {
   const uint16_t* base;
   long ld;
   int M, m0, lane, w;
+  template <bool TOK = false>
   __device__ __forceinline__ void issue(uint8_t* lds, int k0, int k_end,
                                         const int* tok = nullptr) const {
 #pragma unroll
@@ -646,8 +680,8 @@ struct LoadKM {
       const int kr = blk * 2 + (lane >> 5);
       const int s = lane & 31;
       const int col = (((s >> 1) ^ wg_swz(kr)) & 15) * 16 + (s & 1) * 8;
-      const int k = tok ? tok[kr] : k0 + kr;
-      const bool ok = (tok ? k >= 0 : k < k_end) && (m0 + col < M);
+      const int k = TOK ? tok[kr] : k0 + kr;
+      const bool ok = (TOK ? k >= 0 : k < k_end) && (m0 + col < M);
       const uint16_t* src = ok ? base + (long)k * ld + m0 + col : g_zero_row + col;
       // Issued by inline assembly: with the builtin the compiler treats these
       // LDS writes as possibly aliasing every later LDS read and waits for the
@@ -689,6 +723,7 @@ __device__ __forceinline__ long long uniform64(long long v) {
 // dW_gu tiles read dispatched row r from token xrows[r] / K: the token rows of
 // stage k are looked up one stage ahead into an LDS list (s_tok, double
 // buffered), from which the next stage's loads take their addresses.
+template <bool GATHER>
 __global__ __launch_bounds__(512) void wgrad_kernel(
     const uint16_t* __restrict__ xp, const int32_t* __restrict__ xrows, int K,
     const uint16_t* __restrict__ abuf, const uint16_t* __restrict__ dh,
@@ -699,7 +734,7 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
   constexpr int STAGE = 2 * BK * WG_ROWB;  // A + B tiles
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
   __shared__ long long s_it[257];  // first k-step of each expert's tiles; s_it[E_l] = W
-  __shared__ int s_tok[2][BK];     // source token rows of the next two stages (fused permute)
+  __shared__ int s_tok[GATHER ? 2 : 1][BK];  // source token rows of the next two stages
   const int tdm = (d + 255) / 256, tdn = (F + 255) / 256;
   const int tgm = (2 * F + 255) / 256, tgn = (d + 255) / 256;
   const int per_e = tdm * tdn + tgm * tgn;
@@ -763,7 +798,7 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
       t -= tdm * tdn;
       Asrc = dh;
       Bsrc = xp;
-      gat = xrows != nullptr;
+      gat = GATHER;
       M = 2 * F;
       N = d;
       m0 = (t / tgn) * 256;
@@ -783,15 +818,20 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
     // source token of dispatched row r (-1 past the expert's end)
     auto token = [&](int r) { return r < r1 ? xrows[r] / K : -1; };
     if (nk > 0) {  // block-uniform
-      if (gat) {
-        if (tid < BK) {
-          s_tok[0][tid] = token(r0 + tid);
-          s_tok[1][tid] = token(r0 + BK + tid);
+      if constexpr (GATHER) {
+        if (gat) {
+          if (tid < BK) {
+            s_tok[0][tid] = token(r0 + tid);
+            s_tok[1][tid] = token(r0 + BK + tid);
+          }
+          __syncthreads();
         }
-        __syncthreads();
       }
       la.issue(smem, r0, r1);
-      lb.issue(smem + BK * WG_ROWB, r0, r1, gat ? s_tok[0] : nullptr);
+      if (GATHER && gat)
+        lb.template issue<true>(smem + BK * WG_ROWB, r0, r1, s_tok[0]);
+      else
+        lb.issue(smem + BK * WG_ROWB, r0, r1);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       for (int kt = 0; kt < nk; ++kt) {
@@ -799,14 +839,16 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
         uint8_t* nxt = smem + ((kt + 1) & 1) * STAGE;
         if (kt + 1 < nk) {
           la.issue(nxt, r0 + (kt + 1) * BK, r1);
-          lb.issue(nxt + BK * WG_ROWB, r0 + (kt + 1) * BK, r1,
-                   gat ? s_tok[(kt + 1) & 1] : nullptr);
+          if (GATHER && gat)
+            lb.template issue<true>(nxt + BK * WG_ROWB, 0, 0, s_tok[(kt + 1) & 1]);
+          else
+            lb.issue(nxt + BK * WG_ROWB, r0 + (kt + 1) * BK, r1);
         }
         // token rows of stage kt + 2, stored into the list stage kt used
         // (its last reader, the issue of stage kt, is behind the previous
         // barrier)
         int tk = -1;
-        if (gat && tid < BK) tk = token(r0 + (kt + 2) * BK + tid);
+        if (GATHER && gat && tid < BK) tk = token(r0 + (kt + 2) * BK + tid);
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
           bf16x8_t a[TM], b[TN];
@@ -821,7 +863,7 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        if (gat && tid < BK) s_tok[kt & 1][tid] = tk;
+        if (GATHER && gat && tid < BK) s_tok[kt & 1][tid] = tk;
         __syncthreads();
       }
     }
@@ -1015,10 +1057,18 @@ int launch_ffn_wgrad_bf16(const moe_shape* s, const void* xp, const int32_t* xro
   const long per_e = (long)((d + 255) / 256) * ((F + 255) / 256) +
                      (long)((2 * F + 255) / 256) * ((d + 255) / 256);
   const int grid = persistent_grid(E_l * per_e);
-  MOE_LAUNCH("wgrad", st,
-             wgrad_kernel<<<grid, 512, 0, st>>>(
-                 (const uint16_t*)xp, xrows, (int)s->K, (const uint16_t*)a, (const uint16_t*)dh,
-                 (const uint16_t*)dyp, offsets, dW_gu, dW_down, E_l, d, F, accumulate ? 1 : 0));
+  if (xrows)
+    MOE_LAUNCH("wgrad", st,
+               wgrad_kernel<true><<<grid, 512, 0, st>>>(
+                   (const uint16_t*)xp, xrows, (int)s->K, (const uint16_t*)a,
+                   (const uint16_t*)dh, (const uint16_t*)dyp, offsets, dW_gu, dW_down, E_l, d, F,
+                   accumulate ? 1 : 0));
+  else
+    MOE_LAUNCH("wgrad", st,
+               wgrad_kernel<false><<<grid, 512, 0, st>>>(
+                   (const uint16_t*)xp, nullptr, (int)s->K, (const uint16_t*)a,
+                   (const uint16_t*)dh, (const uint16_t*)dyp, offsets, dW_gu, dW_down, E_l, d, F,
+                   accumulate ? 1 : 0));
   return check_launch("wgrad GEMM");
 }
 
