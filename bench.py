@@ -20,7 +20,7 @@ import sys
 import time
 
 METRIC = "MoE layer fwd+bwd tokens/s on 1 MI355X; grouped-GEMM MFMA util %; dispatch HBM GB/s"
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 (and fp16) matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
 
 GEMM_KERNELS = ("ffn_gate_up", "ffn_down", "dgrad_act", "dgrad_in", "wgrad")
@@ -36,7 +36,7 @@ def algorithmic(w, N, T_loc):
     """Per-launch algorithmic work: flops for the GEMMs, HBM bytes for the
     permute kernels (one pass over each operand, no re-reads)."""
     d, F, T, K, E = w.d, w.F, w.T, w.K, w.E
-    b = 2 if w.dtype == "bf16" else 4
+    b = 4 if w.dtype == "f32" else 2
     return {
         "ffn_gate_up": ("flop", 2.0 * N * d * 2 * F),
         "ffn_down": ("flop", 2.0 * N * F * d),
@@ -128,7 +128,8 @@ def cpu_oracle_baseline(w, inp, target_s=10.0):
         reps += 1
     return {"value": reps * Ts / total, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {Ts} of {w.T} tokens of {w.name}, full weights, {reps} x one "
-                      f"forward+backward (float64 numpy, bf16 rounding points), {total:.1f} s"}
+                      f"forward+backward (float64 numpy, {w.dtype} rounding points), "
+                      f"{total:.1f} s"}
 
 
 def main():
@@ -180,7 +181,8 @@ def main():
         f"{w.dtype} route={w.route}")
     inp = make_inputs(w, seed=0, microbatches=2)
     s = M.shape_of(w)
-    D = lambda a: torch.from_numpy(a).to("cuda", torch.bfloat16 if w.dtype == "bf16" else torch.float32)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(w.dtype, torch.float32)
+    D = lambda a: torch.from_numpy(a).to("cuda", tdt)
     F32 = lambda a: torch.from_numpy(a).to("cuda")
     topk = w.route == "topk"
     mode = M.MOE_ROUTE_TOPK if topk else M.MOE_ROUTE_FORCE_BALANCE

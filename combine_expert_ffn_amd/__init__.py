@@ -14,7 +14,7 @@ import ctypes as C
 from ._lib import (  # noqa: F401
     LIB_PATH, MB_FIELDS, MoeError, MoeMB, MoeShape, MoeStep, check, lib,
     MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MOE_ERR_HIP,
-    MOE_ERR_UNSUPPORTED, MOE_ERR_ARG, MOE_F32, MOE_BF16, MOE_ROUTE_TOPK,
+    MOE_ERR_UNSUPPORTED, MOE_ERR_ARG, MOE_F32, MOE_BF16, MOE_F16, MOE_ROUTE_TOPK,
     MOE_ROUTE_TOPK_FROM_LOGITS, MOE_ROUTE_FORCE_BALANCE, MOE_ACCUM_DX, MOE_ACCUM_DW,
     MOE_STEP_SERIALIZE, MOE_STEP_EAGER_WGRAD, MOE_STEP_SKIP_WGRAD, MOE_STEP_FUSED_PERMUTE,
 )
@@ -44,7 +44,7 @@ def _ws(ws):
 
 
 def make_shape(T, d, F, E, e_lo, E_l, K, dtype) -> MoeShape:
-    dt = {"bf16": MOE_BF16, "f32": MOE_F32}.get(dtype, dtype)
+    dt = {"bf16": MOE_BF16, "f16": MOE_F16, "f32": MOE_F32}.get(dtype, dtype)
     return MoeShape(int(T), int(d), int(F), int(E), int(e_lo), int(E_l), int(K), int(dt), 0)
 
 
@@ -180,7 +180,7 @@ class MicroBatch:
         import numpy as np
         import torch
 
-        dt = torch.bfloat16 if s.dtype == MOE_BF16 else torch.float32
+        dt = {MOE_BF16: torch.bfloat16, MOE_F16: torch.float16}.get(s.dtype, torch.float32)
         T, d, F, E, E_l, K = s.T, s.d, s.F, s.E, s.E_l, s.K
         cap = T * K
         f32, i32 = torch.float32, torch.int32

@@ -21,6 +21,7 @@ MOE_ERR_ARG = -7
 
 MOE_F32 = 0
 MOE_BF16 = 1
+MOE_F16 = 2
 
 MOE_ROUTE_TOPK = 0
 MOE_ROUTE_TOPK_FROM_LOGITS = 1

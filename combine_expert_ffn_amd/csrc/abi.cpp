@@ -57,8 +57,8 @@ void KernelTimer::stop() {
 
 static int validate_shape(const moe_shape* s) {
   if (!s) return set_error(MOE_ERR_NULL, "shape is NULL");
-  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16)
-    return set_error(MOE_ERR_DTYPE, "dtype %d is neither MOE_F32 nor MOE_BF16", s->dtype);
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16 && s->dtype != MOE_F16)
+    return set_error(MOE_ERR_DTYPE, "dtype %d is not MOE_F32, MOE_BF16 or MOE_F16", s->dtype);
   if (s->reserved != 0) return set_error(MOE_ERR_ARG, "shape.reserved must be 0");
   if (s->T < 0) return set_error(MOE_ERR_SHAPE, "T = %lld < 0", (long long)s->T);
   if (s->E < 1 || s->E > 512)
@@ -108,7 +108,7 @@ static int do_route(const moe_shape* s, int mode, const void* x, const void* W_r
   int rc;
   if (mode == MOE_ROUTE_FORCE_BALANCE) return launch_force_balance(s, idx, st);
   if (mode == MOE_ROUTE_TOPK) {
-    if (s->dtype == MOE_BF16 && s->T > 0) {
+    if (is16(s) && s->T > 0) {
       if ((rc = launch_transpose_wr(s, W_r, ws, st))) return rc;
     }
     if ((rc = launch_router_logits(s, x, W_r, ws, bias, logits, st))) return rc;
@@ -127,7 +127,7 @@ static int do_dispatch(const moe_shape* s, const void* x, const int32_t* idx, in
 
 // The fused permute addresses x with 32-bit byte offsets.
 static int check_gather_x(const moe_shape* s, const char* fn) {
-  const int64_t es = s->dtype == MOE_BF16 ? 2 : 4;
+  const int64_t es = (int64_t)elt_bytes(s);
   if (s->T * s->d * es >= (1LL << 31))
     return set_error(MOE_ERR_SHAPE, "%s: x is %lld bytes, the fused permute needs < 2^31", fn,
                      (long long)(s->T * s->d * es));
@@ -233,7 +233,7 @@ int moe_route(const moe_shape* s, int mode, const void* x, const void* W_r, cons
       REQUIRE(W_r);
       REQUIRE(logits);
       REQUIRE(gates);
-      if (s->dtype == MOE_BF16) {
+      if (is16(s)) {
         REQUIRE(ws);
         if (int rc = need_ws(__func__, ws_bytes, ws_wrt_bytes(s))) return rc;
       }
@@ -341,7 +341,7 @@ int moe_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h, const int3
   REQUIRE(W_down);
   REQUIRE(dh);
   REQUIRE(dxp);
-  if (s->dtype == MOE_BF16) {
+  if (is16(s)) {
     REQUIRE(ws);
     if (int rc = need_ws(__func__, ws_bytes, ws_wT_offset(s) + ws_wT_bytes(s))) return rc;
   }

@@ -261,7 +261,7 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
 }
 
 static inline int row_chunks(const moe_shape* s) {
-  return (int)(s->d * (s->dtype == MOE_BF16 ? 2 : 4) / 16);
+  return (int)(s->d * (int64_t)elt_bytes(s) / 16);
 }
 
 int launch_permute(const moe_shape* s, const void* x, const int32_t* row_of_pair, void* xp,
@@ -347,20 +347,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
   }
 }
 
+template <typename T>
+static void combine_t(const moe_shape* s, const void* yp, const float* gates,
+                      const int32_t* row_of_pair, void* out, hipStream_t st) {
+  MOE_LAUNCH("combine", st,
+             combine_kernel<T, 4><<<(unsigned)cdiv(s->T, 4), 256, 0, st>>>(
+                 (const uint4*)yp, gates, row_of_pair, (uint4*)out, (int)s->T, (int)s->K,
+                 row_chunks(s)));
+}
+
 int launch_combine(const moe_shape* s, const void* yp, const float* gates,
                    const int32_t* row_of_pair, void* out, hipStream_t st) {
   if (s->T == 0) return MOE_OK;
-  const unsigned grid = (unsigned)cdiv(s->T, 4);
-  if (s->dtype == MOE_BF16)
-    MOE_LAUNCH("combine", st,
-               combine_kernel<uint16_t, 4><<<grid, 256, 0, st>>>((const uint4*)yp, gates, row_of_pair,
-                                                      (uint4*)out, (int)s->T, (int)s->K,
-                                                      row_chunks(s)));
-  else
-    MOE_LAUNCH("combine", st,
-               combine_kernel<float, 4><<<grid, 256, 0, st>>>((const uint4*)yp, gates, row_of_pair,
-                                                   (uint4*)out, (int)s->T, (int)s->K,
-                                                   row_chunks(s)));
+  if (s->dtype == MOE_BF16) combine_t<uint16_t>(s, yp, gates, row_of_pair, out, st);
+  else if (s->dtype == MOE_F16) combine_t<_Float16>(s, yp, gates, row_of_pair, out, st);
+  else combine_t<float>(s, yp, gates, row_of_pair, out, st);
   return check_launch("combine");
 }
 
@@ -454,34 +455,30 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
   }
 }
 
+template <typename T, int MAXC>
+static void combine_bwd_t(const moe_shape* s, const void* dout, const void* yp,
+                          const float* gates, const int32_t* row_of_pair, void* dyp,
+                          float* dgates, hipStream_t st) {
+  MOE_LAUNCH("combine_bwd", st,
+             combine_bwd_kernel<T, MAXC><<<(unsigned)cdiv(s->T, 4), 256, 0, st>>>(
+                 (const uint4*)dout, (const uint4*)yp, gates, row_of_pair, (uint4*)dyp, dgates,
+                 (int)s->T, (int)s->K, row_chunks(s)));
+}
+
 int launch_combine_bwd(const moe_shape* s, const void* dout, const void* yp, const float* gates,
                        const int32_t* row_of_pair, void* dyp, float* dgates, hipStream_t st) {
   if (s->T == 0) return MOE_OK;
-  const unsigned grid = (unsigned)cdiv(s->T, 4);
   const int nch = row_chunks(s);
-  // d <= 16384: bf16 rows <= 2048 chunks, f32 rows <= 4096 chunks
+  // d <= 16384: 16-bit rows <= 2048 chunks, f32 rows <= 4096 chunks
   if (s->dtype == MOE_BF16) {
-    if (nch <= 256)
-      MOE_LAUNCH("combine_bwd", st,
-                 combine_bwd_kernel<uint16_t, 4><<<grid, 256, 0, st>>>(
-          (const uint4*)dout, (const uint4*)yp, gates, row_of_pair, (uint4*)dyp, dgates,
-          (int)s->T, (int)s->K, nch));
-    else
-      MOE_LAUNCH("combine_bwd", st,
-                 combine_bwd_kernel<uint16_t, 32><<<grid, 256, 0, st>>>(
-          (const uint4*)dout, (const uint4*)yp, gates, row_of_pair, (uint4*)dyp, dgates,
-          (int)s->T, (int)s->K, nch));
+    if (nch <= 256) combine_bwd_t<uint16_t, 4>(s, dout, yp, gates, row_of_pair, dyp, dgates, st);
+    else combine_bwd_t<uint16_t, 32>(s, dout, yp, gates, row_of_pair, dyp, dgates, st);
+  } else if (s->dtype == MOE_F16) {
+    if (nch <= 256) combine_bwd_t<_Float16, 4>(s, dout, yp, gates, row_of_pair, dyp, dgates, st);
+    else combine_bwd_t<_Float16, 32>(s, dout, yp, gates, row_of_pair, dyp, dgates, st);
   } else {
-    if (nch <= 256)
-      MOE_LAUNCH("combine_bwd", st,
-                 combine_bwd_kernel<float, 4><<<grid, 256, 0, st>>>(
-          (const uint4*)dout, (const uint4*)yp, gates, row_of_pair, (uint4*)dyp, dgates,
-          (int)s->T, (int)s->K, nch));
-    else
-      MOE_LAUNCH("combine_bwd", st,
-                 combine_bwd_kernel<float, 64><<<grid, 256, 0, st>>>(
-          (const uint4*)dout, (const uint4*)yp, gates, row_of_pair, (uint4*)dyp, dgates,
-          (int)s->T, (int)s->K, nch));
+    if (nch <= 256) combine_bwd_t<float, 4>(s, dout, yp, gates, row_of_pair, dyp, dgates, st);
+    else combine_bwd_t<float, 64>(s, dout, yp, gates, row_of_pair, dyp, dgates, st);
   }
   return check_launch("combine bwd");
 }
@@ -581,21 +578,26 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(
   }
 }
 
+template <typename T>
+static void dispatch_bwd_t(const moe_shape* s, const void* dxp, const int32_t* row_of_pair,
+                           const int32_t* idx, const float* dlogits, const void* W_rT, void* dx,
+                           bool accumulate, hipStream_t st) {
+  MOE_LAUNCH("dispatch_bwd", st,
+             dispatch_bwd_kernel<T, 4><<<(unsigned)cdiv(s->T, 4), 256, 0, st>>>(
+                 (const uint4*)dxp, row_of_pair, idx, dlogits, (const uint4*)W_rT, (uint4*)dx,
+                 (int)s->T, (int)s->K, (int)s->E, row_chunks(s), accumulate ? 1 : 0));
+}
+
 int launch_dispatch_bwd(const moe_shape* s, const void* dxp, const int32_t* row_of_pair,
                         const int32_t* idx, const float* dlogits, const void* W_rT, void* dx,
                         bool accumulate, hipStream_t st) {
   if (s->T == 0) return MOE_OK;
-  const unsigned grid = (unsigned)cdiv(s->T, 4);
   if (s->dtype == MOE_BF16)
-    MOE_LAUNCH("dispatch_bwd", st,
-               dispatch_bwd_kernel<uint16_t, 4><<<grid, 256, 0, st>>>(
-        (const uint4*)dxp, row_of_pair, idx, dlogits, (const uint4*)W_rT, (uint4*)dx, (int)s->T,
-        (int)s->K, (int)s->E, row_chunks(s), accumulate ? 1 : 0));
+    dispatch_bwd_t<uint16_t>(s, dxp, row_of_pair, idx, dlogits, W_rT, dx, accumulate, st);
+  else if (s->dtype == MOE_F16)
+    dispatch_bwd_t<_Float16>(s, dxp, row_of_pair, idx, dlogits, W_rT, dx, accumulate, st);
   else
-    MOE_LAUNCH("dispatch_bwd", st,
-               dispatch_bwd_kernel<float, 4><<<grid, 256, 0, st>>>(
-        (const uint4*)dxp, row_of_pair, idx, dlogits, (const uint4*)W_rT, (uint4*)dx, (int)s->T,
-        (int)s->K, (int)s->E, row_chunks(s), accumulate ? 1 : 0));
+    dispatch_bwd_t<float>(s, dxp, row_of_pair, idx, dlogits, W_rT, dx, accumulate, st);
   return check_launch("dispatch bwd");
 }
 

@@ -1,5 +1,5 @@
-// Grouped expert GEMMs in bf16 on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16,
-// float32 accumulation), with the SwiGLU forward and backward fused into the
+// Grouped expert GEMMs in bf16 or fp16 on gfx950 matrix cores
+// (v_mfma_f32_32x32x16_bf16 / _f16, float32 accumulation), with the SwiGLU forward and backward fused into the
 // epilogues.  These are the "expert FFN compute" that the expert-parallel
 // overlap pages hide the token exchange behind (skill card page 1, "What it
 // is"), split into activation gradient (dgrad, D) and weight gradient (wgrad,
@@ -39,6 +39,23 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// 16-bit element types of the matrix-core path.  Operands travel as raw 16-bit
+// patterns (global -> LDS -> registers); only the MFMA and the epilogue's
+// conversions depend on the type.
+struct BF16 {
+  typedef uint16_t elt;  // Chunk<uint16_t> converts bf16
+  static __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+struct F16 {
+  typedef _Float16 elt;
+  static __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+};
 
 constexpr int BK = 64;
 
@@ -155,6 +172,7 @@ __device__ __forceinline__ int st_col(int lane) { return (lane & 7) * 8; }
 // Store a staged 32 x 64 block as bf16 rows: out_row0 points at column 0 of
 // the block's first row, ld is the row stride, rows at or past n_rows are
 // skipped.
+template <class E>
 __device__ __forceinline__ void store_block(const float* blk, uint16_t* out_row0, size_t ld,
                                             int n_rows, int lane) {
 #pragma unroll
@@ -162,7 +180,7 @@ __device__ __forceinline__ void store_block(const float* blk, uint16_t* out_row0
     const int r = st_row(q, lane), c = st_col(lane);
     float f[8];
     ld8(blk + r * EP_LD + c, f);
-    if (r < n_rows) *(uint4*)(out_row0 + r * ld + c) = Chunk<uint16_t>::pack(f);
+    if (r < n_rows) *(uint4*)(out_row0 + r * ld + c) = Chunk<typename E::elt>::pack(f);
   }
 }
 
@@ -185,13 +203,13 @@ __device__ __forceinline__ void read_frags(Frags<TL>& f, const uint16_t* A, cons
     f.a[i] = *(const bf16x8_t*)(A + lds_off(wm * TL::WTM + i * 32 + fr, ch));
 }
 
-template <class TL>
+template <class TL, class E>
 __device__ __forceinline__ void mfmas(const Frags<TL>& f, f32x16_t (&acc)[TL::TM][TL::TN]) {
 #pragma unroll
   for (int i = 0; i < TL::TM; ++i)
 #pragma unroll
     for (int j = 0; j < TL::TN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+      acc[i][j] = E::mfma(f.a[i], f.b[j], acc[i][j]);
 }
 
 // Wave position inside the block tile.  The wave index is moved to a scalar
@@ -250,7 +268,7 @@ __device__ __forceinline__ void store_load(LA& la, LB& lb, uint16_t* An, uint16_
   }
 }
 
-template <class TL, class LA, class LB, bool SCHED = true>
+template <class TL, class E, class LA, class LB, bool SCHED = true>
 __device__ __forceinline__ void mainloop_steps(LA& la, LB& lb, int k_begin, int nk,
                                                uint16_t* smem, f32x16_t (&acc)[TL::TM][TL::TN]) {
   uint16_t* const sA0 = smem;
@@ -280,19 +298,19 @@ __device__ __forceinline__ void mainloop_steps(LA& la, LB& lb, int k_begin, int 
     // slice 0; the other buffer's last readers passed the previous barrier,
     // so the stage in registers can go to it from here on
     read_frags<TL>(f1, A, B, 1, wm, wn, lane);
-    mfmas<TL>(f0, acc);
+    mfmas<TL, E>(f0, acc);
     store_load<0, Q1>(la, lb, An, Bn, kn2);
     if constexpr (SCHED) sched_slice_wv<NM, NR, Q1, Q1>();
     __builtin_amdgcn_sched_barrier(0);
     // slice 1
     read_frags<TL>(f0, A, B, 2, wm, wn, lane);
-    mfmas<TL>(f1, acc);
+    mfmas<TL, E>(f1, acc);
     store_load<Q1, Q2>(la, lb, An, Bn, kn2);
     if constexpr (SCHED) sched_slice_wv<NM, NR, Q2 - Q1, Q2 - Q1>();
     __builtin_amdgcn_sched_barrier(0);
     // slice 2
     read_frags<TL>(f1, A, B, 3, wm, wn, lane);
-    mfmas<TL>(f0, acc);
+    mfmas<TL, E>(f0, acc);
     store_load<Q2, NQ>(la, lb, An, Bn, kn2);
     if constexpr (SCHED) sched_slice_wv<NM, NR, NQ - Q2, NQ - Q2>();
     __builtin_amdgcn_sched_barrier(0);
@@ -300,7 +318,7 @@ __device__ __forceinline__ void mainloop_steps(LA& la, LB& lb, int k_begin, int 
     // first fragments are read while the last slice's MFMAs run
     __syncthreads();
     read_frags<TL>(f0, An, Bn, 0, wm, wn, lane);
-    mfmas<TL>(f1, acc);
+    mfmas<TL, E>(f1, acc);
     if constexpr (SCHED) sched_slice_wv<NM, NR, 0, 0>();
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -310,7 +328,7 @@ __device__ __forceinline__ void mainloop_steps(LA& la, LB& lb, int k_begin, int 
 // The whole main loop over k in [k_begin, k_end) (a multiple of 64 long)
 // for a tile whose loaders are initialised: stage 0 to LDS, stage 1 to
 // registers, then the steps.
-template <class TL, class LA, class LB>
+template <class TL, class E, class LA, class LB>
 __device__ __forceinline__ void mainloop(LA& la, LB& lb, int k_begin, int k_end,
                                          uint16_t* smem, f32x16_t (&acc)[TL::TM][TL::TN]) {
   const int nk = (k_end - k_begin + BK - 1) / BK;
@@ -331,7 +349,7 @@ __device__ __forceinline__ void mainloop(LA& la, LB& lb, int k_begin, int k_end,
   la.load(k1, k_end);
   lb.load(k1, k_end);
   __syncthreads();
-  mainloop_steps<TL>(la, lb, k_begin, nk, smem, acc);
+  mainloop_steps<TL, E>(la, lb, k_begin, nk, smem, acc);
 }
 
 // Persistent schedule: the blocks form G = min(8, grid) groups by block % G
@@ -412,7 +430,7 @@ __global__ __launch_bounds__(TL::NT) void row_grouped_kernel(Op op,
     lb.load(k1, 0);
     __syncthreads();
     f32x16_t acc[TL::TM][TL::TN];
-    mainloop_steps<TL>(la, lb, 0, nk, smem, acc);
+    mainloop_steps<TL, typename Op::Elt>(la, lb, 0, nk, smem, acc);
     const int ce = e, cm0 = m0, cm_end = m_end, cnt = nt;
     sc.t += sc.step;
     const bool more = sc.t < sc.end;  // block-uniform
@@ -438,7 +456,9 @@ __global__ __launch_bounds__(TL::NT) void row_grouped_kernel(Op op,
 // With xrows set, the permute is fused into the A loads: xp is the token
 // matrix x [T][d] and dispatched row r reads token xrows[r] / K (xrows is the
 // dispatch plan's pair_of_row), so the permuted copy of x is never written.
+template <class E>
 struct GateUpOp {
+  typedef E Elt;
   const uint16_t* xp;
   const uint16_t* W_gu;
   uint16_t* h;
@@ -488,9 +508,9 @@ struct GateUpOp {
           for (int t = 0; t < 8; ++t) av[t] = silu_f(g[t]) * u[t];
           if (col_ok && rb + r < m_end) {
             const size_t row = (size_t)(rb + r);
-            *(uint4*)(h + row * 2 * F + j0) = Chunk<uint16_t>::pack(g);
-            *(uint4*)(h + row * 2 * F + F + j0) = Chunk<uint16_t>::pack(u);
-            *(uint4*)(a + row * F + j0) = Chunk<uint16_t>::pack(av);
+            *(uint4*)(h + row * 2 * F + j0) = Chunk<typename E::elt>::pack(g);
+            *(uint4*)(h + row * 2 * F + F + j0) = Chunk<typename E::elt>::pack(u);
+            *(uint4*)(a + row * F + j0) = Chunk<typename E::elt>::pack(av);
           }
         }
       }
@@ -499,7 +519,9 @@ struct GateUpOp {
 };
 
 // forward GEMM2: y_p = a . W_down[e]^T  (A: a rows, K = F; B: W_down rows, K = F)
+template <class E>
 struct DownOp {
+  typedef E Elt;
   const uint16_t* a;
   const uint16_t* W_down;
   uint16_t* yp;
@@ -525,7 +547,7 @@ struct DownOp {
       for (int i = 0; i < TL::TM; ++i) {
         const int rb = m0 + w.wm * TL::WTM + i * 32;
         const float* blk = stage_rows<TL>(acc, i, p, smem, w.wave, w.lane);
-        store_block(blk, yp + (size_t)rb * d + cb, (size_t)d, m_end - rb, w.lane);
+        store_block<E>(blk, yp + (size_t)rb * d + cb, (size_t)d, m_end - rb, w.lane);
       }
     }
   }
@@ -533,7 +555,9 @@ struct DownOp {
 
 // dgrad GEMM A: da = dy_p . W_down[e]  (A: dy_p rows, K = d; B: W_down[e]
 // transposed, W_downT[e] [F][d], K-contiguous) with the SwiGLU backward epilogue.
+template <class E>
 struct DgradActOp {
+  typedef E Elt;
   const uint16_t* dyp;
   const uint16_t* hbuf;
   const uint16_t* W_downT;
@@ -576,8 +600,8 @@ struct DgradActOp {
           const int r = st_row(q, w.lane);
           float da[8], g[8], u[8], dg[8], du[8];
           ld8(blk + r * EP_LD + c, da);
-          Chunk<uint16_t>::unpack(gv[q], g);
-          Chunk<uint16_t>::unpack(uv[q], u);
+          Chunk<typename E::elt>::unpack(gv[q], g);
+          Chunk<typename E::elt>::unpack(uv[q], u);
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
             const float sg = sigmoid_f(g[t]);
@@ -586,8 +610,8 @@ struct DgradActOp {
           }
           if (rb + r < m_end) {
             const size_t row = (size_t)(rb + r);
-            *(uint4*)(dh + row * 2 * F + cb + c) = Chunk<uint16_t>::pack(dg);
-            *(uint4*)(dh + row * 2 * F + F + cb + c) = Chunk<uint16_t>::pack(du);
+            *(uint4*)(dh + row * 2 * F + cb + c) = Chunk<typename E::elt>::pack(dg);
+            *(uint4*)(dh + row * 2 * F + F + cb + c) = Chunk<typename E::elt>::pack(du);
           }
         }
       }
@@ -597,7 +621,9 @@ struct DgradActOp {
 
 // dgrad GEMM B: dxp = dh . W_gu[e]  (A: dh rows, K = 2F; B: W_gu[e]
 // transposed, W_guT[e] [d][2F], K-contiguous)
+template <class E>
 struct DgradInOp {
+  typedef E Elt;
   const uint16_t* dh;
   const uint16_t* W_guT;
   uint16_t* dxp;
@@ -624,7 +650,7 @@ struct DgradInOp {
       for (int i = 0; i < TL::TM; ++i) {
         const int rb = m0 + w.wm * TL::WTM + i * 32;
         const float* blk = stage_rows<TL>(acc, i, p, smem, w.wave, w.lane);
-        store_block(blk, dxp + (size_t)rb * d + cb, (size_t)d, m_end - rb, w.lane);
+        store_block<E>(blk, dxp + (size_t)rb * d + cb, (size_t)d, m_end - rb, w.lane);
       }
     }
   }
@@ -723,7 +749,7 @@ __device__ __forceinline__ long long uniform64(long long v) {
 // dW_gu tiles read dispatched row r from token xrows[r] / K: the token rows of
 // stage k are looked up one stage ahead into an LDS list (s_tok, double
 // buffered), from which the next stage's loads take their addresses.
-template <bool GATHER>
+template <bool GATHER, class E>
 __global__ __launch_bounds__(512) void wgrad_kernel(
     const uint16_t* __restrict__ xp, const int32_t* __restrict__ xrows, int K,
     const uint16_t* __restrict__ abuf, const uint16_t* __restrict__ dh,
@@ -860,7 +886,7 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
           for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+              acc[i][j] = E::mfma(a[i], b[j], acc[i][j]);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (GATHER && gat && tid < BK) s_tok[kt & 1][tid] = tk;
@@ -899,7 +925,7 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
 // router logits: l = x . W_r + bias with W_r given transposed (W_rT [E][d]),
 // float32 output.
 // ---------------------------------------------------------------------------
-template <class TL>
+template <class TL, class EL>
 __global__ __launch_bounds__(TL::NT) void router_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W_rT,
     const float* __restrict__ bias, float* __restrict__ logits, int T, int d, int E,
@@ -914,7 +940,7 @@ __global__ __launch_bounds__(TL::NT) void router_kernel(
     la.init(x + (size_t)m0 * d, [&](int r) { return (min(m0 + r, T - 1) - m0) * d; }, tid);
     lb.init(W_rT + (size_t)n0 * d, [&](int n) { return (min(n0 + n, E - 1) - n0) * d; }, tid);
     f32x16_t acc[TL::TM][TL::TN];
-    mainloop<TL>(la, lb, 0, d, smem, acc);
+    mainloop<TL, EL>(la, lb, 0, d, smem, acc);
 #pragma unroll
     for (int j = 0; j < TL::TN; ++j) {
       const int col = n0 + wn * TL::WTN + j * 32 + (lane & 31);
@@ -995,30 +1021,89 @@ int launch_row_grouped(const char* name, const moe_shape* s, const Op& op,
   return check_launch(name);
 }
 
-}  // namespace
-
 // ---------------------------------------------------------------------------
-// launchers (bf16)
+// launchers (16-bit types, dispatched on shape->dtype)
 // ---------------------------------------------------------------------------
-int launch_ffn_fwd_bf16(const moe_shape* s, const void* xp, const int32_t* xrows,
-                        const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
-                        const void* W_down, void* h, void* a, void* yp, hipStream_t st) {
+template <class E>
+int ffn_fwd_t(const moe_shape* s, const void* xp, const int32_t* xrows, const int32_t* offsets,
+              const int32_t* tile_offsets, const void* W_gu, const void* W_down, void* h,
+              void* a, void* yp, hipStream_t st) {
   const int d = (int)s->d, F = (int)s->F;
-  GateUpOp g{(const uint16_t*)xp, (const uint16_t*)W_gu, (uint16_t*)h, (uint16_t*)a, d, F,
-             xrows, (int)s->K};
+  GateUpOp<E> g{(const uint16_t*)xp, (const uint16_t*)W_gu, (uint16_t*)h, (uint16_t*)a, d, F,
+                xrows, (int)s->K};
   if (int rc = launch_row_grouped("ffn_gate_up", s, g, offsets, tile_offsets,
                                   (F + T256::BN / 2 - 1) / (T256::BN / 2), st))
     return rc;
-  DownOp dn{(const uint16_t*)a, (const uint16_t*)W_down, (uint16_t*)yp, d, F};
+  DownOp<E> dn{(const uint16_t*)a, (const uint16_t*)W_down, (uint16_t*)yp, d, F};
   return launch_row_grouped("ffn_down", s, dn, offsets, tile_offsets,
                             (d + T256::BN - 1) / T256::BN, st);
 }
 
-int launch_dgrad_weights_bf16(const moe_shape* s, const void* W_gu, const void* W_down,
+template <class E>
+int ffn_dgrad_t(const moe_shape* s, const void* dyp, const void* h, const int32_t* offsets,
+                const int32_t* tile_offsets, void* dh, void* dxp, void* ws, hipStream_t st) {
+  const int d = (int)s->d, F = (int)s->F;
+  const uint16_t* W_downT = (const uint16_t*)((char*)ws + ws_wT_offset(s));
+  const uint16_t* W_guT = (const uint16_t*)((const char*)W_downT + ws_wT_down_bytes(s));
+  DgradActOp<E> da{(const uint16_t*)dyp, (const uint16_t*)h, W_downT, (uint16_t*)dh, d, F};
+  if (int rc = launch_row_grouped("dgrad_act", s, da, offsets, tile_offsets,
+                                  (F + T256::BN - 1) / T256::BN, st))
+    return rc;
+  DgradInOp<E> di{(const uint16_t*)dh, W_guT, (uint16_t*)dxp, d, F};
+  return launch_row_grouped("dgrad_in", s, di, offsets, tile_offsets,
+                            (d + T256::BN - 1) / T256::BN, st);
+}
+
+template <class E>
+void wgrad_t(const moe_shape* s, const void* xp, const int32_t* xrows, const void* a,
+             const void* dh, const void* dyp, const int32_t* offsets, float* dW_gu,
+             float* dW_down, bool accumulate, hipStream_t st) {
+  const int d = (int)s->d, F = (int)s->F, E_l = (int)s->E_l;
+  const long per_e = (long)((d + 255) / 256) * ((F + 255) / 256) +
+                     (long)((2 * F + 255) / 256) * ((d + 255) / 256);
+  const int grid = persistent_grid(E_l * per_e);
+  if (xrows)
+    MOE_LAUNCH("wgrad", st,
+               wgrad_kernel<true, E><<<grid, 512, 0, st>>>(
+                   (const uint16_t*)xp, xrows, (int)s->K, (const uint16_t*)a,
+                   (const uint16_t*)dh, (const uint16_t*)dyp, offsets, dW_gu, dW_down, E_l, d, F,
+                   accumulate ? 1 : 0));
+  else
+    MOE_LAUNCH("wgrad", st,
+               wgrad_kernel<false, E><<<grid, 512, 0, st>>>(
+                   (const uint16_t*)xp, nullptr, (int)s->K, (const uint16_t*)a,
+                   (const uint16_t*)dh, (const uint16_t*)dyp, offsets, dW_gu, dW_down, E_l, d, F,
+                   accumulate ? 1 : 0));
+}
+
+template <class E>
+void router_t(const moe_shape* s, const void* x, const void* W_rT, const float* bias,
+              float* logits, hipStream_t st) {
+  using TR = Tile<128, 128, 2, 2>;
+  const int T = (int)s->T, d = (int)s->d, En = (int)s->E;
+  const int nt = (En + TR::BN - 1) / TR::BN, mt = (T + TR::BM - 1) / TR::BM;
+  const int grid = persistent_grid((long)mt * nt);
+  MOE_LAUNCH("router", st,
+             router_kernel<TR, E><<<grid, TR::NT, 0, st>>>((const uint16_t*)x,
+                                                           (const uint16_t*)W_rT, bias, logits, T,
+                                                           d, En, nt, mt));
+}
+
+}  // namespace
+
+int launch_ffn_fwd_mfma(const moe_shape* s, const void* xp, const int32_t* xrows,
+                        const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
+                        const void* W_down, void* h, void* a, void* yp, hipStream_t st) {
+  return s->dtype == MOE_F16
+             ? ffn_fwd_t<F16>(s, xp, xrows, offsets, tile_offsets, W_gu, W_down, h, a, yp, st)
+             : ffn_fwd_t<BF16>(s, xp, xrows, offsets, tile_offsets, W_gu, W_down, h, a, yp, st);
+}
+
+int launch_dgrad_weights_mfma(const moe_shape* s, const void* W_gu, const void* W_down,
                               void* ws, hipStream_t st) {
   const int d = (int)s->d, F = (int)s->F, E_l = (int)s->E_l;
-  // K-contiguous copies of the weights: W_downT[e] = W_down[e]^T [F][d],
-  // W_guT[e] = W_gu[e]^T [d][2F]
+  // K-contiguous copies of the weights (16-bit moves, any 16-bit type):
+  // W_downT[e] = W_down[e]^T [F][d], W_guT[e] = W_gu[e]^T [d][2F]
   uint16_t* W_downT = (uint16_t*)((char*)ws + ws_wT_offset(s));
   uint16_t* W_guT = (uint16_t*)((char*)W_downT + ws_wT_down_bytes(s));
   MOE_LAUNCH("transpose_w", st,
@@ -1031,56 +1116,32 @@ int launch_dgrad_weights_bf16(const moe_shape* s, const void* W_gu, const void* 
   return check_launch("transpose W_gu");
 }
 
-int launch_ffn_dgrad_bf16(const moe_shape* s, const void* dyp, const void* h,
+int launch_ffn_dgrad_mfma(const moe_shape* s, const void* dyp, const void* h,
                           const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
                           const void* W_down, void* dh, void* dxp, void* ws, bool weights_ready,
                           hipStream_t st) {
-  const int d = (int)s->d, F = (int)s->F;
   if (!weights_ready)
-    if (int rc = launch_dgrad_weights_bf16(s, W_gu, W_down, ws, st)) return rc;
-  const uint16_t* W_downT = (const uint16_t*)((char*)ws + ws_wT_offset(s));
-  const uint16_t* W_guT = (const uint16_t*)((const char*)W_downT + ws_wT_down_bytes(s));
-  DgradActOp da{(const uint16_t*)dyp, (const uint16_t*)h, W_downT, (uint16_t*)dh, d, F};
-  if (int rc = launch_row_grouped("dgrad_act", s, da, offsets, tile_offsets,
-                                  (F + T256::BN - 1) / T256::BN, st))
-    return rc;
-  DgradInOp di{(const uint16_t*)dh, W_guT, (uint16_t*)dxp, d, F};
-  return launch_row_grouped("dgrad_in", s, di, offsets, tile_offsets,
-                            (d + T256::BN - 1) / T256::BN, st);
+    if (int rc = launch_dgrad_weights_mfma(s, W_gu, W_down, ws, st)) return rc;
+  return s->dtype == MOE_F16
+             ? ffn_dgrad_t<F16>(s, dyp, h, offsets, tile_offsets, dh, dxp, ws, st)
+             : ffn_dgrad_t<BF16>(s, dyp, h, offsets, tile_offsets, dh, dxp, ws, st);
 }
 
-int launch_ffn_wgrad_bf16(const moe_shape* s, const void* xp, const int32_t* xrows,
+int launch_ffn_wgrad_mfma(const moe_shape* s, const void* xp, const int32_t* xrows,
                           const void* a, const void* dh, const void* dyp,
                           const int32_t* offsets, float* dW_gu, float* dW_down, bool accumulate,
                           hipStream_t st) {
-  const int d = (int)s->d, F = (int)s->F, E_l = (int)s->E_l;
-  const long per_e = (long)((d + 255) / 256) * ((F + 255) / 256) +
-                     (long)((2 * F + 255) / 256) * ((d + 255) / 256);
-  const int grid = persistent_grid(E_l * per_e);
-  if (xrows)
-    MOE_LAUNCH("wgrad", st,
-               wgrad_kernel<true><<<grid, 512, 0, st>>>(
-                   (const uint16_t*)xp, xrows, (int)s->K, (const uint16_t*)a,
-                   (const uint16_t*)dh, (const uint16_t*)dyp, offsets, dW_gu, dW_down, E_l, d, F,
-                   accumulate ? 1 : 0));
+  if (s->dtype == MOE_F16)
+    wgrad_t<F16>(s, xp, xrows, a, dh, dyp, offsets, dW_gu, dW_down, accumulate, st);
   else
-    MOE_LAUNCH("wgrad", st,
-               wgrad_kernel<false><<<grid, 512, 0, st>>>(
-                   (const uint16_t*)xp, nullptr, (int)s->K, (const uint16_t*)a,
-                   (const uint16_t*)dh, (const uint16_t*)dyp, offsets, dW_gu, dW_down, E_l, d, F,
-                   accumulate ? 1 : 0));
+    wgrad_t<BF16>(s, xp, xrows, a, dh, dyp, offsets, dW_gu, dW_down, accumulate, st);
   return check_launch("wgrad GEMM");
 }
 
-int launch_router_logits_bf16(const moe_shape* s, const void* x, const void* W_rT,
+int launch_router_logits_mfma(const moe_shape* s, const void* x, const void* W_rT,
                               const float* bias, float* logits, hipStream_t st) {
-  using TR = Tile<128, 128, 2, 2>;
-  const int T = (int)s->T, d = (int)s->d, E = (int)s->E;
-  const int nt = (E + TR::BN - 1) / TR::BN, mt = (T + TR::BM - 1) / TR::BM;
-  const int grid = persistent_grid((long)mt * nt);
-  MOE_LAUNCH("router", st,
-             router_kernel<TR><<<grid, TR::NT, 0, st>>>((const uint16_t*)x, (const uint16_t*)W_rT,
-                                                        bias, logits, T, d, E, nt, mt));
+  if (s->dtype == MOE_F16) router_t<F16>(s, x, W_rT, bias, logits, st);
+  else router_t<BF16>(s, x, W_rT, bias, logits, st);
   return check_launch("router GEMM");
 }
 

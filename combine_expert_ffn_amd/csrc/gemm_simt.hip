@@ -1,9 +1,9 @@
 // Expert GEMMs in float32: one thread per output element, float32
 // accumulation in k order.  This is the float32 mode of the library (small
-// layers, exact-to-1e-5 checks); bf16 layers use the matrix-core kernels in
-// gemm_mfma.hip.  Same formulas as there: SwiGLU expert FFN forward, its
-// activation gradient (D) and weight gradient (W) (1F1B note page 2, "MoE 1F1B
-// overlap").
+// layers, exact-to-1e-5 checks); bf16 and fp16 layers use the matrix-core
+// kernels in gemm_mfma.hip.  Same formulas as there: SwiGLU expert FFN forward,
+// its activation gradient (D) and weight gradient (W) (1F1B note page 2, "MoE
+// 1F1B overlap").
 #include "moe_internal.h"
 
 namespace moe {
@@ -131,16 +131,16 @@ __global__ __launch_bounds__(256) void f32_wgrad_kernel(
   *o = accumulate ? *o + acc : acc;
 }
 
-int launch_ffn_fwd_bf16(const moe_shape* s, const void* xp, const int32_t* xrows,
+int launch_ffn_fwd_mfma(const moe_shape* s, const void* xp, const int32_t* xrows,
                         const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
                         const void* W_down, void* h, void* a, void* yp, hipStream_t st);
-int launch_dgrad_weights_bf16(const moe_shape* s, const void* W_gu, const void* W_down,
+int launch_dgrad_weights_mfma(const moe_shape* s, const void* W_gu, const void* W_down,
                               void* ws, hipStream_t st);
-int launch_ffn_dgrad_bf16(const moe_shape* s, const void* dyp, const void* h,
+int launch_ffn_dgrad_mfma(const moe_shape* s, const void* dyp, const void* h,
                           const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
                           const void* W_down, void* dh, void* dxp, void* ws, bool weights_ready,
                           hipStream_t st);
-int launch_ffn_wgrad_bf16(const moe_shape* s, const void* xp, const int32_t* xrows,
+int launch_ffn_wgrad_mfma(const moe_shape* s, const void* xp, const int32_t* xrows,
                           const void* a, const void* dh, const void* dyp,
                           const int32_t* offsets, float* dW_gu, float* dW_down, bool accumulate,
                           hipStream_t st);
@@ -149,8 +149,8 @@ int launch_ffn_fwd(const moe_shape* s, const void* xp, const int32_t* xrows,
                    const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
                    const void* W_down, void* h, void* a, void* yp, hipStream_t st) {
   if (s->T == 0) return MOE_OK;
-  if (s->dtype == MOE_BF16)
-    return launch_ffn_fwd_bf16(s, xp, xrows, offsets, tile_offsets, W_gu, W_down, h, a, yp, st);
+  if (is16(s))
+    return launch_ffn_fwd_mfma(s, xp, xrows, offsets, tile_offsets, W_gu, W_down, h, a, yp, st);
   const long cap = s->T * s->K;
   const int d = (int)s->d, F = (int)s->F, E_l = (int)s->E_l;
   MOE_LAUNCH("f32_gate_up", st,
@@ -165,16 +165,16 @@ int launch_ffn_fwd(const moe_shape* s, const void* xp, const int32_t* xrows,
 
 int launch_dgrad_weights(const moe_shape* s, const void* W_gu, const void* W_down, void* ws,
                          hipStream_t st) {
-  if (s->T == 0 || s->dtype != MOE_BF16) return MOE_OK;
-  return launch_dgrad_weights_bf16(s, W_gu, W_down, ws, st);
+  if (s->T == 0 || !is16(s)) return MOE_OK;
+  return launch_dgrad_weights_mfma(s, W_gu, W_down, ws, st);
 }
 
 int launch_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h, const int32_t* offsets,
                      const int32_t* tile_offsets, const void* W_gu, const void* W_down, void* dh,
                      void* dxp, void* ws, bool weights_ready, hipStream_t st) {
   if (s->T == 0) return MOE_OK;
-  if (s->dtype == MOE_BF16)
-    return launch_ffn_dgrad_bf16(s, dyp, h, offsets, tile_offsets, W_gu, W_down, dh, dxp, ws,
+  if (is16(s))
+    return launch_ffn_dgrad_mfma(s, dyp, h, offsets, tile_offsets, W_gu, W_down, dh, dxp, ws,
                                  weights_ready, st);
   const long cap = s->T * s->K;
   const int d = (int)s->d, F = (int)s->F, E_l = (int)s->E_l;
@@ -192,8 +192,8 @@ int launch_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h, const i
 int launch_ffn_wgrad(const moe_shape* s, const void* xp, const int32_t* xrows, const void* a,
                      const void* dh, const void* dyp, const int32_t* offsets, float* dW_gu,
                      float* dW_down, bool accumulate, hipStream_t st) {
-  if (s->dtype == MOE_BF16)
-    return launch_ffn_wgrad_bf16(s, xp, xrows, a, dh, dyp, offsets, dW_gu, dW_down, accumulate,
+  if (is16(s))
+    return launch_ffn_wgrad_mfma(s, xp, xrows, a, dh, dyp, offsets, dW_gu, dW_down, accumulate,
                                  st);
   const long n = s->E_l * (s->d * s->F + 2 * s->F * s->d);
   MOE_LAUNCH("f32_wgrad", st,

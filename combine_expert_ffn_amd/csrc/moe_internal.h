@@ -36,7 +36,14 @@ template <> struct Elt<uint16_t> {
   static __device__ __forceinline__ void st(uint16_t* p, float v) { *p = f2bf(v); }
 };
 
-// Unpack a 16-byte chunk into floats (8 bf16 or 4 f32).
+// fp16 (IEEE binary16) is stored as _Float16; the conversions round to
+// nearest even (v_cvt_f16_f32 under the default rounding mode).
+template <> struct Elt<_Float16> {
+  static __device__ __forceinline__ float ld(const _Float16* p) { return (float)*p; }
+  static __device__ __forceinline__ void st(_Float16* p, float v) { *p = (_Float16)v; }
+};
+
+// Unpack a 16-byte chunk into floats (8 bf16, 8 fp16 or 4 f32).
 template <typename T> struct Chunk;
 template <> struct Chunk<uint16_t> {
   static constexpr int N = 8;
@@ -55,6 +62,21 @@ template <> struct Chunk<uint16_t> {
     r.z = pack_bf2(f[4], f[5]);
     r.w = pack_bf2(f[6], f[7]);
     return r;
+  }
+};
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+template <> struct Chunk<_Float16> {
+  static constexpr int N = 8;
+  static __device__ __forceinline__ void unpack(const uint4& v, float* f) {
+    const f16x8_t h = __builtin_bit_cast(f16x8_t, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (float)h[i];
+  }
+  static __device__ __forceinline__ uint4 pack(const float* f) {
+    f16x8_t h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = (_Float16)f[i];
+    return __builtin_bit_cast(uint4, h);
   }
 };
 template <> struct Chunk<float> {
@@ -117,21 +139,24 @@ constexpr int kRouterChunk = 256;
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// 16-bit data types (bf16, fp16) take the matrix-core path.
+inline bool is16(const moe_shape* s) { return s->dtype != MOE_F32; }
+inline size_t elt_bytes(const moe_shape* s) { return is16(s) ? 2 : 4; }
+
 // Workspace layout pieces (bytes).
 inline size_t ws_plan_bytes(const moe_shape* s) {
   int64_t nb = cdiv(s->T * s->K, kPlanChunk);
   return align_up((size_t)(2 * s->E_l * nb) * sizeof(int32_t), 256);
 }
 inline size_t ws_wrt_bytes(const moe_shape* s) {
-  size_t es = s->dtype == MOE_BF16 ? 2 : 4;
-  return align_up((size_t)(s->E * s->d) * es, 256);
+  return align_up((size_t)(s->E * s->d) * elt_bytes(s), 256);
 }
 inline size_t ws_router_partial_bytes(const moe_shape* s) {
   int64_t nc = cdiv(s->T, kRouterChunk);
   return align_up((size_t)(nc * s->d * s->E) * sizeof(float), 256);
 }
-// Transposed expert weights for the bf16 dgrad: W_downT [E_l][F][d] then
-// W_guT [E_l][d][2F] (bf16).  The float32 dgrad needs none.  They sit after
+// Transposed expert weights for the 16-bit dgrad: W_downT [E_l][F][d] then
+// W_guT [E_l][d][2F].  The float32 dgrad needs none.  They sit after
 // the regions of the plan, the transposed router weights and the router
 // gradient partials, so a step can write them while the same micro-batch's
 // router backward still uses its partials.
@@ -142,11 +167,11 @@ inline size_t ws_wT_offset(const moe_shape* s) {
   return align_up(b, 256);
 }
 inline size_t ws_wT_down_bytes(const moe_shape* s) {
-  return s->dtype == MOE_BF16 ? align_up((size_t)(s->E_l * s->F * s->d) * 2, 256) : 0;
+  return is16(s) ? align_up((size_t)(s->E_l * s->F * s->d) * 2, 256) : 0;
 }
 inline size_t ws_wT_bytes(const moe_shape* s) {
-  return s->dtype == MOE_BF16 ? ws_wT_down_bytes(s) + align_up((size_t)(s->E_l * 2 * s->F * s->d) * 2, 256)
-                              : 0;
+  return is16(s) ? ws_wT_down_bytes(s) + align_up((size_t)(s->E_l * 2 * s->F * s->d) * 2, 256)
+                 : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -181,7 +206,7 @@ int launch_dispatch_bwd(const moe_shape* s, const void* dxp, const int32_t* row_
 int launch_ffn_fwd(const moe_shape* s, const void* xp, const int32_t* xrows,
                    const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
                    const void* W_down, void* h, void* a, void* yp, hipStream_t st);
-// The bf16 dgrad's transposed weight copies (into ws at ws_wT_offset); a
+// The 16-bit dgrad's transposed weight copies (into ws at ws_wT_offset); a
 // no-op in float32.
 int launch_dgrad_weights(const moe_shape* s, const void* W_gu, const void* W_down, void* ws,
                          hipStream_t st);

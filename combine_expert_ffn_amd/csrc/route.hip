@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void transpose_wr_kernel(const T* __restrict__
 
 int launch_transpose_wr(const moe_shape* s, const void* W_r, void* W_rT, hipStream_t st) {
   dim3 grid((unsigned)cdiv(s->d, 32), (unsigned)cdiv(s->E, 32));
-  if (s->dtype == MOE_BF16)
+  if (is16(s))  // a 16-bit copy: the same kernel for bf16 and fp16
     MOE_LAUNCH("transpose_wr", st,
                transpose_wr_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)W_r, (uint16_t*)W_rT,
                                                         (int)s->d, (int)s->E));
@@ -46,7 +46,7 @@ int launch_transpose_wr(const moe_shape* s, const void* W_r, void* W_rT, hipStre
 
 // ---------------------------------------------------------------------------
 // float32 router logits: one thread per (t, e), float32 accumulation.
-// (The bf16 path uses the MFMA GEMM in gemm_mfma.hip.)
+// (The 16-bit path uses the MFMA GEMM in gemm_mfma.hip.)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void router_logits_f32_kernel(const float* __restrict__ x,
                                                                 const float* __restrict__ W_r,
@@ -63,13 +63,13 @@ __global__ __launch_bounds__(256) void router_logits_f32_kernel(const float* __r
   logits[i] = acc;
 }
 
-int launch_router_logits_bf16(const moe_shape* s, const void* x, const void* W_rT,
+int launch_router_logits_mfma(const moe_shape* s, const void* x, const void* W_rT,
                               const float* bias, float* logits, hipStream_t st);
 
 int launch_router_logits(const moe_shape* s, const void* x, const void* W_r, const void* W_rT,
                          const float* bias, float* logits, hipStream_t st) {
   if (s->T == 0) return MOE_OK;
-  if (s->dtype == MOE_BF16) return launch_router_logits_bf16(s, x, W_rT, bias, logits, st);
+  if (is16(s)) return launch_router_logits_mfma(s, x, W_rT, bias, logits, st);
   const long n = s->T * s->E;
   MOE_LAUNCH("router_logits_f32", st,
              router_logits_f32_kernel<<<(unsigned)cdiv(n, 256), 256, 0, st>>>(
@@ -276,6 +276,11 @@ int launch_route_bwd(const moe_shape* s, const float* dgates, const float* gates
       MOE_LAUNCH("dwr_partial", st,
                  dwr_partial_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)x, dlogits, partial,
                                                          (int)s->T, (int)s->d, (int)s->E));
+    else if (s->dtype == MOE_F16)
+      MOE_LAUNCH("dwr_partial", st,
+                 dwr_partial_kernel<_Float16><<<grid, 256, 0, st>>>((const _Float16*)x, dlogits,
+                                                                    partial, (int)s->T,
+                                                                    (int)s->d, (int)s->E));
     else
       MOE_LAUNCH("dwr_partial", st,
                  dwr_partial_kernel<float><<<grid, 256, 0, st>>>((const float*)x, dlogits, partial,

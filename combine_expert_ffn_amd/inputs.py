@@ -8,7 +8,8 @@ data is not used: shapes follow each workload's description, values are
 synthetic.
 
 Recipe: numpy PCG64 with the given seed; normals drawn in float64, cast to
-float32, then (for bf16 workloads) rounded to bfloat16 by torch's RNE cast.
+float32, then (for bf16 / f16 workloads) rounded to bfloat16 by torch's RNE cast
+or to IEEE binary16 by numpy's RNE cast.
 Draw order: x, W_r, W_gu, W_down, dout, then gates (forced-balance workloads).
 A second micro-batch draws its x and dout after all of the above.
 """
@@ -31,7 +32,7 @@ class Workload:
     e_lo: int
     E_l: int
     K: int
-    dtype: str                 # "f32" or "bf16"
+    dtype: str                 # "f32", "bf16" or "f16"
     route: str                 # "topk" or "force_balance"
     weight_std: float = 0.02
     zipf_s: float = 0.0        # >0: per-expert router bias -s*ln(e+1)
@@ -62,6 +63,10 @@ WORKLOADS = {
     # Whole 128-expert layer on one GPU (EP=1), top-8.
     "ep1_128exp_bf16": Workload("ep1_128exp_bf16", T=16384, d=2048, F=768, E=128, e_lo=0,
                                 E_l=128, K=8, dtype="bf16", route="topk"),
+    # the forced-balance EP16 rank shapes in IEEE fp16 (the pages' other
+    # mixed-precision setting)
+    "ep16_rank_f16": Workload("ep16_rank_f16", T=4096, d=2048, F=768, E=8, e_lo=0,
+                              E_l=8, K=8, dtype="f16", route="force_balance"),
 }
 
 
@@ -81,10 +86,12 @@ def _normal(rng, shape, scale, chunk_rows=None):
 
 
 def _to_dtype(a: np.ndarray, dtype: str) -> np.ndarray:
-    """Round float32 values to the storage type (RNE for bf16) and return them as
-    float32 arrays holding exactly representable values."""
+    """Round float32 values to the storage type (RNE for bf16 and f16) and return
+    them as float32 arrays holding exactly representable values."""
     if dtype == "f32":
         return a
+    if dtype == "f16":
+        return a.astype(np.float16).astype(np.float32)
     import torch
 
     return torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
@@ -131,7 +138,7 @@ def to_device(arrays: dict, dtype: str, device="cuda"):
     bias in float32."""
     import torch
 
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(dtype, torch.float32)
     res = {}
     for k, v in arrays.items():
         if v is None:

@@ -25,7 +25,8 @@
  *  - Every call is asynchronous on the given stream and never synchronises the
  *    device.  Buffers must stay alive until that stream's work completes (the
  *    free-input hazard the 1F1B note reports under "TP=1 bug", page 2).
- *  - Activations ("data" tensors) are in shape->dtype (MOE_BF16 or MOE_F32).
+ *  - Activations ("data" tensors) are in shape->dtype (MOE_BF16, MOE_F16 or
+ *    MOE_F32).
  *    Logits, gates, gate gradients, logit gradients and weight gradients are
  *    always float32; indices and maps are int32.  Layouts are row-major.
  *  - Results are deterministic: the same inputs give bit-identical outputs,
@@ -47,7 +48,7 @@ extern "C" {
 #define MOE_OK               0
 #define MOE_ERR_NULL        -1   /* a required pointer is NULL                 */
 #define MOE_ERR_SHAPE       -2   /* a size is outside the supported range      */
-#define MOE_ERR_DTYPE       -3   /* dtype is not MOE_F32 / MOE_BF16            */
+#define MOE_ERR_DTYPE       -3   /* dtype is not MOE_F32 / MOE_BF16 / MOE_F16  */
 #define MOE_ERR_WORKSPACE   -4   /* workspace smaller than required            */
 #define MOE_ERR_HIP         -5   /* a HIP runtime call or launch failed        */
 #define MOE_ERR_UNSUPPORTED -6   /* mode / flag combination not supported      */
@@ -56,6 +57,9 @@ extern "C" {
 /* ---- data types ---------------------------------------------------------- */
 #define MOE_F32   0
 #define MOE_BF16  1
+#define MOE_F16   2   /* IEEE binary16 (the pages' other mixed precision, fp16
+                         next to bf16): same matrix-core path as bf16, with
+                         float32 accumulation and round-to-nearest-even stores */
 
 /* ---- routing modes ------------------------------------------------------- */
 /* Top-K over router logits = x . W_r (+ bias); gates = softmax over the K

@@ -22,7 +22,8 @@ Every function is numpy in float64.  Precision modes:
 * ``"f32"``  – outputs rounded to float32 (the fp32 configuration);
 * ``"bf16"`` – activation-sized outputs rounded to bfloat16 (round to nearest
   even) at the contract points; router logits, gates, gate gradients, logit
-  gradients and weight gradients are float32.
+  gradients and weight gradients are float32;
+* ``"f16"``  – the same with IEEE binary16 in place of bfloat16.
 
 Pinned by ``tests/test_oracle_pins.py`` (brute force, closed forms, invariants,
 finite differences, library routines) and the hand-worked fixture in
@@ -32,6 +33,7 @@ print no worked example for this layer.
 
 from .moe_oracle import (  # noqa: F401
     round_bf16,
+    round_f16,
     store,
     router_logits,
     topk_route,

@@ -16,7 +16,7 @@ from __future__ import annotations
 
 import numpy as np
 
-PRECISIONS = ("f64", "f32", "bf16")
+PRECISIONS = ("f64", "f32", "bf16", "f16")
 
 
 # ----------------------------------------------------------------------------
@@ -36,6 +36,24 @@ def round_bf16(a) -> np.ndarray:
     return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
+def round_f16(a) -> np.ndarray:
+    """Round to IEEE binary16 with round-to-nearest-even, returned as float64.
+
+    As for bfloat16, the value is first rounded to float32 (the accumulator),
+    then to the binary16 grid: with |v| = m * 2^e, 1 <= m < 2, the spacing of
+    binary16 values is 2^(e - 10) for normal numbers (e >= -14) and the fixed
+    2^-24 below, so v is divided by that spacing, rounded to the nearest
+    integer with ties to even, and scaled back.  Magnitudes that round to
+    2^16 or beyond overflow to infinity.
+    """
+    v = np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)
+    _, ex = np.frexp(v)                      # v = f * 2^ex, 0.5 <= |f| < 1
+    e = np.maximum(ex - 1, -14)
+    q = np.ldexp(1.0, e - 10)
+    r = np.rint(v / q) * q                   # rint: ties to even
+    return np.where(np.abs(r) >= 65536.0, np.copysign(np.inf, v), r)
+
+
 def round_f32(a) -> np.ndarray:
     return np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)
 
@@ -48,6 +66,8 @@ def store(v, prec: str) -> np.ndarray:
         return round_f32(v)
     if prec == "bf16":
         return round_bf16(v)
+    if prec == "f16":
+        return round_f16(v)
     raise ValueError(prec)
 
 

@@ -1,7 +1,8 @@
 """Shared helpers for the GPU parity tests: device transfer, the oracle reference
 for a workload, tolerance checks.  Parity bar: bit-exact for indices, counts,
 maps and the permuted copy; |gpu - ref| <= tau * max(1, |ref|) elementwise for
-floating point, tau = 2e-2 (bf16 data, float32 accumulation) or 1e-5 (float32)."""
+floating point, tau = 2e-2 (bf16 data, float32 accumulation), 4e-3 (fp16 data,
+float32 accumulation) or 1e-5 (float32)."""
 
 from __future__ import annotations
 
@@ -13,7 +14,7 @@ import torch
 import combine_expert_ffn_amd as M
 import oracle as O
 
-TAU = {"bf16": 2e-2, "f32": 1e-5}
+TAU = {"bf16": 2e-2, "f16": 4e-3, "f32": 1e-5}
 
 
 def log(msg):
@@ -22,18 +23,20 @@ def log(msg):
 
 
 def dev(a, dtype, device="cuda"):
-    """numpy -> device tensor; dtype 'bf16' | 'f32' | 'i32' | 'f32x' (float32 always)."""
+    """numpy -> device tensor; dtype 'bf16' | 'f16' | 'f32' | 'i32' | 'f32x' (float32 always)."""
     a = np.ascontiguousarray(a)
     if dtype == "i32":
         return torch.from_numpy(a.astype(np.int32)).to(device)
     if dtype in ("f32", "f32x"):
         return torch.from_numpy(a.astype(np.float32)).to(device)
+    if dtype == "f16":
+        return torch.from_numpy(a.astype(np.float32)).to(device=device, dtype=torch.float16)
     return torch.from_numpy(a.astype(np.float32)).to(device=device, dtype=torch.bfloat16)
 
 
 def host(t):
     """device tensor -> numpy (float64 for floating point, as-is for integers)."""
-    if t.dtype == torch.bfloat16:
+    if t.dtype in (torch.bfloat16, torch.float16):
         t = t.float()
     a = t.detach().cpu().numpy()
     return a.astype(np.float64) if a.dtype.kind == "f" else a

@@ -73,6 +73,16 @@ def test_shape_validation(kw, code):
     assert M.moe_workspace_bytes(s) == 0
 
 
+def test_all_three_dtypes_accepted():
+    for dt in ("f32", "bf16", "f16"):
+        s = _shape(dtype=dt)
+        assert M.moe_workspace_bytes(s) > 0, dt
+        # validation passes the shape and stops at the first NULL pointer
+        assert M.lib().moe_combine(C.byref(s), None, FAKE, FAKE, FAKE, None) == M.MOE_ERR_NULL
+    # the 16-bit types both need the transposed-weight workspace of the dgrad
+    assert M.moe_workspace_bytes(_shape(dtype="f16")) == M.moe_workspace_bytes(_shape(dtype="bf16"))
+
+
 def test_null_pointers_rejected():
     s = _shape()
     L = M.lib()

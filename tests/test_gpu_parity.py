@@ -44,6 +44,13 @@ SMALL = {
     # the largest supported FFN width
     "wide_ffn_bf16": Workload("wide_ffn_bf16", T=40, d=64, F=16384, E=2, e_lo=0, E_l=2, K=2,
                               dtype="bf16", route="topk"),
+    # IEEE fp16 data on the same matrix-core path (the pages' other precision)
+    "fb_ragged_f16": Workload("fb_ragged_f16", T=330, d=256, F=192, E=8, e_lo=0, E_l=8, K=8,
+                              dtype="f16", route="force_balance"),
+    "zipf_window_f16": Workload("zipf_window_f16", T=700, d=192, F=320, E=64, e_lo=0, E_l=8,
+                                K=6, dtype="f16", route="topk", zipf_s=1.1),
+    "mid_window_f16": Workload("mid_window_f16", T=150, d=64, F=64, E=16, e_lo=5, E_l=3, K=4,
+                               dtype="f16", route="topk"),
     # the largest router (E = 512, K = 16) with the largest window (256 experts)
     "max_router_bf16": Workload("max_router_bf16", T=200, d=128, F=64, E=512, e_lo=128,
                                 E_l=256, K=16, dtype="bf16", route="topk"),
@@ -64,11 +71,11 @@ def _pad(a, rows):
 
 
 def _tau(w):
-    """bf16: 2e-2.  float32: 1e-5 at the configured sizes; sequential float32
+    """bf16: 2e-2, fp16: 4e-3.  float32: 1e-5 at the configured sizes; sequential float32
     accumulation error grows like sqrt(reduction length) * eps, so reductions
     over d > 128 get 1e-5 * sqrt(d / 128)."""
-    if w.dtype == "bf16":
-        return TAU["bf16"]
+    if w.dtype in ("bf16", "f16"):
+        return TAU[w.dtype]
     return TAU["f32"] * max(1.0, (w.d / 128) ** 0.5)
 
 
@@ -240,7 +247,8 @@ def _layer_step(w, inp, flags=0, s_copy=None):
 
 @pytest.mark.parametrize("fused", [False, True], ids=["", "fused_permute"])
 @pytest.mark.parametrize("name", ["tiny_f32", "fb_ragged_bf16", "zipf_window_bf16",
-                                  "many_experts_bf16", "mid_window_bf16", "max_router_bf16"])
+                                  "many_experts_bf16", "mid_window_bf16", "max_router_bf16",
+                                  "fb_ragged_f16", "zipf_window_f16"])
 def test_chain_parity(name, fused):
     w = SMALL[name]
     log(f"[chain parity] {name}{' fused permute' if fused else ''}")

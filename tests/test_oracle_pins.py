@@ -112,6 +112,38 @@ def test_round_bf16_matches_torch_cast():
     assert np.array_equal(got.view(np.uint64), ref.view(np.uint64))
 
 
+def test_round_f16_matches_numpy_cast():
+    rng = np.random.default_rng(7)
+    v = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-9, 5, 20000),
+        np.array([0.0, 1.0, -1.0, 65504.0, -65504.0, 6.1e-5, 6.0e-8, 3.0e-8]),
+    ]).astype(np.float32)
+    # exact ties between neighbouring binary16 values, normal and subnormal
+    ties = np.array([1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 1024.5, 1025.5, 3 * 2.0 ** -25,
+                     5 * 2.0 ** -25, -(1 + 2.0 ** -11)], np.float32)
+    v = np.concatenate([v, ties])
+    ref = v.astype(np.float16).astype(np.float64)
+    got = O.round_f16(v)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("x,want", [
+    (1 + 2.0 ** -11, 1.0),                         # tie -> even mantissa (...0)
+    (1 + 3 * 2.0 ** -11, 1 + 2.0 ** -9),           # tie -> even mantissa (...10)
+    (1 + 2.0 ** -11 + 2.0 ** -20, 1 + 2.0 ** -10),  # just above the tie
+    (65504.0, 65504.0),                            # largest finite binary16
+    (65519.0, 65504.0),                            # below the overflow threshold
+    (65520.0, np.inf),                             # rounds to 2^16: overflow
+    (2.0 ** -24, 2.0 ** -24),                      # smallest subnormal
+    (2.0 ** -25, 0.0),                             # tie between 0 and 2^-24 -> 0
+    (3 * 2.0 ** -26, 2.0 ** -24),                  # above that tie
+    (2.0 ** -14 - 2.0 ** -25, 2.0 ** -14),         # subnormal tie -> even (2^-14)
+])
+def test_round_f16_closed_forms(x, want):
+    assert O.round_f16(np.array([x, -x]))[0] == want
+    assert O.round_f16(np.array([-x]))[0] == -want
+
+
 # ----------------------------------------------------------------------------
 # routing: brute force and closed forms
 # ----------------------------------------------------------------------------
