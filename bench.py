@@ -33,16 +33,19 @@ def err(*a):
 
 
 def algorithmic(w, N, T_loc):
-    """Per-launch algorithmic work: flops for the GEMMs, HBM bytes for the
-    permute kernels (one pass over each operand, no re-reads)."""
+    """Algorithmic work per step (one launch of each, plus the shared expert's
+    launches of the same GEMMs over all T tokens when the workload has one):
+    flops for the GEMMs, HBM bytes for the permute kernels (one pass over each
+    operand, no re-reads)."""
     d, F, T, K, E = w.d, w.F, w.T, w.K, w.E
     b = 4 if w.dtype == "f32" else 2
+    Fs = w.F_s
     return {
-        "ffn_gate_up": ("flop", 2.0 * N * d * 2 * F),
-        "ffn_down": ("flop", 2.0 * N * F * d),
-        "dgrad_act": ("flop", 2.0 * N * d * F),
-        "dgrad_in": ("flop", 2.0 * N * 2 * F * d),
-        "wgrad": ("flop", 6.0 * N * d * F),
+        "ffn_gate_up": ("flop", 2.0 * N * d * 2 * F + 2.0 * T * d * 2 * Fs),
+        "ffn_down": ("flop", 2.0 * N * F * d + 2.0 * T * Fs * d),
+        "dgrad_act": ("flop", 2.0 * N * d * F + 2.0 * T * d * Fs),
+        "dgrad_in": ("flop", 2.0 * N * 2 * F * d + 2.0 * T * 2 * Fs * d),
+        "wgrad": ("flop", 6.0 * N * d * F + 6.0 * T * d * Fs),
         "router": ("flop", 2.0 * T * d * E),
         # x rows of tokens with a local expert + row map -> N rows
         "permute": ("byte", T_loc * d * b + 4.0 * T * K + N * d * b),
@@ -192,19 +195,25 @@ def main():
     dW_gu = torch.zeros(w.E_l, 2 * w.F, w.d, dtype=torch.float32, device="cuda")
     dW_down = torch.zeros(w.E_l, w.d, w.F, dtype=torch.float32, device="cuda")
     dW_r = torch.zeros(w.d, w.E, dtype=torch.float32, device="cuda") if topk else None
-    ws = torch.empty(M.moe_step_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(M.moe_step_workspace_bytes_shared(s, w.F_s), dtype=torch.uint8,
+                     device="cuda")
     fused = args.fused_permute == "on"
     FUSED = M.MOE_STEP_FUSED_PERMUTE if fused else 0
+    shared = None
+    if w.F_s:  # a shared expert beside the routed ones
+        shared = (D(inp["W_gu_s"]), D(inp["W_down_s"]),
+                  torch.zeros(2 * w.F_s, w.d, dtype=torch.float32, device="cuda"),
+                  torch.zeros(w.d, w.F_s, dtype=torch.float32, device="cuda"))
     mbs = [M.MicroBatch(s, x=D(inp["x"]), dout=D(inp["dout"]),
-                        gates=None if topk else F32(inp["gates"]), fused=fused),
+                        gates=None if topk else F32(inp["gates"]), fused=fused, F_s=w.F_s),
            M.MicroBatch(s, x=D(inp["x_b"]), dout=D(inp["dout_b"]),
-                        gates=None if topk else F32(inp["gates_b"]), fused=fused)]
+                        gates=None if topk else F32(inp["gates_b"]), fused=fused, F_s=w.F_s)]
     s0 = torch.cuda.current_stream()
     s1 = torch.cuda.Stream()
 
     def step(fwd, bwd, flags):
         st = M.make_step(s, mode, W_gu, W_down, dW_gu, dW_down, ws, fwd=fwd, bwd=bwd, W_r=W_r,
-                         bias=bias, dW_r=dW_r, accumulate=M.MOE_ACCUM_DW)
+                         bias=bias, dW_r=dW_r, accumulate=M.MOE_ACCUM_DW, shared=shared)
         M.moe_overlap_step(st, s0, s1, flags | FUSED)
 
     def run_loop(n, flags, i0):
@@ -266,7 +275,7 @@ def main():
             for j in (i, i + 1):
                 st = M.make_step(s, mode, W_gu, W_down, dW_gu, dW_down, ws, fwd=mbs[(j + 1) % 2],
                                  bwd=mbs[j % 2], W_r=W_r, bias=bias, dW_r=dW_r,
-                                 accumulate=M.MOE_ACCUM_DW)
+                                 accumulate=M.MOE_ACCUM_DW, shared=shared)
                 M.moe_overlap_step(st, c0, s1, FUSED)
                 sts.append(st)
         i += 2
@@ -315,14 +324,15 @@ def main():
         avg_s = tot_ms / 1e3 / max(n, 1)
         ent = {"avg_us": round(avg_s * 1e6, 2), "launches_per_step": round(n / args.steps, 3),
                "ms_per_step": round(tot_ms / args.steps, 4)}
+        step_s = tot_ms / 1e3 / args.steps   # this kernel's time per step
         if name in work:
-            kind, amount = work[name]
+            kind, amount = work[name]      # per step
             if kind == "flop":
-                ach = amount / avg_s / 1e12
+                ach = amount / step_s / 1e12
                 ent.update(achieved=round(ach, 1), unit="TFLOP/s",
                            frac=round(ach / PEAK_BF16_TFLOPS, 4))
             else:
-                ach = amount / avg_s / 1e9
+                ach = amount / step_s / 1e9
                 ent.update(achieved=round(ach, 1), unit="GB/s", frac=round(ach / PEAK_HBM_GBS, 4))
         if name in traffic:
             ent["traffic"] = traffic[name]
@@ -332,13 +342,15 @@ def main():
     gemm = [k for k in GEMM_KERNELS if k in kern]
     dom = max(gemm, key=lambda k: kern[k][0])
     dom_avg_s = kern[dom][0] / 1e3 / kern[dom][1]
-    dom_ach = work[dom][1] / dom_avg_s / 1e12
-    gemm_flops = sum(work[k][1] * kern[k][1] for k in gemm)
+    dom_per_step = kern[dom][1] / args.steps
+    dom_ach = work[dom][1] / (dom_avg_s * dom_per_step) / 1e12
+    gemm_flops = sum(work[k][1] * args.steps for k in gemm)
     gemm_s = sum(kern[k][0] / 1e3 for k in gemm)
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(dom_ach, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dom_ach / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic.get(dom),
-                "algorithmic_per_launch": f"{work[dom][1]:.4g} flop",
+                "algorithmic_per_launch": f"{work[dom][1] / dom_per_step:.4g} flop",
+                "launches_per_step": round(dom_per_step, 3),
                 "avg_launch_us": round(dom_avg_s * 1e6, 2)}
     # the dispatch kernel; with the fused permute there is none (GEMM1 gathers x),
     # and the forward's remaining permute-class kernel, combine, is reported
@@ -368,7 +380,8 @@ def main():
                    "E_l": w.E_l, "K": w.K, "routing": w.route, "N_rows": N,
                    "step": "1F1B: forward of one micro-batch + backward of the other, "
                            "two streams, wgrad deferred", "launch": launch,
-                   "permute": "fused into GEMM1 and wgrad" if fused else "separate kernel"},
+                   "permute": "fused into GEMM1 and wgrad" if fused else "separate kernel",
+                   "shared_expert_F": w.F_s},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "grouped_gemm_mfma_util": round(gemm_flops / gemm_s / 1e12 / PEAK_BF16_TFLOPS, 4),

@@ -57,6 +57,35 @@ def moe_workspace_bytes(s: MoeShape) -> int:
     return lib().moe_workspace_bytes(C.byref(s))
 
 
+def moe_step_workspace_bytes_shared(s: MoeShape, F_s: int) -> int:
+    return lib().moe_step_workspace_bytes_shared(C.byref(s), int(F_s))
+
+
+def moe_shared_workspace_bytes(s: MoeShape, F_s: int) -> int:
+    return lib().moe_shared_workspace_bytes(C.byref(s), int(F_s))
+
+
+def moe_shared_expert_fwd(s, F_s, x, W_gu_s, W_down_s, h_s, a_s, y_s, ws, stream=None):
+    wp, wb = _ws(ws)
+    check(lib().moe_shared_expert_fwd(C.byref(s), int(F_s), _p(x), _p(W_gu_s), _p(W_down_s),
+                                      _p(h_s), _p(a_s), _p(y_s), wp, wb, _stream(stream)))
+
+
+def moe_shared_expert_dgrad(s, F_s, dout, h_s, W_gu_s, W_down_s, dh_s, dx_s, ws, stream=None):
+    wp, wb = _ws(ws)
+    check(lib().moe_shared_expert_dgrad(C.byref(s), int(F_s), _p(dout), _p(h_s), _p(W_gu_s),
+                                        _p(W_down_s), _p(dh_s), _p(dx_s), wp, wb,
+                                        _stream(stream)))
+
+
+def moe_shared_expert_wgrad(s, F_s, x, a_s, dh_s, dout, dW_gu_s, dW_down_s, accumulate, ws,
+                            stream=None):
+    wp, wb = _ws(ws)
+    check(lib().moe_shared_expert_wgrad(C.byref(s), int(F_s), _p(x), _p(a_s), _p(dh_s),
+                                        _p(dout), _p(dW_gu_s), _p(dW_down_s), int(accumulate),
+                                        wp, wb, _stream(stream)))
+
+
 def moe_step_workspace_bytes(s: MoeShape) -> int:
     return lib().moe_step_workspace_bytes(C.byref(s))
 
@@ -173,10 +202,11 @@ def moe_timing_report() -> dict:
 # ---------------------------------------------------------------------------
 class MicroBatch:
     """Device buffers of one micro-batch for shape ``s`` (sizes per include/moe.h).
-    With ``fused=True`` (steps run with MOE_STEP_FUSED_PERMUTE) no xp is allocated."""
+    With ``fused=True`` (steps run with MOE_STEP_FUSED_PERMUTE) no xp is allocated;
+    with ``F_s > 0`` the shared expert's buffers are allocated too."""
 
     def __init__(self, s: MoeShape, device="cuda", x=None, dout=None, gates=None, logits=None,
-                 fused=False):
+                 fused=False, F_s=0):
         import numpy as np
         import torch
 
@@ -208,14 +238,21 @@ class MicroBatch:
         self.dh = e(cap, 2 * F)
         self.dxp = e(cap, d)
         self.dx = e(T, d)
+        Fs = int(F_s)
+        self.h_s = e(T, 2 * Fs) if Fs else None
+        self.a_s = e(T, Fs) if Fs else None
+        self.y_s = e(T, d) if Fs else None
+        self.dh_s = e(T, 2 * Fs) if Fs else None
+        self.dx_s = e(T, d) if Fs else None
 
     def struct(self) -> MoeMB:
         return MoeMB(*[_p(getattr(self, n)) for n in MB_FIELDS])
 
 
 def make_step(s: MoeShape, route_mode, W_gu, W_down, dW_gu, dW_down, ws, fwd=None, bwd=None,
-              W_r=None, bias=None, dW_r=None, accumulate=0):
-    """Build a MoeStep; the returned object keeps the micro-batch structs alive."""
+              W_r=None, bias=None, dW_r=None, accumulate=0, shared=None):
+    """Build a MoeStep; the returned object keeps the micro-batch structs alive.
+    ``shared`` = (W_gu_s, W_down_s, dW_gu_s, dW_down_s) adds a shared expert."""
     fs = fwd.struct() if fwd is not None else None
     bs = bwd.struct() if bwd is not None else None
     st = MoeStep(s, int(route_mode), int(accumulate), _p(W_r), _p(bias), _p(W_gu), _p(W_down),
@@ -223,5 +260,10 @@ def make_step(s: MoeShape, route_mode, W_gu, W_down, dW_gu, dW_down, ws, fwd=Non
                  C.pointer(fs) if fs is not None else None,
                  C.pointer(bs) if bs is not None else None,
                  ws.data_ptr(), ws.numel() * ws.element_size())
+    if shared is not None:
+        W_gu_s, W_down_s, dW_gu_s, dW_down_s = shared
+        st.F_s = int(W_down_s.shape[1])
+        st.W_gu_s, st.W_down_s = _p(W_gu_s), _p(W_down_s)
+        st.dW_gu_s, st.dW_down_s = _p(dW_gu_s), _p(dW_down_s)
     st._keep = (fs, bs)
     return st

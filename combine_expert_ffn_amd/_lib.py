@@ -44,7 +44,8 @@ class MoeShape(C.Structure):
 
 MB_FIELDS = ["x", "logits", "idx", "gates", "counts", "offsets", "row_of_pair",
              "pair_of_row", "tile_offsets", "xp", "h", "a", "yp", "out",
-             "dout", "dyp", "dgates", "dlogits", "dh", "dxp", "dx"]
+             "dout", "dyp", "dgates", "dlogits", "dh", "dxp", "dx",
+             "h_s", "a_s", "y_s", "dh_s", "dx_s"]
 
 
 class MoeMB(C.Structure):
@@ -56,7 +57,9 @@ class MoeStep(C.Structure):
                 ("W_r", C.c_void_p), ("bias", C.c_void_p), ("W_gu", C.c_void_p),
                 ("W_down", C.c_void_p), ("dW_r", C.c_void_p), ("dW_gu", C.c_void_p),
                 ("dW_down", C.c_void_p), ("fwd", C.POINTER(MoeMB)), ("bwd", C.POINTER(MoeMB)),
-                ("ws", C.c_void_p), ("ws_bytes", C.c_size_t)]
+                ("ws", C.c_void_p), ("ws_bytes", C.c_size_t),
+                ("F_s", C.c_int64), ("W_gu_s", C.c_void_p), ("W_down_s", C.c_void_p),
+                ("dW_gu_s", C.c_void_p), ("dW_down_s", C.c_void_p)]
 
 
 _P = C.c_void_p
@@ -64,6 +67,14 @@ _SP = C.POINTER(MoeShape)
 SIGNATURES = {
     "moe_workspace_bytes": (C.c_size_t, [_SP]),
     "moe_step_workspace_bytes": (C.c_size_t, [_SP]),
+    "moe_step_workspace_bytes_shared": (C.c_size_t, [_SP, C.c_int64]),
+    "moe_shared_workspace_bytes": (C.c_size_t, [_SP, C.c_int64]),
+    "moe_shared_expert_fwd": (C.c_int, [_SP, C.c_int64, _P, _P, _P, _P, _P, _P, _P, C.c_size_t,
+                                        _P]),
+    "moe_shared_expert_dgrad": (C.c_int, [_SP, C.c_int64, _P, _P, _P, _P, _P, _P, _P,
+                                          C.c_size_t, _P]),
+    "moe_shared_expert_wgrad": (C.c_int, [_SP, C.c_int64, _P, _P, _P, _P, _P, _P, C.c_int, _P,
+                                          C.c_size_t, _P]),
     "moe_tile_m": (C.c_int, []),
     "moe_last_error": (C.c_char_p, []),
     "moe_version": (C.c_int, []),

@@ -125,6 +125,58 @@ static int do_dispatch(const moe_shape* s, const void* x, const int32_t* idx, in
   return launch_permute(s, x, row_of_pair, xp, st);
 }
 
+// The shared expert as a grouped-GEMM shape: one expert over all T rows.
+static moe_shape shared_shape(const moe_shape* s, int64_t F_s) {
+  moe_shape ss = *s;
+  ss.F = F_s;
+  ss.E = 1;
+  ss.e_lo = 0;
+  ss.E_l = 1;
+  ss.K = 1;
+  return ss;
+}
+static int validate_shared(int64_t F_s) {
+  if (F_s < 64 || F_s > 16384 || F_s % 64)
+    return set_error(MOE_ERR_SHAPE, "F_s = %lld must be a multiple of 64 in [64, 16384]",
+                     (long long)F_s);
+  return MOE_OK;
+}
+// Shared-expert workspace: its 4-entry plan in the first 256 bytes, then the
+// layout of a grouped call on the shared shape (the dgrad's weight copies).
+constexpr size_t kSharedPlanBytes = 256;
+static size_t ws_shared(const moe_shape* s, int64_t F_s) {
+  const moe_shape ss = shared_shape(s, F_s);
+  return kSharedPlanBytes + ws_wT_offset(&ss) + ws_wT_bytes(&ss);
+}
+static int do_shared_fwd(const moe_shape* s, int64_t F_s, const void* x, const void* W_gu_s,
+                         const void* W_down_s, void* h_s, void* a_s, void* y_s, void* ws,
+                         hipStream_t st) {
+  if (s->T == 0) return MOE_OK;
+  const moe_shape ss = shared_shape(s, F_s);
+  int32_t* plan = (int32_t*)ws;
+  if (int rc = launch_shared_plan(s->T, plan, st)) return rc;
+  return launch_ffn_fwd(&ss, x, nullptr, plan, plan + 2, W_gu_s, W_down_s, h_s, a_s, y_s, st);
+}
+static int do_shared_dgrad(const moe_shape* s, int64_t F_s, const void* dout, const void* h_s,
+                           const void* W_gu_s, const void* W_down_s, void* dh_s, void* dx_s,
+                           void* ws, hipStream_t st) {
+  if (s->T == 0) return MOE_OK;
+  const moe_shape ss = shared_shape(s, F_s);
+  int32_t* plan = (int32_t*)ws;
+  if (int rc = launch_shared_plan(s->T, plan, st)) return rc;
+  return launch_ffn_dgrad(&ss, dout, h_s, plan, plan + 2, W_gu_s, W_down_s, dh_s, dx_s,
+                          (char*)ws + kSharedPlanBytes, false, st);
+}
+static int do_shared_wgrad(const moe_shape* s, int64_t F_s, const void* x, const void* a_s,
+                           const void* dh_s, const void* dout, float* dW_gu_s, float* dW_down_s,
+                           bool accumulate, void* ws, hipStream_t st) {
+  const moe_shape ss = shared_shape(s, F_s);
+  int32_t* plan = (int32_t*)ws;
+  if (int rc = launch_shared_plan(s->T, plan, st)) return rc;
+  return launch_ffn_wgrad(&ss, x, nullptr, a_s, dh_s, dout, plan, dW_gu_s, dW_down_s, accumulate,
+                          st);
+}
+
 // The fused permute addresses x with 32-bit byte offsets.
 static int check_gather_x(const moe_shape* s, const char* fn) {
   const int64_t es = (int64_t)elt_bytes(s);
@@ -136,12 +188,12 @@ static int check_gather_x(const moe_shape* s, const char* fn) {
 
 static int do_dispatch_bwd(const moe_shape* s, const void* dxp, const int32_t* row_of_pair,
                            const int32_t* idx, const float* dlogits, const void* W_r, void* dx,
-                           bool accumulate, void* ws, hipStream_t st) {
+                           bool accumulate, void* ws, hipStream_t st, const void* add = nullptr) {
   if (dlogits && s->T > 0) {
     int rc = launch_transpose_wr(s, W_r, ws, st);
     if (rc) return rc;
   }
-  return launch_dispatch_bwd(s, dxp, row_of_pair, idx, dlogits, ws, dx, accumulate, st);
+  return launch_dispatch_bwd(s, dxp, row_of_pair, idx, dlogits, ws, add, dx, accumulate, st);
 }
 
 }  // namespace moe
@@ -158,6 +210,18 @@ size_t moe_workspace_bytes(const moe_shape* s) {
 size_t moe_step_workspace_bytes(const moe_shape* s) {
   if (validate_shape(s)) return 0;
   return 2 * ws_one(s);
+}
+
+size_t moe_shared_workspace_bytes(const moe_shape* s, int64_t F_s) {
+  if (validate_shape(s) || validate_shared(F_s)) return 0;
+  return ws_shared(s, F_s);
+}
+
+size_t moe_step_workspace_bytes_shared(const moe_shape* s, int64_t F_s) {
+  if (validate_shape(s)) return 0;
+  if (F_s == 0) return 2 * ws_one(s);
+  if (validate_shared(F_s)) return 0;
+  return 2 * ws_one(s) + 2 * ws_shared(s, F_s);
 }
 
 int moe_tile_m(void) { return kTileM; }
@@ -312,7 +376,7 @@ int moe_combine(const moe_shape* s, const void* yp, const float* gates,
   REQUIRE(gates);
   REQUIRE(row_of_pair);
   REQUIRE(out);
-  return launch_combine(s, yp, gates, row_of_pair, out, stream);
+  return launch_combine(s, yp, gates, row_of_pair, nullptr, out, stream);
 }
 
 int moe_combine_bwd(const moe_shape* s, const void* dout, const void* yp, const float* gates,
@@ -388,6 +452,62 @@ int moe_ffn_wgrad_gather(const moe_shape* s, const void* x, const int32_t* pair_
                           (accumulate & MOE_ACCUM_DW) != 0, stream);
 }
 
+int moe_shared_expert_fwd(const moe_shape* s, int64_t F_s, const void* x, const void* W_gu_s,
+                          const void* W_down_s, void* h_s, void* a_s, void* y_s, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  if (int rc = validate_shape(s)) return rc;
+  if (int rc = validate_shared(F_s)) return rc;
+  REQUIRE(x);
+  REQUIRE(W_gu_s);
+  REQUIRE(W_down_s);
+  REQUIRE(h_s);
+  REQUIRE(a_s);
+  REQUIRE(y_s);
+  REQUIRE(ws);
+  if (int rc = need_ws(__func__, ws_bytes, ws_shared(s, F_s))) return rc;
+  return do_shared_fwd(s, F_s, x, W_gu_s, W_down_s, h_s, a_s, y_s, ws, stream);
+}
+
+int moe_shared_expert_dgrad(const moe_shape* s, int64_t F_s, const void* dout, const void* h_s,
+                            const void* W_gu_s, const void* W_down_s, void* dh_s, void* dx_s,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  if (int rc = validate_shape(s)) return rc;
+  if (int rc = validate_shared(F_s)) return rc;
+  REQUIRE(dout);
+  REQUIRE(h_s);
+  REQUIRE(W_gu_s);
+  REQUIRE(W_down_s);
+  REQUIRE(dh_s);
+  REQUIRE(dx_s);
+  REQUIRE(ws);
+  if (int rc = need_ws(__func__, ws_bytes, ws_shared(s, F_s))) return rc;
+  return do_shared_dgrad(s, F_s, dout, h_s, W_gu_s, W_down_s, dh_s, dx_s, ws, stream);
+}
+
+int moe_shared_expert_wgrad(const moe_shape* s, int64_t F_s, const void* x, const void* a_s,
+                            const void* dh_s, const void* dout, float* dW_gu_s,
+                            float* dW_down_s, int accumulate, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  g_err[0] = 0;
+  if (int rc = validate_shape(s)) return rc;
+  if (int rc = validate_shared(F_s)) return rc;
+  REQUIRE(x);
+  REQUIRE(a_s);
+  REQUIRE(dh_s);
+  REQUIRE(dout);
+  REQUIRE(dW_gu_s);
+  REQUIRE(dW_down_s);
+  REQUIRE(ws);
+  if (accumulate & ~(MOE_ACCUM_DX | MOE_ACCUM_DW))
+    return set_error(MOE_ERR_ARG, "moe_shared_expert_wgrad: unknown accumulate bits 0x%x",
+                     accumulate);
+  if (int rc = need_ws(__func__, ws_bytes, ws_shared(s, F_s))) return rc;
+  return do_shared_wgrad(s, F_s, x, a_s, dh_s, dout, dW_gu_s, dW_down_s,
+                         (accumulate & MOE_ACCUM_DW) != 0, ws, stream);
+}
+
 int moe_route_bwd(const moe_shape* s, int mode, const float* dgates, const float* gates,
                   const int32_t* idx, const void* x, float* dlogits, float* dW_r, int accumulate,
                   void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -441,7 +561,7 @@ int moe_dispatch_bwd(const moe_shape* s, const void* dxp, const int32_t* row_of_
 namespace moe {
 
 struct StepEvents {
-  hipEvent_t start, cb, route, dgrad, disp, fwd, end;
+  hipEvent_t start, shared_a, shared_b, end;
 };
 
 // One event set per (host thread, device); events are only recorded and waited
@@ -453,7 +573,7 @@ static int step_events(StepEvents** out) {
   if ((int)sets.size() <= dev) sets.resize(dev + 1, nullptr);
   if (!sets[dev]) {
     StepEvents* e = new StepEvents();
-    hipEvent_t* all[] = {&e->start, &e->cb, &e->route, &e->dgrad, &e->disp, &e->fwd, &e->end};
+    hipEvent_t* all[] = {&e->start, &e->shared_a, &e->shared_b, &e->end};
     for (hipEvent_t* p : all)
       if (hipEventCreateWithFlags(p, hipEventDisableTiming) != hipSuccess)
         return set_error(MOE_ERR_HIP, "hipEventCreateWithFlags failed");
@@ -522,6 +642,8 @@ struct StepCtx {
   void* wsB;
   bool router;  // TOPK mode: router weights are differentiated
   bool fused;   // fused permute: no xp, GEMM1 / wgrad gather from x
+  void* wsSA;   // shared-expert workspace of the forward micro-batch
+  void* wsSB;   // and of the backward one
 };
 
 static int fwd_route(const StepCtx& c, const moe_mb* A, hipStream_t q) {
@@ -537,8 +659,22 @@ static int fwd_ffn(const StepCtx& c, const moe_mb* A, hipStream_t q) {
                         A->offsets, A->tile_offsets, c.st->W_gu, c.st->W_down, A->h, A->a,
                         A->yp, q);
 }
+static bool has_shared(const StepCtx& c) { return c.st->F_s > 0; }
 static int fwd_combine(const StepCtx& c, const moe_mb* A, hipStream_t q) {
-  return launch_combine(c.s, A->yp, A->gates, A->row_of_pair, A->out, q);
+  return launch_combine(c.s, A->yp, A->gates, A->row_of_pair, has_shared(c) ? A->y_s : nullptr,
+                        A->out, q);
+}
+static int fwd_shared(const StepCtx& c, const moe_mb* A, hipStream_t q) {
+  return do_shared_fwd(c.s, c.st->F_s, A->x, c.st->W_gu_s, c.st->W_down_s, A->h_s, A->a_s,
+                       A->y_s, c.wsSA, q);
+}
+static int bwd_shared_dgrad(const StepCtx& c, const moe_mb* B, hipStream_t q) {
+  return do_shared_dgrad(c.s, c.st->F_s, B->dout, B->h_s, c.st->W_gu_s, c.st->W_down_s, B->dh_s,
+                         B->dx_s, c.wsSB, q);
+}
+static int bwd_shared_wgrad(const StepCtx& c, const moe_mb* B, hipStream_t q) {
+  return do_shared_wgrad(c.s, c.st->F_s, B->x, B->a_s, B->dh_s, B->dout, c.st->dW_gu_s,
+                         c.st->dW_down_s, (c.st->accumulate & MOE_ACCUM_DW) != 0, c.wsSB, q);
 }
 static int bwd_combine(const StepCtx& c, const moe_mb* B, hipStream_t q) {
   return launch_combine_bwd(c.s, B->dout, B->yp, B->gates, B->row_of_pair, B->dyp, B->dgates, q);
@@ -550,16 +686,14 @@ static int bwd_route(const StepCtx& c, const moe_mb* B, hipStream_t q) {
                           with_dw ? c.st->dW_r : nullptr,
                           (c.st->accumulate & MOE_ACCUM_DW) != 0, c.wsB, q);
 }
-static int bwd_dgrad_weights(const StepCtx& c, hipStream_t q) {
-  return launch_dgrad_weights(c.s, c.st->W_gu, c.st->W_down, c.wsB, q);
-}
 static int bwd_dgrad(const StepCtx& c, const moe_mb* B, bool weights_ready, hipStream_t q) {
   return launch_ffn_dgrad(c.s, B->dyp, B->h, B->offsets, B->tile_offsets, c.st->W_gu,
                           c.st->W_down, B->dh, B->dxp, c.wsB, weights_ready, q);
 }
 static int bwd_dispatch(const StepCtx& c, const moe_mb* B, hipStream_t q) {
   return do_dispatch_bwd(c.s, B->dxp, B->row_of_pair, B->idx, c.router ? B->dlogits : nullptr,
-                         c.st->W_r, B->dx, false, c.wsB, q);
+                         c.st->W_r, B->dx, false, c.wsB, q,
+                         has_shared(c) ? B->dx_s : nullptr);
 }
 static int bwd_wgrad(const StepCtx& c, const moe_mb* B, hipStream_t q) {
   return launch_ffn_wgrad(c.s, c.fused ? B->x : B->xp, c.fused ? B->pair_of_row : nullptr,
@@ -600,19 +734,48 @@ extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t 
   }
   if (A && B && A == B)
     return set_error(MOE_ERR_ARG, "moe_overlap_step: fwd and bwd micro-batches must differ");
+  const bool shared = st->F_s != 0;
+  if (shared) {
+    TRY(validate_shared(st->F_s));
+    REQUIRE(st->W_gu_s);
+    REQUIRE(st->W_down_s);
+    if (A) {
+      REQUIRE(A->h_s);
+      REQUIRE(A->a_s);
+      REQUIRE(A->y_s);
+    }
+    if (B) {
+      REQUIRE(B->x);
+      REQUIRE(B->h_s);
+      REQUIRE(B->a_s);
+      REQUIRE(B->dh_s);
+      REQUIRE(B->dx_s);
+      REQUIRE(st->dW_gu_s);
+      REQUIRE(st->dW_down_s);
+    }
+  }
   REQUIRE(st->ws);
   const size_t one = ws_one(s);
-  if (int rc = need_ws(__func__, st->ws_bytes, 2 * one)) return rc;
+  const size_t sh = shared ? ws_shared(s, st->F_s) : 0;
+  if (int rc = need_ws(__func__, st->ws_bytes, 2 * one + 2 * sh)) return rc;
 
-  StepCtx c{st, s, st->ws, (char*)st->ws + one, mode == MOE_ROUTE_TOPK, fused};
+  StepCtx c{st, s, st->ws, (char*)st->ws + one, mode == MOE_ROUTE_TOPK, fused,
+            (char*)st->ws + 2 * one, (char*)st->ws + 2 * one + sh};
   const bool serial = (flags & MOE_STEP_SERIALIZE) || s0 == s1;
   const bool eager = (flags & MOE_STEP_EAGER_WGRAD) != 0;
   const bool skip_w = (flags & MOE_STEP_SKIP_WGRAD) != 0;
   if (eager && skip_w)
     return set_error(MOE_ERR_ARG, "moe_overlap_step: EAGER_WGRAD and SKIP_WGRAD exclude each other");
 
+  // B's weight gradients: the routed experts', then the shared expert's
+  auto wgrads = [&](hipStream_t q) -> int {
+    TRY(bwd_wgrad(c, B, q));
+    if (shared) TRY(bwd_shared_wgrad(c, B, q));
+    return MOE_OK;
+  };
   if (serial) {  // the forward-then-backward order of a non-overlapped layer
     if (A) {
+      if (shared) TRY(fwd_shared(c, A, s0));
       TRY(fwd_route(c, A, s0));
       TRY(fwd_dispatch(c, A, s0));
       TRY(fwd_ffn(c, A, s0));
@@ -622,9 +785,10 @@ extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t 
       TRY(bwd_combine(c, B, s0));
       TRY(bwd_route(c, B, s0));
       TRY(bwd_dgrad(c, B, false, s0));
-      if (eager) TRY(bwd_wgrad(c, B, s0));
+      if (shared) TRY(bwd_shared_dgrad(c, B, s0));
+      if (eager) TRY(wgrads(s0));
       TRY(bwd_dispatch(c, B, s0));
-      if (!eager && !skip_w) TRY(bwd_wgrad(c, B, s0));
+      if (!eager && !skip_w) TRY(wgrads(s0));
     }
     return MOE_OK;
   }
@@ -637,19 +801,32 @@ extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t 
   // The micro-batches share no buffers (each has its own half of the
   // workspace), so each runs in order on its own stream and the hardware
   // interleaves the two streams' kernels.
+  // A shared expert runs on the stream of the other micro-batch: A's shared
+  // forward at the head of s0, B's shared D at the head of s1, each joined
+  // where its output is summed in (A's combine, B's dispatch backward).
+  if (shared && A) {
+    TRY(fwd_shared(c, A, s0));
+    HIPTRY(hipEventRecord(ev->shared_a, s0));
+  }
+  if (shared && B) {
+    TRY(bwd_shared_dgrad(c, B, s1));
+    HIPTRY(hipEventRecord(ev->shared_b, s1));
+  }
   if (A) {  // the forward micro-batch, start to end on s1
     TRY(fwd_route(c, A, s1));
     TRY(fwd_dispatch(c, A, s1));
     TRY(fwd_ffn(c, A, s1));
+    if (shared) HIPTRY(hipStreamWaitEvent(s1, ev->shared_a, 0));
     TRY(fwd_combine(c, A, s1));
   }
   if (B) {  // the backward micro-batch on s0
     TRY(bwd_combine(c, B, s0));
     TRY(bwd_route(c, B, s0));
     TRY(bwd_dgrad(c, B, false, s0));
-    if (eager) TRY(bwd_wgrad(c, B, s0));
+    if (shared) HIPTRY(hipStreamWaitEvent(s0, ev->shared_b, 0));
+    if (eager) TRY(wgrads(s0));
     TRY(bwd_dispatch(c, B, s0));
-    if (!eager && !skip_w) TRY(bwd_wgrad(c, B, s0));
+    if (!eager && !skip_w) TRY(wgrads(s0));
   }
   // s0 ends after everything the step issued on s1
   HIPTRY(hipEventRecord(ev->end, s1));

@@ -157,6 +157,22 @@ __global__ __launch_bounds__(256) void plan_rank_kernel(const int32_t* __restric
   for (long r = r0 + tid; r < min(npairs, p0 + (long)kPlanChunk); r += 256) pair_of_row[r] = -1;
 }
 
+// The dispatch plan of the shared expert: one expert over all T rows in token
+// order: offsets {0, T}, tile_offsets {0, ceil(T / kTileM)}.
+__global__ void shared_plan_kernel(int32_t* __restrict__ plan, int T_) {
+  if (threadIdx.x == 0) {
+    plan[0] = 0;
+    plan[1] = T_;
+    plan[2] = 0;
+    plan[3] = (T_ + kTileM - 1) / kTileM;
+  }
+}
+
+int launch_shared_plan(int64_t T, int32_t* plan, hipStream_t st) {
+  MOE_LAUNCH("shared_plan", st, shared_plan_kernel<<<1, 64, 0, st>>>(plan, (int)T));
+  return check_launch("shared plan");
+}
+
 int launch_plan(const moe_shape* s, const int32_t* idx, int32_t* counts, int32_t* offsets,
                 int32_t* row_of_pair, int32_t* pair_of_row, int32_t* tile_offsets, void* ws,
                 hipStream_t st) {
@@ -274,13 +290,15 @@ int launch_permute(const moe_shape* s, const void* x, const int32_t* row_of_pair
 }
 
 // ---------------------------------------------------------------------------
-// combine: out[t] = sum_k gates[t,k] * yp[row(t,k)] over local k ascending,
-// float32 accumulation, one rounding.  One wave per token.
+// combine: out[t] = [add[t] +] sum_k gates[t,k] * yp[row(t,k)] over local k
+// ascending, float32 accumulation, one rounding.  add (nullable) is a
+// token-aligned term such as the shared expert's output.  One wave per token.
 // ---------------------------------------------------------------------------
 template <typename T, int MAXC>
 __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ yp,
                                                       const float* __restrict__ gates,
                                                       const int32_t* __restrict__ row_of_pair,
+                                                      const uint4* __restrict__ add,
                                                       uint4* __restrict__ out, int T_, int K,
                                                       int nch) {
   constexpr int CN = Chunk<T>::N;
@@ -298,9 +316,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
     }
     float acc[MAXC][CN];
 #pragma unroll
-    for (int i = 0; i < MAXC; ++i)
+    for (int i = 0; i < MAXC; ++i) {
+      if (add) {  // uniform
+        Chunk<T>::unpack(add[(size_t)t * nch + cc[i]], acc[i]);
+      } else {
 #pragma unroll
-      for (int q = 0; q < CN; ++q) acc[i][q] = 0.f;
+        for (int q = 0; q < CN; ++q) acc[i][q] = 0.f;
+      }
+    }
     // two rows per pass: both rows' loads are issued before the first FMA;
     // the sum still runs over the rows in ascending slot order
     LocalRows lr = lr0;
@@ -349,19 +372,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
 
 template <typename T>
 static void combine_t(const moe_shape* s, const void* yp, const float* gates,
-                      const int32_t* row_of_pair, void* out, hipStream_t st) {
+                      const int32_t* row_of_pair, const void* add, void* out, hipStream_t st) {
   MOE_LAUNCH("combine", st,
              combine_kernel<T, 4><<<(unsigned)cdiv(s->T, 4), 256, 0, st>>>(
-                 (const uint4*)yp, gates, row_of_pair, (uint4*)out, (int)s->T, (int)s->K,
-                 row_chunks(s)));
+                 (const uint4*)yp, gates, row_of_pair, (const uint4*)add, (uint4*)out, (int)s->T,
+                 (int)s->K, row_chunks(s)));
 }
 
 int launch_combine(const moe_shape* s, const void* yp, const float* gates,
-                   const int32_t* row_of_pair, void* out, hipStream_t st) {
+                   const int32_t* row_of_pair, const void* add, void* out, hipStream_t st) {
   if (s->T == 0) return MOE_OK;
-  if (s->dtype == MOE_BF16) combine_t<uint16_t>(s, yp, gates, row_of_pair, out, st);
-  else if (s->dtype == MOE_F16) combine_t<_Float16>(s, yp, gates, row_of_pair, out, st);
-  else combine_t<float>(s, yp, gates, row_of_pair, out, st);
+  if (s->dtype == MOE_BF16) combine_t<uint16_t>(s, yp, gates, row_of_pair, add, out, st);
+  else if (s->dtype == MOE_F16) combine_t<_Float16>(s, yp, gates, row_of_pair, add, out, st);
+  else combine_t<float>(s, yp, gates, row_of_pair, add, out, st);
   return check_launch("combine");
 }
 
@@ -484,7 +507,7 @@ int launch_combine_bwd(const moe_shape* s, const void* dout, const void* yp, con
 }
 
 // ---------------------------------------------------------------------------
-// dispatch backward: dx[t] = [dx[t]] + sum_k dxp[row(t,k)]
+// dispatch backward: dx[t] = [dx[t]] + [add[t]] + sum_k dxp[row(t,k)]
 //                            [+ sum_k dlogits[t, e_k] * W_rT[e_k]]   (e_k = idx[t,k])
 // float32 accumulation, one rounding.  One wave per token.
 // ---------------------------------------------------------------------------
@@ -492,8 +515,8 @@ template <typename T, int MAXC>
 __global__ __launch_bounds__(256) void dispatch_bwd_kernel(
     const uint4* __restrict__ dxp, const int32_t* __restrict__ row_of_pair,
     const int32_t* __restrict__ idx, const float* __restrict__ dlogits,
-    const uint4* __restrict__ W_rT, uint4* __restrict__ dx, int T_, int K, int E, int nch,
-    int accumulate) {
+    const uint4* __restrict__ W_rT, const uint4* __restrict__ add, uint4* __restrict__ dx,
+    int T_, int K, int E, int nch, int accumulate) {
   constexpr int CN = Chunk<T>::N;
   const int t = uniform_token((int)(((long)blockIdx.x * 256 + threadIdx.x) >> 6));
   const int lane = threadIdx.x & 63;
@@ -515,6 +538,12 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(
       } else {
 #pragma unroll
         for (int q = 0; q < CN; ++q) acc[i][q] = 0.f;
+      }
+      if (add) {  // uniform: a token-aligned term (the shared expert's input gradient)
+        float f[CN];
+        Chunk<T>::unpack(add[(size_t)t * nch + cc[i]], f);
+#pragma unroll
+        for (int q = 0; q < CN; ++q) acc[i][q] += f[q];
       }
     }
     // two rows per pass, summed in ascending slot order
@@ -580,24 +609,25 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(
 
 template <typename T>
 static void dispatch_bwd_t(const moe_shape* s, const void* dxp, const int32_t* row_of_pair,
-                           const int32_t* idx, const float* dlogits, const void* W_rT, void* dx,
-                           bool accumulate, hipStream_t st) {
+                           const int32_t* idx, const float* dlogits, const void* W_rT,
+                           const void* add, void* dx, bool accumulate, hipStream_t st) {
   MOE_LAUNCH("dispatch_bwd", st,
              dispatch_bwd_kernel<T, 4><<<(unsigned)cdiv(s->T, 4), 256, 0, st>>>(
-                 (const uint4*)dxp, row_of_pair, idx, dlogits, (const uint4*)W_rT, (uint4*)dx,
-                 (int)s->T, (int)s->K, (int)s->E, row_chunks(s), accumulate ? 1 : 0));
+                 (const uint4*)dxp, row_of_pair, idx, dlogits, (const uint4*)W_rT,
+                 (const uint4*)add, (uint4*)dx, (int)s->T, (int)s->K, (int)s->E, row_chunks(s),
+                 accumulate ? 1 : 0));
 }
 
 int launch_dispatch_bwd(const moe_shape* s, const void* dxp, const int32_t* row_of_pair,
-                        const int32_t* idx, const float* dlogits, const void* W_rT, void* dx,
-                        bool accumulate, hipStream_t st) {
+                        const int32_t* idx, const float* dlogits, const void* W_rT,
+                        const void* add, void* dx, bool accumulate, hipStream_t st) {
   if (s->T == 0) return MOE_OK;
   if (s->dtype == MOE_BF16)
-    dispatch_bwd_t<uint16_t>(s, dxp, row_of_pair, idx, dlogits, W_rT, dx, accumulate, st);
+    dispatch_bwd_t<uint16_t>(s, dxp, row_of_pair, idx, dlogits, W_rT, add, dx, accumulate, st);
   else if (s->dtype == MOE_F16)
-    dispatch_bwd_t<_Float16>(s, dxp, row_of_pair, idx, dlogits, W_rT, dx, accumulate, st);
+    dispatch_bwd_t<_Float16>(s, dxp, row_of_pair, idx, dlogits, W_rT, add, dx, accumulate, st);
   else
-    dispatch_bwd_t<float>(s, dxp, row_of_pair, idx, dlogits, W_rT, dx, accumulate, st);
+    dispatch_bwd_t<float>(s, dxp, row_of_pair, idx, dlogits, W_rT, add, dx, accumulate, st);
   return check_launch("dispatch bwd");
 }
 

@@ -193,13 +193,17 @@ int launch_plan(const moe_shape* s, const int32_t* idx, int32_t* counts, int32_t
                 hipStream_t st);
 int launch_permute(const moe_shape* s, const void* x, const int32_t* row_of_pair, void* xp,
                    hipStream_t st);
+// writes the shared expert's plan: plan[0..1] = offsets {0, T}, plan[2..3] =
+// tile_offsets {0, ceil(T / kTileM)}
+int launch_shared_plan(int64_t T, int32_t* plan, hipStream_t st);
+// add (nullable): a token-aligned [T][d] term summed in before the one rounding
 int launch_combine(const moe_shape* s, const void* yp, const float* gates,
-                   const int32_t* row_of_pair, void* out, hipStream_t st);
+                   const int32_t* row_of_pair, const void* add, void* out, hipStream_t st);
 int launch_combine_bwd(const moe_shape* s, const void* dout, const void* yp, const float* gates,
                        const int32_t* row_of_pair, void* dyp, float* dgates, hipStream_t st);
 int launch_dispatch_bwd(const moe_shape* s, const void* dxp, const int32_t* row_of_pair,
-                        const int32_t* idx, const float* dlogits, const void* W_rT, void* dx,
-                        bool accumulate, hipStream_t st);
+                        const int32_t* idx, const float* dlogits, const void* W_rT,
+                        const void* add, void* dx, bool accumulate, hipStream_t st);
 // expert GEMMs.  xrows: null, or the plan's pair_of_row for the fused permute,
 // in which case xp is the token matrix x and dispatched row r of the GEMM1 (and
 // wgrad dW_gu) operand is token xrows[r] / K.

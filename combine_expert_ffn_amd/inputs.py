@@ -38,6 +38,7 @@ class Workload:
     zipf_s: float = 0.0        # >0: per-expert router bias -s*ln(e+1)
     microbatches: int = 1
     note: str = ""
+    F_s: int = 0               # >0: a shared expert of this FFN width
 
     def with_tokens(self, T: int) -> "Workload":
         return replace(self, T=T)
@@ -67,6 +68,10 @@ WORKLOADS = {
     # mixed-precision setting)
     "ep16_rank_f16": Workload("ep16_rank_f16", T=4096, d=2048, F=768, E=8, e_lo=0,
                               E_l=8, K=8, dtype="f16", route="force_balance"),
+    # the ep16 step with a shared expert of width 2F beside the routed experts
+    "ep16_rank_shared_bf16": Workload("ep16_rank_shared_bf16", T=4096, d=2048, F=768, E=8,
+                                      e_lo=0, E_l=8, K=8, dtype="bf16",
+                                      route="force_balance", F_s=1536),
 }
 
 
@@ -101,7 +106,9 @@ def make_inputs(w: Workload, seed: int = 0, microbatches: int | None = None) -> 
     """All inputs of one workload as float32 numpy arrays (values representable
     in ``w.dtype``).  Keys: x, W_r (None for forced balance), bias (or None),
     W_gu [E_l,2F,d], W_down [E_l,d,F], dout, gates (forced balance only), and
-    x_b, dout_b (, gates_b) for a second micro-batch."""
+    x_b, dout_b (, gates_b) for a second micro-batch, and W_gu_s [2F_s,d],
+    W_down_s [d,F_s] for a shared expert (drawn last, so the other draws do not
+    depend on it)."""
     microbatches = w.microbatches if microbatches is None else microbatches
     rng = np.random.Generator(np.random.PCG64(seed))
     out = {}
@@ -130,6 +137,9 @@ def make_inputs(w: Workload, seed: int = 0, microbatches: int | None = None) -> 
         if w.route == "force_balance":
             e = rng.standard_exponential((w.T, w.K))
             out["gates_b"] = (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
+    if w.F_s > 0:
+        out["W_gu_s"] = _to_dtype(_normal(rng, (2 * w.F_s, w.d), w.weight_std, 1), w.dtype)
+        out["W_down_s"] = _to_dtype(_normal(rng, (w.d, w.F_s), w.weight_std, 1), w.dtype)
     return out
 
 

@@ -268,6 +268,34 @@ int moe_dispatch_bwd(const moe_shape* s, const void* dxp,
                      const float* dlogits, const void* W_r, void* dx,
                      int accumulate, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---- shared expert -------------------------------------------------------- */
+/*
+ * The shared expert (page 1 lists the shared-expert overlap among the
+ * options): one SwiGLU FFN of width F_s that every token passes through beside
+ * the routed experts; its output is added to the combine's and its input
+ * gradient to the dispatch backward's.  It is an expert over all T tokens in
+ * token order with gate 1, so it runs on the same grouped GEMMs.
+ *   W_gu_s [2F_s,d] (rows [0,F_s) gate, [F_s,2F_s) up), W_down_s [d,F_s] (dtype)
+ *   F_s a multiple of 64 in [64, 16384]; workspace moe_shared_workspace_bytes.
+ */
+size_t moe_shared_workspace_bytes(const moe_shape* s, int64_t F_s);
+/* h_s [T,2F_s], a_s [T,F_s], y_s [T,d] out: the FFN of x [T,d]. */
+int moe_shared_expert_fwd(const moe_shape* s, int64_t F_s, const void* x,
+                          const void* W_gu_s, const void* W_down_s, void* h_s, void* a_s,
+                          void* y_s, void* ws, size_t ws_bytes, hipStream_t stream);
+/* its D for output gradient dout [T,d]: dh_s [T,2F_s], dx_s [T,d] out
+ * (same formulas as moe_ffn_dgrad). */
+int moe_shared_expert_dgrad(const moe_shape* s, int64_t F_s, const void* dout,
+                            const void* h_s, const void* W_gu_s, const void* W_down_s,
+                            void* dh_s, void* dx_s, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+/* its W: dW_gu_s = dh_s^T . x [2F_s,d], dW_down_s = dout^T . a_s [d,F_s] (f32);
+ * accumulate & MOE_ACCUM_DW adds to the existing values. */
+int moe_shared_expert_wgrad(const moe_shape* s, int64_t F_s, const void* x, const void* a_s,
+                            const void* dh_s, const void* dout, float* dW_gu_s,
+                            float* dW_down_s, int accumulate, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
 /* ---- two-micro-batch step ------------------------------------------------ */
 /* One micro-batch's buffers (sizes as in the calls above). */
 typedef struct moe_mb {
@@ -294,6 +322,12 @@ typedef struct moe_mb {
   void* dh;
   void* dxp;
   void* dx;
+  /* shared expert (used when moe_step.F_s > 0) */
+  void* h_s;    /* [T,2F_s] forward, saved for the backward */
+  void* a_s;    /* [T,F_s]  forward, saved for the backward */
+  void* y_s;    /* [T,d]    forward */
+  void* dh_s;   /* [T,2F_s] backward */
+  void* dx_s;   /* [T,d]    backward */
 } moe_mb;
 
 typedef struct moe_step {
@@ -310,9 +344,20 @@ typedef struct moe_step {
   const moe_mb* fwd;      /* micro-batch forwarded in this step, or NULL */
   const moe_mb* bwd;      /* micro-batch back-propagated in this step (its
                              forward buffers hold its forward results), or NULL */
-  void* ws;               /* >= moe_step_workspace_bytes(&shape) */
+  void* ws;               /* >= moe_step_workspace_bytes(&shape), or
+                             moe_step_workspace_bytes_shared(&shape, F_s) */
   size_t ws_bytes;
+  /* shared expert: F_s = 0 for none */
+  int64_t F_s;
+  const void* W_gu_s;     /* [2F_s,d] */
+  const void* W_down_s;   /* [d,F_s] */
+  float* dW_gu_s;         /* [2F_s,d] (accumulate as dW_gu) */
+  float* dW_down_s;       /* [d,F_s] */
 } moe_step;
+
+/* Bytes of workspace moe_overlap_step needs with a shared expert of width F_s
+ * (F_s = 0: moe_step_workspace_bytes). */
+size_t moe_step_workspace_bytes_shared(const moe_shape* s, int64_t F_s);
 
 /*
  * moe_overlap_step - forward of micro-batch `fwd` and backward of micro-batch
@@ -324,6 +369,10 @@ typedef struct moe_step {
  *   s_copy:    A.route, A.dispatch, A.ffn_fwd, A.combine
  *   s_compute: B.combine_bwd, B.route_bwd, B.dgrad, B.dispatch_bwd,
  *              B.wgrad (deferred: last, unless MOE_STEP_EAGER_WGRAD)
+ * With a shared expert (F_s > 0) A's shared forward runs on s_compute and B's
+ * shared D on s_copy, each beside the other micro-batch's chain; A's combine
+ * adds y_s, B's dispatch backward adds dx_s, and B's shared W follows B's
+ * routed W (both left out with MOE_STEP_SKIP_WGRAD).
  * On return, work on s_compute depends on everything the step issued, so a
  * caller that waits for s_compute sees all results.  Results are bit-identical
  * to MOE_STEP_SERIALIZE (all calls on s_compute in forward-then-backward order).

@@ -49,4 +49,7 @@ from .moe_oracle import (  # noqa: F401
     ffn_wgrad,
     layer_forward,
     layer_backward,
+    shared_expert_fwd,
+    shared_expert_dgrad,
+    shared_expert_wgrad,
 )

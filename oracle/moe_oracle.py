@@ -217,13 +217,14 @@ def expert_ffn_fwd(xp, offsets, W_gu, W_down, prec="bf16"):
 # ----------------------------------------------------------------------------
 # combine (expert-grouped rows -> tokens, gate-weighted)
 # ----------------------------------------------------------------------------
-def combine(yp, gates, row_of_pair, prec="bf16") -> np.ndarray:
-    """out[t] = sum over local slots k (ascending) of gates[t,k] * y_p[row(t,k)];
-    a token with no local slot gets 0."""
+def combine(yp, gates, row_of_pair, prec="bf16", add=None) -> np.ndarray:
+    """out[t] = [add[t] +] sum over local slots k (ascending) of
+    gates[t,k] * y_p[row(t,k)]; a token with no local slot gets add[t] (or 0).
+    ``add`` is a token-aligned term, the shared expert's output."""
     yp = np.asarray(yp, np.float64)
     gates = np.asarray(gates, np.float64)
     T, K = row_of_pair.shape
-    out = np.zeros((T, yp.shape[1]))
+    out = np.zeros((T, yp.shape[1])) if add is None else np.asarray(add, np.float64).copy()
     for k in range(K):
         r = row_of_pair[:, k]
         m = r >= 0
@@ -340,17 +341,21 @@ def route_bwd(dgates, gates, idx, x, E: int, dW_r_prev=None, prec="bf16"):
     return dlogits, dW_r
 
 
-def dispatch_bwd(dxp, row_of_pair, dlogits=None, W_r=None, dx_prev=None, prec="bf16"):
+def dispatch_bwd(dxp, row_of_pair, dlogits=None, W_r=None, dx_prev=None, prec="bf16",
+                 add=None):
     """Gradient with respect to the layer input x:
 
-    dx[t] = [dx_prev[t]] + sum over local slots k of dxp[row(t,k)]
+    dx[t] = [dx_prev[t]] + [add[t]] + sum over local slots k of dxp[row(t,k)]
             [+ (dlogits . W_r^T)[t]   when the router is differentiated],
-    stored once.
+    stored once.  ``add`` is a token-aligned term, the shared expert's input
+    gradient.
     """
     dxp = np.asarray(dxp, np.float64)
     T, K = row_of_pair.shape
     d = dxp.shape[1]
     dx = np.zeros((T, d)) if dx_prev is None else np.asarray(dx_prev, np.float64).copy()
+    if add is not None:
+        dx += np.asarray(add, np.float64)
     for k in range(K):
         r = row_of_pair[:, k]
         m = r >= 0
@@ -361,15 +366,44 @@ def dispatch_bwd(dxp, row_of_pair, dlogits=None, W_r=None, dx_prev=None, prec="b
 
 
 # ----------------------------------------------------------------------------
+# shared expert: one SwiGLU FFN every token passes through, beside the routed
+# experts (skill card page 1 names the shared-expert overlap), i.e. an expert
+# over all T rows in token order with gate 1
+# ----------------------------------------------------------------------------
+def shared_expert_fwd(x, W_gu_s, W_down_s, prec="bf16"):
+    """h_s = [g, u] = x . W_gu_s^T, a_s = silu(g) * u, y_s = a_s . W_down_s^T."""
+    T = np.asarray(x).shape[0]
+    return expert_ffn_fwd(x, np.array([0, T]), np.asarray(W_gu_s)[None],
+                          np.asarray(W_down_s)[None], prec)
+
+
+def shared_expert_dgrad(dout, h_s, W_gu_s, W_down_s, prec="bf16"):
+    """dh_s and dx_s of the shared expert for output gradient dout."""
+    T = np.asarray(dout).shape[0]
+    return ffn_dgrad(dout, h_s, np.array([0, T]), np.asarray(W_gu_s)[None],
+                     np.asarray(W_down_s)[None], prec)
+
+
+def shared_expert_wgrad(x, a_s, dh_s, dout, dW_gu_prev=None, dW_down_prev=None, prec="bf16"):
+    """dW_gu_s = dh_s^T . x, dW_down_s = dout^T . a_s (float32)."""
+    T = np.asarray(x).shape[0]
+    gu, dn = ffn_wgrad(x, a_s, dh_s, dout, np.array([0, T]),
+                       None if dW_gu_prev is None else np.asarray(dW_gu_prev)[None],
+                       None if dW_down_prev is None else np.asarray(dW_down_prev)[None], prec)
+    return gu[0], dn[0]
+
+
+# ----------------------------------------------------------------------------
 # whole layer, in the pages' phase order
 # ----------------------------------------------------------------------------
 def layer_forward(x, K, e_lo, E_l, W_gu, W_down, *, W_r=None, bias=None, E=None,
                   logits=None, force_balance=False, gates=None, tile_m=256,
-                  prec="bf16"):
+                  prec="bf16", shared=None):
     """route -> dispatch (plan + permute) -> expert FFN -> combine.
 
     Routing: ``force_balance`` (idx from the closed form, ``gates`` given), or
-    top-K over ``logits`` when given, else over x . W_r + bias.
+    top-K over ``logits`` when given, else over x . W_r + bias.  ``shared`` =
+    (W_gu_s, W_down_s) adds the shared expert's output into the combine.
     """
     x = np.asarray(x, np.float64)
     T = x.shape[0]
@@ -387,14 +421,20 @@ def layer_forward(x, K, e_lo, E_l, W_gu, W_down, *, W_r=None, bias=None, E=None,
     N = int(plan["offsets"][E_l])
     xp = permute(x, plan["pair_of_row"], K, N)
     h, a, yp = expert_ffn_fwd(xp, plan["offsets"], W_gu, W_down, prec)
-    out = combine(yp, g, plan["row_of_pair"], prec)
+    sh = {}
+    if shared is not None:
+        h_s, a_s, y_s = shared_expert_fwd(x, shared[0], shared[1], prec)
+        sh = dict(h_s=h_s, a_s=a_s, y_s=y_s)
+    out = combine(yp, g, plan["row_of_pair"], prec, add=sh.get("y_s"))
     return dict(logits=lg, idx=idx, gates=g, N=N, xp=xp, h=h, a=a, yp=yp, out=out,
-                E=E, **plan)
+                E=E, **plan, **sh)
 
 
 def layer_backward(fwd, x, dout, W_gu, W_down, *, W_r=None, differentiate_router=True,
-                   prec="bf16"):
-    """combine bwd -> router bwd -> expert D (dgrad) -> dispatch bwd -> expert W (wgrad)."""
+                   prec="bf16", shared=None):
+    """combine bwd -> router bwd -> expert D (dgrad) -> dispatch bwd -> expert W (wgrad).
+    With ``shared`` = (W_gu_s, W_down_s) the shared expert's D joins the
+    dispatch backward and its W follows the routed W."""
     N = fwd["N"]
     dyp, dgates = combine_bwd(dout, fwd["yp"], fwd["gates"], fwd["row_of_pair"], N, prec)
     dlogits = dW_r = None
@@ -402,9 +442,16 @@ def layer_backward(fwd, x, dout, W_gu, W_down, *, W_r=None, differentiate_router
         dlogits, dW_r = route_bwd(dgates, fwd["gates"], fwd["idx"],
                                   x if W_r is not None else None, fwd["E"], prec=prec)
     dh, dxp = ffn_dgrad(dyp, fwd["h"], fwd["offsets"], W_gu, W_down, prec)
+    sh = {}
+    if shared is not None:
+        dh_s, dx_s = shared_expert_dgrad(dout, fwd["h_s"], shared[0], shared[1], prec)
+        sh = dict(dh_s=dh_s, dx_s=dx_s)
     dx = dispatch_bwd(dxp, fwd["row_of_pair"],
                       dlogits if (differentiate_router and W_r is not None) else None,
-                      W_r, None, prec)
+                      W_r, None, prec, add=sh.get("dx_s"))
     dW_gu, dW_down = ffn_wgrad(fwd["xp"], fwd["a"], dh, dyp, fwd["offsets"], prec=prec)
+    if shared is not None:
+        sh["dW_gu_s"], sh["dW_down_s"] = shared_expert_wgrad(
+            np.asarray(x, np.float64), fwd["a_s"], sh["dh_s"], dout, prec=prec)
     return dict(dyp=dyp, dgates=dgates, dlogits=dlogits, dW_r=dW_r, dh=dh, dxp=dxp,
-                dx=dx, dW_gu=dW_gu, dW_down=dW_down)
+                dx=dx, dW_gu=dW_gu, dW_down=dW_down, **sh)

@@ -37,9 +37,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_struct_layouts_match_header():
     assert C.sizeof(_lib.MoeShape) == 7 * 8 + 2 * 4
-    assert C.sizeof(_lib.MoeMB) == len(_lib.MB_FIELDS) * 8
-    # shape + 2 ints + 7 pointers + 2 mb pointers + ws + ws_bytes
-    assert C.sizeof(_lib.MoeStep) == C.sizeof(_lib.MoeShape) + 8 + 7 * 8 + 2 * 8 + 8 + 8
+    assert C.sizeof(_lib.MoeMB) == len(_lib.MB_FIELDS) * 8 == 26 * 8
+    # shape + 2 ints + 7 pointers + 2 mb pointers + ws + ws_bytes + F_s + 4 shared pointers
+    assert C.sizeof(_lib.MoeStep) == C.sizeof(_lib.MoeShape) + 8 + 7 * 8 + 2 * 8 + 8 + 8 + 8 + 4 * 8
 
 
 def _shape(**kw):
@@ -134,6 +134,35 @@ def test_fused_permute_validation():
     assert b"pair_of_row" in L.moe_last_error()
     assert L.moe_overlap_step(C.byref(st), None, None, 0) == M.MOE_ERR_NULL  # unfused needs xp
     assert b"xp" in L.moe_last_error()
+
+
+def test_shared_expert_validation():
+    L = M.lib()
+    s = _shape()
+    assert M.moe_shared_workspace_bytes(s, 96) == 0          # F_s not a multiple of 64
+    assert M.moe_shared_workspace_bytes(s, 128) > 256
+    assert M.moe_step_workspace_bytes_shared(s, 0) == M.moe_step_workspace_bytes(s)
+    assert (M.moe_step_workspace_bytes_shared(s, 128)
+            == M.moe_step_workspace_bytes(s) + 2 * M.moe_shared_workspace_bytes(s, 128))
+    assert L.moe_shared_expert_fwd(C.byref(s), 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   1 << 30, None) == M.MOE_ERR_SHAPE
+    assert L.moe_shared_expert_fwd(C.byref(s), 128, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   1 << 30, None) == M.MOE_ERR_NULL
+    assert L.moe_shared_expert_dgrad(C.byref(s), 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     16, None) == M.MOE_ERR_WORKSPACE
+    assert L.moe_shared_expert_wgrad(C.byref(s), 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8,
+                                     FAKE, 1 << 30, None) == M.MOE_ERR_ARG
+    # a step with a shared expert needs its weights, buffers and the larger workspace
+    mb = _lib.MoeMB(*([0x1000] * len(_lib.MB_FIELDS)))
+    st = _lib.MoeStep(s, M.MOE_ROUTE_FORCE_BALANCE, 0, None, None, 0x1000, 0x1000, None, 0x1000,
+                      0x1000, C.pointer(mb), None, 0x1000, M.moe_step_workspace_bytes(s),
+                      128, None, 0x1000, 0x1000, 0x1000)
+    assert L.moe_overlap_step(C.byref(st), None, None, 0) == M.MOE_ERR_NULL
+    assert b"W_gu_s" in L.moe_last_error()
+    st.W_gu_s = 0x1000
+    assert L.moe_overlap_step(C.byref(st), None, None, 0) == M.MOE_ERR_WORKSPACE
+    st.F_s = 96
+    assert L.moe_overlap_step(C.byref(st), None, None, 0) == M.MOE_ERR_SHAPE
 
 
 def test_workspace_size_checked():

@@ -282,6 +282,117 @@ def test_chain_parity(name, fused):
         close("dW_r", host(g["dW_r"]), refb["dW_r"], tau)
 
 
+SHARED = {"tiny_f32": 128, "fb_ragged_bf16": 192, "zipf_window_f16": 128,
+          "mid_window_bf16": 64}
+
+
+@pytest.mark.parametrize("name", list(SHARED))
+def test_shared_expert_stage(name):
+    """The shared expert's three calls against the oracle, fed the oracle's
+    inputs; accumulate adds exactly."""
+    w = SMALL[name]
+    Fs = SHARED[name]
+    log(f"[shared stage] {name}: F_s={Fs} {w.dtype}")
+    prec, tau = w.dtype, _tau(w)
+    rng = np.random.default_rng(21)
+    x_h = O.store(rng.standard_normal((w.T, w.d)), prec)
+    Wgu_h = O.store(0.05 * rng.standard_normal((2 * Fs, w.d)), prec)
+    Wd_h = O.store(0.05 * rng.standard_normal((w.d, Fs)), prec)
+    dout_h = O.store(rng.standard_normal((w.T, w.d)), prec)
+    s = M.shape_of(w)
+    D = lambda a: dev(a, prec)
+    x, Wgu, Wd, dout = D(x_h), D(Wgu_h), D(Wd_h), D(dout_h)
+    ws = torch.empty(M.moe_shared_workspace_bytes(s, Fs), dtype=torch.uint8, device="cuda")
+    mb = M.MicroBatch(s, F_s=Fs)
+    M.moe_shared_expert_fwd(s, Fs, x, Wgu, Wd, mb.h_s, mb.a_s, mb.y_s, ws)
+    h_r, a_r, y_r = O.shared_expert_fwd(x_h, Wgu_h, Wd_h, prec)
+    close("h_s", host(mb.h_s), h_r, tau)
+    close("a_s", host(mb.a_s), a_r, tau)
+    close("y_s", host(mb.y_s), y_r, tau)
+    M.moe_shared_expert_dgrad(s, Fs, dout, D(h_r), Wgu, Wd, mb.dh_s, mb.dx_s, ws)
+    dh_r, dx_r = O.shared_expert_dgrad(dout_h, h_r, Wgu_h, Wd_h, prec)
+    close("dh_s", host(mb.dh_s), dh_r, tau)
+    close("dx_s", host(mb.dx_s), dx_r, tau)
+    dWgu = torch.full((2 * Fs, w.d), 3.0, device="cuda")
+    dWd = torch.full((w.d, Fs), 3.0, device="cuda")
+    M.moe_shared_expert_wgrad(s, Fs, x, D(a_r), D(dh_r), dout, dWgu, dWd, 0, ws)
+    gu_r, dn_r = O.shared_expert_wgrad(x_h, a_r, dh_r, dout_h, prec=prec)
+    mag_gu, mag_dn = O.shared_expert_wgrad(np.abs(x_h), np.abs(a_r), np.abs(dh_r),
+                                           np.abs(dout_h), prec="f64")
+    close_reduction("dW_gu_s", host(dWgu), gu_r, mag_gu, tau)
+    close_reduction("dW_down_s", host(dWd), dn_r, mag_dn, tau)
+    first = (dWgu.clone(), dWd.clone())
+    M.moe_shared_expert_wgrad(s, Fs, x, D(a_r), D(dh_r), dout, dWgu, dWd, M.MOE_ACCUM_DW, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dWgu, 2 * first[0]) and torch.equal(dWd, 2 * first[1])
+
+
+@pytest.mark.parametrize("name", ["fb_ragged_bf16", "zipf_window_f16", "tiny_f32"])
+def test_chain_parity_shared_expert(name):
+    """The whole layer with a shared expert through moe_overlap_step, against
+    the oracle; the overlapped step (shared forward and D on the other
+    micro-batch's stream) is bit-identical to the serialized one."""
+    w = SMALL[name]
+    Fs = SHARED[name]
+    log(f"[shared chain] {name}: F_s={Fs}")
+    prec, tau = w.dtype, TAU[w.dtype]
+    inp = make_inputs(w, seed=0)
+    rng = np.random.default_rng(23)
+    Wgu_h = O.store(0.05 * rng.standard_normal((2 * Fs, w.d)), prec)
+    Wd_h = O.store(0.05 * rng.standard_normal((w.d, Fs)), prec)
+    X, ref, refb = _oracle(w, inp, prec)
+    fb = w.route == "force_balance"
+    ref = O.layer_forward(X["x"], w.K, w.e_lo, w.E_l, X["W_gu"], X["W_down"], W_r=X["W_r"],
+                          bias=X["bias"], E=w.E, force_balance=fb, gates=X["gates"],
+                          tile_m=M.moe_tile_m(), prec=prec, shared=(Wgu_h, Wd_h))
+    refb = O.layer_backward(ref, X["x"], X["dout"], X["W_gu"], X["W_down"], W_r=X["W_r"],
+                            differentiate_router=not fb, prec=prec, shared=(Wgu_h, Wd_h))
+    s = M.shape_of(w)
+    D = lambda a: dev(a, prec)
+    topk = not fb
+    results = {}
+    for tag, flags, side in (("serial", M.MOE_STEP_SERIALIZE, False), ("overlap", 0, True)):
+        A = M.MicroBatch(s, x=D(inp["x"]), dout=D(inp["dout"]),
+                         gates=None if topk else dev(inp["gates"], "f32x"), F_s=Fs)
+        W_gu, W_down = D(inp["W_gu"]), D(inp["W_down"])
+        W_r = D(inp["W_r"]) if topk else None
+        bias = dev(inp["bias"], "f32x") if inp["bias"] is not None else None
+        dW_gu = torch.empty(w.E_l, 2 * w.F, w.d, device="cuda")
+        dW_down = torch.empty(w.E_l, w.d, w.F, device="cuda")
+        dW_r = torch.empty(w.d, w.E, device="cuda") if topk else None
+        dWgu_s = torch.empty(2 * Fs, w.d, device="cuda")
+        dWd_s = torch.empty(w.d, Fs, device="cuda")
+        sh = (D(Wgu_h), D(Wd_h), dWgu_s, dWd_s)
+        ws = torch.empty(M.moe_step_workspace_bytes_shared(s, Fs), dtype=torch.uint8,
+                         device="cuda")
+        mode = M.MOE_ROUTE_TOPK if topk else M.MOE_ROUTE_FORCE_BALANCE
+        s0 = torch.cuda.current_stream()
+        s1 = torch.cuda.Stream() if side else s0
+        st = M.make_step(s, mode, W_gu, W_down, dW_gu, dW_down, ws, fwd=A, W_r=W_r, bias=bias,
+                         dW_r=dW_r, shared=sh)
+        M.moe_overlap_step(st, s0, s1, flags)
+        st = M.make_step(s, mode, W_gu, W_down, dW_gu, dW_down, ws, bwd=A, W_r=W_r, bias=bias,
+                         dW_r=dW_r, shared=sh)
+        M.moe_overlap_step(st, s0, s1, flags)
+        torch.cuda.synchronize()
+        results[tag] = dict(A=A, dWgu_s=dWgu_s, dWd_s=dWd_s, dW_gu=dW_gu, dW_down=dW_down)
+    r, q = results["overlap"], results["serial"]
+    for k in ("out", "dx", "y_s", "dx_s", "dh_s", "dgates"):
+        assert torch.equal(getattr(r["A"], k), getattr(q["A"], k)), k
+    for k in ("dWgu_s", "dWd_s", "dW_gu", "dW_down"):
+        assert torch.equal(r[k], q[k]), k
+    A = r["A"]
+    if topk and np.any(host(A.idx) != ref["idx"]):
+        pytest.skip("near-tie routing difference; the stage tests cover it")
+    close("y_s", host(A.y_s), ref["y_s"], tau)
+    close("out", host(A.out), ref["out"], tau)
+    close("dx_s", host(A.dx_s), refb["dx_s"], tau)
+    close("dx", host(A.dx), refb["dx"], tau)
+    close("dW_gu_s", host(r["dWgu_s"]), refb["dW_gu_s"], tau)
+    close("dW_down_s", host(r["dWd_s"]), refb["dW_down_s"], tau)
+    close("dW_gu", host(r["dW_gu"]), refb["dW_gu"], tau)
+
+
 def test_empty_experts_and_no_tokens():
     # logits crafted so that local experts 3 and 5 receive no token
     w = Workload("empty", T=96, d=64, F=64, E=8, e_lo=0, E_l=8, K=2, dtype="bf16", route="topk")

@@ -286,6 +286,74 @@ def test_ffn_combine_match_brute_force():
     np.testing.assert_allclose(f["out"], ref, rtol=1e-12, atol=1e-12)
 
 
+def test_shared_expert_matches_brute_force():
+    """The shared expert adds, to every token's output, its own SwiGLU FFN
+    computed element by element (fsum), whatever the routing; with a zero
+    down projection the layer is unchanged."""
+    rng = np.random.default_rng(17)
+    T, d, F, Fs, E, K, e_lo, E_l = 13, 6, 4, 5, 6, 2, 2, 3
+    x = rng.standard_normal((T, d))
+    W_r = rng.standard_normal((d, E))
+    W_gu = rng.standard_normal((E_l, 2 * F, d)) * 0.5
+    W_down = rng.standard_normal((E_l, d, F)) * 0.5
+    W_gu_s = rng.standard_normal((2 * Fs, d)) * 0.5
+    W_down_s = rng.standard_normal((d, Fs)) * 0.5
+    base = O.layer_forward(x, K, e_lo, E_l, W_gu, W_down, W_r=W_r, tile_m=4, prec="f64")
+    f = O.layer_forward(x, K, e_lo, E_l, W_gu, W_down, W_r=W_r, tile_m=4, prec="f64",
+                        shared=(W_gu_s, W_down_s))
+    ref = np.zeros((T, d))
+    for t in range(T):
+        for j in range(Fs):
+            gv = math.fsum(W_gu_s[j, c] * x[t, c] for c in range(d))
+            uv = math.fsum(W_gu_s[Fs + j, c] * x[t, c] for c in range(d))
+            ref[t] += W_down_s[:, j] * (gv / (1.0 + math.exp(-gv)) * uv)
+    np.testing.assert_allclose(f["out"] - base["out"], ref, rtol=1e-12, atol=1e-12)
+    z = O.layer_forward(x, K, e_lo, E_l, W_gu, W_down, W_r=W_r, tile_m=4, prec="f64",
+                        shared=(W_gu_s, np.zeros_like(W_down_s)))
+    assert np.array_equal(z["out"], base["out"])
+
+
+def test_finite_differences_shared_expert():
+    """Gradients of the layer with a shared expert with respect to x and the
+    shared weights, by central differences in float64."""
+    rng = np.random.default_rng(19)
+    T, d, F, Fs, E, K, e_lo, E_l = 5, 4, 3, 3, 4, 2, 0, 3
+    x = rng.standard_normal((T, d))
+    W_r = rng.standard_normal((d, E))
+    W_gu = rng.standard_normal((E_l, 2 * F, d))
+    W_down = rng.standard_normal((E_l, d, F))
+    W_gu_s = rng.standard_normal((2 * Fs, d))
+    W_down_s = rng.standard_normal((d, Fs))
+    dout = rng.standard_normal((T, d))
+
+    def loss():
+        f = O.layer_forward(x, K, e_lo, E_l, W_gu, W_down, W_r=W_r, tile_m=4, prec="f64",
+                            shared=(W_gu_s, W_down_s))
+        return float(np.sum(f["out"] * dout)), f["idx"]
+
+    f = O.layer_forward(x, K, e_lo, E_l, W_gu, W_down, W_r=W_r, tile_m=4, prec="f64",
+                        shared=(W_gu_s, W_down_s))
+    b = O.layer_backward(f, x, dout, W_gu, W_down, W_r=W_r, prec="f64",
+                         shared=(W_gu_s, W_down_s))
+    h = 1e-6
+    checked = 0
+    for name, P, G in (("x", x, b["dx"]), ("W_gu_s", W_gu_s, b["dW_gu_s"]),
+                       ("W_down_s", W_down_s, b["dW_down_s"])):
+        for i in np.ndindex(P.shape):
+            old = P[i]
+            P[i] = old + h
+            lp, ip = loss()
+            P[i] = old - h
+            lm, im = loss()
+            P[i] = old
+            if not (np.array_equal(ip, f["idx"]) and np.array_equal(im, f["idx"])):
+                continue
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - G[i]) <= 1e-6 * max(1.0, abs(fd)), (name, i, fd, G[i])
+            checked += 1
+    assert checked > 0.9 * (x.size + W_gu_s.size + W_down_s.size)
+
+
 def test_identity_experts_combine_gives_gate_weighted_x():
     rng = np.random.default_rng(8)
     T, d, E, K = 40, 8, 5, 2
