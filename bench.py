@@ -149,6 +149,17 @@ def main():
     ap.add_argument("--fused-permute", choices=("on", "off"), default="off",
                     help="fuse the permute into the expert GEMMs (MOE_STEP_FUSED_PERMUTE): GEMM1 "
                          "and wgrad read the token rows of x through the dispatch plan, no xp")
+    ap.add_argument("--wgrad-order", choices=("mid", "last"), default="mid",
+                    help="where the backward micro-batch's wgrad runs on its stream: between the "
+                         "two dgrad GEMMs (mid, MOE_STEP_MID_WGRAD) or after the dispatch "
+                         "backward (last); the same order is used for the serialized steps")
+    ap.add_argument("--pipeline", choices=("on", "off"), default="on",
+                    help="run the overlapped steps G at a time through moe_overlap_steps, the "
+                         "streams' roles alternating so consecutive steps overlap (on), or one "
+                         "moe_overlap_step call per step, joined at every step boundary (off)")
+    ap.add_argument("--group", type=int, default=10,
+                    help="steps per moe_overlap_steps call and per captured graph (even; "
+                         "--steps must be a multiple of it)")
     ap.add_argument("--overlapped-only", action="store_true",
                     help="run only the warm-up and the overlapped steps and print no JSON line: "
                          "the program to trace with rocprofv3 --kernel-trace for the overlap of "
@@ -198,7 +209,15 @@ def main():
     ws = torch.empty(M.moe_step_workspace_bytes_shared(s, w.F_s), dtype=torch.uint8,
                      device="cuda")
     fused = args.fused_permute == "on"
-    FUSED = M.MOE_STEP_FUSED_PERMUTE if fused else 0
+    pipelined = args.pipeline == "on"
+    G = args.group
+    if G < 2 or G % 2 or args.steps % G or args.warmup % 2:
+        err("bench.py: --group must be even and divide --steps; --warmup must be even")
+        sys.exit(2)
+    # flags of every step: the fused permute and the wgrad's place in the
+    # backward stream's order (both leave the results unchanged)
+    FUSED = ((M.MOE_STEP_FUSED_PERMUTE if fused else 0) |
+             (M.MOE_STEP_MID_WGRAD if args.wgrad_order == "mid" else 0))
     shared = None
     if w.F_s:  # a shared expert beside the routed ones
         shared = (D(inp["W_gu_s"]), D(inp["W_down_s"]),
@@ -216,10 +235,26 @@ def main():
                          bias=bias, dW_r=dW_r, accumulate=M.MOE_ACCUM_DW, shared=shared)
         M.moe_overlap_step(st, s0, s1, flags | FUSED)
 
-    def run_loop(n, flags, i0):
-        for i in range(i0, i0 + n):
-            step(mbs[(i + 1) % 2], mbs[i % 2], flags)
+    def make(i):  # step i forwards one micro-batch and back-propagates the other
+        return M.make_step(s, mode, W_gu, W_down, dW_gu, dW_down, ws, fwd=mbs[(i + 1) % 2],
+                           bwd=mbs[i % 2], W_r=W_r, bias=bias, dW_r=dW_r,
+                           accumulate=M.MOE_ACCUM_DW, shared=shared)
+
+    def issue(i0, n, flags, q):
+        """Issue steps i0 .. i0+n-1 on q (and s1): one pipelined moe_overlap_steps
+        call per group of G steps for overlapped steps with --pipeline on, else one
+        moe_overlap_step call per step."""
+        if pipelined and not flags & M.MOE_STEP_SERIALIZE:
+            for g0 in range(i0, i0 + n, G):
+                M.moe_overlap_steps([make(j) for j in range(g0, min(g0 + G, i0 + n))], q, s1,
+                                    flags | FUSED)
+        else:
+            for j in range(i0, i0 + n):
+                M.moe_overlap_step(make(j), q, s1, flags | FUSED)
         return i0 + n
+
+    def run_loop(n, flags, i0):
+        return issue(i0, n, flags, s0)
 
     step(mbs[0], None, 0)  # prime: micro-batch 0 forwarded
     if args.counter_pass:
@@ -264,25 +299,22 @@ def main():
     # ---- timed region 1b: the same overlapped steps replayed from a HIP graph
     # holding two consecutive steps (the micro-batches swap roles each step)
     # -> value.  The library records only kernels and events into the graph.
-    launch = "eager launches"
-    if args.graph == "on":
+    def graph_ms(i, flags):
+        """Capture G consecutive steps with `flags` into one HIP graph (G even, so
+        the micro-batches' roles at the end match the start), replay it (warm-up,
+        then exactly --steps steps timed); returns (ms per step, wall ms per
+        step, i)."""
         g = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
         cap.wait_stream(s0)
         with torch.cuda.graph(g, stream=cap, capture_error_mode="thread_local"):
-            c0 = torch.cuda.current_stream()
-            sts = []
-            for j in (i, i + 1):
-                st = M.make_step(s, mode, W_gu, W_down, dW_gu, dW_down, ws, fwd=mbs[(j + 1) % 2],
-                                 bwd=mbs[j % 2], W_r=W_r, bias=bias, dW_r=dW_r,
-                                 accumulate=M.MOE_ACCUM_DW, shared=shared)
-                M.moe_overlap_step(st, c0, s1, FUSED)
-                sts.append(st)
-        i += 2
-        for _ in range(max(1, args.warmup // 2)):
+            issue(i, G, flags, torch.cuda.current_stream())
+        i += G
+        warm = max(1, args.warmup // G)
+        for _ in range(warm):
             g.replay()
         torch.cuda.synchronize()
-        reps = max(1, args.steps // 2)
+        reps = args.steps // G
         t0 = time.perf_counter()
         ev0.record(s0)
         for _ in range(reps):
@@ -290,15 +322,34 @@ def main():
         ev1.record(s0)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        i += 2 * (reps + max(1, args.warmup // 2))
-        ms_step = ev0.elapsed_time(ev1) / (2 * reps)
-        launch = "hipGraph replay (two steps per graph)"
-        err(f"[bench] overlapped, graph replay: {ms_step:.4f} ms/step "
-            f"(wall {1e3 * wall / (2 * reps):.4f})")
+        i += G * (reps + warm)
+        return ev0.elapsed_time(ev1) / (G * reps), 1e3 * wall / (G * reps), i
+
+    launch = "eager launches"
+    ms_serial_graph = None
+    if args.graph == "on":
+        ms_step, wall_ms, i = graph_ms(i, 0)
+        launch = f"hipGraph replay ({G} steps per graph)"
+        err(f"[bench] overlapped, graph replay: {ms_step:.4f} ms/step (wall {wall_ms:.4f})")
+        ms_serial_graph, wall_ms, i = graph_ms(i, M.MOE_STEP_SERIALIZE)
+        err(f"[bench] serialized, graph replay: {ms_serial_graph:.4f} ms/step "
+            f"(wall {wall_ms:.4f})")
+
+    # ---- timed region 1c: the same steps serialized on one stream, eager
+    i = run_loop(args.warmup, M.MOE_STEP_SERIALIZE, i)
+    torch.cuda.synchronize()
+    ev0.record(s0)
+    i = run_loop(args.steps, M.MOE_STEP_SERIALIZE, i)
+    ev1.record(s0)
+    torch.cuda.synchronize()
+    ms_serial_eager = ev0.elapsed_time(ev1) / args.steps
+    err(f"[bench] serialized, eager: {ms_serial_eager:.4f} ms/step -> overlap "
+        f"x{ms_serial_eager / ms_eager:.3f} (eager vs eager)")
 
     # ---- timed region 2: the same steps serialized on one stream, with every
     # kernel bracketed by HIP events on its stream (no concurrency, so each
-    # kernel's interval is its own execution)
+    # kernel's interval is its own execution); per-kernel times only, the
+    # events' own cost makes this step time no baseline
     i = run_loop(args.warmup, M.MOE_STEP_SERIALIZE, i)
     M.moe_timing_reset()
     M.moe_timing_enable(64 * args.steps)
@@ -308,10 +359,10 @@ def main():
     ev1.record(s0)
     torch.cuda.synchronize()
     M.moe_timing_disable()
-    ms_serial = ev0.elapsed_time(ev1) / args.steps
+    ms_serial_events = ev0.elapsed_time(ev1) / args.steps
     kern = M.moe_timing_report()
-    err(f"[bench] serialized (kernel events on): {ms_serial:.4f} ms/step -> overlap "
-        f"x{ms_serial / ms_eager:.3f} (eager vs eager)")
+    err(f"[bench] serialized (kernel events on): {ms_serial_events:.4f} ms/step")
+    ms_serial = ms_serial_graph if ms_serial_graph is not None else ms_serial_eager
 
     nonfinite = int(sum((~torch.isfinite(t.float())).sum().item()
                         for mb in mbs for t in (mb.out, mb.dx)))
@@ -379,7 +430,13 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d": w.d, "F": w.F, "E": w.E, "e_lo": w.e_lo,
                    "E_l": w.E_l, "K": w.K, "routing": w.route, "N_rows": N,
                    "step": "1F1B: forward of one micro-batch + backward of the other, "
-                           "two streams, wgrad deferred", "launch": launch,
+                           "two streams, " + ("wgrad between the two dgrad GEMMs"
+                                              if args.wgrad_order == "mid" else
+                                              "wgrad deferred to the end"),
+                   "launch": launch,
+                   "pipeline": (f"moe_overlap_steps, {G} steps per call, stream roles "
+                                "alternating" if pipelined else
+                                "one moe_overlap_step per step, joined at each boundary"),
                    "permute": "fused into GEMM1 and wgrad" if fused else "separate kernel",
                    "shared_expert_F": w.F_s},
         "roofline": roofline,
@@ -387,9 +444,13 @@ def main():
         "grouped_gemm_mfma_util": round(gemm_flops / gemm_s / 1e12 / PEAK_BF16_TFLOPS, 4),
         "dispatch_hbm_gbs": disp.get("achieved"),
         "dispatch_hbm_kernel": disp_kernel,
+        # serialized = the same steps on one stream, launched the same way
+        # (graph replay or eager) as the overlapped value, no kernel events
+        "serialized_ms_per_step": round(ms_serial, 4),
+        "overlap_speedup": round(ms_serial / ms_step, 4),
         "eager_overlapped_ms_per_step": round(ms_eager, 4),
-        "serialized_ms_per_step": None if ms_serial is None else round(ms_serial, 4),
-        "overlap_speedup": None if ms_serial is None else round(ms_serial / ms_eager, 4),
+        "eager_serialized_ms_per_step": round(ms_serial_eager, 4),
+        "eager_overlap_speedup": round(ms_serial_eager / ms_eager, 4),
         "kernels": kernels,
         "nonfinite_outputs": nonfinite,
     }

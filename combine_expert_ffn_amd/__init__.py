@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     MOE_ERR_UNSUPPORTED, MOE_ERR_ARG, MOE_F32, MOE_BF16, MOE_F16, MOE_ROUTE_TOPK,
     MOE_ROUTE_TOPK_FROM_LOGITS, MOE_ROUTE_FORCE_BALANCE, MOE_ACCUM_DX, MOE_ACCUM_DW,
     MOE_STEP_SERIALIZE, MOE_STEP_EAGER_WGRAD, MOE_STEP_SKIP_WGRAD, MOE_STEP_FUSED_PERMUTE,
+    MOE_STEP_MID_WGRAD,
 )
 
 
@@ -166,6 +167,13 @@ def moe_dispatch_bwd(s, dxp, row_of_pair, idx, dlogits, W_r, dx, accumulate, ws,
 
 def moe_overlap_step(step: MoeStep, s_compute=None, s_copy=None, flags=0):
     check(lib().moe_overlap_step(C.byref(step), _stream(s_compute), _stream(s_copy), int(flags)))
+
+
+def moe_overlap_steps(steps, s_compute=None, s_copy=None, flags=0):
+    """Run the MoeStep list `steps` as consecutive pipelined 1F1B steps."""
+    arr = (MoeStep * len(steps))(*steps)
+    check(lib().moe_overlap_steps(arr, len(steps), _stream(s_compute), _stream(s_copy),
+                                  int(flags)))
 
 
 def moe_timing_enable(max_records=4096):

@@ -34,6 +34,7 @@ MOE_STEP_SERIALIZE = 1
 MOE_STEP_EAGER_WGRAD = 2
 MOE_STEP_SKIP_WGRAD = 4
 MOE_STEP_FUSED_PERMUTE = 8
+MOE_STEP_MID_WGRAD = 16
 
 
 class MoeShape(C.Structure):
@@ -91,6 +92,7 @@ SIGNATURES = {
                                 _P]),
     "moe_dispatch_bwd": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, C.c_int, _P, C.c_size_t, _P]),
     "moe_overlap_step": (C.c_int, [C.POINTER(MoeStep), _P, _P, C.c_int]),
+    "moe_overlap_steps": (C.c_int, [C.POINTER(MoeStep), C.c_int, _P, _P, C.c_int]),
     "moe_timing_enable": (C.c_int, [C.c_int]),
     "moe_timing_disable": (C.c_int, []),
     "moe_timing_reset": (C.c_int, []),

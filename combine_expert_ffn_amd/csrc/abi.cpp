@@ -686,9 +686,10 @@ static int bwd_route(const StepCtx& c, const moe_mb* B, hipStream_t q) {
                           with_dw ? c.st->dW_r : nullptr,
                           (c.st->accumulate & MOE_ACCUM_DW) != 0, c.wsB, q);
 }
-static int bwd_dgrad(const StepCtx& c, const moe_mb* B, bool weights_ready, hipStream_t q) {
+static int bwd_dgrad(const StepCtx& c, const moe_mb* B, bool weights_ready, hipStream_t q,
+                     int parts = kDgradBoth) {
   return launch_ffn_dgrad(c.s, B->dyp, B->h, B->offsets, B->tile_offsets, c.st->W_gu,
-                          c.st->W_down, B->dh, B->dxp, c.wsB, weights_ready, q);
+                          c.st->W_down, B->dh, B->dxp, c.wsB, weights_ready, q, parts);
 }
 static int bwd_dispatch(const StepCtx& c, const moe_mb* B, hipStream_t q) {
   return do_dispatch_bwd(c.s, B->dxp, B->row_of_pair, B->idx, c.router ? B->dlogits : nullptr,
@@ -701,22 +702,25 @@ static int bwd_wgrad(const StepCtx& c, const moe_mb* B, hipStream_t q) {
                           c.st->dW_down, (c.st->accumulate & MOE_ACCUM_DW) != 0, q);
 }
 
-}  // namespace moe
-
-extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t s1, int flags) {
-  g_err[0] = 0;
+// Host-side checks of one step description (flags, route mode, buffers,
+// workspace); fn names the entry point in the error message.
+static int check_step(const moe_step* st, int flags, const char* fn) {
   REQUIRE(st);
   const moe_shape* s = &st->shape;
   if (int rc = validate_shape(s)) return rc;
   if (flags & ~(MOE_STEP_SERIALIZE | MOE_STEP_EAGER_WGRAD | MOE_STEP_SKIP_WGRAD |
-                MOE_STEP_FUSED_PERMUTE))
-    return set_error(MOE_ERR_ARG, "moe_overlap_step: unknown flags 0x%x", flags);
+                MOE_STEP_FUSED_PERMUTE | MOE_STEP_MID_WGRAD))
+    return set_error(MOE_ERR_ARG, "%s: unknown flags 0x%x", fn, flags);
+  if ((flags & MOE_STEP_EAGER_WGRAD ? 1 : 0) + (flags & MOE_STEP_SKIP_WGRAD ? 1 : 0) +
+          (flags & MOE_STEP_MID_WGRAD ? 1 : 0) > 1)
+    return set_error(MOE_ERR_ARG, "%s: EAGER_WGRAD, SKIP_WGRAD and MID_WGRAD exclude each other",
+                     fn);
   const int mode = st->route_mode;
   if (mode != MOE_ROUTE_TOPK && mode != MOE_ROUTE_TOPK_FROM_LOGITS &&
       mode != MOE_ROUTE_FORCE_BALANCE)
-    return set_error(MOE_ERR_ARG, "moe_overlap_step: unknown route mode %d", mode);
+    return set_error(MOE_ERR_ARG, "%s: unknown route mode %d", fn, mode);
   if (st->accumulate & ~(MOE_ACCUM_DX | MOE_ACCUM_DW))
-    return set_error(MOE_ERR_ARG, "moe_overlap_step: unknown accumulate bits 0x%x",
+    return set_error(MOE_ERR_ARG, "%s: unknown accumulate bits 0x%x", fn,
                      st->accumulate);
   REQUIRE(st->W_gu);
   REQUIRE(st->W_down);
@@ -724,7 +728,7 @@ extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t 
   const moe_mb* A = st->fwd;
   const moe_mb* B = st->bwd;
   const bool fused = (flags & MOE_STEP_FUSED_PERMUTE) != 0;
-  if (fused) TRY(check_gather_x(s, "moe_overlap_step"));
+  if (fused) TRY(check_gather_x(s, fn));
   if (A) TRY(validate_mb_fwd(A, mode, fused));
   if (B) {
     TRY(validate_mb_bwd(B, mode, fused));
@@ -733,7 +737,7 @@ extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t 
     if (mode == MOE_ROUTE_TOPK && st->dW_r) REQUIRE(B->x);
   }
   if (A && B && A == B)
-    return set_error(MOE_ERR_ARG, "moe_overlap_step: fwd and bwd micro-batches must differ");
+    return set_error(MOE_ERR_ARG, "%s: fwd and bwd micro-batches must differ", fn);
   const bool shared = st->F_s != 0;
   if (shared) {
     TRY(validate_shared(st->F_s));
@@ -757,15 +761,29 @@ extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t 
   REQUIRE(st->ws);
   const size_t one = ws_one(s);
   const size_t sh = shared ? ws_shared(s, st->F_s) : 0;
-  if (int rc = need_ws(__func__, st->ws_bytes, 2 * one + 2 * sh)) return rc;
+  if (int rc = need_ws(fn, st->ws_bytes, 2 * one + 2 * sh)) return rc;
+  return MOE_OK;
+}
 
+}  // namespace moe
+
+extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t s1, int flags) {
+  g_err[0] = 0;
+  if (int rc = check_step(st, flags, "moe_overlap_step")) return rc;
+  const moe_shape* s = &st->shape;
+  const int mode = st->route_mode;
+  const moe_mb* A = st->fwd;
+  const moe_mb* B = st->bwd;
+  const bool fused = (flags & MOE_STEP_FUSED_PERMUTE) != 0;
+  const bool shared = st->F_s != 0;
+  const size_t one = ws_one(s);
+  const size_t sh = shared ? ws_shared(s, st->F_s) : 0;
   StepCtx c{st, s, st->ws, (char*)st->ws + one, mode == MOE_ROUTE_TOPK, fused,
             (char*)st->ws + 2 * one, (char*)st->ws + 2 * one + sh};
   const bool serial = (flags & MOE_STEP_SERIALIZE) || s0 == s1;
   const bool eager = (flags & MOE_STEP_EAGER_WGRAD) != 0;
   const bool skip_w = (flags & MOE_STEP_SKIP_WGRAD) != 0;
-  if (eager && skip_w)
-    return set_error(MOE_ERR_ARG, "moe_overlap_step: EAGER_WGRAD and SKIP_WGRAD exclude each other");
+  const bool mid = (flags & MOE_STEP_MID_WGRAD) != 0;
 
   // B's weight gradients: the routed experts', then the shared expert's
   auto wgrads = [&](hipStream_t q) -> int {
@@ -781,7 +799,16 @@ extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t 
       TRY(fwd_ffn(c, A, s0));
       TRY(fwd_combine(c, A, s0));
     }
-    if (B) {
+    if (B && mid) {
+      TRY(bwd_combine(c, B, s0));
+      TRY(bwd_route(c, B, s0));
+      TRY(bwd_dgrad(c, B, false, s0, kDgradAct));
+      TRY(bwd_wgrad(c, B, s0));
+      TRY(bwd_dgrad(c, B, true, s0, kDgradIn));
+      if (shared) TRY(bwd_shared_dgrad(c, B, s0));
+      TRY(bwd_dispatch(c, B, s0));
+      if (shared) TRY(bwd_shared_wgrad(c, B, s0));
+    } else if (B) {
       TRY(bwd_combine(c, B, s0));
       TRY(bwd_route(c, B, s0));
       TRY(bwd_dgrad(c, B, false, s0));
@@ -819,7 +846,16 @@ extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t 
     if (shared) HIPTRY(hipStreamWaitEvent(s1, ev->shared_a, 0));
     TRY(fwd_combine(c, A, s1));
   }
-  if (B) {  // the backward micro-batch on s0
+  if (B && mid) {  // the backward micro-batch on s0, routed W between the two D GEMMs
+    TRY(bwd_combine(c, B, s0));
+    TRY(bwd_route(c, B, s0));
+    TRY(bwd_dgrad(c, B, false, s0, kDgradAct));
+    TRY(bwd_wgrad(c, B, s0));
+    TRY(bwd_dgrad(c, B, true, s0, kDgradIn));
+    if (shared) HIPTRY(hipStreamWaitEvent(s0, ev->shared_b, 0));
+    TRY(bwd_dispatch(c, B, s0));
+    if (shared) TRY(bwd_shared_wgrad(c, B, s0));
+  } else if (B) {  // the backward micro-batch on s0
     TRY(bwd_combine(c, B, s0));
     TRY(bwd_route(c, B, s0));
     TRY(bwd_dgrad(c, B, false, s0));
@@ -829,6 +865,164 @@ extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t 
     if (!eager && !skip_w) TRY(wgrads(s0));
   }
   // s0 ends after everything the step issued on s1
+  HIPTRY(hipEventRecord(ev->end, s1));
+  HIPTRY(hipStreamWaitEvent(s0, ev->end, 0));
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// several consecutive steps with the streams' roles alternating
+// ---------------------------------------------------------------------------
+namespace moe {
+
+struct MultiEvents {
+  hipEvent_t start, end, dwr, dw, dws;
+};
+
+// One set per (host thread, device), as step_events; every wait of a call is
+// on a record issued earlier in the same call.
+static int multi_events(MultiEvents** out) {
+  static thread_local std::vector<MultiEvents*> sets;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return set_error(MOE_ERR_HIP, "hipGetDevice failed");
+  if ((int)sets.size() <= dev) sets.resize(dev + 1, nullptr);
+  if (!sets[dev]) {
+    MultiEvents* e = new MultiEvents();
+    hipEvent_t* all[] = {&e->start, &e->end, &e->dwr, &e->dw, &e->dws};
+    for (hipEvent_t* p : all)
+      if (hipEventCreateWithFlags(p, hipEventDisableTiming) != hipSuccess)
+        return set_error(MOE_ERR_HIP, "hipEventCreateWithFlags failed");
+    sets[dev] = e;
+  }
+  *out = sets[dev];
+  return MOE_OK;
+}
+
+static bool same_mb(const moe_mb* a, const moe_mb* b) {
+  if (!a || !b) return a == b;
+  return a == b || memcmp(a, b, sizeof(moe_mb)) == 0;
+}
+
+// The forward chain of one micro-batch on one stream (its shared expert first).
+static int fwd_chain(const StepCtx& c, const moe_mb* A, hipStream_t q) {
+  if (has_shared(c)) TRY(fwd_shared(c, A, q));
+  TRY(fwd_route(c, A, q));
+  TRY(fwd_dispatch(c, A, q));
+  TRY(fwd_ffn(c, A, q));
+  return fwd_combine(c, A, q);
+}
+
+// The backward chain of one micro-batch on one stream.  Each weight-gradient
+// accumulation (router dW_r, routed dW, shared dW) waits for the previous
+// step's accumulation into the same buffer (on the other stream) when
+// `prev` is set, and records its own, so the sums happen in step order.
+static int bwd_chain(const StepCtx& c, const moe_mb* B, hipStream_t q, bool mid, bool eager,
+                     const MultiEvents* ev, bool prev) {
+  const bool shared = has_shared(c);
+  const bool dwr = c.router && c.st->dW_r;
+  auto wait = [&](hipEvent_t e) -> int {
+    if (prev) HIPTRY(hipStreamWaitEvent(q, e, 0));
+    return MOE_OK;
+  };
+  auto routed_w = [&]() -> int {
+    TRY(wait(ev->dw));
+    TRY(bwd_wgrad(c, B, q));
+    HIPTRY(hipEventRecord(ev->dw, q));
+    return MOE_OK;
+  };
+  auto shared_w = [&]() -> int {
+    if (!shared) return MOE_OK;
+    TRY(wait(ev->dws));
+    TRY(bwd_shared_wgrad(c, B, q));
+    HIPTRY(hipEventRecord(ev->dws, q));
+    return MOE_OK;
+  };
+  TRY(bwd_combine(c, B, q));
+  if (dwr) TRY(wait(ev->dwr));
+  TRY(bwd_route(c, B, q));
+  if (dwr) HIPTRY(hipEventRecord(ev->dwr, q));
+  if (mid) {
+    TRY(bwd_dgrad(c, B, false, q, kDgradAct));
+    TRY(routed_w());
+    TRY(bwd_dgrad(c, B, true, q, kDgradIn));
+    if (shared) TRY(bwd_shared_dgrad(c, B, q));
+    TRY(bwd_dispatch(c, B, q));
+    return shared_w();
+  }
+  TRY(bwd_dgrad(c, B, false, q));
+  if (shared) TRY(bwd_shared_dgrad(c, B, q));
+  if (eager) {
+    TRY(routed_w());
+    TRY(shared_w());
+    return bwd_dispatch(c, B, q);
+  }
+  TRY(bwd_dispatch(c, B, q));
+  TRY(routed_w());
+  return shared_w();
+}
+
+}  // namespace moe
+
+extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, hipStream_t s1,
+                                 int flags) {
+  using namespace moe;
+  g_err[0] = 0;
+  REQUIRE(steps);
+  if (n < 1) return set_error(MOE_ERR_ARG, "moe_overlap_steps: n = %d, need at least 1", n);
+  if (flags & MOE_STEP_SKIP_WGRAD)
+    return set_error(MOE_ERR_ARG,
+                     "moe_overlap_steps: SKIP_WGRAD is not supported (the backward stream "
+                     "alternates between steps)");
+  for (int j = 0; j < n; ++j) {
+    const moe_step* st = &steps[j];
+    if (int rc = check_step(st, flags, "moe_overlap_steps")) return rc;
+    if (st->fwd && st->bwd && same_mb(st->fwd, st->bwd))
+      return set_error(MOE_ERR_ARG,
+                       "moe_overlap_steps: step %d forwards and back-propagates the same "
+                       "micro-batch", j);
+    if (j > 0 && !same_mb(st->bwd, steps[j - 1].fwd))
+      return set_error(MOE_ERR_ARG,
+                       "moe_overlap_steps: step %d must back-propagate the micro-batch that "
+                       "step %d forwarded", j, j - 1);
+  }
+  const bool serial = (flags & MOE_STEP_SERIALIZE) || s0 == s1;
+  if (serial) {
+    for (int j = 0; j < n; ++j) TRY(moe_overlap_step(&steps[j], s0, s0, flags));
+    return MOE_OK;
+  }
+  MultiEvents* ev = nullptr;
+  TRY(multi_events(&ev));
+  const bool mid = (flags & MOE_STEP_MID_WGRAD) != 0;
+  const bool eager = (flags & MOE_STEP_EAGER_WGRAD) != 0;
+  const bool fused = (flags & MOE_STEP_FUSED_PERMUTE) != 0;
+  HIPTRY(hipEventRecord(ev->start, s0));
+  HIPTRY(hipStreamWaitEvent(s1, ev->start, 0));
+  bool prev_b = false;  // the previous step of this call had a backward
+  for (int j = 0; j < n; ++j) {
+    const moe_step* st = &steps[j];
+    const moe_shape* s = &st->shape;
+    const size_t one = ws_one(s);
+    const size_t sh = st->F_s ? ws_shared(s, st->F_s) : 0;
+    // Step j runs its forward on P and its backward on Q; the roles swap every
+    // step, so the forward of step j follows, on its stream, the backward of
+    // step j - 1 (whose micro-batch buffers it may reuse), and the backward of
+    // step j follows the forward of the same micro-batch in step j - 1.  Each
+    // stream owns one half of the workspace (s1 the first), so no half is
+    // used by both streams at once.
+    const bool even = (j & 1) == 0;
+    hipStream_t P = even ? s1 : s0, Q = even ? s0 : s1;
+    char* ws = (char*)st->ws;
+    char* half_s1 = ws;
+    char* half_s0 = ws + one;
+    char* shalf_s1 = ws + 2 * one;
+    char* shalf_s0 = ws + 2 * one + sh;
+    StepCtx c{st, s, even ? half_s1 : half_s0, even ? half_s0 : half_s1,
+              st->route_mode == MOE_ROUTE_TOPK, fused,
+              even ? shalf_s1 : shalf_s0, even ? shalf_s0 : shalf_s1};
+    if (st->fwd) TRY(fwd_chain(c, st->fwd, P));
+    if (st->bwd) TRY(bwd_chain(c, st->bwd, Q, mid, eager, ev, prev_b));
+    prev_b = st->bwd != nullptr;
+  }
   HIPTRY(hipEventRecord(ev->end, s1));
   HIPTRY(hipStreamWaitEvent(s0, ev->end, 0));
   return MOE_OK;

@@ -1041,14 +1041,18 @@ int ffn_fwd_t(const moe_shape* s, const void* xp, const int32_t* xrows, const in
 
 template <class E>
 int ffn_dgrad_t(const moe_shape* s, const void* dyp, const void* h, const int32_t* offsets,
-                const int32_t* tile_offsets, void* dh, void* dxp, void* ws, hipStream_t st) {
+                const int32_t* tile_offsets, void* dh, void* dxp, void* ws, hipStream_t st,
+                int parts) {
   const int d = (int)s->d, F = (int)s->F;
   const uint16_t* W_downT = (const uint16_t*)((char*)ws + ws_wT_offset(s));
   const uint16_t* W_guT = (const uint16_t*)((const char*)W_downT + ws_wT_down_bytes(s));
-  DgradActOp<E> da{(const uint16_t*)dyp, (const uint16_t*)h, W_downT, (uint16_t*)dh, d, F};
-  if (int rc = launch_row_grouped("dgrad_act", s, da, offsets, tile_offsets,
-                                  (F + T256::BN - 1) / T256::BN, st))
-    return rc;
+  if (parts & kDgradAct) {
+    DgradActOp<E> da{(const uint16_t*)dyp, (const uint16_t*)h, W_downT, (uint16_t*)dh, d, F};
+    if (int rc = launch_row_grouped("dgrad_act", s, da, offsets, tile_offsets,
+                                    (F + T256::BN - 1) / T256::BN, st))
+      return rc;
+  }
+  if (!(parts & kDgradIn)) return MOE_OK;
   DgradInOp<E> di{(const uint16_t*)dh, W_guT, (uint16_t*)dxp, d, F};
   return launch_row_grouped("dgrad_in", s, di, offsets, tile_offsets,
                             (d + T256::BN - 1) / T256::BN, st);
@@ -1119,12 +1123,12 @@ int launch_dgrad_weights_mfma(const moe_shape* s, const void* W_gu, const void* 
 int launch_ffn_dgrad_mfma(const moe_shape* s, const void* dyp, const void* h,
                           const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
                           const void* W_down, void* dh, void* dxp, void* ws, bool weights_ready,
-                          hipStream_t st) {
+                          hipStream_t st, int parts) {
   if (!weights_ready)
     if (int rc = launch_dgrad_weights_mfma(s, W_gu, W_down, ws, st)) return rc;
   return s->dtype == MOE_F16
-             ? ffn_dgrad_t<F16>(s, dyp, h, offsets, tile_offsets, dh, dxp, ws, st)
-             : ffn_dgrad_t<BF16>(s, dyp, h, offsets, tile_offsets, dh, dxp, ws, st);
+             ? ffn_dgrad_t<F16>(s, dyp, h, offsets, tile_offsets, dh, dxp, ws, st, parts)
+             : ffn_dgrad_t<BF16>(s, dyp, h, offsets, tile_offsets, dh, dxp, ws, st, parts);
 }
 
 int launch_ffn_wgrad_mfma(const moe_shape* s, const void* xp, const int32_t* xrows,

@@ -139,7 +139,7 @@ int launch_dgrad_weights_mfma(const moe_shape* s, const void* W_gu, const void* 
 int launch_ffn_dgrad_mfma(const moe_shape* s, const void* dyp, const void* h,
                           const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
                           const void* W_down, void* dh, void* dxp, void* ws, bool weights_ready,
-                          hipStream_t st);
+                          hipStream_t st, int parts);
 int launch_ffn_wgrad_mfma(const moe_shape* s, const void* xp, const int32_t* xrows,
                           const void* a, const void* dh, const void* dyp,
                           const int32_t* offsets, float* dW_gu, float* dW_down, bool accumulate,
@@ -171,18 +171,21 @@ int launch_dgrad_weights(const moe_shape* s, const void* W_gu, const void* W_dow
 
 int launch_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h, const int32_t* offsets,
                      const int32_t* tile_offsets, const void* W_gu, const void* W_down, void* dh,
-                     void* dxp, void* ws, bool weights_ready, hipStream_t st) {
+                     void* dxp, void* ws, bool weights_ready, hipStream_t st, int parts) {
   if (s->T == 0) return MOE_OK;
   if (is16(s))
     return launch_ffn_dgrad_mfma(s, dyp, h, offsets, tile_offsets, W_gu, W_down, dh, dxp, ws,
-                                 weights_ready, st);
+                                 weights_ready, st, parts);
   const long cap = s->T * s->K;
   const int d = (int)s->d, F = (int)s->F, E_l = (int)s->E_l;
-  MOE_LAUNCH("f32_dgrad_act", st,
-             f32_dgrad_act_kernel<<<(unsigned)cdiv(cap * F, 256), 256, 0, st>>>(
-      (const float*)dyp, (const float*)h, offsets, (const float*)W_down, (float*)dh, cap, E_l, d,
-      F));
-  if (int rc = check_launch("f32 dgrad (activation)")) return rc;
+  if (parts & kDgradAct) {
+    MOE_LAUNCH("f32_dgrad_act", st,
+               f32_dgrad_act_kernel<<<(unsigned)cdiv(cap * F, 256), 256, 0, st>>>(
+        (const float*)dyp, (const float*)h, offsets, (const float*)W_down, (float*)dh, cap, E_l,
+        d, F));
+    if (int rc = check_launch("f32 dgrad (activation)")) return rc;
+  }
+  if (!(parts & kDgradIn)) return MOE_OK;
   MOE_LAUNCH("f32_dgrad_in", st,
              f32_dgrad_in_kernel<<<(unsigned)cdiv(cap * d, 256), 256, 0, st>>>(
       (const float*)dh, offsets, (const float*)W_gu, (float*)dxp, cap, E_l, d, F));

@@ -215,10 +215,14 @@ int launch_ffn_fwd(const moe_shape* s, const void* xp, const int32_t* xrows,
 int launch_dgrad_weights(const moe_shape* s, const void* W_gu, const void* W_down, void* ws,
                          hipStream_t st);
 // weights_ready: launch_dgrad_weights already ran on this ws (ordered before
-// this call), so the copies are not made again.
+// this call), so the copies are not made again.  parts selects the GEMMs:
+// kDgradAct (dy_p -> dh, with the SwiGLU backward), kDgradIn (dh -> dx_p), or
+// both in that order; a call with kDgradIn alone needs the copies made.
+enum { kDgradAct = 1, kDgradIn = 2, kDgradBoth = 3 };
 int launch_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h, const int32_t* offsets,
                      const int32_t* tile_offsets, const void* W_gu, const void* W_down, void* dh,
-                     void* dxp, void* ws, bool weights_ready, hipStream_t st);
+                     void* dxp, void* ws, bool weights_ready, hipStream_t st,
+                     int parts = kDgradBoth);
 int launch_ffn_wgrad(const moe_shape* s, const void* xp, const int32_t* xrows, const void* a,
                      const void* dh, const void* dyp, const int32_t* offsets, float* dW_gu,
                      float* dW_down, bool accumulate, hipStream_t st);

@@ -91,6 +91,13 @@ extern "C" {
                                    permute, moe_permute_fusion); xp of both
                                    micro-batches may be NULL, and `bwd` needs x
                                    and pair_of_row                                */
+#define MOE_STEP_MID_WGRAD   16 /* the routed experts' wgrad between the two dgrad
+                                   GEMMs (after dy_p -> dh, before dh -> dx_p)
+                                   instead of last: on one GPU, where the dispatch
+                                   backward is a local gather, this lets the wgrad's
+                                   partial last round of tiles share the chip with
+                                   the other stream's GEMMs.  Excludes EAGER_WGRAD
+                                   and SKIP_WGRAD; results are unchanged           */
 
 /*
  * Layer shape.  T tokens of hidden size d; E experts routed over, of which the
@@ -368,7 +375,9 @@ size_t moe_step_workspace_bytes_shared(const moe_shape* s, int64_t F_s);
  * last partial wave of tiles beside the other stream's work):
  *   s_copy:    A.route, A.dispatch, A.ffn_fwd, A.combine
  *   s_compute: B.combine_bwd, B.route_bwd, B.dgrad, B.dispatch_bwd,
- *              B.wgrad (deferred: last, unless MOE_STEP_EAGER_WGRAD)
+ *              B.wgrad (deferred: last, unless MOE_STEP_EAGER_WGRAD; with
+ *              MOE_STEP_MID_WGRAD the dgrad is split and the order is
+ *              dgrad(dy_p -> dh), wgrad, dgrad(dh -> dx_p), dispatch_bwd)
  * With a shared expert (F_s > 0) A's shared forward runs on s_compute and B's
  * shared D on s_copy, each beside the other micro-batch's chain; A's combine
  * adds y_s, B's dispatch backward adds dx_s, and B's shared W follows B's
@@ -384,6 +393,35 @@ size_t moe_step_workspace_bytes_shared(const moe_shape* s, int64_t F_s);
  */
 int moe_overlap_step(const moe_step* st, hipStream_t s_compute, hipStream_t s_copy,
                      int flags);
+
+/*
+ * moe_overlap_steps - n consecutive steps of the 1F1B schedule (1F1B note
+ * page 2, "MoE 1F1B overlap": the micro-batch forwarded in one step is
+ * back-propagated in the next), pipelined across the step boundaries.
+ * steps[j] describes step j as for moe_overlap_step; for j >= 1, steps[j].bwd
+ * must hold the same buffers as steps[j-1].fwd (field by field; both may be
+ * NULL), and no step may forward and back-propagate the same buffers.
+ * The streams' roles alternate: step j runs its forward chain on s_copy when j
+ * is even and on s_compute when j is odd, and its backward chain on the other
+ * stream (each chain in moe_overlap_step's order, the shared expert's forward
+ * and D on the chain's own stream).  So step j's backward follows the forward
+ * of the same micro-batch on its stream and starts while step j-1's backward
+ * still runs on the other one, and a forward may reuse the buffers of the
+ * micro-batch back-propagated in the step before.  Each stream owns one half of
+ * the workspace.  The only other cross-stream waits order the weight-gradient
+ * sums (dW_r, dW_gu/dW_down, the shared expert's): each step's sum into a
+ * buffer waits for the previous step's, so every sum happens in step order.
+ * Flags as moe_overlap_step, except MOE_STEP_SKIP_WGRAD (rejected: the wgrad's
+ * stream alternates).  Results are bit-identical to n moe_overlap_step calls
+ * with MOE_STEP_SERIALIZE.  s_copy forks from s_compute at the start and joins
+ * it at the end, so on return work on s_compute depends on everything the call
+ * issued; the call may be captured into a HIP graph on s_compute.  Errors: as
+ * moe_overlap_step (checked for every step before anything is launched), and
+ * MOE_ERR_ARG for n < 1, a step whose bwd is not the previous step's fwd, or
+ * SKIP_WGRAD.
+ */
+int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s_compute, hipStream_t s_copy,
+                      int flags);
 
 /* ---- kernel timing -------------------------------------------------------- */
 /*

@@ -24,7 +24,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("moe_route", "moe_dispatch", "moe_expert_ffn_fwd", "moe_combine", "moe_ffn_dgrad",
               "moe_ffn_wgrad", "moe_overlap_step", "moe_combine_bwd", "moe_dispatch_bwd",
-              "moe_route_bwd", "moe_workspace_bytes", "moe_last_error"):
+              "moe_route_bwd", "moe_workspace_bytes", "moe_last_error", "moe_overlap_steps"):
         assert n in names
 
 
@@ -211,6 +211,45 @@ def test_step_rejects_small_workspace_and_same_microbatch():
     mb2 = _lib.MoeMB(*([0x2000] * len(_lib.MB_FIELDS)))
     st.bwd = C.pointer(mb2)
     st.ws_bytes = 1 << 40
-    flags = M.MOE_STEP_EAGER_WGRAD | M.MOE_STEP_SKIP_WGRAD
-    assert M.lib().moe_overlap_step(C.byref(st), None, None, flags) == M.MOE_ERR_ARG
-    assert b"exclude" in M.lib().moe_last_error()
+    for flags in (M.MOE_STEP_EAGER_WGRAD | M.MOE_STEP_SKIP_WGRAD,
+                  M.MOE_STEP_MID_WGRAD | M.MOE_STEP_SKIP_WGRAD,
+                  M.MOE_STEP_MID_WGRAD | M.MOE_STEP_EAGER_WGRAD):
+        assert M.lib().moe_overlap_step(C.byref(st), None, None, flags) == M.MOE_ERR_ARG
+        assert b"exclude" in M.lib().moe_last_error()
+    # an unknown flag bit is rejected
+    assert M.lib().moe_overlap_step(C.byref(st), None, None, 64) == M.MOE_ERR_ARG
+
+
+def test_multi_step_rejects_bad_chains():
+    """moe_overlap_steps checks every step before it launches anything."""
+    s = _shape()
+    L = M.lib()
+    m1 = _lib.MoeMB(*([0x1000] * len(_lib.MB_FIELDS)))
+    m2 = _lib.MoeMB(*([0x2000] * len(_lib.MB_FIELDS)))
+    m2_copy = _lib.MoeMB(*([0x2000] * len(_lib.MB_FIELDS)))   # same buffers, other struct
+    m3 = _lib.MoeMB(*([0x3000] * len(_lib.MB_FIELDS)))
+
+    def step(fwd, bwd, ws_bytes=1 << 40):
+        return _lib.MoeStep(s, M.MOE_ROUTE_FORCE_BALANCE, 0, None, None, 0x1000, 0x1000, None,
+                            0x1000, 0x1000, C.pointer(fwd) if fwd else None,
+                            C.pointer(bwd) if bwd else None, 0x1000, ws_bytes)
+
+    def run(steps, flags=0):
+        arr = (_lib.MoeStep * len(steps))(*steps)
+        return L.moe_overlap_steps(arr, len(steps), None, None, flags)
+
+    assert L.moe_overlap_steps(None, 1, None, None, 0) == M.MOE_ERR_NULL
+    arr = (_lib.MoeStep * 1)(step(m1, None))
+    assert L.moe_overlap_steps(arr, 0, None, None, 0) == M.MOE_ERR_ARG
+    # the backward of step 1 must be the micro-batch step 0 forwarded
+    assert run([step(m1, None), step(m2, m3)]) == M.MOE_ERR_ARG
+    assert b"must back-propagate" in L.moe_last_error()
+    # forward and backward of one step on the same buffers (distinct structs)
+    assert run([step(m2, None), step(m2_copy, m2)]) == M.MOE_ERR_ARG
+    assert b"same" in L.moe_last_error()
+    # the caller-deferred wgrad has no fixed stream to follow here
+    assert run([step(m1, m2)], M.MOE_STEP_SKIP_WGRAD) == M.MOE_ERR_ARG
+    assert b"SKIP_WGRAD" in L.moe_last_error()
+    assert run([step(m1, m2)], M.MOE_STEP_MID_WGRAD | M.MOE_STEP_EAGER_WGRAD) == M.MOE_ERR_ARG
+    # a later step's small workspace is found before anything runs
+    assert run([step(m1, m2), step(m2, m1, ws_bytes=8)]) == M.MOE_ERR_WORKSPACE

@@ -46,11 +46,13 @@ class Net:
         return M.MicroBatch(self.s, x=D(x), dout=D(dout),
                             gates=None if gates is None else dev(gates, "f32x"), fused=fused)
 
+    def make(self, fwd, bwd, accumulate=0):
+        return M.make_step(self.s, self.mode, self.W_gu, self.W_down, self.dW_gu, self.dW_down,
+                           self.ws, fwd=fwd, bwd=bwd, W_r=self.W_r, bias=self.bias,
+                           dW_r=self.dW_r, accumulate=accumulate)
+
     def step(self, fwd, bwd, s0, s1, flags, accumulate=0):
-        st = M.make_step(self.s, self.mode, self.W_gu, self.W_down, self.dW_gu, self.dW_down,
-                         self.ws, fwd=fwd, bwd=bwd, W_r=self.W_r, bias=self.bias,
-                         dW_r=self.dW_r, accumulate=accumulate)
-        M.moe_overlap_step(st, s0, s1, flags)
+        M.moe_overlap_step(self.make(fwd, bwd, accumulate), s0, s1, flags)
 
 
 def _rows(t, idx):
@@ -177,33 +179,44 @@ def test_overlap_equals_serialized_two_microbatch():
                         acc, s0)
 
     fp = M.MOE_STEP_FUSED_PERMUTE
+    mid = M.MOE_STEP_MID_WGRAD
     for tag, flags, copy in (("serial", M.MOE_STEP_SERIALIZE, s0), ("overlap", 0, s1),
                              ("eager", M.MOE_STEP_EAGER_WGRAD, s1),
                              ("skip", M.MOE_STEP_SKIP_WGRAD, s1),
-                             ("fused", fp, s1), ("fused_serial", fp | M.MOE_STEP_SERIALIZE, s0)):
+                             ("fused", fp, s1), ("fused_serial", fp | M.MOE_STEP_SERIALIZE, s0),
+                             ("mid", mid, s1), ("mid_serial", mid | M.MOE_STEP_SERIALIZE, s0),
+                             ("mid_fused", mid | fp, s1), ("multi", -1, s1),
+                             ("multi_mid", -1 ^ mid, s1)):
+        multi = flags < 0       # the three steps in one pipelined moe_overlap_steps call
+        flags = ~flags if multi else flags
         skip = flags == M.MOE_STEP_SKIP_WGRAD
         A = net.mb(inp["x"], inp["dout"], fused=bool(flags & fp))
         B = net.mb(inp["x_b"], inp["dout_b"], fused=bool(flags & fp))
-        net.step(A, None, s0, copy, flags)
-        net.step(B, A, s0, copy, flags)                        # A's grads overwrite
-        if skip:
-            late_wgrad(A, 0)
-        net.step(None, B, s0, copy, flags, M.MOE_ACCUM_DW)     # B's grads accumulate
-        if skip:
-            late_wgrad(B, M.MOE_ACCUM_DW)
+        if multi:
+            M.moe_overlap_steps([net.make(A, None), net.make(B, A),
+                                 net.make(None, B, M.MOE_ACCUM_DW)], s0, copy, flags)
+        else:
+            net.step(A, None, s0, copy, flags)
+            net.step(B, A, s0, copy, flags)                    # A's grads overwrite
+            if skip:
+                late_wgrad(A, 0)
+            net.step(None, B, s0, copy, flags, M.MOE_ACCUM_DW)  # B's grads accumulate
+            if skip:
+                late_wgrad(B, M.MOE_ACCUM_DW)
         torch.cuda.synchronize()
         results[tag] = dict(A=A, B=B, dW_gu=net.dW_gu.clone(), dW_down=net.dW_down.clone(),
                             dW_r=net.dW_r.clone())
     ref = results["serial"]
-    for tag in ("overlap", "eager", "skip", "fused", "fused_serial"):
+    for tag in ("overlap", "eager", "skip", "fused", "fused_serial", "mid", "mid_serial",
+                "mid_fused", "multi", "multi_mid"):
         r = results[tag]
         for mbn in ("A", "B"):
             for k in ("idx", "gates", "row_of_pair", "out", "dgates", "dlogits", "dx", "yp"):
                 assert torch.equal(getattr(r[mbn], k), getattr(ref[mbn], k)), (tag, mbn, k)
         for k in ("dW_gu", "dW_down", "dW_r"):
             assert torch.equal(r[k], ref[k]), (tag, k)
-    log("[overlap] overlapped, eager-wgrad, caller-deferred-wgrad and fused-permute steps "
-        "bit-identical to serialized")
+    log("[overlap] overlapped, eager-wgrad, caller-deferred-wgrad, mid-wgrad, fused-permute "
+        "and pipelined multi-step runs bit-identical to serialized")
     # oracle on samples of micro-batch A (weight grads hold A + B)
     r = results["overlap"]
     A, B = r["A"], r["B"]

@@ -351,7 +351,9 @@ def test_chain_parity_shared_expert(name):
     D = lambda a: dev(a, prec)
     topk = not fb
     results = {}
-    for tag, flags, side in (("serial", M.MOE_STEP_SERIALIZE, False), ("overlap", 0, True)):
+    MID = M.MOE_STEP_MID_WGRAD
+    for tag, flags, side in (("serial", M.MOE_STEP_SERIALIZE, False), ("overlap", 0, True),
+                             ("mid", MID, True), ("mid_serial", MID | M.MOE_STEP_SERIALIZE, False)):
         A = M.MicroBatch(s, x=D(inp["x"]), dout=D(inp["dout"]),
                          gates=None if topk else dev(inp["gates"], "f32x"), F_s=Fs)
         W_gu, W_down = D(inp["W_gu"]), D(inp["W_down"])
@@ -376,11 +378,14 @@ def test_chain_parity_shared_expert(name):
         M.moe_overlap_step(st, s0, s1, flags)
         torch.cuda.synchronize()
         results[tag] = dict(A=A, dWgu_s=dWgu_s, dWd_s=dWd_s, dW_gu=dW_gu, dW_down=dW_down)
-    r, q = results["overlap"], results["serial"]
-    for k in ("out", "dx", "y_s", "dx_s", "dh_s", "dgates"):
-        assert torch.equal(getattr(r["A"], k), getattr(q["A"], k)), k
-    for k in ("dWgu_s", "dWd_s", "dW_gu", "dW_down"):
-        assert torch.equal(r[k], q[k]), k
+    q = results["serial"]
+    for tag in ("overlap", "mid", "mid_serial"):
+        r = results[tag]
+        for k in ("out", "dx", "y_s", "dx_s", "dh_s", "dgates"):
+            assert torch.equal(getattr(r["A"], k), getattr(q["A"], k)), (tag, k)
+        for k in ("dWgu_s", "dWd_s", "dW_gu", "dW_down"):
+            assert torch.equal(r[k], q[k]), (tag, k)
+    r = results["overlap"]
     A = r["A"]
     if topk and np.any(host(A.idx) != ref["idx"]):
         pytest.skip("near-tie routing difference; the stage tests cover it")
@@ -585,3 +590,93 @@ def test_wgrad_schedules(counts, d, F):
     M.moe_ffn_wgrad(s, xp, a, dh, dyp, offsets, dW[0], dW[1], M.MOE_ACCUM_DW)
     assert torch.equal(dW[0], 2 * first[0]) and torch.equal(dW[1], 2 * first[1])
     torch.cuda.synchronize()
+
+
+def _pingpong_steps(s, mode, W, grads, ws, mbs, n, shared=None, W_r=None, bias=None):
+    """n consecutive 1F1B steps over two buffer sets: step j forwards mbs[j % 2]
+    (none in the last step) and back-propagates mbs[(j - 1) % 2] (none in the
+    first); the first backward overwrites the weight gradients, later ones add."""
+    W_gu, W_down = W
+    dW_gu, dW_down, dW_r = grads
+    steps = []
+    for j in range(n):
+        fwd = mbs[j % 2] if j < n - 1 else None
+        bwd = mbs[(j - 1) % 2] if j > 0 else None
+        steps.append(M.make_step(s, mode, W_gu, W_down, dW_gu, dW_down, ws, fwd=fwd, bwd=bwd,
+                                 W_r=W_r, bias=bias, dW_r=dW_r,
+                                 accumulate=M.MOE_ACCUM_DW if j > 1 else 0, shared=shared))
+    return steps
+
+
+@pytest.mark.parametrize("name,shared,flags", [
+    ("zipf_window_bf16", False, 0),
+    ("zipf_window_bf16", False, M.MOE_STEP_MID_WGRAD),
+    ("zipf_window_bf16", True, M.MOE_STEP_MID_WGRAD | M.MOE_STEP_FUSED_PERMUTE),
+    ("fb_ragged_bf16", True, M.MOE_STEP_EAGER_WGRAD),
+    ("mid_window_f16", False, M.MOE_STEP_MID_WGRAD),
+    ("tiny_f32", True, M.MOE_STEP_MID_WGRAD),
+])
+def test_multi_step_pipelined_equals_serialized(name, shared, flags):
+    """moe_overlap_steps (streams alternating, steps overlapping) against the same
+    five steps one by one with MOE_STEP_SERIALIZE: every output, gradient and
+    weight-gradient sum bit-identical."""
+    w = SMALL[name]
+    prec = w.dtype
+    log(f"[multi-step] {name}: shared={shared} flags={flags}")
+    inp = make_inputs(w, seed=0, microbatches=2)
+    s = M.shape_of(w)
+    D = lambda a: dev(a, prec)
+    topk = w.route == "topk"
+    mode = M.MOE_ROUTE_TOPK if topk else M.MOE_ROUTE_FORCE_BALANCE
+    fused = bool(flags & M.MOE_STEP_FUSED_PERMUTE)
+    Fs = 128 if shared else 0
+    rng = np.random.default_rng(31)
+    Wgu_s = D(O.store(0.05 * rng.standard_normal((2 * Fs, w.d)), prec)) if shared else None
+    Wd_s = D(O.store(0.05 * rng.standard_normal((w.d, Fs)), prec)) if shared else None
+    W = (D(inp["W_gu"]), D(inp["W_down"]))
+    W_r = D(inp["W_r"]) if topk else None
+    bias = dev(inp["bias"], "f32x") if inp["bias"] is not None else None
+    s0 = torch.cuda.current_stream()
+    s1 = torch.cuda.Stream()
+    res = {}
+    for tag in ("serial", "pipelined"):
+        mbs = [M.MicroBatch(s, x=D(inp[xk]), dout=D(inp[dk]),
+                            gates=None if topk else dev(inp[gk], "f32x"), fused=fused, F_s=Fs)
+               for xk, dk, gk in (("x", "dout", "gates"), ("x_b", "dout_b", "gates_b"))]
+        grads = (torch.full((w.E_l, 2 * w.F, w.d), float("nan"), device="cuda"),
+                 torch.full((w.E_l, w.d, w.F), float("nan"), device="cuda"),
+                 torch.full((w.d, w.E), float("nan"), device="cuda") if topk else None)
+        sh = None
+        if shared:
+            sh = (Wgu_s, Wd_s, torch.full((2 * Fs, w.d), float("nan"), device="cuda"),
+                  torch.full((w.d, Fs), float("nan"), device="cuda"))
+        ws = torch.empty(M.moe_step_workspace_bytes_shared(s, Fs), dtype=torch.uint8,
+                         device="cuda")
+        steps = _pingpong_steps(s, mode, W, grads, ws, mbs, 5, shared=sh, W_r=W_r, bias=bias)
+        if tag == "serial":
+            for st in steps:
+                M.moe_overlap_step(st, s0, s0, flags | M.MOE_STEP_SERIALIZE)
+        else:
+            M.moe_overlap_steps(steps, s0, s1, flags)
+        torch.cuda.synchronize()
+        res[tag] = (mbs, grads, sh)
+    (ma, ga, sa), (mb, gb, sb) = res["serial"], res["pipelined"]
+    keys = ["out", "dx", "dgates", "idx", "gates", "row_of_pair", "offsets", "counts"]
+    if topk:
+        keys += ["logits", "dlogits"]
+    if shared:
+        keys += ["y_s", "dx_s", "dh_s"]
+    for i in range(2):
+        for k in keys:
+            assert torch.equal(getattr(mb[i], k), getattr(ma[i], k)), (i, k)
+        # dispatched-row buffers: rows past N are never written
+        N = int(ma[i].offsets[w.E_l])
+        for k in ("yp", "dh", "a", "dyp", "dxp"):
+            assert torch.equal(getattr(mb[i], k)[:N], getattr(ma[i], k)[:N]), (i, k)
+    for k, (a, b) in enumerate(zip(ga, gb)):
+        if a is not None:
+            assert torch.equal(a, b), ("dW", k)
+            assert torch.isfinite(a).all(), ("dW", k)
+    if shared:
+        assert torch.equal(sa[2], sb[2]) and torch.equal(sa[3], sb[3])
+    log(f"[multi-step] {name}: bit-identical")
