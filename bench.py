@@ -211,8 +211,9 @@ def main():
     fused = args.fused_permute == "on"
     pipelined = args.pipeline == "on"
     G = args.group
-    if G < 2 or G % 2 or args.steps % G or args.warmup % 2:
-        err("bench.py: --group must be even and divide --steps; --warmup must be even")
+    timed_graphs = not (args.counter_pass or args.serialized_only or args.overlapped_only)
+    if G < 2 or G % 2 or (timed_graphs and args.graph == "on" and args.steps % G):
+        err("bench.py: --group must be even and divide --steps")
         sys.exit(2)
     # flags of every step: the fused permute and the wgrad's place in the
     # backward stream's order (both leave the results unchanged)

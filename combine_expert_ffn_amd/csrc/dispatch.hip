@@ -40,24 +40,26 @@ __global__ __launch_bounds__(256) void plan_hist_kernel(const int32_t* __restric
 // ---------------------------------------------------------------------------
 // plan step 2: one block.  Exclusive scan of blockcnt in (expert, block) order
 // -> blockbase; counts, offsets and tile_offsets.
+// The block is 256 threads (one wave per SIMD, few registers), so that it fits
+// on a CU beside a block of a persistent expert GEMM running on the other
+// stream, instead of waiting for one to retire.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void plan_scan_kernel(const int32_t* __restrict__ blockcnt,
-                                                         int32_t* __restrict__ blockbase,
-                                                         int E_l, int NB,
-                                                         int32_t* __restrict__ counts,
-                                                         int32_t* __restrict__ offsets,
-                                                         int32_t* __restrict__ tile_offsets) {
-  __shared__ int part[1024];
+constexpr int kScanThreads = 256;
+__global__ __launch_bounds__(kScanThreads) void plan_scan_kernel(
+    const int32_t* __restrict__ blockcnt, int32_t* __restrict__ blockbase, int E_l, int NB,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ tile_offsets) {
+  __shared__ int part[kScanThreads];
   const int n = E_l * NB;
   const int tid = threadIdx.x;
-  const int per = (n + 1023) / 1024;
+  const int per = (n + kScanThreads - 1) / kScanThreads;
   const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
   int s = 0;
   for (int i = i0; i < i1; ++i) s += blockcnt[i];
   part[tid] = s;
   __syncthreads();
-  // Hillis-Steele inclusive scan over the 1024 partial sums
-  for (int o = 1; o < 1024; o <<= 1) {
+  // Hillis-Steele inclusive scan over the partial sums
+  for (int o = 1; o < kScanThreads; o <<= 1) {
     const int v = tid >= o ? part[tid - o] : 0;
     __syncthreads();
     part[tid] += v;
@@ -69,9 +71,9 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(const int32_t* __restri
     run += blockcnt[i];
   }
   __syncthreads();
-  const int total = part[1023];
+  const int total = part[kScanThreads - 1];
   // offsets[j] = blockbase[j*NB] (start of expert j's segment); offsets[E_l] = N
-  for (int j = tid; j <= E_l; j += 1024) {
+  for (int j = tid; j <= E_l; j += kScanThreads) {
     int off;
     if (j == E_l) off = total;
     else if (NB == 0) off = 0;
@@ -187,7 +189,7 @@ int launch_plan(const moe_shape* s, const int32_t* idx, int32_t* counts, int32_t
     if ((rc = check_launch("plan histogram"))) return rc;
   }
   MOE_LAUNCH("plan_scan", st,
-             plan_scan_kernel<<<1, 1024, 0, st>>>(blockcnt, blockbase, (int)s->E_l, NB, counts, offsets,
+             plan_scan_kernel<<<1, kScanThreads, 0, st>>>(blockcnt, blockbase, (int)s->E_l, NB, counts, offsets,
                                        tile_offsets));
   if ((rc = check_launch("plan scan"))) return rc;
   if (NB > 0) {
