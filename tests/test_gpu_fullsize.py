@@ -253,12 +253,16 @@ def test_overlap_equals_serialized_two_microbatch():
         close(f"dW_down A+B (expert {j})", host(net.dW_down[j])[np.ix_(I, Fc)], prev[1][0], tau)
 
 
-def test_step_graph_replay_matches_eager():
-    """Two 1F1B steps captured into one HIP graph (stream 1 forked from and
-    joined to the capture stream by the step's own events) and replayed three
+@pytest.mark.parametrize("pipelined", [False, True])
+def test_step_graph_replay_matches_eager(pipelined):
+    """G 1F1B steps captured into one HIP graph (stream 1 forked from and
+    joined to the capture stream by the steps' own events) and replayed three
     times, with eager work and synchronisation between replays: after every
     replay the micro-batch outputs and the accumulated weight gradients equal
-    those of the same steps launched eagerly, bit for bit."""
+    those of the same steps launched eagerly one by one, bit for bit.  Captured
+    either as G moe_overlap_step calls (G = 2) or as one pipelined
+    moe_overlap_steps call with the wgrad between the dgrad GEMMs (G = 4), the
+    form bench.py times."""
     w = Workload("graph_bf16", T=330, d=256, F=192, E=16, e_lo=4, E_l=8, K=4, dtype="bf16",
                  route="topk", zipf_s=1.1)
     inp = make_inputs(w, seed=3, microbatches=2)
@@ -277,18 +281,19 @@ def test_step_graph_replay_matches_eager():
         mbs = [net.mb(inp["x"], inp["dout"]), net.mb(inp["x_b"], inp["dout_b"])]
         return net, mbs
 
+    G = 4 if pipelined else 2
     s1 = torch.cuda.Stream()
-    # eager: prime, then six steps, a snapshot after every second step
+    # eager: prime, then 3 G steps, a snapshot after every G-th step
     net, mbs = fresh()
     s0 = torch.cuda.current_stream()
     net.step(mbs[0], None, s0, s1, 0)
     ref = []
-    for j in range(6):
+    for j in range(3 * G):
         net.step(mbs[(j + 1) % 2], mbs[j % 2], s0, s1, 0, M.MOE_ACCUM_DW)
-        if j % 2 == 1:
+        if j % G == G - 1:
             torch.cuda.synchronize()
             ref.append(state(net, mbs))
-    # graph: prime eagerly, capture two steps, replay three times
+    # graph: prime eagerly, capture G steps, replay three times
     net, mbs = fresh()
     net.step(mbs[0], None, s0, s1, 0)
     torch.cuda.synchronize()
@@ -297,8 +302,12 @@ def test_step_graph_replay_matches_eager():
     cap.wait_stream(s0)
     with torch.cuda.graph(g, stream=cap, capture_error_mode="thread_local"):
         c0 = torch.cuda.current_stream()
-        for j in range(2):
-            net.step(mbs[(j + 1) % 2], mbs[j % 2], c0, s1, 0, M.MOE_ACCUM_DW)
+        if pipelined:
+            M.moe_overlap_steps([net.make(mbs[(j + 1) % 2], mbs[j % 2], M.MOE_ACCUM_DW)
+                                 for j in range(G)], c0, s1, M.MOE_STEP_MID_WGRAD)
+        else:
+            for j in range(G):
+                net.step(mbs[(j + 1) % 2], mbs[j % 2], c0, s1, 0, M.MOE_ACCUM_DW)
     for r in range(3):
         g.replay()
         torch.cuda.synchronize()
