@@ -912,35 +912,48 @@ static int fwd_chain(const StepCtx& c, const moe_mb* A, hipStream_t q) {
   return fwd_combine(c, A, q);
 }
 
+// Which weight-gradient accumulation events this call has recorded.
+struct AccumOrder {
+  const MultiEvents* ev;
+  bool dwr, dw, dws;
+};
+
 // The backward chain of one micro-batch on one stream.  Each weight-gradient
-// accumulation (router dW_r, routed dW, shared dW) waits for the previous
-// step's accumulation into the same buffer (on the other stream) when
-// `prev` is set, and records its own, so the sums happen in step order.
+// accumulation (router dW_r, routed dW, shared dW) waits for the latest
+// earlier accumulation into the same buffer in this call (on either stream),
+// and records its own, so the sums happen in step order.  Only events
+// recorded in this call are waited on.
 static int bwd_chain(const StepCtx& c, const moe_mb* B, hipStream_t q, bool mid, bool eager,
-                     const MultiEvents* ev, bool prev) {
+                     AccumOrder& ord) {
   const bool shared = has_shared(c);
   const bool dwr = c.router && c.st->dW_r;
-  auto wait = [&](hipEvent_t e) -> int {
-    if (prev) HIPTRY(hipStreamWaitEvent(q, e, 0));
+  const MultiEvents* ev = ord.ev;
+  auto wait = [&](hipEvent_t e, bool recorded) -> int {
+    if (recorded) HIPTRY(hipStreamWaitEvent(q, e, 0));
     return MOE_OK;
   };
   auto routed_w = [&]() -> int {
-    TRY(wait(ev->dw));
+    TRY(wait(ev->dw, ord.dw));
     TRY(bwd_wgrad(c, B, q));
     HIPTRY(hipEventRecord(ev->dw, q));
+    ord.dw = true;
     return MOE_OK;
   };
   auto shared_w = [&]() -> int {
     if (!shared) return MOE_OK;
-    TRY(wait(ev->dws));
+    TRY(wait(ev->dws, ord.dws));
     TRY(bwd_shared_wgrad(c, B, q));
     HIPTRY(hipEventRecord(ev->dws, q));
+    ord.dws = true;
     return MOE_OK;
   };
   TRY(bwd_combine(c, B, q));
-  if (dwr) TRY(wait(ev->dwr));
+  if (dwr) TRY(wait(ev->dwr, ord.dwr));
   TRY(bwd_route(c, B, q));
-  if (dwr) HIPTRY(hipEventRecord(ev->dwr, q));
+  if (dwr) {
+    HIPTRY(hipEventRecord(ev->dwr, q));
+    ord.dwr = true;
+  }
   if (mid) {
     TRY(bwd_dgrad(c, B, false, q, kDgradAct));
     TRY(routed_w());
@@ -997,7 +1010,7 @@ extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, h
   const bool fused = (flags & MOE_STEP_FUSED_PERMUTE) != 0;
   HIPTRY(hipEventRecord(ev->start, s0));
   HIPTRY(hipStreamWaitEvent(s1, ev->start, 0));
-  bool prev_b = false;  // the previous step of this call had a backward
+  AccumOrder ord{ev, false, false, false};
   for (int j = 0; j < n; ++j) {
     const moe_step* st = &steps[j];
     const moe_shape* s = &st->shape;
@@ -1020,8 +1033,7 @@ extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, h
               st->route_mode == MOE_ROUTE_TOPK, fused,
               even ? shalf_s1 : shalf_s0, even ? shalf_s0 : shalf_s1};
     if (st->fwd) TRY(fwd_chain(c, st->fwd, P));
-    if (st->bwd) TRY(bwd_chain(c, st->bwd, Q, mid, eager, ev, prev_b));
-    prev_b = st->bwd != nullptr;
+    if (st->bwd) TRY(bwd_chain(c, st->bwd, Q, mid, eager, ord));
   }
   HIPTRY(hipEventRecord(ev->end, s1));
   HIPTRY(hipStreamWaitEvent(s0, ev->end, 0));

@@ -410,7 +410,8 @@ int moe_overlap_step(const moe_step* st, hipStream_t s_compute, hipStream_t s_co
  * micro-batch back-propagated in the step before.  Each stream owns one half of
  * the workspace.  The only other cross-stream waits order the weight-gradient
  * sums (dW_r, dW_gu/dW_down, the shared expert's): each step's sum into a
- * buffer waits for the previous step's, so every sum happens in step order.
+ * buffer waits for the latest earlier sum into it in the same call, on either
+ * stream, so every sum happens in step order.
  * Flags as moe_overlap_step, except MOE_STEP_SKIP_WGRAD (rejected: the wgrad's
  * stream alternates).  Results are bit-identical to n moe_overlap_step calls
  * with MOE_STEP_SERIALIZE.  s_copy forks from s_compute at the start and joins

@@ -680,3 +680,61 @@ def test_multi_step_pipelined_equals_serialized(name, shared, flags):
     if shared:
         assert torch.equal(sa[2], sb[2]) and torch.equal(sa[3], sb[3])
     log(f"[multi-step] {name}: bit-identical")
+
+
+@pytest.mark.parametrize("name,shared", [("zipf_window_bf16", False), ("fb_ragged_bf16", True)])
+def test_multi_step_gapped_chain(name, shared):
+    """A pipelined chain whose backwards are not in consecutive steps: step 1
+    back-propagates on one stream, steps 2 and 3 have none, step 4
+    back-propagates on the other stream.  Step 4's weight-gradient sums must
+    still follow step 1's: results bit-identical to the steps serialized."""
+    w = SMALL[name]
+    prec = w.dtype
+    log(f"[multi-step gaps] {name}: shared={shared}")
+    inp = make_inputs(w, seed=1, microbatches=2)
+    s = M.shape_of(w)
+    D = lambda a: dev(a, prec)
+    topk = w.route == "topk"
+    mode = M.MOE_ROUTE_TOPK if topk else M.MOE_ROUTE_FORCE_BALANCE
+    Fs = 128 if shared else 0
+    rng = np.random.default_rng(7)
+    Wgu_s = D(O.store(0.05 * rng.standard_normal((2 * Fs, w.d)), prec)) if shared else None
+    Wd_s = D(O.store(0.05 * rng.standard_normal((w.d, Fs)), prec)) if shared else None
+    W_gu, W_down = D(inp["W_gu"]), D(inp["W_down"])
+    W_r = D(inp["W_r"]) if topk else None
+    bias = dev(inp["bias"], "f32x") if inp["bias"] is not None else None
+    s0 = torch.cuda.current_stream()
+    s1 = torch.cuda.Stream()
+    res = {}
+    for tag in ("serial", "pipelined"):
+        m = [M.MicroBatch(s, x=D(inp[xk]), dout=D(inp[dk]),
+                          gates=None if topk else dev(inp[gk], "f32x"), F_s=Fs)
+             for xk, dk, gk in (("x", "dout", "gates"), ("x_b", "dout_b", "gates_b"))]
+        dW = (torch.full((w.E_l, 2 * w.F, w.d), 0.5, device="cuda"),
+              torch.full((w.E_l, w.d, w.F), 0.5, device="cuda"),
+              torch.full((w.d, w.E), 0.5, device="cuda") if topk else None)
+        sh = (Wgu_s, Wd_s, torch.full((2 * Fs, w.d), 0.5, device="cuda"),
+              torch.full((w.d, Fs), 0.5, device="cuda")) if shared else None
+        ws = torch.empty(M.moe_step_workspace_bytes_shared(s, Fs), dtype=torch.uint8,
+                         device="cuda")
+        plan = [(m[0], None), (None, m[0]), (None, None), (m[1], None), (None, m[1])]
+        steps = [M.make_step(s, mode, W_gu, W_down, dW[0], dW[1], ws, fwd=f, bwd=b, W_r=W_r,
+                             bias=bias, dW_r=dW[2], accumulate=M.MOE_ACCUM_DW, shared=sh)
+                 for f, b in plan]
+        if tag == "serial":
+            for st in steps:
+                M.moe_overlap_step(st, s0, s0, M.MOE_STEP_MID_WGRAD | M.MOE_STEP_SERIALIZE)
+        else:
+            M.moe_overlap_steps(steps, s0, s1, M.MOE_STEP_MID_WGRAD)
+        torch.cuda.synchronize()
+        res[tag] = (m, dW, sh)
+    (ma, ga, sa), (mb, gb, sb) = res["serial"], res["pipelined"]
+    for i in range(2):
+        for k in ("out", "dx", "dgates"):
+            assert torch.equal(getattr(mb[i], k), getattr(ma[i], k)), (i, k)
+    for k, (a, b) in enumerate(zip(ga, gb)):
+        if a is not None:
+            assert torch.equal(a, b), ("dW", k)
+    if shared:
+        assert torch.equal(sa[2], sb[2]) and torch.equal(sa[3], sb[3])
+    log(f"[multi-step gaps] {name}: bit-identical")
