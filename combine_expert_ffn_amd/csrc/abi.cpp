@@ -993,6 +993,13 @@ extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, h
       return set_error(MOE_ERR_ARG,
                        "moe_overlap_steps: step %d forwards and back-propagates the same "
                        "micro-batch", j);
+    // each stream owns a fixed half of the one workspace, laid out by the shape
+    if (j > 0 && (memcmp(&st->shape, &steps[0].shape, sizeof(moe_shape)) != 0 ||
+                  st->ws != steps[0].ws || st->ws_bytes != steps[0].ws_bytes ||
+                  st->F_s != steps[0].F_s))
+      return set_error(MOE_ERR_ARG,
+                       "moe_overlap_steps: step %d differs from step 0 in shape, workspace or "
+                       "shared-expert width", j);
     if (j > 0 && !same_mb(st->bwd, steps[j - 1].fwd))
       return set_error(MOE_ERR_ARG,
                        "moe_overlap_steps: step %d must back-propagate the micro-batch that "

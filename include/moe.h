@@ -398,9 +398,11 @@ int moe_overlap_step(const moe_step* st, hipStream_t s_compute, hipStream_t s_co
  * moe_overlap_steps - n consecutive steps of the 1F1B schedule (1F1B note
  * page 2, "MoE 1F1B overlap": the micro-batch forwarded in one step is
  * back-propagated in the next), pipelined across the step boundaries.
- * steps[j] describes step j as for moe_overlap_step; for j >= 1, steps[j].bwd
- * must hold the same buffers as steps[j-1].fwd (field by field; both may be
- * NULL), and no step may forward and back-propagate the same buffers.
+ * steps[j] describes step j as for moe_overlap_step; all steps share one shape,
+ * one workspace (ws, ws_bytes) and one shared-expert width F_s; for j >= 1,
+ * steps[j].bwd must hold the same buffers as steps[j-1].fwd (field by field;
+ * both may be NULL), and no step may forward and back-propagate the same
+ * buffers.
  * The streams' roles alternate: step j runs its forward chain on s_copy when j
  * is even and on s_compute when j is odd, and its backward chain on the other
  * stream (each chain in moe_overlap_step's order, the shared expert's forward
@@ -418,8 +420,8 @@ int moe_overlap_step(const moe_step* st, hipStream_t s_compute, hipStream_t s_co
  * it at the end, so on return work on s_compute depends on everything the call
  * issued; the call may be captured into a HIP graph on s_compute.  Errors: as
  * moe_overlap_step (checked for every step before anything is launched), and
- * MOE_ERR_ARG for n < 1, a step whose bwd is not the previous step's fwd, or
- * SKIP_WGRAD.
+ * MOE_ERR_ARG for n < 1, a step whose bwd is not the previous step's fwd, steps
+ * with different shapes, workspaces or F_s, or SKIP_WGRAD.
  */
 int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s_compute, hipStream_t s_copy,
                       int flags);

@@ -253,3 +253,11 @@ def test_multi_step_rejects_bad_chains():
     assert run([step(m1, m2)], M.MOE_STEP_MID_WGRAD | M.MOE_STEP_EAGER_WGRAD) == M.MOE_ERR_ARG
     # a later step's small workspace is found before anything runs
     assert run([step(m1, m2), step(m2, m1, ws_bytes=8)]) == M.MOE_ERR_WORKSPACE
+    # the streams' workspace halves are laid out once: every step shares the shape
+    other = step(m2, m1)
+    other.shape.T = s.T * 2
+    assert run([step(m1, m2), other]) == M.MOE_ERR_ARG
+    assert b"differs from step 0" in L.moe_last_error()
+    other = step(m2, m1)
+    other.ws = 0x2000
+    assert run([step(m1, m2), other]) == M.MOE_ERR_ARG
