@@ -749,13 +749,19 @@ __device__ __forceinline__ long long uniform64(long long v) {
 // dW_gu tiles read dispatched row r from token xrows[r] / K: the token rows of
 // stage k are looked up one stage ahead into an LDS list (s_tok, double
 // buffered), from which the next stage's loads take their addresses.
-template <bool GATHER, class E>
+//
+// ROUTER reuses the kernel for the router weight gradient: the "experts" are
+// chunks of rchunk tokens (chunk c = rows [c rchunk, min((c+1) rchunk, rows))),
+// only the first product is formed, dyp holds x [T][d], abuf holds the split
+// dlogits [T][F] (F = 2E) and dW_down receives one float32 partial [d][F] per
+// chunk; offsets, xp, dh and dW_gu are unused.
+template <bool GATHER, class E, bool ROUTER = false>
 __global__ __launch_bounds__(512) void wgrad_kernel(
     const uint16_t* __restrict__ xp, const int32_t* __restrict__ xrows, int K,
     const uint16_t* __restrict__ abuf, const uint16_t* __restrict__ dh,
     const uint16_t* __restrict__ dyp, const int32_t* __restrict__ offsets,
     float* __restrict__ dW_gu, float* __restrict__ dW_down, int E_l, int d, int F,
-    int accumulate) {
+    int accumulate, int rchunk = 0, int rows = 0) {
   constexpr int NW = 8, WGN = 4, WTM = 128, WTN = 64, TM = 4, TN = 2;
   constexpr int STAGE = 2 * BK * WG_ROWB;  // A + B tiles
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
@@ -763,7 +769,9 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
   __shared__ int s_tok[GATHER ? 2 : 1][BK];  // source token rows of the next two stages
   const int tdm = (d + 255) / 256, tdn = (F + 255) / 256;
   const int tgm = (2 * F + 255) / 256, tgn = (d + 255) / 256;
-  const int per_e = tdm * tdn + tgm * tgn;
+  const int per_e = tdm * tdn + (ROUTER ? 0 : tgm * tgn);
+  // first row of expert (or token chunk) e
+  auto off = [&](int e) { return ROUTER ? min(e * rchunk, rows) : offsets[e]; };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   // Work-balanced schedule: a tile costs nk_e = max(1, ceil(rows_e / 64))
@@ -776,7 +784,7 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
     long long acc_it = 0;
     for (int e = 0; e < E_l; ++e) {
       s_it[e] = acc_it;
-      const int nk = (offsets[e + 1] - offsets[e] + BK - 1) / BK;
+      const int nk = (off(e + 1) - off(e) + BK - 1) / BK;
       acc_it += (long long)per_e * (nk > 0 ? nk : 1);
     }
     s_it[E_l] = acc_it;
@@ -807,7 +815,7 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
       const long long nk_e = (uniform64(s_it[e + 1]) - it0) / per_e;
       if (it0 + t * nk_e >= hi) break;  // uniform
     }
-    const int r0 = offsets[e], r1 = offsets[e + 1];
+    const int r0 = off(e), r1 = off(e + 1);
     const uint16_t *Asrc, *Bsrc;
     int M, N, m0, n0;
     float* out;
@@ -1140,6 +1148,21 @@ int launch_ffn_wgrad_mfma(const moe_shape* s, const void* xp, const int32_t* xro
   else
     wgrad_t<BF16>(s, xp, xrows, a, dh, dyp, offsets, dW_gu, dW_down, accumulate, st);
   return check_launch("wgrad GEMM");
+}
+
+int launch_router_wgrad_mfma(const moe_shape* s, const void* x, const void* dl_split,
+                             float* partial, hipStream_t st) {
+  const int d = (int)s->d, N = 2 * (int)s->E, T = (int)s->T;
+  const int chunk = (int)router_mfma_chunk(s->T);
+  const int nchunks = (int)cdiv(s->T, chunk);
+  const long tiles = (long)nchunks * ((d + 255) / 256) * ((N + 255) / 256);
+  if (tiles == 0) return MOE_OK;
+  const int grid = persistent_grid(tiles);
+  MOE_LAUNCH("dwr_mfma", st,
+             (wgrad_kernel<false, BF16, true><<<grid, 512, 0, st>>>(
+                 nullptr, nullptr, 0, (const uint16_t*)dl_split, nullptr, (const uint16_t*)x,
+                 nullptr, nullptr, partial, nchunks, d, N, 0, chunk, T)));
+  return check_launch("router dW_r GEMM");
 }
 
 int launch_router_logits_mfma(const moe_shape* s, const void* x, const void* W_rT,

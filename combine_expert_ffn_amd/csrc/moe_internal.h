@@ -151,9 +151,24 @@ inline size_t ws_plan_bytes(const moe_shape* s) {
 inline size_t ws_wrt_bytes(const moe_shape* s) {
   return align_up((size_t)(s->E * s->d) * elt_bytes(s), 256);
 }
+// The 16-bit router weight gradient on the matrix cores (bf16 data): dlogits
+// as two bf16 terms per value (hi | lo, [T][2E]), and per chunk of
+// router_mfma_chunk(T) tokens a float32 partial [d][2E] of x^T [hi | lo].
+inline int64_t router_mfma_chunk(int64_t T) {
+  const int64_t c = align_up((size_t)cdiv(T, 32), 64);
+  return c > kRouterChunk ? c : kRouterChunk;
+}
+inline size_t ws_router_split_bytes(const moe_shape* s) {
+  return align_up((size_t)(s->T * 2 * s->E) * 2, 256);
+}
 inline size_t ws_router_partial_bytes(const moe_shape* s) {
-  int64_t nc = cdiv(s->T, kRouterChunk);
-  return align_up((size_t)(nc * s->d * s->E) * sizeof(float), 256);
+  const int64_t nc = cdiv(s->T, kRouterChunk);
+  const size_t valu = align_up((size_t)(nc * s->d * s->E) * sizeof(float), 256);
+  if (s->dtype != MOE_BF16) return valu;
+  const int64_t nm = cdiv(s->T, router_mfma_chunk(s->T));
+  const size_t mfma =
+      ws_router_split_bytes(s) + align_up((size_t)(nm * s->d * 2 * s->E) * sizeof(float), 256);
+  return mfma > valu ? mfma : valu;
 }
 // Transposed expert weights for the 16-bit dgrad: W_downT [E_l][F][d] then
 // W_guT [E_l][d][2F].  The float32 dgrad needs none.  They sit after

@@ -65,6 +65,8 @@ __global__ __launch_bounds__(256) void router_logits_f32_kernel(const float* __r
 
 int launch_router_logits_mfma(const moe_shape* s, const void* x, const void* W_rT,
                               const float* bias, float* logits, hipStream_t st);
+int launch_router_wgrad_mfma(const moe_shape* s, const void* x, const void* dl_split,
+                             float* partial, hipStream_t st);
 
 int launch_router_logits(const moe_shape* s, const void* x, const void* W_r, const void* W_rT,
                          const float* bias, float* logits, hipStream_t st) {
@@ -164,10 +166,14 @@ int launch_force_balance(const moe_shape* s, int32_t* idx, hipStream_t st) {
 // dlogits: one wave per token; lane k < K holds slot k.  Every lane writes its
 // own logits' final value once (0 unless selected).
 // ---------------------------------------------------------------------------
+// With split set, dlogits is also written as two bf16 terms, split[t][e] =
+// hi = bf16(v) and split[t][E + e] = lo = bf16(v - hi), for the matrix-core
+// weight gradient (hi + lo carries about 16 significant bits of v).
 __global__ __launch_bounds__(256) void dlogits_kernel(const float* __restrict__ dgates,
                                                       const float* __restrict__ gates,
                                                       const int32_t* __restrict__ idx,
-                                                      float* __restrict__ dlogits, int T, int E,
+                                                      float* __restrict__ dlogits,
+                                                      uint16_t* __restrict__ split, int T, int E,
                                                       int K) {
   const int t = (int)(((long)blockIdx.x * 256 + threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
@@ -190,7 +196,14 @@ __global__ __launch_bounds__(256) void dlogits_kernel(const float* __restrict__ 
       const float dk = __shfl(dsel, k, 64);
       if (ek == e) val += dk;
     }
-    if (e < E) out[e] = val;
+    if (e < E) {
+      out[e] = val;
+      if (split) {
+        const uint16_t hi = f2bf(val);
+        split[(size_t)t * 2 * E + e] = hi;
+        split[(size_t)t * 2 * E + E + e] = f2bf(val - bf2f(hi));
+      }
+    }
   }
 }
 
@@ -247,6 +260,24 @@ __global__ __launch_bounds__(256) void dwr_partial_kernel(const T* __restrict__ 
   }
 }
 
+// dW_r from the matrix-core partials: partial[c][i][f], f < 2E, of chunk c;
+// dW_r[i][e] = [dW_r] + sum_c (partial[c][i][e] + partial[c][i][E + e]) in
+// chunk order.
+__global__ __launch_bounds__(256) void dwr_reduce_split_kernel(const float* __restrict__ partial,
+                                                               float* __restrict__ dW_r, int d,
+                                                               int E, int nchunks,
+                                                               int accumulate) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long)d * E) return;
+  const long row = i / E, e = i % E;
+  float acc = accumulate ? dW_r[i] : 0.f;
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const float* p = partial + ((size_t)ch * d + row) * 2 * E;
+    acc += p[e] + p[E + e];
+  }
+  dW_r[i] = acc;
+}
+
 __global__ __launch_bounds__(256) void dwr_reduce_kernel(const float* __restrict__ partial,
                                                          float* __restrict__ dW_r, long n,
                                                          int nchunks, int accumulate) {
@@ -260,14 +291,28 @@ __global__ __launch_bounds__(256) void dwr_reduce_kernel(const float* __restrict
 int launch_route_bwd(const moe_shape* s, const float* dgates, const float* gates,
                      const int32_t* idx, const void* x, float* dlogits, float* dW_r,
                      bool accumulate, void* ws, hipStream_t st) {
+  // bf16 data: dW_r = x^T dlogits on the matrix cores from a two-term bf16
+  // split of dlogits (the workspace holds the split, then the partials)
+  const bool mfma = x && dW_r && s->dtype == MOE_BF16 && s->T > 0;
+  uint16_t* split = mfma ? (uint16_t*)ws : nullptr;
   if (s->T > 0) {
     MOE_LAUNCH("dlogits", st,
-               dlogits_kernel<<<(unsigned)cdiv(s->T, 4), 256, 0, st>>>(dgates, gates, idx, dlogits,
-                                                            (int)s->T, (int)s->E, (int)s->K));
+               dlogits_kernel<<<(unsigned)cdiv(s->T, 4), 256, 0, st>>>(
+                   dgates, gates, idx, dlogits, split, (int)s->T, (int)s->E, (int)s->K));
     int rc = check_launch("router dlogits");
     if (rc) return rc;
   }
   if (!x || !dW_r) return MOE_OK;
+  if (mfma) {
+    float* partial = (float*)((char*)ws + ws_router_split_bytes(s));
+    if (int rc = launch_router_wgrad_mfma(s, x, split, partial, st)) return rc;
+    const int nchunks = (int)cdiv(s->T, router_mfma_chunk(s->T));
+    const long n = s->d * s->E;
+    MOE_LAUNCH("dwr_reduce", st,
+               dwr_reduce_split_kernel<<<(unsigned)cdiv(n, 256), 256, 0, st>>>(
+                   partial, dW_r, (int)s->d, (int)s->E, nchunks, accumulate ? 1 : 0));
+    return check_launch("router dW_r reduce");
+  }
   const int nchunks = (int)cdiv(s->T, kRouterChunk);
   float* partial = (float*)ws;
   if (nchunks > 0) {

@@ -255,6 +255,11 @@ int moe_ffn_wgrad_gather(const moe_shape* s, const void* x, const int32_t* pair_
  *   dlogits[t, idx[t,j]] = g_j * (dg_j - sum_k g_k dg_k); other logits 0.  [T,E] f32
  *   dW_r = x^T . dlogits  [d,E] f32 (skipped when x or dW_r is NULL; with
  *   accumulate & MOE_ACCUM_DW added to the existing value)
+ * With bf16 data, dW_r runs on the matrix cores: dlogits is split into two
+ * bf16 terms per value (hi = bf16(v), lo = bf16(v - hi), about 16 significant
+ * bits together), each chunk of tokens gives a float32 partial of x^T [hi|lo],
+ * and the partials are summed in a fixed order (deterministic).  fp16 and f32
+ * data use float32 vector arithmetic.
  */
 int moe_route_bwd(const moe_shape* s, int mode, const float* dgates,
                   const float* gates, const int32_t* idx, const void* x,

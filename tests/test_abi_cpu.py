@@ -80,7 +80,9 @@ def test_all_three_dtypes_accepted():
         # validation passes the shape and stops at the first NULL pointer
         assert M.lib().moe_combine(C.byref(s), None, FAKE, FAKE, FAKE, None) == M.MOE_ERR_NULL
     # the 16-bit types both need the transposed-weight workspace of the dgrad
-    assert M.moe_workspace_bytes(_shape(dtype="f16")) == M.moe_workspace_bytes(_shape(dtype="bf16"))
+    # bf16's router weight gradient runs on the matrix cores and also holds the
+    # split dlogits and per-chunk partials of [d, 2E]; fp16 needs no more than that
+    assert M.moe_workspace_bytes(_shape(dtype="f16")) <= M.moe_workspace_bytes(_shape(dtype="bf16"))
 
 
 def test_null_pointers_rejected():

@@ -150,7 +150,9 @@ def sampled_check(w, inp, A, net, rng, nrows=192, ntok=96, wgrad_prev=None):
 
 
 @pytest.mark.parametrize("name,T", [("ep16_rank_bf16", None), ("ep8_rank_zipf_bf16", None),
-                                    ("ep1_128exp_bf16", 16384), ("ep16_rank_f16", None)])
+                                    ("ep1_128exp_bf16", 16384), ("ep16_rank_f16", None),
+                                    # the size that matches the 524288 dispatched rows
+                                    ("ep1_128exp_bf16", 65536)])
 def test_fullsize_sampled(name, T):
     w = WORKLOADS[name] if T is None else WORKLOADS[name].with_tokens(T)
     log(f"[full size] {name}: T={w.T} d={w.d} F={w.F} E={w.E} E_l={w.E_l} K={w.K}")

@@ -738,3 +738,35 @@ def test_multi_step_gapped_chain(name, shared):
     if shared:
         assert torch.equal(sa[2], sb[2]) and torch.equal(sa[3], sb[3])
     log(f"[multi-step gaps] {name}: bit-identical")
+
+
+def test_router_weight_grad_split_precision():
+    """bf16 dW_r runs on the matrix cores from dlogits split into two bf16 terms.
+    Against float64 x^T dlogits computed from the GPU's own float32 dlogits, the
+    error must stay near float32 rounding (a single bf16 term would be ~1e-3 of
+    the largest entry); with accumulate the previous value is added once."""
+    w = Workload("router_split_bf16", T=4096, d=256, F=64, E=64, e_lo=0, E_l=8, K=6,
+                 dtype="bf16", route="topk")
+    log(f"[router split] T={w.T} d={w.d} E={w.E} K={w.K}")
+    rng = np.random.default_rng(5)
+    s = M.shape_of(w)
+    x_h = O.store(rng.standard_normal((w.T, w.d)), "bf16")
+    logits = rng.standard_normal((w.T, w.E)).astype(np.float32)
+    idx_h, gates_h = O.topk_route(logits.astype(np.float64), w.K, "bf16")
+    dgates_h = rng.standard_normal((w.T, w.K)).astype(np.float32)
+    x = dev(x_h, "bf16")
+    idx, gates, dgates = dev(idx_h, "i32"), dev(gates_h, "f32x"), dev(dgates_h, "f32x")
+    dlogits = torch.empty(w.T, w.E, device="cuda")
+    dW_r = torch.empty(w.d, w.E, device="cuda")
+    ws = torch.empty(M.moe_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    M.moe_route_bwd(s, M.MOE_ROUTE_TOPK, dgates, gates, idx, x, dlogits, dW_r, 0, ws)
+    torch.cuda.synchronize()
+    ref = x_h.astype(np.float64).T @ host(dlogits)
+    err = np.abs(host(dW_r) - ref).max() / np.abs(ref).max()
+    log(f"[router split] max |err| / max |ref| = {err:.2e}")
+    assert err < 5e-4, err
+    prev = dW_r.clone()
+    M.moe_route_bwd(s, M.MOE_ROUTE_TOPK, dgates, gates, idx, x, dlogits, dW_r,
+                    M.MOE_ACCUM_DW, ws)
+    torch.cuda.synchronize()
+    assert torch.allclose(dW_r, 2 * prev, rtol=1e-5, atol=1e-6)
