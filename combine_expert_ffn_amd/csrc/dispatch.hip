@@ -49,42 +49,80 @@ __global__ __launch_bounds__(kScanThreads) void plan_scan_kernel(
     const int32_t* __restrict__ blockcnt, int32_t* __restrict__ blockbase, int E_l, int NB,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ tile_offsets) {
-  __shared__ int part[kScanThreads];
+  constexpr int NW = kScanThreads / 64;
+  __shared__ int wsum[NW];
+  __shared__ int s_off[257];  // E_l <= 256
   const int n = E_l * NB;
-  const int tid = threadIdx.x;
-  const int per = (n + kScanThreads - 1) / kScanThreads;
-  const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // wave w scans the contiguous range [b0, b1) (b0 a multiple of 256), 256
+  // entries per step: lane l takes entries 4l .. 4l + 3 of the step (one
+  // 16-byte load when all four are in range)
+  const int per = ((n + NW - 1) / NW + 255) / 256 * 256;
+  const int b0 = min(n, w * per), b1 = min(n, b0 + per);
+  // the caller's workspace carries no alignment promise: vector loads only
+  // when its base is 16-byte aligned (wave-uniform)
+  const bool vec = ((uintptr_t)blockcnt & 15) == 0;
+  auto load4 = [&](int i, int (&v)[4]) {
+    if (vec && i + 3 < b1) {
+      const int4 q = *(const int4*)(blockcnt + i);
+      v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = i + k < b1 ? blockcnt[i + k] : 0;
+    }
+  };
   int s = 0;
-  for (int i = i0; i < i1; ++i) s += blockcnt[i];
-  part[tid] = s;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the partial sums
-  for (int o = 1; o < kScanThreads; o <<= 1) {
-    const int v = tid >= o ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+#pragma unroll 2
+  for (int c = b0; c < b1; c += 256) {
+    int v[4];
+    load4(c + 4 * lane, v);
+    s += v[0] + v[1] + v[2] + v[3];
   }
-  int run = part[tid] - s;  // exclusive prefix of this thread's segment
-  for (int i = i0; i < i1; ++i) {
-    blockbase[i] = run;
-    run += blockcnt[i];
-  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  if (lane == 0) wsum[w] = s;
   __syncthreads();
-  const int total = part[kScanThreads - 1];
-  // offsets[j] = blockbase[j*NB] (start of expert j's segment); offsets[E_l] = N
-  for (int j = tid; j <= E_l; j += kScanThreads) {
-    int off;
-    if (j == E_l) off = total;
-    else if (NB == 0) off = 0;
-    else off = blockbase[(size_t)j * NB];
-    offsets[j] = off;
+  int carry = 0, total = 0;
+#pragma unroll
+  for (int u = 0; u < NW; ++u) {
+    if (u < w) carry += wsum[u];
+    total += wsum[u];
   }
+  // exclusive prefix: per lane over its four entries, then a wave inclusive
+  // scan of the lane sums and the running carry; the start of expert j's
+  // segment (entry j * NB) goes to LDS
+  for (int c = b0; c < b1; c += 256) {
+    const int i = c + 4 * lane;
+    int v[4];
+    load4(i, v);
+    const int t = v[0] + v[1] + v[2] + v[3];
+    int incl = t;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += u;
+    }
+    int ex = carry + incl - t;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (i + k < b1) {
+        blockbase[i + k] = ex;
+        if ((i + k) % NB == 0) s_off[(i + k) / NB] = ex;
+      }
+      ex += v[k];
+    }
+    carry += __shfl(incl, 63, 64);
+  }
+  if (tid == 0) s_off[E_l] = total;
+  if (NB == 0)
+    for (int j = tid; j < E_l; j += kScanThreads) s_off[j] = 0;
   __syncthreads();
+  // offsets[j] = start of expert j's segment; offsets[E_l] = N
+  for (int j = tid; j <= E_l; j += kScanThreads) offsets[j] = s_off[j];
   if (tid == 0) {
     int acc = 0;
     for (int j = 0; j < E_l; ++j) {
-      const int c = offsets[j + 1] - offsets[j];
+      const int c = s_off[j + 1] - s_off[j];
       counts[j] = c;
       if (tile_offsets) tile_offsets[j] = acc;
       acc += (c + kTileM - 1) / kTileM;
