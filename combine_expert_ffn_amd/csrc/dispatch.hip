@@ -146,11 +146,13 @@ __global__ __launch_bounds__(256) void plan_rank_kernel(const int32_t* __restric
                                                         int32_t* __restrict__ pair_of_row) {
   __shared__ int running[256];
   __shared__ int wcnt[4][256];
+  __shared__ unsigned long long wmask[4][256];  // lanes of wave w holding expert j
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   for (int j = tid; j < E_l; j += 256) {
     running[j] = blockbase[(size_t)j * NB + b];
     wcnt[0][j] = wcnt[1][j] = wcnt[2][j] = wcnt[3][j] = 0;
+    wmask[0][j] = wmask[1][j] = wmask[2][j] = wmask[3][j] = 0ull;
   }
   __syncthreads();
   const long p0 = (long)b * kPlanChunk;
@@ -163,15 +165,18 @@ __global__ __launch_bounds__(256) void plan_rank_kernel(const int32_t* __restric
       const int jj = idx[p] - e_lo;
       if (jj >= 0 && jj < E_l) j = jj;
     }
-    unsigned long long active = __ballot(j >= 0);
+    // stable rank among the wave's lanes with the same expert: each lane sets
+    // its bit in its expert's mask, reads the mask back (the LDS operations of
+    // one wave complete in order) and counts the lower lanes, then the mask is
+    // cleared for the next round; constant work however many experts the wave
+    // holds
     int myrank = 0;
-    while (active) {  // wave-uniform loop: one pass per distinct expert in the wave
-      const int leader = __ffsll((long long)active) - 1;
-      const int jl = __shfl(j, leader, 64);
-      const unsigned long long m = __ballot(j == jl);
-      if (j == jl) myrank = __popcll(m & lt_mask);
-      if (lane == leader) wcnt[w][jl] = __popcll(m);
-      active &= ~m;
+    if (j >= 0) {
+      atomicOr(&wmask[w][j], 1ull << lane);
+      const unsigned long long m = wmask[w][j];
+      myrank = __popcll(m & lt_mask);
+      wcnt[w][j] = __popcll(m);
+      wmask[w][j] = 0ull;
     }
     __syncthreads();
     if (p < p1) {
