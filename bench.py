@@ -47,6 +47,9 @@ def algorithmic(w, N, T_loc):
         "dgrad_in": ("flop", 2.0 * N * 2 * F * d + 2.0 * T * 2 * Fs * d),
         "wgrad": ("flop", 6.0 * N * d * F + 6.0 * T * d * Fs),
         "router": ("flop", 2.0 * T * d * E),
+        # router weight gradient x^T dlogits on the matrix cores (bf16 data);
+        # the two-term split of dlogits forms it twice, counted once here
+        "dwr_mfma": ("flop", 2.0 * T * d * E),
         # x rows of tokens with a local expert + row map -> N rows
         "permute": ("byte", T_loc * d * b + 4.0 * T * K + N * d * b),
         # y_p rows + gates + row map -> out
