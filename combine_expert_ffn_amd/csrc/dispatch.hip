@@ -627,20 +627,44 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(
       }
     }
     if (dlogits) {
-      for (int k = 0; k < K; ++k) {
-        const int e = idx[(size_t)t * K + k];
-        if (e < 0 || e >= E) continue;
-        const float gl = dlogits[(size_t)t * E + e];
-        const uint4* wr = W_rT + (size_t)e * nch;
-        uint4 wv[MAXC];
+      // two slots per pass: both W_r rows are loaded before the first FMA;
+      // the terms are still added in slot order, and a slot whose expert is
+      // out of range is skipped (uniform: one token per wave)
+      for (int k = 0; k < K; k += 2) {
+        const int e0 = idx[(size_t)t * K + k];
+        const int e1 = k + 1 < K ? idx[(size_t)t * K + k + 1] : -1;
+        const bool ok0 = e0 >= 0 && e0 < E, ok1 = e1 >= 0 && e1 < E;
+        const uint4* w0 = W_rT + (size_t)(ok0 ? e0 : 0) * nch;
+        const uint4* w1 = W_rT + (size_t)(ok1 ? e1 : 0) * nch;
+        uint4 wv0[MAXC], wv1[MAXC];
 #pragma unroll
-        for (int i = 0; i < MAXC; ++i) wv[i] = wr[cc[i]];
+        for (int i = 0; i < MAXC; ++i) wv0[i] = w0[cc[i]];
+#pragma unroll
+        for (int i = 0; i < MAXC; ++i) wv1[i] = w1[cc[i]];
 #pragma unroll
         for (int i = 0; i < MAXC; ++i) {
-          float f[CN];
-          Chunk<T>::unpack(wv[i], f);
+          pin(wv0[i]);
+          pin(wv1[i]);
+        }
+        if (ok0) {
+          const float gl = dlogits[(size_t)t * E + e0];
 #pragma unroll
-          for (int q = 0; q < CN; ++q) acc[i][q] = fmaf(gl, f[q], acc[i][q]);
+          for (int i = 0; i < MAXC; ++i) {
+            float f[CN];
+            Chunk<T>::unpack(wv0[i], f);
+#pragma unroll
+            for (int q = 0; q < CN; ++q) acc[i][q] = fmaf(gl, f[q], acc[i][q]);
+          }
+        }
+        if (ok1) {
+          const float gl = dlogits[(size_t)t * E + e1];
+#pragma unroll
+          for (int i = 0; i < MAXC; ++i) {
+            float f[CN];
+            Chunk<T>::unpack(wv1[i], f);
+#pragma unroll
+            for (int q = 0; q < CN; ++q) acc[i][q] = fmaf(gl, f[q], acc[i][q]);
+          }
         }
       }
     }
