@@ -877,6 +877,7 @@ namespace moe {
 
 struct MultiEvents {
   hipEvent_t start, end, dwr, dw, dws;
+  hipEvent_t bend[2];  // end of the backward chain of the steps of each parity
 };
 
 // One set per (host thread, device), as step_events; every wait of a call is
@@ -888,7 +889,7 @@ static int multi_events(MultiEvents** out) {
   if ((int)sets.size() <= dev) sets.resize(dev + 1, nullptr);
   if (!sets[dev]) {
     MultiEvents* e = new MultiEvents();
-    hipEvent_t* all[] = {&e->start, &e->end, &e->dwr, &e->dw, &e->dws};
+    hipEvent_t* all[] = {&e->start, &e->end, &e->dwr, &e->dw, &e->dws, &e->bend[0], &e->bend[1]};
     for (hipEvent_t* p : all)
       if (hipEventCreateWithFlags(p, hipEventDisableTiming) != hipSuccess)
         return set_error(MOE_ERR_HIP, "hipEventCreateWithFlags failed");
@@ -1018,6 +1019,7 @@ extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, h
   HIPTRY(hipEventRecord(ev->start, s0));
   HIPTRY(hipStreamWaitEvent(s1, ev->start, 0));
   AccumOrder ord{ev, false, false, false};
+  bool bend_rec[2] = {false, false};  // bend[p] recorded in this call
   for (int j = 0; j < n; ++j) {
     const moe_step* st = &steps[j];
     const moe_shape* s = &st->shape;
@@ -1039,8 +1041,20 @@ extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, h
     StepCtx c{st, s, even ? half_s1 : half_s0, even ? half_s0 : half_s1,
               st->route_mode == MOE_ROUTE_TOPK, fused,
               even ? shalf_s1 : shalf_s0, even ? shalf_s0 : shalf_s1};
-    if (st->fwd) TRY(fwd_chain(c, st->fwd, P));
-    if (st->bwd) TRY(bwd_chain(c, st->bwd, Q, mid, eager, ord));
+    // The forward of step j also waits for the backward of step j - 2 (on
+    // the other stream), the last earlier chain not ordered before it by its
+    // stream, so a forward may reuse the buffers of any micro-batch
+    // back-propagated in an earlier step.  That backward has normally ended
+    // long before.
+    if (st->fwd) {
+      if (bend_rec[j & 1]) HIPTRY(hipStreamWaitEvent(P, ev->bend[j & 1], 0));
+      TRY(fwd_chain(c, st->fwd, P));
+    }
+    if (st->bwd) {
+      TRY(bwd_chain(c, st->bwd, Q, mid, eager, ord));
+      HIPTRY(hipEventRecord(ev->bend[j & 1], Q));
+      bend_rec[j & 1] = true;
+    }
   }
   HIPTRY(hipEventRecord(ev->end, s1));
   HIPTRY(hipStreamWaitEvent(s0, ev->end, 0));

@@ -413,9 +413,11 @@ int moe_overlap_step(const moe_step* st, hipStream_t s_compute, hipStream_t s_co
  * stream (each chain in moe_overlap_step's order, the shared expert's forward
  * and D on the chain's own stream).  So step j's backward follows the forward
  * of the same micro-batch on its stream and starts while step j-1's backward
- * still runs on the other one, and a forward may reuse the buffers of the
- * micro-batch back-propagated in the step before.  Each stream owns one half of
- * the workspace.  The only other cross-stream waits order the weight-gradient
+ * still runs on the other one.  Step j's forward waits for the end of step
+ * j-2's backward (on the other stream; it has normally ended long before), so
+ * a forward may reuse the buffers of any micro-batch back-propagated in an
+ * earlier step.  Each stream owns one half of the workspace.  The only other
+ * cross-stream waits order the weight-gradient
  * sums (dW_r, dW_gu/dW_down, the shared expert's): each step's sum into a
  * buffer waits for the latest earlier sum into it in the same call, on either
  * stream, so every sum happens in step order.
