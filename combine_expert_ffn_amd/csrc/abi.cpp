@@ -112,8 +112,9 @@ static int do_route(const moe_shape* s, int mode, const void* x, const void* W_r
       if ((rc = launch_transpose_wr(s, W_r, ws, st))) return rc;
     }
     if ((rc = launch_router_logits(s, x, W_r, ws, bias, logits, st))) return rc;
+    return launch_topk(s, logits, idx, gates, is16(s) ? ws : nullptr, bias, st);
   }
-  return launch_topk(s, logits, idx, gates, st);
+  return launch_topk(s, logits, idx, gates, nullptr, nullptr, st);
 }
 
 // xp == NULL: the plan only (fused permute)
@@ -299,7 +300,8 @@ int moe_route(const moe_shape* s, int mode, const void* x, const void* W_r, cons
       REQUIRE(gates);
       if (is16(s)) {
         REQUIRE(ws);
-        if (int rc = need_ws(__func__, ws_bytes, ws_wrt_bytes(s))) return rc;
+        if (int rc = need_ws(__func__, ws_bytes, ws_wrt_bytes(s) + ws_router_fwd_bytes(s)))
+          return rc;
       }
       break;
     case MOE_ROUTE_TOPK_FROM_LOGITS:

@@ -933,33 +933,39 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
 // router logits: l = x . W_r + bias with W_r given transposed (W_rT [E][d]),
 // float32 output.
 // ---------------------------------------------------------------------------
+// With splits > 1 the reduction over d is cut into `splits` equal ranges (one
+// per block-tile pass) and range s writes its float32 partial, without the
+// bias, to partial + s * T * E; the top-k kernel adds the ranges.
 template <class TL, class EL>
 __global__ __launch_bounds__(TL::NT) void router_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W_rT,
     const float* __restrict__ bias, float* __restrict__ logits, int T, int d, int E,
-    int n_tiles, int m_tiles) {
+    int n_tiles, int m_tiles, int splits, float* __restrict__ partial) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[TL::LDS_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / TL::WGN, wn = wave % TL::WGN;
-  for (Sched sc(m_tiles * n_tiles); sc.t < sc.end; sc.t += sc.step) {
-    const int m0 = (sc.t / n_tiles) * TL::BM, n0 = (sc.t % n_tiles) * TL::BN;
+  const int dk = d / splits;  // a multiple of 64
+  for (Sched sc(m_tiles * n_tiles * splits); sc.t < sc.end; sc.t += sc.step) {
+    const int sp = sc.t % splits, tile = sc.t / splits;
+    const int m0 = (tile / n_tiles) * TL::BM, n0 = (tile % n_tiles) * TL::BN;
     LoadK<TL::BM, TL::NT> la;
     LoadK<TL::BN, TL::NT> lb;
     la.init(x + (size_t)m0 * d, [&](int r) { return (min(m0 + r, T - 1) - m0) * d; }, tid);
     lb.init(W_rT + (size_t)n0 * d, [&](int n) { return (min(n0 + n, E - 1) - n0) * d; }, tid);
     f32x16_t acc[TL::TM][TL::TN];
-    mainloop<TL, EL>(la, lb, 0, d, smem, acc);
+    mainloop<TL, EL>(la, lb, sp * dk, (sp + 1) * dk, smem, acc);
+    float* out = splits > 1 ? partial + (size_t)sp * T * E : logits;
 #pragma unroll
     for (int j = 0; j < TL::TN; ++j) {
       const int col = n0 + wn * TL::WTN + j * 32 + (lane & 31);
       if (col >= E) continue;
-      const float b = bias ? bias[col] : 0.f;
+      const float b = (bias && splits == 1) ? bias[col] : 0.f;
 #pragma unroll
       for (int i = 0; i < TL::TM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = m0 + wm * TL::WTM + i * 32 + out_row(lane, r);
-          if (row < T) logits[(size_t)row * E + col] = acc[i][j][r] + b;
+          if (row < T) out[(size_t)row * E + col] = acc[i][j][r] + b;
         }
     }
   }
@@ -1090,15 +1096,16 @@ void wgrad_t(const moe_shape* s, const void* xp, const int32_t* xrows, const voi
 
 template <class E>
 void router_t(const moe_shape* s, const void* x, const void* W_rT, const float* bias,
-              float* logits, hipStream_t st) {
+              float* logits, float* partial, hipStream_t st) {
   using TR = Tile<128, 128, 2, 2>;
   const int T = (int)s->T, d = (int)s->d, En = (int)s->E;
   const int nt = (En + TR::BN - 1) / TR::BN, mt = (T + TR::BM - 1) / TR::BM;
-  const int grid = persistent_grid((long)mt * nt);
+  const int splits = router_splits(s);
+  const int grid = persistent_grid((long)mt * nt * splits);
   MOE_LAUNCH("router", st,
              router_kernel<TR, E><<<grid, TR::NT, 0, st>>>((const uint16_t*)x,
                                                            (const uint16_t*)W_rT, bias, logits, T,
-                                                           d, En, nt, mt));
+                                                           d, En, nt, mt, splits, partial));
 }
 
 }  // namespace
@@ -1166,9 +1173,10 @@ int launch_router_wgrad_mfma(const moe_shape* s, const void* x, const void* dl_s
 }
 
 int launch_router_logits_mfma(const moe_shape* s, const void* x, const void* W_rT,
-                              const float* bias, float* logits, hipStream_t st) {
-  if (s->dtype == MOE_F16) router_t<F16>(s, x, W_rT, bias, logits, st);
-  else router_t<BF16>(s, x, W_rT, bias, logits, st);
+                              const float* bias, float* logits, float* partial,
+                              hipStream_t st) {
+  if (s->dtype == MOE_F16) router_t<F16>(s, x, W_rT, bias, logits, partial, st);
+  else router_t<BF16>(s, x, W_rT, bias, logits, partial, st);
   return check_launch("router GEMM");
 }
 

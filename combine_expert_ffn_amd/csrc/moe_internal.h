@@ -170,6 +170,22 @@ inline size_t ws_router_partial_bytes(const moe_shape* s) {
       ws_router_split_bytes(s) + align_up((size_t)(nm * s->d * 2 * s->E) * sizeof(float), 256);
   return mfma > valu ? mfma : valu;
 }
+// Split-K factor of the 16-bit router GEMM (K = d runs through 128 x 128
+// tiles one latency-bound k-step at a time; with few tiles the chip idles):
+// S <= 8, a power of two dividing d / 64, raised while tiles * S < 256.
+// The S float32 partials of the logits [S][T][E] follow the transposed router
+// weights in the workspace; top-k sums them.
+inline int router_splits(const moe_shape* s) {
+  if (!is16(s)) return 1;
+  const int64_t tiles = cdiv(s->T, 128) * cdiv(s->E, 128);
+  int S = 1;
+  while (S < 8 && tiles * S < 256 && (s->d / 64) % (2 * S) == 0) S *= 2;
+  return S;
+}
+inline size_t ws_router_fwd_bytes(const moe_shape* s) {
+  const int S = router_splits(s);
+  return S > 1 ? align_up((size_t)(S * s->T * s->E) * sizeof(float), 256) : 0;
+}
 // Transposed expert weights for the 16-bit dgrad: W_downT [E_l][F][d] then
 // W_guT [E_l][d][2F].  The float32 dgrad needs none.  They sit after
 // the regions of the plan, the transposed router weights and the router
@@ -177,7 +193,7 @@ inline size_t ws_router_partial_bytes(const moe_shape* s) {
 // router backward still uses its partials.
 inline size_t ws_wT_offset(const moe_shape* s) {
   size_t b = ws_plan_bytes(s);
-  if (ws_wrt_bytes(s) > b) b = ws_wrt_bytes(s);
+  if (ws_wrt_bytes(s) + ws_router_fwd_bytes(s) > b) b = ws_wrt_bytes(s) + ws_router_fwd_bytes(s);
   if (ws_router_partial_bytes(s) > b) b = ws_router_partial_bytes(s);
   return align_up(b, 256);
 }
@@ -196,8 +212,10 @@ inline size_t ws_wT_bytes(const moe_shape* s) {
 int launch_transpose_wr(const moe_shape* s, const void* W_r, void* W_rT, hipStream_t st);
 int launch_router_logits(const moe_shape* s, const void* x, const void* W_r,
                          const void* W_rT, const float* bias, float* logits, hipStream_t st);
-int launch_topk(const moe_shape* s, const float* logits, int32_t* idx, float* gates,
-                hipStream_t st);
+// ws: the workspace of a preceding 16-bit router GEMM (finish its split-K
+// partials into logits first), or NULL (logits are given)
+int launch_topk(const moe_shape* s, float* logits, int32_t* idx, float* gates, const void* ws,
+                const float* bias, hipStream_t st);
 int launch_force_balance(const moe_shape* s, int32_t* idx, hipStream_t st);
 int launch_route_bwd(const moe_shape* s, const float* dgates, const float* gates,
                      const int32_t* idx, const void* x, float* dlogits, float* dW_r,

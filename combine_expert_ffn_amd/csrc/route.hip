@@ -64,14 +64,19 @@ __global__ __launch_bounds__(256) void router_logits_f32_kernel(const float* __r
 }
 
 int launch_router_logits_mfma(const moe_shape* s, const void* x, const void* W_rT,
-                              const float* bias, float* logits, hipStream_t st);
+                              const float* bias, float* logits, float* partial,
+                              hipStream_t st);
 int launch_router_wgrad_mfma(const moe_shape* s, const void* x, const void* dl_split,
                              float* partial, hipStream_t st);
 
 int launch_router_logits(const moe_shape* s, const void* x, const void* W_r, const void* W_rT,
                          const float* bias, float* logits, hipStream_t st) {
   if (s->T == 0) return MOE_OK;
-  if (is16(s)) return launch_router_logits_mfma(s, x, W_rT, bias, logits, st);
+  // 16-bit: W_rT is the workspace base, the split-K partials follow it (with
+  // more than one split the logits are finished by the top-k kernel)
+  if (is16(s))
+    return launch_router_logits_mfma(s, x, W_rT, bias, logits,
+                                     (float*)((char*)W_rT + ws_wrt_bytes(s)), st);
   const long n = s->T * s->E;
   MOE_LAUNCH("router_logits_f32", st,
              router_logits_f32_kernel<<<(unsigned)cdiv(n, 256), 256, 0, st>>>(
@@ -84,19 +89,39 @@ int launch_router_logits(const moe_shape* s, const void* x, const void* W_r, con
 // (E <= 512).  K rounds of a wave-wide argmax; ties go to the lower expert
 // index.  Lane k keeps selection k; gates = softmax over the selected logits.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
+// With partial set, the logits are first finished here: the sum of the router
+// GEMM's split-K partials [splits][T][E] in split order, plus the bias, which
+// is also written to logits.
+__global__ __launch_bounds__(256) void topk_kernel(float* __restrict__ logits,
                                                    int32_t* __restrict__ idx,
                                                    float* __restrict__ gates, int T, int E,
-                                                   int K) {
+                                                   int K, const float* __restrict__ partial,
+                                                   int splits, const float* __restrict__ bias) {
   const int t = (int)(((long)blockIdx.x * 256 + threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= T) return;  // uniform per wave
-  const float* row = logits + (size_t)t * E;
+  float* row = logits + (size_t)t * E;
   float v[8];
+  if (partial) {  // uniform
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int e = lane + 64 * j;
-    v[j] = e < E ? row[e] : 0.f;
+    for (int j = 0; j < 8; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E) {
+        float acc = partial[(size_t)t * E + e];
+        for (int sp = 1; sp < splits; ++sp) acc += partial[((size_t)sp * T + t) * E + e];
+        if (bias) acc += bias[e];
+        row[e] = acc;
+        v[j] = acc;
+      } else {
+        v[j] = 0.f;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = lane + 64 * j;
+      v[j] = e < E ? row[e] : 0.f;
+    }
   }
   unsigned taken = 0;
   float selv = 0.f;
@@ -138,12 +163,17 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   }
 }
 
-int launch_topk(const moe_shape* s, const float* logits, int32_t* idx, float* gates,
-                hipStream_t st) {
+int launch_topk(const moe_shape* s, float* logits, int32_t* idx, float* gates,
+                const void* ws, const float* bias, hipStream_t st) {
   if (s->T == 0) return MOE_OK;
+  // ws set: the logits are the router GEMM's split-K partials (in ws after the
+  // transposed router weights) when it ran with more than one split
+  const int splits = ws ? router_splits(s) : 1;
+  const float* partial =
+      splits > 1 ? (const float*)((const char*)ws + ws_wrt_bytes(s)) : nullptr;
   MOE_LAUNCH("topk", st,
-             topk_kernel<<<(unsigned)cdiv(s->T, 4), 256, 0, st>>>(logits, idx, gates, (int)s->T,
-                                                       (int)s->E, (int)s->K));
+             topk_kernel<<<(unsigned)cdiv(s->T, 4), 256, 0, st>>>(
+                 logits, idx, gates, (int)s->T, (int)s->E, (int)s->K, partial, splits, bias));
   return check_launch("top-k");
 }
 
