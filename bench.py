@@ -138,6 +138,24 @@ def cpu_oracle_baseline(w, inp, target_s=10.0):
                       f"{total:.1f} s"}
 
 
+def group_plan(K, G0):
+    """Steps per captured graph for K timed steps: (G, rem) with G even and
+    G * reps + rem == K, rem in {0, 1} (one eager step when K is odd); G0 when
+    it divides K, else the largest even divisor of K (or of K - 1) up to 2 G0;
+    (None, K) when K is too small for a graph."""
+    def best(n):
+        if n >= 2 and n % G0 == 0:
+            return G0
+        c = [g for g in range(2, min(n, 2 * G0) + 1, 2) if n % g == 0]
+        return max(c) if c else None
+
+    g = best(K)
+    if g:
+        return g, 0
+    g = best(K - 1) if K > 1 else None
+    return (g, 1) if g else (None, K)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,9 +232,8 @@ def main():
     fused = args.fused_permute == "on"
     pipelined = args.pipeline == "on"
     G = args.group
-    timed_graphs = not (args.counter_pass or args.serialized_only or args.overlapped_only)
-    if G < 2 or G % 2 or (timed_graphs and args.graph == "on" and args.steps % G):
-        err("bench.py: --group must be even and divide --steps")
+    if G < 2 or G % 2:
+        err("bench.py: --group must be even")
         sys.exit(2)
     # flags of every step: the fused permute and the wgrad's place in the
     # backward stream's order (both leave the results unchanged)
@@ -303,37 +320,54 @@ def main():
     # ---- timed region 1b: the same overlapped steps replayed from a HIP graph
     # holding two consecutive steps (the micro-batches swap roles each step)
     # -> value.  The library records only kernels and events into the graph.
+    Gk, rem = group_plan(args.steps, G)
+
     def graph_ms(i, flags):
-        """Capture G consecutive steps with `flags` into one HIP graph (G even, so
-        the micro-batches' roles at the end match the start), replay it (warm-up,
-        then exactly --steps steps timed); returns (ms per step, wall ms per
-        step, i)."""
+        """Capture Gk consecutive steps with `flags` into one HIP graph (Gk even,
+        so the micro-batches' roles at the end match the start), replay it
+        (warm-up, then timed), and time exactly --steps steps: the replays plus
+        `rem` (0 or 1) eager steps inside the same timed region; returns (ms per
+        step, wall ms per step, i)."""
+        K = args.steps
+        if Gk is None:  # too few steps for a graph: all eager
+            i = issue(i, max(2, args.warmup), flags, s0)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            ev0.record(s0)
+            i = issue(i, K, flags, s0)
+            ev1.record(s0)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            return ev0.elapsed_time(ev1) / K, 1e3 * wall / K, i
         g = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
         cap.wait_stream(s0)
         with torch.cuda.graph(g, stream=cap, capture_error_mode="thread_local"):
-            issue(i, G, flags, torch.cuda.current_stream())
-        i += G
-        warm = max(1, args.warmup // G)
+            issue(i, Gk, flags, torch.cuda.current_stream())
+        i += Gk
+        warm = max(1, args.warmup // Gk)
         for _ in range(warm):
             g.replay()
         torch.cuda.synchronize()
-        reps = args.steps // G
+        reps = (K - rem) // Gk
+        i += Gk * warm
         t0 = time.perf_counter()
         ev0.record(s0)
         for _ in range(reps):
             g.replay()
+        i += Gk * reps
+        i = issue(i, rem, flags, s0)
         ev1.record(s0)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        i += G * (reps + warm)
-        return ev0.elapsed_time(ev1) / (G * reps), 1e3 * wall / (G * reps), i
+        return ev0.elapsed_time(ev1) / K, 1e3 * wall / K, i
 
     launch = "eager launches"
     ms_serial_graph = None
     if args.graph == "on":
         ms_step, wall_ms, i = graph_ms(i, 0)
-        launch = f"hipGraph replay ({G} steps per graph)"
+        launch = (f"hipGraph replay ({Gk} steps per graph)" if Gk else "eager launches") + \
+            (" + 1 eager step" if Gk and rem else "")
         err(f"[bench] overlapped, graph replay: {ms_step:.4f} ms/step (wall {wall_ms:.4f})")
         ms_serial_graph, wall_ms, i = graph_ms(i, M.MOE_STEP_SERIALIZE)
         err(f"[bench] serialized, graph replay: {ms_serial_graph:.4f} ms/step "

@@ -1,0 +1,22 @@
+"""bench.py's timing plan (host logic, no GPU): any --steps K is timed exactly,
+as replays of an even-length graph of steps plus at most one eager step."""
+
+import os
+import sys
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+
+import bench  # noqa: E402
+
+
+def test_group_plan_covers_every_step_count():
+    for G0 in (2, 10, 16):
+        for K in range(1, 201):
+            g, rem = bench.group_plan(K, G0)
+            if g is None:
+                assert rem == K and K < 3, (G0, K)
+                continue
+            assert g % 2 == 0 and 2 <= g <= 2 * G0, (G0, K, g)
+            assert rem in (0, 1) and (K - rem) % g == 0 and K - rem >= g, (G0, K, g, rem)
+            if K % G0 == 0:
+                assert (g, rem) == (G0, 0), (G0, K, g, rem)
