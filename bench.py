@@ -132,7 +132,17 @@ def cpu_oracle_baseline(w, inp, target_s=10.0):
     while total < target_s:
         total += run(Ts)
         reps += 1
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     return {"value": reps * Ts / total, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model,
             "sample": f"first {Ts} of {w.T} tokens of {w.name}, full weights, {reps} x one "
                       f"forward+backward (float64 numpy, {w.dtype} rounding points), "
                       f"{total:.1f} s"}
@@ -321,6 +331,7 @@ def main():
     # holding two consecutive steps (the micro-batches swap roles each step)
     # -> value.  The library records only kernels and events into the graph.
     Gk, rem = group_plan(args.steps, G)
+    medians = {}  # median per-step time over the graph replays, by serialize flag
 
     def graph_ms(i, flags):
         """Capture Gk consecutive steps with `flags` into one HIP graph (Gk even,
@@ -351,15 +362,21 @@ def main():
         torch.cuda.synchronize()
         reps = (K - rem) // Gk
         i += Gk * warm
+        # an event after every replay as well: per-replay times for the median
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
         t0 = time.perf_counter()
         ev0.record(s0)
-        for _ in range(reps):
+        for r in range(reps):
             g.replay()
+            marks[r].record(s0)
         i += Gk * reps
         i = issue(i, rem, flags, s0)
         ev1.record(s0)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        per = [ev0.elapsed_time(marks[0]) / Gk] + [marks[r - 1].elapsed_time(marks[r]) / Gk
+                                                  for r in range(1, reps)]
+        medians[flags & M.MOE_STEP_SERIALIZE] = sorted(per)[len(per) // 2]
         return ev0.elapsed_time(ev1) / K, 1e3 * wall / K, i
 
     launch = "eager launches"
@@ -485,6 +502,11 @@ def main():
         # serialized = the same steps on one stream, launched the same way
         # (graph replay or eager) as the overlapped value, no kernel events
         "serialized_ms_per_step": round(ms_serial, 4),
+        # median over the timed graph replays of their per-step time
+        "median_replay_ms_per_step": (round(medians[0], 4) if 0 in medians else None),
+        "median_replay_serialized_ms_per_step": (
+            round(medians[M.MOE_STEP_SERIALIZE], 4) if M.MOE_STEP_SERIALIZE in medians
+            else None),
         "overlap_speedup": round(ms_serial / ms_step, 4),
         "eager_overlapped_ms_per_step": round(ms_eager, 4),
         "eager_serialized_ms_per_step": round(ms_serial_eager, 4),
