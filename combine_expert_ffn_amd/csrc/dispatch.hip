@@ -6,8 +6,8 @@
 //
 // The plan is a deterministic stable counting sort of the (token, slot) pairs
 // by local expert: per-block LDS histograms, one exclusive scan over
-// (expert, block), then an in-block stable rank from wave ballots + popcounts
-// and a per-wave LDS prefix.  No global atomics decide positions, so the maps
+// (expert, block), then an in-block stable rank from per-(wave, expert) LDS
+// lane masks and a per-wave LDS prefix.  No global atomics decide positions, so the maps
 // are bit-identical run to run.
 //
 // The copies are token-major: one wave per token reads the token's row once
@@ -134,8 +134,10 @@ __global__ __launch_bounds__(kScanThreads) void plan_scan_kernel(
 // ---------------------------------------------------------------------------
 // plan step 3: stable in-block rank -> row_of_pair, pair_of_row.
 // Rounds of 256 pairs; within a wave, pairs with the same expert are ranked by
-// ballot + popcount (one pass per distinct expert present in the wave); across
-// waves by a per-wave count prefix in LDS; across rounds by a running count.
+// a 64-bit LDS lane mask per (wave, expert): each lane ORs in its bit, reads
+// the mask back and counts the lower lanes (the cost does not depend on how
+// many distinct experts the wave holds); across waves by a per-wave count
+// prefix in LDS; across rounds by a running count.
 // Also writes -1 into pair_of_row rows [N, cap) of this block's range.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void plan_rank_kernel(const int32_t* __restrict__ idx,

@@ -127,6 +127,14 @@ int moe_version(void);
 
 /*
  * moe_route - routing (router scores, top-K selection, gates).
+ * Passages: the router is the layer's first MoE scope, captured in a graph of
+ * its own with the permutation plan (skill card page 1, "HybridEP benchmark":
+ * Transformer Engine graph scopes moe_router and moe_preprocess, and "Routing:
+ * force balance"); routing precedes the dispatch phase in the phase chain
+ * attn -> dispatch -> mlp -> combine (1F1B note page 2, "how the 8 ops are
+ * split").  The routing function itself is not given on the pages; top-K
+ * softmax over router logits (gates renormalised over the selected experts)
+ * is the reading used.
  *   x      [T,d] dtype        (MOE_ROUTE_TOPK only)
  *   W_r    [d,E] dtype        (MOE_ROUTE_TOPK only)
  *   bias   [E] f32 or NULL    (MOE_ROUTE_TOPK only; added to the logits, so it
@@ -166,7 +174,11 @@ int moe_dispatch(const moe_shape* s, const void* x, const int32_t* idx,
                  void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * moe_expert_ffn_fwd - per local expert j (rows [offsets[j], offsets[j+1])):
+ * moe_expert_ffn_fwd - the expert FFN computation that the token exchange is
+ * overlapped with (skill card page 1, "What it is"), the mlp phase between
+ * dispatch and combine (1F1B note page 2, "how the 8 ops are split").  The
+ * pages do not give the expert type; a SwiGLU FFN is the reading used.  Per
+ * local expert j (rows [offsets[j], offsets[j+1])):
  *   [g,u] = xp . W_gu[j]^T,  a = silu(g) * u,  y_p = a . W_down[j]^T
  *   xp [T*K,d], W_gu [E_l,2F,d] (rows [0,F) gate, [F,2F) up), W_down [E_l,d,F]
  *   h  [T*K,2F] out (g and u, saved for the backward), a [T*K,F] out,
@@ -251,7 +263,14 @@ int moe_ffn_wgrad_gather(const moe_shape* s, const void* x, const int32_t* pair_
 /*
  * moe_route_bwd - backward of the top-K softmax gates and of the router
  * product (TOPK modes; returns MOE_ERR_UNSUPPORTED for FORCE_BALANCE, whose
- * gates are inputs with gradient dgates).
+ * gates are inputs with gradient dgates).  Passage: the backward chain runs
+ * combine -> mlp -> dispatch -> attn, each phase returning the gradient of its
+ * input (1F1B note page 2, "how the 8 ops are split"); the gates' gradient
+ * (dgates, from moe_combine_bwd) reaches the router logits here, and the
+ * router's weight gradient is accumulated like every weight gradient there
+ * (accumulate_grad=True).  The router's input-gradient term, dlogits . W_r^T,
+ * is not formed here: moe_dispatch_bwd adds it to dx in the same pass as the
+ * dispatched rows, so dx is rounded once.
  *   dlogits[t, idx[t,j]] = g_j * (dg_j - sum_k g_k dg_k); other logits 0.  [T,E] f32
  *   dW_r = x^T . dlogits  [d,E] f32 (skipped when x or dW_r is NULL; with
  *   accumulate & MOE_ACCUM_DW added to the existing value)

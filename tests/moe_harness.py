@@ -34,8 +34,12 @@ def dev(a, dtype, device="cuda"):
     return torch.from_numpy(a.astype(np.float32)).to(device=device, dtype=torch.bfloat16)
 
 
-def host(t):
-    """device tensor -> numpy (float64 for floating point, as-is for integers)."""
+def host(t, rows=None):
+    """device tensor -> numpy (float64 for floating point, as-is for integers).
+    With ``rows`` only the first ``rows`` rows are copied: row buffers are sized
+    to the cap T*K and rows [N, cap) hold whatever the allocation held."""
+    if rows is not None:
+        t = t[: int(rows)]
     if t.dtype in (torch.bfloat16, torch.float16):
         t = t.float()
     a = t.detach().cpu().numpy()

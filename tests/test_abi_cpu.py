@@ -263,3 +263,19 @@ def test_multi_step_rejects_bad_chains():
     other = step(m2, m1)
     other.ws = 0x2000
     assert run([step(m1, m2), other]) == M.MOE_ERR_ARG
+
+
+def test_binding_rejects_bad_tensors_before_the_call():
+    """The Python binding checks device, dtype, contiguity and size of every
+    tensor against the shape before passing raw pointers (no GPU needed: a
+    host tensor is rejected first)."""
+    import torch
+
+    s = _shape()
+    t = torch.zeros(4)
+    with pytest.raises(M.MoeError, match="not on the GPU"):
+        M.moe_combine(s, t, t, t, t)
+    with pytest.raises(M.MoeError, match="is None"):
+        M.moe_combine(s, None, t, t, t)
+    with pytest.raises(M.MoeError, match="not a torch tensor"):
+        M.moe_combine(s, 123, t, t, t)

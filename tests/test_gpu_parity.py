@@ -51,6 +51,10 @@ SMALL = {
                                 K=6, dtype="f16", route="topk", zipf_s=1.1),
     "mid_window_f16": Workload("mid_window_f16", T=150, d=64, F=64, E=16, e_lo=5, E_l=3, K=4,
                                dtype="f16", route="topk"),
+    # forced balance with K < E over a window: slot k of token t goes to expert
+    # (t*K + k) mod E, a third of the slots are not local
+    "fb_k3_window_bf16": Workload("fb_k3_window_bf16", T=333, d=128, F=128, E=12, e_lo=4,
+                                  E_l=8, K=3, dtype="bf16", route="force_balance"),
     # the largest router (E = 512, K = 16) with the largest window (256 experts)
     "max_router_bf16": Workload("max_router_bf16", T=200, d=128, F=64, E=512, e_lo=128,
                                 E_l=256, K=16, dtype="bf16", route="topk"),
@@ -136,7 +140,7 @@ def test_stage_parity(name):
     exact("tile_offsets", host(mb.tile_offsets), ref["tile_offsets"])
     exact("row_of_pair", host(mb.row_of_pair), ref["row_of_pair"])
     exact("pair_of_row", host(mb.pair_of_row), ref["pair_of_row"])
-    exact("xp", host(mb.xp)[:N], ref["xp"])
+    exact("xp", host(mb.xp, N), ref["xp"])
 
     # plan only (the fused permute's dispatch): the same plan, no xp
     fz = M.MicroBatch(s, fused=True)
@@ -147,15 +151,15 @@ def test_stage_parity(name):
 
     # ---- expert FFN forward
     M.moe_expert_ffn_fwd(s, mb.xp, mb.offsets, mb.tile_offsets, W_gu, W_down, mb.h, mb.a, mb.yp)
-    close("h", host(mb.h)[:N], ref["h"], tau)
-    close("a", host(mb.a)[:N], ref["a"], tau)
-    close("yp", host(mb.yp)[:N], ref["yp"], tau)
+    close("h", host(mb.h, N), ref["h"], tau)
+    close("a", host(mb.a, N), ref["a"], tau)
+    close("yp", host(mb.yp, N), ref["yp"], tau)
     # fused permute: GEMM1 gathers the token rows of x itself; same arithmetic,
     # so the same bits as on the materialised xp
     M.moe_expert_ffn_fwd_gather(s, x, fz.pair_of_row, fz.offsets, fz.tile_offsets, W_gu, W_down,
                                 fz.h, fz.a, fz.yp)
     for k in ("h", "a", "yp"):
-        exact(f"{k} (fused permute)", host(getattr(fz, k))[:N], host(getattr(mb, k))[:N])
+        exact(f"{k} (fused permute)", host(getattr(fz, k), N), host(getattr(mb, k), N))
 
     # ---- combine (oracle y_p)
     yp_r = D(_pad(ref["yp"], cap))
@@ -164,7 +168,7 @@ def test_stage_parity(name):
 
     # ---- combine backward
     M.moe_combine_bwd(s, dout, yp_r, gates_r, mb.row_of_pair, mb.dyp, mb.dgates)
-    close("dyp", host(mb.dyp)[:N], refb["dyp"], tau)
+    close("dyp", host(mb.dyp, N), refb["dyp"], tau)
     close("dgates", host(mb.dgates), refb["dgates"], tau)
 
     # ---- router backward (oracle dgates)
@@ -182,8 +186,8 @@ def test_stage_parity(name):
     dyp_r = D(_pad(refb["dyp"], cap))
     h_r = D(_pad(ref["h"], cap))
     M.moe_ffn_dgrad(s, dyp_r, h_r, mb.offsets, mb.tile_offsets, W_gu, W_down, mb.dh, mb.dxp, ws)
-    close("dh", host(mb.dh)[:N], refb["dh"], tau)
-    close("dxp", host(mb.dxp)[:N], refb["dxp"], tau)
+    close("dh", host(mb.dh, N), refb["dh"], tau)
+    close("dxp", host(mb.dxp, N), refb["dxp"], tau)
 
     # ---- dispatch backward (oracle dxp, dlogits)
     dxp_r = D(_pad(refb["dxp"], cap))
@@ -247,7 +251,7 @@ def _layer_step(w, inp, flags=0, s_copy=None):
 
 @pytest.mark.parametrize("fused", [False, True], ids=["", "fused_permute"])
 @pytest.mark.parametrize("name", ["tiny_f32", "fb_ragged_bf16", "zipf_window_bf16",
-                                  "many_experts_bf16", "mid_window_bf16", "max_router_bf16",
+                                  "fb_k3_window_bf16", "many_experts_bf16", "mid_window_bf16", "max_router_bf16",
                                   "fb_ragged_f16", "zipf_window_f16"])
 def test_chain_parity(name, fused):
     w = SMALL[name]
@@ -267,12 +271,12 @@ def test_chain_parity(name, fused):
     N = ref["N"]
     exact("row_of_pair", host(A.row_of_pair), ref["row_of_pair"])
     if not fused:
-        exact("xp", host(A.xp)[:N], ref["xp"])
+        exact("xp", host(A.xp, N), ref["xp"])
     for k in ("h", "a", "yp"):
-        close(k, host(getattr(A, k))[:N], ref[k], tau)
+        close(k, host(getattr(A, k), N), ref[k], tau)
     close("out", host(A.out), ref["out"], tau)
     for k in ("dyp", "dh", "dxp"):
-        close(k, host(getattr(A, k))[:N], refb[k], tau)
+        close(k, host(getattr(A, k), N), refb[k], tau)
     close("dgates", host(A.dgates), refb["dgates"], tau)
     close("dx", host(A.dx), refb["dx"], tau)
     close("dW_gu", host(g["dW_gu"]), refb["dW_gu"], tau)
@@ -447,6 +451,47 @@ def test_empty_experts_and_no_tokens():
     torch.cuda.synchronize()
     assert torch.all(mb0.counts == 0) and torch.all(mb0.offsets == 0)
     assert torch.all(dW_gu == 0) and torch.all(dW_down == 0)
+
+
+@pytest.mark.parametrize("name,fused", [("mid_window_bf16", False), ("fb_k3_window_bf16", False),
+                                        ("zipf_window_bf16", True)])
+def test_rows_past_N_untouched(name, fused):
+    """Row buffers are sized to the cap T*K; the calls write rows [0, N) only
+    (and pair_of_row = -1 on [N, cap)), as include/moe.h states."""
+    w = SMALL[name]
+    log(f"[edge] rows >= N untouched: {name}{' fused permute' if fused else ''}")
+    inp = make_inputs(w, seed=0)
+    s = M.shape_of(w)
+    D = lambda a: dev(a, w.dtype)
+    topk = w.route == "topk"
+    A = M.MicroBatch(s, x=D(inp["x"]), dout=D(inp["dout"]),
+                     gates=None if topk else dev(inp["gates"], "f32x"), fused=fused)
+    rows = [k for k in ("xp", "h", "a", "yp", "dyp", "dh", "dxp") if getattr(A, k) is not None]
+    for k in rows:
+        getattr(A, k).fill_(123.0)
+    A.pair_of_row.fill_(77)
+    W_gu, W_down = D(inp["W_gu"]), D(inp["W_down"])
+    W_r = D(inp["W_r"]) if topk else None
+    bias = dev(inp["bias"], "f32x") if inp["bias"] is not None else None
+    dW_gu = torch.empty(w.E_l, 2 * w.F, w.d, dtype=torch.float32, device="cuda")
+    dW_down = torch.empty(w.E_l, w.d, w.F, dtype=torch.float32, device="cuda")
+    dW_r = torch.empty(w.d, w.E, dtype=torch.float32, device="cuda") if topk else None
+    ws = torch.empty(M.moe_step_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    mode = M.MOE_ROUTE_TOPK if topk else M.MOE_ROUTE_FORCE_BALANCE
+    flags = M.MOE_STEP_FUSED_PERMUTE if fused else 0
+    for fwd, bwd in ((A, None), (None, A)):
+        st = M.make_step(s, mode, W_gu, W_down, dW_gu, dW_down, ws, fwd=fwd, bwd=bwd, W_r=W_r,
+                         bias=bias, dW_r=dW_r)
+        M.moe_overlap_step(st, torch.cuda.current_stream(), torch.cuda.Stream(), flags)
+    torch.cuda.synchronize()
+    N = int(A.offsets[-1].item())
+    assert 0 < N < w.T * w.K, "the workload must leave rows past N"
+    for k in rows:
+        tail = getattr(A, k)[N:]
+        assert torch.all(tail.float() == 123.0), f"{k}: a row past N was written"
+        assert torch.all(torch.isfinite(getattr(A, k)[:N].float())), f"{k}: non-finite row"
+    assert torch.all(A.pair_of_row[N:] == -1)
+    assert torch.all(A.pair_of_row[:N] >= 0)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

@@ -195,6 +195,52 @@ def test_force_balance_closed_form_counts():
     assert plan["counts"].tolist() == [512] * 8
 
 
+HAND = os.path.join(os.path.dirname(__file__), "golden", "force_balance_and_accumulate.json")
+
+
+@pytest.fixture(scope="module")
+def hand():
+    with open(HAND) as f:
+        return json.load(f)
+
+
+def test_force_balance_hand_listed_slot_map(hand):
+    # K != E, where a per-token map such as (t + k) mod E would differ
+    for c in hand["force_balance"]["cases"]:
+        got = O.force_balance_idx(c["T"], c["K"], c["E"])
+        assert got.dtype == np.int32
+        assert got.tolist() == c["idx"], c
+
+
+def test_route_bwd_accumulate_hand_worked(hand):
+    h = hand["route_bwd_accumulate"]
+    a = lambda k: np.array(h[k], np.float64)
+    for prec in ("f64", "f32", "bf16"):
+        dl, dW = O.route_bwd(a("dgates"), a("gates"), np.array(h["idx"], np.int32), a("x"), 2,
+                             dW_r_prev=a("dW_r_prev"), prec=prec)
+        assert np.array_equal(dl, a("dlogits")), prec
+        assert np.array_equal(dW, a("dW_r")), prec
+    # without the prior value: the plain product
+    _, dW0 = O.route_bwd(a("dgates"), a("gates"), np.array(h["idx"], np.int32), a("x"), 2,
+                         prec="f64")
+    assert np.array_equal(dW0, a("dW_r") - a("dW_r_prev"))
+
+
+def test_dispatch_bwd_accumulate_hand_worked(hand):
+    h = hand["dispatch_bwd_accumulate"]
+    a = lambda k: np.array(h[k], np.float64)
+    rop = np.array(h["row_of_pair"], np.int32)
+    for prec in ("f64", "f32", "bf16"):
+        dx = O.dispatch_bwd(a("dxp"), rop, dx_prev=a("dx_prev"), prec=prec)
+        assert np.array_equal(dx, a("dx_no_router")), prec
+        dx = O.dispatch_bwd(a("dxp"), rop, dlogits=a("dlogits"), W_r=a("W_r"),
+                            dx_prev=a("dx_prev"), prec=prec)
+        assert np.array_equal(dx, a("dx_with_router")), prec
+        # the shared expert's term enters the same sum
+        dx = O.dispatch_bwd(a("dxp"), rop, dx_prev=a("dx_prev"), add=a("dx_prev"), prec=prec)
+        assert np.array_equal(dx, a("dx_no_router") + a("dx_prev")), prec
+
+
 # ----------------------------------------------------------------------------
 # dispatch plan: invariants and library routine (bincount, stable argsort)
 # ----------------------------------------------------------------------------
