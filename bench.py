@@ -3,62 +3,103 @@
 
 One step = the 1F1B two-micro-batch step of the expert-parallel overlap pages
 (1F1B note page 2, "MoE 1F1B overlap"): the forward of one micro-batch and the
-backward (dgrad, then wgrad deferred past the other's expert GEMMs) of the other,
-on two streams, so that every step passes T tokens through the whole layer
-forward and backward.  Throughput = T / step time (tokens/s).  Inputs are
-synthetic (seeded), resident in HBM before the timed region.
+backward (dgrad, then wgrad deferred past the other's expert GEMMs) of the
+other, on two streams, so that every step passes T tokens through the whole
+layer forward and backward.  Throughput = T / step time (tokens/s).  Inputs are
+synthetic (seeded), resident in HBM before the timed region.  The default
+workload is the whole 128-expert layer on one GPU (T = 16384, d = 2048,
+F = 768, top-8, bf16), the largest configuration that fits one GPU.
 
 Prints ONE JSON line on stdout; diagnostics go to stderr.
+
+``--summarize KIND`` turns rocprofv3 output into the summaries kept under
+profiles/ (kernel trace, HBM traffic, MFMA counters, stream overlap); it needs
+no GPU.
 """
 
 from __future__ import annotations
 
 import argparse
+import collections
+import csv
 import json
 import os
+import statistics
 import sys
 import time
 
 METRIC = "MoE layer fwd+bwd tokens/s on 1 MI355X; grouped-GEMM MFMA util %; dispatch HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 (and fp16) matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+DEFAULT_WORKLOAD = "ep1_128exp_bf16"
+OVERLAP_WORKLOAD = "two_microbatch_bf16"
 
 GEMM_KERNELS = ("ffn_gate_up", "ffn_down", "dgrad_act", "dgrad_in", "wgrad")
 COPY_PROBE_BYTES = 1 << 30
-TRAFFIC_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
 def err(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic(w, N, T_loc):
-    """Algorithmic work per step (one launch of each, plus the shared expert's
-    launches of the same GEMMs over all T tokens when the workload has one):
-    flops for the GEMMs, HBM bytes for the permute kernels (one pass over each
-    operand, no re-reads)."""
-    d, F, T, K, E = w.d, w.F, w.T, w.K, w.E
+def algorithmic(w, N, T_loc, accumulate=True, fused=False):
+    """Algorithmic work per step of each kernel (one launch of each, plus the
+    shared expert's launches of the same GEMMs over all T tokens when the
+    workload has one): {name: {"flop": F, "byte": B}}.  Bytes count one pass
+    over every operand and result (no re-reads); the GEMMs' bytes include the
+    expert weights, and wgrad's the float32 weight gradients (read and written
+    with accumulate, written without)."""
+    d, F, T, K, E, E_l = w.d, w.F, w.T, w.K, w.E, w.E_l
     b = 4 if w.dtype == "f32" else 2
     Fs = w.F_s
-    return {
-        "ffn_gate_up": ("flop", 2.0 * N * d * 2 * F + 2.0 * T * d * 2 * Fs),
-        "ffn_down": ("flop", 2.0 * N * F * d + 2.0 * T * Fs * d),
-        "dgrad_act": ("flop", 2.0 * N * d * F + 2.0 * T * d * Fs),
-        "dgrad_in": ("flop", 2.0 * N * 2 * F * d + 2.0 * T * 2 * Fs * d),
-        "wgrad": ("flop", 6.0 * N * d * F + 6.0 * T * d * Fs),
-        "router": ("flop", 2.0 * T * d * E),
+    wgu, wdn = E_l * 2 * F * d * b, E_l * d * F * b          # expert weights
+    sgu, sdn = 2 * Fs * d * b, d * Fs * b                    # shared expert weights
+    dW = 4.0 * (E_l * 3 * F * d + 3 * Fs * d)                # float32 dW_gu + dW_down
+    xin = (T_loc if fused else N) * d * b                    # GEMM1 A operand rows
+    out = {
+        "ffn_gate_up": {"flop": 2.0 * N * d * 2 * F + 2.0 * T * d * 2 * Fs,
+                        "byte": xin + wgu + N * 3 * F * b + T * d * b * (Fs > 0) + sgu
+                        + T * 3 * Fs * b},
+        "ffn_down": {"flop": 2.0 * N * F * d + 2.0 * T * Fs * d,
+                     "byte": N * F * b + wdn + N * d * b + T * Fs * b + sdn + T * d * b * (Fs > 0)},
+        "dgrad_act": {"flop": 2.0 * N * d * F + 2.0 * T * d * Fs,
+                      "byte": N * d * b + wdn + N * 2 * F * b * 2
+                      + (T * d * b + sdn + T * 2 * Fs * b * 2) * (Fs > 0)},
+        "dgrad_in": {"flop": 2.0 * N * 2 * F * d + 2.0 * T * 2 * Fs * d,
+                     "byte": N * 2 * F * b + wgu + N * d * b
+                     + (T * 2 * Fs * b + sgu + T * d * b) * (Fs > 0)},
+        "wgrad": {"flop": 6.0 * N * d * F + 6.0 * T * d * Fs,
+                  "byte": N * (d + F + 2 * F) * b + xin + T * (2 * d + 3 * Fs) * b * (Fs > 0)
+                  + dW * (2 if accumulate else 1)},
+        "router": {"flop": 2.0 * T * d * E, "byte": T * d * b + d * E * b + 4.0 * T * E},
         # router weight gradient x^T dlogits on the matrix cores (bf16 data);
         # the two-term split of dlogits forms it twice, counted once here
-        "dwr_mfma": ("flop", 2.0 * T * d * E),
+        "dwr_mfma": {"flop": 2.0 * T * d * E, "byte": T * d * b + 4.0 * T * E},
         # x rows of tokens with a local expert + row map -> N rows
-        "permute": ("byte", T_loc * d * b + 4.0 * T * K + N * d * b),
+        "permute": {"byte": T_loc * d * b + 4.0 * T * K + N * d * b},
         # y_p rows + gates + row map -> out
-        "combine": ("byte", N * d * b + 8.0 * T * K + T * d * b),
+        "combine": {"byte": N * d * b + 8.0 * T * K + T * d * b},
         # dout + y_p rows + gates + map -> dy_p rows + dgates
-        "combine_bwd": ("byte", T * d * b + 2.0 * N * d * b + 12.0 * T * K),
+        "combine_bwd": {"byte": T * d * b + 2.0 * N * d * b + 12.0 * T * K},
         # dx_p rows + map -> dx
-        "dispatch_bwd": ("byte", N * d * b + 4.0 * T * K + T * d * b),
+        "dispatch_bwd": {"byte": N * d * b + 4.0 * T * K + T * d * b},
     }
+    return out
+
+
+def rate(work, seconds):
+    """(bound, achieved, peak, unit, frac) of one launch: the kernel is bound
+    by whichever of its flops at the matrix-core peak and its bytes at the HBM
+    peak takes longer, and is rated against that peak."""
+    t_f = work.get("flop", 0.0) / (PEAK_BF16_TFLOPS * 1e12)
+    t_b = work.get("byte", 0.0) / (PEAK_HBM_GBS * 1e9)
+    if t_f >= t_b:
+        ach = work["flop"] / seconds / 1e12
+        return "mfma", ach, PEAK_BF16_TFLOPS, "TFLOP/s", ach / PEAK_BF16_TFLOPS
+    ach = work["byte"] / seconds / 1e9
+    return "hbm", ach, PEAK_HBM_GBS, "GB/s", ach / PEAK_HBM_GBS
 
 
 KERNEL_SOURCE = {k: "gemm_mfma.hip" for k in GEMM_KERNELS}
@@ -69,8 +110,7 @@ KERNEL_SOURCE.update({k: "dispatch.hip" for k in ("permute", "combine", "combine
 def kernel_source_hash(name):
     """sha256 of the source that defines kernel `name` and the shared header."""
     import hashlib
-    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "combine_expert_ffn_amd",
-                        "csrc")
+    csrc = os.path.join(ROOT, "combine_expert_ffn_amd", "csrc")
     h = hashlib.sha256()
     for f in (KERNEL_SOURCE[name], "moe_internal.h"):
         with open(os.path.join(csrc, f), "rb") as fh:
@@ -166,17 +206,142 @@ def group_plan(K, G0):
     return (g, 1) if g else (None, K)
 
 
+# ---------------------------------------------------------------------------
+# one workload's device state and step issue
+# ---------------------------------------------------------------------------
+class Layer:
+    """Weights, gradient buffers, workspace and two micro-batches of one
+    workload on the GPU, and the issue of 1F1B steps on two streams."""
+
+    def __init__(self, w, args, s0, s1):
+        import torch
+        import combine_expert_ffn_amd as M
+        from combine_expert_ffn_amd.inputs import make_inputs
+
+        self.M, self.w, self.s0, self.s1 = M, w, s0, s1
+        self.inp = inp = make_inputs(w, seed=0, microbatches=2)
+        s = self.s = M.shape_of(w)
+        tdt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(w.dtype, torch.float32)
+        D = lambda a: torch.from_numpy(a).to("cuda", tdt)
+        F32 = lambda a: torch.from_numpy(a).to("cuda")
+        self.topk = topk = w.route == "topk"
+        self.mode = M.MOE_ROUTE_TOPK if topk else M.MOE_ROUTE_FORCE_BALANCE
+        self.W_gu, self.W_down = D(inp["W_gu"]), D(inp["W_down"])
+        self.W_r = D(inp["W_r"]) if topk else None
+        self.bias = F32(inp["bias"]) if inp["bias"] is not None else None
+        z = lambda *sh: torch.zeros(*sh, dtype=torch.float32, device="cuda")
+        self.dW_gu, self.dW_down = z(w.E_l, 2 * w.F, w.d), z(w.E_l, w.d, w.F)
+        self.dW_r = z(w.d, w.E) if topk else None
+        self.ws = torch.empty(M.moe_step_workspace_bytes_shared(s, w.F_s), dtype=torch.uint8,
+                              device="cuda")
+        self.fused = args.fused_permute == "on"
+        self.pipelined = args.pipeline == "on"
+        self.G = args.group
+        # flags of every step: the fused permute and the wgrad's place in the
+        # backward stream's order (both leave the results unchanged)
+        self.FLAGS = ((M.MOE_STEP_FUSED_PERMUTE if self.fused else 0) |
+                      (M.MOE_STEP_MID_WGRAD if args.wgrad_order == "mid" else 0))
+        self.shared = None
+        if w.F_s:  # a shared expert beside the routed ones
+            self.shared = (D(inp["W_gu_s"]), D(inp["W_down_s"]), z(2 * w.F_s, w.d),
+                           z(w.d, w.F_s))
+        mk = lambda x, dout, g: M.MicroBatch(s, x=D(x), dout=D(dout),
+                                             gates=None if topk else F32(g), fused=self.fused,
+                                             F_s=w.F_s)
+        self.mbs = [mk(inp["x"], inp["dout"], inp["gates"]),
+                    mk(inp["x_b"], inp["dout_b"], inp.get("gates_b"))]
+        self.i = 0  # steps issued so far (after the priming forward)
+        M.moe_overlap_step(self.make_step(self.mbs[0], None), s0, s1, self.FLAGS)
+
+    def make_step(self, fwd, bwd):
+        M = self.M
+        return M.make_step(self.s, self.mode, self.W_gu, self.W_down, self.dW_gu, self.dW_down,
+                           self.ws, fwd=fwd, bwd=bwd, W_r=self.W_r, bias=self.bias,
+                           dW_r=self.dW_r, accumulate=M.MOE_ACCUM_DW, shared=self.shared)
+
+    def make(self, i):  # step i forwards one micro-batch and back-propagates the other
+        return self.make_step(self.mbs[(i + 1) % 2], self.mbs[i % 2])
+
+    def issue(self, n, flags, q=None):
+        """Issue the next n steps on q (and s1): one pipelined moe_overlap_steps
+        call per group of G steps for overlapped steps with --pipeline on, else
+        one moe_overlap_step call per step (serialized steps run the same
+        groups through moe_overlap_steps with MOE_STEP_SERIALIZE)."""
+        M = self.M
+        q = q or self.s0
+        i0 = self.i
+        if self.pipelined:
+            for g0 in range(i0, i0 + n, self.G):
+                M.moe_overlap_steps([self.make(j) for j in range(g0, min(g0 + self.G, i0 + n))],
+                                    q, self.s1, flags | self.FLAGS)
+        else:
+            for j in range(i0, i0 + n):
+                M.moe_overlap_step(self.make(j), q, self.s1, flags | self.FLAGS)
+        self.i += n
+
+    def capture(self, n, flags):
+        """A HIP graph of the next n steps (n even: the micro-batches' roles at
+        its end match its start, so it can be replayed)."""
+        import torch
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(self.s0)
+        with torch.cuda.graph(g, stream=cap, capture_error_mode="thread_local"):
+            self.issue(n, flags, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        return g
+
+
+def ab_medians(runs, rounds, s0):
+    """Alternate the timed callables of `runs` ({name: (fn, steps)}) for
+    `rounds` rounds, each run bracketed by events on s0; returns
+    {name: median ms per step}.  Alternating keeps the two schedules under the
+    same clock and thermal state."""
+    import torch
+    per = {k: [] for k in runs}
+    for _ in range(rounds):
+        for k, (fn, n) in runs.items():
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(s0)
+            fn()
+            b.record(s0)
+            torch.cuda.synchronize()
+            per[k].append(a.elapsed_time(b) / n)
+    return {k: statistics.median(v) for k, v in per.items()}
+
+
+def overlap_ab(L, G, rounds, graph):
+    """Overlapped against serialized steps of layer L, alternated (A/B), as
+    replays of two captured G-step graphs (graph=True) or as eager groups of G
+    steps; returns (overlapped ms, serialized ms) medians per step."""
+    M = L.M
+    if graph:
+        go = L.capture(G, 0)
+        gs = L.capture(G, M.MOE_STEP_SERIALIZE)
+        for _ in range(2):
+            go.replay()
+            gs.replay()
+        runs = {"o": (go.replay, G), "s": (gs.replay, G)}
+    else:
+        runs = {"o": (lambda: L.issue(G, 0), G),
+                "s": (lambda: L.issue(G, M.MOE_STEP_SERIALIZE), G)}
+        for f, _ in runs.values():
+            f()
+    med = ab_medians(runs, rounds, L.s0)
+    return med["o"], med["s"]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="ep16_rank_bf16")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--tokens", type=int, default=None, help="override T of the workload")
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
     ap.add_argument("--graph", choices=("on", "off"), default="on",
-                    help="time the overlapped steps as replays of a HIP graph that holds two "
-                         "steps (on) or as eager launches (off)")
+                    help="time the overlapped steps as replays of a HIP graph of --group steps "
+                         "(on) or as eager launches (off)")
     ap.add_argument("--fused-permute", choices=("on", "off"), default="off",
                     help="fuse the permute into the expert GEMMs (MOE_STEP_FUSED_PERMUTE): GEMM1 "
                          "and wgrad read the token rows of x through the dispatch plan, no xp")
@@ -189,8 +354,12 @@ def main():
                          "streams' roles alternating so consecutive steps overlap (on), or one "
                          "moe_overlap_step call per step, joined at every step boundary (off)")
     ap.add_argument("--group", type=int, default=10,
-                    help="steps per moe_overlap_steps call and per captured graph (even; "
-                         "--steps must be a multiple of it)")
+                    help="steps per moe_overlap_steps call and per captured graph (even)")
+    ap.add_argument("--ab-rounds", type=int, default=6,
+                    help="rounds of the alternating overlapped / serialized comparison")
+    ap.add_argument("--overlap-workload", default=OVERLAP_WORKLOAD,
+                    help="second workload whose overlapped / serialized ratio is reported too "
+                         "(the two-micro-batch top-8 configuration); 'none' to skip")
     ap.add_argument("--overlapped-only", action="store_true",
                     help="run only the warm-up and the overlapped steps and print no JSON line: "
                          "the program to trace with rocprofv3 --kernel-trace for the overlap of "
@@ -201,9 +370,20 @@ def main():
                          "bench's event timings (taken on the serialized steps)")
     ap.add_argument("--counter-pass", action="store_true",
                     help="run a few serialized steps and a copy probe of known size, print no "
-                         "JSON line: the program to run under rocprofv3 --pmc FETCH_SIZE / "
-                         "WRITE_SIZE for the per-kernel HBM traffic")
+                         "JSON line: the program to run under rocprofv3 --pmc for the per-kernel "
+                         "HBM traffic (FETCH_SIZE / WRITE_SIZE) and MFMA counters")
+    ap.add_argument("--summarize", choices=("kernels", "traffic", "mfma", "overlap"),
+                    help="write profiles/<kind>_<workload>.md from rocprofv3 output (no GPU)")
+    ap.add_argument("--inputs", nargs="+", help="rocprofv3 files for --summarize: a kernel "
+                    "trace (kernels, overlap), FETCH_SIZE then WRITE_SIZE counter csv "
+                    "(traffic), or the MFMA counter csv (mfma)")
+    ap.add_argument("--profile-cmd", action="append", default=[],
+                    help="the command(s) that made the --inputs, quoted in the summary")
+    ap.add_argument("--out", default=None, help="summary file (default profiles/<kind>_<wl>.md)")
     args = ap.parse_args()
+
+    if args.summarize:
+        return summarize(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -213,83 +393,27 @@ def main():
 
     import torch
     import combine_expert_ffn_amd as M
-    from combine_expert_ffn_amd.inputs import WORKLOADS, make_inputs
+    from combine_expert_ffn_amd.inputs import WORKLOADS
 
     if not torch.cuda.is_available():
         err("bench.py: no GPU visible")
         sys.exit(1)
     M.lib()  # fails loudly if libmoe.so is not built
+    if args.group < 2 or args.group % 2:
+        err("bench.py: --group must be even")
+        sys.exit(2)
     w = WORKLOADS[args.workload]
     if args.tokens:
         w = w.with_tokens(args.tokens)
     err(f"[bench] workload {w.name}: T={w.T} d={w.d} F={w.F} E={w.E} E_l={w.E_l} K={w.K} "
         f"{w.dtype} route={w.route}")
-    inp = make_inputs(w, seed=0, microbatches=2)
-    s = M.shape_of(w)
-    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(w.dtype, torch.float32)
-    D = lambda a: torch.from_numpy(a).to("cuda", tdt)
-    F32 = lambda a: torch.from_numpy(a).to("cuda")
-    topk = w.route == "topk"
-    mode = M.MOE_ROUTE_TOPK if topk else M.MOE_ROUTE_FORCE_BALANCE
-    W_gu, W_down = D(inp["W_gu"]), D(inp["W_down"])
-    W_r = D(inp["W_r"]) if topk else None
-    bias = F32(inp["bias"]) if inp["bias"] is not None else None
-    dW_gu = torch.zeros(w.E_l, 2 * w.F, w.d, dtype=torch.float32, device="cuda")
-    dW_down = torch.zeros(w.E_l, w.d, w.F, dtype=torch.float32, device="cuda")
-    dW_r = torch.zeros(w.d, w.E, dtype=torch.float32, device="cuda") if topk else None
-    ws = torch.empty(M.moe_step_workspace_bytes_shared(s, w.F_s), dtype=torch.uint8,
-                     device="cuda")
-    fused = args.fused_permute == "on"
-    pipelined = args.pipeline == "on"
-    G = args.group
-    if G < 2 or G % 2:
-        err("bench.py: --group must be even")
-        sys.exit(2)
-    # flags of every step: the fused permute and the wgrad's place in the
-    # backward stream's order (both leave the results unchanged)
-    FUSED = ((M.MOE_STEP_FUSED_PERMUTE if fused else 0) |
-             (M.MOE_STEP_MID_WGRAD if args.wgrad_order == "mid" else 0))
-    shared = None
-    if w.F_s:  # a shared expert beside the routed ones
-        shared = (D(inp["W_gu_s"]), D(inp["W_down_s"]),
-                  torch.zeros(2 * w.F_s, w.d, dtype=torch.float32, device="cuda"),
-                  torch.zeros(w.d, w.F_s, dtype=torch.float32, device="cuda"))
-    mbs = [M.MicroBatch(s, x=D(inp["x"]), dout=D(inp["dout"]),
-                        gates=None if topk else F32(inp["gates"]), fused=fused, F_s=w.F_s),
-           M.MicroBatch(s, x=D(inp["x_b"]), dout=D(inp["dout_b"]),
-                        gates=None if topk else F32(inp["gates_b"]), fused=fused, F_s=w.F_s)]
     s0 = torch.cuda.current_stream()
     s1 = torch.cuda.Stream()
+    L = Layer(w, args, s0, s1)
+    SER = M.MOE_STEP_SERIALIZE
 
-    def step(fwd, bwd, flags):
-        st = M.make_step(s, mode, W_gu, W_down, dW_gu, dW_down, ws, fwd=fwd, bwd=bwd, W_r=W_r,
-                         bias=bias, dW_r=dW_r, accumulate=M.MOE_ACCUM_DW, shared=shared)
-        M.moe_overlap_step(st, s0, s1, flags | FUSED)
-
-    def make(i):  # step i forwards one micro-batch and back-propagates the other
-        return M.make_step(s, mode, W_gu, W_down, dW_gu, dW_down, ws, fwd=mbs[(i + 1) % 2],
-                           bwd=mbs[i % 2], W_r=W_r, bias=bias, dW_r=dW_r,
-                           accumulate=M.MOE_ACCUM_DW, shared=shared)
-
-    def issue(i0, n, flags, q):
-        """Issue steps i0 .. i0+n-1 on q (and s1): one pipelined moe_overlap_steps
-        call per group of G steps for overlapped steps with --pipeline on, else one
-        moe_overlap_step call per step."""
-        if pipelined and not flags & M.MOE_STEP_SERIALIZE:
-            for g0 in range(i0, i0 + n, G):
-                M.moe_overlap_steps([make(j) for j in range(g0, min(g0 + G, i0 + n))], q, s1,
-                                    flags | FUSED)
-        else:
-            for j in range(i0, i0 + n):
-                M.moe_overlap_step(make(j), q, s1, flags | FUSED)
-        return i0 + n
-
-    def run_loop(n, flags, i0):
-        return issue(i0, n, flags, s0)
-
-    step(mbs[0], None, 0)  # prime: micro-batch 0 forwarded
     if args.counter_pass:
-        run_loop(args.steps, M.MOE_STEP_SERIALIZE, 0)
+        L.issue(args.steps, SER)
         # copy probe: a plain elementwise pass (negation) that reads and writes
         # COPY_PROBE_BYTES each, larger than the last-level cache, so the
         # counters' reading for it calibrates bytes per counted KiB
@@ -301,145 +425,121 @@ def main():
         err(f"[bench] counter pass done: {args.steps} serialized steps, 3 copy probes of "
             f"{COPY_PROBE_BYTES} bytes")
         return
-    i = run_loop(args.warmup, 0, 0)
+    L.issue(args.warmup, 0)
     torch.cuda.synchronize()
-    counts = [mbs[k].counts.cpu() for k in range(2)]
-    N = int(counts[0].sum())
-    T_loc = int((mbs[0].row_of_pair >= 0).any(dim=1).sum())
+    counts = L.mbs[0].counts.cpu()
+    N = int(counts.sum())
+    T_loc = int((L.mbs[0].row_of_pair >= 0).any(dim=1).sum())
 
     if args.serialized_only:
-        i = run_loop(args.warmup + args.steps, M.MOE_STEP_SERIALIZE, i)
+        L.issue(args.warmup + args.steps, SER)
         torch.cuda.synchronize()
         err(f"[bench] serialized-only pass done: {args.warmup + args.steps} steps")
         return
-    # ---- timed region 1: overlapped 1F1B steps (the product schedule) -> value
-    torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(s0)
-    i = run_loop(args.steps, 0, i)
-    ev1.record(s0)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
-    err(f"[bench] overlapped: {ms_step:.4f} ms/step (wall {1e3 * wall / args.steps:.4f})")
     if args.overlapped_only:
+        ev0.record(s0)
+        L.issue(args.steps, 0)
+        ev1.record(s0)
+        torch.cuda.synchronize()
+        err(f"[bench] overlapped-only: {ev0.elapsed_time(ev1) / args.steps:.4f} ms/step")
         return
-    ms_eager = ms_step
 
-    # ---- timed region 1b: the same overlapped steps replayed from a HIP graph
-    # holding two consecutive steps (the micro-batches swap roles each step)
-    # -> value.  The library records only kernels and events into the graph.
-    Gk, rem = group_plan(args.steps, G)
-    medians = {}  # median per-step time over the graph replays, by serialize flag
-
-    def graph_ms(i, flags):
-        """Capture Gk consecutive steps with `flags` into one HIP graph (Gk even,
-        so the micro-batches' roles at the end match the start), replay it
-        (warm-up, then timed), and time exactly --steps steps: the replays plus
-        `rem` (0 or 1) eager steps inside the same timed region; returns (ms per
-        step, wall ms per step, i)."""
-        K = args.steps
-        if Gk is None:  # too few steps for a graph: all eager
-            i = issue(i, max(2, args.warmup), flags, s0)
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            ev0.record(s0)
-            i = issue(i, K, flags, s0)
-            ev1.record(s0)
-            torch.cuda.synchronize()
-            wall = time.perf_counter() - t0
-            return ev0.elapsed_time(ev1) / K, 1e3 * wall / K, i
-        g = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream()
-        cap.wait_stream(s0)
-        with torch.cuda.graph(g, stream=cap, capture_error_mode="thread_local"):
-            issue(i, Gk, flags, torch.cuda.current_stream())
-        i += Gk
-        warm = max(1, args.warmup // Gk)
-        for _ in range(warm):
+    # ---- timed region: exactly --steps overlapped 1F1B steps -> value.  With
+    # --graph on they are replays of one captured graph of Gk steps (plus one
+    # eager step when --steps is odd); the library records only kernels and
+    # events into the graph.
+    K = args.steps
+    Gk, rem = group_plan(K, args.group) if args.graph == "on" else (None, K)
+    replay_ms = []
+    if Gk:
+        g = L.capture(Gk, 0)
+        for _ in range(max(1, args.warmup // Gk)):
             g.replay()
         torch.cuda.synchronize()
         reps = (K - rem) // Gk
-        i += Gk * warm
-        # an event after every replay as well: per-replay times for the median
         marks = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
         t0 = time.perf_counter()
         ev0.record(s0)
         for r in range(reps):
             g.replay()
             marks[r].record(s0)
-        i += Gk * reps
-        i = issue(i, rem, flags, s0)
+        L.issue(rem, 0)
         ev1.record(s0)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        per = [ev0.elapsed_time(marks[0]) / Gk] + [marks[r - 1].elapsed_time(marks[r]) / Gk
-                                                  for r in range(1, reps)]
-        medians[flags & M.MOE_STEP_SERIALIZE] = sorted(per)[len(per) // 2]
-        return ev0.elapsed_time(ev1) / K, 1e3 * wall / K, i
+        replay_ms = [ev0.elapsed_time(marks[0]) / Gk] + \
+            [marks[r - 1].elapsed_time(marks[r]) / Gk for r in range(1, reps)]
+        launch = f"hipGraph replay ({Gk} steps per graph)" + (" + 1 eager step" if rem else "")
+    else:
+        t0 = time.perf_counter()
+        ev0.record(s0)
+        L.issue(K, 0)
+        ev1.record(s0)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        launch = "eager launches"
+    ms_step = ev0.elapsed_time(ev1) / K
+    err(f"[bench] overlapped ({launch}): {ms_step:.4f} ms/step (wall {1e3 * wall / K:.4f})")
 
-    launch = "eager launches"
-    ms_serial_graph = None
-    if args.graph == "on":
-        ms_step, wall_ms, i = graph_ms(i, 0)
-        launch = (f"hipGraph replay ({Gk} steps per graph)" if Gk else "eager launches") + \
-            (" + 1 eager step" if Gk and rem else "")
-        err(f"[bench] overlapped, graph replay: {ms_step:.4f} ms/step (wall {wall_ms:.4f})")
-        ms_serial_graph, wall_ms, i = graph_ms(i, M.MOE_STEP_SERIALIZE)
-        err(f"[bench] serialized, graph replay: {ms_serial_graph:.4f} ms/step "
-            f"(wall {wall_ms:.4f})")
+    # ---- overlapped against serialized, alternated (A/B) after the timed
+    # region, as graph replays and as eager launches
+    G = args.group
+    o_g, s_g = overlap_ab(L, G, args.ab_rounds, graph=True)
+    err(f"[bench] A/B graph replays: overlapped {o_g:.4f} / serialized {s_g:.4f} ms/step "
+        f"-> x{s_g / o_g:.3f}")
+    o_e, s_e = overlap_ab(L, G, args.ab_rounds, graph=False)
+    err(f"[bench] A/B eager: overlapped {o_e:.4f} / serialized {s_e:.4f} ms/step "
+        f"-> x{s_e / o_e:.3f}")
 
-    # ---- timed region 1c: the same steps serialized on one stream, eager
-    i = run_loop(args.warmup, M.MOE_STEP_SERIALIZE, i)
-    torch.cuda.synchronize()
-    ev0.record(s0)
-    i = run_loop(args.steps, M.MOE_STEP_SERIALIZE, i)
-    ev1.record(s0)
-    torch.cuda.synchronize()
-    ms_serial_eager = ev0.elapsed_time(ev1) / args.steps
-    err(f"[bench] serialized, eager: {ms_serial_eager:.4f} ms/step -> overlap "
-        f"x{ms_serial_eager / ms_eager:.3f} (eager vs eager)")
-
-    # ---- timed region 2: the same steps serialized on one stream, with every
-    # kernel bracketed by HIP events on its stream (no concurrency, so each
-    # kernel's interval is its own execution); per-kernel times only, the
-    # events' own cost makes this step time no baseline
-    i = run_loop(args.warmup, M.MOE_STEP_SERIALIZE, i)
+    # ---- per-kernel times: serialized steps with every kernel bracketed by
+    # HIP events on its stream (no concurrency, so each kernel's interval is
+    # its own execution); the events' own cost makes this step time no baseline
+    L.issue(args.warmup, SER)
     M.moe_timing_reset()
-    M.moe_timing_enable(64 * args.steps)
+    M.moe_timing_enable(64 * K)
     torch.cuda.synchronize()
-    ev0.record(s0)
-    i = run_loop(args.steps, M.MOE_STEP_SERIALIZE, i)
-    ev1.record(s0)
+    L.issue(K, SER)
     torch.cuda.synchronize()
     M.moe_timing_disable()
-    ms_serial_events = ev0.elapsed_time(ev1) / args.steps
     kern = M.moe_timing_report()
-    err(f"[bench] serialized (kernel events on): {ms_serial_events:.4f} ms/step")
-    ms_serial = ms_serial_graph if ms_serial_graph is not None else ms_serial_eager
-
     nonfinite = int(sum((~torch.isfinite(t.float())).sum().item()
-                        for mb in mbs for t in (mb.out, mb.dx)))
+                        for mb in L.mbs for t in (mb.out, mb.dx)))
+    peak_mem = torch.cuda.max_memory_allocated()
+
+    # ---- the two-micro-batch top-8 configuration's overlap figure
+    c4 = None
+    if args.overlap_workload != "none" and args.overlap_workload != w.name:
+        w4 = WORKLOADS[args.overlap_workload]
+        L4 = Layer(w4, args, s0, s1)
+        L4.issue(args.warmup, 0)
+        o4, s4 = overlap_ab(L4, G, args.ab_rounds, graph=True)
+        o4e, s4e = overlap_ab(L4, G, args.ab_rounds, graph=False)
+        c4 = {"workload": w4.name, "T": w4.T, "E": w4.E, "K": w4.K, "routing": w4.route,
+              "overlapped_ms_per_step": round(o4, 4), "serialized_ms_per_step": round(s4, 4),
+              "overlap_speedup": round(s4 / o4, 4),
+              "eager_overlapped_ms_per_step": round(o4e, 4),
+              "eager_serialized_ms_per_step": round(s4e, 4),
+              "eager_overlap_speedup": round(s4e / o4e, 4),
+              "method": f"median of {args.ab_rounds} alternating {G}-step runs each"}
+        err(f"[bench] {w4.name}: graph x{s4 / o4:.3f}, eager x{s4e / o4e:.3f}")
+        del L4
+        torch.cuda.synchronize()
 
     # ---- per-kernel achieved rates from the live kernel events
-    work = algorithmic(w, N, T_loc)
+    work = algorithmic(w, N, T_loc, accumulate=True, fused=L.fused)
     traffic = stored_traffic(w.name) if args.tokens is None else {}
     kernels = {}
     for name, (tot_ms, n) in sorted(kern.items(), key=lambda kv: -kv[1][0]):
         avg_s = tot_ms / 1e3 / max(n, 1)
-        ent = {"avg_us": round(avg_s * 1e6, 2), "launches_per_step": round(n / args.steps, 3),
-               "ms_per_step": round(tot_ms / args.steps, 4)}
-        step_s = tot_ms / 1e3 / args.steps   # this kernel's time per step
+        ent = {"avg_us": round(avg_s * 1e6, 2), "launches_per_step": round(n / K, 3),
+               "ms_per_step": round(tot_ms / K, 4)}
+        step_s = tot_ms / 1e3 / K   # this kernel's time per step
         if name in work:
-            kind, amount = work[name]      # per step
-            if kind == "flop":
-                ach = amount / step_s / 1e12
-                ent.update(achieved=round(ach, 1), unit="TFLOP/s",
-                           frac=round(ach / PEAK_BF16_TFLOPS, 4))
-            else:
-                ach = amount / step_s / 1e9
-                ent.update(achieved=round(ach, 1), unit="GB/s", frac=round(ach / PEAK_HBM_GBS, 4))
+            bound, ach, peak, unit, frac = rate(work[name], step_s)
+            ent.update(bound=bound, achieved=round(ach, 1), unit=unit, frac=round(frac, 4))
+            if "flop" in work[name]:
+                ent["mfma_frac"] = round(work[name]["flop"] / step_s / 1e12 / PEAK_BF16_TFLOPS, 4)
         if name in traffic:
             ent["traffic"] = traffic[name]
         kernels[name] = ent
@@ -448,25 +548,27 @@ def main():
     gemm = [k for k in GEMM_KERNELS if k in kern]
     dom = max(gemm, key=lambda k: kern[k][0])
     dom_avg_s = kern[dom][0] / 1e3 / kern[dom][1]
-    dom_per_step = kern[dom][1] / args.steps
-    dom_ach = work[dom][1] / (dom_avg_s * dom_per_step) / 1e12
-    gemm_flops = sum(work[k][1] * args.steps for k in gemm)
-    gemm_s = sum(kern[k][0] / 1e3 for k in gemm)
-    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(dom_ach, 1),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dom_ach / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic.get(dom),
-                "algorithmic_per_launch": f"{work[dom][1] / dom_per_step:.4g} flop",
+    dom_per_step = kern[dom][1] / K
+    per_launch = {u: v / dom_per_step for u, v in work[dom].items()}
+    bound, ach, peak, unit, frac = rate(per_launch, dom_avg_s)
+    roofline = {"kernel": dom, "bound": bound, "achieved": round(ach, 1), "peak": peak,
+                "unit": unit, "frac": round(frac, 4), "traffic": traffic.get(dom),
+                "algorithmic_per_launch": {"flop": f"{per_launch['flop']:.4g}",
+                                           "byte": f"{per_launch['byte']:.4g}"},
+                "mfma_frac": round(per_launch["flop"] / dom_avg_s / 1e12 / PEAK_BF16_TFLOPS, 4),
                 "launches_per_step": round(dom_per_step, 3),
                 "avg_launch_us": round(dom_avg_s * 1e6, 2)}
+    gemm_flops = sum(work[k]["flop"] * K for k in gemm)
+    gemm_s = sum(kern[k][0] / 1e3 for k in gemm)
     # the dispatch kernel; with the fused permute there is none (GEMM1 gathers x),
     # and the forward's remaining permute-class kernel, combine, is reported
-    disp_kernel = "combine" if fused else "permute"
+    disp_kernel = "combine" if L.fused else "permute"
     disp = kernels.get(disp_kernel, {})
 
     tokens_per_s = w.T / (ms_step / 1e3)
     cpu = None
     if args.cpu_baseline == "on":
-        cpu = cpu_oracle_baseline(w, inp)
+        cpu = cpu_oracle_baseline(w, L.inp)
         err(f"[bench] cpu oracle: {cpu}")
 
     line = {
@@ -474,7 +576,7 @@ def main():
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
@@ -488,33 +590,364 @@ def main():
                            "two streams, " + ("wgrad between the two dgrad GEMMs"
                                               if args.wgrad_order == "mid" else
                                               "wgrad deferred to the end"),
+                   "weight_grads": "float32, accumulated every step",
                    "launch": launch,
                    "pipeline": (f"moe_overlap_steps, {G} steps per call, stream roles "
-                                "alternating" if pipelined else
+                                "alternating" if L.pipelined else
                                 "one moe_overlap_step per step, joined at each boundary"),
-                   "permute": "fused into GEMM1 and wgrad" if fused else "separate kernel",
+                   "permute": "fused into GEMM1 and wgrad" if L.fused else "separate kernel",
                    "shared_expert_F": w.F_s},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "grouped_gemm_mfma_util": round(gemm_flops / gemm_s / 1e12 / PEAK_BF16_TFLOPS, 4),
         "dispatch_hbm_gbs": disp.get("achieved"),
         "dispatch_hbm_kernel": disp_kernel,
-        # serialized = the same steps on one stream, launched the same way
-        # (graph replay or eager) as the overlapped value, no kernel events
-        "serialized_ms_per_step": round(ms_serial, 4),
-        # median over the timed graph replays of their per-step time
-        "median_replay_ms_per_step": (round(medians[0], 4) if 0 in medians else None),
-        "median_replay_serialized_ms_per_step": (
-            round(medians[M.MOE_STEP_SERIALIZE], 4) if M.MOE_STEP_SERIALIZE in medians
-            else None),
-        "overlap_speedup": round(ms_serial / ms_step, 4),
-        "eager_overlapped_ms_per_step": round(ms_eager, 4),
-        "eager_serialized_ms_per_step": round(ms_serial_eager, 4),
-        "eager_overlap_speedup": round(ms_serial_eager / ms_eager, 4),
+        "median_replay_ms_per_step": (round(statistics.median(replay_ms), 4)
+                                      if replay_ms else None),
+        # overlapped vs serialized: medians of alternating runs of the same
+        # steps (graph replays, then eager launches)
+        "overlapped_ms_per_step_ab": round(o_g, 4),
+        "serialized_ms_per_step": round(s_g, 4),
+        "overlap_speedup": round(s_g / o_g, 4),
+        "eager_overlapped_ms_per_step": round(o_e, 4),
+        "eager_serialized_ms_per_step": round(s_e, 4),
+        "eager_overlap_speedup": round(s_e / o_e, 4),
+        "overlap_two_microbatch": c4,
+        "peak_device_memory_gib": round(peak_mem / 2 ** 30, 2),
         "kernels": kernels,
         "nonfinite_outputs": nonfinite,
     }
     print(json.dumps(line), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 output -> profiles/ summaries (no GPU needed)
+# ---------------------------------------------------------------------------
+# kernel symbol -> the name the library times it under (MOE_LAUNCH); wgrad_kernel
+# is split by its ROUTER template argument (the router weight gradient reuses it)
+_CLASS = [("GateUpOp", "ffn_gate_up"), ("DownOp", "ffn_down"), ("DgradActOp", "dgrad_act"),
+          ("DgradInOp", "dgrad_in"), ("combine_bwd_kernel", "combine_bwd"),
+          ("dispatch_bwd_kernel", "dispatch_bwd"), ("combine_kernel", "combine"),
+          ("permute_kernel", "permute"), ("transpose_batched_kernel", "transpose_w"),
+          ("transpose_wr_kernel", "transpose_wr"), ("plan_hist_kernel", "plan_hist"),
+          ("plan_scan_kernel", "plan_scan"), ("plan_rank_kernel", "plan_rank"),
+          ("force_balance_kernel", "force_balance"), ("router_kernel", "router"),
+          ("topk_kernel", "topk"), ("dlogits_kernel", "dlogits"),
+          ("dwr_reduce", "dwr_reduce"), ("dwr_partial_kernel", "dwr_partial"),
+          ("shared_plan_kernel", "shared_plan")]
+
+
+def bench_name(sym):
+    """The library's timing name of a kernel symbol, or None (not ours)."""
+    if "moe::" not in sym:
+        return None
+    i = sym.find("wgrad_kernel<")
+    if i >= 0 and "f32_wgrad" not in sym:
+        depth, j, args, cur = 0, i + len("wgrad_kernel<"), [], ""
+        while j < len(sym):
+            ch = sym[j]
+            if ch == "<":
+                depth += 1
+            elif ch == ">":
+                if depth == 0:
+                    break
+                depth -= 1
+            if ch == "," and depth == 0:
+                args.append(cur.strip())
+                cur = ""
+            else:
+                cur += ch
+            j += 1
+        args.append(cur.strip())
+        return "dwr_mfma" if args and args[-1] == "true" else "wgrad"
+    for k, v in _CLASS:
+        if k in sym:
+            return v
+    return None
+
+
+def read_trace(path):
+    """[(symbol, start_ns, end_ns)] of a rocprofv3 kernel trace (csv or rocpd db)."""
+    if path.endswith(".db"):
+        import sqlite3
+        c = sqlite3.connect(path)
+        rows = c.execute("select name, start, end from kernels order by start")
+        return [(r[0], int(r[1]), int(r[2])) for r in rows]
+    out = []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            out.append((r["Kernel_Name"], int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    out.sort(key=lambda r: r[1])
+    return out
+
+
+def read_counters(path):
+    """{dispatch: (symbol, {counter: value summed over instances}, duration_ns)}."""
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    sym, dur = {}, {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            d = int(r["Dispatch_Id"])
+            per[d][r["Counter_Name"]] += float(r["Counter_Value"])
+            sym[d] = r["Kernel_Name"]
+            dur[d] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    return {d: (sym[d], dict(per[d]), dur[d]) for d in per}
+
+
+def _workload_for_summary(args):
+    from combine_expert_ffn_amd.inputs import WORKLOADS
+    w = WORKLOADS[args.workload]
+    if args.tokens:
+        w = w.with_tokens(args.tokens)
+    # every expert local (the default workload): N = T*K rows, all T tokens
+    N, T_loc = (w.T * w.K, w.T) if w.E_l == w.E else (None, None)
+    return w, N, T_loc
+
+
+def _cmds(args):
+    return "\n".join(args.profile_cmd) if args.profile_cmd else "(not given)"
+
+
+def summarize(args):
+    w, N, T_loc = _workload_for_summary(args)
+    out = args.out or os.path.join(TRAFFIC_DIR, f"{args.summarize}_{w.name}.md")
+    desc = (f"{w.name} (T={w.T}, d={w.d}, F={w.F}, {w.E_l} of {w.E} experts local, top-{w.K}, "
+            f"{w.dtype}, {w.route})")
+    txt = {"kernels": _sum_kernels, "traffic": _sum_traffic, "mfma": _sum_mfma,
+           "overlap": _sum_overlap}[args.summarize](args, w, N, T_loc, desc)
+    with open(out, "w") as fh:
+        fh.write(txt)
+    err(f"[summarize] wrote {out}")
+
+
+def _sum_kernels(args, w, N, T_loc, desc):
+    rows = [(bench_name(s), s, a, b) for s, a, b in read_trace(args.inputs[0])]
+    by = collections.OrderedDict()
+    for name, sym, a, b in rows:
+        if name:
+            by.setdefault(name, []).append((b - a) / 1e3)
+    total = sum(sum(v) for v in by.values())
+    work = algorithmic(w, N, T_loc) if N is not None else {}
+    lines = []
+    for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        h = v[len(v) // 2:]
+        rated = ""
+        if k in work and k != "dwr_mfma":
+            bound, ach, peak, unit, frac = rate(work[k], statistics.mean(h) / 1e6)
+            rated = f"{bound} {ach:.1f} {unit} = {frac:.3f}"
+        lines.append(f"| {k} | {len(v)} | {sum(v):.1f} | {sum(v) / len(v):.2f} | "
+                     f"{statistics.median(h):.2f} | {statistics.mean(h):.2f} | "
+                     f"{100 * sum(v) / total:.2f} | {rated} |")
+    return f"""# Kernel trace: {desc}
+
+Command (run from the repository root on one MI355X):
+
+```
+{_cmds(args)}
+```
+
+Kernel trace of the library's kernels (durations in microseconds), summarised
+by `python bench.py --summarize kernels --workload {w.name} --inputs <trace>`.
+`avg` is the mean over all calls; `steady median` / `steady mean` drop the
+first half of each kernel's calls (the first calls of a fresh process run
+slower while the clocks settle).  `rate` divides the kernel's algorithmic work
+per launch (bench.py `algorithmic`: flops, and bytes with one pass over every
+operand and result, float32 weight gradients read and written) by the steady
+mean and rates it against whichever MI355X peak bounds it (2.5 PFLOP/s dense
+bf16 or 8 TB/s HBM).
+
+| kernel | calls | total us | avg us | steady median us | steady mean us | % | rate (bound, achieved = frac of peak) |
+|---|---|---|---|---|---|---|---|
+""" + "\n".join(lines) + "\n"
+
+
+def _sum_traffic(args, w, N, T_loc, desc):
+    F, W = read_counters(args.inputs[0]), read_counters(args.inputs[1])
+    probe_kib = COPY_PROBE_BYTES / 1024
+
+    def probe(rec, counter):
+        v = [c.get(counter, 0.0) for s, c, _ in rec.values() if "neg_kernel" in s or
+             ("neg" in s and "at::native" in s)]
+        return statistics.median(v)
+
+    pf, pw = probe(F, "FETCH_SIZE"), probe(W, "WRITE_SIZE")
+    ff, fw = probe_kib / pf, probe_kib / pw
+
+    def per_kernel(rec, counter):
+        agg = collections.defaultdict(list)
+        for s, c, _ in rec.values():
+            b = bench_name(s)
+            if b:
+                agg[b].append(c.get(counter, 0.0))
+        return agg
+
+    aF, aW = per_kernel(F, "FETCH_SIZE"), per_kernel(W, "WRITE_SIZE")
+    work = algorithmic(w, N, T_loc) if N is not None else {}
+    rec = {"workload": w.name, "copy_probe_bytes": COPY_PROBE_BYTES,
+           "fetch_factor": round(ff, 4), "write_factor": round(fw, 4), "kernels": {}}
+    lines = []
+    for k in sorted(aF, key=lambda k: -statistics.median(aF[k])):
+        if k not in aW:
+            continue
+        f, wr = statistics.median(aF[k]), statistics.median(aW[k])
+        rb, wb = f * ff * 1024, wr * fw * 1024
+        alg = work.get(k, {}).get("byte")
+        ent = {"fetch_kib_per_dispatch": round(f, 1), "write_kib_per_dispatch": round(wr, 1),
+               "dispatches": len(aF[k]), "hbm_bytes_per_launch": int(round(rb + wb))}
+        if k in KERNEL_SOURCE:
+            ent["source_sha256"] = kernel_source_hash(k)
+        rec["kernels"][k] = ent
+        lines.append(f"| {k} | {len(aF[k])} | {f:.0f} | {wr:.0f} | {rb / 1e6:.1f} | "
+                     f"{wb / 1e6:.1f} | " + (f"{alg / 1e6:.1f} | {(rb + wb) / alg:.2f} |"
+                                             if alg else "- | - |"))
+    return f"""# HBM traffic per kernel launch: {desc}
+
+Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, as rocprofv3 reports
+them), each from its own run of the same program, scaled by what the same
+counter reads for a copy probe of known size (an elementwise negation reading
+and writing {COPY_PROBE_BYTES} bytes, larger than the last-level cache); per
+kernel the median over its dispatches.  Summarised by `python bench.py
+--summarize traffic --workload {w.name} --inputs <fetch csv> <write csv>`.
+Kernels are named by the library's launch names; the router weight gradient
+(wgrad_kernel with its ROUTER template argument set) is `dwr_mfma`, not
+`wgrad`.  `algorithmic` is one pass over every operand and result (bench.py
+`algorithmic`, float32 weight gradients read and written).
+
+Commands (run from the repository root on one MI355X):
+
+```
+{_cmds(args)}
+```
+
+Copy probe: FETCH_SIZE {pf:.0f} KiB (factor {ff:.4f}), WRITE_SIZE {pw:.0f} KiB (factor {fw:.4f}) for {probe_kib:.0f} KiB moved each way.
+
+| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | written MB (scaled) | algorithmic MB | measured / algorithmic |
+|---|---|---|---|---|---|---|---|
+""" + "\n".join(lines) + """
+
+Machine-readable record (bench.py reads `hbm_bytes_per_launch` while the kernel's source hash still matches):
+
+```json
+""" + json.dumps(rec, indent=1) + "\n```\n"
+
+
+def _sum_mfma(args, w, N, T_loc, desc):
+    rec = read_counters(args.inputs[0])
+    work = algorithmic(w, N, T_loc) if N is not None else {}
+    SIMDS, XCDS = 1024, 8
+    peak_per_clk = PEAK_BF16_TFLOPS * 1e12 / 2.4e9
+    agg = collections.defaultdict(list)
+    for s, c, dur in rec.values():
+        b = bench_name(s)
+        if b in GEMM_KERNELS or b in ("router", "dwr_mfma"):
+            agg[b].append((c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0),
+                           c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0),
+                           c.get("GRBM_GUI_ACTIVE", 0.0), dur))
+    lines = []
+    for k, v in sorted(agg.items(), key=lambda kv: -statistics.median(x[3] for x in kv[1])):
+        busy = statistics.median(x[0] for x in v)
+        mops = statistics.median(x[1] for x in v)
+        gui = statistics.median(x[2] for x in v) / XCDS
+        us = statistics.median(x[3] for x in v) / 1e3
+        fl = mops * 512
+        alg = work.get(k, {}).get("flop")
+        lines.append(f"| {k} | {len(v)} | {us:.1f} | {gui / (us * 1e3):.2f} | "
+                     f"{100 * busy / (gui * SIMDS):.1f} | {fl / 1e9:.1f} | "
+                     + (f"{alg / 1e9:.1f} | " if alg else "- | ")
+                     + f"{100 * fl / (gui * peak_per_clk):.1f} | {fl / (us * 1e-6) / 1e12:.0f} |")
+    return f"""# Matrix-core counters per GEMM: {desc}
+
+Counters SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16 and
+GRBM_GUI_ACTIVE per dispatch (medians over each kernel's dispatches),
+summarised by `python bench.py --summarize mfma --workload {w.name} --inputs
+<counter csv>`.  `clock` = GPU-active cycles (per XCD) / duration; `MFMA busy`
+= busy cycles / (active cycles x 1024 SIMDs); counted flops = MOPS x 512;
+`of peak at clock` = counted flops / (active cycles x 2.5 PFLOP/s / 2.4 GHz),
+i.e. the matrix cores' share at the clock the kernel actually ran at.
+
+Command (run from the repository root on one MI355X):
+
+```
+{_cmds(args)}
+```
+
+| kernel | dispatches | us | clock GHz | MFMA busy % | counted GFLOP | algorithmic GFLOP | of peak at clock % | TFLOP/s |
+|---|---|---|---|---|---|---|---|---|
+""" + "\n".join(lines) + "\n"
+
+
+def _union(iv):
+    merged = []
+    for s, e in sorted(iv):
+        if merged and s <= merged[-1][1]:
+            merged[-1][1] = max(merged[-1][1], e)
+        else:
+            merged.append([s, e])
+    return merged
+
+
+def _length(m):
+    return sum(e - s for s, e in m)
+
+
+def _intersect(a, b):
+    i = j = 0
+    out = []
+    while i < len(a) and j < len(b):
+        s, e = max(a[i][0], b[j][0]), min(a[i][1], b[j][1])
+        if s < e:
+            out.append((s, e))
+        if a[i][1] < b[j][1]:
+            i += 1
+        else:
+            j += 1
+    return out
+
+
+_GEMM_CLASS = GEMM_KERNELS + ("transpose_w", "router", "dwr_mfma")
+_PERM_CLASS = ("permute", "combine", "combine_bwd", "dispatch_bwd", "plan_hist", "plan_scan",
+               "plan_rank", "force_balance", "topk", "dlogits", "dwr_reduce", "transpose_wr")
+
+
+def _sum_overlap(args, w, N, T_loc, desc):
+    rows = [(bench_name(s), a, b) for s, a, b in read_trace(args.inputs[0])]
+    rows = [r for r in rows if r[0]]
+    t0, t1 = rows[0][1], max(r[2] for r in rows)
+    cut = t0 + 0.4 * (t1 - t0)
+    sel = [r for r in rows if r[1] >= cut]
+    g = _union([(a, b) for n, a, b in sel if n in _GEMM_CLASS])
+    p = _union([(a, b) for n, a, b in sel if n in _PERM_CLASS])
+    busy = _union([(a, b) for n, a, b in sel])
+    inter = _intersect(g, p)
+    ng = sum(1 for r in sel if r[0] in _GEMM_CLASS)
+    npm = sum(1 for r in sel if r[0] in _PERM_CLASS)
+    wend = [b for n, a, b in rows if n == "wgrad"]
+    half = wend[len(wend) // 2:]
+    step_us = (half[-1] - half[0]) / 1e3 / max(1, len(half) - 1) if len(half) > 1 else float("nan")
+    return f"""# Overlap of the two streams: pipelined 1F1B steps, {desc}
+
+Command (run from the repository root on one MI355X):
+
+```
+{_cmds(args)}
+```
+
+The steps run through `moe_overlap_steps` (the streams' roles alternating each
+step, routed wgrad between the two dgrad GEMMs), eager launches under the
+profiler.  Interval analysis over the last 60 % of the trace, summarised by
+`python bench.py --summarize overlap --workload {w.name} --inputs <trace>`.
+GEMM class: expert GEMMs, router GEMMs and weight transposes; dispatch/combine
+class: plan, top-k, permute, combine and their backwards.
+
+| quantity | value |
+|---|---|
+| GEMM-class kernels / union (us) | {ng} / {_length(g) / 1e3:.1f} |
+| dispatch/combine-class kernels / union (us) | {npm} / {_length(p) / 1e3:.1f} |
+| intersection (us) | {_length(inter) / 1e3:.1f} |
+| share of dispatch/combine time under a GEMM | {100 * _length(inter) / max(1, _length(p)):.2f} % |
+| busy (any kernel) union (us) | {_length(busy) / 1e3:.1f} |
+| steady step time under the profiler (us, wgrad to wgrad, second half) | {step_us:.1f} |
+"""
 
 
 if __name__ == "__main__":

@@ -646,6 +646,9 @@ struct StepCtx {
   bool fused;   // fused permute: no xp, GEMM1 / wgrad gather from x
   void* wsSA;   // shared-expert workspace of the forward micro-batch
   void* wsSB;   // and of the backward one
+  void* wsW;    // non-null: a workspace whose dgrad weight copies are already
+                // made (once per moe_overlap_steps call); the dgrad reads them
+                // there instead of making its own
 };
 
 static int fwd_route(const StepCtx& c, const moe_mb* A, hipStream_t q) {
@@ -691,7 +694,8 @@ static int bwd_route(const StepCtx& c, const moe_mb* B, hipStream_t q) {
 static int bwd_dgrad(const StepCtx& c, const moe_mb* B, bool weights_ready, hipStream_t q,
                      int parts = kDgradBoth) {
   return launch_ffn_dgrad(c.s, B->dyp, B->h, B->offsets, B->tile_offsets, c.st->W_gu,
-                          c.st->W_down, B->dh, B->dxp, c.wsB, weights_ready, q, parts);
+                          c.st->W_down, B->dh, B->dxp, c.wsW ? c.wsW : c.wsB,
+                          c.wsW ? true : weights_ready, q, parts);
 }
 static int bwd_dispatch(const StepCtx& c, const moe_mb* B, hipStream_t q) {
   return do_dispatch_bwd(c.s, B->dxp, B->row_of_pair, B->idx, c.router ? B->dlogits : nullptr,
@@ -769,9 +773,9 @@ static int check_step(const moe_step* st, int flags, const char* fn) {
 
 }  // namespace moe
 
-extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t s1, int flags) {
-  g_err[0] = 0;
-  if (int rc = check_step(st, flags, "moe_overlap_step")) return rc;
+namespace moe {
+// One step (arguments checked by the caller).  wsW: see StepCtx.
+static int step_impl(const moe_step* st, hipStream_t s0, hipStream_t s1, int flags, void* wsW) {
   const moe_shape* s = &st->shape;
   const int mode = st->route_mode;
   const moe_mb* A = st->fwd;
@@ -781,7 +785,7 @@ extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t 
   const size_t one = ws_one(s);
   const size_t sh = shared ? ws_shared(s, st->F_s) : 0;
   StepCtx c{st, s, st->ws, (char*)st->ws + one, mode == MOE_ROUTE_TOPK, fused,
-            (char*)st->ws + 2 * one, (char*)st->ws + 2 * one + sh};
+            (char*)st->ws + 2 * one, (char*)st->ws + 2 * one + sh, wsW};
   const bool serial = (flags & MOE_STEP_SERIALIZE) || s0 == s1;
   const bool eager = (flags & MOE_STEP_EAGER_WGRAD) != 0;
   const bool skip_w = (flags & MOE_STEP_SKIP_WGRAD) != 0;
@@ -870,6 +874,14 @@ extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t 
   HIPTRY(hipEventRecord(ev->end, s1));
   HIPTRY(hipStreamWaitEvent(s0, ev->end, 0));
   return MOE_OK;
+}
+}  // namespace moe
+
+extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t s1, int flags) {
+  using namespace moe;
+  g_err[0] = 0;
+  if (int rc = check_step(st, flags, "moe_overlap_step")) return rc;
+  return step_impl(st, s0, s1, flags, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -1007,10 +1019,24 @@ extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, h
       return set_error(MOE_ERR_ARG,
                        "moe_overlap_steps: step %d must back-propagate the micro-batch that "
                        "step %d forwarded", j, j - 1);
+    if (j > 0 && (st->W_gu != steps[0].W_gu || st->W_down != steps[0].W_down))
+      return set_error(MOE_ERR_ARG,
+                       "moe_overlap_steps: step %d has other expert weights than step 0", j);
+  }
+  // The expert weights are the same for every step of the call, so the
+  // dgrad's transposed copies of them are made once, at the start, into the
+  // first half of the workspace, and every step's dgrad on either stream reads
+  // them there (no other call writes that region during the call).
+  bool any_bwd = false;
+  for (int j = 0; j < n; ++j) any_bwd |= steps[j].bwd != nullptr;
+  void* wsW = nullptr;
+  if (any_bwd) {
+    wsW = steps[0].ws;
+    TRY(launch_dgrad_weights(&steps[0].shape, steps[0].W_gu, steps[0].W_down, wsW, s0));
   }
   const bool serial = (flags & MOE_STEP_SERIALIZE) || s0 == s1;
   if (serial) {
-    for (int j = 0; j < n; ++j) TRY(moe_overlap_step(&steps[j], s0, s0, flags));
+    for (int j = 0; j < n; ++j) TRY(step_impl(&steps[j], s0, s0, flags, wsW));
     return MOE_OK;
   }
   MultiEvents* ev = nullptr;
@@ -1042,7 +1068,7 @@ extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, h
     char* shalf_s0 = ws + 2 * one + sh;
     StepCtx c{st, s, even ? half_s1 : half_s0, even ? half_s0 : half_s1,
               st->route_mode == MOE_ROUTE_TOPK, fused,
-              even ? shalf_s1 : shalf_s0, even ? shalf_s0 : shalf_s1};
+              even ? shalf_s1 : shalf_s0, even ? shalf_s0 : shalf_s1, wsW};
     // The forward of step j also waits for the backward of step j - 2 (on
     // the other stream), the last earlier chain not ordered before it by its
     // stream, so a forward may reuse the buffers of any micro-batch

@@ -423,7 +423,10 @@ int moe_overlap_step(const moe_step* st, hipStream_t s_compute, hipStream_t s_co
  * page 2, "MoE 1F1B overlap": the micro-batch forwarded in one step is
  * back-propagated in the next), pipelined across the step boundaries.
  * steps[j] describes step j as for moe_overlap_step; all steps share one shape,
- * one workspace (ws, ws_bytes) and one shared-expert width F_s; for j >= 1,
+ * one workspace (ws, ws_bytes), one shared-expert width F_s and the same expert
+ * weights (W_gu, W_down: the micro-batches of one layer between two weight
+ * updates), whose transposed copies for the dgrad are made once, at the start
+ * of the call, and read by every step's dgrad on either stream; for j >= 1,
  * steps[j].bwd must hold the same buffers as steps[j-1].fwd (field by field;
  * both may be NULL), and no step may forward and back-propagate the same
  * buffers.
@@ -447,7 +450,7 @@ int moe_overlap_step(const moe_step* st, hipStream_t s_compute, hipStream_t s_co
  * issued; the call may be captured into a HIP graph on s_compute.  Errors: as
  * moe_overlap_step (checked for every step before anything is launched), and
  * MOE_ERR_ARG for n < 1, a step whose bwd is not the previous step's fwd, steps
- * with different shapes, workspaces or F_s, or SKIP_WGRAD.
+ * with different shapes, workspaces, F_s or expert weights, or SKIP_WGRAD.
  */
 int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s_compute, hipStream_t s_copy,
                       int flags);
