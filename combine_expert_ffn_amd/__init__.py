@@ -215,6 +215,19 @@ def _chk_ffn(s, fn, offsets, tile_offsets, W_gu, W_down, **rows):
         _chk(s, fn, n, t, kind, cols)
 
 
+def moe_dispatch_noalloc(s, x, idx, counts, offsets, row_of_pair, pair_of_row, tile_offsets, xp,
+                         stream=None):
+    _chk_plan(s, "moe_dispatch_noalloc", x, idx, counts, offsets, row_of_pair, pair_of_row,
+              tile_offsets, xp)
+    check(lib().moe_dispatch_noalloc(C.byref(s), _p(x), _p(idx), _p(counts), _p(offsets),
+                                     _p(row_of_pair), _p(pair_of_row), _p(tile_offsets), _p(xp),
+                                     _stream(stream)))
+
+
+def moe_dispatch_noalloc_max_scratch() -> int:
+    return lib().moe_dispatch_noalloc_max_scratch()
+
+
 def moe_expert_ffn_fwd(s, xp, offsets, tile_offsets, W_gu, W_down, h, a, yp, stream=None):
     cap, d, F = s.T * s.K, s.d, s.F
     _chk_ffn(s, "moe_expert_ffn_fwd", offsets, tile_offsets, W_gu, W_down,

@@ -81,6 +81,8 @@ SIGNATURES = {
     "moe_version": (C.c_int, []),
     "moe_route": (C.c_int, [_SP, C.c_int, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "moe_dispatch": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+    "moe_dispatch_noalloc": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_dispatch_noalloc_max_scratch": (C.c_size_t, []),
     "moe_expert_ffn_fwd": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_expert_ffn_fwd_gather": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_combine": (C.c_int, [_SP, _P, _P, _P, _P, _P]),

@@ -558,6 +558,69 @@ int moe_dispatch_bwd(const moe_shape* s, const void* dxp, const int32_t* row_of_
 }  // extern "C"
 
 // ---------------------------------------------------------------------------
+// dispatch without a caller workspace: the plan's scratch is a fixed device
+// array of this library (one copy per GPU, held until the process ends)
+// ---------------------------------------------------------------------------
+namespace moe {
+
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// The array's device address on the current device, looked up once per
+// device with that device current.  In host code `scratch` names a host-side
+// stand-in, not device memory, so only this address may reach a kernel.
+static int scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess)
+    return set_error(MOE_ERR_HIP, "moe_dispatch_noalloc: hipGetDevice failed");
+  if (dev < 0 || dev >= 64)
+    return set_error(MOE_ERR_UNSUPPORTED, "moe_dispatch_noalloc: device %d >= 64", dev);
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return set_error(MOE_ERR_HIP, "moe_dispatch_noalloc: hipGetSymbolAddress(scratch): %s",
+                       hipGetErrorString(e));
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" size_t moe_dispatch_noalloc_max_scratch(void) { return moe::kNoAllocScratchBytes; }
+
+extern "C" int moe_dispatch_noalloc(const moe_shape* s, const void* x, const int32_t* idx,
+                                    int32_t* counts, int32_t* offsets, int32_t* row_of_pair,
+                                    int32_t* pair_of_row, int32_t* tile_offsets, void* xp,
+                                    hipStream_t stream) {
+  using namespace moe;
+  g_err[0] = 0;
+  if (int rc = validate_shape(s)) return rc;
+  if (xp) REQUIRE(x);
+  REQUIRE(idx);
+  REQUIRE(counts);
+  REQUIRE(offsets);
+  REQUIRE(row_of_pair);
+  REQUIRE(pair_of_row);
+  REQUIRE(tile_offsets);
+  const size_t need = ws_plan_bytes(s);
+  if (need > kNoAllocScratchBytes)
+    return set_error(MOE_ERR_WORKSPACE,
+                     "moe_dispatch_noalloc: the plan needs %zu bytes of scratch (2 * E_l * "
+                     "ceil(T*K / %d) * 4), more than the library's fixed %zu; use moe_dispatch "
+                     "with a workspace", need, kPlanChunk, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (int rc = scratch_address(&ws)) return rc;
+  return do_dispatch(s, x, idx, counts, offsets, row_of_pair, pair_of_row, tile_offsets, xp, ws,
+                     stream);
+}
+
+// ---------------------------------------------------------------------------
 // two-micro-batch step
 // ---------------------------------------------------------------------------
 namespace moe {

@@ -174,6 +174,32 @@ int moe_dispatch(const moe_shape* s, const void* x, const int32_t* idx,
                  void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_dispatch_noalloc - moe_dispatch for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same plan and permute, with identical results, but
+ * the plan's scratch is a fixed device array inside the library instead of a
+ * caller workspace, and the call allocates nothing.  Arguments as
+ * moe_dispatch, without ws.
+ *   Limit: the plan scratch, 2 * E_l * ceil(T*K / 2048) * 4 bytes (rounded up
+ *   to 256), must fit moe_dispatch_noalloc_max_scratch() = 4 MiB (e.g. every
+ *   E_l = 128 shape with T*K <= 8M pairs); larger shapes return
+ *   MOE_ERR_WORKSPACE before anything is launched.
+ *   Sharing: each GPU holds one copy of the array, from the first call on that
+ *   device until the process ends; every call on a GPU uses that GPU's copy,
+ *   so calls that overlap on one GPU (other streams, other host threads) race
+ *   and must be ordered by the caller.  Nothing in the scratch needs to start
+ *   at zero: each call writes every entry it reads.
+ *   The first call on a device looks the array's address up (with that device
+ *   current); errors of that lookup return MOE_ERR_HIP.
+ */
+int moe_dispatch_noalloc(const moe_shape* s, const void* x, const int32_t* idx,
+                         int32_t* counts, int32_t* offsets, int32_t* row_of_pair,
+                         int32_t* pair_of_row, int32_t* tile_offsets, void* xp,
+                         hipStream_t stream);
+/* Bytes of the fixed scratch array moe_dispatch_noalloc uses (4 MiB). */
+size_t moe_dispatch_noalloc_max_scratch(void);
+
+/*
  * moe_expert_ffn_fwd - the expert FFN computation that the token exchange is
  * overlapped with (skill card page 1, "What it is"), the mlp phase between
  * dispatch and combine (1F1B note page 2, "how the 8 ops are split").  The

@@ -279,3 +279,20 @@ def test_binding_rejects_bad_tensors_before_the_call():
         M.moe_combine(s, None, t, t, t)
     with pytest.raises(M.MoeError, match="not a torch tensor"):
         M.moe_combine(s, 123, t, t, t)
+
+
+def test_noalloc_dispatch_rejects_shapes_beyond_its_scratch():
+    """moe_dispatch_noalloc's plan scratch is a fixed 4 MiB array: a shape whose
+    plan needs more is rejected on the host before anything runs (no GPU
+    needed), with the limit in the message."""
+    assert M.moe_dispatch_noalloc_max_scratch() == 4 << 20
+    FAKE = C.c_void_p(0x1000)
+    # 256 local experts x ceil(2^24 / 2048) plan blocks x 2 x 4 bytes = 16 MiB
+    s = M.make_shape(1 << 21, 64, 64, 256, 0, 256, 8, "bf16")
+    rc = M.lib().moe_dispatch_noalloc(C.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      None)
+    assert rc == M.MOE_ERR_WORKSPACE
+    assert b"4194304" in M.lib().moe_last_error()
+    rc = M.lib().moe_dispatch_noalloc(C.byref(s), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      None)
+    assert rc == M.MOE_ERR_NULL
