@@ -543,10 +543,11 @@ def test_wgrad_gather_scattered_tokens():
     pairs = rng.permutation(T * K)[:N]             # pair t*K + k of each row
     x_h = rng.standard_normal((T, d))
     x = dev(x_h, "bf16")
-    xp = dev(x_h[pairs // K], "bf16")
-    a = dev(0.3 * rng.standard_normal((N, F)), "bf16")
-    dh = dev(0.5 * rng.standard_normal((N, 2 * F)), "bf16")
-    dyp = dev(0.1 * rng.standard_normal((N, d)), "bf16")
+    # row buffers sized to the cap T*K, as include/moe.h gives them
+    xp = dev(_pad(x_h[pairs // K], T * K), "bf16")
+    a = dev(_pad(0.3 * rng.standard_normal((N, F)), T * K), "bf16")
+    dh = dev(_pad(0.5 * rng.standard_normal((N, 2 * F)), T * K), "bf16")
+    dyp = dev(_pad(0.1 * rng.standard_normal((N, d)), T * K), "bf16")
     offsets = dev(off, "i32")
     por = dev(np.concatenate([pairs, -np.ones(T * K - N)]), "i32")
     log(f"[wgrad gather] counts={counts} T={T} K={K}")
@@ -610,17 +611,18 @@ def test_wgrad_schedules(counts, d, F):
     rng = np.random.default_rng(17)
     pairs = rng.permutation(T * K)[:N]
     x_h = rng.standard_normal((T, d))
-    x, xp = dev(x_h, "bf16"), dev(x_h[pairs // K], "bf16")
-    a = dev(0.3 * rng.standard_normal((N, F)), "bf16")
-    dh = dev(0.5 * rng.standard_normal((N, 2 * F)), "bf16")
-    dyp = dev(0.1 * rng.standard_normal((N, d)), "bf16")
+    # row buffers sized to the cap T*K, as include/moe.h gives them
+    x, xp = dev(x_h, "bf16"), dev(_pad(x_h[pairs // K], T * K), "bf16")
+    a = dev(_pad(0.3 * rng.standard_normal((N, F)), T * K), "bf16")
+    dh = dev(_pad(0.5 * rng.standard_normal((N, 2 * F)), T * K), "bf16")
+    dyp = dev(_pad(0.1 * rng.standard_normal((N, d)), T * K), "bf16")
     offsets = dev(off, "i32")
     por = dev(np.concatenate([pairs, -np.ones(T * K - N)]), "i32")
     log(f"[wgrad schedules] counts={counts} d={d} F={F}")
     dW = [torch.full((E_l, 2 * F, d), 5.0, device="cuda"),
           torch.full((E_l, d, F), 5.0, device="cuda")]
     M.moe_ffn_wgrad(s, xp, a, dh, dyp, offsets, dW[0], dW[1], 0)
-    X = [host(t) for t in (xp, a, dh, dyp)]
+    X = [host(t, N) for t in (xp, a, dh, dyp)]
     ref_gu, ref_dn = O.ffn_wgrad(*X, off)
     mag_gu, mag_dn = O.ffn_wgrad(*[np.abs(t) for t in X], off, prec="f64")
     close_reduction("dW_gu", host(dW[0]), ref_gu, mag_gu, 1e-5)
