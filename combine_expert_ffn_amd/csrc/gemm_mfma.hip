@@ -33,6 +33,8 @@
 // plan's tile_offsets (tiles of kTileM rows).
 #include "moe_internal.h"
 
+#include <type_traits>
+
 namespace moe {
 namespace {
 
@@ -755,13 +757,15 @@ __device__ __forceinline__ long long uniform64(long long v) {
 // only the first product is formed, dyp holds x [T][d], abuf holds the split
 // dlogits [T][F] (F = 2E) and dW_down receives one float32 partial [d][F] per
 // chunk; offsets, xp, dh and dW_gu are unused.
-template <bool GATHER, class E, bool ROUTER = false>
+// ACC: add into the existing values of dW (gradient accumulation) instead of
+// overwriting them.
+template <bool GATHER, class E, bool ROUTER, bool ACC>
 __global__ __launch_bounds__(512) void wgrad_kernel(
     const uint16_t* __restrict__ xp, const int32_t* __restrict__ xrows, int K,
     const uint16_t* __restrict__ abuf, const uint16_t* __restrict__ dh,
     const uint16_t* __restrict__ dyp, const int32_t* __restrict__ offsets,
     float* __restrict__ dW_gu, float* __restrict__ dW_down, int E_l, int d, int F,
-    int accumulate, int rchunk = 0, int rows = 0) {
+    int rchunk = 0, int rows = 0) {
   constexpr int NW = 8, WGN = 4, WTM = 128, WTN = 64, TM = 4, TN = 2;
   constexpr int STAGE = 2 * BK * WG_ROWB;  // A + B tiles
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
@@ -807,40 +811,73 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
     const long long nk0 = (uniform64(s_it[a + 1]) - it0) / per_e;
     gt0 = (long long)a * per_e + (lo - it0 + nk0 - 1) / nk0;
   }
-  for (long long gt = gt0 + slot; gt < (long long)E_l * per_e; gt += nslots) {
+  // Tile gt of the expert-major order: its expert, operands, output and
+  // k-steps; valid = false once the group's range of work is done.
+  struct TileJob {
+    bool valid, gat;
+    int r0, r1, M, N, m0, n0, nk;
+    const uint16_t *Asrc, *Bsrc;
+    float* out;
+  };
+  auto job = [&](long long gt) {
+    TileJob j{};
+    j.valid = false;
+    if (gt >= (long long)E_l * per_e) return j;
     const int e = (int)(gt / per_e);
     int t = (int)(gt % per_e);
     {
       const long long it0 = uniform64(s_it[e]);
       const long long nk_e = (uniform64(s_it[e + 1]) - it0) / per_e;
-      if (it0 + t * nk_e >= hi) break;  // uniform
+      if (it0 + t * nk_e >= hi) return j;  // uniform
     }
-    const int r0 = off(e), r1 = off(e + 1);
-    const uint16_t *Asrc, *Bsrc;
-    int M, N, m0, n0;
-    float* out;
-    bool gat = false;  // block-uniform
+    j.valid = true;
+    j.r0 = off(e);
+    j.r1 = off(e + 1);
+    j.nk = (j.r1 - j.r0 + BK - 1) / BK;
+    j.gat = false;
     if (t < tdm * tdn) {
-      Asrc = dyp;
-      Bsrc = abuf;
-      M = d;
-      N = F;
-      m0 = (t / tdn) * 256;
-      n0 = (t % tdn) * 256;
-      out = dW_down + (size_t)e * d * F;
+      j.Asrc = dyp;
+      j.Bsrc = abuf;
+      j.M = d;
+      j.N = F;
+      j.m0 = (t / tdn) * 256;
+      j.n0 = (t % tdn) * 256;
+      j.out = dW_down + (size_t)e * d * F;
     } else {
       t -= tdm * tdn;
-      Asrc = dh;
-      Bsrc = xp;
-      gat = GATHER;
-      M = 2 * F;
-      N = d;
-      m0 = (t / tgn) * 256;
-      n0 = (t % tgn) * 256;
-      out = dW_gu + (size_t)e * 2 * F * d;
+      j.Asrc = dh;
+      j.Bsrc = xp;
+      j.gat = GATHER;
+      j.M = 2 * F;
+      j.N = d;
+      j.m0 = (t / tgn) * 256;
+      j.n0 = (t % tgn) * 256;
+      j.out = dW_gu + (size_t)e * 2 * F * d;
     }
-    const LoadKM<NW> la{Asrc, (long)M, M, m0, lane, wave};
-    const LoadKM<NW> lb{Bsrc, (long)N, N, n0, lane, wave};
+    return j;
+  };
+  // source token of dispatched row r of tile job c (-1 past the expert's end)
+  auto token = [&](const TileJob& c, int r) { return r < c.r1 ? xrows[r] / K : -1; };
+  // Stage 0 of a tile into LDS buffer 0.  A tile that does not gather has it
+  // issued early, right after the previous tile's main loop (the LDS is free
+  // then), so that its loads are in flight during that tile's epilogue.
+  auto issue_stage0 = [&](const TileJob& c) {
+    const LoadKM<NW> la{c.Asrc, (long)c.M, c.M, c.m0, lane, wave};
+    const LoadKM<NW> lb{c.Bsrc, (long)c.N, c.N, c.n0, lane, wave};
+    la.issue(smem, c.r0, c.r1);
+    if (GATHER && c.gat)
+      lb.template issue<true>(smem + BK * WG_ROWB, c.r0, c.r1, s_tok[0]);
+    else
+      lb.issue(smem + BK * WG_ROWB, c.r0, c.r1);
+  };
+  TileJob cur = job(gt0 + slot);
+  long long gt = gt0 + slot;
+  bool pre = cur.valid && cur.nk > 0 && !(GATHER && cur.gat);
+  if (pre) issue_stage0(cur);
+  while (cur.valid) {
+    const LoadKM<NW> la{cur.Asrc, (long)cur.M, cur.M, cur.m0, lane, wave};
+    const LoadKM<NW> lb{cur.Bsrc, (long)cur.N, cur.N, cur.n0, lane, wave};
+    const int r0 = cur.r0, r1 = cur.r1, nk = cur.nk;
     f32x16_t acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -848,48 +885,44 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    const int nk = (r1 - r0 + BK - 1) / BK;
-    // source token of dispatched row r (-1 past the expert's end)
-    auto token = [&](int r) { return r < r1 ? xrows[r] / K : -1; };
     if (nk > 0) {  // block-uniform
-      if constexpr (GATHER) {
-        if (gat) {
-          if (tid < BK) {
-            s_tok[0][tid] = token(r0 + tid);
-            s_tok[1][tid] = token(r0 + BK + tid);
+      if (!pre) {
+        if constexpr (GATHER) {
+          if (cur.gat) {
+            if (tid < BK) {
+              s_tok[0][tid] = token(cur, r0 + tid);
+              s_tok[1][tid] = token(cur, r0 + BK + tid);
+            }
+            __syncthreads();
           }
-          __syncthreads();
         }
+        issue_stage0(cur);
       }
-      la.issue(smem, r0, r1);
-      if (GATHER && gat)
-        lb.template issue<true>(smem + BK * WG_ROWB, r0, r1, s_tok[0]);
-      else
-        lb.issue(smem + BK * WG_ROWB, r0, r1);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       for (int kt = 0; kt < nk; ++kt) {
-        uint8_t* cur = smem + (kt & 1) * STAGE;
-        uint8_t* nxt = smem + ((kt + 1) & 1) * STAGE;
+        uint8_t* cur_s = smem + (kt & 1) * STAGE;
+        uint8_t* nxt_s = smem + ((kt + 1) & 1) * STAGE;
         if (kt + 1 < nk) {
-          la.issue(nxt, r0 + (kt + 1) * BK, r1);
-          if (GATHER && gat)
-            lb.template issue<true>(nxt + BK * WG_ROWB, 0, 0, s_tok[(kt + 1) & 1]);
+          la.issue(nxt_s, r0 + (kt + 1) * BK, r1);
+          if (GATHER && cur.gat)
+            lb.template issue<true>(nxt_s + BK * WG_ROWB, 0, 0, s_tok[(kt + 1) & 1]);
           else
-            lb.issue(nxt + BK * WG_ROWB, r0 + (kt + 1) * BK, r1);
+            lb.issue(nxt_s + BK * WG_ROWB, r0 + (kt + 1) * BK, r1);
         }
         // token rows of stage kt + 2, stored into the list stage kt used
         // (its last reader, the issue of stage kt, is behind the previous
         // barrier)
         int tk = -1;
-        if (GATHER && gat && tid < BK) tk = token(r0 + (kt + 2) * BK + tid);
+        if (GATHER && cur.gat && tid < BK) tk = token(cur, r0 + (kt + 2) * BK + tid);
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
           bf16x8_t a[TM], b[TN];
 #pragma unroll
-          for (int i = 0; i < TM; ++i) a[i] = frag_tr(cur, wm * WTM + i * 32, kk, lane);
+          for (int i = 0; i < TM; ++i) a[i] = frag_tr(cur_s, wm * WTM + i * 32, kk, lane);
 #pragma unroll
-          for (int j = 0; j < TN; ++j) b[j] = frag_tr(cur + BK * WG_ROWB, wn * WTN + j * 32, kk, lane);
+          for (int j = 0; j < TN; ++j)
+            b[j] = frag_tr(cur_s + BK * WG_ROWB, wn * WTN + j * 32, kk, lane);
 #pragma unroll
           for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -897,35 +930,81 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
               acc[i][j] = E::mfma(a[i], b[j], acc[i][j]);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        if (GATHER && gat && tid < BK) s_tok[kt & 1][tid] = tk;
+        if (GATHER && cur.gat && tid < BK) s_tok[kt & 1][tid] = tk;
         __syncthreads();
       }
     }
-    // With accumulate, the 16 previous values of a 32x32 piece are loaded
-    // together (clamped, always valid addresses) before the first store, so
-    // each piece waits for memory once.
+    // the next tile's stage 0 goes out before this tile's epilogue
+    gt += nslots;
+    const TileJob nxt = job(gt);
+    pre = nxt.valid && nxt.nk > 0 && !(GATHER && nxt.gat);
+    if (pre) issue_stage0(nxt);
+    // Epilogue.  The eight 32 x 32 pieces of the wave's tile are written in
+    // batches of PB; with ACC, the previous values of batch b + 1 are loaded
+    // before batch b is stored, so each batch's loads are in flight while the
+    // batch before it is added and stored (a load issued after the stores
+    // could not be waited for without waiting for them: the vector memory
+    // counter retires in order).  Accesses go through a buffer resource over
+    // the tile's rows [m0, min(m0 + 256, M)); the row part of an element's
+    // offset is the same for every lane, so it is a scalar offset and the
+    // accesses need no address registers.  No branch decides what is
+    // written: an access the tile does not own -- a 32-row piece past M
+    // (M - m0 is a multiple of 64, so a piece lies wholly inside or past it)
+    // or a lane whose column is past N -- has 2^31 added to its vector offset,
+    // beyond the resource's size, so the buffer range check drops it (a load
+    // returns 0); a piece past M also gets a zero scalar offset.
+    const int M = cur.M, N = cur.N, m0 = cur.m0, n0 = cur.n0;
+    const int rows_in = min(256, M - m0);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(cur.out + (size_t)m0 * N), (short)0, rows_in * N * 4, 0x00020000);
+    const int wrow = __builtin_amdgcn_readfirstlane(wm * WTM);
+    constexpr int PB = GATHER ? 1 : 2;  // pieces per batch (register budget)
+    constexpr int NBAT = TM * TN / PB;
+    // piece q = j * TM + i: column strip j, row block i.  in_rows(q) = 1 when
+    // the piece starts before row rows_in (wave-uniform), else 0.
+    auto in_rows = [&](int q) { return (int)((uint32_t)(wrow + (q % TM) * 32 - rows_in) >> 31); };
+    auto voff = [&](int q) {
+      const int col = n0 + wn * WTN + (q / TM) * 32 + (lane & 31);
+      const uint32_t out_col = (uint32_t)(N - 1 - col) >> 31;  // 1 when col >= N
+      const uint32_t drop = (out_col | (uint32_t)(1 - in_rows(q))) << 31;
+      return (int)(((uint32_t)(4 * (lane >> 5) * N + col) * 4u) | drop);
+    };
+    auto soff = [&](int q, int r) {
+      return in_rows(q) * ((wrow + (q % TM) * 32 + 8 * (r >> 2) + (r & 3)) * N * 4);
+    };
+    float prev[PB][16];
+    auto load_batch = [&](int b) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wn * WTN + j * 32 + (lane & 31);
-      const bool col_ok = col < N;
-      const int colc = col_ok ? col : N - 1;
+      for (int p = 0; p < PB; ++p)
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int rb = m0 + wm * WTM + i * 32;
-        float prev[16];
-        if (accumulate) {  // uniform
+        for (int r = 0; r < 16; ++r)
+          prev[p][r] = __uint_as_float(
+              __builtin_amdgcn_raw_buffer_load_b32(rs, voff(b * PB + p), soff(b * PB + p, r), 0));
+    };
+    if constexpr (ACC) load_batch(0);
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            prev[r] = out[(size_t)min(rb + out_row(lane, r), M - 1) * N + colc];
-        }
+    for (int b = 0; b < NBAT; ++b) {
+      float v[PB][16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rb + out_row(lane, r);
-          if (col_ok && row < M)
-            out[(size_t)row * N + col] = accumulate ? prev[r] + acc[i][j][r] : acc[i][j][r];
-        }
+      for (int p = 0; p < PB; ++p) {
+        const int q = b * PB + p;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          v[p][r] = ACC ? prev[p][r] + acc[q % TM][q / TM][r] : acc[q % TM][q / TM][r];
       }
+      if (ACC && b + 1 < NBAT) load_batch(b + 1);
+      // keep the next batch's loads ahead of this batch's stores (the
+      // scheduler would otherwise sink them below the stores)
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int p = 0; p < PB; ++p)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[p][r]), rs, voff(b * PB + p),
+                                                soff(b * PB + p, r), 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    cur = nxt;
   }
 }
 
@@ -1080,18 +1159,22 @@ void wgrad_t(const moe_shape* s, const void* xp, const int32_t* xrows, const voi
   const long per_e = (long)((d + 255) / 256) * ((F + 255) / 256) +
                      (long)((2 * F + 255) / 256) * ((d + 255) / 256);
   const int grid = persistent_grid(E_l * per_e);
-  if (xrows)
+  auto go = [&](auto gather, auto acc) {
     MOE_LAUNCH("wgrad", st,
-               wgrad_kernel<true, E><<<grid, 512, 0, st>>>(
-                   (const uint16_t*)xp, xrows, (int)s->K, (const uint16_t*)a,
-                   (const uint16_t*)dh, (const uint16_t*)dyp, offsets, dW_gu, dW_down, E_l, d, F,
-                   accumulate ? 1 : 0));
-  else
-    MOE_LAUNCH("wgrad", st,
-               wgrad_kernel<false, E><<<grid, 512, 0, st>>>(
-                   (const uint16_t*)xp, nullptr, (int)s->K, (const uint16_t*)a,
-                   (const uint16_t*)dh, (const uint16_t*)dyp, offsets, dW_gu, dW_down, E_l, d, F,
-                   accumulate ? 1 : 0));
+               (wgrad_kernel<decltype(gather)::value, E, false, decltype(acc)::value>
+                <<<grid, 512, 0, st>>>((const uint16_t*)xp, xrows, (int)s->K,
+                                       (const uint16_t*)a, (const uint16_t*)dh,
+                                       (const uint16_t*)dyp, offsets, dW_gu, dW_down, E_l, d, F)));
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  if (xrows) {
+    if (accumulate) go(T_{}, T_{});
+    else go(T_{}, F_{});
+  } else {
+    if (accumulate) go(F_{}, T_{});
+    else go(F_{}, F_{});
+  }
 }
 
 template <class E>
@@ -1166,9 +1249,9 @@ int launch_router_wgrad_mfma(const moe_shape* s, const void* x, const void* dl_s
   if (tiles == 0) return MOE_OK;
   const int grid = persistent_grid(tiles);
   MOE_LAUNCH("dwr_mfma", st,
-             (wgrad_kernel<false, BF16, true><<<grid, 512, 0, st>>>(
+             (wgrad_kernel<false, BF16, true, false><<<grid, 512, 0, st>>>(
                  nullptr, nullptr, 0, (const uint16_t*)dl_split, nullptr, (const uint16_t*)x,
-                 nullptr, nullptr, partial, nchunks, d, N, 0, chunk, T)));
+                 nullptr, nullptr, partial, nchunks, d, N, chunk, T)));
   return check_launch("router dW_r GEMM");
 }
 
