@@ -1001,8 +1001,9 @@ struct AccumOrder {
 // earlier accumulation into the same buffer in this call (on either stream),
 // and records its own, so the sums happen in step order.  Only events
 // recorded in this call are waited on.
+// skip: leave the weight gradients (routed and shared) to the caller.
 static int bwd_chain(const StepCtx& c, const moe_mb* B, hipStream_t q, bool mid, bool eager,
-                     AccumOrder& ord) {
+                     bool skip, AccumOrder& ord) {
   const bool shared = has_shared(c);
   const bool dwr = c.router && c.st->dW_r;
   const MultiEvents* ev = ord.ev;
@@ -1048,6 +1049,7 @@ static int bwd_chain(const StepCtx& c, const moe_mb* B, hipStream_t q, bool mid,
     return bwd_dispatch(c, B, q);
   }
   TRY(bwd_dispatch(c, B, q));
+  if (skip) return MOE_OK;
   TRY(routed_w());
   return shared_w();
 }
@@ -1060,10 +1062,6 @@ extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, h
   g_err[0] = 0;
   REQUIRE(steps);
   if (n < 1) return set_error(MOE_ERR_ARG, "moe_overlap_steps: n = %d, need at least 1", n);
-  if (flags & MOE_STEP_SKIP_WGRAD)
-    return set_error(MOE_ERR_ARG,
-                     "moe_overlap_steps: SKIP_WGRAD is not supported (the backward stream "
-                     "alternates between steps)");
   for (int j = 0; j < n; ++j) {
     const moe_step* st = &steps[j];
     if (int rc = check_step(st, flags, "moe_overlap_steps")) return rc;
@@ -1098,8 +1096,12 @@ extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, h
     TRY(launch_dgrad_weights(&steps[0].shape, steps[0].W_gu, steps[0].W_down, wsW, s0));
   }
   const bool serial = (flags & MOE_STEP_SERIALIZE) || s0 == s1;
+  // SKIP_WGRAD leaves the weight gradients of the last step's backward
+  // micro-batch to the caller; the earlier steps' run as usual
+  const bool skip_last = (flags & MOE_STEP_SKIP_WGRAD) != 0;
   if (serial) {
-    for (int j = 0; j < n; ++j) TRY(step_impl(&steps[j], s0, s0, flags, wsW));
+    for (int j = 0; j < n; ++j)
+      TRY(step_impl(&steps[j], s0, s0, j == n - 1 ? flags : flags & ~MOE_STEP_SKIP_WGRAD, wsW));
     return MOE_OK;
   }
   MultiEvents* ev = nullptr;
@@ -1142,7 +1144,7 @@ extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, h
       TRY(fwd_chain(c, st->fwd, P));
     }
     if (st->bwd) {
-      TRY(bwd_chain(c, st->bwd, Q, mid, eager, ord));
+      TRY(bwd_chain(c, st->bwd, Q, mid, eager, skip_last && j == n - 1, ord));
       HIPTRY(hipEventRecord(ev->bend[j & 1], Q));
       bend_rec[j & 1] = true;
     }

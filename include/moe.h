@@ -469,14 +469,20 @@ int moe_overlap_step(const moe_step* st, hipStream_t s_compute, hipStream_t s_co
  * sums (dW_r, dW_gu/dW_down, the shared expert's): each step's sum into a
  * buffer waits for the latest earlier sum into it in the same call, on either
  * stream, so every sum happens in step order.
- * Flags as moe_overlap_step, except MOE_STEP_SKIP_WGRAD (rejected: the wgrad's
- * stream alternates).  Results are bit-identical to n moe_overlap_step calls
- * with MOE_STEP_SERIALIZE.  s_copy forks from s_compute at the start and joins
+ * Flags as moe_overlap_step; MOE_STEP_SKIP_WGRAD leaves out the weight
+ * gradients (routed and shared) of the LAST step's backward micro-batch only:
+ * the caller issues moe_ffn_wgrad (and moe_shared_expert_wgrad) for it after
+ * the call -- on s_compute, or on another stream after an event recorded on
+ * s_compute, e.g. while the next layer's forward runs (page 1,
+ * delay_wgrad_compute) -- and its inputs (xp or x with pair_of_row, a, dh, dyp,
+ * offsets) must stay intact until then; the earlier steps' weight gradients
+ * run as usual.  Results are bit-identical to n moe_overlap_step calls
+ * with MOE_STEP_SERIALIZE (with SKIP_WGRAD on the last).  s_copy forks from s_compute at the start and joins
  * it at the end, so on return work on s_compute depends on everything the call
  * issued; the call may be captured into a HIP graph on s_compute.  Errors: as
  * moe_overlap_step (checked for every step before anything is launched), and
- * MOE_ERR_ARG for n < 1, a step whose bwd is not the previous step's fwd, steps
- * with different shapes, workspaces, F_s or expert weights, or SKIP_WGRAD.
+ * MOE_ERR_ARG for n < 1, a step whose bwd is not the previous step's fwd, or
+ * steps with different shapes, workspaces, F_s or expert weights.
  */
 int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s_compute, hipStream_t s_copy,
                       int flags);

@@ -249,10 +249,14 @@ def test_multi_step_rejects_bad_chains():
     # forward and backward of one step on the same buffers (distinct structs)
     assert run([step(m2, None), step(m2_copy, m2)]) == M.MOE_ERR_ARG
     assert b"same" in L.moe_last_error()
-    # the caller-deferred wgrad has no fixed stream to follow here
-    assert run([step(m1, m2)], M.MOE_STEP_SKIP_WGRAD) == M.MOE_ERR_ARG
-    assert b"SKIP_WGRAD" in L.moe_last_error()
+    # the caller-deferred wgrad excludes the other wgrad placements
+    assert run([step(m1, m2)], M.MOE_STEP_SKIP_WGRAD | M.MOE_STEP_MID_WGRAD) == M.MOE_ERR_ARG
     assert run([step(m1, m2)], M.MOE_STEP_MID_WGRAD | M.MOE_STEP_EAGER_WGRAD) == M.MOE_ERR_ARG
+    # every step must use the same expert weights (their dgrad copies are made once)
+    w2 = step(m2, m1)
+    w2.W_gu = 0x5000
+    assert run([step(m1, m2), w2]) == M.MOE_ERR_ARG
+    assert b"expert weights" in L.moe_last_error()
     # a later step's small workspace is found before anything runs
     assert run([step(m1, m2), step(m2, m1, ws_bytes=8)]) == M.MOE_ERR_WORKSPACE
     # the streams' workspace halves are laid out once: every step shares the shape

@@ -863,3 +863,144 @@ def test_multi_step_three_buffer_sets():
     for k in range(3):
         assert torch.equal(ga[k], gb[k]), ("dW", k)
     log("[multi-step 3 sets] bit-identical")
+
+
+def test_cross_layer_delayed_wgrad():
+    """Delayed wgrad across layers on the product path: moe_overlap_steps with
+    MOE_STEP_SKIP_WGRAD leaves the last step's routed weight gradient to the
+    caller, who issues it on a third stream while the next layer's forward
+    runs on the step streams (the pages' delay_wgrad_compute).  Every output of
+    both layers and both layers' weight gradients are bit-identical to the
+    serial order (the wgrad inside the call, then the next layer)."""
+    w = SMALL["zipf_window_bf16"]
+    log("[cross-layer wgrad] two layers, delayed wgrad beside the next layer's forward")
+    s = M.shape_of(w)
+    inpL = make_inputs(w, seed=0, microbatches=2)
+    inpM = make_inputs(w, seed=1)
+    D = lambda a: dev(a, w.dtype)
+    mode = M.MOE_ROUTE_TOPK
+    layers = []
+    for inp in (inpL, inpM):
+        layers.append(dict(W_gu=D(inp["W_gu"]), W_down=D(inp["W_down"]), W_r=D(inp["W_r"]),
+                           bias=dev(inp["bias"], "f32x")))
+
+    def run(delayed):
+        torch.manual_seed(0)
+        s0 = torch.cuda.current_stream()
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        g = [dict(dW_gu=torch.zeros(w.E_l, 2 * w.F, w.d, device="cuda"),
+                  dW_down=torch.zeros(w.E_l, w.d, w.F, device="cuda"),
+                  dW_r=torch.zeros(w.d, w.E, device="cuda"),
+                  ws=torch.empty(M.moe_step_workspace_bytes(s), dtype=torch.uint8,
+                                 device="cuda")) for _ in range(2)]
+        A = M.MicroBatch(s, x=D(inpL["x"]), dout=D(inpL["dout"]))
+        B = M.MicroBatch(s, x=D(inpL["x_b"]), dout=D(inpL["dout_b"]))
+        C = M.MicroBatch(s)
+
+        def mk(li, fwd, bwd, acc):
+            L_, G = layers[li], g[li]
+            return M.make_step(s, mode, L_["W_gu"], L_["W_down"], G["dW_gu"], G["dW_down"],
+                               G["ws"], fwd=fwd, bwd=bwd, W_r=L_["W_r"], bias=L_["bias"],
+                               dW_r=G["dW_r"], accumulate=acc)
+
+        # layer L: A forwarded, then (B forward, A backward), then B backward
+        M.moe_overlap_step(mk(0, A, None, 0), s0, s1, 0)
+        steps = [mk(0, B, A, 0), mk(0, None, B, M.MOE_ACCUM_DW)]
+        if delayed:
+            M.moe_overlap_steps(steps, s0, s1, M.MOE_STEP_SKIP_WGRAD)
+            done = torch.cuda.Event()
+            done.record(s0)
+            s2.wait_event(done)
+            M.moe_ffn_wgrad(s, B.xp, B.a, B.dh, B.dyp, B.offsets, g[0]["dW_gu"],
+                            g[0]["dW_down"], M.MOE_ACCUM_DW, s2)
+        else:
+            M.moe_overlap_steps(steps, s0, s1, M.MOE_STEP_SERIALIZE)
+        # the next layer's forward, on the step streams, takes A's output
+        C.x.copy_(A.out)
+        M.moe_overlap_step(mk(1, C, None, 0), s0, s1, 0 if delayed else M.MOE_STEP_SERIALIZE)
+        s0.wait_stream(s2)
+        torch.cuda.synchronize()
+        return A, B, C, g
+
+    ref = run(False)
+    got = run(True)
+    # row buffers are compared on their rows [0, N) (rows past N are never written)
+    for mb_r, mb_g, name in zip(ref[:3], got[:3], "ABC"):
+        N = int(mb_r.offsets[-1].item())
+        for k in ("out", "idx", "gates", "row_of_pair"):
+            assert torch.equal(getattr(mb_g, k), getattr(mb_r, k)), (name, k)
+        for k in ("h", "a", "yp"):
+            assert torch.equal(getattr(mb_g, k)[:N], getattr(mb_r, k)[:N]), (name, k)
+    for mb_r, mb_g, name in zip(ref[:2], got[:2], "AB"):
+        N = int(mb_r.offsets[-1].item())
+        for k in ("dx", "dgates", "dlogits"):
+            assert torch.equal(getattr(mb_g, k), getattr(mb_r, k)), (name, k)
+        for k in ("dh", "dyp"):
+            assert torch.equal(getattr(mb_g, k)[:N], getattr(mb_r, k)[:N]), (name, k)
+    for li in range(2):
+        for k in ("dW_gu", "dW_down", "dW_r"):
+            assert torch.equal(got[3][li][k], ref[3][li][k]), (li, k)
+    # and the weight gradient of layer L holds both micro-batches (oracle, sampled rows)
+    prec, tau = w.dtype, TAU[w.dtype]
+    A, B = got[0], got[1]
+    prev = None
+    for mb in (A, B):
+        off = host(mb.offsets)
+        N = int(off[-1])
+        gu, dn = O.ffn_wgrad(host(mb.xp, N), host(mb.a, N), host(mb.dh, N), host(mb.dyp, N),
+                             off, dW_gu_prev=None if prev is None else prev[0],
+                             dW_down_prev=None if prev is None else prev[1], prec=prec)
+        prev = (gu, dn)
+    close("dW_gu (A + B)", host(got[3][0]["dW_gu"]), prev[0], tau)
+    close("dW_down (A + B)", host(got[3][0]["dW_down"]), prev[1], tau)
+    log("[cross-layer wgrad] bit-identical to the serial order; dW against the oracle")
+
+
+def test_token_chunks_equal_whole_microbatch():
+    """A micro-batch split into token chunks that run as consecutive pipelined
+    1F1B steps (how a chunked step head is expressed here: each chunk's route,
+    plan and permute overlap the previous chunk's GEMMs on the other stream)
+    gives the same per-token results, bit for bit, as the whole micro-batch;
+    the weight gradients differ only in how the float32 sums are grouped."""
+    w = SMALL["zipf_window_bf16"]
+    log("[chunks] one micro-batch against the same tokens in two chunks")
+    T2 = w.T // 2
+    inp = make_inputs(w, seed=0)
+    D = lambda a: dev(a, w.dtype)
+    mode = M.MOE_ROUTE_TOPK
+    W_gu, W_down, W_r = D(inp["W_gu"]), D(inp["W_down"]), D(inp["W_r"])
+    bias = dev(inp["bias"], "f32x")
+    s0 = torch.cuda.current_stream()
+    s1 = torch.cuda.Stream()
+
+    def grads():
+        return (torch.zeros(w.E_l, 2 * w.F, w.d, device="cuda"),
+                torch.zeros(w.E_l, w.d, w.F, device="cuda"), torch.zeros(w.d, w.E, device="cuda"))
+
+    # whole micro-batch: forward, then backward
+    s = M.shape_of(w)
+    gw = grads()
+    ws = torch.empty(M.moe_step_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    X = M.MicroBatch(s, x=D(inp["x"]), dout=D(inp["dout"]))
+    mk = lambda sh, g, ws_, f, b, acc: M.make_step(sh, mode, W_gu, W_down, g[0], g[1], ws_, fwd=f,
+                                                   bwd=b, W_r=W_r, bias=bias, dW_r=g[2],
+                                                   accumulate=acc)
+    M.moe_overlap_steps([mk(s, gw, ws, X, None, 0), mk(s, gw, ws, None, X, 0)], s0, s1, 0)
+    # two chunks of T/2 tokens as consecutive micro-batches
+    sc = M.shape_of(w, T=T2)
+    gc = grads()
+    wsc = torch.empty(M.moe_step_workspace_bytes(sc), dtype=torch.uint8, device="cuda")
+    C0 = M.MicroBatch(sc, x=D(inp["x"][:T2]), dout=D(inp["dout"][:T2]))
+    C1 = M.MicroBatch(sc, x=D(inp["x"][T2:]), dout=D(inp["dout"][T2:]))
+    M.moe_overlap_steps([mk(sc, gc, wsc, C0, None, 0), mk(sc, gc, wsc, C1, C0, 0),
+                         mk(sc, gc, wsc, None, C1, M.MOE_ACCUM_DW)], s0, s1,
+                        M.MOE_STEP_MID_WGRAD)
+    torch.cuda.synchronize()
+    for k in ("out", "dx", "idx", "gates", "dgates", "dlogits", "logits"):
+        whole = getattr(X, k)
+        both = torch.cat([getattr(C0, k), getattr(C1, k)])
+        assert torch.equal(whole, both), k
+    tau = TAU[w.dtype]
+    for a_, b_, k in zip(gw, gc, ("dW_gu", "dW_down", "dW_r")):
+        close(f"{k} (chunks vs whole)", host(b_), host(a_), tau)
+    log("[chunks] per-token results bit-identical; weight gradients within tolerance")
