@@ -44,13 +44,15 @@ def err(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic(w, N, T_loc, accumulate=True, fused=False):
+def algorithmic(w, N, T_loc, accumulate=True, fused=False, fcb=False):
     """Algorithmic work per step of each kernel (one launch of each, plus the
     shared expert's launches of the same GEMMs over all T tokens when the
     workload has one): {name: {"flop": F, "byte": B}}.  Bytes count one pass
     over every operand and result (no re-reads); the GEMMs' bytes include the
     expert weights, and wgrad's the float32 weight gradients (read and written
-    with accumulate, written without)."""
+    with accumulate, written without).  fused: the permute fused into GEMM1
+    and wgrad (x rows instead of xp); fcb: the fused combine backward (dout
+    rows instead of dy_p, ag written by dgrad_act)."""
     d, F, T, K, E, E_l = w.d, w.F, w.T, w.K, w.E, w.E_l
     b = 4 if w.dtype == "f32" else 2
     Fs = w.F_s
@@ -58,6 +60,8 @@ def algorithmic(w, N, T_loc, accumulate=True, fused=False):
     sgu, sdn = 2 * Fs * d * b, d * Fs * b                    # shared expert weights
     dW = 4.0 * (E_l * 3 * F * d + 3 * Fs * d)                # float32 dW_gu + dW_down
     xin = (T_loc if fused else N) * d * b                    # GEMM1 A operand rows
+    dyin = (T_loc if fcb else N) * d * b                     # dgrad / wgrad dy operand rows
+    agout = N * F * b if fcb else 0                          # ag written by dgrad_act
     out = {
         "ffn_gate_up": {"flop": 2.0 * N * d * 2 * F + 2.0 * T * d * 2 * Fs,
                         "byte": xin + wgu + N * 3 * F * b + T * d * b * (Fs > 0) + sgu
@@ -65,13 +69,13 @@ def algorithmic(w, N, T_loc, accumulate=True, fused=False):
         "ffn_down": {"flop": 2.0 * N * F * d + 2.0 * T * Fs * d,
                      "byte": N * F * b + wdn + N * d * b + T * Fs * b + sdn + T * d * b * (Fs > 0)},
         "dgrad_act": {"flop": 2.0 * N * d * F + 2.0 * T * d * Fs,
-                      "byte": N * d * b + wdn + N * 2 * F * b * 2
+                      "byte": dyin + wdn + N * 2 * F * b * 2 + agout
                       + (T * d * b + sdn + T * 2 * Fs * b * 2) * (Fs > 0)},
         "dgrad_in": {"flop": 2.0 * N * 2 * F * d + 2.0 * T * 2 * Fs * d,
                      "byte": N * 2 * F * b + wgu + N * d * b
                      + (T * 2 * Fs * b + sgu + T * d * b) * (Fs > 0)},
         "wgrad": {"flop": 6.0 * N * d * F + 6.0 * T * d * Fs,
-                  "byte": N * (d + F + 2 * F) * b + xin + T * (2 * d + 3 * Fs) * b * (Fs > 0)
+                  "byte": dyin + N * (F + 2 * F) * b + xin + T * (2 * d + 3 * Fs) * b * (Fs > 0)
                   + dW * (2 if accumulate else 1)},
         "router": {"flop": 2.0 * T * d * E, "byte": T * d * b + d * E * b + 4.0 * T * E},
         # router weight gradient x^T dlogits on the matrix cores (bf16 data);
@@ -81,8 +85,8 @@ def algorithmic(w, N, T_loc, accumulate=True, fused=False):
         "permute": {"byte": T_loc * d * b + 4.0 * T * K + N * d * b},
         # y_p rows + gates + row map -> out
         "combine": {"byte": N * d * b + 8.0 * T * K + T * d * b},
-        # dout + y_p rows + gates + map -> dy_p rows + dgates
-        "combine_bwd": {"byte": T * d * b + 2.0 * N * d * b + 12.0 * T * K},
+        # dout + y_p rows + gates + map -> dy_p rows (not with fcb) + dgates
+        "combine_bwd": {"byte": T * d * b + (1 if fcb else 2) * N * d * b + 12.0 * T * K},
         # dx_p rows + map -> dx
         "dispatch_bwd": {"byte": N * d * b + 4.0 * T * K + T * d * b},
     }
@@ -235,11 +239,13 @@ class Layer:
         self.ws = torch.empty(M.moe_step_workspace_bytes_shared(s, w.F_s), dtype=torch.uint8,
                               device="cuda")
         self.fused = args.fused_permute == "on"
+        self.fcb = args.fused_combine_bwd == "on"
         self.pipelined = args.pipeline == "on"
         self.G = args.group
         # flags of every step: the fused permute and the wgrad's place in the
         # backward stream's order (both leave the results unchanged)
         self.FLAGS = ((M.MOE_STEP_FUSED_PERMUTE if self.fused else 0) |
+                      (M.MOE_STEP_FUSED_COMBINE_BWD if self.fcb else 0) |
                       (M.MOE_STEP_MID_WGRAD if args.wgrad_order == "mid" else 0))
         self.shared = None
         if w.F_s:  # a shared expert beside the routed ones
@@ -247,7 +253,7 @@ class Layer:
                            z(w.d, w.F_s))
         mk = lambda x, dout, g: M.MicroBatch(s, x=D(x), dout=D(dout),
                                              gates=None if topk else F32(g), fused=self.fused,
-                                             F_s=w.F_s)
+                                             F_s=w.F_s, fused_bwd=self.fcb)
         self.mbs = [mk(inp["x"], inp["dout"], inp["gates"]),
                     mk(inp["x_b"], inp["dout_b"], inp.get("gates_b"))]
         self.i = 0  # steps issued so far (after the priming forward)
@@ -345,6 +351,10 @@ def main():
     ap.add_argument("--fused-permute", choices=("on", "off"), default="off",
                     help="fuse the permute into the expert GEMMs (MOE_STEP_FUSED_PERMUTE): GEMM1 "
                          "and wgrad read the token rows of x through the dispatch plan, no xp")
+    ap.add_argument("--fused-combine-bwd", choices=("on", "off"), default="off",
+                    help="fuse the combine backward into the expert GEMMs "
+                         "(MOE_STEP_FUSED_COMBINE_BWD): no dy_p; dgrad and wgrad read the dout "
+                         "rows through the dispatch plan and apply the gates")
     ap.add_argument("--wgrad-order", choices=("mid", "last"), default="mid",
                     help="where the backward micro-batch's wgrad runs on its stream: between the "
                          "two dgrad GEMMs (mid, MOE_STEP_MID_WGRAD) or after the dispatch "
@@ -527,7 +537,7 @@ def main():
         torch.cuda.synchronize()
 
     # ---- per-kernel achieved rates from the live kernel events
-    work = algorithmic(w, N, T_loc, accumulate=True, fused=L.fused)
+    work = algorithmic(w, N, T_loc, accumulate=True, fused=L.fused, fcb=L.fcb)
     traffic = stored_traffic(w.name) if args.tokens is None else {}
     kernels = {}
     for name, (tot_ms, n) in sorted(kern.items(), key=lambda kv: -kv[1][0]):
@@ -596,6 +606,8 @@ def main():
                                 "alternating" if L.pipelined else
                                 "one moe_overlap_step per step, joined at each boundary"),
                    "permute": "fused into GEMM1 and wgrad" if L.fused else "separate kernel",
+                   "combine_backward": ("fused into dgrad and wgrad (no dy_p)" if L.fcb
+                                        else "separate kernel writing dy_p"),
                    "shared_expert_F": w.F_s},
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -727,7 +739,8 @@ def _sum_kernels(args, w, N, T_loc, desc):
         if name:
             by.setdefault(name, []).append((b - a) / 1e3)
     total = sum(sum(v) for v in by.values())
-    work = algorithmic(w, N, T_loc) if N is not None else {}
+    work = (algorithmic(w, N, T_loc, fused=args.fused_permute == "on",
+                        fcb=args.fused_combine_bwd == "on") if N is not None else {})
     lines = []
     for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
         h = v[len(v) // 2:]
@@ -782,7 +795,8 @@ def _sum_traffic(args, w, N, T_loc, desc):
         return agg
 
     aF, aW = per_kernel(F, "FETCH_SIZE"), per_kernel(W, "WRITE_SIZE")
-    work = algorithmic(w, N, T_loc) if N is not None else {}
+    work = (algorithmic(w, N, T_loc, fused=args.fused_permute == "on",
+                        fcb=args.fused_combine_bwd == "on") if N is not None else {})
     rec = {"workload": w.name, "copy_probe_bytes": COPY_PROBE_BYTES,
            "fetch_factor": round(ff, 4), "write_factor": round(fw, 4), "kernels": {}}
     lines = []
@@ -833,7 +847,8 @@ Machine-readable record (bench.py reads `hbm_bytes_per_launch` while the kernel'
 
 def _sum_mfma(args, w, N, T_loc, desc):
     rec = read_counters(args.inputs[0])
-    work = algorithmic(w, N, T_loc) if N is not None else {}
+    work = (algorithmic(w, N, T_loc, fused=args.fused_permute == "on",
+                        fcb=args.fused_combine_bwd == "on") if N is not None else {})
     SIMDS, XCDS = 1024, 8
     peak_per_clk = PEAK_BF16_TFLOPS * 1e12 / 2.4e9
     agg = collections.defaultdict(list)

@@ -17,7 +17,7 @@ from ._lib import (  # noqa: F401
     MOE_ERR_UNSUPPORTED, MOE_ERR_ARG, MOE_F32, MOE_BF16, MOE_F16, MOE_ROUTE_TOPK,
     MOE_ROUTE_TOPK_FROM_LOGITS, MOE_ROUTE_FORCE_BALANCE, MOE_ACCUM_DX, MOE_ACCUM_DW,
     MOE_STEP_SERIALIZE, MOE_STEP_EAGER_WGRAD, MOE_STEP_SKIP_WGRAD, MOE_STEP_FUSED_PERMUTE,
-    MOE_STEP_MID_WGRAD,
+    MOE_STEP_MID_WGRAD, MOE_STEP_FUSED_COMBINE_BWD,
 )
 
 
@@ -259,12 +259,13 @@ def moe_combine(s, yp, gates, row_of_pair, out, stream=None):
 
 
 def moe_combine_bwd(s, dout, yp, gates, row_of_pair, dyp, dgates, stream=None):
+    """dyp None: dgates only (the fused combine backward)."""
     fn, T, d, K = "moe_combine_bwd", s.T, s.d, s.K
     _chk(s, fn, "dout", dout, _DATA, T * d)
     _chk(s, fn, "yp", yp, _DATA, T * K * d)
     _chk(s, fn, "gates", gates, _F32, T * K)
     _chk(s, fn, "row_of_pair", row_of_pair, _I32, T * K)
-    _chk(s, fn, "dyp", dyp, _DATA, T * K * d)
+    _chk(s, fn, "dyp", dyp, _DATA, T * K * d, optional=True)
     _chk(s, fn, "dgates", dgates, _F32, T * K)
     check(lib().moe_combine_bwd(C.byref(s), _p(dout), _p(yp), _p(gates), _p(row_of_pair),
                                 _p(dyp), _p(dgates), _stream(stream)))
@@ -301,6 +302,35 @@ def moe_ffn_wgrad_gather(s, x, pair_of_row, a, dh, dyp, offsets, dW_gu, dW_down,
     check(lib().moe_ffn_wgrad_gather(C.byref(s), _p(x), _p(pair_of_row), _p(a), _p(dh), _p(dyp),
                                      _p(offsets), _p(dW_gu), _p(dW_down), int(accumulate),
                                      _stream(stream)))
+
+
+def moe_ffn_dgrad_gather(s, dout, pair_of_row, gates, h, offsets, tile_offsets, W_gu, W_down, dh,
+                         dxp, ag, ws, stream=None):
+    cap, d, F = s.T * s.K, s.d, s.F
+    _chk_ffn(s, "moe_ffn_dgrad_gather", offsets, tile_offsets, W_gu, W_down,
+             dout=(dout, s.T * d, _DATA), pair_of_row=(pair_of_row, cap, _I32),
+             gates=(gates, cap, _F32), h=(h, cap * 2 * F, _DATA), dh=(dh, cap * 2 * F, _DATA),
+             dxp=(dxp, cap * d, _DATA), ag=(ag, cap * F, _DATA))
+    _chk_ws("moe_ffn_dgrad_gather", ws)
+    wp, wb = _ws(ws)
+    check(lib().moe_ffn_dgrad_gather(C.byref(s), _p(dout), _p(pair_of_row), _p(gates), _p(h),
+                                     _p(offsets), _p(tile_offsets), _p(W_gu), _p(W_down), _p(dh),
+                                     _p(dxp), _p(ag), wp, wb, _stream(stream)))
+
+
+def moe_ffn_wgrad_fused(s, xp, x, pair_of_row, ag, dh, dout, offsets, dW_gu, dW_down,
+                        accumulate=0, stream=None):
+    """xp None: the dW_gu operand is gathered from x through pair_of_row too."""
+    cap, d, F, E_l = s.T * s.K, s.d, s.F, s.E_l
+    fn = "moe_ffn_wgrad_fused"
+    _chk(s, fn, "xp", xp, _DATA, cap * d, optional=True)
+    _chk(s, fn, "x", x, _DATA, s.T * d, optional=xp is not None)
+    _chk_ffn(s, fn, offsets, False, False, False, pair_of_row=(pair_of_row, cap, _I32),
+             ag=(ag, cap * F, _DATA), dh=(dh, cap * 2 * F, _DATA), dout=(dout, s.T * d, _DATA),
+             dW_gu=(dW_gu, E_l * 2 * F * d, _F32), dW_down=(dW_down, E_l * d * F, _F32))
+    check(lib().moe_ffn_wgrad_fused(C.byref(s), _p(xp), _p(x), _p(pair_of_row), _p(ag), _p(dh),
+                                    _p(dout), _p(offsets), _p(dW_gu), _p(dW_down),
+                                    int(accumulate), _stream(stream)))
 
 
 def moe_route_bwd(s, mode, dgates, gates, idx, x, dlogits, dW_r, accumulate, ws, stream=None):
@@ -378,10 +408,11 @@ def moe_timing_report() -> dict:
 class MicroBatch:
     """Device buffers of one micro-batch for shape ``s`` (sizes per include/moe.h).
     With ``fused=True`` (steps run with MOE_STEP_FUSED_PERMUTE) no xp is allocated;
-    with ``F_s > 0`` the shared expert's buffers are allocated too."""
+    with ``fused_bwd=True`` (MOE_STEP_FUSED_COMBINE_BWD) ag is allocated and dyp
+    is not; with ``F_s > 0`` the shared expert's buffers are allocated too."""
 
     def __init__(self, s: MoeShape, device="cuda", x=None, dout=None, gates=None, logits=None,
-                 fused=False, F_s=0):
+                 fused=False, F_s=0, fused_bwd=False):
         import numpy as np
         import torch
 
@@ -410,7 +441,7 @@ class MicroBatch:
         self.yp = e(cap, d)
         self.out = e(T, d)
         self.dout = dout if dout is not None else e(T, d)
-        self.dyp = e(cap, d)
+        self.dyp = None if fused_bwd else e(cap, d)
         self.dgates = e(T, K, dtype=f32)
         self.dlogits = e(T, E, dtype=f32)
         self.dh = e(cap, 2 * F)
@@ -422,6 +453,7 @@ class MicroBatch:
         self.y_s = e(T, d) if Fs else None
         self.dh_s = e(T, 2 * Fs) if Fs else None
         self.dx_s = e(T, d) if Fs else None
+        self.ag = e(cap, F) if fused_bwd else None
 
     def struct(self) -> MoeMB:
         return MoeMB(*[_p(getattr(self, n)) for n in MB_FIELDS])

@@ -35,6 +35,7 @@ MOE_STEP_EAGER_WGRAD = 2
 MOE_STEP_SKIP_WGRAD = 4
 MOE_STEP_FUSED_PERMUTE = 8
 MOE_STEP_MID_WGRAD = 16
+MOE_STEP_FUSED_COMBINE_BWD = 32
 
 
 class MoeShape(C.Structure):
@@ -46,7 +47,7 @@ class MoeShape(C.Structure):
 MB_FIELDS = ["x", "logits", "idx", "gates", "counts", "offsets", "row_of_pair",
              "pair_of_row", "tile_offsets", "xp", "h", "a", "yp", "out",
              "dout", "dyp", "dgates", "dlogits", "dh", "dxp", "dx",
-             "h_s", "a_s", "y_s", "dh_s", "dx_s"]
+             "h_s", "a_s", "y_s", "dh_s", "dx_s", "ag"]
 
 
 class MoeMB(C.Structure):
@@ -90,6 +91,9 @@ SIGNATURES = {
     "moe_ffn_dgrad": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "moe_ffn_wgrad": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, C.c_int, _P]),
     "moe_ffn_wgrad_gather": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, C.c_int, _P]),
+    "moe_ffn_dgrad_gather": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                       C.c_size_t, _P]),
+    "moe_ffn_wgrad_fused": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, C.c_int, _P]),
     "moe_route_bwd": (C.c_int, [_SP, C.c_int, _P, _P, _P, _P, _P, _P, C.c_int, _P, C.c_size_t,
                                 _P]),
     "moe_dispatch_bwd": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, C.c_int, _P, C.c_size_t, _P]),

@@ -178,12 +178,14 @@ static int do_shared_wgrad(const moe_shape* s, int64_t F_s, const void* x, const
                           st);
 }
 
-// The fused permute addresses x with 32-bit byte offsets.
+// The gathering GEMMs (fused permute, fused combine backward) address the
+// token matrices x and dout [T][d] with 32-bit byte offsets.
 static int check_gather_x(const moe_shape* s, const char* fn) {
   const int64_t es = (int64_t)elt_bytes(s);
   if (s->T * s->d * es >= (1LL << 31))
-    return set_error(MOE_ERR_SHAPE, "%s: x is %lld bytes, the fused permute needs < 2^31", fn,
-                     (long long)(s->T * s->d * es));
+    return set_error(MOE_ERR_SHAPE,
+                     "%s: a [T,d] token matrix is %lld bytes, the gathering GEMMs need < 2^31",
+                     fn, (long long)(s->T * s->d * es));
   return MOE_OK;
 }
 
@@ -389,7 +391,6 @@ int moe_combine_bwd(const moe_shape* s, const void* dout, const void* yp, const 
   REQUIRE(yp);
   REQUIRE(gates);
   REQUIRE(row_of_pair);
-  REQUIRE(dyp);
   REQUIRE(dgates);
   return launch_combine_bwd(s, dout, yp, gates, row_of_pair, dyp, dgates, stream);
 }
@@ -452,6 +453,56 @@ int moe_ffn_wgrad_gather(const moe_shape* s, const void* x, const int32_t* pair_
   if (int rc = check_gather_x(s, __func__)) return rc;
   return launch_ffn_wgrad(s, x, pair_of_row, a, dh, dyp, offsets, dW_gu, dW_down,
                           (accumulate & MOE_ACCUM_DW) != 0, stream);
+}
+
+int moe_ffn_dgrad_gather(const moe_shape* s, const void* dout, const int32_t* pair_of_row,
+                         const float* gates, const void* h, const int32_t* offsets,
+                         const int32_t* tile_offsets, const void* W_gu, const void* W_down,
+                         void* dh, void* dxp, void* ag, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  g_err[0] = 0;
+  if (int rc = validate_shape(s)) return rc;
+  REQUIRE(dout);
+  REQUIRE(pair_of_row);
+  REQUIRE(gates);
+  REQUIRE(h);
+  REQUIRE(offsets);
+  REQUIRE(tile_offsets);
+  REQUIRE(W_gu);
+  REQUIRE(W_down);
+  REQUIRE(dh);
+  REQUIRE(dxp);
+  REQUIRE(ag);
+  if (int rc = check_gather_x(s, __func__)) return rc;
+  if (is16(s)) {
+    REQUIRE(ws);
+    if (int rc = need_ws(__func__, ws_bytes, ws_wT_offset(s) + ws_wT_bytes(s))) return rc;
+  }
+  const FusedCombineBwd fc{pair_of_row, gates, ag};
+  return launch_ffn_dgrad(s, dout, h, offsets, tile_offsets, W_gu, W_down, dh, dxp, ws, false,
+                          stream, kDgradBoth, &fc);
+}
+
+int moe_ffn_wgrad_fused(const moe_shape* s, const void* xp, const void* x,
+                        const int32_t* pair_of_row, const void* ag, const void* dh,
+                        const void* dout, const int32_t* offsets, float* dW_gu, float* dW_down,
+                        int accumulate, hipStream_t stream) {
+  g_err[0] = 0;
+  if (int rc = validate_shape(s)) return rc;
+  if (!xp) REQUIRE(x);
+  REQUIRE(pair_of_row);
+  REQUIRE(ag);
+  REQUIRE(dh);
+  REQUIRE(dout);
+  REQUIRE(offsets);
+  REQUIRE(dW_gu);
+  REQUIRE(dW_down);
+  if (accumulate & ~(MOE_ACCUM_DX | MOE_ACCUM_DW))
+    return set_error(MOE_ERR_ARG, "moe_ffn_wgrad_fused: unknown accumulate bits 0x%x",
+                     accumulate);
+  if (int rc = check_gather_x(s, __func__)) return rc;
+  return launch_ffn_wgrad(s, xp ? xp : x, xp ? nullptr : pair_of_row, ag, dh, dout, offsets,
+                          dW_gu, dW_down, (accumulate & MOE_ACCUM_DW) != 0, stream, pair_of_row);
 }
 
 int moe_shared_expert_fwd(const moe_shape* s, int64_t F_s, const void* x, const void* W_gu_s,
@@ -666,7 +717,7 @@ static int validate_mb_fwd(const moe_mb* m, int mode, bool fused) {
   return MOE_OK;
 }
 
-static int validate_mb_bwd(const moe_mb* m, int mode, bool fused) {
+static int validate_mb_bwd(const moe_mb* m, int mode, bool fused, bool fcb) {
   REQUIRE(m->idx);
   REQUIRE(m->gates);
   REQUIRE(m->offsets);
@@ -682,7 +733,12 @@ static int validate_mb_bwd(const moe_mb* m, int mode, bool fused) {
   REQUIRE(m->a);
   REQUIRE(m->yp);
   REQUIRE(m->dout);
-  REQUIRE(m->dyp);
+  if (fcb) {
+    REQUIRE(m->ag);
+    REQUIRE(m->pair_of_row);
+  } else {
+    REQUIRE(m->dyp);
+  }
   REQUIRE(m->dgates);
   REQUIRE(m->dh);
   REQUIRE(m->dxp);
@@ -707,6 +763,7 @@ struct StepCtx {
   void* wsB;
   bool router;  // TOPK mode: router weights are differentiated
   bool fused;   // fused permute: no xp, GEMM1 / wgrad gather from x
+  bool fcb;     // fused combine backward: no dy_p, dgrad / wgrad gather from dout
   void* wsSA;   // shared-expert workspace of the forward micro-batch
   void* wsSB;   // and of the backward one
   void* wsW;    // non-null: a workspace whose dgrad weight copies are already
@@ -745,7 +802,8 @@ static int bwd_shared_wgrad(const StepCtx& c, const moe_mb* B, hipStream_t q) {
                          c.st->dW_down_s, (c.st->accumulate & MOE_ACCUM_DW) != 0, c.wsSB, q);
 }
 static int bwd_combine(const StepCtx& c, const moe_mb* B, hipStream_t q) {
-  return launch_combine_bwd(c.s, B->dout, B->yp, B->gates, B->row_of_pair, B->dyp, B->dgates, q);
+  return launch_combine_bwd(c.s, B->dout, B->yp, B->gates, B->row_of_pair,
+                            c.fcb ? nullptr : B->dyp, B->dgates, q);
 }
 static int bwd_route(const StepCtx& c, const moe_mb* B, hipStream_t q) {
   if (c.st->route_mode == MOE_ROUTE_FORCE_BALANCE) return MOE_OK;
@@ -756,9 +814,10 @@ static int bwd_route(const StepCtx& c, const moe_mb* B, hipStream_t q) {
 }
 static int bwd_dgrad(const StepCtx& c, const moe_mb* B, bool weights_ready, hipStream_t q,
                      int parts = kDgradBoth) {
-  return launch_ffn_dgrad(c.s, B->dyp, B->h, B->offsets, B->tile_offsets, c.st->W_gu,
-                          c.st->W_down, B->dh, B->dxp, c.wsW ? c.wsW : c.wsB,
-                          c.wsW ? true : weights_ready, q, parts);
+  const FusedCombineBwd fc{B->pair_of_row, B->gates, B->ag};
+  return launch_ffn_dgrad(c.s, c.fcb ? B->dout : B->dyp, B->h, B->offsets, B->tile_offsets,
+                          c.st->W_gu, c.st->W_down, B->dh, B->dxp, c.wsW ? c.wsW : c.wsB,
+                          c.wsW ? true : weights_ready, q, parts, c.fcb ? &fc : nullptr);
 }
 static int bwd_dispatch(const StepCtx& c, const moe_mb* B, hipStream_t q) {
   return do_dispatch_bwd(c.s, B->dxp, B->row_of_pair, B->idx, c.router ? B->dlogits : nullptr,
@@ -767,8 +826,9 @@ static int bwd_dispatch(const StepCtx& c, const moe_mb* B, hipStream_t q) {
 }
 static int bwd_wgrad(const StepCtx& c, const moe_mb* B, hipStream_t q) {
   return launch_ffn_wgrad(c.s, c.fused ? B->x : B->xp, c.fused ? B->pair_of_row : nullptr,
-                          B->a, B->dh, B->dyp, B->offsets, c.st->dW_gu,
-                          c.st->dW_down, (c.st->accumulate & MOE_ACCUM_DW) != 0, q);
+                          c.fcb ? B->ag : B->a, B->dh, c.fcb ? B->dout : B->dyp, B->offsets,
+                          c.st->dW_gu, c.st->dW_down, (c.st->accumulate & MOE_ACCUM_DW) != 0, q,
+                          c.fcb ? B->pair_of_row : nullptr);
 }
 
 // Host-side checks of one step description (flags, route mode, buffers,
@@ -778,7 +838,7 @@ static int check_step(const moe_step* st, int flags, const char* fn) {
   const moe_shape* s = &st->shape;
   if (int rc = validate_shape(s)) return rc;
   if (flags & ~(MOE_STEP_SERIALIZE | MOE_STEP_EAGER_WGRAD | MOE_STEP_SKIP_WGRAD |
-                MOE_STEP_FUSED_PERMUTE | MOE_STEP_MID_WGRAD))
+                MOE_STEP_FUSED_PERMUTE | MOE_STEP_MID_WGRAD | MOE_STEP_FUSED_COMBINE_BWD))
     return set_error(MOE_ERR_ARG, "%s: unknown flags 0x%x", fn, flags);
   if ((flags & MOE_STEP_EAGER_WGRAD ? 1 : 0) + (flags & MOE_STEP_SKIP_WGRAD ? 1 : 0) +
           (flags & MOE_STEP_MID_WGRAD ? 1 : 0) > 1)
@@ -797,10 +857,11 @@ static int check_step(const moe_step* st, int flags, const char* fn) {
   const moe_mb* A = st->fwd;
   const moe_mb* B = st->bwd;
   const bool fused = (flags & MOE_STEP_FUSED_PERMUTE) != 0;
-  if (fused) TRY(check_gather_x(s, fn));
+  const bool fcb = (flags & MOE_STEP_FUSED_COMBINE_BWD) != 0;
+  if (fused || fcb) TRY(check_gather_x(s, fn));
   if (A) TRY(validate_mb_fwd(A, mode, fused));
   if (B) {
-    TRY(validate_mb_bwd(B, mode, fused));
+    TRY(validate_mb_bwd(B, mode, fused, fcb));
     REQUIRE(st->dW_gu);
     REQUIRE(st->dW_down);
     if (mode == MOE_ROUTE_TOPK && st->dW_r) REQUIRE(B->x);
@@ -848,7 +909,8 @@ static int step_impl(const moe_step* st, hipStream_t s0, hipStream_t s1, int fla
   const size_t one = ws_one(s);
   const size_t sh = shared ? ws_shared(s, st->F_s) : 0;
   StepCtx c{st, s, st->ws, (char*)st->ws + one, mode == MOE_ROUTE_TOPK, fused,
-            (char*)st->ws + 2 * one, (char*)st->ws + 2 * one + sh, wsW};
+            (flags & MOE_STEP_FUSED_COMBINE_BWD) != 0, (char*)st->ws + 2 * one,
+            (char*)st->ws + 2 * one + sh, wsW};
   const bool serial = (flags & MOE_STEP_SERIALIZE) || s0 == s1;
   const bool eager = (flags & MOE_STEP_EAGER_WGRAD) != 0;
   const bool skip_w = (flags & MOE_STEP_SKIP_WGRAD) != 0;
@@ -1132,7 +1194,7 @@ extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, h
     char* shalf_s1 = ws + 2 * one;
     char* shalf_s0 = ws + 2 * one + sh;
     StepCtx c{st, s, even ? half_s1 : half_s0, even ? half_s0 : half_s1,
-              st->route_mode == MOE_ROUTE_TOPK, fused,
+              st->route_mode == MOE_ROUTE_TOPK, fused, (flags & MOE_STEP_FUSED_COMBINE_BWD) != 0,
               even ? shalf_s1 : shalf_s0, even ? shalf_s0 : shalf_s1, wsW};
     // The forward of step j also waits for the backward of step j - 2 (on
     // the other stream), the last earlier chain not ordered before it by its

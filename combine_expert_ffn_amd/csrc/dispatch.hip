@@ -437,9 +437,10 @@ int launch_combine(const moe_shape* s, const void* yp, const float* gates,
 
 // ---------------------------------------------------------------------------
 // combine backward: dyp[r] = g * dout[t]; dgates[t,k] = <dout[t], yp[r]>.
-// One wave per token; dout row held in registers.
+// One wave per token; dout row held in registers.  WRITE_DYP = false: dgates
+// only (the fused combine backward: the expert GEMMs gather dout themselves).
 // ---------------------------------------------------------------------------
-template <typename T, int MAXC>
+template <typename T, int MAXC, bool WRITE_DYP>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restrict__ dout,
                                                           const uint4* __restrict__ yp,
                                                           const float* __restrict__ gates,
@@ -500,7 +501,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
             dot = fmaf(dv[i][q], y[q], dot);
             o[q] = g * dv[i][q];
           }
-          dyp[(size_t)r * nch + c] = Chunk<T>::pack(o);
+          if constexpr (WRITE_DYP) dyp[(size_t)r * nch + c] = Chunk<T>::pack(o);
         }
       }
     } else {
@@ -516,7 +517,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
             dot = fmaf(dv[i][q], y[q], dot);
             o[q] = g * dv[i][q];
           }
-          dyp[(size_t)r * nch + c] = Chunk<T>::pack(o);
+          if constexpr (WRITE_DYP) dyp[(size_t)r * nch + c] = Chunk<T>::pack(o);
         }
       }
     }
@@ -529,10 +530,16 @@ template <typename T, int MAXC>
 static void combine_bwd_t(const moe_shape* s, const void* dout, const void* yp,
                           const float* gates, const int32_t* row_of_pair, void* dyp,
                           float* dgates, hipStream_t st) {
-  MOE_LAUNCH("combine_bwd", st,
-             combine_bwd_kernel<T, MAXC><<<(unsigned)cdiv(s->T, 4), 256, 0, st>>>(
-                 (const uint4*)dout, (const uint4*)yp, gates, row_of_pair, (uint4*)dyp, dgates,
-                 (int)s->T, (int)s->K, row_chunks(s)));
+  if (dyp)
+    MOE_LAUNCH("combine_bwd", st,
+               (combine_bwd_kernel<T, MAXC, true><<<(unsigned)cdiv(s->T, 4), 256, 0, st>>>(
+                   (const uint4*)dout, (const uint4*)yp, gates, row_of_pair, (uint4*)dyp, dgates,
+                   (int)s->T, (int)s->K, row_chunks(s))));
+  else
+    MOE_LAUNCH("combine_bwd", st,
+               (combine_bwd_kernel<T, MAXC, false><<<(unsigned)cdiv(s->T, 4), 256, 0, st>>>(
+                   (const uint4*)dout, (const uint4*)yp, gates, row_of_pair, nullptr, dgates,
+                   (int)s->T, (int)s->K, row_chunks(s))));
 }
 
 int launch_combine_bwd(const moe_shape* s, const void* dout, const void* yp, const float* gates,

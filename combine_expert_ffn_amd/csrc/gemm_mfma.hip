@@ -557,7 +557,15 @@ struct DownOp {
 
 // dgrad GEMM A: da = dy_p . W_down[e]  (A: dy_p rows, K = d; B: W_down[e]
 // transposed, W_downT[e] [F][d], K-contiguous) with the SwiGLU backward epilogue.
-template <class E>
+//
+// With FUSED (the fused combine backward), dy_p is never materialised:
+// dyp is the token matrix dout [T][d], dispatched row r of the A operand is
+// token xrows[r] / K (xrows is the plan's pair_of_row), and the gate of the
+// row, gates[xrows[r]], scales the float32 product in the epilogue, so
+// da = g . (dout . W_down[e]).  The epilogue then also writes
+// ag = g . silu(g_h) . u_h from the stored h, the operand that takes the
+// gate into the dW_down product of the weight gradient.
+template <class E, bool FUSED = false>
 struct DgradActOp {
   typedef E Elt;
   const uint16_t* dyp;
@@ -565,23 +573,46 @@ struct DgradActOp {
   const uint16_t* W_downT;
   uint16_t* dh;
   int d, F;
+  const int32_t* xrows;
+  int K;
+  const float* gates;
+  uint16_t* ag;
   __device__ __forceinline__ int k_len() const { return d; }
   template <class TL, class LA, class LB>
   __device__ __forceinline__ void init(int e, int m0, int m_end, int nt, LA& la, LB& lb,
                                        int tid) const {
     const int nb = nt * TL::BN;
     const uint16_t* WdT = W_downT + (size_t)e * F * d;
-    la.init(dyp + (size_t)m0 * d, [&](int r) { return (min(m0 + r, m_end - 1) - m0) * d; }, tid);
+    if constexpr (FUSED)
+      la.init(dyp, [&](int r) { return xrows[min(m0 + r, m_end - 1)] / K * d; }, tid);
+    else
+      la.init(dyp + (size_t)m0 * d, [&](int r) { return (min(m0 + r, m_end - 1) - m0) * d; },
+              tid);
     lb.init(WdT, [&](int n) { return min(nb + n, F - 1) * d; }, tid);
   }
   // The h chunks of this lane's rows are loaded (16 bytes each, rows clamped
   // to valid ones) before the block is staged, so their latency overlaps the
-  // staging.
+  // staging.  FUSED: the gates of all the lane's rows are loaded first, the
+  // pair indices of the rows together and then the gates together, so the
+  // dependent loads cost two memory waits per tile.
   template <class TL>
   __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TL::TM][TL::TN], int e, int m0,
                                            int m_end, int nt, uint16_t* smem) const {
     const WavePos w = WavePos::of<TL>();
     const int c = st_col(w.lane);
+    float grow[FUSED ? TL::TM : 1][4];
+    if constexpr (FUSED) {
+      int pr[TL::TM][4];
+#pragma unroll
+      for (int i = 0; i < TL::TM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          pr[i][q] = xrows[min(m0 + w.wm * TL::WTM + i * 32 + st_row(q, w.lane), m_end - 1)];
+#pragma unroll
+      for (int i = 0; i < TL::TM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) grow[i][q] = gates[pr[i][q]];
+    }
 #pragma unroll
     for (int p = 0; p < TL::TN / 2; ++p) {
       const int cb = nt * TL::BN + w.wn * TL::WTN + p * 64;
@@ -590,30 +621,36 @@ struct DgradActOp {
       for (int i = 0; i < TL::TM; ++i) {
         const int rb = m0 + w.wm * TL::WTM + i * 32;
         uint4 gv[4], uv[4];
+        float gr[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const size_t rowc = (size_t)min(rb + st_row(q, w.lane), m_end - 1);
           gv[q] = *(const uint4*)(hbuf + rowc * 2 * F + cb + c);
           uv[q] = *(const uint4*)(hbuf + rowc * 2 * F + F + cb + c);
+          if constexpr (FUSED) gr[q] = grow[i][q];
         }
         const float* blk = stage_rows<TL>(acc, i, p, smem, w.wave, w.lane);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int r = st_row(q, w.lane);
-          float da[8], g[8], u[8], dg[8], du[8];
+          float da[8], g[8], u[8], dg[8], du[8], av[8];
           ld8(blk + r * EP_LD + c, da);
           Chunk<typename E::elt>::unpack(gv[q], g);
           Chunk<typename E::elt>::unpack(uv[q], u);
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
             const float sg = sigmoid_f(g[t]);
-            dg[t] = da[t] * u[t] * sg * (1.0f + g[t] * (1.0f - sg));
-            du[t] = da[t] * g[t] * sg;
+            const float dat = FUSED ? da[t] * gr[q] : da[t];
+            dg[t] = dat * u[t] * sg * (1.0f + g[t] * (1.0f - sg));
+            du[t] = dat * g[t] * sg;
+            if constexpr (FUSED) av[t] = gr[q] * (g[t] * sg) * u[t];
           }
           if (rb + r < m_end) {
             const size_t row = (size_t)(rb + r);
             *(uint4*)(dh + row * 2 * F + cb + c) = Chunk<typename E::elt>::pack(dg);
             *(uint4*)(dh + row * 2 * F + F + cb + c) = Chunk<typename E::elt>::pack(du);
+            if constexpr (FUSED)
+              *(uint4*)(ag + row * F + cb + c) = Chunk<typename E::elt>::pack(av);
           }
         }
       }
@@ -757,9 +794,14 @@ __device__ __forceinline__ long long uniform64(long long v) {
 // only the first product is formed, dyp holds x [T][d], abuf holds the split
 // dlogits [T][F] (F = 2E) and dW_down receives one float32 partial [d][F] per
 // chunk; offsets, xp, dh and dW_gu are unused.
+// GD (the fused combine backward): dy_p is not materialised; dyp is the token
+// matrix dout [T][d], the dW_down tiles read dispatched row r of their A
+// operand from token xrows[r] / K through the same LDS token list, and abuf
+// holds ag = gate . a, so dW_down[e] = sum_r dout[t_r] (outer) ag[r].
+//
 // ACC: add into the existing values of dW (gradient accumulation) instead of
 // overwriting them.
-template <bool GATHER, class E, bool ROUTER, bool ACC>
+template <bool GATHER, class E, bool ROUTER, bool ACC, bool GD = false>
 __global__ __launch_bounds__(512) void wgrad_kernel(
     const uint16_t* __restrict__ xp, const int32_t* __restrict__ xrows, int K,
     const uint16_t* __restrict__ abuf, const uint16_t* __restrict__ dh,
@@ -770,7 +812,7 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
   constexpr int STAGE = 2 * BK * WG_ROWB;  // A + B tiles
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
   __shared__ long long s_it[257];  // first k-step of each expert's tiles; s_it[E_l] = W
-  __shared__ int s_tok[GATHER ? 2 : 1][BK];  // source token rows of the next two stages
+  __shared__ int s_tok[(GATHER || GD) ? 2 : 1][BK];  // source token rows of the next two stages
   const int tdm = (d + 255) / 256, tdn = (F + 255) / 256;
   const int tgm = (2 * F + 255) / 256, tgn = (d + 255) / 256;
   const int per_e = tdm * tdn + (ROUTER ? 0 : tgm * tgn);
@@ -814,7 +856,7 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
   // Tile gt of the expert-major order: its expert, operands, output and
   // k-steps; valid = false once the group's range of work is done.
   struct TileJob {
-    bool valid, gat;
+    bool valid, gat, ga, gb;  // gathers a token-indexed operand: A (dW_down), B (dW_gu)
     int r0, r1, M, N, m0, n0, nk;
     const uint16_t *Asrc, *Bsrc;
     float* out;
@@ -834,8 +876,9 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
     j.r0 = off(e);
     j.r1 = off(e + 1);
     j.nk = (j.r1 - j.r0 + BK - 1) / BK;
-    j.gat = false;
     if (t < tdm * tdn) {
+      j.ga = GD;
+      j.gb = false;
       j.Asrc = dyp;
       j.Bsrc = abuf;
       j.M = d;
@@ -847,13 +890,15 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
       t -= tdm * tdn;
       j.Asrc = dh;
       j.Bsrc = xp;
-      j.gat = GATHER;
+      j.ga = false;
+      j.gb = GATHER;
       j.M = 2 * F;
       j.N = d;
       j.m0 = (t / tgn) * 256;
       j.n0 = (t % tgn) * 256;
       j.out = dW_gu + (size_t)e * 2 * F * d;
     }
+    j.gat = j.ga || j.gb;
     return j;
   };
   // source token of dispatched row r of tile job c (-1 past the expert's end)
@@ -864,15 +909,18 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
   auto issue_stage0 = [&](const TileJob& c) {
     const LoadKM<NW> la{c.Asrc, (long)c.M, c.M, c.m0, lane, wave};
     const LoadKM<NW> lb{c.Bsrc, (long)c.N, c.N, c.n0, lane, wave};
-    la.issue(smem, c.r0, c.r1);
-    if (GATHER && c.gat)
+    if (GD && c.ga)
+      la.template issue<true>(smem, c.r0, c.r1, s_tok[0]);
+    else
+      la.issue(smem, c.r0, c.r1);
+    if (GATHER && c.gb)
       lb.template issue<true>(smem + BK * WG_ROWB, c.r0, c.r1, s_tok[0]);
     else
       lb.issue(smem + BK * WG_ROWB, c.r0, c.r1);
   };
   TileJob cur = job(gt0 + slot);
   long long gt = gt0 + slot;
-  bool pre = cur.valid && cur.nk > 0 && !(GATHER && cur.gat);
+  bool pre = cur.valid && cur.nk > 0 && !((GATHER || GD) && cur.gat);
   if (pre) issue_stage0(cur);
   while (cur.valid) {
     const LoadKM<NW> la{cur.Asrc, (long)cur.M, cur.M, cur.m0, lane, wave};
@@ -887,7 +935,7 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     if (nk > 0) {  // block-uniform
       if (!pre) {
-        if constexpr (GATHER) {
+        if constexpr (GATHER || GD) {
           if (cur.gat) {
             if (tid < BK) {
               s_tok[0][tid] = token(cur, r0 + tid);
@@ -904,8 +952,11 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
         uint8_t* cur_s = smem + (kt & 1) * STAGE;
         uint8_t* nxt_s = smem + ((kt + 1) & 1) * STAGE;
         if (kt + 1 < nk) {
-          la.issue(nxt_s, r0 + (kt + 1) * BK, r1);
-          if (GATHER && cur.gat)
+          if (GD && cur.ga)
+            la.template issue<true>(nxt_s, 0, 0, s_tok[(kt + 1) & 1]);
+          else
+            la.issue(nxt_s, r0 + (kt + 1) * BK, r1);
+          if (GATHER && cur.gb)
             lb.template issue<true>(nxt_s + BK * WG_ROWB, 0, 0, s_tok[(kt + 1) & 1]);
           else
             lb.issue(nxt_s + BK * WG_ROWB, r0 + (kt + 1) * BK, r1);
@@ -914,7 +965,7 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
         // (its last reader, the issue of stage kt, is behind the previous
         // barrier)
         int tk = -1;
-        if (GATHER && cur.gat && tid < BK) tk = token(cur, r0 + (kt + 2) * BK + tid);
+        if ((GATHER || GD) && cur.gat && tid < BK) tk = token(cur, r0 + (kt + 2) * BK + tid);
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
           bf16x8_t a[TM], b[TN];
@@ -930,15 +981,28 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
               acc[i][j] = E::mfma(a[i], b[j], acc[i][j]);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        if (GATHER && cur.gat && tid < BK) s_tok[kt & 1][tid] = tk;
+        if ((GATHER || GD) && cur.gat && tid < BK) s_tok[kt & 1][tid] = tk;
         __syncthreads();
       }
     }
-    // the next tile's stage 0 goes out before this tile's epilogue
+    // the next tile's stage 0 goes out before this tile's epilogue (a tile
+    // that gathers first has its first two token lists written: this tile's
+    // last reader of the lists is behind the main loop's final barrier)
     gt += nslots;
     const TileJob nxt = job(gt);
-    pre = nxt.valid && nxt.nk > 0 && !(GATHER && nxt.gat);
-    if (pre) issue_stage0(nxt);
+    pre = nxt.valid && nxt.nk > 0;
+    if (pre) {
+      if constexpr (GATHER || GD) {
+        if (nxt.gat) {  // block-uniform
+          if (tid < BK) {
+            s_tok[0][tid] = token(nxt, nxt.r0 + tid);
+            s_tok[1][tid] = token(nxt, nxt.r0 + BK + tid);
+          }
+          __syncthreads();
+        }
+      }
+      issue_stage0(nxt);
+    }
     // Epilogue.  The eight 32 x 32 pieces of the wave's tile are written in
     // batches of PB; with ACC, the previous values of batch b + 1 are loaded
     // before batch b is stored, so each batch's loads are in flight while the
@@ -1135,15 +1199,23 @@ int ffn_fwd_t(const moe_shape* s, const void* xp, const int32_t* xrows, const in
 template <class E>
 int ffn_dgrad_t(const moe_shape* s, const void* dyp, const void* h, const int32_t* offsets,
                 const int32_t* tile_offsets, void* dh, void* dxp, void* ws, hipStream_t st,
-                int parts) {
+                int parts, const FusedCombineBwd* fc) {
   const int d = (int)s->d, F = (int)s->F;
   const uint16_t* W_downT = (const uint16_t*)((char*)ws + ws_wT_offset(s));
   const uint16_t* W_guT = (const uint16_t*)((const char*)W_downT + ws_wT_down_bytes(s));
   if (parts & kDgradAct) {
-    DgradActOp<E> da{(const uint16_t*)dyp, (const uint16_t*)h, W_downT, (uint16_t*)dh, d, F};
-    if (int rc = launch_row_grouped("dgrad_act", s, da, offsets, tile_offsets,
-                                    (F + T256::BN - 1) / T256::BN, st))
-      return rc;
+    const int nt = (F + T256::BN - 1) / T256::BN;
+    if (fc) {
+      DgradActOp<E, true> da{(const uint16_t*)dyp, (const uint16_t*)h, W_downT, (uint16_t*)dh,
+                             d, F, fc->pair_of_row, (int)s->K, fc->gates, (uint16_t*)fc->ag};
+      if (int rc = launch_row_grouped("dgrad_act", s, da, offsets, tile_offsets, nt, st))
+        return rc;
+    } else {
+      DgradActOp<E> da{(const uint16_t*)dyp, (const uint16_t*)h, W_downT, (uint16_t*)dh, d, F,
+                       nullptr, 0, nullptr, nullptr};
+      if (int rc = launch_row_grouped("dgrad_act", s, da, offsets, tile_offsets, nt, st))
+        return rc;
+    }
   }
   if (!(parts & kDgradIn)) return MOE_OK;
   DgradInOp<E> di{(const uint16_t*)dh, W_guT, (uint16_t*)dxp, d, F};
@@ -1154,26 +1226,33 @@ int ffn_dgrad_t(const moe_shape* s, const void* dyp, const void* h, const int32_
 template <class E>
 void wgrad_t(const moe_shape* s, const void* xp, const int32_t* xrows, const void* a,
              const void* dh, const void* dyp, const int32_t* offsets, float* dW_gu,
-             float* dW_down, bool accumulate, hipStream_t st) {
+             float* dW_down, bool accumulate, hipStream_t st, const int32_t* dyrows) {
   const int d = (int)s->d, F = (int)s->F, E_l = (int)s->E_l;
   const long per_e = (long)((d + 255) / 256) * ((F + 255) / 256) +
                      (long)((2 * F + 255) / 256) * ((d + 255) / 256);
   const int grid = persistent_grid(E_l * per_e);
-  auto go = [&](auto gather, auto acc) {
+  // both gathers take their token list from the plan's pair_of_row
+  const int32_t* rows = xrows ? xrows : dyrows;
+  auto go = [&](auto gather, auto gd, auto acc) {
     MOE_LAUNCH("wgrad", st,
-               (wgrad_kernel<decltype(gather)::value, E, false, decltype(acc)::value>
-                <<<grid, 512, 0, st>>>((const uint16_t*)xp, xrows, (int)s->K,
+               (wgrad_kernel<decltype(gather)::value, E, false, decltype(acc)::value,
+                             decltype(gd)::value>
+                <<<grid, 512, 0, st>>>((const uint16_t*)xp, rows, (int)s->K,
                                        (const uint16_t*)a, (const uint16_t*)dh,
                                        (const uint16_t*)dyp, offsets, dW_gu, dW_down, E_l, d, F)));
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
+  auto acc_ = [&](auto gather, auto gd) {
+    if (accumulate) go(gather, gd, T_{});
+    else go(gather, gd, F_{});
+  };
   if (xrows) {
-    if (accumulate) go(T_{}, T_{});
-    else go(T_{}, F_{});
+    if (dyrows) acc_(T_{}, T_{});
+    else acc_(T_{}, F_{});
   } else {
-    if (accumulate) go(F_{}, T_{});
-    else go(F_{}, F_{});
+    if (dyrows) acc_(F_{}, T_{});
+    else acc_(F_{}, F_{});
   }
 }
 
@@ -1221,22 +1300,22 @@ int launch_dgrad_weights_mfma(const moe_shape* s, const void* W_gu, const void* 
 int launch_ffn_dgrad_mfma(const moe_shape* s, const void* dyp, const void* h,
                           const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
                           const void* W_down, void* dh, void* dxp, void* ws, bool weights_ready,
-                          hipStream_t st, int parts) {
+                          hipStream_t st, int parts, const FusedCombineBwd* fc) {
   if (!weights_ready)
     if (int rc = launch_dgrad_weights_mfma(s, W_gu, W_down, ws, st)) return rc;
   return s->dtype == MOE_F16
-             ? ffn_dgrad_t<F16>(s, dyp, h, offsets, tile_offsets, dh, dxp, ws, st, parts)
-             : ffn_dgrad_t<BF16>(s, dyp, h, offsets, tile_offsets, dh, dxp, ws, st, parts);
+             ? ffn_dgrad_t<F16>(s, dyp, h, offsets, tile_offsets, dh, dxp, ws, st, parts, fc)
+             : ffn_dgrad_t<BF16>(s, dyp, h, offsets, tile_offsets, dh, dxp, ws, st, parts, fc);
 }
 
 int launch_ffn_wgrad_mfma(const moe_shape* s, const void* xp, const int32_t* xrows,
                           const void* a, const void* dh, const void* dyp,
                           const int32_t* offsets, float* dW_gu, float* dW_down, bool accumulate,
-                          hipStream_t st) {
+                          hipStream_t st, const int32_t* dyrows) {
   if (s->dtype == MOE_F16)
-    wgrad_t<F16>(s, xp, xrows, a, dh, dyp, offsets, dW_gu, dW_down, accumulate, st);
+    wgrad_t<F16>(s, xp, xrows, a, dh, dyp, offsets, dW_gu, dW_down, accumulate, st, dyrows);
   else
-    wgrad_t<BF16>(s, xp, xrows, a, dh, dyp, offsets, dW_gu, dW_down, accumulate, st);
+    wgrad_t<BF16>(s, xp, xrows, a, dh, dyp, offsets, dW_gu, dW_down, accumulate, st, dyrows);
   return check_launch("wgrad GEMM");
 }
 

@@ -65,8 +65,12 @@ __global__ __launch_bounds__(256) void f32_down_kernel(const float* __restrict__
   yp[(size_t)row * d + c] = y;
 }
 
+// xrows: null, or pair_of_row for the fused combine backward: dyp is then
+// dout, row r reads token xrows[r] / K, the product is scaled by the pair's
+// gate and ag = gate * silu(g) * u is written too.
 __global__ __launch_bounds__(256) void f32_dgrad_act_kernel(
-    const float* __restrict__ dyp, const float* __restrict__ hbuf,
+    const float* __restrict__ dyp, const int32_t* __restrict__ xrows, int K,
+    const float* __restrict__ gates, float* __restrict__ ag, const float* __restrict__ hbuf,
     const int32_t* __restrict__ offsets, const float* __restrict__ W_down,
     float* __restrict__ dh, long cap, int E_l, int d, int F) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
@@ -74,15 +78,18 @@ __global__ __launch_bounds__(256) void f32_dgrad_act_kernel(
   const int row = (int)(i / F), j = (int)(i % F);
   if (row >= offsets[E_l]) return;
   const int e = expert_of_row(offsets, E_l, row);
-  const float* dy = dyp + (size_t)row * d;
+  const float* dy = dyp + (size_t)(xrows ? xrows[row] / K : row) * d;
   const float* w = W_down + (size_t)e * d * F + j;
   float da = 0.f;
   for (int c = 0; c < d; ++c) da = fmaf(dy[c], w[(size_t)c * F], da);
+  const float gate = xrows ? gates[xrows[row]] : 1.f;
+  da *= gate;
   const float g = hbuf[(size_t)row * 2 * F + j];
   const float u = hbuf[(size_t)row * 2 * F + F + j];
   const float s = sigmoid_f(g);
   dh[(size_t)row * 2 * F + j] = da * u * s * (1.0f + g * (1.0f - s));
   dh[(size_t)row * 2 * F + F + j] = da * g * s;
+  if (xrows) ag[(size_t)row * F + j] = gate * (g * s) * u;
 }
 
 __global__ __launch_bounds__(256) void f32_dgrad_in_kernel(const float* __restrict__ dh,
@@ -103,10 +110,12 @@ __global__ __launch_bounds__(256) void f32_dgrad_in_kernel(const float* __restri
 }
 
 // dW_down[e][i][f] = sum_r dyp[r][i] a[r][f]; dW_gu[e][m][c] = sum_r dh[r][m] xp[r][c]
+// (dyrows set: dyp is dout and row r of it is token dyrows[r] / K)
 __global__ __launch_bounds__(256) void f32_wgrad_kernel(
     const float* __restrict__ xp, const int32_t* __restrict__ xrows, int K,
     const float* __restrict__ a, const float* __restrict__ dh,
-    const float* __restrict__ dyp, const int32_t* __restrict__ offsets,
+    const float* __restrict__ dyp, const int32_t* __restrict__ dyrows,
+    const int32_t* __restrict__ offsets,
     float* __restrict__ dW_gu, float* __restrict__ dW_down, int E_l, int d, int F,
     int accumulate) {
   const long per_e = (long)d * F + 2L * F * d;
@@ -119,7 +128,8 @@ __global__ __launch_bounds__(256) void f32_wgrad_kernel(
   float* o;
   if (q < (long)d * F) {
     const int ii = (int)(q / F), f = (int)(q % F);
-    for (int r = r0; r < r1; ++r) acc = fmaf(dyp[(size_t)r * d + ii], a[(size_t)r * F + f], acc);
+    for (int r = r0; r < r1; ++r)
+      acc = fmaf(dyp[(size_t)(dyrows ? dyrows[r] / K : r) * d + ii], a[(size_t)r * F + f], acc);
     o = dW_down + (size_t)e * d * F + q;
   } else {
     q -= (long)d * F;
@@ -139,11 +149,11 @@ int launch_dgrad_weights_mfma(const moe_shape* s, const void* W_gu, const void* 
 int launch_ffn_dgrad_mfma(const moe_shape* s, const void* dyp, const void* h,
                           const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
                           const void* W_down, void* dh, void* dxp, void* ws, bool weights_ready,
-                          hipStream_t st, int parts);
+                          hipStream_t st, int parts, const FusedCombineBwd* fc);
 int launch_ffn_wgrad_mfma(const moe_shape* s, const void* xp, const int32_t* xrows,
                           const void* a, const void* dh, const void* dyp,
                           const int32_t* offsets, float* dW_gu, float* dW_down, bool accumulate,
-                          hipStream_t st);
+                          hipStream_t st, const int32_t* dyrows);
 
 int launch_ffn_fwd(const moe_shape* s, const void* xp, const int32_t* xrows,
                    const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
@@ -171,18 +181,20 @@ int launch_dgrad_weights(const moe_shape* s, const void* W_gu, const void* W_dow
 
 int launch_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h, const int32_t* offsets,
                      const int32_t* tile_offsets, const void* W_gu, const void* W_down, void* dh,
-                     void* dxp, void* ws, bool weights_ready, hipStream_t st, int parts) {
+                     void* dxp, void* ws, bool weights_ready, hipStream_t st, int parts,
+                     const FusedCombineBwd* fc) {
   if (s->T == 0) return MOE_OK;
   if (is16(s))
     return launch_ffn_dgrad_mfma(s, dyp, h, offsets, tile_offsets, W_gu, W_down, dh, dxp, ws,
-                                 weights_ready, st, parts);
+                                 weights_ready, st, parts, fc);
   const long cap = s->T * s->K;
   const int d = (int)s->d, F = (int)s->F, E_l = (int)s->E_l;
   if (parts & kDgradAct) {
     MOE_LAUNCH("f32_dgrad_act", st,
                f32_dgrad_act_kernel<<<(unsigned)cdiv(cap * F, 256), 256, 0, st>>>(
-        (const float*)dyp, (const float*)h, offsets, (const float*)W_down, (float*)dh, cap, E_l,
-        d, F));
+        (const float*)dyp, fc ? fc->pair_of_row : nullptr, (int)s->K, fc ? fc->gates : nullptr,
+        fc ? (float*)fc->ag : nullptr, (const float*)h, offsets, (const float*)W_down,
+        (float*)dh, cap, E_l, d, F));
     if (int rc = check_launch("f32 dgrad (activation)")) return rc;
   }
   if (!(parts & kDgradIn)) return MOE_OK;
@@ -194,15 +206,15 @@ int launch_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h, const i
 
 int launch_ffn_wgrad(const moe_shape* s, const void* xp, const int32_t* xrows, const void* a,
                      const void* dh, const void* dyp, const int32_t* offsets, float* dW_gu,
-                     float* dW_down, bool accumulate, hipStream_t st) {
+                     float* dW_down, bool accumulate, hipStream_t st, const int32_t* dyrows) {
   if (is16(s))
     return launch_ffn_wgrad_mfma(s, xp, xrows, a, dh, dyp, offsets, dW_gu, dW_down, accumulate,
-                                 st);
+                                 st, dyrows);
   const long n = s->E_l * (s->d * s->F + 2 * s->F * s->d);
   MOE_LAUNCH("f32_wgrad", st,
              f32_wgrad_kernel<<<(unsigned)cdiv(n, 256), 256, 0, st>>>(
-      (const float*)xp, xrows, (int)s->K, (const float*)a, (const float*)dh, (const float*)dyp, offsets, dW_gu,
-      dW_down, (int)s->E_l, (int)s->d, (int)s->F, accumulate ? 1 : 0));
+      (const float*)xp, xrows, (int)s->K, (const float*)a, (const float*)dh, (const float*)dyp,
+      dyrows, offsets, dW_gu, dW_down, (int)s->E_l, (int)s->d, (int)s->F, accumulate ? 1 : 0));
   return check_launch("f32 wgrad");
 }
 

@@ -252,12 +252,26 @@ int launch_dgrad_weights(const moe_shape* s, const void* W_gu, const void* W_dow
 // kDgradAct (dy_p -> dh, with the SwiGLU backward), kDgradIn (dh -> dx_p), or
 // both in that order; a call with kDgradIn alone needs the copies made.
 enum { kDgradAct = 1, kDgradIn = 2, kDgradBoth = 3 };
+// The fused combine backward: dy_p is not materialised.  The dgrad's first
+// GEMM reads its rows from dout through the plan's pair_of_row (dyp is then
+// dout [T][d]) and scales each by its pair's gate in float32; it also writes
+// ag = gate * silu(g) * u [T*K][F], which the weight gradient's dW_down
+// product takes with the gathered dout rows.
+struct FusedCombineBwd {
+  const int32_t* pair_of_row;
+  const float* gates;  // [T*K], indexed by pair t*K + k
+  void* ag;            // [T*K][F]
+};
 int launch_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h, const int32_t* offsets,
                      const int32_t* tile_offsets, const void* W_gu, const void* W_down, void* dh,
                      void* dxp, void* ws, bool weights_ready, hipStream_t st,
-                     int parts = kDgradBoth);
+                     int parts = kDgradBoth, const FusedCombineBwd* fc = nullptr);
+// dyrows: null, or pair_of_row for the fused combine backward, in which case
+// dyp is dout [T][d] (row r of the dW_down operand is token dyrows[r] / K) and
+// a is ag.
 int launch_ffn_wgrad(const moe_shape* s, const void* xp, const int32_t* xrows, const void* a,
                      const void* dh, const void* dyp, const int32_t* offsets, float* dW_gu,
-                     float* dW_down, bool accumulate, hipStream_t st);
+                     float* dW_down, bool accumulate, hipStream_t st,
+                     const int32_t* dyrows = nullptr);
 
 }  // namespace moe

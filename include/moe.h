@@ -98,6 +98,18 @@ extern "C" {
                                    partial last round of tiles share the chip with
                                    the other stream's GEMMs.  Excludes EAGER_WGRAD
                                    and SKIP_WGRAD; results are unchanged           */
+#define MOE_STEP_FUSED_COMBINE_BWD 32 /* the fused permute's mirror on the backward
+                                   side: the combine backward writes only dgates
+                                   (no dy_p); the dgrad's first GEMM gathers the
+                                   dout rows through pair_of_row and scales them by
+                                   the rows' gates, and writes ag = gate * a' (a'
+                                   recomputed from the stored h); the wgrad's
+                                   dW_down product takes the gathered dout rows
+                                   and ag.  `bwd` needs ag [T*K,F] and pair_of_row;
+                                   its dyp may be NULL.  The results match the
+                                   unfused path within the numeric tolerance (the
+                                   gate is applied in float32 instead of through a
+                                   rounded dy_p), not bit for bit               */
 
 /*
  * Layer shape.  T tokens of hidden size d; E experts routed over, of which the
@@ -244,6 +256,8 @@ int moe_combine(const moe_shape* s, const void* yp, const float* gates,
  * backward first).  For each local pair (t,k) with row r:
  *   dyp[r] = gates[t,k] * dout[t];  dgates[t,k] = <dout[t], yp[r]> (f32)
  * dgates is 0 for non-local pairs.  dout [T,d], dyp [T*K,d] (rows >= N untouched).
+ * dyp may be NULL: dgates only (the fused combine backward, whose GEMMs read
+ * dout themselves: moe_ffn_dgrad_gather, moe_ffn_wgrad_fused).
  */
 int moe_combine_bwd(const moe_shape* s, const void* dout, const void* yp,
                     const float* gates, const int32_t* row_of_pair, void* dyp,
@@ -285,6 +299,38 @@ int moe_ffn_wgrad_gather(const moe_shape* s, const void* x, const int32_t* pair_
                          const void* a, const void* dh, const void* dyp,
                          const int32_t* offsets, float* dW_gu, float* dW_down,
                          int accumulate, hipStream_t stream);
+
+/*
+ * moe_ffn_dgrad_gather - moe_ffn_dgrad with the combine backward fused in (the
+ * mirror, on the backward side, of the fused permute that page 1 lists as
+ * moe_permute_fusion): dy_p is never materialised.  Row r of the first
+ * product reads token pair_of_row[r] / K of dout [T,d] and is scaled by that
+ * pair's gate in float32:
+ *   da = gates[p] * (dout[p / K] . W_down[j]),  p = pair_of_row[r];
+ * dh and dxp as moe_ffn_dgrad.  It also writes, for the fused weight gradient,
+ *   ag [T*K,F]:  ag[r] = gates[p] * silu(g) * u  (g, u from the stored h).
+ * gates [T*K] f32 (the pairs' gates), pair_of_row from moe_dispatch.  dout
+ * must stay below 2^31 bytes.  Results are within the numeric tolerance of
+ * moe_combine_bwd + moe_ffn_dgrad (the gate is not rounded into dy_p first).
+ */
+int moe_ffn_dgrad_gather(const moe_shape* s, const void* dout, const int32_t* pair_of_row,
+                         const float* gates, const void* h, const int32_t* offsets,
+                         const int32_t* tile_offsets, const void* W_gu, const void* W_down,
+                         void* dh, void* dxp, void* ag, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/*
+ * moe_ffn_wgrad_fused - the weight gradient of the fused combine backward:
+ *   dW_down[j] = sum_r dout[pair_of_row[r] / K] (outer) ag[r]     (= dy_p^T . a)
+ *   dW_gu[j]   = sum_r dh[r] (outer) xp[r]
+ * with ag from moe_ffn_dgrad_gather.  xp NULL: the permute is fused too, and
+ * dW_gu reads row r of its operand as token pair_of_row[r] / K of x [T,d].
+ * accumulate as moe_ffn_wgrad.  dout (and x) must stay below 2^31 bytes.
+ */
+int moe_ffn_wgrad_fused(const moe_shape* s, const void* xp, const void* x,
+                        const int32_t* pair_of_row, const void* ag, const void* dh,
+                        const void* dout, const int32_t* offsets, float* dW_gu, float* dW_down,
+                        int accumulate, hipStream_t stream);
 
 /*
  * moe_route_bwd - backward of the top-K softmax gates and of the router
@@ -385,6 +431,8 @@ typedef struct moe_mb {
   void* y_s;    /* [T,d]    forward */
   void* dh_s;   /* [T,2F_s] backward */
   void* dx_s;   /* [T,d]    backward */
+  /* fused combine backward (MOE_STEP_FUSED_COMBINE_BWD) */
+  void* ag;     /* [T*K,F]  gate-scaled activation for the dW_down product */
 } moe_mb;
 
 typedef struct moe_step {

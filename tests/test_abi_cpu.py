@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_struct_layouts_match_header():
     assert C.sizeof(_lib.MoeShape) == 7 * 8 + 2 * 4
-    assert C.sizeof(_lib.MoeMB) == len(_lib.MB_FIELDS) * 8 == 26 * 8
+    assert C.sizeof(_lib.MoeMB) == len(_lib.MB_FIELDS) * 8 == 27 * 8
     # shape + 2 ints + 7 pointers + 2 mb pointers + ws + ws_bytes + F_s + 4 shared pointers
     assert C.sizeof(_lib.MoeStep) == C.sizeof(_lib.MoeShape) + 8 + 7 * 8 + 2 * 8 + 8 + 8 + 8 + 4 * 8
 

@@ -83,6 +83,26 @@ def _tau(w):
     return TAU["f32"] * max(1.0, (w.d / 128) ** 0.5)
 
 
+def _oracle_fused_bwd(w, X, ref, refb, prec):
+    """The oracle for the fused combine backward: the same definitions with
+    rounding only where that path stores a tensor.  dy_p is not stored, so the
+    dgrad takes the unrounded g * dout rows (oracle ffn_dgrad on them); ag =
+    g * silu(g_h) * u_h from the stored h, rounded once; dW_down = sum over
+    rows of dout (outer) ag (oracle ffn_wgrad with those operands)."""
+    K, F, N = w.K, w.F, ref["N"]
+    pr = ref["pair_of_row"][:N]
+    g = np.asarray(ref["gates"], np.float64).reshape(-1)[pr][:, None]
+    dout_rows = X["dout"][pr // K]
+    dh, dxp = O.ffn_dgrad(g * dout_rows, ref["h"], ref["offsets"], X["W_gu"], X["W_down"], prec)
+    hg, hu = ref["h"][:, :F], ref["h"][:, F:]
+    ag = O.store(g * (hg / (1.0 + np.exp(-hg))) * hu, prec)
+    dW_gu, dW_down = O.ffn_wgrad(ref["xp"], ag, dh, dout_rows, ref["offsets"], prec=prec)
+    topk = w.route == "topk"
+    dx = O.dispatch_bwd(dxp, ref["row_of_pair"], refb["dlogits"] if topk else None, X["W_r"],
+                        None, prec)
+    return dict(dh=dh, dxp=dxp, ag=ag, dW_gu=dW_gu, dW_down=dW_down, dx=dx)
+
+
 def _oracle(w, inp, prec):
     X = {k: (None if v is None else np.asarray(v, np.float64)) for k, v in inp.items()}
     fb = w.route == "force_balance"
@@ -189,6 +209,33 @@ def test_stage_parity(name):
     close("dh", host(mb.dh, N), refb["dh"], tau)
     close("dxp", host(mb.dxp, N), refb["dxp"], tau)
 
+    # ---- fused combine backward (oracle dout, h): no dy_p; dgrad gathers dout
+    # and applies the gates, writes ag; wgrad takes dout and ag
+    dg_only = torch.full_like(mb.dgates, 9.0)
+    M.moe_combine_bwd(s, dout, yp_r, gates_r, mb.row_of_pair, None, dg_only)
+    assert torch.equal(dg_only, mb.dgates), "combine backward without dy_p: dgates"
+    fb = M.MicroBatch(s, fused_bwd=True)
+    gflat = gates_r.reshape(-1)
+    M.moe_ffn_dgrad_gather(s, dout, mb.pair_of_row, gflat, h_r, mb.offsets, mb.tile_offsets,
+                           W_gu, W_down, fb.dh, fb.dxp, fb.ag, ws)
+    fo = _oracle_fused_bwd(w, X, ref, refb, prec)
+    close("dh (fused combine bwd)", host(fb.dh, N), fo["dh"], tau)
+    close("dxp (fused combine bwd)", host(fb.dxp, N), fo["dxp"], tau)
+    close("ag (fused combine bwd)", host(fb.ag, N), fo["ag"], tau)
+    fW_gu = torch.full((w.E_l, 2 * w.F, w.d), 7.0, dtype=torch.float32, device="cuda")
+    fW_down = torch.full((w.E_l, w.d, w.F), 7.0, dtype=torch.float32, device="cuda")
+    dh_o = D(_pad(fo["dh"], cap))
+    ag_o = D(_pad(fo["ag"], cap))
+    M.moe_ffn_wgrad_fused(s, mb.xp, None, mb.pair_of_row, ag_o, dh_o, dout, mb.offsets, fW_gu,
+                          fW_down, 0)
+    close("dW_gu (fused combine bwd)", host(fW_gu), fo["dW_gu"], tau)
+    close("dW_down (fused combine bwd)", host(fW_down), fo["dW_down"], tau)
+    g2 = [torch.full_like(fW_gu, 7.0), torch.full_like(fW_down, 7.0)]
+    M.moe_ffn_wgrad_fused(s, None, x, mb.pair_of_row, ag_o, dh_o, dout, mb.offsets, g2[0], g2[1],
+                          0)   # the permute fused as well: dW_gu gathers x
+    exact("dW_gu (fused combine bwd + fused permute)", host(g2[0]), host(fW_gu))
+    exact("dW_down (fused combine bwd + fused permute)", host(g2[1]), host(fW_down))
+
     # ---- dispatch backward (oracle dxp, dlogits)
     dxp_r = D(_pad(refb["dxp"], cap))
     dl_r = dev(refb["dlogits"], "f32x") if topk else None
@@ -228,7 +275,8 @@ def _layer_step(w, inp, flags=0, s_copy=None):
     topk = w.route == "topk"
     A = M.MicroBatch(s, x=D(inp["x"]), dout=D(inp["dout"]),
                      gates=None if topk else dev(inp["gates"], "f32x"),
-                     fused=bool(flags & M.MOE_STEP_FUSED_PERMUTE))
+                     fused=bool(flags & M.MOE_STEP_FUSED_PERMUTE),
+                     fused_bwd=bool(flags & M.MOE_STEP_FUSED_COMBINE_BWD))
     W_gu, W_down = D(inp["W_gu"]), D(inp["W_down"])
     W_r = D(inp["W_r"]) if topk else None
     bias = dev(inp["bias"], "f32x") if inp["bias"] is not None else None
@@ -249,17 +297,23 @@ def _layer_step(w, inp, flags=0, s_copy=None):
     return A, dict(dW_gu=dW_gu, dW_down=dW_down, dW_r=dW_r)
 
 
-@pytest.mark.parametrize("fused", [False, True], ids=["", "fused_permute"])
+CHAIN_FLAGS = {"": 0, "fused_permute": 1, "fused_combine_bwd": 2, "fused_both": 3}
+
+
+@pytest.mark.parametrize("variant", list(CHAIN_FLAGS))
 @pytest.mark.parametrize("name", ["tiny_f32", "fb_ragged_bf16", "zipf_window_bf16",
                                   "fb_k3_window_bf16", "many_experts_bf16", "mid_window_bf16", "max_router_bf16",
                                   "fb_ragged_f16", "zipf_window_f16"])
-def test_chain_parity(name, fused):
+def test_chain_parity(name, variant):
     w = SMALL[name]
-    log(f"[chain parity] {name}{' fused permute' if fused else ''}")
+    v = CHAIN_FLAGS[variant]
+    fused, fcb = bool(v & 1), bool(v & 2)
+    log(f"[chain parity] {name} {variant}")
     prec, tau = w.dtype, TAU[w.dtype]
     inp = make_inputs(w, seed=0)
     X, ref, refb = _oracle(w, inp, prec)
-    A, g = _layer_step(w, inp, M.MOE_STEP_FUSED_PERMUTE if fused else 0)
+    A, g = _layer_step(w, inp, (M.MOE_STEP_FUSED_PERMUTE if fused else 0) |
+                       (M.MOE_STEP_FUSED_COMBINE_BWD if fcb else 0))
     if w.route == "topk":
         close("logits", host(A.logits), ref["logits"], tau)
         gi = host(A.idx)
@@ -275,7 +329,9 @@ def test_chain_parity(name, fused):
     for k in ("h", "a", "yp"):
         close(k, host(getattr(A, k), N), ref[k], tau)
     close("out", host(A.out), ref["out"], tau)
-    for k in ("dyp", "dh", "dxp"):
+    if fcb:  # the fused combine backward: its own rounding points
+        refb = dict(refb, **_oracle_fused_bwd(w, X, ref, refb, prec))
+    for k in ("dh", "dxp") if fcb else ("dyp", "dh", "dxp"):
         close(k, host(getattr(A, k), N), refb[k], tau)
     close("dgates", host(A.dgates), refb["dgates"], tau)
     close("dx", host(A.dx), refb["dx"], tau)
@@ -662,6 +718,8 @@ def _pingpong_steps(s, mode, W, grads, ws, mbs, n, shared=None, W_r=None, bias=N
     ("fb_ragged_bf16", True, M.MOE_STEP_EAGER_WGRAD),
     ("mid_window_f16", False, M.MOE_STEP_MID_WGRAD),
     ("tiny_f32", True, M.MOE_STEP_MID_WGRAD),
+    ("zipf_window_bf16", False, M.MOE_STEP_MID_WGRAD | M.MOE_STEP_FUSED_COMBINE_BWD),
+    ("fb_ragged_bf16", True, M.MOE_STEP_FUSED_COMBINE_BWD | M.MOE_STEP_FUSED_PERMUTE),
 ])
 def test_multi_step_pipelined_equals_serialized(name, shared, flags):
     """moe_overlap_steps (streams alternating, steps overlapping) against the same
@@ -676,6 +734,7 @@ def test_multi_step_pipelined_equals_serialized(name, shared, flags):
     topk = w.route == "topk"
     mode = M.MOE_ROUTE_TOPK if topk else M.MOE_ROUTE_FORCE_BALANCE
     fused = bool(flags & M.MOE_STEP_FUSED_PERMUTE)
+    fcb = bool(flags & M.MOE_STEP_FUSED_COMBINE_BWD)
     Fs = 128 if shared else 0
     rng = np.random.default_rng(31)
     Wgu_s = D(O.store(0.05 * rng.standard_normal((2 * Fs, w.d)), prec)) if shared else None
@@ -688,7 +747,8 @@ def test_multi_step_pipelined_equals_serialized(name, shared, flags):
     res = {}
     for tag in ("serial", "pipelined"):
         mbs = [M.MicroBatch(s, x=D(inp[xk]), dout=D(inp[dk]),
-                            gates=None if topk else dev(inp[gk], "f32x"), fused=fused, F_s=Fs)
+                            gates=None if topk else dev(inp[gk], "f32x"), fused=fused, F_s=Fs,
+                            fused_bwd=fcb)
                for xk, dk, gk in (("x", "dout", "gates"), ("x_b", "dout_b", "gates_b"))]
         grads = (torch.full((w.E_l, 2 * w.F, w.d), float("nan"), device="cuda"),
                  torch.full((w.E_l, w.d, w.F), float("nan"), device="cuda"),
@@ -718,7 +778,7 @@ def test_multi_step_pipelined_equals_serialized(name, shared, flags):
             assert torch.equal(getattr(mb[i], k), getattr(ma[i], k)), (i, k)
         # dispatched-row buffers: rows past N are never written
         N = int(ma[i].offsets[w.E_l])
-        for k in ("yp", "dh", "a", "dyp", "dxp"):
+        for k in ("yp", "dh", "a", "dxp") + (("ag",) if fcb else ("dyp",)):
             assert torch.equal(getattr(mb[i], k)[:N], getattr(ma[i], k)[:N]), (i, k)
     for k, (a, b) in enumerate(zip(ga, gb)):
         if a is not None:

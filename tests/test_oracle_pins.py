@@ -539,3 +539,33 @@ def test_bf16_oracle_within_tolerance_of_f64_oracle():
     if same.all():
         for k in ("dx", "dW_gu", "dW_down", "dW_r"):
             assert np.all(np.abs(g16[k] - g64[k]) <= tol(g64[k])), k
+
+
+def test_fused_combine_backward_reading_equals_the_plain_definition():
+    """The fused combine backward feeds the expert dgrad with g * dout rows
+    gathered through pair_of_row and the wgrad with dout rows and ag = g * a.
+    In exact (float64) arithmetic both are the plain definition: dgrad of the
+    combine backward's dy_p, and dW_down = dy_p^T a."""
+    rng = np.random.default_rng(23)
+    T, d, F, E, K = 40, 16, 8, 4, 2
+    x = rng.standard_normal((T, d))
+    W_r = 0.3 * rng.standard_normal((d, E))
+    W_gu = 0.3 * rng.standard_normal((E, 2 * F, d))
+    W_down = 0.3 * rng.standard_normal((E, d, F))
+    dout = rng.standard_normal((T, d))
+    f = O.layer_forward(x, K, 0, E, W_gu, W_down, W_r=W_r, tile_m=8, prec="f64")
+    N = f["N"]
+    dyp, _ = O.combine_bwd(dout, f["yp"], f["gates"], f["row_of_pair"], N, prec="f64")
+    pr = f["pair_of_row"][:N]
+    g = f["gates"].reshape(-1)[pr][:, None]
+    rows = dout[pr // K]
+    dh1, dxp1 = O.ffn_dgrad(dyp, f["h"], f["offsets"], W_gu, W_down, prec="f64")
+    dh2, dxp2 = O.ffn_dgrad(g * rows, f["h"], f["offsets"], W_gu, W_down, prec="f64")
+    np.testing.assert_allclose(dh2, dh1, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dxp2, dxp1, rtol=1e-12, atol=1e-12)
+    hg, hu = f["h"][:, :F], f["h"][:, F:]
+    ag = g * (hg / (1.0 + np.exp(-hg))) * hu
+    np.testing.assert_allclose(ag, g * f["a"], rtol=1e-12, atol=1e-12)   # a = silu(g) u
+    _, dn1 = O.ffn_wgrad(f["xp"], f["a"], dh1, dyp, f["offsets"], prec="f64")
+    _, dn2 = O.ffn_wgrad(f["xp"], ag, dh1, rows, f["offsets"], prec="f64")
+    np.testing.assert_allclose(dn2, dn1, rtol=1e-12, atol=1e-12)
