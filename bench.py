@@ -390,6 +390,10 @@ def main():
     ap.add_argument("--profile-cmd", action="append", default=[],
                     help="the command(s) that made the --inputs, quoted in the summary")
     ap.add_argument("--out", default=None, help="summary file (default profiles/<kind>_<wl>.md)")
+    ap.add_argument("--n-rows", type=int, default=None,
+                    help="--summarize with a local expert window: the rows dispatched to it")
+    ap.add_argument("--t-loc", type=int, default=None,
+                    help="--summarize with a local expert window: tokens with a local expert")
     args = ap.parse_args()
 
     if args.summarize:
@@ -440,6 +444,7 @@ def main():
     counts = L.mbs[0].counts.cpu()
     N = int(counts.sum())
     T_loc = int((L.mbs[0].row_of_pair >= 0).any(dim=1).sum())
+    err(f"[bench] dispatched rows N = {N}, tokens with a local expert T_loc = {T_loc}")
 
     if args.serialized_only:
         L.issue(args.warmup + args.steps, SER)
@@ -636,7 +641,8 @@ def main():
 # rocprofv3 output -> profiles/ summaries (no GPU needed)
 # ---------------------------------------------------------------------------
 # kernel symbol -> the name the library times it under (MOE_LAUNCH); wgrad_kernel
-# is split by its ROUTER template argument (the router weight gradient reuses it)
+# is split by its ROUTER template argument (the third: the router weight
+# gradient reuses the kernel)
 _CLASS = [("GateUpOp", "ffn_gate_up"), ("DownOp", "ffn_down"), ("DgradActOp", "dgrad_act"),
           ("DgradInOp", "dgrad_in"), ("combine_bwd_kernel", "combine_bwd"),
           ("dispatch_bwd_kernel", "dispatch_bwd"), ("combine_kernel", "combine"),
@@ -671,7 +677,8 @@ def bench_name(sym):
                 cur += ch
             j += 1
         args.append(cur.strip())
-        return "dwr_mfma" if args and args[-1] == "true" else "wgrad"
+        # wgrad_kernel<GATHER, element type, ROUTER, ACC, GD>
+        return "dwr_mfma" if len(args) > 2 and args[2] == "true" else "wgrad"
     for k, v in _CLASS:
         if k in sym:
             return v
@@ -711,8 +718,9 @@ def _workload_for_summary(args):
     w = WORKLOADS[args.workload]
     if args.tokens:
         w = w.with_tokens(args.tokens)
-    # every expert local (the default workload): N = T*K rows, all T tokens
-    N, T_loc = (w.T * w.K, w.T) if w.E_l == w.E else (None, None)
+    # every expert local: N = T*K rows, all T tokens; a window: as given
+    # (the bench line's config.N_rows and the tokens with a local expert)
+    N, T_loc = (w.T * w.K, w.T) if w.E_l == w.E else (args.n_rows, args.t_loc)
     return w, N, T_loc
 
 
