@@ -507,7 +507,7 @@ struct GateUpOp {
           ld8(blk + r * EP_LD + (w.lane & 3) * 8, g);
           ld8(blk + r * EP_LD + 32 + (w.lane & 3) * 8, u);
 #pragma unroll
-          for (int t = 0; t < 8; ++t) av[t] = silu_f(g[t]) * u[t];
+          for (int t = 0; t < 8; ++t) av[t] = silu_fast(g[t]) * u[t];
           if (col_ok && rb + r < m_end) {
             const size_t row = (size_t)(rb + r);
             *(uint4*)(h + row * 2 * F + j0) = Chunk<typename E::elt>::pack(g);
@@ -639,7 +639,7 @@ struct DgradActOp {
           Chunk<typename E::elt>::unpack(uv[q], u);
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
-            const float sg = sigmoid_f(g[t]);
+            const float sg = sigmoid_fast(g[t]);
             const float dat = FUSED ? da[t] * gr[q] : da[t];
             dg[t] = dat * u[t] * sg * (1.0f + g[t] * (1.0f - sg));
             du[t] = dat * g[t] * sg;

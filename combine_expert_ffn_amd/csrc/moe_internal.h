@@ -15,15 +15,15 @@ namespace moe {
 __device__ __forceinline__ float bf2f(uint16_t v) {
   return __uint_as_float(((uint32_t)v) << 16);
 }
-// float32 -> bfloat16, round to nearest even (NaN stays a quiet NaN).
+// float32 -> bfloat16, round to nearest even (NaN stays a NaN): gfx950's
+// v_cvt_pk_bf16_f32, two values per instruction.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <typename T> struct Elt;
@@ -99,6 +99,15 @@ template <> struct Chunk<float> {
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 __device__ __forceinline__ float sigmoid_f(float g) { return 1.0f / (1.0f + expf(-g)); }
+// The same for the 16-bit matrix-core epilogues, whose results are rounded to
+// bf16 / fp16 (8 / 11 significant bits) right away: exp2 and reciprocal on the
+// transcendental unit (v_exp_f32, v_rcp_f32, about 1 ulp each), five
+// instructions instead of a correctly rounded expf and an IEEE division.
+// Limits as above: sigmoid -> 0 and silu -> -0 for g -> -inf.
+__device__ __forceinline__ float sigmoid_fast(float g) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+}
+__device__ __forceinline__ float silu_fast(float g) { return g * sigmoid_fast(g); }
 
 // Wave-wide float sum (wave64).
 __device__ __forceinline__ float wave_sum(float v) {
