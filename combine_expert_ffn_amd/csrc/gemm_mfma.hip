@@ -590,10 +590,12 @@ struct DgradActOp {
               tid);
     lb.init(WdT, [&](int n) { return min(nb + n, F - 1) * d; }, tid);
   }
-  // The h chunks of this lane's rows are loaded (16 bytes each, rows clamped
-  // to valid ones) before the block is staged, so their latency overlaps the
-  // staging.  FUSED: the gates of all the lane's rows are loaded first, the
-  // pair indices of the rows together and then the gates together, so the
+  // The h chunks of this lane's rows (16 bytes each, rows clamped to valid
+  // ones) are loaded one row block ahead: block 0's before the first block
+  // is staged, and block i + 1's pass q into the registers that block i's
+  // pass q has just consumed, so each load has a block's work to arrive.
+  // FUSED: the gates of all the lane's rows are loaded first, the pair
+  // indices of the rows together and then the gates together, so the
   // dependent loads cost two memory waits per tile.
   template <class TL>
   __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TL::TM][TL::TN], int e, int m0,
@@ -617,18 +619,18 @@ struct DgradActOp {
     for (int p = 0; p < TL::TN / 2; ++p) {
       const int cb = nt * TL::BN + w.wn * TL::WTN + p * 64;
       if (cb >= F) continue;  // F is a multiple of 64; wave-uniform
+      const int rb0 = m0 + w.wm * TL::WTM;
+      uint4 gv[4], uv[4];
+      auto load_h = [&](int i, int q) {
+        const size_t rowc = (size_t)min(rb0 + i * 32 + st_row(q, w.lane), m_end - 1);
+        gv[q] = *(const uint4*)(hbuf + rowc * 2 * F + cb + c);
+        uv[q] = *(const uint4*)(hbuf + rowc * 2 * F + F + cb + c);
+      };
+#pragma unroll
+      for (int q = 0; q < 4; ++q) load_h(0, q);
 #pragma unroll
       for (int i = 0; i < TL::TM; ++i) {
-        const int rb = m0 + w.wm * TL::WTM + i * 32;
-        uint4 gv[4], uv[4];
-        float gr[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const size_t rowc = (size_t)min(rb + st_row(q, w.lane), m_end - 1);
-          gv[q] = *(const uint4*)(hbuf + rowc * 2 * F + cb + c);
-          uv[q] = *(const uint4*)(hbuf + rowc * 2 * F + F + cb + c);
-          if constexpr (FUSED) gr[q] = grow[i][q];
-        }
+        const int rb = rb0 + i * 32;
         const float* blk = stage_rows<TL>(acc, i, p, smem, w.wave, w.lane);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -637,13 +639,15 @@ struct DgradActOp {
           ld8(blk + r * EP_LD + c, da);
           Chunk<typename E::elt>::unpack(gv[q], g);
           Chunk<typename E::elt>::unpack(uv[q], u);
+          if (i + 1 < TL::TM) load_h(i + 1, q);
+          const float gr = FUSED ? grow[FUSED ? i : 0][q] : 1.0f;  // the row's gate
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
             const float sg = sigmoid_fast(g[t]);
-            const float dat = FUSED ? da[t] * gr[q] : da[t];
+            const float dat = FUSED ? da[t] * gr : da[t];
             dg[t] = dat * u[t] * sg * (1.0f + g[t] * (1.0f - sg));
             du[t] = dat * g[t] * sg;
-            if constexpr (FUSED) av[t] = gr[q] * (g[t] * sg) * u[t];
+            if constexpr (FUSED) av[t] = gr * (g[t] * sg) * u[t];
           }
           if (rb + r < m_end) {
             const size_t row = (size_t)(rb + r);
