@@ -205,14 +205,100 @@ __device__ __forceinline__ void read_frags(Frags<TL>& f, const uint16_t* A, cons
     f.a[i] = *(const bf16x8_t*)(A + lds_off(wm * TL::WTM + i * 32 + fr, ch));
 }
 
-template <class TL, class E>
+template <class TL, class E, bool NSIDE = false>
 __device__ __forceinline__ void mfmas(const Frags<TL>& f, f32x16_t (&acc)[TL::TM][TL::TN]) {
 #pragma unroll
   for (int i = 0; i < TL::TM; ++i)
 #pragma unroll
     for (int j = 0; j < TL::TN; ++j)
-      acc[i][j] = E::mfma(f.a[i], f.b[j], acc[i][j]);
+      acc[i][j] = NSIDE ? E::mfma(f.b[j], f.a[i], acc[i][j]) : E::mfma(f.a[i], f.b[j], acc[i][j]);
 }
+
+// Stage tiles in natural [64 k][256 col] layout (the wgrad operands, which
+// are contiguous along M/N while the reduction runs over rows): the MFMA
+// operands, 8 consecutive k of one column per lane, are assembled from two
+// LDS transpose reads (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane s addresses row k0 + s/4 at columns c0 + 4*(s%4), and lane t receives
+// rows k0..k0+3 of column c0 + t.
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+constexpr int WG_ROWB = 256 * 2;  // bytes per natural-layout tile row (256 columns)
+
+// Physical 32-byte chunk of logical chunk c in tile row k: rows k..k+3 of a
+// transpose read land in distinct bank groups.
+__device__ __forceinline__ int wg_swz(int k) { return ((k & 3) << 1) | ((k >> 2) & 1); }
+__device__ __forceinline__ int wg_byte(int k, int col) {
+  return k * WG_ROWB + ((((col >> 4) ^ wg_swz(k)) & 15) << 5) + ((col & 15) << 1);
+}
+
+// Fragment readers of the main loop.  RowFrags: tiles [rows][64 k] (operands
+// contiguous along K), one 16-byte LDS read per MFMA operand.
+struct RowFrags {
+  static constexpr int READS = 1;       // LDS read instructions per fragment
+  static constexpr bool NSIDE = false;  // the MFMA takes the M-side fragment first
+  template <class TL>
+  __device__ __forceinline__ void read(Frags<TL>& f, const uint16_t* A, const uint16_t* B, int kk,
+                                       int wm, int wn, int lane) const {
+    read_frags<TL>(f, A, B, kk, wm, wn, lane);
+  }
+};
+// TrFrags: natural-layout tiles read by transpose.  With g = lane / 16 and
+// t = lane % 16, half h of the operand for columns [cb, cb + 32) (cb a
+// multiple of 32) reads tile row kr = 8 (g / 2) + t / 4 + 4h at physical
+// 32-byte chunk ((cb / 16 + g % 2) ^ wg_swz(kr)) and byte 8 (t % 4) in it;
+// wg_swz(kr) = 2 (t / 4) + h is below 8 and cb / 16 is even, so the chunk is
+// (cb / 16) ^ u_h with the per-lane u_h = (g % 2) ^ wg_swz(kr): each read
+// costs one XOR of a block-uniform value with u_h and one shift-add onto the
+// per-lane row base.  With HOIST the twelve resulting addresses are left to
+// the compiler, which keeps them in registers across the main loop (fewer
+// instructions per slice); without, they are formed at each read, which needs
+// twelve registers fewer.  The MFMA takes the N-side fragment first, so a
+// block of four accumulator registers holds four consecutive columns of one
+// output row.
+template <class TL, bool HOIST>
+struct TrFrags {
+  static constexpr int READS = 2;
+  static constexpr bool NSIDE = true;
+  int rb[2], u[2];  // per half: row byte base + 8 (t % 4), chunk XOR term
+  int wm, wn;
+  __device__ __forceinline__ void init(int wm_, int wn_, int lane) {
+    wm = wm_;
+    wn = wn_;
+    const int g = lane >> 4, t = lane & 15;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kr = ((g >> 1) << 3) + (t >> 2) + 4 * h;
+      rb[h] = kr * WG_ROWB + ((t & 3) << 3);
+      u[h] = (g & 1) ^ wg_swz(kr);
+    }
+  }
+  __device__ __forceinline__ static bf16x8_t frag(const uint16_t* tile, int cb, int kk,
+                                                  const int (&rb)[2], const int (&u)[2]) {
+    const uint8_t* t8 = (const uint8_t*)tile + kk * 16 * WG_ROWB;
+    const int c16 = cb >> 4;  // block-uniform
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4_t*)(t8 + rb[0] + ((c16 ^ u[0]) << 5)));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4_t*)(t8 + rb[1] + ((c16 ^ u[1]) << 5)));
+    const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+  }
+  template <class>
+  __device__ __forceinline__ void read(Frags<TL>& f, const uint16_t* A, const uint16_t* B, int kk,
+                                       int, int, int) const {
+    // without HOIST the per-lane terms pass through an empty asm, so the
+    // addresses cannot be hoisted out of the main loop
+    int r[2] = {rb[0], rb[1]}, x[2] = {u[0], u[1]};
+    if constexpr (!HOIST) asm volatile("" : "+v"(r[0]), "+v"(r[1]), "+v"(x[0]), "+v"(x[1]));
+#pragma unroll
+    for (int j = 0; j < TL::TN; ++j) f.b[j] = frag(B, wn * TL::WTN + j * 32, kk, r, x);
+#pragma unroll
+    for (int i = 0; i < TL::TM; ++i) f.a[i] = frag(A, wm * TL::WTM + i * 32, kk, r, x);
+  }
+};
 
 // Wave position inside the block tile.  The wave index is moved to a scalar
 // register and the lane index is recomputed where it is needed (from the exec
@@ -270,9 +356,10 @@ __device__ __forceinline__ void store_load(LA& la, LB& lb, uint16_t* An, uint16_
   }
 }
 
-template <class TL, class E, class LA, class LB, bool SCHED = true>
+template <class TL, class E, class LA, class LB, bool SCHED = true, class FR = RowFrags>
 __device__ __forceinline__ void mainloop_steps(LA& la, LB& lb, int k_begin, int nk,
-                                               uint16_t* smem, f32x16_t (&acc)[TL::TM][TL::TN]) {
+                                               uint16_t* smem, f32x16_t (&acc)[TL::TM][TL::TN],
+                                               const FR& fr = FR{}) {
   uint16_t* const sA0 = smem;
   uint16_t* const sA1 = smem + TL::BM * BK;
   uint16_t* const sB0 = smem + 2 * TL::BM * BK;
@@ -285,11 +372,11 @@ __device__ __forceinline__ void mainloop_steps(LA& la, LB& lb, int k_begin, int 
     for (int j = 0; j < TL::TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  constexpr int NM = TL::TM * TL::TN, NR = TL::TM + TL::TN;
+  constexpr int NM = TL::TM * TL::TN, NR = (TL::TM + TL::TN) * FR::READS;
   constexpr int NQ = LA::CH + LB::CH;  // chunks per stage, spread over slices 0..2
   constexpr int Q1 = NQ / 3, Q2 = 2 * NQ / 3;
   Frags<TL> f0, f1;
-  read_frags<TL>(f0, sA0, sB0, 0, wm, wn, lane);
+  fr.template read<TL>(f0, sA0, sB0, 0, wm, wn, lane);
   for (int kt = 0; kt < nk; ++kt) {
     const bool odd = kt & 1;
     const uint16_t* A = odd ? sA1 : sA0;
@@ -299,28 +386,28 @@ __device__ __forceinline__ void mainloop_steps(LA& la, LB& lb, int k_begin, int 
     const int kn2 = k_begin + (kt + 2 < nk ? kt + 2 : nk - 1) * BK;
     // slice 0; the other buffer's last readers passed the previous barrier,
     // so the stage in registers can go to it from here on
-    read_frags<TL>(f1, A, B, 1, wm, wn, lane);
-    mfmas<TL, E>(f0, acc);
+    fr.template read<TL>(f1, A, B, 1, wm, wn, lane);
+    mfmas<TL, E, FR::NSIDE>(f0, acc);
     store_load<0, Q1>(la, lb, An, Bn, kn2);
     if constexpr (SCHED) sched_slice_wv<NM, NR, Q1, Q1>();
     __builtin_amdgcn_sched_barrier(0);
     // slice 1
-    read_frags<TL>(f0, A, B, 2, wm, wn, lane);
-    mfmas<TL, E>(f1, acc);
+    fr.template read<TL>(f0, A, B, 2, wm, wn, lane);
+    mfmas<TL, E, FR::NSIDE>(f1, acc);
     store_load<Q1, Q2>(la, lb, An, Bn, kn2);
     if constexpr (SCHED) sched_slice_wv<NM, NR, Q2 - Q1, Q2 - Q1>();
     __builtin_amdgcn_sched_barrier(0);
     // slice 2
-    read_frags<TL>(f1, A, B, 3, wm, wn, lane);
-    mfmas<TL, E>(f0, acc);
+    fr.template read<TL>(f1, A, B, 3, wm, wn, lane);
+    mfmas<TL, E, FR::NSIDE>(f0, acc);
     store_load<Q2, NQ>(la, lb, An, Bn, kn2);
     if constexpr (SCHED) sched_slice_wv<NM, NR, NQ - Q2, NQ - Q2>();
     __builtin_amdgcn_sched_barrier(0);
     // the next stage is complete once every wave passes the barrier; its
     // first fragments are read while the last slice's MFMAs run
     __syncthreads();
-    read_frags<TL>(f0, An, Bn, 0, wm, wn, lane);
-    mfmas<TL, E>(f1, acc);
+    fr.template read<TL>(f0, An, Bn, 0, wm, wn, lane);
+    mfmas<TL, E, FR::NSIDE>(f1, acc);
     if constexpr (SCHED) sched_slice_wv<NM, NR, 0, 0>();
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -703,81 +790,100 @@ struct DgradInOp {
 // wgrad: per local expert e over its rows [offsets[e], offsets[e+1]):
 //   dW_down[e] (d x F)  = dy_p^T . a      (A: dy_p, M = d;  B: a,  N = F)
 //   dW_gu[e]   (2F x d) = dh^T   . xp     (A: dh,   M = 2F; B: xp, N = d)
-// Both operands are contiguous along M/N (the reduction runs over rows), so
-// each 64-row stage is copied straight into LDS in its natural [k][col]
-// layout (16-byte global loads, one 1 KiB LDS block per wave instruction)
-// and the MFMA operands, 8 consecutive k of one column per lane, are
-// assembled from two LDS transpose reads (ds_read_b64_tr_b16): within each
-// group of 16 lanes, lane s addresses row k0 + s/4 at columns c0 + 4*(s%4),
-// and lane t receives rows k0..k0+3 of column c0 + t.  Rows past the expert's
-// end and columns past the matrix read a zero row instead, so no masking is
-// needed.  One launch covers both products of every expert.
+// Both operands are contiguous along M/N (the reduction runs over rows), so a
+// 64-row stage is copied with 16-byte row-contiguous loads into a natural
+// [k][col] LDS tile and read back by transpose (TrFrags).  One launch covers
+// both products of every expert.
 // ---------------------------------------------------------------------------
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef short i16x8_t __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-__device__ uint16_t g_zero_row[256];  // zero-initialised device memory
+// Loader of one wgrad operand: a stage is the [64 k][256 col] tile at rows
+// [k0, k0 + 64) of the expert's rows, columns [m0, m0 + 256).  Thread t's
+// chunk c is tile row c * 16 + t / 32, columns m0 + 8 (t % 32)..+7, so a wave
+// instruction reads two 512-byte row pieces; it is stored to the LDS tile at
+// the position frag_at expects.  A direct operand is read through a buffer
+// resource rebuilt per stage over rows [k0, rows) of the expert (offsets stay
+// small, whatever the operand's size), so rows past the expert's end read as
+// zero; columns past M, only in a tile that crosses M, read the next row's
+// values and only reach outputs the epilogue does not store.  A gathered
+// operand's row k is token rows_of[r0 + k] / K of the token matrix; each
+// chunk's token is loaded one stage ahead (when the chunk is loaded for the
+// stage before), and a row past the expert's end gets an offset past the
+// resource, which reads as zero.
+template <bool CAN_GATHER, int NT = 512>
+struct WgLoad {
+  static constexpr int CH = 64 * 32 / NT;  // 16-byte chunks per thread and stage
+  static constexpr int NLOAD = CH, NSTORE = CH;
+  u32x4_t v[CH];  // the stage in flight
+  __amdgpu_buffer_rsrc_t rsrc;
+  const uint16_t* base;  // direct: the expert's first row; gathered: the token matrix
+  long ld;               // elements per operand row
+  int rows;              // rows of the expert
+  uint32_t voff;         // byte offset of chunk 0 within a stage (direct) / a row (gathered)
+  int dst0;              // byte offset of chunk 0 in an LDS tile
+  bool gat;
+  const int32_t* rows_of;
+  int r0, K, trow;
+  int tok_next[CH];  // rows_of value of each chunk's row in the next stage loaded (-1: none)
 
-constexpr int WG_ROWB = 256 * 2;  // bytes per LDS tile row (256 columns)
-
-// Physical 32-byte chunk of logical chunk c in tile row k: rows k..k+3 of a
-// transpose read land in distinct bank groups.
-__device__ __forceinline__ int wg_swz(int k) { return ((k & 3) << 1) | ((k >> 2) & 1); }
-__device__ __forceinline__ int wg_byte(int k, int col) {
-  return k * WG_ROWB + ((((col >> 4) ^ wg_swz(k)) & 15) << 5) + ((col & 15) << 1);
-}
-
-// Direct global -> LDS loader of a [64 k][256 col] tile (16 bytes per lane;
-// a wave instruction fills one contiguous 1 KiB block of LDS, addressed by m0).
-// With tok set (an LDS array of the stage's 64 source rows, -1 past the
-// expert's end), k-row kr of the stage is read from row tok[kr] of base: the
-// gathered operand of the fused permute.
-template <int NW>
-struct LoadKM {
-  static constexpr int PER = BK / 2 / NW;  // wave instructions per stage
-  const uint16_t* base;
-  long ld;
-  int M, m0, lane, w;
-  template <bool TOK = false>
-  __device__ __forceinline__ void issue(uint8_t* lds, int k0, int k_end,
-                                        const int* tok = nullptr) const {
+  __device__ __forceinline__ void init(const uint16_t* src, long ld_, int m0, int r0_, int r1,
+                                       bool gathered, const int32_t* xrows, int K_, int tid) {
+    ld = ld_;
+    rows = r1 - r0_;
+    trow = tid >> 5;
+    const uint32_t coff = (uint32_t)(m0 + 8 * (tid & 31)) * 2u;
+    dst0 = wg_byte(trow, 8 * (tid & 31));
+    gat = CAN_GATHER && gathered;
+    if (CAN_GATHER && gat) {
+      base = src;
+      voff = coff;
+      rows_of = xrows;
+      r0 = r0_;
+      K = K_;
+      // every token is a row of the matrix; only the past-the-end marker
+      // exceeds the records limit
+      rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, 0x7fffffff, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int blk = i * NW + w;
-      const int kr = blk * 2 + (lane >> 5);
-      const int s = lane & 31;
-      const int col = (((s >> 1) ^ wg_swz(kr)) & 15) * 16 + (s & 1) * 8;
-      const int k = TOK ? tok[kr] : k0 + kr;
-      const bool ok = (TOK ? k >= 0 : k < k_end) && (m0 + col < M);
-      const uint16_t* src = ok ? base + (long)k * ld + m0 + col : g_zero_row + col;
-      // Issued by inline assembly: with the builtin the compiler treats these
-      // LDS writes as possibly aliasing every later LDS read and waits for the
-      // next stage's loads before reading the current stage, which serialises
-      // the prefetch.  Completion is awaited explicitly (vmcnt) before the
-      // barrier that publishes the stage.
-      const uint32_t m0v =
-          __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)(lds + blk * 1024));
-      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                   :
-                   : "v"(src), "s"(m0v)
-                   : "memory", "m0");
+      for (int c = 0; c < CH; ++c) tok_next[c] = token(0, c);
+    } else {
+      base = src + (size_t)r0_ * ld_;
+      voff = (uint32_t)trow * (uint32_t)(ld_ * 2) + coff;
     }
   }
+  // rows_of value of chunk c's row in stage k0 (-1 past the expert's end)
+  __device__ __forceinline__ int token(int k0, int c) const {
+    const int k = k0 + c * 16 + trow;
+    return k < rows ? rows_of[r0 + k] : -1;
+  }
+  __device__ __forceinline__ void load_c(int c, int k0) {
+    if (CAN_GATHER && gat) {
+      const int t = tok_next[c];
+      tok_next[c] = token(k0 + 64, c);
+      const uint32_t off =
+          t >= 0 ? (uint32_t)((unsigned)t / (unsigned)K) * (uint32_t)(ld * 2) + voff : 0x80000000u;
+      v[c] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off, 0, 0);
+    } else {
+      if (c == 0) {
+        const long left = (long)(rows - k0) * ld * 2;
+        const int nrec = left <= 0 ? 0 : (left > 0x7fffffffL ? 0x7fffffff : (int)left);
+        rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)k0 * ld), (short)0, nrec,
+                                                 0x00020000);
+      }
+      v[c] = __builtin_amdgcn_raw_buffer_load_b128(
+          rsrc, (int)(voff + (uint32_t)(c * 16) * (uint32_t)(ld * 2)), 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store_c(int c, uint16_t* lds) const {
+    *(u32x4_t*)((uint8_t*)lds + dst0 + c * 16 * WG_ROWB) = v[c];
+  }
+  __device__ __forceinline__ void load(int k0, int /*k_end*/) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) load_c(c, k0);
+  }
+  __device__ __forceinline__ void store(uint16_t* lds) const {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) store_c(c, lds);
+  }
 };
-
-// MFMA 32x32x16 operand for tile columns [cb, cb + 32) and k slice kk.
-__device__ __forceinline__ bf16x8_t frag_tr(const uint8_t* lds, int cb, int kk, int lane) {
-  const int g = lane >> 4, t = lane & 15;
-  const int col = cb + ((g & 1) << 4) + ((t & 3) << 2);
-  const int kr = kk * 16 + ((g >> 1) << 3) + (t >> 2);
-  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lds + wg_byte(kr, col)));
-  const i16x4_t hi =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lds + wg_byte(kr + 4, col)));
-  const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8_t, v);
-}
 
 // A wave-uniform 64-bit value moved to scalar registers.
 __device__ __forceinline__ long long uniform64(long long v) {
@@ -786,12 +892,15 @@ __device__ __forceinline__ long long uniform64(long long v) {
   return (long long)(((unsigned long long)hi << 32) | lo);
 }
 
-// 256 x 256 output tiles, 8 waves (2 x 4), wave tile 128 x 64.
+// 256 x 256 output tiles, 8 waves (2 x 4), wave tile 128 x 64, on the main
+// loop of the row-grouped GEMMs (two LDS stages of 64 rows, the stage after
+// next in registers; see mainloop_steps) with transposed fragment reads.
+// Tiles are software-pipelined across the persistent loop like the
+// row-grouped GEMMs': the next tile's first stage is loaded before this
+// tile's epilogue issues its stores.
 //
 // With xrows set (the fused permute), xp is the token matrix x [T][d] and the
-// dW_gu tiles read dispatched row r from token xrows[r] / K: the token rows of
-// stage k are looked up one stage ahead into an LDS list (s_tok, double
-// buffered), from which the next stage's loads take their addresses.
+// dW_gu tiles read dispatched row r from token xrows[r] / K.
 //
 // ROUTER reuses the kernel for the router weight gradient: the "experts" are
 // chunks of rchunk tokens (chunk c = rows [c rchunk, min((c+1) rchunk, rows))),
@@ -800,8 +909,8 @@ __device__ __forceinline__ long long uniform64(long long v) {
 // chunk; offsets, xp, dh and dW_gu are unused.
 // GD (the fused combine backward): dy_p is not materialised; dyp is the token
 // matrix dout [T][d], the dW_down tiles read dispatched row r of their A
-// operand from token xrows[r] / K through the same LDS token list, and abuf
-// holds ag = gate . a, so dW_down[e] = sum_r dout[t_r] (outer) ag[r].
+// operand from token xrows[r] / K in the same way, and abuf holds
+// ag = gate . a, so dW_down[e] = sum_r dout[t_r] (outer) ag[r].
 //
 // ACC: add into the existing values of dW (gradient accumulation) instead of
 // overwriting them.
@@ -812,22 +921,22 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
     const uint16_t* __restrict__ dyp, const int32_t* __restrict__ offsets,
     float* __restrict__ dW_gu, float* __restrict__ dW_down, int E_l, int d, int F,
     int rchunk = 0, int rows = 0) {
-  constexpr int NW = 8, WGN = 4, WTM = 128, WTN = 64, TM = 4, TN = 2;
-  constexpr int STAGE = 2 * BK * WG_ROWB;  // A + B tiles
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
-  __shared__ long long s_it[257];  // first k-step of each expert's tiles; s_it[E_l] = W
-  __shared__ int s_tok[(GATHER || GD) ? 2 : 1][BK];  // source token rows of the next two stages
+  using TL = T256;
+  constexpr int WTM = TL::WTM, WTN = TL::WTN, TM = TL::TM, TN = TL::TN;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[TL::LDS_ELEMS];
+  __shared__ long long s_it[257];  // first cost unit of each expert's tiles; s_it[E_l] = W
   const int tdm = (d + 255) / 256, tdn = (F + 255) / 256;
   const int tgm = (2 * F + 255) / 256, tgn = (d + 255) / 256;
   const int per_e = tdm * tdn + (ROUTER ? 0 : tgm * tgn);
   // first row of expert (or token chunk) e
   auto off = [&](int e) { return ROUTER ? min(e * rchunk, rows) : offsets[e]; };
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WGN, wn = wave % WGN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w / TL::WGN, wn = w % TL::WGN;
   // Work-balanced schedule: a tile costs nk_e = max(1, ceil(rows_e / 64))
-  // k-steps (experts' row counts differ) and the W steps of all tiles are laid
+  // units (experts' row counts differ) and the W units of all tiles are laid
   // out tile-major.  XCD g (the hardware places block b on XCD b % 8) takes
-  // the tiles whose first step falls in [W*g/8, W*(g+1)/8), so the XCDs get
+  // the tiles whose first unit falls in [W*g/8, W*(g+1)/8), so the XCDs get
   // equal work, and its blocks take those tiles round robin, so the tiles
   // running together share operand rows in the XCD's L2.
   if (tid == 0) {
@@ -860,7 +969,7 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
   // Tile gt of the expert-major order: its expert, operands, output and
   // k-steps; valid = false once the group's range of work is done.
   struct TileJob {
-    bool valid, gat, ga, gb;  // gathers a token-indexed operand: A (dW_down), B (dW_gu)
+    bool valid, ga, gb;  // gathers a token-indexed operand: A (dW_down), B (dW_gu)
     int r0, r1, M, N, m0, n0, nk;
     const uint16_t *Asrc, *Bsrc;
     float* out;
@@ -902,176 +1011,162 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
       j.n0 = (t % tgn) * 256;
       j.out = dW_gu + (size_t)e * 2 * F * d;
     }
-    j.gat = j.ga || j.gb;
     return j;
   };
-  // source token of dispatched row r of tile job c (-1 past the expert's end)
-  auto token = [&](const TileJob& c, int r) { return r < c.r1 ? xrows[r] / K : -1; };
-  // Stage 0 of a tile into LDS buffer 0.  A tile that does not gather has it
-  // issued early, right after the previous tile's main loop (the LDS is free
-  // then), so that its loads are in flight during that tile's epilogue.
-  auto issue_stage0 = [&](const TileJob& c) {
-    const LoadKM<NW> la{c.Asrc, (long)c.M, c.M, c.m0, lane, wave};
-    const LoadKM<NW> lb{c.Bsrc, (long)c.N, c.N, c.n0, lane, wave};
-    if (GD && c.ga)
-      la.template issue<true>(smem, c.r0, c.r1, s_tok[0]);
-    else
-      la.issue(smem, c.r0, c.r1);
-    if (GATHER && c.gb)
-      lb.template issue<true>(smem + BK * WG_ROWB, c.r0, c.r1, s_tok[0]);
-    else
-      lb.issue(smem + BK * WG_ROWB, c.r0, c.r1);
+  // the gathering variants hold token registers: addresses formed per read
+  using FR = TrFrags<TL, !(GATHER || GD)>;
+  FR fr;
+  fr.init(wm, wn, lane);
+  WgLoad<GD> la;
+  WgLoad<GATHER> lb;
+  auto init_loaders = [&](const TileJob& c) {
+    la.init(c.Asrc, c.M, c.m0, c.r0, c.r1, c.ga, xrows, K, tid);
+    lb.init(c.Bsrc, c.N, c.n0, c.r0, c.r1, c.gb, xrows, K, tid);
   };
-  TileJob cur = job(gt0 + slot);
   long long gt = gt0 + slot;
-  bool pre = cur.valid && cur.nk > 0 && !((GATHER || GD) && cur.gat);
-  if (pre) issue_stage0(cur);
-  while (cur.valid) {
-    const LoadKM<NW> la{cur.Asrc, (long)cur.M, cur.M, cur.m0, lane, wave};
-    const LoadKM<NW> lb{cur.Bsrc, (long)cur.N, cur.N, cur.n0, lane, wave};
-    const int r0 = cur.r0, r1 = cur.r1, nk = cur.nk;
+  TileJob cur = job(gt);
+  if (!cur.valid) return;  // block-uniform
+  init_loaders(cur);
+  la.load(0, 0);
+  lb.load(0, 0);
+  for (;;) {
+    const int nk = cur.nk;
+    la.store(smem);
+    lb.store(smem + 2 * TL::BM * BK);
+    la.load(nk > 1 ? BK : 0, 0);
+    lb.load(nk > 1 ? BK : 0, 0);
+    __syncthreads();
     f32x16_t acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    if (nk > 0) {  // block-uniform
-      if (!pre) {
-        if constexpr (GATHER || GD) {
-          if (cur.gat) {
-            if (tid < BK) {
-              s_tok[0][tid] = token(cur, r0 + tid);
-              s_tok[1][tid] = token(cur, r0 + BK + tid);
-            }
-            __syncthreads();
-          }
-        }
-        issue_stage0(cur);
-      }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      for (int kt = 0; kt < nk; ++kt) {
-        uint8_t* cur_s = smem + (kt & 1) * STAGE;
-        uint8_t* nxt_s = smem + ((kt + 1) & 1) * STAGE;
-        if (kt + 1 < nk) {
-          if (GD && cur.ga)
-            la.template issue<true>(nxt_s, 0, 0, s_tok[(kt + 1) & 1]);
-          else
-            la.issue(nxt_s, r0 + (kt + 1) * BK, r1);
-          if (GATHER && cur.gb)
-            lb.template issue<true>(nxt_s + BK * WG_ROWB, 0, 0, s_tok[(kt + 1) & 1]);
-          else
-            lb.issue(nxt_s + BK * WG_ROWB, r0 + (kt + 1) * BK, r1);
-        }
-        // token rows of stage kt + 2, stored into the list stage kt used
-        // (its last reader, the issue of stage kt, is behind the previous
-        // barrier)
-        int tk = -1;
-        if ((GATHER || GD) && cur.gat && tid < BK) tk = token(cur, r0 + (kt + 2) * BK + tid);
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-          bf16x8_t a[TM], b[TN];
-#pragma unroll
-          for (int i = 0; i < TM; ++i) a[i] = frag_tr(cur_s, wm * WTM + i * 32, kk, lane);
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            b[j] = frag_tr(cur_s + BK * WG_ROWB, wn * WTN + j * 32, kk, lane);
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-              acc[i][j] = E::mfma(a[i], b[j], acc[i][j]);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        if ((GATHER || GD) && cur.gat && tid < BK) s_tok[kt & 1][tid] = tk;
-        __syncthreads();
-      }
-    }
-    // the next tile's stage 0 goes out before this tile's epilogue (a tile
-    // that gathers first has its first two token lists written: this tile's
-    // last reader of the lists is behind the main loop's final barrier)
+    mainloop_steps<TL, E, WgLoad<GD>, WgLoad<GATHER>, true, FR>(la, lb, 0, nk, smem, acc, fr);
     gt += nslots;
     const TileJob nxt = job(gt);
-    pre = nxt.valid && nxt.nk > 0;
-    if (pre) {
-      if constexpr (GATHER || GD) {
-        if (nxt.gat) {  // block-uniform
-          if (tid < BK) {
-            s_tok[0][tid] = token(nxt, nxt.r0 + tid);
-            s_tok[1][tid] = token(nxt, nxt.r0 + BK + tid);
-          }
-          __syncthreads();
-        }
+    // the next tile's first stage is loaded during this tile's epilogue,
+    // behind the epilogue's first loads and ahead of its stores
+    auto next_stage0 = [&]() {
+      if (nxt.valid) {  // block-uniform
+        init_loaders(nxt);
+        la.load(0, 0);
+        lb.load(0, 0);
       }
-      issue_stage0(nxt);
-    }
-    // Epilogue.  The eight 32 x 32 pieces of the wave's tile are written in
-    // batches of PB; with ACC, the previous values of batch b + 1 are loaded
-    // before batch b is stored, so each batch's loads are in flight while the
-    // batch before it is added and stored (a load issued after the stores
-    // could not be waited for without waiting for them: the vector memory
-    // counter retires in order).  Accesses go through a buffer resource over
-    // the tile's rows [m0, min(m0 + 256, M)); the row part of an element's
-    // offset is the same for every lane, so it is a scalar offset and the
-    // accesses need no address registers.  No branch decides what is
-    // written: an access the tile does not own -- a 32-row piece past M
-    // (M - m0 is a multiple of 64, so a piece lies wholly inside or past it)
-    // or a lane whose column is past N -- has 2^31 added to its vector offset,
-    // beyond the resource's size, so the buffer range check drops it (a load
-    // returns 0); a piece past M also gets a zero scalar offset.
+    };
+    // Epilogue.  Accumulator block acc[i][j] registers 4q..4q+3 hold output
+    // row wm*128 + i*32 + lane%32 of the tile, columns wn*64 + j*32 + 8q +
+    // 4*(lane/32) + 0..3 (TrFrags: the N-side fragment is the MFMA's first
+    // operand).  Each 32 x 32 piece pc = i*TN + j goes through a 4 KiB slot
+    // of the wave's 16 KiB of LDS (all of it is free: the main loop ended
+    // with a barrier, and the next tile's first stage is in registers):
+    // written as 16-byte chunks, a row's chunks XOR-swizzled by the row, and
+    // read back as 8 rows x 128 bytes per instruction, lane l taking row
+    // l/8 + 8p, columns 4*(l%8)..+3, so every global access is 16 bytes per
+    // lane and 128 contiguous bytes per row.  LDS operations of one wave
+    // complete in order, so no barrier is needed between a write and its
+    // read-back, or between a slot's read-back and its next write.  dW is
+    // touched once per launch: its loads and stores are non-temporal.
+    // Global accesses go through a buffer resource over the tile's rows
+    // [m0, min(m0 + 256, M)).  No branch decides what is written: an access
+    // the tile does not own -- a 32-row piece past M (M - m0 is a multiple
+    // of 64, so a piece lies wholly inside or past it) or columns past N --
+    // has 2^31 added to its offset, beyond the resource's size, so the
+    // buffer range check drops it (a load returns 0).
     const int M = cur.M, N = cur.N, m0 = cur.m0, n0 = cur.n0;
     const int rows_in = min(256, M - m0);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(cur.out + (size_t)m0 * N), (short)0, rows_in * N * 4, 0x00020000);
-    const int wrow = __builtin_amdgcn_readfirstlane(wm * WTM);
-    constexpr int PB = GATHER ? 1 : 2;  // pieces per batch (register budget)
-    constexpr int NBAT = TM * TN / PB;
-    // piece q = j * TM + i: column strip j, row block i.  in_rows(q) = 1 when
-    // the piece starts before row rows_in (wave-uniform), else 0.
-    auto in_rows = [&](int q) { return (int)((uint32_t)(wrow + (q % TM) * 32 - rows_in) >> 31); };
-    auto voff = [&](int q) {
-      const int col = n0 + wn * WTN + (q / TM) * 32 + (lane & 31);
-      const uint32_t out_col = (uint32_t)(N - 1 - col) >> 31;  // 1 when col >= N
-      const uint32_t drop = (out_col | (uint32_t)(1 - in_rows(q))) << 31;
-      return (int)(((uint32_t)(4 * (lane >> 5) * N + col) * 4u) | drop);
-    };
-    auto soff = [&](int q, int r) {
-      return in_rows(q) * ((wrow + (q % TM) * 32 + 8 * (r >> 2) + (r & 3)) * N * 4);
-    };
-    float prev[PB][16];
-    auto load_batch = [&](int b) {
+    constexpr int NT_ = 2;  // cache policy: non-temporal
+    uint8_t* const ep = (uint8_t*)smem + w * 16384;
+    auto ep_write = [&](int i, int j, int slot) {
+      const int r = lane & 31;
 #pragma unroll
-      for (int p = 0; p < PB; ++p)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          prev[p][r] = __uint_as_float(
-              __builtin_amdgcn_raw_buffer_load_b32(rs, voff(b * PB + p), soff(b * PB + p, r), 0));
-    };
-    if constexpr (ACC) load_batch(0);
-#pragma unroll
-    for (int b = 0; b < NBAT; ++b) {
-      float v[PB][16];
-#pragma unroll
-      for (int p = 0; p < PB; ++p) {
-        const int q = b * PB + p;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          v[p][r] = ACC ? prev[p][r] + acc[q % TM][q / TM][r] : acc[q % TM][q / TM][r];
+      for (int q = 0; q < 4; ++q) {
+        const int c = 2 * q + (lane >> 5);
+        const f32x4_t v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                           acc[i][j][4 * q + 3]};
+        *(f32x4_t*)(ep + slot * 4096 + r * 128 + ((c ^ (r & 7)) << 4)) = v;
       }
-      if (ACC && b + 1 < NBAT) load_batch(b + 1);
-      // keep the next batch's loads ahead of this batch's stores (the
-      // scheduler would otherwise sink them below the stores)
+    };
+    auto ep_read = [&](int p, int slot) {
+      const int r = (lane >> 3) + 8 * p, c = lane & 7;
+      return *(const f32x4_t*)(ep + slot * 4096 + r * 128 + ((c ^ (r & 7)) << 4));
+    };
+    auto piece_in = [&](int i) { return (uint32_t)(wm * WTM + i * 32 - rows_in) >> 31; };
+    // byte offset of this lane's chunk of piece (i, j), row group p, column e
+    // of the chunk (drop bit included)
+    auto voff = [&](int i, int j, int p, int e = 0) {
+      const int col = n0 + wn * WTN + j * 32 + 4 * (lane & 7) + e;
+      const int row = wm * WTM + i * 32 + (lane >> 3) + 8 * p;
+      const uint32_t drop = ((uint32_t)(N - 1 - col) >> 31) | (1u - piece_in(i));
+      return (int)(((uint32_t)(row * N + col) * 4u) | (drop << 31));
+    };
+    constexpr int NP = TM * TN;  // pieces
+    constexpr int NS = 4;        // LDS slots per wave
+    if constexpr (!ROUTER) {
+      // N is a multiple of 4: a chunk of four columns lies wholly inside or
+      // past it.  With ACC, pieces 0..NS-1 first go to their LDS slots, which
+      // frees their registers for the previous values of PF pieces, all
+      // loaded at once; piece pc + PF is loaded into piece pc's registers as
+      // soon as those are consumed.  Piece pc is then read back (pieces past
+      // NS are staged through the slot of piece pc - NS, already read), added
+      // to its previous values and stored.  The next tile's first stage is
+      // loaded once half of the pieces are stored.
+      constexpr int PF = 5;
+      f32x4_t prev[ACC ? PF : 1][4];
+      auto load_piece = [&](int pc) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          prev[pc % PF][p] = __builtin_bit_cast(
+              f32x4_t,
+              __builtin_amdgcn_raw_buffer_load_b128(rs, voff(pc / TN, pc % TN, p), 0, NT_));
+      };
+      if constexpr (ACC) {
+#pragma unroll
+        for (int pc = 0; pc < NS; ++pc) ep_write(pc / TN, pc % TN, pc);
+#pragma unroll
+        for (int pc = 0; pc < PF; ++pc) load_piece(pc);
+      } else {
+        next_stage0();
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int p = 0; p < PB; ++p)
+      for (int pc = 0; pc < NP; ++pc) {
+        const int i = pc / TN, j = pc % TN, slot = pc % NS;
+        if (!ACC || pc >= NS) ep_write(i, j, slot);
+        f32x4_t v[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[p][r]), rs, voff(b * PB + p),
-                                                soff(b * PB + p, r), 0);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int p = 0; p < 4; ++p) {
+          v[p] = ep_read(p, slot);
+          if constexpr (ACC) v[p] += prev[pc % PF][p];
+        }
+        // (ahead of the stores: a load issued after a store could not be
+        // waited for without it, vector memory operations complete in order)
+        if (ACC && pc + PF < NP) load_piece(pc + PF);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v[p]), rs,
+                                                 voff(i, j, p), 0, NT_);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ACC && pc == NP / 2 - 1) next_stage0();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      // the router's N = 2E need not be a multiple of 4: 4-byte stores, each
+      // column checked
+      next_stage0();
+#pragma unroll
+      for (int pc = 0; pc < NP; ++pc) {
+        const int i = pc / TN, j = pc % TN;
+        ep_write(i, j, 0);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const f32x4_t v = ep_read(p, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[e]), rs, voff(i, j, p, e), 0, 0);
+        }
+      }
     }
+    __syncthreads();  // staging reads done before the next tile's first stage lands in LDS
+    if (!nxt.valid) break;
     cur = nxt;
   }
 }
