@@ -382,11 +382,15 @@ def main():
                     help="run a few serialized steps and a copy probe of known size, print no "
                          "JSON line: the program to run under rocprofv3 --pmc for the per-kernel "
                          "HBM traffic (FETCH_SIZE / WRITE_SIZE) and MFMA counters")
-    ap.add_argument("--summarize", choices=("kernels", "traffic", "mfma", "overlap"),
+    ap.add_argument("--roctx", action="store_true",
+                    help="bracket every phase of the step with a roctx range (MOE_ROCTX=1): "
+                         "run eagerly (--graph off) under rocprofv3 --marker-trace")
+    ap.add_argument("--summarize", choices=("kernels", "traffic", "mfma", "overlap", "phases"),
                     help="write profiles/<kind>_<workload>.md from rocprofv3 output (no GPU)")
     ap.add_argument("--inputs", nargs="+", help="rocprofv3 files for --summarize: a kernel "
                     "trace (kernels, overlap), FETCH_SIZE then WRITE_SIZE counter csv "
-                    "(traffic), or the MFMA counter csv (mfma)")
+                    "(traffic), the MFMA counter csv (mfma), or a kernel trace, a HIP API "
+                    "trace and a marker trace of one --roctx run (phases)")
     ap.add_argument("--profile-cmd", action="append", default=[],
                     help="the command(s) that made the --inputs, quoted in the summary")
     ap.add_argument("--out", default=None, help="summary file (default profiles/<kind>_<wl>.md)")
@@ -398,6 +402,8 @@ def main():
 
     if args.summarize:
         return summarize(args)
+    if args.roctx:  # read by the library at its first phase
+        os.environ["MOE_ROCTX"] = "1"
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -734,7 +740,8 @@ def summarize(args):
     desc = (f"{w.name} (T={w.T}, d={w.d}, F={w.F}, {w.E_l} of {w.E} experts local, top-{w.K}, "
             f"{w.dtype}, {w.route})")
     txt = {"kernels": _sum_kernels, "traffic": _sum_traffic, "mfma": _sum_mfma,
-           "overlap": _sum_overlap}[args.summarize](args, w, N, T_loc, desc)
+           "overlap": _sum_overlap, "phases": _sum_phases}[args.summarize](args, w, N, T_loc,
+                                                                         desc)
     with open(out, "w") as fh:
         fh.write(txt)
     err(f"[summarize] wrote {out}")
@@ -970,6 +977,101 @@ class: plan, top-k, permute, combine and their backwards.
 | share of dispatch/combine time under a GEMM | {100 * _length(inter) / max(1, _length(p)):.2f} % |
 | busy (any kernel) union (us) | {_length(busy) / 1e3:.1f} |
 | steady step time under the profiler (us, wgrad to wgrad, second half) | {step_us:.1f} |
+"""
+
+
+def _rows(path):
+    with open(path) as fh:
+        return list(csv.DictReader(fh))
+
+
+def _field(r, *names):
+    for n in names:
+        if n in r and r[n] != "":
+            return r[n]
+    raise KeyError(f"none of {names} in {sorted(r)}")
+
+
+def _sum_phases(args, w, N, T_loc, desc):
+    """Per-phase GPU time from a --roctx run: each kernel belongs to the roctx
+    range (on the launching thread) that contains the host call launching it,
+    matched through the launch's correlation id.  A phase's time per
+    occurrence is the summed duration of the kernels of one of its ranges;
+    the table gives the median over the second half of its occurrences (the
+    first calls of a process run slower while the clocks settle)."""
+    import bisect
+    kern, api, mark = (_rows(p) for p in args.inputs[:3])
+    launch = {}
+    for r in api:
+        launch[_field(r, "Correlation_Id")] = (_field(r, "Thread_Id"),
+                                               int(_field(r, "Start_Timestamp")))
+    ranges = collections.defaultdict(list)  # thread -> [(start, end, name)]
+    for r in mark:
+        name = _field(r, "Function", "Message", "Name")
+        if not name.startswith("moe."):
+            continue
+        ranges[_field(r, "Thread_Id")].append((int(_field(r, "Start_Timestamp")),
+                                               int(_field(r, "End_Timestamp")), name))
+    for t in ranges:
+        ranges[t].sort()
+    starts = {t: [a for a, _, _ in v] for t, v in ranges.items()}
+    inst = collections.defaultdict(lambda: collections.defaultdict(float))  # phase -> range -> us
+    names = collections.defaultdict(set)
+    count = collections.Counter()
+    unmatched = 0
+    for r in kern:
+        n = bench_name(_field(r, "Kernel_Name"))
+        if not n:
+            continue
+        a, b = int(_field(r, "Start_Timestamp")), int(_field(r, "End_Timestamp"))
+        th, t = launch.get(_field(r, "Correlation_Id"), (None, None))
+        key = None
+        if th in ranges:
+            i = bisect.bisect_right(starts[th], t) - 1
+            if i >= 0 and ranges[th][i][1] >= t:
+                key = (ranges[th][i][2], (th, i))
+        if key is None:
+            unmatched += 1
+            key = ("(outside any range)", (None, 0))
+        inst[key[0]][key[1]] += (b - a) / 1e3
+        names[key[0]].add(n)
+        count[key[0]] += 1
+    rows = []
+    for ph, d in inst.items():
+        vals = [d[k] for k in sorted(d)]
+        tail = vals[len(vals) // 2:]
+        rows.append((statistics.median(tail), ph, len(vals), count[ph], sum(vals)))
+    rows.sort(reverse=True)
+    total = sum(r[0] for r in rows)
+    lines = [f"| `{ph}` | {nr} | {nk} | {', '.join(sorted(names[ph]))} | {tot:.1f} | {med:.1f} | "
+             f"{100 * med / max(total, 1e-9):.1f} |" for med, ph, nr, nk, tot in rows]
+    table = "\n".join(lines)
+    return f"""# Phases of the step (roctx ranges): {desc}
+
+Command (run from the repository root on one MI355X):
+
+```
+{_cmds(args)}
+```
+
+`bench.py --roctx` sets MOE_ROCTX=1, so the library brackets each phase of the
+step with a roctx range `moe.<phase>` (route, dispatch, expert FFN forward,
+combine, and their backwards; the activation- and input-gradient halves of
+the expert dgrad separately when the weight gradient runs between them; the
+weight gradients; the dgrad weight copies made once per call).  The steps run
+eagerly and serialized, so a phase's kernels run alone and their summed
+durations are the phase's GPU time.  Each kernel is assigned to the range
+that contains the host call that launched it (HIP API trace, matched by
+correlation id), summarised by `python bench.py --summarize phases --workload
+{w.name} --inputs <kernel trace> <HIP API trace> <marker trace>`.  `per
+occurrence` is the median, over the second half of a phase's occurrences, of
+the summed kernel time of one range (the first calls of a process run slower
+while the clocks settle); `share` is its part of the sum of those medians.
+Kernels outside every range: {unmatched}.
+
+| phase | occurrences | kernels | kernel names | GPU time, all (us) | per occurrence (us) | share % |
+|---|---|---|---|---|---|---|
+{table}
 """
 
 

@@ -3,8 +3,10 @@
 // before the first launch, so a rejected call writes nothing.
 #include "moe_internal.h"
 
+#include <dlfcn.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -27,6 +29,47 @@ int check_launch(const char* what) {
   if (e != hipSuccess) return set_error(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return MOE_OK;
 }
+
+// ---------------------------------------------------------------------------
+// Phase ranges for profilers.  With MOE_ROCTX=1 in the environment (read
+// once), each phase of the step (route, dispatch, expert forward, combine and
+// their backwards, the weight gradients) is bracketed by a roctx range
+// ("moe.<phase>"), which rocprofv3 --marker-trace records: host-side ranges
+// around the phase's launches, from which a trace maps each kernel to its
+// phase through its launch call.  The roctx library is opened at run time, so
+// the library has no link dependency on it; without the variable (or without
+// the library) a phase costs one predictable branch.
+// ---------------------------------------------------------------------------
+struct Roctx {
+  int (*push)(const char*) = nullptr;
+  int (*pop)() = nullptr;
+};
+static const Roctx& roctx() {
+  static const Roctx r = [] {
+    Roctx x;
+    const char* e = getenv("MOE_ROCTX");
+    if (!e || strcmp(e, "1") != 0) return x;
+    for (const char* lib : {"librocprofiler-sdk-roctx.so.1", "libroctx64.so.4"}) {
+      void* h = dlopen(lib, RTLD_NOW | RTLD_LOCAL);
+      if (!h) continue;
+      x.push = (int (*)(const char*))dlsym(h, "roctxRangePushA");
+      x.pop = (int (*)())dlsym(h, "roctxRangePop");
+      if (x.push && x.pop) return x;
+      x = Roctx{};
+    }
+    return x;
+  }();
+  return r;
+}
+struct PhaseRange {
+  const bool on;
+  explicit PhaseRange(const char* name) : on(roctx().push != nullptr) {
+    if (on) roctx().push(name);
+  }
+  ~PhaseRange() {
+    if (on) roctx().pop();
+  }
+};
 
 // ---------------------------------------------------------------------------
 // kernel timing
@@ -772,40 +815,49 @@ struct StepCtx {
 };
 
 static int fwd_route(const StepCtx& c, const moe_mb* A, hipStream_t q) {
+  const PhaseRange pr("moe.route");
   return do_route(c.s, c.st->route_mode, A->x, c.st->W_r, c.st->bias, A->logits, A->idx,
                   A->gates, c.wsA, q);
 }
 static int fwd_dispatch(const StepCtx& c, const moe_mb* A, hipStream_t q) {
+  const PhaseRange pr("moe.dispatch");
   return do_dispatch(c.s, A->x, A->idx, A->counts, A->offsets, A->row_of_pair, A->pair_of_row,
                      A->tile_offsets, c.fused ? nullptr : A->xp, c.wsA, q);
 }
 static int fwd_ffn(const StepCtx& c, const moe_mb* A, hipStream_t q) {
+  const PhaseRange pr("moe.expert_ffn_fwd");
   return launch_ffn_fwd(c.s, c.fused ? A->x : A->xp, c.fused ? A->pair_of_row : nullptr,
                         A->offsets, A->tile_offsets, c.st->W_gu, c.st->W_down, A->h, A->a,
                         A->yp, q);
 }
 static bool has_shared(const StepCtx& c) { return c.st->F_s > 0; }
 static int fwd_combine(const StepCtx& c, const moe_mb* A, hipStream_t q) {
+  const PhaseRange pr("moe.combine");
   return launch_combine(c.s, A->yp, A->gates, A->row_of_pair, has_shared(c) ? A->y_s : nullptr,
                         A->out, q);
 }
 static int fwd_shared(const StepCtx& c, const moe_mb* A, hipStream_t q) {
+  const PhaseRange pr("moe.shared_fwd");
   return do_shared_fwd(c.s, c.st->F_s, A->x, c.st->W_gu_s, c.st->W_down_s, A->h_s, A->a_s,
                        A->y_s, c.wsSA, q);
 }
 static int bwd_shared_dgrad(const StepCtx& c, const moe_mb* B, hipStream_t q) {
+  const PhaseRange pr("moe.shared_dgrad");
   return do_shared_dgrad(c.s, c.st->F_s, B->dout, B->h_s, c.st->W_gu_s, c.st->W_down_s, B->dh_s,
                          B->dx_s, c.wsSB, q);
 }
 static int bwd_shared_wgrad(const StepCtx& c, const moe_mb* B, hipStream_t q) {
+  const PhaseRange pr("moe.shared_wgrad");
   return do_shared_wgrad(c.s, c.st->F_s, B->x, B->a_s, B->dh_s, B->dout, c.st->dW_gu_s,
                          c.st->dW_down_s, (c.st->accumulate & MOE_ACCUM_DW) != 0, c.wsSB, q);
 }
 static int bwd_combine(const StepCtx& c, const moe_mb* B, hipStream_t q) {
+  const PhaseRange pr("moe.combine_bwd");
   return launch_combine_bwd(c.s, B->dout, B->yp, B->gates, B->row_of_pair,
                             c.fcb ? nullptr : B->dyp, B->dgates, q);
 }
 static int bwd_route(const StepCtx& c, const moe_mb* B, hipStream_t q) {
+  const PhaseRange pr("moe.route_bwd");
   if (c.st->route_mode == MOE_ROUTE_FORCE_BALANCE) return MOE_OK;
   const bool with_dw = c.router && c.st->dW_r;
   return launch_route_bwd(c.s, B->dgates, B->gates, B->idx, with_dw ? B->x : nullptr, B->dlogits,
@@ -814,17 +866,22 @@ static int bwd_route(const StepCtx& c, const moe_mb* B, hipStream_t q) {
 }
 static int bwd_dgrad(const StepCtx& c, const moe_mb* B, bool weights_ready, hipStream_t q,
                      int parts = kDgradBoth) {
+  const PhaseRange pr(parts == kDgradAct  ? "moe.expert_dgrad_act"
+                      : parts == kDgradIn ? "moe.expert_dgrad_in"
+                                          : "moe.expert_dgrad");
   const FusedCombineBwd fc{B->pair_of_row, B->gates, B->ag};
   return launch_ffn_dgrad(c.s, c.fcb ? B->dout : B->dyp, B->h, B->offsets, B->tile_offsets,
                           c.st->W_gu, c.st->W_down, B->dh, B->dxp, c.wsW ? c.wsW : c.wsB,
                           c.wsW ? true : weights_ready, q, parts, c.fcb ? &fc : nullptr);
 }
 static int bwd_dispatch(const StepCtx& c, const moe_mb* B, hipStream_t q) {
+  const PhaseRange pr("moe.dispatch_bwd");
   return do_dispatch_bwd(c.s, B->dxp, B->row_of_pair, B->idx, c.router ? B->dlogits : nullptr,
                          c.st->W_r, B->dx, false, c.wsB, q,
                          has_shared(c) ? B->dx_s : nullptr);
 }
 static int bwd_wgrad(const StepCtx& c, const moe_mb* B, hipStream_t q) {
+  const PhaseRange pr("moe.expert_wgrad");
   return launch_ffn_wgrad(c.s, c.fused ? B->x : B->xp, c.fused ? B->pair_of_row : nullptr,
                           c.fcb ? B->ag : B->a, B->dh, c.fcb ? B->dout : B->dyp, B->offsets,
                           c.st->dW_gu, c.st->dW_down, (c.st->accumulate & MOE_ACCUM_DW) != 0, q,
@@ -1155,6 +1212,7 @@ extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, h
   void* wsW = nullptr;
   if (any_bwd) {
     wsW = steps[0].ws;
+    const PhaseRange pr("moe.dgrad_weights");
     TRY(launch_dgrad_weights(&steps[0].shape, steps[0].W_gu, steps[0].W_down, wsW, s0));
   }
   const bool serial = (flags & MOE_STEP_SERIALIZE) || s0 == s1;
