@@ -276,6 +276,18 @@ struct LocalRows {
   __device__ __forceinline__ int row(int k) const { return __builtin_amdgcn_readlane(rk, k); }
 };
 
+// A 16-byte load with the non-temporal cache policy, for the gathered row
+// streams (y_p in the combine and its backward, dx_p in the dispatch
+// backward): each row is read once per launch, so it should not displace
+// what the next kernels read (measured on the 128-expert layer: combine
+// 126 -> 106 us).  Stores keep the default policy: their rows (x_p, dy_p) are
+// read back by the expert GEMMs that follow.
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4_nt v = __builtin_nontemporal_load((const u32x4_nt*)p);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // Keep a loaded chunk in registers where it was loaded: without this the
 // compiler may move a side-effect-free load next to each of its uses (into a
 // conditional block or a loop), where its latency is no longer overlapped.
@@ -382,9 +394,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
       const uint4* s1 = yp + (size_t)lr.row(k1) * nch;
       uint4 v0[MAXC], v1[MAXC];
 #pragma unroll
-      for (int i = 0; i < MAXC; ++i) v0[i] = s0[cc[i]];
+      for (int i = 0; i < MAXC; ++i) v0[i] = load_nt(&s0[cc[i]]);
 #pragma unroll
-      for (int i = 0; i < MAXC; ++i) v1[i] = s1[cc[i]];
+      for (int i = 0; i < MAXC; ++i) v1[i] = load_nt(&s1[cc[i]]);
 #pragma unroll
       for (int i = 0; i < MAXC; ++i) {
         pin(v0[i]);
@@ -486,7 +498,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
 #pragma unroll
       for (int i = 0; i < MAXC; ++i) {
         const int c = lane + 64 * i;
-        yv[i] = yp[(size_t)r * nch + (c < nch ? c : nch - 1)];
+        yv[i] = load_nt(&yp[(size_t)r * nch + (c < nch ? c : nch - 1)]);
       }
 #pragma unroll
       for (int i = 0; i < MAXC; ++i) pin(yv[i]);
@@ -511,7 +523,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
         const int c = lane + 64 * i;
         if (c < nch) {
           float y[CN], o[CN];
-          Chunk<T>::unpack(yp[(size_t)r * nch + c], y);
+          Chunk<T>::unpack(load_nt(&yp[(size_t)r * nch + c]), y);
 #pragma unroll
           for (int q = 0; q < CN; ++q) {
             dot = fmaf(dv[i][q], y[q], dot);
@@ -610,9 +622,9 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(
       const uint4* s1 = dxp + (size_t)lr.row(k1) * nch;
       uint4 v0[MAXC], v1[MAXC];
 #pragma unroll
-      for (int i = 0; i < MAXC; ++i) v0[i] = s0[cc[i]];
+      for (int i = 0; i < MAXC; ++i) v0[i] = load_nt(&s0[cc[i]]);
 #pragma unroll
-      for (int i = 0; i < MAXC; ++i) v1[i] = s1[cc[i]];
+      for (int i = 0; i < MAXC; ++i) v1[i] = load_nt(&s1[cc[i]]);
 #pragma unroll
       for (int i = 0; i < MAXC; ++i) {
         pin(v0[i]);
