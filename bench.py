@@ -44,7 +44,7 @@ def err(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic(w, N, T_loc, accumulate=True, fused=False, fcb=False):
+def algorithmic(w, N, T_loc, accumulate=True, fused=False, fcb=False, pair=False):
     """Algorithmic work per step of each kernel (one launch of each, plus the
     shared expert's launches of the same GEMMs over all T tokens when the
     workload has one): {name: {"flop": F, "byte": B}}.  Bytes count one pass
@@ -52,7 +52,9 @@ def algorithmic(w, N, T_loc, accumulate=True, fused=False, fcb=False):
     expert weights, and wgrad's the float32 weight gradients (read and written
     with accumulate, written without).  fused: the permute fused into GEMM1
     and wgrad (x rows instead of xp); fcb: the fused combine backward (dout
-    rows instead of dy_p, ag written by dgrad_act)."""
+    rows instead of dy_p, ag written by dgrad_act); pair: the routed experts'
+    weight gradients of two consecutive steps in one launch, so per step the
+    float32 weight gradients are read and written half as often."""
     d, F, T, K, E, E_l = w.d, w.F, w.T, w.K, w.E, w.E_l
     b = 4 if w.dtype == "f32" else 2
     Fs = w.F_s
@@ -76,7 +78,7 @@ def algorithmic(w, N, T_loc, accumulate=True, fused=False, fcb=False):
                      + (T * 2 * Fs * b + sgu + T * d * b) * (Fs > 0)},
         "wgrad": {"flop": 6.0 * N * d * F + 6.0 * T * d * Fs,
                   "byte": dyin + N * (F + 2 * F) * b + xin + T * (2 * d + 3 * Fs) * b * (Fs > 0)
-                  + dW * (2 if accumulate else 1)},
+                  + dW * (2 if accumulate else 1) * (0.5 if pair else 1.0)},
         "router": {"flop": 2.0 * T * d * E, "byte": T * d * b + d * E * b + 4.0 * T * E},
         # router weight gradient x^T dlogits on the matrix cores (bf16 data);
         # the two-term split of dlogits forms it twice, counted once here
@@ -192,22 +194,24 @@ def cpu_oracle_baseline(w, inp, target_s=10.0):
                       f"{total:.1f} s"}
 
 
-def group_plan(K, G0):
-    """Steps per captured graph for K timed steps: (G, rem) with G even and
-    G * reps + rem == K, rem in {0, 1} (one eager step when K is odd); G0 when
-    it divides K, else the largest even divisor of K (or of K - 1) up to 2 G0;
-    (None, K) when K is too small for a graph."""
+def group_plan(K, G0, unit=2):
+    """Steps per captured graph for K timed steps: (G, rem) with G a multiple
+    of `unit` (the steps after which the micro-batch buffer sets are back in
+    their roles, times the steps a paired weight gradient spans) and
+    G * reps + rem == K, rem < unit eager steps; G0 when it divides K - rem,
+    else the largest such divisor of K - rem up to 2 G0; (None, K) when K is
+    too small for a graph."""
     def best(n):
-        if n >= 2 and n % G0 == 0:
+        if n >= unit and n % G0 == 0:
             return G0
-        c = [g for g in range(2, min(n, 2 * G0) + 1, 2) if n % g == 0]
+        c = [g for g in range(unit, min(n, 2 * G0) + 1, unit) if n % g == 0]
         return max(c) if c else None
 
-    g = best(K)
-    if g:
-        return g, 0
-    g = best(K - 1) if K > 1 else None
-    return (g, 1) if g else (None, K)
+    for rem in range(unit):
+        g = best(K - rem) if K - rem >= unit else None
+        if g:
+            return g, rem
+    return None, K
 
 
 # ---------------------------------------------------------------------------
@@ -240,13 +244,19 @@ class Layer:
                               device="cuda")
         self.fused = args.fused_permute == "on"
         self.fcb = args.fused_combine_bwd == "on"
+        # the paired weight gradient keeps the micro-batch back-propagated in
+        # step j until step j + 1: three buffer sets in rotation
+        self.pair = (args.pair_wgrad == "on" and args.pipeline == "on" and
+                     not (self.fused or self.fcb))
+        self.R = 3 if self.pair else 2
         self.pipelined = args.pipeline == "on"
         self.G = args.group
         # flags of every step: the fused permute and the wgrad's place in the
         # backward stream's order (both leave the results unchanged)
         self.FLAGS = ((M.MOE_STEP_FUSED_PERMUTE if self.fused else 0) |
                       (M.MOE_STEP_FUSED_COMBINE_BWD if self.fcb else 0) |
-                      (M.MOE_STEP_MID_WGRAD if args.wgrad_order == "mid" else 0))
+                      (M.MOE_STEP_MID_WGRAD if args.wgrad_order == "mid" else 0) |
+                      (M.MOE_STEP_PAIR_WGRAD if self.pair else 0))
         self.shared = None
         if w.F_s:  # a shared expert beside the routed ones
             self.shared = (D(inp["W_gu_s"]), D(inp["W_down_s"]), z(2 * w.F_s, w.d),
@@ -256,8 +266,13 @@ class Layer:
                                              F_s=w.F_s, fused_bwd=self.fcb)
         self.mbs = [mk(inp["x"], inp["dout"], inp["gates"]),
                     mk(inp["x_b"], inp["dout_b"], inp.get("gates_b"))]
+        if self.R == 3:  # the third set: the first one's tokens in reverse order
+            g = inp["gates"]
+            self.mbs.append(mk(inp["x"][::-1].copy(), inp["dout"][::-1].copy(),
+                               None if g is None else g[::-1].copy()))
         self.i = 0  # steps issued so far (after the priming forward)
-        M.moe_overlap_step(self.make_step(self.mbs[0], None), s0, s1, self.FLAGS)
+        M.moe_overlap_step(self.make_step(self.mbs[0], None), s0, s1,
+                           self.FLAGS & ~M.MOE_STEP_PAIR_WGRAD)
 
     def make_step(self, fwd, bwd):
         M = self.M
@@ -265,8 +280,8 @@ class Layer:
                            self.ws, fwd=fwd, bwd=bwd, W_r=self.W_r, bias=self.bias,
                            dW_r=self.dW_r, accumulate=M.MOE_ACCUM_DW, shared=self.shared)
 
-    def make(self, i):  # step i forwards one micro-batch and back-propagates the other
-        return self.make_step(self.mbs[(i + 1) % 2], self.mbs[i % 2])
+    def make(self, i):  # step i forwards one micro-batch and back-propagates another
+        return self.make_step(self.mbs[(i + 1) % self.R], self.mbs[i % self.R])
 
     def issue(self, n, flags, q=None):
         """Issue the next n steps on q (and s1): one pipelined moe_overlap_steps
@@ -363,8 +378,15 @@ def main():
                     help="run the overlapped steps G at a time through moe_overlap_steps, the "
                          "streams' roles alternating so consecutive steps overlap (on), or one "
                          "moe_overlap_step call per step, joined at every step boundary (off)")
-    ap.add_argument("--group", type=int, default=10,
-                    help="steps per moe_overlap_steps call and per captured graph (even)")
+    ap.add_argument("--pair-wgrad", choices=("on", "off"), default="off",
+                    help="pair the routed experts' weight gradients of consecutive steps "
+                         "(MOE_STEP_PAIR_WGRAD: one launch per two steps, dW read and written "
+                         "once for both; three micro-batch buffer sets); not with the fused "
+                         "paths.  Off by default: its one graph-captured run ended in a host "
+                         "fault whose cause is not found")
+    ap.add_argument("--group", type=int, default=None,
+                    help="steps per moe_overlap_steps call and per captured graph: a "
+                         "multiple of 2, of 6 with --pair-wgrad on (default 10, 12)")
     ap.add_argument("--ab-rounds", type=int, default=6,
                     help="rounds of the alternating overlapped / serialized comparison")
     ap.add_argument("--overlap-workload", default=OVERLAP_WORKLOAD,
@@ -419,8 +441,13 @@ def main():
         err("bench.py: no GPU visible")
         sys.exit(1)
     M.lib()  # fails loudly if libmoe.so is not built
-    if args.group < 2 or args.group % 2:
-        err("bench.py: --group must be even")
+    pairing = args.pair_wgrad == "on" and args.pipeline == "on" and \
+        args.fused_permute == "off" and args.fused_combine_bwd == "off"
+    unit = 6 if pairing else 2  # buffer-set rotation (3 or 2) x paired steps (2)
+    if args.group is None:
+        args.group = 12 if pairing else 10
+    if args.group < unit or args.group % unit:
+        err(f"bench.py: --group must be a multiple of {unit}")
         sys.exit(2)
     w = WORKLOADS[args.workload]
     if args.tokens:
@@ -471,7 +498,7 @@ def main():
     # eager step when --steps is odd); the library records only kernels and
     # events into the graph.
     K = args.steps
-    Gk, rem = group_plan(K, args.group) if args.graph == "on" else (None, K)
+    Gk, rem = group_plan(K, args.group, unit) if args.graph == "on" else (None, K)
     replay_ms = []
     if Gk:
         g = L.capture(Gk, 0)
@@ -491,7 +518,8 @@ def main():
         wall = time.perf_counter() - t0
         replay_ms = [ev0.elapsed_time(marks[0]) / Gk] + \
             [marks[r - 1].elapsed_time(marks[r]) / Gk for r in range(1, reps)]
-        launch = f"hipGraph replay ({Gk} steps per graph)" + (" + 1 eager step" if rem else "")
+        launch = f"hipGraph replay ({Gk} steps per graph)" + \
+            (f" + {rem} eager step{'s' if rem > 1 else ''}" if rem else "")
     else:
         t0 = time.perf_counter()
         ev0.record(s0)
@@ -548,7 +576,7 @@ def main():
         torch.cuda.synchronize()
 
     # ---- per-kernel achieved rates from the live kernel events
-    work = algorithmic(w, N, T_loc, accumulate=True, fused=L.fused, fcb=L.fcb)
+    work = algorithmic(w, N, T_loc, accumulate=True, fused=L.fused, fcb=L.fcb, pair=L.pair)
     traffic = stored_traffic(w.name) if args.tokens is None else {}
     kernels = {}
     for name, (tot_ms, n) in sorted(kern.items(), key=lambda kv: -kv[1][0]):
@@ -611,7 +639,9 @@ def main():
                            "two streams, " + ("wgrad between the two dgrad GEMMs"
                                               if args.wgrad_order == "mid" else
                                               "wgrad deferred to the end"),
-                   "weight_grads": "float32, accumulated every step",
+                   "weight_grads": "float32, accumulated every step" + (
+                       "; the routed experts' of steps 2i and 2i+1 in one launch"
+                       if L.pair else ""),
                    "launch": launch,
                    "pipeline": (f"moe_overlap_steps, {G} steps per call, stream roles "
                                 "alternating" if L.pipelined else

@@ -17,7 +17,7 @@ from ._lib import (  # noqa: F401
     MOE_ERR_UNSUPPORTED, MOE_ERR_ARG, MOE_F32, MOE_BF16, MOE_F16, MOE_ROUTE_TOPK,
     MOE_ROUTE_TOPK_FROM_LOGITS, MOE_ROUTE_FORCE_BALANCE, MOE_ACCUM_DX, MOE_ACCUM_DW,
     MOE_STEP_SERIALIZE, MOE_STEP_EAGER_WGRAD, MOE_STEP_SKIP_WGRAD, MOE_STEP_FUSED_PERMUTE,
-    MOE_STEP_MID_WGRAD, MOE_STEP_FUSED_COMBINE_BWD,
+    MOE_STEP_MID_WGRAD, MOE_STEP_FUSED_COMBINE_BWD, MOE_STEP_PAIR_WGRAD,
 )
 
 
@@ -290,6 +290,21 @@ def moe_ffn_wgrad(s, xp, a, dh, dyp, offsets, dW_gu, dW_down, accumulate=0, stre
              dW_down=(dW_down, E_l * d * F, _F32))
     check(lib().moe_ffn_wgrad(C.byref(s), _p(xp), _p(a), _p(dh), _p(dyp), _p(offsets),
                               _p(dW_gu), _p(dW_down), int(accumulate), _stream(stream)))
+
+
+def moe_ffn_wgrad_pair(s, xp, a, dh, dyp, offsets, xp2, a2, dh2, dyp2, offsets2, dW_gu, dW_down,
+                       accumulate=0, stream=None):
+    cap, d, F, E_l = s.T * s.K, s.d, s.F, s.E_l
+    for sfx, (o, x_, a_, h_, y_) in (("", (offsets, xp, a, dh, dyp)),
+                                     ("2", (offsets2, xp2, a2, dh2, dyp2))):
+        _chk_ffn(s, "moe_ffn_wgrad_pair", o, False, False, False,
+                 **{"xp" + sfx: (x_, cap * d, _DATA), "a" + sfx: (a_, cap * F, _DATA),
+                    "dh" + sfx: (h_, cap * 2 * F, _DATA), "dyp" + sfx: (y_, cap * d, _DATA)})
+    _chk(s, "moe_ffn_wgrad_pair", "dW_gu", dW_gu, _F32, E_l * 2 * F * d)
+    _chk(s, "moe_ffn_wgrad_pair", "dW_down", dW_down, _F32, E_l * d * F)
+    check(lib().moe_ffn_wgrad_pair(C.byref(s), _p(xp), _p(a), _p(dh), _p(dyp), _p(offsets),
+                                   _p(xp2), _p(a2), _p(dh2), _p(dyp2), _p(offsets2), _p(dW_gu),
+                                   _p(dW_down), int(accumulate), _stream(stream)))
 
 
 def moe_ffn_wgrad_gather(s, x, pair_of_row, a, dh, dyp, offsets, dW_gu, dW_down, accumulate=0,

@@ -36,6 +36,7 @@ MOE_STEP_SKIP_WGRAD = 4
 MOE_STEP_FUSED_PERMUTE = 8
 MOE_STEP_MID_WGRAD = 16
 MOE_STEP_FUSED_COMBINE_BWD = 32
+MOE_STEP_PAIR_WGRAD = 64
 
 
 class MoeShape(C.Structure):
@@ -90,6 +91,8 @@ SIGNATURES = {
     "moe_combine_bwd": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P]),
     "moe_ffn_dgrad": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "moe_ffn_wgrad": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, C.c_int, _P]),
+    "moe_ffn_wgrad_pair": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                     C.c_int, _P]),
     "moe_ffn_wgrad_gather": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, C.c_int, _P]),
     "moe_ffn_dgrad_gather": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        C.c_size_t, _P]),

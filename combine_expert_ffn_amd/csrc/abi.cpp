@@ -477,6 +477,33 @@ int moe_ffn_wgrad(const moe_shape* s, const void* xp, const void* a, const void*
                           (accumulate & MOE_ACCUM_DW) != 0, stream);
 }
 
+int moe_ffn_wgrad_pair(const moe_shape* s, const void* xp, const void* a, const void* dh,
+                       const void* dyp, const int32_t* offsets, const void* xp2,
+                       const void* a2, const void* dh2, const void* dyp2,
+                       const int32_t* offsets2, float* dW_gu, float* dW_down, int accumulate,
+                       hipStream_t stream) {
+  g_err[0] = 0;
+  if (int rc = validate_shape(s)) return rc;
+  REQUIRE(xp);
+  REQUIRE(a);
+  REQUIRE(dh);
+  REQUIRE(dyp);
+  REQUIRE(offsets);
+  REQUIRE(xp2);
+  REQUIRE(a2);
+  REQUIRE(dh2);
+  REQUIRE(dyp2);
+  REQUIRE(offsets2);
+  REQUIRE(dW_gu);
+  REQUIRE(dW_down);
+  if (accumulate & ~(MOE_ACCUM_DX | MOE_ACCUM_DW))
+    return set_error(MOE_ERR_ARG, "moe_ffn_wgrad_pair: unknown accumulate bits 0x%x",
+                     accumulate);
+  return launch_ffn_wgrad_pair(s, WgrOps{xp, a, dh, dyp, offsets},
+                               WgrOps{xp2, a2, dh2, dyp2, offsets2}, dW_gu, dW_down,
+                               (accumulate & MOE_ACCUM_DW) != 0, stream);
+}
+
 int moe_ffn_wgrad_gather(const moe_shape* s, const void* x, const int32_t* pair_of_row,
                          const void* a, const void* dh, const void* dyp, const int32_t* offsets,
                          float* dW_gu, float* dW_down, int accumulate, hipStream_t stream) {
@@ -888,6 +915,15 @@ static int bwd_wgrad(const StepCtx& c, const moe_mb* B, hipStream_t q) {
                           c.fcb ? B->pair_of_row : nullptr);
 }
 
+// The routed experts' weight gradients of micro-batches A (deferred by the
+// step before) and B in one launch (materialised xp and dy_p).
+static int bwd_wgrad_pair(const StepCtx& c, const moe_mb* A, const moe_mb* B, hipStream_t q) {
+  const PhaseRange pr("moe.expert_wgrad_pair");
+  return launch_ffn_wgrad_pair(c.s, WgrOps{A->xp, A->a, A->dh, A->dyp, A->offsets},
+                               WgrOps{B->xp, B->a, B->dh, B->dyp, B->offsets}, c.st->dW_gu,
+                               c.st->dW_down, (c.st->accumulate & MOE_ACCUM_DW) != 0, q);
+}
+
 // Host-side checks of one step description (flags, route mode, buffers,
 // workspace); fn names the entry point in the error message.
 static int check_step(const moe_step* st, int flags, const char* fn) {
@@ -895,8 +931,14 @@ static int check_step(const moe_step* st, int flags, const char* fn) {
   const moe_shape* s = &st->shape;
   if (int rc = validate_shape(s)) return rc;
   if (flags & ~(MOE_STEP_SERIALIZE | MOE_STEP_EAGER_WGRAD | MOE_STEP_SKIP_WGRAD |
-                MOE_STEP_FUSED_PERMUTE | MOE_STEP_MID_WGRAD | MOE_STEP_FUSED_COMBINE_BWD))
+                MOE_STEP_FUSED_PERMUTE | MOE_STEP_MID_WGRAD | MOE_STEP_FUSED_COMBINE_BWD |
+                MOE_STEP_PAIR_WGRAD))
     return set_error(MOE_ERR_ARG, "%s: unknown flags 0x%x", fn, flags);
+  if ((flags & MOE_STEP_PAIR_WGRAD) &&
+      (flags & (MOE_STEP_FUSED_PERMUTE | MOE_STEP_FUSED_COMBINE_BWD)))
+    return set_error(MOE_ERR_UNSUPPORTED,
+                     "%s: PAIR_WGRAD reads materialised xp and dy_p: not with FUSED_PERMUTE or "
+                     "FUSED_COMBINE_BWD", fn);
   if ((flags & MOE_STEP_EAGER_WGRAD ? 1 : 0) + (flags & MOE_STEP_SKIP_WGRAD ? 1 : 0) +
           (flags & MOE_STEP_MID_WGRAD ? 1 : 0) > 1)
     return set_error(MOE_ERR_ARG, "%s: EAGER_WGRAD, SKIP_WGRAD and MID_WGRAD exclude each other",
@@ -1063,6 +1105,9 @@ extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t 
   using namespace moe;
   g_err[0] = 0;
   if (int rc = check_step(st, flags, "moe_overlap_step")) return rc;
+  if (flags & MOE_STEP_PAIR_WGRAD)
+    return set_error(MOE_ERR_ARG, "moe_overlap_step: PAIR_WGRAD pairs consecutive steps: use "
+                                  "moe_overlap_steps");
   return step_impl(st, s0, s1, flags, nullptr);
 }
 
@@ -1074,6 +1119,7 @@ namespace moe {
 struct MultiEvents {
   hipEvent_t start, end, dwr, dw, dws;
   hipEvent_t bend[2];  // end of the backward chain of the steps of each parity
+  hipEvent_t pair;     // PAIR_WGRAD: the deferred micro-batch's dh is written
 };
 
 // One set per (host thread, device), as step_events; every wait of a call is
@@ -1085,7 +1131,8 @@ static int multi_events(MultiEvents** out) {
   if ((int)sets.size() <= dev) sets.resize(dev + 1, nullptr);
   if (!sets[dev]) {
     MultiEvents* e = new MultiEvents();
-    hipEvent_t* all[] = {&e->start, &e->end, &e->dwr, &e->dw, &e->dws, &e->bend[0], &e->bend[1]};
+    hipEvent_t* all[] = {&e->start, &e->end,     &e->dwr,     &e->dw,
+                         &e->dws,   &e->bend[0], &e->bend[1], &e->pair};
     for (hipEvent_t* p : all)
       if (hipEventCreateWithFlags(p, hipEventDisableTiming) != hipSuccess)
         return set_error(MOE_ERR_HIP, "hipEventCreateWithFlags failed");
@@ -1098,6 +1145,21 @@ static int multi_events(MultiEvents** out) {
 static bool same_mb(const moe_mb* a, const moe_mb* b) {
   if (!a || !b) return a == b;
   return a == b || memcmp(a, b, sizeof(moe_mb)) == 0;
+}
+
+// PAIR_WGRAD: whether the forward of micro-batch A writes into any buffer the
+// paired weight gradient reads from micro-batch B (xp, a, dh, dy_p, offsets).
+static bool fwd_overwrites_wgrad_inputs(const moe_mb* A, const moe_mb* B) {
+  if (!A || !B) return false;
+  const void* reads[] = {B->xp, B->a, B->dh, B->dyp, B->offsets};
+  const void* writes[] = {A->logits, A->idx,         A->gates,       A->counts, A->offsets,
+                          A->row_of_pair, A->pair_of_row, A->tile_offsets, A->xp, A->h,
+                          A->a,      A->yp,          A->out,         A->h_s,    A->a_s,
+                          A->y_s};
+  for (const void* r : reads)
+    for (const void* w : writes)
+      if (r && r == w) return true;
+  return false;
 }
 
 // The forward chain of one micro-batch on one stream (its shared expert first).
@@ -1121,8 +1183,14 @@ struct AccumOrder {
 // and records its own, so the sums happen in step order.  Only events
 // recorded in this call are waited on.
 // skip: leave the weight gradients (routed and shared) to the caller.
+// With PAIR_WGRAD, rw says what the routed experts' weight gradient does:
+// kRwOwn (B's alone), kRwDefer (none: record ev->pair once dh is written, the
+// next step pairs it) or kRwPair (B's together with prev's, the micro-batch
+// deferred by the step before, after waiting for ev->pair).
+enum { kRwOwn, kRwDefer, kRwPair };
 static int bwd_chain(const StepCtx& c, const moe_mb* B, hipStream_t q, bool mid, bool eager,
-                     bool skip, AccumOrder& ord) {
+                     bool skip, AccumOrder& ord, int rw = kRwOwn,
+                     const moe_mb* prev = nullptr) {
   const bool shared = has_shared(c);
   const bool dwr = c.router && c.st->dW_r;
   const MultiEvents* ev = ord.ev;
@@ -1131,10 +1199,21 @@ static int bwd_chain(const StepCtx& c, const moe_mb* B, hipStream_t q, bool mid,
     return MOE_OK;
   };
   auto routed_w = [&]() -> int {
+    if (rw == kRwDefer) return MOE_OK;
     TRY(wait(ev->dw, ord.dw));
-    TRY(bwd_wgrad(c, B, q));
+    if (rw == kRwPair) {
+      HIPTRY(hipStreamWaitEvent(q, ev->pair, 0));
+      TRY(bwd_wgrad_pair(c, prev, B, q));
+    } else {
+      TRY(bwd_wgrad(c, B, q));
+    }
     HIPTRY(hipEventRecord(ev->dw, q));
     ord.dw = true;
+    return MOE_OK;
+  };
+  // B's dh is written: the paired weight gradient of the next step may read it
+  auto dh_done = [&]() -> int {
+    if (rw == kRwDefer) HIPTRY(hipEventRecord(ev->pair, q));
     return MOE_OK;
   };
   auto shared_w = [&]() -> int {
@@ -1154,6 +1233,7 @@ static int bwd_chain(const StepCtx& c, const moe_mb* B, hipStream_t q, bool mid,
   }
   if (mid) {
     TRY(bwd_dgrad(c, B, false, q, kDgradAct));
+    TRY(dh_done());
     TRY(routed_w());
     TRY(bwd_dgrad(c, B, true, q, kDgradIn));
     if (shared) TRY(bwd_shared_dgrad(c, B, q));
@@ -1161,6 +1241,7 @@ static int bwd_chain(const StepCtx& c, const moe_mb* B, hipStream_t q, bool mid,
     return shared_w();
   }
   TRY(bwd_dgrad(c, B, false, q));
+  TRY(dh_done());
   if (shared) TRY(bwd_shared_dgrad(c, B, q));
   if (eager) {
     TRY(routed_w());
@@ -1219,11 +1300,32 @@ extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, h
   // SKIP_WGRAD leaves the weight gradients of the last step's backward
   // micro-batch to the caller; the earlier steps' run as usual
   const bool skip_last = (flags & MOE_STEP_SKIP_WGRAD) != 0;
-  if (serial) {
+  // PAIR_WGRAD: steps j and j + 1 (both with a backward micro-batch, the last
+  // step left out with SKIP_WGRAD) pair their routed weight gradients, from
+  // the first step on; an unpaired step keeps its own
+  const bool pair = (flags & MOE_STEP_PAIR_WGRAD) != 0;
+  std::vector<int> rw(n, kRwOwn);
+  if (pair) {
+    const int last = skip_last ? n - 1 : n;  // steps that may pair
+    for (int j = 0; j + 1 < last; ++j) {
+      if (!steps[j].bwd || !steps[j + 1].bwd) continue;
+      if (fwd_overwrites_wgrad_inputs(steps[j + 1].fwd, steps[j].bwd))
+        return set_error(MOE_ERR_ARG,
+                         "moe_overlap_steps: PAIR_WGRAD: step %d forwards into a buffer that "
+                         "the weight gradient of step %d's backward micro-batch reads in step "
+                         "%d", j + 1, j, j + 1);
+      rw[j] = kRwDefer;
+      rw[j + 1] = kRwPair;
+      ++j;
+    }
+  }
+  if (serial && !pair) {
     for (int j = 0; j < n; ++j)
       TRY(step_impl(&steps[j], s0, s0, j == n - 1 ? flags : flags & ~MOE_STEP_SKIP_WGRAD, wsW));
     return MOE_OK;
   }
+  // (serialized with PAIR_WGRAD: the same chains, all on s0, forward then
+  // backward, which is the serialized order)
   MultiEvents* ev = nullptr;
   TRY(multi_events(&ev));
   const bool mid = (flags & MOE_STEP_MID_WGRAD) != 0;
@@ -1245,7 +1347,7 @@ extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, h
     // stream owns one half of the workspace (s1 the first), so no half is
     // used by both streams at once.
     const bool even = (j & 1) == 0;
-    hipStream_t P = even ? s1 : s0, Q = even ? s0 : s1;
+    hipStream_t P = serial ? s0 : (even ? s1 : s0), Q = serial ? s0 : (even ? s0 : s1);
     char* ws = (char*)st->ws;
     char* half_s1 = ws;
     char* half_s0 = ws + one;
@@ -1264,7 +1366,8 @@ extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, h
       TRY(fwd_chain(c, st->fwd, P));
     }
     if (st->bwd) {
-      TRY(bwd_chain(c, st->bwd, Q, mid, eager, skip_last && j == n - 1, ord));
+      TRY(bwd_chain(c, st->bwd, Q, mid, eager, skip_last && j == n - 1, ord, rw[j],
+                    rw[j] == kRwPair ? steps[j - 1].bwd : nullptr));
       HIPTRY(hipEventRecord(ev->bend[j & 1], Q));
       bend_rec[j & 1] = true;
     }

@@ -808,7 +808,10 @@ struct DgradInOp {
 // operand's row k is token rows_of[r0 + k] / K of the token matrix; each
 // chunk's token is loaded one stage ahead (when the chunk is loaded for the
 // stage before), and a row past the expert's end gets an offset past the
-// resource, which reads as zero.
+// resource, which reads as zero.  A direct operand may have a second
+// segment (second()): stages from row kB on read rows k - kB of another
+// operand's expert rows (the paired weight gradient: one reduction over two
+// micro-batches' rows, each segment padded with zero rows to whole stages).
 template <bool CAN_GATHER, int NT = 512>
 struct WgLoad {
   static constexpr int CH = 64 * 32 / NT;  // 16-byte chunks per thread and stage
@@ -824,6 +827,8 @@ struct WgLoad {
   const int32_t* rows_of;
   int r0, K, trow;
   int tok_next[CH];  // rows_of value of each chunk's row in the next stage loaded (-1: none)
+  const uint16_t* base2;  // second segment (direct operands): its expert's first row
+  int rows2, kB;          // its rows, and the first stage row that reads it
 
   __device__ __forceinline__ void init(const uint16_t* src, long ld_, int m0, int r0_, int r1,
                                        bool gathered, const int32_t* xrows, int K_, int tid) {
@@ -848,6 +853,12 @@ struct WgLoad {
       base = src + (size_t)r0_ * ld_;
       voff = (uint32_t)trow * (uint32_t)(ld_ * 2) + coff;
     }
+    kB = 0x7fffffff;
+  }
+  __device__ __forceinline__ void second(const uint16_t* src, int r0_, int r1, int kB_) {
+    base2 = src + (size_t)r0_ * ld;
+    rows2 = r1 - r0_;
+    kB = kB_;
   }
   // rows_of value of chunk c's row in stage k0 (-1 past the expert's end)
   __device__ __forceinline__ int token(int k0, int c) const {
@@ -863,9 +874,12 @@ struct WgLoad {
       v[c] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off, 0, 0);
     } else {
       if (c == 0) {
-        const long left = (long)(rows - k0) * ld * 2;
+        const bool sec = k0 >= kB;  // block-uniform
+        const uint16_t* b = sec ? base2 : base;
+        const int k = sec ? k0 - kB : k0;
+        const long left = (long)((sec ? rows2 : rows) - k) * ld * 2;
         const int nrec = left <= 0 ? 0 : (left > 0x7fffffffL ? 0x7fffffff : (int)left);
-        rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)k0 * ld), (short)0, nrec,
+        rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(b + (size_t)k * ld), (short)0, nrec,
                                                  0x00020000);
       }
       v[c] = __builtin_amdgcn_raw_buffer_load_b128(
@@ -914,13 +928,22 @@ __device__ __forceinline__ long long uniform64(long long v) {
 //
 // ACC: add into the existing values of dW (gradient accumulation) instead of
 // overwriting them.
-template <bool GATHER, class E, bool ROUTER, bool ACC, bool GD = false>
+// PAIR (the paired weight gradient, with neither gather): the reduction of
+// every tile runs over the expert's rows of a second micro-batch too (sec:
+// its xp, a, dh, dy_p and offsets), after the first one's, in one float32
+// accumulation, so dW is read and written once for both.
+struct WgSecond {
+  const uint16_t *xp, *abuf, *dh, *dyp;
+  const int32_t* offsets;
+};
+template <bool GATHER, class E, bool ROUTER, bool ACC, bool GD = false, bool PAIR = false>
 __global__ __launch_bounds__(512) void wgrad_kernel(
     const uint16_t* __restrict__ xp, const int32_t* __restrict__ xrows, int K,
     const uint16_t* __restrict__ abuf, const uint16_t* __restrict__ dh,
     const uint16_t* __restrict__ dyp, const int32_t* __restrict__ offsets,
     float* __restrict__ dW_gu, float* __restrict__ dW_down, int E_l, int d, int F,
-    int rchunk = 0, int rows = 0) {
+    int rchunk = 0, int rows = 0, WgSecond sec = WgSecond{}) {
+  static_assert(!PAIR || !(GATHER || GD || ROUTER), "the paired wgrad reads direct operands");
   using TL = T256;
   constexpr int WTM = TL::WTM, WTN = TL::WTN, TM = TL::TM, TN = TL::TN;
   __shared__ __attribute__((aligned(16))) uint16_t smem[TL::LDS_ELEMS];
@@ -928,8 +951,14 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
   const int tdm = (d + 255) / 256, tdn = (F + 255) / 256;
   const int tgm = (2 * F + 255) / 256, tgn = (d + 255) / 256;
   const int per_e = tdm * tdn + (ROUTER ? 0 : tgm * tgn);
-  // first row of expert (or token chunk) e
+  // first row of expert (or token chunk) e; with PAIR, of the second
+  // micro-batch's expert e too
   auto off = [&](int e) { return ROUTER ? min(e * rchunk, rows) : offsets[e]; };
+  auto off2 = [&](int e) { return PAIR ? sec.offsets[e] : 0; };
+  // stages of expert e: each segment padded to whole stages
+  auto stages = [&](int e) {
+    return (off(e + 1) - off(e) + BK - 1) / BK + (off2(e + 1) - off2(e) + BK - 1) / BK;
+  };
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w / TL::WGN, wn = w % TL::WGN;
@@ -943,7 +972,7 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
     long long acc_it = 0;
     for (int e = 0; e < E_l; ++e) {
       s_it[e] = acc_it;
-      const int nk = (off(e + 1) - off(e) + BK - 1) / BK;
+      const int nk = stages(e);
       acc_it += (long long)per_e * (nk > 0 ? nk : 1);
     }
     s_it[E_l] = acc_it;
@@ -973,6 +1002,9 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
     int r0, r1, M, N, m0, n0, nk;
     const uint16_t *Asrc, *Bsrc;
     float* out;
+    // PAIR: the second micro-batch's rows and operands, from stage row kB on
+    int r0b, r1b, kB;
+    const uint16_t *Asrc2, *Bsrc2;
   };
   auto job = [&](long long gt) {
     TileJob j{};
@@ -988,12 +1020,17 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
     j.valid = true;
     j.r0 = off(e);
     j.r1 = off(e + 1);
-    j.nk = (j.r1 - j.r0 + BK - 1) / BK;
+    j.nk = stages(e);
+    j.r0b = off2(e);
+    j.r1b = off2(e + 1);
+    j.kB = (j.r1 - j.r0 + BK - 1) / BK * BK;
     if (t < tdm * tdn) {
       j.ga = GD;
       j.gb = false;
       j.Asrc = dyp;
       j.Bsrc = abuf;
+      j.Asrc2 = sec.dyp;
+      j.Bsrc2 = sec.abuf;
       j.M = d;
       j.N = F;
       j.m0 = (t / tdn) * 256;
@@ -1003,6 +1040,8 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
       t -= tdm * tdn;
       j.Asrc = dh;
       j.Bsrc = xp;
+      j.Asrc2 = sec.dh;
+      j.Bsrc2 = sec.xp;
       j.ga = false;
       j.gb = GATHER;
       j.M = 2 * F;
@@ -1022,6 +1061,10 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
   auto init_loaders = [&](const TileJob& c) {
     la.init(c.Asrc, c.M, c.m0, c.r0, c.r1, c.ga, xrows, K, tid);
     lb.init(c.Bsrc, c.N, c.n0, c.r0, c.r1, c.gb, xrows, K, tid);
+    if constexpr (PAIR) {
+      la.second(c.Asrc2, c.r0b, c.r1b, c.kB);
+      lb.second(c.Bsrc2, c.r0b, c.r1b, c.kB);
+    }
   };
   long long gt = gt0 + slot;
   TileJob cur = job(gt);
@@ -1355,6 +1398,29 @@ void wgrad_t(const moe_shape* s, const void* xp, const int32_t* xrows, const voi
   }
 }
 
+// The paired weight gradient of two micro-batches (same shape): one launch
+// whose reduction runs over both micro-batches' rows of each expert.
+template <class E>
+void wgrad_pair_t(const moe_shape* s, const WgrOps& A, const WgrOps& B, float* dW_gu,
+                  float* dW_down, bool accumulate, hipStream_t st) {
+  const int d = (int)s->d, F = (int)s->F, E_l = (int)s->E_l;
+  const long per_e = (long)((d + 255) / 256) * ((F + 255) / 256) +
+                     (long)((2 * F + 255) / 256) * ((d + 255) / 256);
+  const int grid = persistent_grid(E_l * per_e);
+  const WgSecond sec{(const uint16_t*)B.xp, (const uint16_t*)B.a, (const uint16_t*)B.dh,
+                     (const uint16_t*)B.dyp, B.offsets};
+  auto go = [&](auto acc) {
+    MOE_LAUNCH("wgrad", st,
+               (wgrad_kernel<false, E, false, decltype(acc)::value, false, true>
+                <<<grid, 512, 0, st>>>((const uint16_t*)A.xp, nullptr, (int)s->K,
+                                       (const uint16_t*)A.a, (const uint16_t*)A.dh,
+                                       (const uint16_t*)A.dyp, A.offsets, dW_gu, dW_down, E_l, d,
+                                       F, 0, 0, sec)));
+  };
+  if (accumulate) go(std::true_type{});
+  else go(std::false_type{});
+}
+
 template <class E>
 void router_t(const moe_shape* s, const void* x, const void* W_rT, const float* bias,
               float* logits, float* partial, hipStream_t st) {
@@ -1416,6 +1482,13 @@ int launch_ffn_wgrad_mfma(const moe_shape* s, const void* xp, const int32_t* xro
   else
     wgrad_t<BF16>(s, xp, xrows, a, dh, dyp, offsets, dW_gu, dW_down, accumulate, st, dyrows);
   return check_launch("wgrad GEMM");
+}
+
+int launch_ffn_wgrad_pair_mfma(const moe_shape* s, const WgrOps& A, const WgrOps& B,
+                               float* dW_gu, float* dW_down, bool accumulate, hipStream_t st) {
+  if (s->dtype == MOE_F16) wgrad_pair_t<F16>(s, A, B, dW_gu, dW_down, accumulate, st);
+  else wgrad_pair_t<BF16>(s, A, B, dW_gu, dW_down, accumulate, st);
+  return check_launch("paired wgrad GEMM");
 }
 
 int launch_router_wgrad_mfma(const moe_shape* s, const void* x, const void* dl_split,

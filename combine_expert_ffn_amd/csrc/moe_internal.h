@@ -282,5 +282,17 @@ int launch_ffn_wgrad(const moe_shape* s, const void* xp, const int32_t* xrows, c
                      const void* dh, const void* dyp, const int32_t* offsets, float* dW_gu,
                      float* dW_down, bool accumulate, hipStream_t st,
                      const int32_t* dyrows = nullptr);
+// The operands of one micro-batch's weight gradient (materialised xp and dy_p).
+struct WgrOps {
+  const void *xp, *a, *dh, *dyp;
+  const int32_t* offsets;
+};
+// The paired weight gradient: dW (+)= the weight gradients of micro-batches A
+// and B, reduced over both one's rows of each expert in one accumulation, so
+// dW is read and written once.
+int launch_ffn_wgrad_pair(const moe_shape* s, const WgrOps& A, const WgrOps& B, float* dW_gu,
+                          float* dW_down, bool accumulate, hipStream_t st);
+int launch_ffn_wgrad_pair_mfma(const moe_shape* s, const WgrOps& A, const WgrOps& B,
+                               float* dW_gu, float* dW_down, bool accumulate, hipStream_t st);
 
 }  // namespace moe

@@ -110,6 +110,13 @@ extern "C" {
                                    unfused path within the numeric tolerance (the
                                    gate is applied in float32 instead of through a
                                    rounded dy_p), not bit for bit               */
+#define MOE_STEP_PAIR_WGRAD 64 /* moe_overlap_steps: the routed experts' weight
+                                 gradients of steps 2i and 2i + 1 in one launch
+                                 (moe_ffn_wgrad_pair) in step 2i + 1: step 2i's
+                                 backward micro-batch must stay intact until
+                                 then (step 2i + 1 may not forward into its
+                                 buffers); not with the fused permute or the
+                                 fused combine backward */
 
 /*
  * Layer shape.  T tokens of hidden size d; E experts routed over, of which the
@@ -288,6 +295,27 @@ int moe_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h,
 int moe_ffn_wgrad(const moe_shape* s, const void* xp, const void* a,
                   const void* dh, const void* dyp, const int32_t* offsets,
                   float* dW_gu, float* dW_down, int accumulate, hipStream_t stream);
+
+/*
+ * moe_ffn_wgrad_pair - the weight gradients of two micro-batches of one shape
+ * in one launch: the deferred W (page 1, delay_wgrad_compute) of one
+ * micro-batch issued together with the next one's.  For each expert the
+ * reduction runs over micro-batch A's rows (xp, a, dh, dyp, offsets), then
+ * B's (xp2, a2, dh2, dyp2, offsets2), in one float32 accumulation:
+ *   dW_down[j] (+)= sum_{r in A} dyp[r] (outer) a[r] + sum_{r in B} dyp2[r] (outer) a2[r]
+ *   dW_gu[j]   (+)= sum_{r in A} dh[r] (outer) xp[r] + sum_{r in B} dh2[r] (outer) xp2[r]
+ * so dW is read and written once for both (with gradient accumulation, half
+ * the weight-gradient traffic of two moe_ffn_wgrad calls).  The sum equals
+ * two moe_ffn_wgrad calls up to float32 rounding order, not bit for bit.
+ * accumulate as moe_ffn_wgrad.  Layouts and sizes as moe_ffn_wgrad, for each
+ * micro-batch.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ARG (unknown
+ * accumulate bits).
+ */
+int moe_ffn_wgrad_pair(const moe_shape* s, const void* xp, const void* a, const void* dh,
+                       const void* dyp, const int32_t* offsets, const void* xp2,
+                       const void* a2, const void* dh2, const void* dyp2,
+                       const int32_t* offsets2, float* dW_gu, float* dW_down, int accumulate,
+                       hipStream_t stream);
 
 /*
  * moe_ffn_wgrad_gather - moe_ffn_wgrad with the fused permute: dW_gu reads

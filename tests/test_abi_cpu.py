@@ -189,10 +189,14 @@ def test_modes_and_flags_rejected():
                            None, 0, None, 0, None) == M.MOE_ERR_UNSUPPORTED
     assert L.moe_ffn_wgrad(C.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8,
                            None) == M.MOE_ERR_ARG
+    # the paired weight gradient: unknown accumulate bits, a missing operand
+    assert L.moe_ffn_wgrad_pair(C.byref(s), *([FAKE] * 12), 8, None) == M.MOE_ERR_ARG
+    assert L.moe_ffn_wgrad_pair(C.byref(s), *([FAKE] * 6), None, *([FAKE] * 5), 0,
+                                None) == M.MOE_ERR_NULL
     st = _lib.MoeStep()
     st.shape = s
     st.route_mode = M.MOE_ROUTE_FORCE_BALANCE
-    assert L.moe_overlap_step(C.byref(st), None, None, 64) == M.MOE_ERR_ARG
+    assert L.moe_overlap_step(C.byref(st), None, None, 128) == M.MOE_ERR_ARG
     st.route_mode = 5
     assert L.moe_overlap_step(C.byref(st), None, None, 0) == M.MOE_ERR_ARG
     st.route_mode = M.MOE_ROUTE_FORCE_BALANCE

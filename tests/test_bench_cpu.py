@@ -1,5 +1,7 @@
 """bench.py's timing plan (host logic, no GPU): any --steps K is timed exactly,
-as replays of an even-length graph of steps plus at most one eager step."""
+as replays of a graph whose length is a multiple of the unit (2 steps; 6 with
+the paired weight gradient over three buffer sets) plus fewer than a unit of
+eager steps."""
 
 import os
 import sys
@@ -18,5 +20,18 @@ def test_group_plan_covers_every_step_count():
                 continue
             assert g % 2 == 0 and 2 <= g <= 2 * G0, (G0, K, g)
             assert rem in (0, 1) and (K - rem) % g == 0 and K - rem >= g, (G0, K, g, rem)
+            if K % G0 == 0:
+                assert (g, rem) == (G0, 0), (G0, K, g, rem)
+
+
+def test_group_plan_paired_unit():
+    for G0 in (6, 12, 24):
+        for K in range(1, 201):
+            g, rem = bench.group_plan(K, G0, 6)
+            if g is None:
+                assert rem == K and K < 6, (G0, K)
+                continue
+            assert g % 6 == 0 and 6 <= g <= 2 * G0, (G0, K, g)
+            assert 0 <= rem < 6 and (K - rem) % g == 0 and K - rem >= g, (G0, K, g, rem)
             if K % G0 == 0:
                 assert (g, rem) == (G0, 0), (G0, K, g, rem)
