@@ -264,16 +264,19 @@ struct TrFrags {
   static constexpr bool NSIDE = true;
   int rb[2], u[2];  // per half: row byte base + 8 (t % 4), chunk XOR term
   int wm, wn;
-  __device__ __forceinline__ void init(int wm_, int wn_, int lane) {
-    wm = wm_;
-    wn = wn_;
+  __device__ __forceinline__ static void terms(int lane, int (&r)[2], int (&x)[2]) {
     const int g = lane >> 4, t = lane & 15;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int kr = ((g >> 1) << 3) + (t >> 2) + 4 * h;
-      rb[h] = kr * WG_ROWB + ((t & 3) << 3);
-      u[h] = (g & 1) ^ wg_swz(kr);
+      r[h] = kr * WG_ROWB + ((t & 3) << 3);
+      x[h] = (g & 1) ^ wg_swz(kr);
     }
+  }
+  __device__ __forceinline__ void init(int wm_, int wn_, int lane) {
+    wm = wm_;
+    wn = wn_;
+    if constexpr (HOIST) terms(lane, rb, u);
   }
   __device__ __forceinline__ static bf16x8_t frag(const uint16_t* tile, int cb, int kk,
                                                   const int (&rb)[2], const int (&u)[2]) {
@@ -289,10 +292,15 @@ struct TrFrags {
   template <class>
   __device__ __forceinline__ void read(Frags<TL>& f, const uint16_t* A, const uint16_t* B, int kk,
                                        int, int, int) const {
-    // without HOIST the per-lane terms pass through an empty asm, so the
-    // addresses cannot be hoisted out of the main loop
+    // without HOIST the per-lane terms are recomputed here from the lane
+    // index, made opaque by an empty asm, so neither they nor the addresses
+    // occupy registers across the main loop
     int r[2] = {rb[0], rb[1]}, x[2] = {u[0], u[1]};
-    if constexpr (!HOIST) asm volatile("" : "+v"(r[0]), "+v"(r[1]), "+v"(x[0]), "+v"(x[1]));
+    if constexpr (!HOIST) {
+      int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+      asm volatile("" : "+v"(lane));
+      terms(lane, r, x);
+    }
 #pragma unroll
     for (int j = 0; j < TL::TN; ++j) f.b[j] = frag(B, wn * TL::WTN + j * 32, kk, r, x);
 #pragma unroll
@@ -817,73 +825,86 @@ struct WgLoad {
   static constexpr int CH = 64 * 32 / NT;  // 16-byte chunks per thread and stage
   static constexpr int NLOAD = CH, NSTORE = CH;
   u32x4_t v[CH];  // the stage in flight
-  __amdgpu_buffer_rsrc_t rsrc;
-  const uint16_t* base;  // direct: the expert's first row; gathered: the token matrix
-  long ld;               // elements per operand row
-  int rows;              // rows of the expert
-  uint32_t voff;         // byte offset of chunk 0 within a stage (direct) / a row (gathered)
-  int dst0;              // byte offset of chunk 0 in an LDS tile
+  __amdgpu_buffer_rsrc_t rsrc;  // direct: the current stage's rows
+  const uint16_t* base;         // direct: the expert's first row
+  long ld;                      // elements per operand row
+  int rows;                     // rows of the expert
+  uint32_t voff;                // direct: byte offset of chunk 0 within a stage
+  int dst0;                     // byte offset of chunk 0 in an LDS tile
+  const uint16_t* base2;        // second segment (direct operands): its expert's first row
+  int rows2, kB;                // its rows, and the first stage row that reads it
+  // CAN_GATHER: with gat set (block-uniform) the operand is gathered.  The
+  // gathered and the direct offset are both formed and one is selected, so
+  // the chunk loads have no branch (a branch around them costs a full wait
+  // for every outstanding load where the paths merge).
   bool gat;
-  const int32_t* rows_of;
+  __amdgpu_buffer_rsrc_t rsrc_g;  // the token matrix
+  __amdgpu_buffer_rsrc_t rtok;    // rows_of entries [0, n_rows)
+  uint32_t coff;                  // byte offset of this thread's columns within a row
   int r0, K, trow;
-  int tok_next[CH];  // rows_of value of each chunk's row in the next stage loaded (-1: none)
-  const uint16_t* base2;  // second segment (direct operands): its expert's first row
-  int rows2, kB;          // its rows, and the first stage row that reads it
+  // rows_of value of each chunk's row in the next stage loaded (a vector, so
+  // that it stays in registers)
+  typedef int i32xCH_t __attribute__((ext_vector_type(CH)));
+  i32xCH_t tok_next;
 
   __device__ __forceinline__ void init(const uint16_t* src, long ld_, int m0, int r0_, int r1,
-                                       bool gathered, const int32_t* xrows, int K_, int tid) {
+                                       bool gathered, const int32_t* xrows, int K_, int tid,
+                                       int n_rows = 0) {
     ld = ld_;
     rows = r1 - r0_;
     trow = tid >> 5;
-    const uint32_t coff = (uint32_t)(m0 + 8 * (tid & 31)) * 2u;
+    coff = (uint32_t)(m0 + 8 * (tid & 31)) * 2u;
     dst0 = wg_byte(trow, 8 * (tid & 31));
+    base = src + (size_t)r0_ * ld_;
+    voff = (uint32_t)trow * (uint32_t)(ld_ * 2) + coff;
+    kB = 0x7fffffff;
     gat = CAN_GATHER && gathered;
-    if (CAN_GATHER && gat) {
-      base = src;
-      voff = coff;
-      rows_of = xrows;
-      r0 = r0_;
-      K = K_;
+    if constexpr (CAN_GATHER) {
       // every token is a row of the matrix; only the past-the-end marker
       // exceeds the records limit
-      rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, 0x7fffffff, 0x00020000);
+      rsrc_g = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, 0x7fffffff, 0x00020000);
+      rtok = __builtin_amdgcn_make_buffer_rsrc((void*)xrows, (short)0, n_rows * 4, 0x00020000);
+      r0 = r0_;
+      K = K_;
 #pragma unroll
       for (int c = 0; c < CH; ++c) tok_next[c] = token(0, c);
-    } else {
-      base = src + (size_t)r0_ * ld_;
-      voff = (uint32_t)trow * (uint32_t)(ld_ * 2) + coff;
     }
-    kB = 0x7fffffff;
   }
   __device__ __forceinline__ void second(const uint16_t* src, int r0_, int r1, int kB_) {
     base2 = src + (size_t)r0_ * ld;
     rows2 = r1 - r0_;
     kB = kB_;
   }
-  // rows_of value of chunk c's row in stage k0 (-1 past the expert's end)
+  // rows_of value of chunk c's row in stage k0, read without a branch at an
+  // index clamped into the expert's rows (for an expert with none, index
+  // r0 - 1, past the resource when r0 = 0, which reads 0); whether the row
+  // exists is decided where the value is used
   __device__ __forceinline__ int token(int k0, int c) const {
-    const int k = k0 + c * 16 + trow;
-    return k < rows ? rows_of[r0 + k] : -1;
+    const int k = min(k0 + c * 16 + trow, rows - 1);
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(rtok, (r0 + k) * 4, 0, 0);
   }
   __device__ __forceinline__ void load_c(int c, int k0) {
-    if (CAN_GATHER && gat) {
+    if (c == 0) {  // the direct resource of stage k0
+      const bool sec = k0 >= kB;  // block-uniform
+      const uint16_t* b = sec ? base2 : base;
+      const int k = sec ? k0 - kB : k0;
+      const long left = (long)((sec ? rows2 : rows) - k) * ld * 2;
+      const int nrec = left <= 0 ? 0 : (left > 0x7fffffffL ? 0x7fffffff : (int)left);
+      rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(b + (size_t)k * ld), (short)0, nrec,
+                                               0x00020000);
+    }
+    const uint32_t off_d = voff + (uint32_t)(c * 16) * (uint32_t)(ld * 2);
+    if constexpr (CAN_GATHER) {
+      // the token is consumed before the next one is loaded into its
+      // register, so that load needs no copy (and no wait)
       const int t = tok_next[c];
+      const uint32_t row_off = ((unsigned)t / (unsigned)K) * (uint32_t)(ld * 2) + coff;
+      const uint32_t off_g = k0 + c * 16 + trow < rows ? row_off : 0x80000000u;
+      v[c] = __builtin_amdgcn_raw_buffer_load_b128(gat ? rsrc_g : rsrc, (int)(gat ? off_g : off_d),
+                                                   0, 0);
       tok_next[c] = token(k0 + 64, c);
-      const uint32_t off =
-          t >= 0 ? (uint32_t)((unsigned)t / (unsigned)K) * (uint32_t)(ld * 2) + voff : 0x80000000u;
-      v[c] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off, 0, 0);
     } else {
-      if (c == 0) {
-        const bool sec = k0 >= kB;  // block-uniform
-        const uint16_t* b = sec ? base2 : base;
-        const int k = sec ? k0 - kB : k0;
-        const long left = (long)((sec ? rows2 : rows) - k) * ld * 2;
-        const int nrec = left <= 0 ? 0 : (left > 0x7fffffffL ? 0x7fffffff : (int)left);
-        rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(b + (size_t)k * ld), (short)0, nrec,
-                                                 0x00020000);
-      }
-      v[c] = __builtin_amdgcn_raw_buffer_load_b128(
-          rsrc, (int)(voff + (uint32_t)(c * 16) * (uint32_t)(ld * 2)), 0, 0);
+      v[c] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off_d, 0, 0);
     }
   }
   __device__ __forceinline__ void store_c(int c, uint16_t* lds) const {
@@ -1054,13 +1075,15 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
   };
   // the gathering variants hold token registers: addresses formed per read
   using FR = TrFrags<TL, !(GATHER || GD)>;
+  // dispatched rows (the token lists' extent)
+  const int n_rows = (GATHER || GD) ? __builtin_amdgcn_readfirstlane(off(E_l)) : 0;
   FR fr;
   fr.init(wm, wn, lane);
   WgLoad<GD> la;
   WgLoad<GATHER> lb;
   auto init_loaders = [&](const TileJob& c) {
-    la.init(c.Asrc, c.M, c.m0, c.r0, c.r1, c.ga, xrows, K, tid);
-    lb.init(c.Bsrc, c.N, c.n0, c.r0, c.r1, c.gb, xrows, K, tid);
+    la.init(c.Asrc, c.M, c.m0, c.r0, c.r1, c.ga, xrows, K, tid, n_rows);
+    lb.init(c.Bsrc, c.N, c.n0, c.r0, c.r1, c.gb, xrows, K, tid, n_rows);
     if constexpr (PAIR) {
       la.second(c.Asrc2, c.r0b, c.r1b, c.kB);
       lb.second(c.Bsrc2, c.r0b, c.r1b, c.kB);
@@ -1142,7 +1165,9 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
     };
     constexpr int NP = TM * TN;  // pieces
     constexpr int NS = 4;        // LDS slots per wave
-    if constexpr (!ROUTER) {
+    if constexpr (ROUTER) next_stage0();
+    // the router's N = 2E need not be a multiple of 4 (block-uniform)
+    if (!ROUTER || (N & 3) == 0) {
       // N is a multiple of 4: a chunk of four columns lies wholly inside or
       // past it.  With ACC, pieces 0..NS-1 first go to their LDS slots, which
       // frees their registers for the previous values of PF pieces, all
@@ -1165,7 +1190,7 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
         for (int pc = 0; pc < NS; ++pc) ep_write(pc / TN, pc % TN, pc);
 #pragma unroll
         for (int pc = 0; pc < PF; ++pc) load_piece(pc);
-      } else {
+      } else if constexpr (!ROUTER) {
         next_stage0();
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -1192,9 +1217,7 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
-      // the router's N = 2E need not be a multiple of 4: 4-byte stores, each
-      // column checked
-      next_stage0();
+      // 4-byte stores, each column checked
 #pragma unroll
       for (int pc = 0; pc < NP; ++pc) {
         const int i = pc / TN, j = pc % TN;
