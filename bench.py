@@ -382,8 +382,9 @@ def main():
                     help="pair the routed experts' weight gradients of consecutive steps "
                          "(MOE_STEP_PAIR_WGRAD: one launch per two steps, dW read and written "
                          "once for both; three micro-batch buffer sets); not with the fused "
-                         "paths.  Off by default: its one graph-captured run ended in a host "
-                         "fault whose cause is not found")
+                         "paths, and with --graph off only (the library rejects paired steps "
+                         "under stream capture: a captured run ended in a host crash whose "
+                         "cause is not found)")
     ap.add_argument("--group", type=int, default=None,
                     help="steps per moe_overlap_steps call and per captured graph: a "
                          "multiple of 2, of 6 with --pair-wgrad on (default 10, 12)")
@@ -446,6 +447,9 @@ def main():
     unit = 6 if pairing else 2  # buffer-set rotation (3 or 2) x paired steps (2)
     if args.group is None:
         args.group = 12 if pairing else 10
+    if pairing and args.graph == "on":
+        err("bench.py: --pair-wgrad on needs --graph off (paired steps are not captured)")
+        sys.exit(2)
     if args.group < unit or args.group % unit:
         err(f"bench.py: --group must be a multiple of {unit}")
         sys.exit(2)
@@ -534,12 +538,15 @@ def main():
     # ---- overlapped against serialized, alternated (A/B) after the timed
     # region, as graph replays and as eager launches
     G = args.group
-    o_g, s_g = overlap_ab(L, G, args.ab_rounds, graph=True)
-    err(f"[bench] A/B graph replays: overlapped {o_g:.4f} / serialized {s_g:.4f} ms/step "
-        f"-> x{s_g / o_g:.3f}")
+    if args.graph == "on":
+        o_g, s_g = overlap_ab(L, G, args.ab_rounds, graph=True)
+        err(f"[bench] A/B graph replays: overlapped {o_g:.4f} / serialized {s_g:.4f} ms/step "
+            f"-> x{s_g / o_g:.3f}")
     o_e, s_e = overlap_ab(L, G, args.ab_rounds, graph=False)
     err(f"[bench] A/B eager: overlapped {o_e:.4f} / serialized {s_e:.4f} ms/step "
         f"-> x{s_e / o_e:.3f}")
+    if args.graph != "on":  # no graphs: the eager comparison stands for both
+        o_g, s_g = o_e, s_e
 
     # ---- per-kernel times: serialized steps with every kernel bracketed by
     # HIP events on its stream (no concurrency, so each kernel's interval is
@@ -562,8 +569,9 @@ def main():
         w4 = WORKLOADS[args.overlap_workload]
         L4 = Layer(w4, args, s0, s1)
         L4.issue(args.warmup, 0)
-        o4, s4 = overlap_ab(L4, G, args.ab_rounds, graph=True)
         o4e, s4e = overlap_ab(L4, G, args.ab_rounds, graph=False)
+        o4, s4 = (overlap_ab(L4, G, args.ab_rounds, graph=True) if args.graph == "on"
+                  else (o4e, s4e))
         c4 = {"workload": w4.name, "T": w4.T, "E": w4.E, "K": w4.K, "routing": w4.route,
               "overlapped_ms_per_step": round(o4, 4), "serialized_ms_per_step": round(s4, 4),
               "overlap_speedup": round(s4 / o4, 4),

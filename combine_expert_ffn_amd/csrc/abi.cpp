@@ -1284,6 +1284,16 @@ extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, h
       return set_error(MOE_ERR_ARG,
                        "moe_overlap_steps: step %d has other expert weights than step 0", j);
   }
+  if (flags & MOE_STEP_PAIR_WGRAD) {
+    // A graph-captured run of paired steps ended in a host crash whose cause
+    // is not known: paired steps are issued eagerly only.
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s0, &cs) != hipSuccess)
+      return set_error(MOE_ERR_HIP, "moe_overlap_steps: hipStreamIsCapturing failed");
+    if (cs != hipStreamCaptureStatusNone)
+      return set_error(MOE_ERR_UNSUPPORTED,
+                       "moe_overlap_steps: PAIR_WGRAD is not supported under stream capture");
+  }
   // The expert weights are the same for every step of the call, so the
   // dgrad's transposed copies of them are made once, at the start, into the
   // first half of the workspace, and every step's dgrad on either stream reads

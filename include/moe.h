@@ -116,7 +116,8 @@ extern "C" {
                                  backward micro-batch must stay intact until
                                  then (step 2i + 1 may not forward into its
                                  buffers); not with the fused permute or the
-                                 fused combine backward */
+                                 fused combine backward, and not under stream
+                                 capture (MOE_ERR_UNSUPPORTED) */
 
 /*
  * Layer shape.  T tokens of hidden size d; E experts routed over, of which the

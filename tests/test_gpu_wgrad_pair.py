@@ -9,8 +9,8 @@ moe_overlap_steps.
   paired steps serialized, and equal within float32 rounding to the unpaired
   steps;
 * the checks: pairing needs the micro-batch back-propagated in step j intact
-  in step j + 1, moe_overlap_step rejects the flag, the fused paths are not
-  supported with it.
+  in step j + 1, moe_overlap_step rejects the flag, the fused paths and
+  stream capture are not supported with it.
 """
 
 import numpy as np
@@ -185,3 +185,25 @@ def test_pair_steps_checks():
         M.moe_overlap_steps(steps, s0, s1, M.MOE_STEP_PAIR_WGRAD | M.MOE_STEP_FUSED_PERMUTE)
     assert e.value.code == M.MOE_ERR_UNSUPPORTED
     torch.cuda.synchronize()
+    # paired steps are issued eagerly only: under stream capture the call
+    # returns the error before it issues anything (the graph holds only the
+    # fill around it)
+    m3 = m2 + [M.MicroBatch(s, x=D(inp["x"][::-1].copy()), dout=D(inp["dout"][::-1].copy()))]
+    steps3 = _steps(s, w, m3, W, dW, ws, 4, W_r, None, 3)
+    probe = torch.zeros(64, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(s0)
+    codes = []
+    with torch.cuda.graph(g, stream=cap, capture_error_mode="thread_local"):
+        probe.add_(1.0)
+        try:
+            M.moe_overlap_steps(steps3, torch.cuda.current_stream(), s1, M.MOE_STEP_PAIR_WGRAD)
+        except M.MoeError as err:
+            codes.append(err.code)
+        probe.add_(1.0)
+    torch.cuda.synchronize()
+    assert codes == [M.MOE_ERR_UNSUPPORTED]
+    g.replay()
+    torch.cuda.synchronize()
+    assert float(probe[0]) == 2.0
