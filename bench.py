@@ -244,6 +244,7 @@ class Layer:
                               device="cuda")
         self.fused = args.fused_permute == "on"
         self.fcb = args.fused_combine_bwd == "on"
+        self.scatter = args.fused_scatter == "on"
         # the paired weight gradient keeps the micro-batch back-propagated in
         # step j until step j + 1: three buffer sets in rotation
         self.pair = (args.pair_wgrad == "on" and args.pipeline == "on" and
@@ -255,6 +256,7 @@ class Layer:
         # backward stream's order (both leave the results unchanged)
         self.FLAGS = ((M.MOE_STEP_FUSED_PERMUTE if self.fused else 0) |
                       (M.MOE_STEP_FUSED_COMBINE_BWD if self.fcb else 0) |
+                      (M.MOE_STEP_FUSED_SCATTER if self.scatter else 0) |
                       (M.MOE_STEP_MID_WGRAD if args.wgrad_order == "mid" else 0) |
                       (M.MOE_STEP_PAIR_WGRAD if self.pair else 0))
         self.shared = None
@@ -370,6 +372,10 @@ def main():
                     help="fuse the combine backward into the expert GEMMs "
                          "(MOE_STEP_FUSED_COMBINE_BWD): no dy_p; dgrad and wgrad read the dout "
                          "rows through the dispatch plan and apply the gates")
+    ap.add_argument("--fused-scatter", choices=("on", "off"), default="off",
+                    help="fuse the unpermute into GEMM2 (MOE_STEP_FUSED_SCATTER): its epilogue "
+                         "writes y by (token, slot) pair, so the combine and its backward read "
+                         "each token's rows as one run (bit-identical results)")
     ap.add_argument("--wgrad-order", choices=("mid", "last"), default="mid",
                     help="where the backward micro-batch's wgrad runs on its stream: between the "
                          "two dgrad GEMMs (mid, MOE_STEP_MID_WGRAD) or after the dispatch "
@@ -655,6 +661,8 @@ def main():
                                 "alternating" if L.pipelined else
                                 "one moe_overlap_step per step, joined at each boundary"),
                    "permute": "fused into GEMM1 and wgrad" if L.fused else "separate kernel",
+                   "y_layout": ("by (token, slot) pair, scattered by GEMM2's epilogue"
+                                if L.scatter else "by dispatched row"),
                    "combine_backward": ("fused into dgrad and wgrad (no dy_p)" if L.fcb
                                         else "separate kernel writing dy_p"),
                    "shared_expert_F": w.F_s},

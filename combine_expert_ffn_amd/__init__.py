@@ -17,7 +17,7 @@ from ._lib import (  # noqa: F401
     MOE_ERR_UNSUPPORTED, MOE_ERR_ARG, MOE_F32, MOE_BF16, MOE_F16, MOE_ROUTE_TOPK,
     MOE_ROUTE_TOPK_FROM_LOGITS, MOE_ROUTE_FORCE_BALANCE, MOE_ACCUM_DX, MOE_ACCUM_DW,
     MOE_STEP_SERIALIZE, MOE_STEP_EAGER_WGRAD, MOE_STEP_SKIP_WGRAD, MOE_STEP_FUSED_PERMUTE,
-    MOE_STEP_MID_WGRAD, MOE_STEP_FUSED_COMBINE_BWD, MOE_STEP_PAIR_WGRAD,
+    MOE_STEP_MID_WGRAD, MOE_STEP_FUSED_COMBINE_BWD, MOE_STEP_PAIR_WGRAD, MOE_STEP_FUSED_SCATTER,
 )
 
 
@@ -246,6 +246,48 @@ def moe_expert_ffn_fwd_gather(s, x, pair_of_row, offsets, tile_offsets, W_gu, W_
     check(lib().moe_expert_ffn_fwd_gather(C.byref(s), _p(x), _p(pair_of_row), _p(offsets),
                                           _p(tile_offsets), _p(W_gu), _p(W_down), _p(h), _p(a),
                                           _p(yp), _stream(stream)))
+
+
+def moe_expert_ffn_fwd_scatter(s, xp, x, pair_of_row, offsets, tile_offsets, W_gu, W_down, h,
+                               a, yq, stream=None):
+    """xp None: GEMM1 gathers x through pair_of_row (the fused permute)."""
+    cap, d, F = s.T * s.K, s.d, s.F
+    fn = "moe_expert_ffn_fwd_scatter"
+    if xp is None and x is None:
+        raise ValueError(f"{fn}: xp and x are both None")
+    ops = dict(pair_of_row=(pair_of_row, cap, _I32), h=(h, cap * 2 * F, _DATA),
+               a=(a, cap * F, _DATA), yq=(yq, cap * d, _DATA))
+    if xp is not None:
+        ops["xp"] = (xp, cap * d, _DATA)
+    else:
+        ops["x"] = (x, s.T * d, _DATA)
+    _chk_ffn(s, fn, offsets, tile_offsets, W_gu, W_down, **ops)
+    check(lib().moe_expert_ffn_fwd_scatter(C.byref(s), _p(xp), _p(x), _p(pair_of_row),
+                                           _p(offsets), _p(tile_offsets), _p(W_gu), _p(W_down),
+                                           _p(h), _p(a), _p(yq), _stream(stream)))
+
+
+def moe_combine_pairs(s, yq, gates, row_of_pair, out, stream=None):
+    fn, T, d, K = "moe_combine_pairs", s.T, s.d, s.K
+    _chk(s, fn, "yq", yq, _DATA, T * K * d)
+    _chk(s, fn, "gates", gates, _F32, T * K)
+    _chk(s, fn, "row_of_pair", row_of_pair, _I32, T * K)
+    _chk(s, fn, "out", out, _DATA, T * d)
+    check(lib().moe_combine_pairs(C.byref(s), _p(yq), _p(gates), _p(row_of_pair), _p(out),
+                                  _stream(stream)))
+
+
+def moe_combine_bwd_pairs(s, dout, yq, gates, row_of_pair, dyp, dgates, stream=None):
+    """dyp None: dgates only (the fused combine backward)."""
+    fn, T, d, K = "moe_combine_bwd_pairs", s.T, s.d, s.K
+    _chk(s, fn, "dout", dout, _DATA, T * d)
+    _chk(s, fn, "yq", yq, _DATA, T * K * d)
+    _chk(s, fn, "gates", gates, _F32, T * K)
+    _chk(s, fn, "row_of_pair", row_of_pair, _I32, T * K)
+    _chk(s, fn, "dyp", dyp, _DATA, T * K * d, optional=True)
+    _chk(s, fn, "dgates", dgates, _F32, T * K)
+    check(lib().moe_combine_bwd_pairs(C.byref(s), _p(dout), _p(yq), _p(gates), _p(row_of_pair),
+                                      _p(dyp), _p(dgates), _stream(stream)))
 
 
 def moe_combine(s, yp, gates, row_of_pair, out, stream=None):

@@ -37,6 +37,7 @@ MOE_STEP_FUSED_PERMUTE = 8
 MOE_STEP_MID_WGRAD = 16
 MOE_STEP_FUSED_COMBINE_BWD = 32
 MOE_STEP_PAIR_WGRAD = 64
+MOE_STEP_FUSED_SCATTER = 128
 
 
 class MoeShape(C.Structure):
@@ -89,6 +90,9 @@ SIGNATURES = {
     "moe_expert_ffn_fwd_gather": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_combine": (C.c_int, [_SP, _P, _P, _P, _P, _P]),
     "moe_combine_bwd": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_expert_ffn_fwd_scatter": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_combine_pairs": (C.c_int, [_SP, _P, _P, _P, _P, _P]),
+    "moe_combine_bwd_pairs": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P]),
     "moe_ffn_dgrad": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "moe_ffn_wgrad": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, C.c_int, _P]),
     "moe_ffn_wgrad_pair": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,

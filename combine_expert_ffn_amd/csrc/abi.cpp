@@ -438,6 +438,51 @@ int moe_combine_bwd(const moe_shape* s, const void* dout, const void* yp, const 
   return launch_combine_bwd(s, dout, yp, gates, row_of_pair, dyp, dgates, stream);
 }
 
+int moe_expert_ffn_fwd_scatter(const moe_shape* s, const void* xp, const void* x,
+                               const int32_t* pair_of_row, const int32_t* offsets,
+                               const int32_t* tile_offsets, const void* W_gu, const void* W_down,
+                               void* h, void* a, void* yq, hipStream_t stream) {
+  g_err[0] = 0;
+  if (int rc = validate_shape(s)) return rc;
+  if (!xp && !x) return set_error(MOE_ERR_NULL, "%s: xp and x are both NULL", __func__);
+  REQUIRE(pair_of_row);
+  REQUIRE(offsets);
+  REQUIRE(tile_offsets);
+  REQUIRE(W_gu);
+  REQUIRE(W_down);
+  REQUIRE(h);
+  REQUIRE(a);
+  REQUIRE(yq);
+  if (!xp)
+    if (int rc = check_gather_x(s, __func__)) return rc;
+  return launch_ffn_fwd(s, xp ? xp : x, xp ? nullptr : pair_of_row, offsets, tile_offsets, W_gu,
+                        W_down, h, a, yq, stream, pair_of_row);
+}
+
+int moe_combine_pairs(const moe_shape* s, const void* yq, const float* gates,
+                      const int32_t* row_of_pair, void* out, hipStream_t stream) {
+  g_err[0] = 0;
+  if (int rc = validate_shape(s)) return rc;
+  REQUIRE(yq);
+  REQUIRE(gates);
+  REQUIRE(row_of_pair);
+  REQUIRE(out);
+  return launch_combine(s, yq, gates, row_of_pair, nullptr, out, stream, true);
+}
+
+int moe_combine_bwd_pairs(const moe_shape* s, const void* dout, const void* yq,
+                          const float* gates, const int32_t* row_of_pair, void* dyp,
+                          float* dgates, hipStream_t stream) {
+  g_err[0] = 0;
+  if (int rc = validate_shape(s)) return rc;
+  REQUIRE(dout);
+  REQUIRE(yq);
+  REQUIRE(gates);
+  REQUIRE(row_of_pair);
+  REQUIRE(dgates);
+  return launch_combine_bwd(s, dout, yq, gates, row_of_pair, dyp, dgates, stream, true);
+}
+
 int moe_ffn_dgrad(const moe_shape* s, const void* dyp, const void* h, const int32_t* offsets,
                   const int32_t* tile_offsets, const void* W_gu, const void* W_down, void* dh,
                   void* dxp, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -839,6 +884,8 @@ struct StepCtx {
   void* wsW;    // non-null: a workspace whose dgrad weight copies are already
                 // made (once per moe_overlap_steps call); the dgrad reads them
                 // there instead of making its own
+  bool scatter;  // fused scatter: GEMM2 writes y by pair, the combine and its
+                 // backward read it so
 };
 
 static int fwd_route(const StepCtx& c, const moe_mb* A, hipStream_t q) {
@@ -855,13 +902,13 @@ static int fwd_ffn(const StepCtx& c, const moe_mb* A, hipStream_t q) {
   const PhaseRange pr("moe.expert_ffn_fwd");
   return launch_ffn_fwd(c.s, c.fused ? A->x : A->xp, c.fused ? A->pair_of_row : nullptr,
                         A->offsets, A->tile_offsets, c.st->W_gu, c.st->W_down, A->h, A->a,
-                        A->yp, q);
+                        A->yp, q, c.scatter ? A->pair_of_row : nullptr);
 }
 static bool has_shared(const StepCtx& c) { return c.st->F_s > 0; }
 static int fwd_combine(const StepCtx& c, const moe_mb* A, hipStream_t q) {
   const PhaseRange pr("moe.combine");
   return launch_combine(c.s, A->yp, A->gates, A->row_of_pair, has_shared(c) ? A->y_s : nullptr,
-                        A->out, q);
+                        A->out, q, c.scatter);
 }
 static int fwd_shared(const StepCtx& c, const moe_mb* A, hipStream_t q) {
   const PhaseRange pr("moe.shared_fwd");
@@ -881,7 +928,7 @@ static int bwd_shared_wgrad(const StepCtx& c, const moe_mb* B, hipStream_t q) {
 static int bwd_combine(const StepCtx& c, const moe_mb* B, hipStream_t q) {
   const PhaseRange pr("moe.combine_bwd");
   return launch_combine_bwd(c.s, B->dout, B->yp, B->gates, B->row_of_pair,
-                            c.fcb ? nullptr : B->dyp, B->dgates, q);
+                            c.fcb ? nullptr : B->dyp, B->dgates, q, c.scatter);
 }
 static int bwd_route(const StepCtx& c, const moe_mb* B, hipStream_t q) {
   const PhaseRange pr("moe.route_bwd");
@@ -932,7 +979,7 @@ static int check_step(const moe_step* st, int flags, const char* fn) {
   if (int rc = validate_shape(s)) return rc;
   if (flags & ~(MOE_STEP_SERIALIZE | MOE_STEP_EAGER_WGRAD | MOE_STEP_SKIP_WGRAD |
                 MOE_STEP_FUSED_PERMUTE | MOE_STEP_MID_WGRAD | MOE_STEP_FUSED_COMBINE_BWD |
-                MOE_STEP_PAIR_WGRAD))
+                MOE_STEP_PAIR_WGRAD | MOE_STEP_FUSED_SCATTER))
     return set_error(MOE_ERR_ARG, "%s: unknown flags 0x%x", fn, flags);
   if ((flags & MOE_STEP_PAIR_WGRAD) &&
       (flags & (MOE_STEP_FUSED_PERMUTE | MOE_STEP_FUSED_COMBINE_BWD)))
@@ -1009,7 +1056,7 @@ static int step_impl(const moe_step* st, hipStream_t s0, hipStream_t s1, int fla
   const size_t sh = shared ? ws_shared(s, st->F_s) : 0;
   StepCtx c{st, s, st->ws, (char*)st->ws + one, mode == MOE_ROUTE_TOPK, fused,
             (flags & MOE_STEP_FUSED_COMBINE_BWD) != 0, (char*)st->ws + 2 * one,
-            (char*)st->ws + 2 * one + sh, wsW};
+            (char*)st->ws + 2 * one + sh, wsW, (flags & MOE_STEP_FUSED_SCATTER) != 0};
   const bool serial = (flags & MOE_STEP_SERIALIZE) || s0 == s1;
   const bool eager = (flags & MOE_STEP_EAGER_WGRAD) != 0;
   const bool skip_w = (flags & MOE_STEP_SKIP_WGRAD) != 0;
@@ -1365,7 +1412,8 @@ extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, h
     char* shalf_s0 = ws + 2 * one + sh;
     StepCtx c{st, s, even ? half_s1 : half_s0, even ? half_s0 : half_s1,
               st->route_mode == MOE_ROUTE_TOPK, fused, (flags & MOE_STEP_FUSED_COMBINE_BWD) != 0,
-              even ? shalf_s1 : shalf_s0, even ? shalf_s0 : shalf_s1, wsW};
+              even ? shalf_s1 : shalf_s0, even ? shalf_s0 : shalf_s1, wsW,
+              (flags & MOE_STEP_FUSED_SCATTER) != 0};
     // The forward of step j also waits for the backward of step j - 2 (on
     // the other stream), the last earlier chain not ordered before it by its
     // stream, so a forward may reuse the buffers of any micro-batch

@@ -359,7 +359,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
                                                       const int32_t* __restrict__ row_of_pair,
                                                       const uint4* __restrict__ add,
                                                       uint4* __restrict__ out, int T_, int K,
-                                                      int nch) {
+                                                      int nch, int pairs) {
   constexpr int CN = Chunk<T>::N;
   const int t = uniform_token((int)(((long)blockIdx.x * 256 + threadIdx.x) >> 6));
   const int lane = threadIdx.x & 63;
@@ -390,8 +390,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
       const int k0 = lr.next();
       const bool two = !lr.empty();
       const int k1 = two ? lr.next() : k0;
-      const uint4* s0 = yp + (size_t)lr.row(k0) * nch;
-      const uint4* s1 = yp + (size_t)lr.row(k1) * nch;
+      // y by dispatched row, or (pairs) by pair: token t's slots are rows
+      // t*K .. t*K + K - 1
+      const uint4* s0 = yp + (size_t)(pairs ? t * K + k0 : lr.row(k0)) * nch;
+      const uint4* s1 = yp + (size_t)(pairs ? t * K + k1 : lr.row(k1)) * nch;
       uint4 v0[MAXC], v1[MAXC];
 #pragma unroll
       for (int i = 0; i < MAXC; ++i) v0[i] = load_nt(&s0[cc[i]]);
@@ -431,19 +433,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
 
 template <typename T>
 static void combine_t(const moe_shape* s, const void* yp, const float* gates,
-                      const int32_t* row_of_pair, const void* add, void* out, hipStream_t st) {
+                      const int32_t* row_of_pair, const void* add, void* out, hipStream_t st,
+                      bool pairs) {
   MOE_LAUNCH("combine", st,
              combine_kernel<T, 4><<<(unsigned)cdiv(s->T, 4), 256, 0, st>>>(
                  (const uint4*)yp, gates, row_of_pair, (const uint4*)add, (uint4*)out, (int)s->T,
-                 (int)s->K, row_chunks(s)));
+                 (int)s->K, row_chunks(s), pairs ? 1 : 0));
 }
 
 int launch_combine(const moe_shape* s, const void* yp, const float* gates,
-                   const int32_t* row_of_pair, const void* add, void* out, hipStream_t st) {
+                   const int32_t* row_of_pair, const void* add, void* out, hipStream_t st,
+                   bool pairs) {
   if (s->T == 0) return MOE_OK;
-  if (s->dtype == MOE_BF16) combine_t<uint16_t>(s, yp, gates, row_of_pair, add, out, st);
-  else if (s->dtype == MOE_F16) combine_t<_Float16>(s, yp, gates, row_of_pair, add, out, st);
-  else combine_t<float>(s, yp, gates, row_of_pair, add, out, st);
+  if (s->dtype == MOE_BF16) combine_t<uint16_t>(s, yp, gates, row_of_pair, add, out, st, pairs);
+  else if (s->dtype == MOE_F16)
+    combine_t<_Float16>(s, yp, gates, row_of_pair, add, out, st, pairs);
+  else combine_t<float>(s, yp, gates, row_of_pair, add, out, st, pairs);
   return check_launch("combine");
 }
 
@@ -459,7 +464,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
                                                           const int32_t* __restrict__ row_of_pair,
                                                           uint4* __restrict__ dyp,
                                                           float* __restrict__ dgates, int T_,
-                                                          int K, int nch) {
+                                                          int K, int nch, int pairs) {
   constexpr int CN = Chunk<T>::N;
   const int t = uniform_token((int)(((long)blockIdx.x * 256 + threadIdx.x) >> 6));
   const int lane = threadIdx.x & 63;
@@ -490,6 +495,8 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
       continue;
     }
     const float g = gates[(size_t)t * K + k];
+    // y's row: the dispatched row, or (pairs) the pair's own row
+    const size_t yr = pairs ? (size_t)t * K + k : (size_t)r;
     float dot = 0.f;
     if constexpr (MAXC <= 4) {
       // the row's chunks are loaded together (clamped indices), then used in
@@ -498,7 +505,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
 #pragma unroll
       for (int i = 0; i < MAXC; ++i) {
         const int c = lane + 64 * i;
-        yv[i] = load_nt(&yp[(size_t)r * nch + (c < nch ? c : nch - 1)]);
+        yv[i] = load_nt(&yp[yr * nch + (c < nch ? c : nch - 1)]);
       }
 #pragma unroll
       for (int i = 0; i < MAXC; ++i) pin(yv[i]);
@@ -523,7 +530,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
         const int c = lane + 64 * i;
         if (c < nch) {
           float y[CN], o[CN];
-          Chunk<T>::unpack(load_nt(&yp[(size_t)r * nch + c]), y);
+          Chunk<T>::unpack(load_nt(&yp[yr * nch + c]), y);
 #pragma unroll
           for (int q = 0; q < CN; ++q) {
             dot = fmaf(dv[i][q], y[q], dot);
@@ -541,33 +548,34 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
 template <typename T, int MAXC>
 static void combine_bwd_t(const moe_shape* s, const void* dout, const void* yp,
                           const float* gates, const int32_t* row_of_pair, void* dyp,
-                          float* dgates, hipStream_t st) {
+                          float* dgates, hipStream_t st, bool pairs) {
   if (dyp)
     MOE_LAUNCH("combine_bwd", st,
                (combine_bwd_kernel<T, MAXC, true><<<(unsigned)cdiv(s->T, 4), 256, 0, st>>>(
                    (const uint4*)dout, (const uint4*)yp, gates, row_of_pair, (uint4*)dyp, dgates,
-                   (int)s->T, (int)s->K, row_chunks(s))));
+                   (int)s->T, (int)s->K, row_chunks(s), pairs ? 1 : 0)));
   else
     MOE_LAUNCH("combine_bwd", st,
                (combine_bwd_kernel<T, MAXC, false><<<(unsigned)cdiv(s->T, 4), 256, 0, st>>>(
                    (const uint4*)dout, (const uint4*)yp, gates, row_of_pair, nullptr, dgates,
-                   (int)s->T, (int)s->K, row_chunks(s))));
+                   (int)s->T, (int)s->K, row_chunks(s), pairs ? 1 : 0)));
 }
 
 int launch_combine_bwd(const moe_shape* s, const void* dout, const void* yp, const float* gates,
-                       const int32_t* row_of_pair, void* dyp, float* dgates, hipStream_t st) {
+                       const int32_t* row_of_pair, void* dyp, float* dgates, hipStream_t st,
+                       bool pairs) {
   if (s->T == 0) return MOE_OK;
   const int nch = row_chunks(s);
   // d <= 16384: 16-bit rows <= 2048 chunks, f32 rows <= 4096 chunks
   if (s->dtype == MOE_BF16) {
-    if (nch <= 256) combine_bwd_t<uint16_t, 4>(s, dout, yp, gates, row_of_pair, dyp, dgates, st);
-    else combine_bwd_t<uint16_t, 32>(s, dout, yp, gates, row_of_pair, dyp, dgates, st);
+    if (nch <= 256) combine_bwd_t<uint16_t, 4>(s, dout, yp, gates, row_of_pair, dyp, dgates, st, pairs);
+    else combine_bwd_t<uint16_t, 32>(s, dout, yp, gates, row_of_pair, dyp, dgates, st, pairs);
   } else if (s->dtype == MOE_F16) {
-    if (nch <= 256) combine_bwd_t<_Float16, 4>(s, dout, yp, gates, row_of_pair, dyp, dgates, st);
-    else combine_bwd_t<_Float16, 32>(s, dout, yp, gates, row_of_pair, dyp, dgates, st);
+    if (nch <= 256) combine_bwd_t<_Float16, 4>(s, dout, yp, gates, row_of_pair, dyp, dgates, st, pairs);
+    else combine_bwd_t<_Float16, 32>(s, dout, yp, gates, row_of_pair, dyp, dgates, st, pairs);
   } else {
-    if (nch <= 256) combine_bwd_t<float, 4>(s, dout, yp, gates, row_of_pair, dyp, dgates, st);
-    else combine_bwd_t<float, 64>(s, dout, yp, gates, row_of_pair, dyp, dgates, st);
+    if (nch <= 256) combine_bwd_t<float, 4>(s, dout, yp, gates, row_of_pair, dyp, dgates, st, pairs);
+    else combine_bwd_t<float, 64>(s, dout, yp, gates, row_of_pair, dyp, dgates, st, pairs);
   }
   return check_launch("combine bwd");
 }

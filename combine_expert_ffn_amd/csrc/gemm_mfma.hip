@@ -186,6 +186,21 @@ __device__ __forceinline__ void store_block(const float* blk, uint16_t* out_row0
   }
 }
 
+// The same with the staged rows scattered: row r of the block goes to row
+// dst[q] of out (out points at the block's first column), where q is the
+// pass that holds r for this lane (r = st_row(q, lane)).
+template <class E>
+__device__ __forceinline__ void store_block_rows(const float* blk, uint16_t* out, size_t ld,
+                                                 const int (&dst)[4], int n_rows, int lane) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = st_row(q, lane), c = st_col(lane);
+    float f[8];
+    ld8(blk + r * EP_LD + c, f);
+    if (r < n_rows) *(uint4*)(out + (size_t)dst[q] * ld + c) = Chunk<typename E::elt>::pack(f);
+  }
+}
+
 template <class TL>
 struct Frags {
   bf16x8_t a[TL::TM], b[TL::TN];
@@ -487,6 +502,16 @@ __device__ __forceinline__ void uniform_row_tile(const int* s_to, const int* s_o
   m_end = __builtin_amdgcn_readfirstlane(m_end);
 }
 
+// Whether an Op's epilogue takes destination rows loaded before it (ROWS).
+template <class Op, class = void>
+struct OpRows {
+  static constexpr bool value = false;
+};
+template <class Op>
+struct OpRows<Op, std::void_t<decltype(Op::ROWS)>> {
+  static constexpr bool value = Op::ROWS;
+};
+
 // ---------------------------------------------------------------------------
 // Row-grouped GEMM (forward and dgrad): M tiles follow the dispatch plan, N
 // tiles are fixed.  Op supplies the loaders (init), the K extent (k_len) and
@@ -529,6 +554,10 @@ __global__ __launch_bounds__(TL::NT) void row_grouped_kernel(Op op,
     f32x16_t acc[TL::TM][TL::TN];
     mainloop_steps<TL, typename Op::Elt>(la, lb, 0, nk, smem, acc);
     const int ce = e, cm0 = m0, cm_end = m_end, cnt = nt;
+    // an epilogue that scatters its rows loads their destinations now, ahead
+    // of the next tile's loads (the memory counter retires in order)
+    int dst[OpRows<Op>::value ? TL::TM : 1][4];
+    if constexpr (OpRows<Op>::value) op.template dest_rows<TL>(cm0, cm_end, dst);
     sc.t += sc.step;
     const bool more = sc.t < sc.end;  // block-uniform
     if (more) {
@@ -538,7 +567,8 @@ __global__ __launch_bounds__(TL::NT) void row_grouped_kernel(Op op,
       la.load(0, 0);
       lb.load(0, 0);
     }
-    op.template epilogue<TL>(acc, ce, cm0, cm_end, cnt, smem);
+    if constexpr (OpRows<Op>::value) op.template epilogue<TL>(acc, ce, cm0, cm_end, cnt, smem, dst);
+    else op.template epilogue<TL>(acc, ce, cm0, cm_end, cnt, smem);
     __syncthreads();  // epilogue staging done before the next tile's stage 0 lands in LDS
     if (!more) break;
   }
@@ -616,13 +646,31 @@ struct GateUpOp {
 };
 
 // forward GEMM2: y_p = a . W_down[e]^T  (A: a rows, K = F; B: W_down rows, K = F)
-template <class E>
+//
+// SCATTER: the epilogue writes dispatched row r of the product to row
+// yrows[r] of yp (yrows is the plan's pair_of_row), so y is laid out by
+// (token, slot) pair, and the combine and its backward read a token's K rows
+// as one contiguous run.
+template <class E, bool SCATTER = false>
 struct DownOp {
   typedef E Elt;
+  static constexpr bool ROWS = SCATTER;
   const uint16_t* a;
   const uint16_t* W_down;
   uint16_t* yp;
   int d, F;
+  const int32_t* yrows;
+  // SCATTER: destination row of each staged row this lane stores, per 32-row
+  // block i of the wave (rows past the expert's end clamp to its last row)
+  template <class TL, int R>
+  __device__ __forceinline__ void dest_rows(int m0, int m_end, int (&dst)[R][4]) const {
+    const WavePos w = WavePos::of<TL>();
+#pragma unroll
+    for (int i = 0; i < TL::TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        dst[i][q] = yrows[min(m0 + w.wm * TL::WTM + i * 32 + st_row(q, w.lane), m_end - 1)];
+  }
   __device__ __forceinline__ int k_len() const { return F; }
   template <class TL, class LA, class LB>
   __device__ __forceinline__ void init(int e, int m0, int m_end, int nt, LA& la, LB& lb,
@@ -632,9 +680,10 @@ struct DownOp {
     la.init(a + (size_t)m0 * F, [&](int r) { return (min(m0 + r, m_end - 1) - m0) * F; }, tid);
     lb.init(Wd, [&](int n) { return min(nb + n, d - 1) * F; }, tid);
   }
-  template <class TL>
+  template <class TL, int R = 1>
   __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[TL::TM][TL::TN], int e, int m0,
-                                           int m_end, int nt, uint16_t* smem) const {
+                                           int m_end, int nt, uint16_t* smem,
+                                           const int (&dst)[R][4] = {}) const {
     const WavePos w = WavePos::of<TL>();
 #pragma unroll
     for (int p = 0; p < TL::TN / 2; ++p) {
@@ -644,7 +693,12 @@ struct DownOp {
       for (int i = 0; i < TL::TM; ++i) {
         const int rb = m0 + w.wm * TL::WTM + i * 32;
         const float* blk = stage_rows<TL>(acc, i, p, smem, w.wave, w.lane);
-        store_block<E>(blk, yp + (size_t)rb * d + cb, (size_t)d, m_end - rb, w.lane);
+        if constexpr (SCATTER) {
+          static_assert(R == TL::TM, "one row set per 32-row block");
+          store_block_rows<E>(blk, yp + cb, (size_t)d, dst[i], m_end - rb, w.lane);
+        } else {
+          store_block<E>(blk, yp + (size_t)rb * d + cb, (size_t)d, m_end - rb, w.lane);
+        }
       }
     }
   }
@@ -1349,16 +1403,20 @@ int launch_row_grouped(const char* name, const moe_shape* s, const Op& op,
 template <class E>
 int ffn_fwd_t(const moe_shape* s, const void* xp, const int32_t* xrows, const int32_t* offsets,
               const int32_t* tile_offsets, const void* W_gu, const void* W_down, void* h,
-              void* a, void* yp, hipStream_t st) {
+              void* a, void* yp, hipStream_t st, const int32_t* yrows) {
   const int d = (int)s->d, F = (int)s->F;
   GateUpOp<E> g{(const uint16_t*)xp, (const uint16_t*)W_gu, (uint16_t*)h, (uint16_t*)a, d, F,
                 xrows, (int)s->K};
   if (int rc = launch_row_grouped("ffn_gate_up", s, g, offsets, tile_offsets,
                                   (F + T256::BN / 2 - 1) / (T256::BN / 2), st))
     return rc;
-  DownOp<E> dn{(const uint16_t*)a, (const uint16_t*)W_down, (uint16_t*)yp, d, F};
-  return launch_row_grouped("ffn_down", s, dn, offsets, tile_offsets,
-                            (d + T256::BN - 1) / T256::BN, st);
+  const int nt = (d + T256::BN - 1) / T256::BN;
+  if (yrows) {
+    DownOp<E, true> dn{(const uint16_t*)a, (const uint16_t*)W_down, (uint16_t*)yp, d, F, yrows};
+    return launch_row_grouped("ffn_down", s, dn, offsets, tile_offsets, nt, st);
+  }
+  DownOp<E> dn{(const uint16_t*)a, (const uint16_t*)W_down, (uint16_t*)yp, d, F, nullptr};
+  return launch_row_grouped("ffn_down", s, dn, offsets, tile_offsets, nt, st);
 }
 
 template <class E>
@@ -1462,10 +1520,12 @@ void router_t(const moe_shape* s, const void* x, const void* W_rT, const float* 
 
 int launch_ffn_fwd_mfma(const moe_shape* s, const void* xp, const int32_t* xrows,
                         const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
-                        const void* W_down, void* h, void* a, void* yp, hipStream_t st) {
-  return s->dtype == MOE_F16
-             ? ffn_fwd_t<F16>(s, xp, xrows, offsets, tile_offsets, W_gu, W_down, h, a, yp, st)
-             : ffn_fwd_t<BF16>(s, xp, xrows, offsets, tile_offsets, W_gu, W_down, h, a, yp, st);
+                        const void* W_down, void* h, void* a, void* yp, hipStream_t st,
+                        const int32_t* yrows) {
+  return s->dtype == MOE_F16 ? ffn_fwd_t<F16>(s, xp, xrows, offsets, tile_offsets, W_gu, W_down,
+                                              h, a, yp, st, yrows)
+                             : ffn_fwd_t<BF16>(s, xp, xrows, offsets, tile_offsets, W_gu,
+                                               W_down, h, a, yp, st, yrows);
 }
 
 int launch_dgrad_weights_mfma(const moe_shape* s, const void* W_gu, const void* W_down,

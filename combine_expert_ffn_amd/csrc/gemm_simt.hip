@@ -52,7 +52,8 @@ __global__ __launch_bounds__(256) void f32_down_kernel(const float* __restrict__
                                                        const int32_t* __restrict__ offsets,
                                                        const float* __restrict__ W_down,
                                                        float* __restrict__ yp, long cap, int E_l,
-                                                       int d, int F) {
+                                                       int d, int F,
+                                                       const int32_t* __restrict__ yrows) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= cap * d) return;
   const int row = (int)(i / d), c = (int)(i % d);
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(256) void f32_down_kernel(const float* __restrict__
   const float* w = W_down + ((size_t)e * d + c) * F;
   float y = 0.f;
   for (int f = 0; f < F; ++f) y = fmaf(ar[f], w[f], y);
-  yp[(size_t)row * d + c] = y;
+  yp[(size_t)(yrows ? yrows[row] : row) * d + c] = y;
 }
 
 // xrows: null, or pair_of_row for the fused combine backward: dyp is then
@@ -155,7 +156,8 @@ __global__ __launch_bounds__(256) void f32_wgrad_kernel(
 
 int launch_ffn_fwd_mfma(const moe_shape* s, const void* xp, const int32_t* xrows,
                         const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
-                        const void* W_down, void* h, void* a, void* yp, hipStream_t st);
+                        const void* W_down, void* h, void* a, void* yp, hipStream_t st,
+                        const int32_t* yrows);
 int launch_dgrad_weights_mfma(const moe_shape* s, const void* W_gu, const void* W_down,
                               void* ws, hipStream_t st);
 int launch_ffn_dgrad_mfma(const moe_shape* s, const void* dyp, const void* h,
@@ -169,10 +171,12 @@ int launch_ffn_wgrad_mfma(const moe_shape* s, const void* xp, const int32_t* xro
 
 int launch_ffn_fwd(const moe_shape* s, const void* xp, const int32_t* xrows,
                    const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
-                   const void* W_down, void* h, void* a, void* yp, hipStream_t st) {
+                   const void* W_down, void* h, void* a, void* yp, hipStream_t st,
+                   const int32_t* yrows) {
   if (s->T == 0) return MOE_OK;
   if (is16(s))
-    return launch_ffn_fwd_mfma(s, xp, xrows, offsets, tile_offsets, W_gu, W_down, h, a, yp, st);
+    return launch_ffn_fwd_mfma(s, xp, xrows, offsets, tile_offsets, W_gu, W_down, h, a, yp, st,
+                               yrows);
   const long cap = s->T * s->K;
   const int d = (int)s->d, F = (int)s->F, E_l = (int)s->E_l;
   MOE_LAUNCH("f32_gate_up", st,
@@ -181,7 +185,7 @@ int launch_ffn_fwd(const moe_shape* s, const void* xp, const int32_t* xrows,
   if (int rc = check_launch("f32 expert GEMM1")) return rc;
   MOE_LAUNCH("f32_down", st,
              f32_down_kernel<<<(unsigned)cdiv(cap * d, 256), 256, 0, st>>>(
-      (const float*)a, offsets, (const float*)W_down, (float*)yp, cap, E_l, d, F));
+      (const float*)a, offsets, (const float*)W_down, (float*)yp, cap, E_l, d, F, yrows));
   return check_launch("f32 expert GEMM2");
 }
 

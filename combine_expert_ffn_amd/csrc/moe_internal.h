@@ -238,20 +238,27 @@ int launch_permute(const moe_shape* s, const void* x, const int32_t* row_of_pair
 // writes the shared expert's plan: plan[0..1] = offsets {0, T}, plan[2..3] =
 // tile_offsets {0, ceil(T / kTileM)}
 int launch_shared_plan(int64_t T, int32_t* plan, hipStream_t st);
-// add (nullable): a token-aligned [T][d] term summed in before the one rounding
+// add (nullable): a token-aligned [T][d] term summed in before the one rounding.
+// pairs: yp is laid out by (token, slot) pair (row t*K + k, written by the
+// forward with yrows set) instead of by dispatched row.
 int launch_combine(const moe_shape* s, const void* yp, const float* gates,
-                   const int32_t* row_of_pair, const void* add, void* out, hipStream_t st);
+                   const int32_t* row_of_pair, const void* add, void* out, hipStream_t st,
+                   bool pairs = false);
 int launch_combine_bwd(const moe_shape* s, const void* dout, const void* yp, const float* gates,
-                       const int32_t* row_of_pair, void* dyp, float* dgates, hipStream_t st);
+                       const int32_t* row_of_pair, void* dyp, float* dgates, hipStream_t st,
+                       bool pairs = false);
 int launch_dispatch_bwd(const moe_shape* s, const void* dxp, const int32_t* row_of_pair,
                         const int32_t* idx, const float* dlogits, const void* W_rT,
                         const void* add, void* dx, bool accumulate, hipStream_t st);
 // expert GEMMs.  xrows: null, or the plan's pair_of_row for the fused permute,
 // in which case xp is the token matrix x and dispatched row r of the GEMM1 (and
-// wgrad dW_gu) operand is token xrows[r] / K.
+// wgrad dW_gu) operand is token xrows[r] / K.  yrows: null, or the plan's
+// pair_of_row, in which case GEMM2 writes dispatched row r to row yrows[r] of
+// yp (y by pair).
 int launch_ffn_fwd(const moe_shape* s, const void* xp, const int32_t* xrows,
                    const int32_t* offsets, const int32_t* tile_offsets, const void* W_gu,
-                   const void* W_down, void* h, void* a, void* yp, hipStream_t st);
+                   const void* W_down, void* h, void* a, void* yp, hipStream_t st,
+                   const int32_t* yrows = nullptr);
 // The 16-bit dgrad's transposed weight copies (into ws at ws_wT_offset); a
 // no-op in float32.
 int launch_dgrad_weights(const moe_shape* s, const void* W_gu, const void* W_down, void* ws,

@@ -118,6 +118,12 @@ extern "C" {
                                  buffers); not with the fused permute or the
                                  fused combine backward, and not under stream
                                  capture (MOE_ERR_UNSUPPORTED) */
+#define MOE_STEP_FUSED_SCATTER 128 /* the unpermute fused into GEMM2: its epilogue
+                                 writes y by (token, slot) pair into the
+                                 micro-batch's yp buffer (moe_expert_ffn_fwd_scatter),
+                                 and the combine and the combine backward read
+                                 a token's slots as one run (moe_combine_pairs,
+                                 moe_combine_bwd_pairs).  Bit-identical results */
 
 /*
  * Layer shape.  T tokens of hidden size d; E experts routed over, of which the
@@ -260,6 +266,35 @@ int moe_combine(const moe_shape* s, const void* yp, const float* gates,
                 const int32_t* row_of_pair, void* out, hipStream_t stream);
 
 /*
+ * moe_expert_ffn_fwd_scatter - moe_expert_ffn_fwd with the unpermute half of
+ * the combine fused into GEMM2's epilogue (page 1 lists the fused permute,
+ * moe_permute_fusion; this is its scatter side): dispatched row r of the
+ * product goes to row pair_of_row[r] of yq, so
+ *   yq [T*K,d]:  yq[t*K+k] = the expert output of pair (t,k) for local pairs
+ * (rows of non-local pairs are not written).  The values are those of
+ * moe_expert_ffn_fwd's yp, bit for bit, at other rows.  xp, or, with xp NULL,
+ * x [T,d] gathered through pair_of_row as moe_expert_ffn_fwd_gather does.
+ * The gate-weighted sum stays in moe_combine_pairs: every token sums K rows,
+ * and a sum in GEMM2's epilogue would need float atomics whose order varies
+ * between runs.
+ */
+int moe_expert_ffn_fwd_scatter(const moe_shape* s, const void* xp, const void* x,
+                               const int32_t* pair_of_row, const int32_t* offsets,
+                               const int32_t* tile_offsets, const void* W_gu,
+                               const void* W_down, void* h, void* a, void* yq,
+                               hipStream_t stream);
+
+/*
+ * moe_combine_pairs - moe_combine over y by pair (yq from
+ * moe_expert_ffn_fwd_scatter): out[t] = sum over local slots k, ascending, of
+ * gates[t,k] * yq[t*K+k], in float32, one rounding; the same result as
+ * moe_combine on the dispatched-row layout, bit for bit.  row_of_pair marks the
+ * local slots (>= 0).
+ */
+int moe_combine_pairs(const moe_shape* s, const void* yq, const float* gates,
+                      const int32_t* row_of_pair, void* out, hipStream_t stream);
+
+/*
  * moe_combine_bwd - backward of combine (page 2, backward chain: combine's
  * backward first).  For each local pair (t,k) with row r:
  *   dyp[r] = gates[t,k] * dout[t];  dgates[t,k] = <dout[t], yp[r]> (f32)
@@ -270,6 +305,16 @@ int moe_combine(const moe_shape* s, const void* yp, const float* gates,
 int moe_combine_bwd(const moe_shape* s, const void* dout, const void* yp,
                     const float* gates, const int32_t* row_of_pair, void* dyp,
                     float* dgates, hipStream_t stream);
+
+/*
+ * moe_combine_bwd_pairs - moe_combine_bwd reading y by pair (yq): dgates[t,k]
+ * = <dout[t], yq[t*K+k]>; dyp is still written by dispatched row
+ * (dyp[row_of_pair[t*K+k]] = gates[t,k] * dout[t]), as the dgrad reads it.
+ * Bit-identical to moe_combine_bwd on the dispatched-row layout.
+ */
+int moe_combine_bwd_pairs(const moe_shape* s, const void* dout, const void* yq,
+                          const float* gates, const int32_t* row_of_pair, void* dyp,
+                          float* dgates, hipStream_t stream);
 
 /*
  * moe_ffn_dgrad - the D of the W/D split (page 2, "MoE 1F1B overlap"): the

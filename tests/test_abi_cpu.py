@@ -196,7 +196,15 @@ def test_modes_and_flags_rejected():
     st = _lib.MoeStep()
     st.shape = s
     st.route_mode = M.MOE_ROUTE_FORCE_BALANCE
-    assert L.moe_overlap_step(C.byref(st), None, None, 128) == M.MOE_ERR_ARG
+    assert L.moe_overlap_step(C.byref(st), None, None, 256) == M.MOE_ERR_ARG
+    # fused scatter: xp and x both missing, a missing map, missing y
+    assert L.moe_expert_ffn_fwd_scatter(C.byref(s), None, None, *([FAKE] * 9),
+                                        None) == M.MOE_ERR_NULL
+    assert L.moe_expert_ffn_fwd_scatter(C.byref(s), FAKE, None, None, *([FAKE] * 8),
+                                        None) == M.MOE_ERR_NULL
+    assert L.moe_combine_pairs(C.byref(s), None, FAKE, FAKE, FAKE, None) == M.MOE_ERR_NULL
+    assert L.moe_combine_bwd_pairs(C.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                   None) == M.MOE_ERR_NULL
     st.route_mode = 5
     assert L.moe_overlap_step(C.byref(st), None, None, 0) == M.MOE_ERR_ARG
     st.route_mode = M.MOE_ROUTE_FORCE_BALANCE

@@ -180,6 +180,16 @@ def test_stage_parity(name):
                                 fz.h, fz.a, fz.yp)
     for k in ("h", "a", "yp"):
         exact(f"{k} (fused permute)", host(getattr(fz, k), N), host(getattr(mb, k), N))
+    # fused scatter: GEMM2 writes y by (token, slot) pair; the same bits at the
+    # pair's own row, from xp or gathering x
+    loc = torch.nonzero(mb.row_of_pair.reshape(-1) >= 0).reshape(-1)
+    rows = mb.row_of_pair.reshape(-1)[loc].long()
+    for src_xp, src_x in ((mb.xp, None), (None, x)):
+        hq, aq, yq = torch.empty_like(mb.h), torch.empty_like(mb.a), torch.empty_like(mb.yp)
+        M.moe_expert_ffn_fwd_scatter(s, src_xp, src_x, mb.pair_of_row, mb.offsets,
+                                     mb.tile_offsets, W_gu, W_down, hq, aq, yq)
+        assert torch.equal(hq[:N], mb.h[:N]) and torch.equal(aq[:N], mb.a[:N])
+        assert torch.equal(yq[loc], mb.yp[rows]), "fused scatter: y by pair"
 
     # ---- combine (oracle y_p)
     yp_r = D(_pad(ref["yp"], cap))
@@ -190,6 +200,19 @@ def test_stage_parity(name):
     M.moe_combine_bwd(s, dout, yp_r, gates_r, mb.row_of_pair, mb.dyp, mb.dgates)
     close("dyp", host(mb.dyp, N), refb["dyp"], tau)
     close("dgates", host(mb.dgates), refb["dgates"], tau)
+
+    # ---- the same on y by pair (fused scatter): bit for bit
+    yq_r = torch.zeros_like(yp_r)
+    yq_r[loc] = yp_r[rows]
+    outq = torch.empty_like(mb.out)
+    M.moe_combine_pairs(s, yq_r, gates_r, mb.row_of_pair, outq)
+    assert torch.equal(outq, mb.out), "combine on y by pair"
+    dypq, dgq = torch.empty_like(mb.dyp), torch.empty_like(mb.dgates)
+    M.moe_combine_bwd_pairs(s, dout, yq_r, gates_r, mb.row_of_pair, dypq, dgq)
+    assert torch.equal(dypq[:N], mb.dyp[:N]) and torch.equal(dgq, mb.dgates)
+    dgq.fill_(float("nan"))
+    M.moe_combine_bwd_pairs(s, dout, yq_r, gates_r, mb.row_of_pair, None, dgq)
+    assert torch.equal(dgq, mb.dgates), "combine backward on y by pair, dgates only"
 
     # ---- router backward (oracle dgates)
     dgates_r = dev(refb["dgates"], "f32x")
@@ -297,7 +320,8 @@ def _layer_step(w, inp, flags=0, s_copy=None):
     return A, dict(dW_gu=dW_gu, dW_down=dW_down, dW_r=dW_r)
 
 
-CHAIN_FLAGS = {"": 0, "fused_permute": 1, "fused_combine_bwd": 2, "fused_both": 3}
+CHAIN_FLAGS = {"": 0, "fused_permute": 1, "fused_combine_bwd": 2, "fused_both": 3,
+               "fused_scatter": 4, "fused_all": 7}
 
 
 @pytest.mark.parametrize("variant", list(CHAIN_FLAGS))
@@ -307,13 +331,14 @@ CHAIN_FLAGS = {"": 0, "fused_permute": 1, "fused_combine_bwd": 2, "fused_both": 
 def test_chain_parity(name, variant):
     w = SMALL[name]
     v = CHAIN_FLAGS[variant]
-    fused, fcb = bool(v & 1), bool(v & 2)
+    fused, fcb, scatter = bool(v & 1), bool(v & 2), bool(v & 4)
     log(f"[chain parity] {name} {variant}")
     prec, tau = w.dtype, TAU[w.dtype]
     inp = make_inputs(w, seed=0)
     X, ref, refb = _oracle(w, inp, prec)
     A, g = _layer_step(w, inp, (M.MOE_STEP_FUSED_PERMUTE if fused else 0) |
-                       (M.MOE_STEP_FUSED_COMBINE_BWD if fcb else 0))
+                       (M.MOE_STEP_FUSED_COMBINE_BWD if fcb else 0) |
+                       (M.MOE_STEP_FUSED_SCATTER if scatter else 0))
     if w.route == "topk":
         close("logits", host(A.logits), ref["logits"], tau)
         gi = host(A.idx)
@@ -327,7 +352,10 @@ def test_chain_parity(name, variant):
     if not fused:
         exact("xp", host(A.xp, N), ref["xp"])
     for k in ("h", "a", "yp"):
-        close(k, host(getattr(A, k), N), ref[k], tau)
+        t = getattr(A, k)
+        if k == "yp" and scatter:  # y by pair: dispatched row r is row pair_of_row[r]
+            t = t[A.pair_of_row[:N].long()]
+        close(k, host(t, N), ref[k], tau)
     close("out", host(A.out), ref["out"], tau)
     if fcb:  # the fused combine backward: its own rounding points
         refb = dict(refb, **_oracle_fused_bwd(w, X, ref, refb, prec))
@@ -720,6 +748,9 @@ def _pingpong_steps(s, mode, W, grads, ws, mbs, n, shared=None, W_r=None, bias=N
     ("tiny_f32", True, M.MOE_STEP_MID_WGRAD),
     ("zipf_window_bf16", False, M.MOE_STEP_MID_WGRAD | M.MOE_STEP_FUSED_COMBINE_BWD),
     ("fb_ragged_bf16", True, M.MOE_STEP_FUSED_COMBINE_BWD | M.MOE_STEP_FUSED_PERMUTE),
+    ("zipf_window_bf16", False, M.MOE_STEP_MID_WGRAD | M.MOE_STEP_FUSED_SCATTER),
+    ("fb_ragged_bf16", True, M.MOE_STEP_FUSED_COMBINE_BWD | M.MOE_STEP_FUSED_PERMUTE |
+     M.MOE_STEP_FUSED_SCATTER),
 ])
 def test_multi_step_pipelined_equals_serialized(name, shared, flags):
     """moe_overlap_steps (streams alternating, steps overlapping) against the same
@@ -779,6 +810,10 @@ def test_multi_step_pipelined_equals_serialized(name, shared, flags):
         # dispatched-row buffers: rows past N are never written
         N = int(ma[i].offsets[w.E_l])
         for k in ("yp", "dh", "a", "dxp") + (("ag",) if fcb else ("dyp",)):
+            if k == "yp" and flags & M.MOE_STEP_FUSED_SCATTER:  # y by pair: local pairs' rows
+                loc = torch.nonzero(ma[i].row_of_pair.reshape(-1) >= 0).reshape(-1)
+                assert torch.equal(mb[i].yp[loc], ma[i].yp[loc]), (i, k)
+                continue
             assert torch.equal(getattr(mb[i], k)[:N], getattr(ma[i], k)[:N]), (i, k)
     for k, (a, b) in enumerate(zip(ga, gb)):
         if a is not None:
@@ -787,6 +822,62 @@ def test_multi_step_pipelined_equals_serialized(name, shared, flags):
     if shared:
         assert torch.equal(sa[2], sb[2]) and torch.equal(sa[3], sb[3])
     log(f"[multi-step] {name}: bit-identical")
+
+
+@pytest.mark.parametrize("name,flags", [
+    ("zipf_window_bf16", M.MOE_STEP_MID_WGRAD),
+    ("mid_window_f32", 0),
+    ("mid_window_f16", M.MOE_STEP_MID_WGRAD),
+    ("fb_k3_window_bf16", M.MOE_STEP_FUSED_PERMUTE | M.MOE_STEP_FUSED_COMBINE_BWD),
+])
+def test_fused_scatter_steps_equal_unfused(name, flags):
+    """Five pipelined steps with MOE_STEP_FUSED_SCATTER (y written by pair in
+    GEMM2's epilogue, read so by the combine and its backward) against the same
+    steps without it: every output and gradient bit-identical."""
+    w = SMALL[name]
+    prec = w.dtype
+    log(f"[fused scatter steps] {name}: flags={flags}")
+    inp = make_inputs(w, seed=2, microbatches=2)
+    s = M.shape_of(w)
+    D = lambda a: dev(a, prec)
+    topk = w.route == "topk"
+    mode = M.MOE_ROUTE_TOPK if topk else M.MOE_ROUTE_FORCE_BALANCE
+    fused = bool(flags & M.MOE_STEP_FUSED_PERMUTE)
+    fcb = bool(flags & M.MOE_STEP_FUSED_COMBINE_BWD)
+    W = (D(inp["W_gu"]), D(inp["W_down"]))
+    W_r = D(inp["W_r"]) if topk else None
+    bias = dev(inp["bias"], "f32x") if inp["bias"] is not None else None
+    s0, s1 = torch.cuda.current_stream(), torch.cuda.Stream()
+    res = {}
+    for tag, fl in (("plain", flags), ("scatter", flags | M.MOE_STEP_FUSED_SCATTER)):
+        mbs = [M.MicroBatch(s, x=D(inp[xk]), dout=D(inp[dk]),
+                            gates=None if topk else dev(inp[gk], "f32x"), fused=fused,
+                            fused_bwd=fcb)
+               for xk, dk, gk in (("x", "dout", "gates"), ("x_b", "dout_b", "gates_b"))]
+        grads = (torch.full((w.E_l, 2 * w.F, w.d), float("nan"), device="cuda"),
+                 torch.full((w.E_l, w.d, w.F), float("nan"), device="cuda"),
+                 torch.full((w.d, w.E), float("nan"), device="cuda") if topk else None)
+        ws = torch.empty(M.moe_step_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+        M.moe_overlap_steps(_pingpong_steps(s, mode, W, grads, ws, mbs, 5, W_r=W_r, bias=bias),
+                            s0, s1, fl)
+        torch.cuda.synchronize()
+        res[tag] = (mbs, grads)
+    (ma, ga), (mb, gb) = res["plain"], res["scatter"]
+    keys = ["out", "dx", "dgates", "idx", "gates", "row_of_pair"] + \
+        (["logits", "dlogits"] if topk else [])
+    for i in range(2):
+        for k in keys:
+            assert torch.equal(getattr(mb[i], k), getattr(ma[i], k)), (i, k)
+        N = int(ma[i].offsets[w.E_l])
+        for k in ("dh", "a", "dxp") + (("ag",) if fcb else ("dyp",)):
+            assert torch.equal(getattr(mb[i], k)[:N], getattr(ma[i], k)[:N]), (i, k)
+        loc = torch.nonzero(ma[i].row_of_pair.reshape(-1) >= 0).reshape(-1)
+        rows = ma[i].row_of_pair.reshape(-1)[loc].long()
+        assert torch.equal(mb[i].yp[loc], ma[i].yp[rows]), (i, "y by pair")
+    for k, (a, b) in enumerate(zip(ga, gb)):
+        if a is not None:
+            assert torch.equal(a, b), ("dW", k)
+    log(f"[fused scatter steps] {name}: bit-identical")
 
 
 @pytest.mark.parametrize("name,shared", [("zipf_window_bf16", False), ("fb_ragged_bf16", True)])
