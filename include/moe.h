@@ -489,7 +489,7 @@ typedef struct moe_mb {
   void* xp;
   void* h;
   void* a;
-  void* yp;
+  void* yp;     /* [T*K,d]: by dispatched row, or by pair with MOE_STEP_FUSED_SCATTER */
   void* out;
   /* backward */
   const void* dout;
