@@ -34,7 +34,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
 DEFAULT_WORKLOAD = "ep1_128exp_bf16"
 OVERLAP_WORKLOAD = "two_microbatch_bf16"
 
-GEMM_KERNELS = ("ffn_gate_up", "ffn_down", "dgrad_act", "dgrad_in", "wgrad")
+GEMM_KERNELS = ("ffn_gate_up", "ffn_down", "dgrad_act", "dgrad_in", "wgrad", "wgrad_pair")
+# kernels whose algorithmic work is given per launch (the others' per step)
+PER_LAUNCH = ("wgrad_pair",)
 COPY_PROBE_BYTES = 1 << 30
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
@@ -44,7 +46,7 @@ def err(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic(w, N, T_loc, accumulate=True, fused=False, fcb=False, pair=False):
+def algorithmic(w, N, T_loc, accumulate=True, fused=False, fcb=False):
     """Algorithmic work per step of each kernel (one launch of each, plus the
     shared expert's launches of the same GEMMs over all T tokens when the
     workload has one): {name: {"flop": F, "byte": B}}.  Bytes count one pass
@@ -52,9 +54,9 @@ def algorithmic(w, N, T_loc, accumulate=True, fused=False, fcb=False, pair=False
     expert weights, and wgrad's the float32 weight gradients (read and written
     with accumulate, written without).  fused: the permute fused into GEMM1
     and wgrad (x rows instead of xp); fcb: the fused combine backward (dout
-    rows instead of dy_p, ag written by dgrad_act); pair: the routed experts'
-    weight gradients of two consecutive steps in one launch, so per step the
-    float32 weight gradients are read and written half as often."""
+    rows instead of dy_p, ag written by dgrad_act).  `wgrad_pair` (the paired
+    weight gradient, one launch per two steps) is given per launch: both
+    micro-batches' operands and one pass over the float32 weight gradients."""
     d, F, T, K, E, E_l = w.d, w.F, w.T, w.K, w.E, w.E_l
     b = 4 if w.dtype == "f32" else 2
     Fs = w.F_s
@@ -78,7 +80,10 @@ def algorithmic(w, N, T_loc, accumulate=True, fused=False, fcb=False, pair=False
                      + (T * 2 * Fs * b + sgu + T * d * b) * (Fs > 0)},
         "wgrad": {"flop": 6.0 * N * d * F + 6.0 * T * d * Fs,
                   "byte": dyin + N * (F + 2 * F) * b + xin + T * (2 * d + 3 * Fs) * b * (Fs > 0)
-                  + dW * (2 if accumulate else 1) * (0.5 if pair else 1.0)},
+                  + dW * (2 if accumulate else 1)},
+        "wgrad_pair": {"flop": 2 * (6.0 * N * d * F),
+                       "byte": 2 * (dyin + N * (F + 2 * F) * b + xin)
+                       + 4.0 * E_l * 3 * F * d * (2 if accumulate else 1)},
         "router": {"flop": 2.0 * T * d * E, "byte": T * d * b + d * E * b + 4.0 * T * E},
         # router weight gradient x^T dlogits on the matrix cores (bf16 data);
         # the two-term split of dlogits forms it twice, counted once here
@@ -362,9 +367,10 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--tokens", type=int, default=None, help="override T of the workload")
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
-    ap.add_argument("--graph", choices=("on", "off"), default="on",
+    ap.add_argument("--graph", choices=("on", "off"), default=None,
                     help="time the overlapped steps as replays of a HIP graph of --group steps "
-                         "(on) or as eager launches (off)")
+                         "(on) or as eager launches (off); default: off with paired weight "
+                         "gradients (the library does not capture them), else on")
     ap.add_argument("--fused-permute", choices=("on", "off"), default="off",
                     help="fuse the permute into the expert GEMMs (MOE_STEP_FUSED_PERMUTE): GEMM1 "
                          "and wgrad read the token rows of x through the dispatch plan, no xp")
@@ -384,7 +390,7 @@ def main():
                     help="run the overlapped steps G at a time through moe_overlap_steps, the "
                          "streams' roles alternating so consecutive steps overlap (on), or one "
                          "moe_overlap_step call per step, joined at every step boundary (off)")
-    ap.add_argument("--pair-wgrad", choices=("on", "off"), default="off",
+    ap.add_argument("--pair-wgrad", choices=("on", "off"), default="on",
                     help="pair the routed experts' weight gradients of consecutive steps "
                          "(MOE_STEP_PAIR_WGRAD: one launch per two steps, dW read and written "
                          "once for both; three micro-batch buffer sets); not with the fused "
@@ -453,6 +459,8 @@ def main():
     unit = 6 if pairing else 2  # buffer-set rotation (3 or 2) x paired steps (2)
     if args.group is None:
         args.group = 12 if pairing else 10
+    if args.graph is None:
+        args.graph = "off" if pairing else "on"
     if pairing and args.graph == "on":
         err("bench.py: --pair-wgrad on needs --graph off (paired steps are not captured)")
         sys.exit(2)
@@ -531,6 +539,10 @@ def main():
         launch = f"hipGraph replay ({Gk} steps per graph)" + \
             (f" + {rem} eager step{'s' if rem > 1 else ''}" if rem else "")
     else:
+        # one more group of warm-up steps, as the graph path replays its
+        # captured group once before the timed region
+        L.issue(args.group, 0)
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
         ev0.record(s0)
         L.issue(K, 0)
@@ -590,7 +602,7 @@ def main():
         torch.cuda.synchronize()
 
     # ---- per-kernel achieved rates from the live kernel events
-    work = algorithmic(w, N, T_loc, accumulate=True, fused=L.fused, fcb=L.fcb, pair=L.pair)
+    work = algorithmic(w, N, T_loc, accumulate=True, fused=L.fused, fcb=L.fcb)
     traffic = stored_traffic(w.name) if args.tokens is None else {}
     kernels = {}
     for name, (tot_ms, n) in sorted(kern.items(), key=lambda kv: -kv[1][0]):
@@ -599,10 +611,11 @@ def main():
                "ms_per_step": round(tot_ms / K, 4)}
         step_s = tot_ms / 1e3 / K   # this kernel's time per step
         if name in work:
-            bound, ach, peak, unit, frac = rate(work[name], step_s)
+            t_s = avg_s if name in PER_LAUNCH else step_s
+            bound, ach, peak, unit, frac = rate(work[name], t_s)
             ent.update(bound=bound, achieved=round(ach, 1), unit=unit, frac=round(frac, 4))
             if "flop" in work[name]:
-                ent["mfma_frac"] = round(work[name]["flop"] / step_s / 1e12 / PEAK_BF16_TFLOPS, 4)
+                ent["mfma_frac"] = round(work[name]["flop"] / t_s / 1e12 / PEAK_BF16_TFLOPS, 4)
         if name in traffic:
             ent["traffic"] = traffic[name]
         kernels[name] = ent
@@ -612,7 +625,8 @@ def main():
     dom = max(gemm, key=lambda k: kern[k][0])
     dom_avg_s = kern[dom][0] / 1e3 / kern[dom][1]
     dom_per_step = kern[dom][1] / K
-    per_launch = {u: v / dom_per_step for u, v in work[dom].items()}
+    per_launch = (work[dom] if dom in PER_LAUNCH else
+                  {u: v / dom_per_step for u, v in work[dom].items()})
     bound, ach, peak, unit, frac = rate(per_launch, dom_avg_s)
     roofline = {"kernel": dom, "bound": bound, "achieved": round(ach, 1), "peak": peak,
                 "unit": unit, "frac": round(frac, 4), "traffic": traffic.get(dom),
@@ -621,7 +635,7 @@ def main():
                 "mfma_frac": round(per_launch["flop"] / dom_avg_s / 1e12 / PEAK_BF16_TFLOPS, 4),
                 "launches_per_step": round(dom_per_step, 3),
                 "avg_launch_us": round(dom_avg_s * 1e6, 2)}
-    gemm_flops = sum(work[k]["flop"] * K for k in gemm)
+    gemm_flops = sum(work[k]["flop"] * (kern[k][1] if k in PER_LAUNCH else K) for k in gemm)
     gemm_s = sum(kern[k][0] / 1e3 for k in gemm)
     # the dispatch kernel; with the fused permute there is none (GEMM1 gathers x),
     # and the forward's remaining permute-class kernel, combine, is reported
@@ -729,8 +743,10 @@ def bench_name(sym):
                 cur += ch
             j += 1
         args.append(cur.strip())
-        # wgrad_kernel<GATHER, element type, ROUTER, ACC, GD>
-        return "dwr_mfma" if len(args) > 2 and args[2] == "true" else "wgrad"
+        # wgrad_kernel<GATHER, element type, ROUTER, ACC, GD, PAIR>
+        if len(args) > 2 and args[2] == "true":
+            return "dwr_mfma"
+        return "wgrad_pair" if len(args) > 5 and args[5] == "true" else "wgrad"
     for k, v in _CLASS:
         if k in sym:
             return v
@@ -997,9 +1013,12 @@ def _sum_overlap(args, w, N, T_loc, desc):
     inter = _intersect(g, p)
     ng = sum(1 for r in sel if r[0] in _GEMM_CLASS)
     npm = sum(1 for r in sel if r[0] in _PERM_CLASS)
-    wend = [b for n, a, b in rows if n == "wgrad"]
+    # one routed wgrad per step, or one paired wgrad per two steps
+    paired = any(n == "wgrad_pair" for n, a, b in rows)
+    wend = [b for n, a, b in rows if n == ("wgrad_pair" if paired else "wgrad")]
     half = wend[len(wend) // 2:]
-    step_us = (half[-1] - half[0]) / 1e3 / max(1, len(half) - 1) if len(half) > 1 else float("nan")
+    step_us = ((half[-1] - half[0]) / 1e3 / max(1, len(half) - 1) / (2 if paired else 1)
+               if len(half) > 1 else float("nan"))
     return f"""# Overlap of the two streams: pipelined 1F1B steps, {desc}
 
 Command (run from the repository root on one MI355X):
@@ -1022,7 +1041,7 @@ class: plan, top-k, permute, combine and their backwards.
 | intersection (us) | {_length(inter) / 1e3:.1f} |
 | share of dispatch/combine time under a GEMM | {100 * _length(inter) / max(1, _length(p)):.2f} % |
 | busy (any kernel) union (us) | {_length(busy) / 1e3:.1f} |
-| steady step time under the profiler (us, wgrad to wgrad, second half) | {step_us:.1f} |
+| steady step time under the profiler (us, wgrad to wgrad, second half{", a paired wgrad per two steps" if paired else ""}) | {step_us:.1f} |
 """
 
 
@@ -1087,10 +1106,17 @@ def _sum_phases(args, w, N, T_loc, desc):
         vals = [d[k] for k in sorted(d)]
         tail = vals[len(vals) // 2:]
         rows.append((statistics.median(tail), ph, len(vals), count[ph], sum(vals)))
+    # per step: a phase's median times its occurrences per step (the phases
+    # that run every step occur most often; the weight copies run once per
+    # call, the paired weight gradient once per two steps)
+    steps = max(r[2] for r in rows)
+    per_step = lambda nr: 1.0 if nr > 0.75 * steps else nr / steps
+    rows = [(med * per_step(nr), med, ph, nr, nk, tot) for med, ph, nr, nk, tot in rows]
     rows.sort(reverse=True)
     total = sum(r[0] for r in rows)
     lines = [f"| `{ph}` | {nr} | {nk} | {', '.join(sorted(names[ph]))} | {tot:.1f} | {med:.1f} | "
-             f"{100 * med / max(total, 1e-9):.1f} |" for med, ph, nr, nk, tot in rows]
+             f"{per:.1f} | {100 * per / max(total, 1e-9):.1f} |"
+             for per, med, ph, nr, nk, tot in rows]
     table = "\n".join(lines)
     return f"""# Phases of the step (roctx ranges): {desc}
 
@@ -1112,11 +1138,15 @@ correlation id), summarised by `python bench.py --summarize phases --workload
 {w.name} --inputs <kernel trace> <HIP API trace> <marker trace>`.  `per
 occurrence` is the median, over the second half of a phase's occurrences, of
 the summed kernel time of one range (the first calls of a process run slower
-while the clocks settle); `share` is its part of the sum of those medians.
+while the clocks settle); `per step` scales it by the phase's occurrences
+per step for the phases that run less than once a step (the weight copies
+once per call, the paired weight gradient once per two steps; the phases
+that run in most steps count once), and `share` is its part of the sum of
+the per-step times.
 Kernels outside every range: {unmatched}.
 
-| phase | occurrences | kernels | kernel names | GPU time, all (us) | per occurrence (us) | share % |
-|---|---|---|---|---|---|---|
+| phase | occurrences | kernels | kernel names | GPU time, all (us) | per occurrence (us) | per step (us) | share % |
+|---|---|---|---|---|---|---|---|
 {table}
 """
 

@@ -1491,7 +1491,7 @@ void wgrad_pair_t(const moe_shape* s, const WgrOps& A, const WgrOps& B, float* d
   const WgSecond sec{(const uint16_t*)B.xp, (const uint16_t*)B.a, (const uint16_t*)B.dh,
                      (const uint16_t*)B.dyp, B.offsets};
   auto go = [&](auto acc) {
-    MOE_LAUNCH("wgrad", st,
+    MOE_LAUNCH("wgrad_pair", st,
                (wgrad_kernel<false, E, false, decltype(acc)::value, false, true>
                 <<<grid, 512, 0, st>>>((const uint16_t*)A.xp, nullptr, (int)s->K,
                                        (const uint16_t*)A.a, (const uint16_t*)A.dh,
