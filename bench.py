@@ -393,10 +393,10 @@ def main():
     ap.add_argument("--pair-wgrad", choices=("on", "off"), default="on",
                     help="pair the routed experts' weight gradients of consecutive steps "
                          "(MOE_STEP_PAIR_WGRAD: one launch per two steps, dW read and written "
-                         "once for both; three micro-batch buffer sets); not with the fused "
-                         "paths, and with --graph off only (the library rejects paired steps "
-                         "under stream capture: a captured run ended in a host crash whose "
-                         "cause is not found)")
+                         "once for both; three micro-batch buffer sets), the default; not with "
+                         "the fused paths, and with --graph off only (the library rejects "
+                         "paired steps under stream capture: a captured run ended in a host "
+                         "crash whose cause is not found)")
     ap.add_argument("--group", type=int, default=None,
                     help="steps per moe_overlap_steps call and per captured graph: a "
                          "multiple of 2, of 6 with --pair-wgrad on (default 10, 12)")
