@@ -963,12 +963,15 @@ static int bwd_wgrad(const StepCtx& c, const moe_mb* B, hipStream_t q) {
 }
 
 // The routed experts' weight gradients of micro-batches A (deferred by the
-// step before) and B in one launch (materialised xp and dy_p).
-static int bwd_wgrad_pair(const StepCtx& c, const moe_mb* A, const moe_mb* B, hipStream_t q) {
+// step before) and B in one launch (materialised xp and dy_p).  B's step
+// accumulates (the pairing plan requires it), so the sum starts from the
+// previous values exactly when A's step asked for that: accumulate_A.
+static int bwd_wgrad_pair(const StepCtx& c, const moe_mb* A, bool accumulate_A,
+                          const moe_mb* B, hipStream_t q) {
   const PhaseRange pr("moe.expert_wgrad_pair");
   return launch_ffn_wgrad_pair(c.s, WgrOps{A->xp, A->a, A->dh, A->dyp, A->offsets},
                                WgrOps{B->xp, B->a, B->dh, B->dyp, B->offsets}, c.st->dW_gu,
-                               c.st->dW_down, (c.st->accumulate & MOE_ACCUM_DW) != 0, q);
+                               c.st->dW_down, accumulate_A, q);
 }
 
 // Host-side checks of one step description (flags, route mode, buffers,
@@ -1233,11 +1236,12 @@ struct AccumOrder {
 // With PAIR_WGRAD, rw says what the routed experts' weight gradient does:
 // kRwOwn (B's alone), kRwDefer (none: record ev->pair once dh is written, the
 // next step pairs it) or kRwPair (B's together with prev's, the micro-batch
-// deferred by the step before, after waiting for ev->pair).
+// deferred by the step before, whose step's accumulate flag is prev_acc,
+// after waiting for ev->pair).
 enum { kRwOwn, kRwDefer, kRwPair };
 static int bwd_chain(const StepCtx& c, const moe_mb* B, hipStream_t q, bool mid, bool eager,
                      bool skip, AccumOrder& ord, int rw = kRwOwn,
-                     const moe_mb* prev = nullptr) {
+                     const moe_mb* prev = nullptr, bool prev_acc = false) {
   const bool shared = has_shared(c);
   const bool dwr = c.router && c.st->dW_r;
   const MultiEvents* ev = ord.ev;
@@ -1250,7 +1254,7 @@ static int bwd_chain(const StepCtx& c, const moe_mb* B, hipStream_t q, bool mid,
     TRY(wait(ev->dw, ord.dw));
     if (rw == kRwPair) {
       HIPTRY(hipStreamWaitEvent(q, ev->pair, 0));
-      TRY(bwd_wgrad_pair(c, prev, B, q));
+      TRY(bwd_wgrad_pair(c, prev, prev_acc, B, q));
     } else {
       TRY(bwd_wgrad(c, B, q));
     }
@@ -1357,15 +1361,19 @@ extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, h
   // SKIP_WGRAD leaves the weight gradients of the last step's backward
   // micro-batch to the caller; the earlier steps' run as usual
   const bool skip_last = (flags & MOE_STEP_SKIP_WGRAD) != 0;
-  // PAIR_WGRAD: steps j and j + 1 (both with a backward micro-batch, the last
-  // step left out with SKIP_WGRAD) pair their routed weight gradients, from
-  // the first step on; an unpaired step keeps its own
+  // PAIR_WGRAD: steps j and j + 1 (both with a backward micro-batch, step
+  // j + 1 accumulating, the last step left out with SKIP_WGRAD) pair their
+  // routed weight gradients, from the first step on; an unpaired step keeps
+  // its own
   const bool pair = (flags & MOE_STEP_PAIR_WGRAD) != 0;
   std::vector<int> rw(n, kRwOwn);
   if (pair) {
     const int last = skip_last ? n - 1 : n;  // steps that may pair
     for (int j = 0; j + 1 < last; ++j) {
       if (!steps[j].bwd || !steps[j + 1].bwd) continue;
+      // step j + 1 must add to what step j leaves (an overwriting step j + 1
+      // discards step j's weight gradients, so there is no sum to pair)
+      if (!(steps[j + 1].accumulate & MOE_ACCUM_DW)) continue;
       if (fwd_overwrites_wgrad_inputs(steps[j + 1].fwd, steps[j].bwd))
         return set_error(MOE_ERR_ARG,
                          "moe_overlap_steps: PAIR_WGRAD: step %d forwards into a buffer that "
@@ -1425,7 +1433,8 @@ extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, h
     }
     if (st->bwd) {
       TRY(bwd_chain(c, st->bwd, Q, mid, eager, skip_last && j == n - 1, ord, rw[j],
-                    rw[j] == kRwPair ? steps[j - 1].bwd : nullptr));
+                    rw[j] == kRwPair ? steps[j - 1].bwd : nullptr,
+                    rw[j] == kRwPair && (steps[j - 1].accumulate & MOE_ACCUM_DW) != 0));
       HIPTRY(hipEventRecord(ev->bend[j & 1], Q));
       bend_rec[j & 1] = true;
     }

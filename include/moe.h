@@ -111,11 +111,14 @@ extern "C" {
                                    gate is applied in float32 instead of through a
                                    rounded dy_p), not bit for bit               */
 #define MOE_STEP_PAIR_WGRAD 64 /* moe_overlap_steps: the routed experts' weight
-                                 gradients of steps 2i and 2i + 1 in one launch
-                                 (moe_ffn_wgrad_pair) in step 2i + 1: step 2i's
-                                 backward micro-batch must stay intact until
-                                 then (step 2i + 1 may not forward into its
-                                 buffers); not with the fused permute or the
+                                 gradients of steps j and j + 1 in one launch
+                                 (moe_ffn_wgrad_pair) in step j + 1, pairs
+                                 formed from the first step on where step j + 1
+                                 accumulates (MOE_ACCUM_DW); the launch
+                                 overwrites or accumulates as step j asks.
+                                 Step j's backward micro-batch must stay intact
+                                 until then (step j + 1 may not forward into
+                                 its buffers); not with the fused permute or the
                                  fused combine backward, and not under stream
                                  capture (MOE_ERR_UNSUPPORTED) */
 #define MOE_STEP_FUSED_SCATTER 128 /* the unpermute fused into GEMM2: its epilogue

@@ -91,23 +91,30 @@ def test_wgrad_pair_against_oracle(prec, countsA, countsB):
         assert torch.equal(again[0], dW[0]) and torch.equal(again[1], dW[1])
 
 
-def _steps(s, w, m, W, dW, ws, n, W_r, bias, rot):
+def _steps(s, w, m, W, dW, ws, n, W_r, bias, rot, overwrite=()):
     """n 1F1B steps over buffer sets m: step j forwards m[j % rot] (none in
-    the last step) and back-propagates m[(j - 1) % rot] (none in the first)."""
+    the last step) and back-propagates m[(j - 1) % rot] (none in the first);
+    the steps in `overwrite` overwrite the weight gradients, the others add."""
     return [M.make_step(s, M.MOE_ROUTE_TOPK, W[0], W[1], dW[0], dW[1], ws,
                         fwd=m[j % rot] if j < n - 1 else None,
                         bwd=m[(j - 1) % rot] if j > 0 else None, W_r=W_r, bias=bias,
-                        dW_r=dW[2], accumulate=M.MOE_ACCUM_DW)
+                        dW_r=dW[2], accumulate=0 if j in overwrite else M.MOE_ACCUM_DW)
             for j in range(n)]
 
 
-@pytest.mark.parametrize("name,n,flags", [
-    ("zipf_bf16", 8, M.MOE_STEP_MID_WGRAD),
-    ("zipf_bf16", 7, 0),
-    ("zipf_bf16", 9, M.MOE_STEP_SKIP_WGRAD),
-    ("mid_f32", 6, M.MOE_STEP_MID_WGRAD),
+@pytest.mark.parametrize("name,n,flags,overwrite", [
+    ("zipf_bf16", 8, M.MOE_STEP_MID_WGRAD, ()),
+    ("zipf_bf16", 7, 0, ()),
+    ("zipf_bf16", 9, M.MOE_STEP_SKIP_WGRAD, ()),
+    ("mid_f32", 6, M.MOE_STEP_MID_WGRAD, ()),
+    # the first backward overwrites: its pair starts from zero
+    ("zipf_bf16", 7, M.MOE_STEP_MID_WGRAD, (1,)),
+    # the second overwrites: steps 1 and 2 do not pair (2 discards 1's sums)
+    ("zipf_bf16", 7, 0, (2,)),
+    # an overwrite in the middle of the run
+    ("mid_f32", 8, M.MOE_STEP_MID_WGRAD, (4,)),
 ])
-def test_pair_steps_pipelined_equals_serialized(name, n, flags):
+def test_pair_steps_pipelined_equals_serialized(name, n, flags, overwrite):
     w = {
         "zipf_bf16": Workload("zipf_bf16", T=700, d=192, F=320, E=64, e_lo=0, E_l=8, K=6,
                               dtype="bf16", route="topk", zipf_s=1.1),
@@ -115,7 +122,7 @@ def test_pair_steps_pipelined_equals_serialized(name, n, flags):
                             dtype="f32", route="topk"),
     }[name]
     prec = w.dtype
-    log(f"[pair steps] {name} n={n} flags={flags}")
+    log(f"[pair steps] {name} n={n} flags={flags} overwrite={overwrite}")
     inp = make_inputs(w, seed=3, microbatches=2)
     s = M.shape_of(w)
     D = lambda a: dev(a, prec)
@@ -134,7 +141,8 @@ def test_pair_steps_pipelined_equals_serialized(name, n, flags):
               torch.full((w.E_l, w.d, w.F), 0.25, device="cuda"),
               torch.full((w.d, w.E), 0.25, device="cuda"))
         ws = torch.empty(M.moe_step_workspace_bytes(s), dtype=torch.uint8, device="cuda")
-        M.moe_overlap_steps(_steps(s, w, m, W, dW, ws, n, W_r, bias, 3), s0, s1, fl)
+        M.moe_overlap_steps(_steps(s, w, m, W, dW, ws, n, W_r, bias, 3, overwrite), s0, s1,
+                            fl)
         if flags & M.MOE_STEP_SKIP_WGRAD:  # the caller's delayed wgrad of the last step
             b = m[(n - 2) % 3]
             M.moe_ffn_wgrad(s, b.xp, b.a, b.dh, b.dyp, b.offsets, dW[0], dW[1],
