@@ -34,9 +34,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
 DEFAULT_WORKLOAD = "ep1_128exp_bf16"
 OVERLAP_WORKLOAD = "two_microbatch_bf16"
 
-GEMM_KERNELS = ("ffn_gate_up", "ffn_down", "dgrad_act", "dgrad_in", "wgrad", "wgrad_pair")
+GEMM_KERNELS = ("ffn_gate_up", "ffn_down", "dgrad_act", "dgrad_in", "wgrad", "wgrad_multi")
 # kernels whose algorithmic work is given per launch (the others' per step)
-PER_LAUNCH = ("wgrad_pair",)
+PER_LAUNCH = ("wgrad_multi",)
 COPY_PROBE_BYTES = 1 << 30
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
@@ -46,7 +46,7 @@ def err(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic(w, N, T_loc, accumulate=True, fused=False, fcb=False):
+def algorithmic(w, N, T_loc, accumulate=True, fused=False, fcb=False, group=2):
     """Algorithmic work per step of each kernel (one launch of each, plus the
     shared expert's launches of the same GEMMs over all T tokens when the
     workload has one): {name: {"flop": F, "byte": B}}.  Bytes count one pass
@@ -54,9 +54,10 @@ def algorithmic(w, N, T_loc, accumulate=True, fused=False, fcb=False):
     expert weights, and wgrad's the float32 weight gradients (read and written
     with accumulate, written without).  fused: the permute fused into GEMM1
     and wgrad (x rows instead of xp); fcb: the fused combine backward (dout
-    rows instead of dy_p, ag written by dgrad_act).  `wgrad_pair` (the paired
-    weight gradient, one launch per two steps) is given per launch: both
-    micro-batches' operands and one pass over the float32 weight gradients."""
+    rows instead of dy_p, ag written by dgrad_act).  `wgrad_multi` (the grouped
+    weight gradient, one launch per `group` steps) is given per launch: the
+    group's micro-batches' operands and one pass over the float32 weight
+    gradients."""
     d, F, T, K, E, E_l = w.d, w.F, w.T, w.K, w.E, w.E_l
     b = 4 if w.dtype == "f32" else 2
     Fs = w.F_s
@@ -81,8 +82,8 @@ def algorithmic(w, N, T_loc, accumulate=True, fused=False, fcb=False):
         "wgrad": {"flop": 6.0 * N * d * F + 6.0 * T * d * Fs,
                   "byte": dyin + N * (F + 2 * F) * b + xin + T * (2 * d + 3 * Fs) * b * (Fs > 0)
                   + dW * (2 if accumulate else 1)},
-        "wgrad_pair": {"flop": 2 * (6.0 * N * d * F),
-                       "byte": 2 * (dyin + N * (F + 2 * F) * b + xin)
+        "wgrad_multi": {"flop": group * (6.0 * N * d * F),
+                        "byte": group * (dyin + N * (F + 2 * F) * b + xin)
                        + 4.0 * E_l * 3 * F * d * (2 if accumulate else 1)},
         "router": {"flop": 2.0 * T * d * E, "byte": T * d * b + d * E * b + 4.0 * T * E},
         # router weight gradient x^T dlogits on the matrix cores (bf16 data);
@@ -227,6 +228,7 @@ class Layer:
     workload on the GPU, and the issue of 1F1B steps on two streams."""
 
     def __init__(self, w, args, s0, s1):
+        import numpy as np
         import torch
         import combine_expert_ffn_amd as M
         from combine_expert_ffn_amd.inputs import make_inputs
@@ -250,11 +252,12 @@ class Layer:
         self.fused = args.fused_permute == "on"
         self.fcb = args.fused_combine_bwd == "on"
         self.scatter = args.fused_scatter == "on"
-        # the paired weight gradient keeps the micro-batch back-propagated in
-        # step j until step j + 1: three buffer sets in rotation
-        self.pair = (args.pair_wgrad == "on" and args.pipeline == "on" and
+        # the grouped weight gradient keeps the micro-batches back-propagated
+        # in a group's steps until its last step: group + 1 buffer sets rotate
+        self.pair = (args.wgrad_group > 1 and args.pipeline == "on" and
                      not (self.fused or self.fcb))
-        self.R = 3 if self.pair else 2
+        self.group = args.wgrad_group if self.pair else 1
+        self.R = self.group + 1 if self.pair else 2
         self.pipelined = args.pipeline == "on"
         self.G = args.group
         # flags of every step: the fused permute and the wgrad's place in the
@@ -263,7 +266,7 @@ class Layer:
                       (M.MOE_STEP_FUSED_COMBINE_BWD if self.fcb else 0) |
                       (M.MOE_STEP_FUSED_SCATTER if self.scatter else 0) |
                       (M.MOE_STEP_MID_WGRAD if args.wgrad_order == "mid" else 0) |
-                      (M.MOE_STEP_PAIR_WGRAD if self.pair else 0))
+                      ({2: M.MOE_STEP_PAIR_WGRAD, 4: M.MOE_STEP_GROUP4_WGRAD}.get(self.group, 0)))
         self.shared = None
         if w.F_s:  # a shared expert beside the routed ones
             self.shared = (D(inp["W_gu_s"]), D(inp["W_down_s"]), z(2 * w.F_s, w.d),
@@ -273,13 +276,20 @@ class Layer:
                                              F_s=w.F_s, fused_bwd=self.fcb)
         self.mbs = [mk(inp["x"], inp["dout"], inp["gates"]),
                     mk(inp["x_b"], inp["dout_b"], inp.get("gates_b"))]
-        if self.R == 3:  # the third set: the first one's tokens in reverse order
-            g = inp["gates"]
-            self.mbs.append(mk(inp["x"][::-1].copy(), inp["dout"][::-1].copy(),
-                               None if g is None else g[::-1].copy()))
+        # more sets: the two draws' tokens in reverse order, then the first
+        # draw's rolled by a few tokens
+        for k in range(2, self.R):
+            src = "" if k % 2 == 0 else "_b"
+            g = inp.get("gates" + src)
+            if k < 4:
+                fx = lambda a: a[::-1].copy()
+            else:
+                fx = lambda a: np.roll(a, 7 * k, axis=0)
+            self.mbs.append(mk(fx(inp["x" + src]), fx(inp["dout" + src]),
+                               None if g is None else fx(g)))
         self.i = 0  # steps issued so far (after the priming forward)
         M.moe_overlap_step(self.make_step(self.mbs[0], None), s0, s1,
-                           self.FLAGS & ~M.MOE_STEP_PAIR_WGRAD)
+                           self.FLAGS & ~(M.MOE_STEP_PAIR_WGRAD | M.MOE_STEP_GROUP4_WGRAD))
 
     def make_step(self, fwd, bwd):
         M = self.M
@@ -390,16 +400,17 @@ def main():
                     help="run the overlapped steps G at a time through moe_overlap_steps, the "
                          "streams' roles alternating so consecutive steps overlap (on), or one "
                          "moe_overlap_step call per step, joined at every step boundary (off)")
-    ap.add_argument("--pair-wgrad", choices=("on", "off"), default="on",
-                    help="pair the routed experts' weight gradients of consecutive steps "
-                         "(MOE_STEP_PAIR_WGRAD: one launch per two steps, dW read and written "
-                         "once for both; three micro-batch buffer sets), the default; not with "
-                         "the fused paths, and with --graph off only (the library rejects "
-                         "paired steps under stream capture: a captured run ended in a host "
-                         "crash whose cause is not found)")
+    ap.add_argument("--wgrad-group", type=int, choices=(1, 2, 4), default=4,
+                    help="steps whose routed experts' weight gradients run as one launch "
+                         "(2: MOE_STEP_PAIR_WGRAD, 4: MOE_STEP_GROUP4_WGRAD; dW read and "
+                         "written once per group; group + 1 micro-batch buffer sets); not "
+                         "with the fused paths, and with --graph off only (the library "
+                         "rejects grouped steps under stream capture: a captured run of "
+                         "paired steps ended in a host crash whose cause is not found)")
     ap.add_argument("--group", type=int, default=None,
                     help="steps per moe_overlap_steps call and per captured graph: a "
-                         "multiple of 2, of 6 with --pair-wgrad on (default 10, 12)")
+                         "multiple of 2, and of the weight-gradient group (default 10, or "
+                         "12 with grouped weight gradients)")
     ap.add_argument("--ab-rounds", type=int, default=6,
                     help="rounds of the alternating overlapped / serialized comparison")
     ap.add_argument("--overlap-workload", default=OVERLAP_WORKLOAD,
@@ -454,15 +465,17 @@ def main():
         err("bench.py: no GPU visible")
         sys.exit(1)
     M.lib()  # fails loudly if libmoe.so is not built
-    pairing = args.pair_wgrad == "on" and args.pipeline == "on" and \
+    pairing = args.wgrad_group > 1 and args.pipeline == "on" and \
         args.fused_permute == "off" and args.fused_combine_bwd == "off"
-    unit = 6 if pairing else 2  # buffer-set rotation (3 or 2) x paired steps (2)
+    # steps after which a captured graph's buffer sets are back in their roles
+    # (graphs hold ungrouped steps only: two sets)
+    unit = args.wgrad_group if pairing else 2
     if args.group is None:
         args.group = 12 if pairing else 10
     if args.graph is None:
         args.graph = "off" if pairing else "on"
     if pairing and args.graph == "on":
-        err("bench.py: --pair-wgrad on needs --graph off (paired steps are not captured)")
+        err("bench.py: grouped weight gradients need --graph off (they are not captured)")
         sys.exit(2)
     if args.group < unit or args.group % unit:
         err(f"bench.py: --group must be a multiple of {unit}")
@@ -602,7 +615,7 @@ def main():
         torch.cuda.synchronize()
 
     # ---- per-kernel achieved rates from the live kernel events
-    work = algorithmic(w, N, T_loc, accumulate=True, fused=L.fused, fcb=L.fcb)
+    work = algorithmic(w, N, T_loc, accumulate=True, fused=L.fused, fcb=L.fcb, group=L.group)
     traffic = stored_traffic(w.name) if args.tokens is None else {}
     kernels = {}
     for name, (tot_ms, n) in sorted(kern.items(), key=lambda kv: -kv[1][0]):
@@ -668,7 +681,7 @@ def main():
                                               if args.wgrad_order == "mid" else
                                               "wgrad deferred to the end"),
                    "weight_grads": "float32, accumulated every step" + (
-                       "; the routed experts' of steps 2i and 2i+1 in one launch"
+                       f"; the routed experts' of each group of {L.group} steps in one launch"
                        if L.pair else ""),
                    "launch": launch,
                    "pipeline": (f"moe_overlap_steps, {G} steps per call, stream roles "
@@ -746,7 +759,7 @@ def bench_name(sym):
         # wgrad_kernel<GATHER, element type, ROUTER, ACC, GD, PAIR>
         if len(args) > 2 and args[2] == "true":
             return "dwr_mfma"
-        return "wgrad_pair" if len(args) > 5 and args[5] == "true" else "wgrad"
+        return "wgrad_multi" if len(args) > 5 and args[5] == "true" else "wgrad"
     for k, v in _CLASS:
         if k in sym:
             return v
@@ -817,7 +830,8 @@ def _sum_kernels(args, w, N, T_loc, desc):
             by.setdefault(name, []).append((b - a) / 1e3)
     total = sum(sum(v) for v in by.values())
     work = (algorithmic(w, N, T_loc, fused=args.fused_permute == "on",
-                        fcb=args.fused_combine_bwd == "on") if N is not None else {})
+                        fcb=args.fused_combine_bwd == "on", group=args.wgrad_group)
+            if N is not None else {})
     lines = []
     for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
         h = v[len(v) // 2:]
@@ -873,7 +887,8 @@ def _sum_traffic(args, w, N, T_loc, desc):
 
     aF, aW = per_kernel(F, "FETCH_SIZE"), per_kernel(W, "WRITE_SIZE")
     work = (algorithmic(w, N, T_loc, fused=args.fused_permute == "on",
-                        fcb=args.fused_combine_bwd == "on") if N is not None else {})
+                        fcb=args.fused_combine_bwd == "on", group=args.wgrad_group)
+            if N is not None else {})
     rec = {"workload": w.name, "copy_probe_bytes": COPY_PROBE_BYTES,
            "fetch_factor": round(ff, 4), "write_factor": round(fw, 4), "kernels": {}}
     lines = []
@@ -925,7 +940,8 @@ Machine-readable record (bench.py reads `hbm_bytes_per_launch` while the kernel'
 def _sum_mfma(args, w, N, T_loc, desc):
     rec = read_counters(args.inputs[0])
     work = (algorithmic(w, N, T_loc, fused=args.fused_permute == "on",
-                        fcb=args.fused_combine_bwd == "on") if N is not None else {})
+                        fcb=args.fused_combine_bwd == "on", group=args.wgrad_group)
+            if N is not None else {})
     SIMDS, XCDS = 1024, 8
     peak_per_clk = PEAK_BF16_TFLOPS * 1e12 / 2.4e9
     agg = collections.defaultdict(list)
@@ -1013,11 +1029,12 @@ def _sum_overlap(args, w, N, T_loc, desc):
     inter = _intersect(g, p)
     ng = sum(1 for r in sel if r[0] in _GEMM_CLASS)
     npm = sum(1 for r in sel if r[0] in _PERM_CLASS)
-    # one routed wgrad per step, or one paired wgrad per two steps
-    paired = any(n == "wgrad_pair" for n, a, b in rows)
-    wend = [b for n, a, b in rows if n == ("wgrad_pair" if paired else "wgrad")]
+    # one routed wgrad per step, or one grouped wgrad per args.wgrad_group steps
+    grouped = any(n == "wgrad_multi" for n, a, b in rows)
+    per = args.wgrad_group if grouped else 1
+    wend = [b for n, a, b in rows if n == ("wgrad_multi" if grouped else "wgrad")]
     half = wend[len(wend) // 2:]
-    step_us = ((half[-1] - half[0]) / 1e3 / max(1, len(half) - 1) / (2 if paired else 1)
+    step_us = ((half[-1] - half[0]) / 1e3 / max(1, len(half) - 1) / per
                if len(half) > 1 else float("nan"))
     return f"""# Overlap of the two streams: pipelined 1F1B steps, {desc}
 
@@ -1041,7 +1058,7 @@ class: plan, top-k, permute, combine and their backwards.
 | intersection (us) | {_length(inter) / 1e3:.1f} |
 | share of dispatch/combine time under a GEMM | {100 * _length(inter) / max(1, _length(p)):.2f} % |
 | busy (any kernel) union (us) | {_length(busy) / 1e3:.1f} |
-| steady step time under the profiler (us, wgrad to wgrad, second half{", a paired wgrad per two steps" if paired else ""}) | {step_us:.1f} |
+| steady step time under the profiler (us, wgrad to wgrad, second half{f", a grouped wgrad per {per} steps" if grouped else ""}) | {step_us:.1f} |
 """
 
 
@@ -1108,7 +1125,7 @@ def _sum_phases(args, w, N, T_loc, desc):
         rows.append((statistics.median(tail), ph, len(vals), count[ph], sum(vals)))
     # per step: a phase's median times its occurrences per step (the phases
     # that run every step occur most often; the weight copies run once per
-    # call, the paired weight gradient once per two steps)
+    # call, the grouped weight gradient once per group of steps)
     steps = max(r[2] for r in rows)
     per_step = lambda nr: 1.0 if nr > 0.75 * steps else nr / steps
     rows = [(med * per_step(nr), med, ph, nr, nk, tot) for med, ph, nr, nk, tot in rows]
@@ -1140,7 +1157,7 @@ occurrence` is the median, over the second half of a phase's occurrences, of
 the summed kernel time of one range (the first calls of a process run slower
 while the clocks settle); `per step` scales it by the phase's occurrences
 per step for the phases that run less than once a step (the weight copies
-once per call, the paired weight gradient once per two steps; the phases
+once per call, the grouped weight gradient once per group of steps; the phases
 that run in most steps count once), and `share` is its part of the sum of
 the per-step times.
 Kernels outside every range: {unmatched}.

@@ -12,12 +12,13 @@ from __future__ import annotations
 import ctypes as C
 
 from ._lib import (  # noqa: F401
-    LIB_PATH, MB_FIELDS, MoeError, MoeMB, MoeShape, MoeStep, check, lib,
+    LIB_PATH, MB_FIELDS, MoeError, MoeMB, MoeShape, MoeStep, MoeWgradOps, check, lib,
     MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MOE_ERR_HIP,
     MOE_ERR_UNSUPPORTED, MOE_ERR_ARG, MOE_F32, MOE_BF16, MOE_F16, MOE_ROUTE_TOPK,
     MOE_ROUTE_TOPK_FROM_LOGITS, MOE_ROUTE_FORCE_BALANCE, MOE_ACCUM_DX, MOE_ACCUM_DW,
     MOE_STEP_SERIALIZE, MOE_STEP_EAGER_WGRAD, MOE_STEP_SKIP_WGRAD, MOE_STEP_FUSED_PERMUTE,
     MOE_STEP_MID_WGRAD, MOE_STEP_FUSED_COMBINE_BWD, MOE_STEP_PAIR_WGRAD, MOE_STEP_FUSED_SCATTER,
+    MOE_STEP_GROUP4_WGRAD,
 )
 
 
@@ -347,6 +348,22 @@ def moe_ffn_wgrad_pair(s, xp, a, dh, dyp, offsets, xp2, a2, dh2, dyp2, offsets2,
     check(lib().moe_ffn_wgrad_pair(C.byref(s), _p(xp), _p(a), _p(dh), _p(dyp), _p(offsets),
                                    _p(xp2), _p(a2), _p(dh2), _p(dyp2), _p(offsets2), _p(dW_gu),
                                    _p(dW_down), int(accumulate), _stream(stream)))
+
+
+def moe_ffn_wgrad_multi(s, ops, dW_gu, dW_down, accumulate=0, stream=None):
+    """ops: a list of (xp, a, dh, dyp, offsets), one per micro-batch, 1 to 4."""
+    cap, d, F, E_l = s.T * s.K, s.d, s.F, s.E_l
+    fn = "moe_ffn_wgrad_multi"
+    arr = (MoeWgradOps * max(1, len(ops)))()
+    for i, (x_, a_, h_, y_, o) in enumerate(ops):
+        _chk_ffn(s, fn, o, False, False, False,
+                 **{f"xp{i}": (x_, cap * d, _DATA), f"a{i}": (a_, cap * F, _DATA),
+                    f"dh{i}": (h_, cap * 2 * F, _DATA), f"dyp{i}": (y_, cap * d, _DATA)})
+        arr[i] = MoeWgradOps(_p(x_), _p(a_), _p(h_), _p(y_), _p(o))
+    _chk(s, fn, "dW_gu", dW_gu, _F32, E_l * 2 * F * d)
+    _chk(s, fn, "dW_down", dW_down, _F32, E_l * d * F)
+    check(lib().moe_ffn_wgrad_multi(C.byref(s), len(ops), arr, _p(dW_gu), _p(dW_down),
+                                    int(accumulate), _stream(stream)))
 
 
 def moe_ffn_wgrad_gather(s, x, pair_of_row, a, dh, dyp, offsets, dW_gu, dW_down, accumulate=0,

@@ -38,6 +38,7 @@ MOE_STEP_MID_WGRAD = 16
 MOE_STEP_FUSED_COMBINE_BWD = 32
 MOE_STEP_PAIR_WGRAD = 64
 MOE_STEP_FUSED_SCATTER = 128
+MOE_STEP_GROUP4_WGRAD = 256
 
 
 class MoeShape(C.Structure):
@@ -54,6 +55,10 @@ MB_FIELDS = ["x", "logits", "idx", "gates", "counts", "offsets", "row_of_pair",
 
 class MoeMB(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in MB_FIELDS]
+
+
+class MoeWgradOps(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("xp", "a", "dh", "dyp", "offsets")]
 
 
 class MoeStep(C.Structure):
@@ -98,6 +103,8 @@ SIGNATURES = {
     "moe_ffn_wgrad_pair": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                      C.c_int, _P]),
     "moe_ffn_wgrad_gather": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, C.c_int, _P]),
+    "moe_ffn_wgrad_multi": (C.c_int, [_SP, C.c_int, C.POINTER(MoeWgradOps), _P, _P, C.c_int,
+                                      _P]),
     "moe_ffn_dgrad_gather": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        C.c_size_t, _P]),
     "moe_ffn_wgrad_fused": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, C.c_int, _P]),

@@ -544,9 +544,37 @@ int moe_ffn_wgrad_pair(const moe_shape* s, const void* xp, const void* a, const 
   if (accumulate & ~(MOE_ACCUM_DX | MOE_ACCUM_DW))
     return set_error(MOE_ERR_ARG, "moe_ffn_wgrad_pair: unknown accumulate bits 0x%x",
                      accumulate);
-  return launch_ffn_wgrad_pair(s, WgrOps{xp, a, dh, dyp, offsets},
-                               WgrOps{xp2, a2, dh2, dyp2, offsets2}, dW_gu, dW_down,
-                               (accumulate & MOE_ACCUM_DW) != 0, stream);
+  const WgrOps ops[2] = {WgrOps{xp, a, dh, dyp, offsets}, WgrOps{xp2, a2, dh2, dyp2, offsets2}};
+  return launch_ffn_wgrad_multi(s, ops, 2, dW_gu, dW_down, (accumulate & MOE_ACCUM_DW) != 0,
+                                stream);
+}
+
+int moe_ffn_wgrad_multi(const moe_shape* s, int n, const moe_wgrad_ops* ops, float* dW_gu,
+                        float* dW_down, int accumulate, hipStream_t stream) {
+  g_err[0] = 0;
+  if (int rc = validate_shape(s)) return rc;
+  REQUIRE(ops);
+  REQUIRE(dW_gu);
+  REQUIRE(dW_down);
+  if (n < 1 || n > kWgGroupMax)
+    return set_error(MOE_ERR_ARG, "moe_ffn_wgrad_multi: n = %d outside [1, %d]", n,
+                     kWgGroupMax);
+  if (accumulate & ~(MOE_ACCUM_DX | MOE_ACCUM_DW))
+    return set_error(MOE_ERR_ARG, "moe_ffn_wgrad_multi: unknown accumulate bits 0x%x",
+                     accumulate);
+  WgrOps w[kWgGroupMax];
+  for (int i = 0; i < n; ++i) {
+    const moe_wgrad_ops& o = ops[i];
+    if (!o.xp || !o.a || !o.dh || !o.dyp || !o.offsets)
+      return set_error(MOE_ERR_NULL, "moe_ffn_wgrad_multi: an operand of micro-batch %d is NULL",
+                       i);
+    w[i] = WgrOps{o.xp, o.a, o.dh, o.dyp, o.offsets};
+  }
+  const bool acc = (accumulate & MOE_ACCUM_DW) != 0;
+  if (n == 1)
+    return launch_ffn_wgrad(s, w[0].xp, nullptr, w[0].a, w[0].dh, w[0].dyp, w[0].offsets, dW_gu,
+                            dW_down, acc, stream);
+  return launch_ffn_wgrad_multi(s, w, n, dW_gu, dW_down, acc, stream);
 }
 
 int moe_ffn_wgrad_gather(const moe_shape* s, const void* x, const int32_t* pair_of_row,
@@ -962,16 +990,19 @@ static int bwd_wgrad(const StepCtx& c, const moe_mb* B, hipStream_t q) {
                           c.fcb ? B->pair_of_row : nullptr);
 }
 
-// The routed experts' weight gradients of micro-batches A (deferred by the
-// step before) and B in one launch (materialised xp and dy_p).  B's step
-// accumulates (the pairing plan requires it), so the sum starts from the
-// previous values exactly when A's step asked for that: accumulate_A.
-static int bwd_wgrad_pair(const StepCtx& c, const moe_mb* A, bool accumulate_A,
-                          const moe_mb* B, hipStream_t q) {
-  const PhaseRange pr("moe.expert_wgrad_pair");
-  return launch_ffn_wgrad_pair(c.s, WgrOps{A->xp, A->a, A->dh, A->dyp, A->offsets},
-                               WgrOps{B->xp, B->a, B->dh, B->dyp, B->offsets}, c.st->dW_gu,
-                               c.st->dW_down, accumulate_A, q);
+// The routed experts' weight gradients of the micro-batches deferred by the
+// steps before (prev[0 .. np), in step order) and of B in one launch
+// (materialised xp and dy_p).  The later steps of a group accumulate (the
+// grouping plan requires it), so the sum starts from the previous values
+// exactly when the group's first step asked for that: first_acc.
+static int bwd_wgrad_group(const StepCtx& c, const moe_mb* const* prev, int np, bool first_acc,
+                           const moe_mb* B, hipStream_t q) {
+  const PhaseRange pr("moe.expert_wgrad_group");
+  WgrOps ops[kWgGroupMax];
+  for (int i = 0; i < np; ++i)
+    ops[i] = WgrOps{prev[i]->xp, prev[i]->a, prev[i]->dh, prev[i]->dyp, prev[i]->offsets};
+  ops[np] = WgrOps{B->xp, B->a, B->dh, B->dyp, B->offsets};
+  return launch_ffn_wgrad_multi(c.s, ops, np + 1, c.st->dW_gu, c.st->dW_down, first_acc, q);
 }
 
 // Host-side checks of one step description (flags, route mode, buffers,
@@ -982,13 +1013,15 @@ static int check_step(const moe_step* st, int flags, const char* fn) {
   if (int rc = validate_shape(s)) return rc;
   if (flags & ~(MOE_STEP_SERIALIZE | MOE_STEP_EAGER_WGRAD | MOE_STEP_SKIP_WGRAD |
                 MOE_STEP_FUSED_PERMUTE | MOE_STEP_MID_WGRAD | MOE_STEP_FUSED_COMBINE_BWD |
-                MOE_STEP_PAIR_WGRAD | MOE_STEP_FUSED_SCATTER))
+                MOE_STEP_PAIR_WGRAD | MOE_STEP_FUSED_SCATTER | MOE_STEP_GROUP4_WGRAD))
     return set_error(MOE_ERR_ARG, "%s: unknown flags 0x%x", fn, flags);
-  if ((flags & MOE_STEP_PAIR_WGRAD) &&
+  if ((flags & MOE_STEP_PAIR_WGRAD) && (flags & MOE_STEP_GROUP4_WGRAD))
+    return set_error(MOE_ERR_ARG, "%s: PAIR_WGRAD and GROUP4_WGRAD exclude each other", fn);
+  if ((flags & (MOE_STEP_PAIR_WGRAD | MOE_STEP_GROUP4_WGRAD)) &&
       (flags & (MOE_STEP_FUSED_PERMUTE | MOE_STEP_FUSED_COMBINE_BWD)))
     return set_error(MOE_ERR_UNSUPPORTED,
-                     "%s: PAIR_WGRAD reads materialised xp and dy_p: not with FUSED_PERMUTE or "
-                     "FUSED_COMBINE_BWD", fn);
+                     "%s: grouped weight gradients read materialised xp and dy_p: not with "
+                     "FUSED_PERMUTE or FUSED_COMBINE_BWD", fn);
   if ((flags & MOE_STEP_EAGER_WGRAD ? 1 : 0) + (flags & MOE_STEP_SKIP_WGRAD ? 1 : 0) +
           (flags & MOE_STEP_MID_WGRAD ? 1 : 0) > 1)
     return set_error(MOE_ERR_ARG, "%s: EAGER_WGRAD, SKIP_WGRAD and MID_WGRAD exclude each other",
@@ -1155,9 +1188,9 @@ extern "C" int moe_overlap_step(const moe_step* st, hipStream_t s0, hipStream_t 
   using namespace moe;
   g_err[0] = 0;
   if (int rc = check_step(st, flags, "moe_overlap_step")) return rc;
-  if (flags & MOE_STEP_PAIR_WGRAD)
-    return set_error(MOE_ERR_ARG, "moe_overlap_step: PAIR_WGRAD pairs consecutive steps: use "
-                                  "moe_overlap_steps");
+  if (flags & (MOE_STEP_PAIR_WGRAD | MOE_STEP_GROUP4_WGRAD))
+    return set_error(MOE_ERR_ARG, "moe_overlap_step: grouped weight gradients span consecutive "
+                                  "steps: use moe_overlap_steps");
   return step_impl(st, s0, s1, flags, nullptr);
 }
 
@@ -1169,7 +1202,8 @@ namespace moe {
 struct MultiEvents {
   hipEvent_t start, end, dwr, dw, dws;
   hipEvent_t bend[2];  // end of the backward chain of the steps of each parity
-  hipEvent_t pair;     // PAIR_WGRAD: the deferred micro-batch's dh is written
+  // grouped weight gradients: the deferred micro-batches' dh are written
+  hipEvent_t grp[kWgGroupMax - 1];
 };
 
 // One set per (host thread, device), as step_events; every wait of a call is
@@ -1181,8 +1215,9 @@ static int multi_events(MultiEvents** out) {
   if ((int)sets.size() <= dev) sets.resize(dev + 1, nullptr);
   if (!sets[dev]) {
     MultiEvents* e = new MultiEvents();
-    hipEvent_t* all[] = {&e->start, &e->end,     &e->dwr,     &e->dw,
-                         &e->dws,   &e->bend[0], &e->bend[1], &e->pair};
+    hipEvent_t* all[] = {&e->start,  &e->end,    &e->dwr,    &e->dw,    &e->dws,
+                         &e->bend[0], &e->bend[1], &e->grp[0], &e->grp[1], &e->grp[2]};
+    static_assert(kWgGroupMax - 1 == 3, "one event per deferred micro-batch of a group");
     for (hipEvent_t* p : all)
       if (hipEventCreateWithFlags(p, hipEventDisableTiming) != hipSuccess)
         return set_error(MOE_ERR_HIP, "hipEventCreateWithFlags failed");
@@ -1197,8 +1232,9 @@ static bool same_mb(const moe_mb* a, const moe_mb* b) {
   return a == b || memcmp(a, b, sizeof(moe_mb)) == 0;
 }
 
-// PAIR_WGRAD: whether the forward of micro-batch A writes into any buffer the
-// paired weight gradient reads from micro-batch B (xp, a, dh, dy_p, offsets).
+// Grouped weight gradients: whether the forward of micro-batch A writes into
+// any buffer the grouped weight gradient reads from micro-batch B (xp, a, dh,
+// dy_p, offsets).
 static bool fwd_overwrites_wgrad_inputs(const moe_mb* A, const moe_mb* B) {
   if (!A || !B) return false;
   const void* reads[] = {B->xp, B->a, B->dh, B->dyp, B->offsets};
@@ -1234,14 +1270,22 @@ struct AccumOrder {
 // recorded in this call are waited on.
 // skip: leave the weight gradients (routed and shared) to the caller.
 // With PAIR_WGRAD, rw says what the routed experts' weight gradient does:
-// kRwOwn (B's alone), kRwDefer (none: record ev->pair once dh is written, the
-// next step pairs it) or kRwPair (B's together with prev's, the micro-batch
-// deferred by the step before, whose step's accumulate flag is prev_acc,
-// after waiting for ev->pair).
-enum { kRwOwn, kRwDefer, kRwPair };
+// With grouped weight gradients, rw says what the routed experts' weight
+// gradient does: kRwOwn (B's alone), kRwDefer (none: record ev->grp[g.slot]
+// once dh is written; the group's last step takes it) or kRwGroup (B's
+// together with the g.np micro-batches deferred by the steps before, after
+// waiting for their events; g.first_acc is the group's first step's
+// accumulate flag).
+enum { kRwOwn, kRwDefer, kRwGroup };
+struct GroupRole {
+  int slot = 0;                                // kRwDefer: its event
+  int np = 0;                                  // kRwGroup: deferred micro-batches
+  const moe_mb* prev[kWgGroupMax - 1] = {};    // in step order
+  bool first_acc = false;
+};
 static int bwd_chain(const StepCtx& c, const moe_mb* B, hipStream_t q, bool mid, bool eager,
                      bool skip, AccumOrder& ord, int rw = kRwOwn,
-                     const moe_mb* prev = nullptr, bool prev_acc = false) {
+                     const GroupRole& g = GroupRole{}) {
   const bool shared = has_shared(c);
   const bool dwr = c.router && c.st->dW_r;
   const MultiEvents* ev = ord.ev;
@@ -1252,9 +1296,9 @@ static int bwd_chain(const StepCtx& c, const moe_mb* B, hipStream_t q, bool mid,
   auto routed_w = [&]() -> int {
     if (rw == kRwDefer) return MOE_OK;
     TRY(wait(ev->dw, ord.dw));
-    if (rw == kRwPair) {
-      HIPTRY(hipStreamWaitEvent(q, ev->pair, 0));
-      TRY(bwd_wgrad_pair(c, prev, prev_acc, B, q));
+    if (rw == kRwGroup) {
+      for (int i = 0; i < g.np; ++i) HIPTRY(hipStreamWaitEvent(q, ev->grp[i], 0));
+      TRY(bwd_wgrad_group(c, g.prev, g.np, g.first_acc, B, q));
     } else {
       TRY(bwd_wgrad(c, B, q));
     }
@@ -1264,7 +1308,7 @@ static int bwd_chain(const StepCtx& c, const moe_mb* B, hipStream_t q, bool mid,
   };
   // B's dh is written: the paired weight gradient of the next step may read it
   auto dh_done = [&]() -> int {
-    if (rw == kRwDefer) HIPTRY(hipEventRecord(ev->pair, q));
+    if (rw == kRwDefer) HIPTRY(hipEventRecord(ev->grp[g.slot], q));
     return MOE_OK;
   };
   auto shared_w = [&]() -> int {
@@ -1335,15 +1379,16 @@ extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, h
       return set_error(MOE_ERR_ARG,
                        "moe_overlap_steps: step %d has other expert weights than step 0", j);
   }
-  if (flags & MOE_STEP_PAIR_WGRAD) {
+  if (flags & (MOE_STEP_PAIR_WGRAD | MOE_STEP_GROUP4_WGRAD)) {
     // A graph-captured run of paired steps ended in a host crash whose cause
-    // is not known: paired steps are issued eagerly only.
+    // is not known: grouped steps are issued eagerly only.
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(s0, &cs) != hipSuccess)
       return set_error(MOE_ERR_HIP, "moe_overlap_steps: hipStreamIsCapturing failed");
     if (cs != hipStreamCaptureStatusNone)
       return set_error(MOE_ERR_UNSUPPORTED,
-                       "moe_overlap_steps: PAIR_WGRAD is not supported under stream capture");
+                       "moe_overlap_steps: grouped weight gradients are not supported under "
+                       "stream capture");
   }
   // The expert weights are the same for every step of the call, so the
   // dgrad's transposed copies of them are made once, at the start, into the
@@ -1361,35 +1406,55 @@ extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, h
   // SKIP_WGRAD leaves the weight gradients of the last step's backward
   // micro-batch to the caller; the earlier steps' run as usual
   const bool skip_last = (flags & MOE_STEP_SKIP_WGRAD) != 0;
-  // PAIR_WGRAD: steps j and j + 1 (both with a backward micro-batch, step
-  // j + 1 accumulating, the last step left out with SKIP_WGRAD) pair their
-  // routed weight gradients, from the first step on; an unpaired step keeps
-  // its own
-  const bool pair = (flags & MOE_STEP_PAIR_WGRAD) != 0;
+  // Grouped weight gradients (PAIR_WGRAD: groups of 2 steps, GROUP4_WGRAD:
+  // of 4): steps j .. j + G - 1 (all with a backward micro-batch, the later
+  // ones accumulating, the last step of the call left out with SKIP_WGRAD)
+  // form a group whose routed weight gradients run as one launch in step
+  // j + G - 1; groups are formed from the first step on, and a step in no
+  // group keeps its own
+  const int G = (flags & MOE_STEP_GROUP4_WGRAD) ? 4 : (flags & MOE_STEP_PAIR_WGRAD) ? 2 : 1;
+  const bool grouped = G > 1;
   std::vector<int> rw(n, kRwOwn);
-  if (pair) {
-    const int last = skip_last ? n - 1 : n;  // steps that may pair
-    for (int j = 0; j + 1 < last; ++j) {
-      if (!steps[j].bwd || !steps[j + 1].bwd) continue;
-      // step j + 1 must add to what step j leaves (an overwriting step j + 1
-      // discards step j's weight gradients, so there is no sum to pair)
-      if (!(steps[j + 1].accumulate & MOE_ACCUM_DW)) continue;
-      if (fwd_overwrites_wgrad_inputs(steps[j + 1].fwd, steps[j].bwd))
-        return set_error(MOE_ERR_ARG,
-                         "moe_overlap_steps: PAIR_WGRAD: step %d forwards into a buffer that "
-                         "the weight gradient of step %d's backward micro-batch reads in step "
-                         "%d", j + 1, j, j + 1);
-      rw[j] = kRwDefer;
-      rw[j + 1] = kRwPair;
-      ++j;
+  std::vector<GroupRole> role(n);
+  if (grouped) {
+    const int last = skip_last ? n - 1 : n;  // steps that may be grouped
+    for (int j = 0; j + G - 1 < last;) {
+      bool ok = true;
+      for (int k = 0; k < G; ++k) ok = ok && steps[j + k].bwd != nullptr;
+      // the later steps must add to what the earlier ones leave (an
+      // overwriting step discards the weight gradients before it)
+      for (int k = 1; k < G; ++k) ok = ok && (steps[j + k].accumulate & MOE_ACCUM_DW) != 0;
+      if (!ok) {
+        ++j;
+        continue;
+      }
+      // a deferred micro-batch's wgrad inputs must stay intact until the
+      // group's last step
+      for (int dd = j; dd < j + G - 1; ++dd)
+        for (int f = dd + 1; f < j + G; ++f)
+          if (fwd_overwrites_wgrad_inputs(steps[f].fwd, steps[dd].bwd))
+            return set_error(MOE_ERR_ARG,
+                             "moe_overlap_steps: grouped weight gradients: step %d forwards "
+                             "into a buffer that the weight gradient of step %d's backward "
+                             "micro-batch reads in step %d", f, dd, j + G - 1);
+      GroupRole& gl = role[j + G - 1];
+      rw[j + G - 1] = kRwGroup;
+      gl.np = G - 1;
+      gl.first_acc = (steps[j].accumulate & MOE_ACCUM_DW) != 0;
+      for (int k = 0; k < G - 1; ++k) {
+        rw[j + k] = kRwDefer;
+        role[j + k].slot = k;
+        gl.prev[k] = steps[j + k].bwd;
+      }
+      j += G;
     }
   }
-  if (serial && !pair) {
+  if (serial && !grouped) {
     for (int j = 0; j < n; ++j)
       TRY(step_impl(&steps[j], s0, s0, j == n - 1 ? flags : flags & ~MOE_STEP_SKIP_WGRAD, wsW));
     return MOE_OK;
   }
-  // (serialized with PAIR_WGRAD: the same chains, all on s0, forward then
+  // (serialized with grouped weight gradients: the same chains, all on s0, forward then
   // backward, which is the serialized order)
   MultiEvents* ev = nullptr;
   TRY(multi_events(&ev));
@@ -1433,8 +1498,7 @@ extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, h
     }
     if (st->bwd) {
       TRY(bwd_chain(c, st->bwd, Q, mid, eager, skip_last && j == n - 1, ord, rw[j],
-                    rw[j] == kRwPair ? steps[j - 1].bwd : nullptr,
-                    rw[j] == kRwPair && (steps[j - 1].accumulate & MOE_ACCUM_DW) != 0));
+                    role[j]));
       HIPTRY(hipEventRecord(ev->bend[j & 1], Q));
       bend_rec[j & 1] = true;
     }

@@ -870,10 +870,12 @@ struct DgradInOp {
 // operand's row k is token rows_of[r0 + k] / K of the token matrix; each
 // chunk's token is loaded one stage ahead (when the chunk is loaded for the
 // stage before), and a row past the expert's end gets an offset past the
-// resource, which reads as zero.  A direct operand may have a second
-// segment (second()): stages from row kB on read rows k - kB of another
-// operand's expert rows (the paired weight gradient: one reduction over two
-// micro-batches' rows, each segment padded with zero rows to whole stages).
+// resource, which reads as zero.  A direct operand may have up to kWgMore
+// more segments (segment()): stages from row kB[s] on read rows k - kB[s] of
+// another operand's expert rows (the grouped weight gradient: one reduction
+// over several micro-batches' rows, each segment padded with zero rows to
+// whole stages).
+constexpr int kWgMore = 3;  // micro-batches beyond the first in one wgrad launch
 template <bool CAN_GATHER, int NT = 512>
 struct WgLoad {
   static constexpr int CH = 64 * 32 / NT;  // 16-byte chunks per thread and stage
@@ -885,8 +887,8 @@ struct WgLoad {
   int rows;                     // rows of the expert
   uint32_t voff;                // direct: byte offset of chunk 0 within a stage
   int dst0;                     // byte offset of chunk 0 in an LDS tile
-  const uint16_t* base2;        // second segment (direct operands): its expert's first row
-  int rows2, kB;                // its rows, and the first stage row that reads it
+  const uint16_t* base2[kWgMore];  // more segments (direct operands): expert's first row
+  int rows2[kWgMore], kB[kWgMore];  // their rows, and the first stage row that reads them
   // CAN_GATHER: with gat set (block-uniform) the operand is gathered.  The
   // gathered and the direct offset are both formed and one is selected, so
   // the chunk loads have no branch (a branch around them costs a full wait
@@ -911,7 +913,8 @@ struct WgLoad {
     dst0 = wg_byte(trow, 8 * (tid & 31));
     base = src + (size_t)r0_ * ld_;
     voff = (uint32_t)trow * (uint32_t)(ld_ * 2) + coff;
-    kB = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < kWgMore; ++q) kB[q] = 0x7fffffff;
     gat = CAN_GATHER && gathered;
     if constexpr (CAN_GATHER) {
       // every token is a row of the matrix; only the past-the-end marker
@@ -924,10 +927,10 @@ struct WgLoad {
       for (int c = 0; c < CH; ++c) tok_next[c] = token(0, c);
     }
   }
-  __device__ __forceinline__ void second(const uint16_t* src, int r0_, int r1, int kB_) {
-    base2 = src + (size_t)r0_ * ld;
-    rows2 = r1 - r0_;
-    kB = kB_;
+  __device__ __forceinline__ void segment(int q, const uint16_t* src, int r0_, int r1, int kB_) {
+    base2[q] = src + (size_t)r0_ * ld;
+    rows2[q] = r1 - r0_;
+    kB[q] = kB_;
   }
   // rows_of value of chunk c's row in stage k0, read without a branch at an
   // index clamped into the expert's rows (for an expert with none, index
@@ -938,11 +941,17 @@ struct WgLoad {
     return (int)__builtin_amdgcn_raw_buffer_load_b32(rtok, (r0 + k) * 4, 0, 0);
   }
   __device__ __forceinline__ void load_c(int c, int k0) {
-    if (c == 0) {  // the direct resource of stage k0
-      const bool sec = k0 >= kB;  // block-uniform
-      const uint16_t* b = sec ? base2 : base;
-      const int k = sec ? k0 - kB : k0;
-      const long left = (long)((sec ? rows2 : rows) - k) * ld * 2;
+    if (c == 0) {  // the direct resource of stage k0 (segments in ascending kB)
+      const uint16_t* b = base;
+      int k = k0, rw = rows;
+#pragma unroll
+      for (int q = 0; q < kWgMore; ++q) {
+        const bool in = k0 >= kB[q];  // block-uniform
+        b = in ? base2[q] : b;
+        k = in ? k0 - kB[q] : k;
+        rw = in ? rows2[q] : rw;
+      }
+      const long left = (long)(rw - k) * ld * 2;
       const int nrec = left <= 0 ? 0 : (left > 0x7fffffffL ? 0x7fffffff : (int)left);
       rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(b + (size_t)k * ld), (short)0, nrec,
                                                0x00020000);
@@ -1003,22 +1012,23 @@ __device__ __forceinline__ long long uniform64(long long v) {
 //
 // ACC: add into the existing values of dW (gradient accumulation) instead of
 // overwriting them.
-// PAIR (the paired weight gradient, with neither gather): the reduction of
-// every tile runs over the expert's rows of a second micro-batch too (sec:
-// its xp, a, dh, dy_p and offsets), after the first one's, in one float32
-// accumulation, so dW is read and written once for both.
-struct WgSecond {
-  const uint16_t *xp, *abuf, *dh, *dyp;
-  const int32_t* offsets;
+// MULTI (the grouped weight gradient, with neither gather): the reduction of
+// every tile runs over the expert's rows of up to kWgMore more micro-batches
+// too (more: their xp, a, dh, dy_p and offsets), after the first one's, in
+// one float32 accumulation, so dW is read and written once for all of them.
+struct WgMore {
+  int n;  // micro-batches given below (0 .. kWgMore)
+  const uint16_t *xp[kWgMore], *abuf[kWgMore], *dh[kWgMore], *dyp[kWgMore];
+  const int32_t* offsets[kWgMore];
 };
-template <bool GATHER, class E, bool ROUTER, bool ACC, bool GD = false, bool PAIR = false>
+template <bool GATHER, class E, bool ROUTER, bool ACC, bool GD = false, bool MULTI = false>
 __global__ __launch_bounds__(512) void wgrad_kernel(
     const uint16_t* __restrict__ xp, const int32_t* __restrict__ xrows, int K,
     const uint16_t* __restrict__ abuf, const uint16_t* __restrict__ dh,
     const uint16_t* __restrict__ dyp, const int32_t* __restrict__ offsets,
     float* __restrict__ dW_gu, float* __restrict__ dW_down, int E_l, int d, int F,
-    int rchunk = 0, int rows = 0, WgSecond sec = WgSecond{}) {
-  static_assert(!PAIR || !(GATHER || GD || ROUTER), "the paired wgrad reads direct operands");
+    int rchunk = 0, int rows = 0, WgMore more = WgMore{}) {
+  static_assert(!MULTI || !(GATHER || GD || ROUTER), "the grouped wgrad reads direct operands");
   using TL = T256;
   constexpr int WTM = TL::WTM, WTN = TL::WTN, TM = TL::TM, TN = TL::TN;
   __shared__ __attribute__((aligned(16))) uint16_t smem[TL::LDS_ELEMS];
@@ -1026,13 +1036,20 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
   const int tdm = (d + 255) / 256, tdn = (F + 255) / 256;
   const int tgm = (2 * F + 255) / 256, tgn = (d + 255) / 256;
   const int per_e = tdm * tdn + (ROUTER ? 0 : tgm * tgn);
-  // first row of expert (or token chunk) e; with PAIR, of the second
-  // micro-batch's expert e too
+  // first row of expert (or token chunk) e; with MULTI, of micro-batch q's
+  // expert e among the others
   auto off = [&](int e) { return ROUTER ? min(e * rchunk, rows) : offsets[e]; };
-  auto off2 = [&](int e) { return PAIR ? sec.offsets[e] : 0; };
+  const int nmore = MULTI ? more.n : 0;
+  auto off2 = [&](int q, int e) { return more.offsets[q][e]; };
   // stages of expert e: each segment padded to whole stages
   auto stages = [&](int e) {
-    return (off(e + 1) - off(e) + BK - 1) / BK + (off2(e + 1) - off2(e) + BK - 1) / BK;
+    int n = (off(e + 1) - off(e) + BK - 1) / BK;
+    if constexpr (MULTI) {
+#pragma unroll
+      for (int q = 0; q < kWgMore; ++q)
+        if (q < nmore) n += (off2(q, e + 1) - off2(q, e) + BK - 1) / BK;
+    }
+    return n;
   };
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1077,35 +1094,46 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
     int r0, r1, M, N, m0, n0, nk;
     const uint16_t *Asrc, *Bsrc;
     float* out;
-    // PAIR: the second micro-batch's rows and operands, from stage row kB on
-    int r0b, r1b, kB;
-    const uint16_t *Asrc2, *Bsrc2;
+    // MULTI: micro-batch q's rows and operands among the others, from stage
+    // row kB[q] on
+    int r0b[kWgMore], r1b[kWgMore], kB[kWgMore];
+    const uint16_t *Asrc2[kWgMore], *Bsrc2[kWgMore];
   };
-  auto job = [&](long long gt) {
+  // Tile t of expert e (the tile index advances by whole slots, so e and t
+  // are kept apart and no division runs between tiles: a division needs
+  // vector registers, which the accumulators hold there)
+  auto job = [&](int e, int t) {
     TileJob j{};
     j.valid = false;
-    if (gt >= (long long)E_l * per_e) return j;
-    const int e = (int)(gt / per_e);
-    int t = (int)(gt % per_e);
+    if (e >= E_l) return j;
     {
       const long long it0 = uniform64(s_it[e]);
-      const long long nk_e = (uniform64(s_it[e + 1]) - it0) / per_e;
-      if (it0 + t * nk_e >= hi) return j;  // uniform
+      const int nk_e = max(1, stages(e));
+      if (it0 + (long long)t * nk_e >= hi) return j;  // uniform
     }
     j.valid = true;
     j.r0 = off(e);
     j.r1 = off(e + 1);
     j.nk = stages(e);
-    j.r0b = off2(e);
-    j.r1b = off2(e + 1);
-    j.kB = (j.r1 - j.r0 + BK - 1) / BK * BK;
-    if (t < tdm * tdn) {
+    const bool down = t < tdm * tdn;
+    if constexpr (MULTI) {
+      int kb = (j.r1 - j.r0 + BK - 1) / BK * BK;
+#pragma unroll
+      for (int q = 0; q < kWgMore; ++q) {
+        if (q >= nmore) break;  // uniform
+        j.r0b[q] = off2(q, e);
+        j.r1b[q] = off2(q, e + 1);
+        j.kB[q] = kb;
+        kb += (j.r1b[q] - j.r0b[q] + BK - 1) / BK * BK;
+        j.Asrc2[q] = down ? more.dyp[q] : more.dh[q];
+        j.Bsrc2[q] = down ? more.abuf[q] : more.xp[q];
+      }
+    }
+    if (down) {
       j.ga = GD;
       j.gb = false;
       j.Asrc = dyp;
       j.Bsrc = abuf;
-      j.Asrc2 = sec.dyp;
-      j.Bsrc2 = sec.abuf;
       j.M = d;
       j.N = F;
       j.m0 = (t / tdn) * 256;
@@ -1115,8 +1143,6 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
       t -= tdm * tdn;
       j.Asrc = dh;
       j.Bsrc = xp;
-      j.Asrc2 = sec.dh;
-      j.Bsrc2 = sec.xp;
       j.ga = false;
       j.gb = GATHER;
       j.M = 2 * F;
@@ -1138,13 +1164,17 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
   auto init_loaders = [&](const TileJob& c) {
     la.init(c.Asrc, c.M, c.m0, c.r0, c.r1, c.ga, xrows, K, tid, n_rows);
     lb.init(c.Bsrc, c.N, c.n0, c.r0, c.r1, c.gb, xrows, K, tid, n_rows);
-    if constexpr (PAIR) {
-      la.second(c.Asrc2, c.r0b, c.r1b, c.kB);
-      lb.second(c.Bsrc2, c.r0b, c.r1b, c.kB);
+    if constexpr (MULTI) {
+#pragma unroll
+      for (int q = 0; q < kWgMore; ++q) {
+        if (q >= nmore) break;  // uniform
+        la.segment(q, c.Asrc2[q], c.r0b[q], c.r1b[q], c.kB[q]);
+        lb.segment(q, c.Bsrc2[q], c.r0b[q], c.r1b[q], c.kB[q]);
+      }
     }
   };
-  long long gt = gt0 + slot;
-  TileJob cur = job(gt);
+  int ge = (int)((gt0 + slot) / per_e), gtt = (int)((gt0 + slot) % per_e);
+  TileJob cur = job(ge, gtt);
   if (!cur.valid) return;  // block-uniform
   init_loaders(cur);
   la.load(0, 0);
@@ -1158,8 +1188,12 @@ __global__ __launch_bounds__(512) void wgrad_kernel(
     __syncthreads();
     f32x16_t acc[TM][TN];
     mainloop_steps<TL, E, WgLoad<GD>, WgLoad<GATHER>, true, FR>(la, lb, 0, nk, smem, acc, fr);
-    gt += nslots;
-    const TileJob nxt = job(gt);
+    gtt += nslots;
+    while (gtt >= per_e) {  // uniform, a few rounds at most
+      gtt -= per_e;
+      ++ge;
+    }
+    const TileJob nxt = job(ge, gtt);
     // the next tile's first stage is loaded during this tile's epilogue,
     // behind the epilogue's first loads and ahead of its stores
     auto next_stage0 = [&]() {
@@ -1479,24 +1513,33 @@ void wgrad_t(const moe_shape* s, const void* xp, const int32_t* xrows, const voi
   }
 }
 
-// The paired weight gradient of two micro-batches (same shape): one launch
-// whose reduction runs over both micro-batches' rows of each expert.
+// The grouped weight gradient of n micro-batches (same shape): one launch
+// whose reduction runs over every micro-batch's rows of each expert.
 template <class E>
-void wgrad_pair_t(const moe_shape* s, const WgrOps& A, const WgrOps& B, float* dW_gu,
-                  float* dW_down, bool accumulate, hipStream_t st) {
+void wgrad_multi_t(const moe_shape* s, const WgrOps* ops, int n, float* dW_gu, float* dW_down,
+                   bool accumulate, hipStream_t st) {
+  static_assert(kWgGroupMax == 1 + kWgMore, "one first micro-batch plus the others");
   const int d = (int)s->d, F = (int)s->F, E_l = (int)s->E_l;
   const long per_e = (long)((d + 255) / 256) * ((F + 255) / 256) +
                      (long)((2 * F + 255) / 256) * ((d + 255) / 256);
   const int grid = persistent_grid(E_l * per_e);
-  const WgSecond sec{(const uint16_t*)B.xp, (const uint16_t*)B.a, (const uint16_t*)B.dh,
-                     (const uint16_t*)B.dyp, B.offsets};
+  WgMore more{};
+  more.n = n - 1;
+  for (int q = 0; q + 1 < n; ++q) {
+    more.xp[q] = (const uint16_t*)ops[q + 1].xp;
+    more.abuf[q] = (const uint16_t*)ops[q + 1].a;
+    more.dh[q] = (const uint16_t*)ops[q + 1].dh;
+    more.dyp[q] = (const uint16_t*)ops[q + 1].dyp;
+    more.offsets[q] = ops[q + 1].offsets;
+  }
+  const WgrOps& A = ops[0];
   auto go = [&](auto acc) {
-    MOE_LAUNCH("wgrad_pair", st,
+    MOE_LAUNCH("wgrad_multi", st,
                (wgrad_kernel<false, E, false, decltype(acc)::value, false, true>
                 <<<grid, 512, 0, st>>>((const uint16_t*)A.xp, nullptr, (int)s->K,
                                        (const uint16_t*)A.a, (const uint16_t*)A.dh,
                                        (const uint16_t*)A.dyp, A.offsets, dW_gu, dW_down, E_l, d,
-                                       F, 0, 0, sec)));
+                                       F, 0, 0, more)));
   };
   if (accumulate) go(std::true_type{});
   else go(std::false_type{});
@@ -1567,11 +1610,11 @@ int launch_ffn_wgrad_mfma(const moe_shape* s, const void* xp, const int32_t* xro
   return check_launch("wgrad GEMM");
 }
 
-int launch_ffn_wgrad_pair_mfma(const moe_shape* s, const WgrOps& A, const WgrOps& B,
-                               float* dW_gu, float* dW_down, bool accumulate, hipStream_t st) {
-  if (s->dtype == MOE_F16) wgrad_pair_t<F16>(s, A, B, dW_gu, dW_down, accumulate, st);
-  else wgrad_pair_t<BF16>(s, A, B, dW_gu, dW_down, accumulate, st);
-  return check_launch("paired wgrad GEMM");
+int launch_ffn_wgrad_multi_mfma(const moe_shape* s, const WgrOps* ops, int n, float* dW_gu,
+                                float* dW_down, bool accumulate, hipStream_t st) {
+  if (s->dtype == MOE_F16) wgrad_multi_t<F16>(s, ops, n, dW_gu, dW_down, accumulate, st);
+  else wgrad_multi_t<BF16>(s, ops, n, dW_gu, dW_down, accumulate, st);
+  return check_launch("grouped wgrad GEMM");
 }
 
 int launch_router_wgrad_mfma(const moe_shape* s, const void* x, const void* dl_split,

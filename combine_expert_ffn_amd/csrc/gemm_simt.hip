@@ -110,6 +110,12 @@ __global__ __launch_bounds__(256) void f32_dgrad_in_kernel(const float* __restri
   dxp[(size_t)row * d + c] = acc;
 }
 
+// The micro-batches after the first of a grouped weight gradient.
+struct WgrMoreF32 {
+  int n;
+  WgrOps ops[kWgGroupMax - 1];
+};
+
 // dW_down[e][i][f] = sum_r dyp[r][i] a[r][f]; dW_gu[e][m][c] = sum_r dh[r][m] xp[r][c]
 // (dyrows set: dyp is dout and row r of it is token dyrows[r] / K)
 __global__ __launch_bounds__(256) void f32_wgrad_kernel(
@@ -118,9 +124,9 @@ __global__ __launch_bounds__(256) void f32_wgrad_kernel(
     const float* __restrict__ dyp, const int32_t* __restrict__ dyrows,
     const int32_t* __restrict__ offsets,
     float* __restrict__ dW_gu, float* __restrict__ dW_down, int E_l, int d, int F,
-    int accumulate, WgrOps second) {
-  // second.offsets set: the paired weight gradient, the sum continuing over
-  // the second micro-batch's rows of the expert (materialised operands)
+    int accumulate, WgrMoreF32 more) {
+  // more.n > 0: the grouped weight gradient, the sum continuing over the
+  // other micro-batches' rows of the expert, in order (materialised operands)
   const long per_e = (long)d * F + 2L * F * d;
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= per_e * E_l) return;
@@ -133,9 +139,9 @@ __global__ __launch_bounds__(256) void f32_wgrad_kernel(
     const int ii = (int)(q / F), f = (int)(q % F);
     for (int r = r0; r < r1; ++r)
       acc = fmaf(dyp[(size_t)(dyrows ? dyrows[r] / K : r) * d + ii], a[(size_t)r * F + f], acc);
-    if (second.offsets) {
-      const float *dy2 = (const float*)second.dyp, *a2 = (const float*)second.a;
-      for (int r = second.offsets[e]; r < second.offsets[e + 1]; ++r)
+    for (int g = 0; g < more.n; ++g) {
+      const float *dy2 = (const float*)more.ops[g].dyp, *a2 = (const float*)more.ops[g].a;
+      for (int r = more.ops[g].offsets[e]; r < more.ops[g].offsets[e + 1]; ++r)
         acc = fmaf(dy2[(size_t)r * d + ii], a2[(size_t)r * F + f], acc);
     }
     o = dW_down + (size_t)e * d * F + q;
@@ -144,9 +150,9 @@ __global__ __launch_bounds__(256) void f32_wgrad_kernel(
     const int m = (int)(q / d), c = (int)(q % d);
     for (int r = r0; r < r1; ++r)
       acc = fmaf(dh[(size_t)r * 2 * F + m], xp[(size_t)(xrows ? xrows[r] / K : r) * d + c], acc);
-    if (second.offsets) {
-      const float *dh2 = (const float*)second.dh, *xp2 = (const float*)second.xp;
-      for (int r = second.offsets[e]; r < second.offsets[e + 1]; ++r)
+    for (int g = 0; g < more.n; ++g) {
+      const float *dh2 = (const float*)more.ops[g].dh, *xp2 = (const float*)more.ops[g].xp;
+      for (int r = more.ops[g].offsets[e]; r < more.ops[g].offsets[e + 1]; ++r)
         acc = fmaf(dh2[(size_t)r * 2 * F + m], xp2[(size_t)r * d + c], acc);
     }
     o = dW_gu + (size_t)e * 2 * F * d + q;
@@ -231,20 +237,24 @@ int launch_ffn_wgrad(const moe_shape* s, const void* xp, const int32_t* xrows, c
              f32_wgrad_kernel<<<(unsigned)cdiv(n, 256), 256, 0, st>>>(
       (const float*)xp, xrows, (int)s->K, (const float*)a, (const float*)dh, (const float*)dyp,
       dyrows, offsets, dW_gu, dW_down, (int)s->E_l, (int)s->d, (int)s->F, accumulate ? 1 : 0,
-      WgrOps{}));
+      WgrMoreF32{}));
   return check_launch("f32 wgrad");
 }
 
-int launch_ffn_wgrad_pair(const moe_shape* s, const WgrOps& A, const WgrOps& B, float* dW_gu,
-                          float* dW_down, bool accumulate, hipStream_t st) {
-  if (is16(s)) return launch_ffn_wgrad_pair_mfma(s, A, B, dW_gu, dW_down, accumulate, st);
-  const long n = s->E_l * (s->d * s->F + 2 * s->F * s->d);
+int launch_ffn_wgrad_multi(const moe_shape* s, const WgrOps* ops, int n, float* dW_gu,
+                           float* dW_down, bool accumulate, hipStream_t st) {
+  if (is16(s)) return launch_ffn_wgrad_multi_mfma(s, ops, n, dW_gu, dW_down, accumulate, st);
+  WgrMoreF32 more{};
+  more.n = n - 1;
+  for (int g = 0; g + 1 < n; ++g) more.ops[g] = ops[g + 1];
+  const WgrOps& A = ops[0];
+  const long cnt = s->E_l * (s->d * s->F + 2 * s->F * s->d);
   MOE_LAUNCH("f32_wgrad", st,
-             f32_wgrad_kernel<<<(unsigned)cdiv(n, 256), 256, 0, st>>>(
+             f32_wgrad_kernel<<<(unsigned)cdiv(cnt, 256), 256, 0, st>>>(
       (const float*)A.xp, nullptr, (int)s->K, (const float*)A.a, (const float*)A.dh,
       (const float*)A.dyp, nullptr, A.offsets, dW_gu, dW_down, (int)s->E_l, (int)s->d,
-      (int)s->F, accumulate ? 1 : 0, B));
-  return check_launch("f32 paired wgrad");
+      (int)s->F, accumulate ? 1 : 0, more));
+  return check_launch("f32 grouped wgrad");
 }
 
 }  // namespace moe

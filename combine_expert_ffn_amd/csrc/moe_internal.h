@@ -294,12 +294,14 @@ struct WgrOps {
   const void *xp, *a, *dh, *dyp;
   const int32_t* offsets;
 };
-// The paired weight gradient: dW (+)= the weight gradients of micro-batches A
-// and B, reduced over both one's rows of each expert in one accumulation, so
-// dW is read and written once.
-int launch_ffn_wgrad_pair(const moe_shape* s, const WgrOps& A, const WgrOps& B, float* dW_gu,
-                          float* dW_down, bool accumulate, hipStream_t st);
-int launch_ffn_wgrad_pair_mfma(const moe_shape* s, const WgrOps& A, const WgrOps& B,
-                               float* dW_gu, float* dW_down, bool accumulate, hipStream_t st);
+// The grouped weight gradient: dW (+)= the weight gradients of micro-batches
+// ops[0 .. n), reduced over all their rows of each expert in one
+// accumulation (in that order), so dW is read and written once; 2 <= n <=
+// kWgGroupMax.
+constexpr int kWgGroupMax = 4;
+int launch_ffn_wgrad_multi(const moe_shape* s, const WgrOps* ops, int n, float* dW_gu,
+                           float* dW_down, bool accumulate, hipStream_t st);
+int launch_ffn_wgrad_multi_mfma(const moe_shape* s, const WgrOps* ops, int n, float* dW_gu,
+                                float* dW_down, bool accumulate, hipStream_t st);
 
 }  // namespace moe

@@ -127,6 +127,13 @@ extern "C" {
                                  and the combine and the combine backward read
                                  a token's slots as one run (moe_combine_pairs,
                                  moe_combine_bwd_pairs).  Bit-identical results */
+#define MOE_STEP_GROUP4_WGRAD 256 /* moe_overlap_steps: as MOE_STEP_PAIR_WGRAD with
+                                 groups of four steps: the routed experts' weight
+                                 gradients of steps j .. j + 3 in one launch
+                                 (moe_ffn_wgrad_multi) in step j + 3, where steps
+                                 j + 1 .. j + 3 accumulate; the deferred
+                                 micro-batches must stay intact until then.
+                                 Excludes MOE_STEP_PAIR_WGRAD */
 
 /*
  * Layer shape.  T tokens of hidden size d; E experts routed over, of which the
@@ -365,6 +372,28 @@ int moe_ffn_wgrad_pair(const moe_shape* s, const void* xp, const void* a, const 
                        const void* a2, const void* dh2, const void* dyp2,
                        const int32_t* offsets2, float* dW_gu, float* dW_down, int accumulate,
                        hipStream_t stream);
+
+/* One micro-batch's weight-gradient operands (device pointers, layouts as
+ * moe_ffn_wgrad). */
+typedef struct moe_wgrad_ops {
+  const void* xp;
+  const void* a;
+  const void* dh;
+  const void* dyp;
+  const int32_t* offsets;
+} moe_wgrad_ops;
+
+/*
+ * moe_ffn_wgrad_multi - moe_ffn_wgrad_pair for n micro-batches, 1 <= n <= 4:
+ * ops [n] (host array) in order; for each expert the reduction runs over
+ * ops[0]'s rows, then ops[1]'s, and so on, in one float32 accumulation, so
+ * dW is read and written once for all n (the deferred W of page 1,
+ * delay_wgrad_compute, gathered over a group of steps).  n = 1 is
+ * moe_ffn_wgrad.  Errors: MOE_ERR_NULL (an operand), MOE_ERR_SHAPE,
+ * MOE_ERR_ARG (n out of range, unknown accumulate bits).
+ */
+int moe_ffn_wgrad_multi(const moe_shape* s, int n, const moe_wgrad_ops* ops, float* dW_gu,
+                        float* dW_down, int accumulate, hipStream_t stream);
 
 /*
  * moe_ffn_wgrad_gather - moe_ffn_wgrad with the fused permute: dW_gu reads

@@ -196,7 +196,17 @@ def test_modes_and_flags_rejected():
     st = _lib.MoeStep()
     st.shape = s
     st.route_mode = M.MOE_ROUTE_FORCE_BALANCE
-    assert L.moe_overlap_step(C.byref(st), None, None, 256) == M.MOE_ERR_ARG
+    assert L.moe_overlap_step(C.byref(st), None, None, 512) == M.MOE_ERR_ARG
+    assert L.moe_overlap_step(C.byref(st), None, None,
+                              M.MOE_STEP_PAIR_WGRAD | M.MOE_STEP_GROUP4_WGRAD) == M.MOE_ERR_ARG
+    # the grouped weight gradient: n out of [1, 4], a missing operand
+    ops = (_lib.MoeWgradOps * 5)(*[_lib.MoeWgradOps(FAKE, FAKE, FAKE, FAKE, FAKE)] * 5)
+    assert L.moe_ffn_wgrad_multi(C.byref(s), 0, ops, FAKE, FAKE, 0, None) == M.MOE_ERR_ARG
+    assert L.moe_ffn_wgrad_multi(C.byref(s), 5, ops, FAKE, FAKE, 0, None) == M.MOE_ERR_ARG
+    assert L.moe_ffn_wgrad_multi(C.byref(s), 3, ops, FAKE, FAKE, 8, None) == M.MOE_ERR_ARG
+    ops[2].dh = None
+    assert L.moe_ffn_wgrad_multi(C.byref(s), 3, ops, FAKE, FAKE, 0, None) == M.MOE_ERR_NULL
+    assert L.moe_ffn_wgrad_multi(C.byref(s), 2, None, FAKE, FAKE, 0, None) == M.MOE_ERR_NULL
     # fused scatter: xp and x both missing, a missing map, missing y
     assert L.moe_expert_ffn_fwd_scatter(C.byref(s), None, None, *([FAKE] * 9),
                                         None) == M.MOE_ERR_NULL

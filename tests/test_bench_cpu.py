@@ -1,7 +1,7 @@
 """bench.py's timing plan (host logic, no GPU): any --steps K is timed exactly,
 as replays of a graph whose length is a multiple of the unit (2 steps; 6 with
 the paired weight gradient over three buffer sets) plus fewer than a unit of
-eager steps; the paired weight gradient's algorithmic work per launch."""
+eager steps; the grouped weight gradient's algorithmic work per launch."""
 
 import os
 import sys
@@ -37,16 +37,18 @@ def test_group_plan_paired_unit():
                 assert (g, rem) == (G0, 0), (G0, K, g, rem)
 
 
-def test_paired_wgrad_work_per_launch():
-    """The paired launch reduces two micro-batches' rows (twice the flops and
-    operand bytes of one wgrad) and reads and writes the float32 dW once."""
+def test_grouped_wgrad_work_per_launch():
+    """The grouped launch reduces the rows of `group` micro-batches (that many
+    times the flops and operand bytes of one wgrad) and reads and writes the
+    float32 dW once."""
     from combine_expert_ffn_amd.inputs import WORKLOADS
     w = WORKLOADS["ep1_128exp_bf16"]
     N, T_loc = w.T * w.K, w.T
-    for acc in (True, False):
-        a = bench.algorithmic(w, N, T_loc, accumulate=acc)
-        dW = 4.0 * w.E_l * 3 * w.F * w.d * (2 if acc else 1)
-        one, two = a["wgrad"], a["wgrad_pair"]
-        assert two["flop"] == 2 * one["flop"]
-        assert abs(two["byte"] - (2 * (one["byte"] - dW) + dW)) < 1.0
-    assert "wgrad_pair" in bench.PER_LAUNCH and "wgrad_pair" in bench.GEMM_KERNELS
+    for group in (2, 3, 4):
+        for acc in (True, False):
+            a = bench.algorithmic(w, N, T_loc, accumulate=acc, group=group)
+            dW = 4.0 * w.E_l * 3 * w.F * w.d * (2 if acc else 1)
+            one, many = a["wgrad"], a["wgrad_multi"]
+            assert many["flop"] == group * one["flop"]
+            assert abs(many["byte"] - (group * (one["byte"] - dW) + dW)) < 1.0
+    assert "wgrad_multi" in bench.PER_LAUNCH and "wgrad_multi" in bench.GEMM_KERNELS

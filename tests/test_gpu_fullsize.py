@@ -320,31 +320,37 @@ def test_step_graph_replay_matches_eager(pipelined):
         log(f"[graph] replay {r}: bit-identical to the eager steps")
 
 
-def test_fullsize_paired_steps():
+@pytest.mark.parametrize("group", [2, 4])
+def test_fullsize_grouped_steps(group):
     """The 128-expert layer in the schedule bench.py times: one pipelined
-    moe_overlap_steps call with the wgrad between the dgrad GEMMs and paired
-    weight gradients (the first two back-propagated micro-batches' in one
-    launch, the third's alone), three micro-batch buffer sets.  Each
+    moe_overlap_steps call with the wgrad between the dgrad GEMMs and grouped
+    weight gradients (the first `group` back-propagated micro-batches' in one
+    launch, the last one's alone), group + 1 micro-batch buffer sets.  Each
     micro-batch's forward and backward outputs on samples, and every entry of
-    three experts' accumulated weight gradients (the sum over the three
+    three experts' accumulated weight gradients (the sum over all the
     micro-batches, from the GPU's own stage inputs), against the oracle."""
     w = WORKLOADS["ep1_128exp_bf16"]
-    log(f"[full size paired] {w.name}: T={w.T} E={w.E} K={w.K}, three micro-batches")
+    nm = group + 1
+    log(f"[full size grouped] {w.name}: T={w.T} E={w.E} K={w.K}, {nm} micro-batches, "
+        f"groups of {group}")
     inp = make_inputs(w, seed=0, microbatches=2)
     net = Net(w, inp)
     for t in (net.dW_gu, net.dW_down, net.dW_r):
         t.zero_()
-    xs = [inp["x"], inp["x_b"], inp["x"][::-1].copy()]
-    ds = [inp["dout"], inp["dout_b"], inp["dout"][::-1].copy()]
-    m = [net.mb(xs[i], ds[i]) for i in range(3)]
+    srcs = [("", lambda a: a), ("_b", lambda a: a), ("", lambda a: a[::-1].copy()),
+            ("_b", lambda a: a[::-1].copy()), ("", lambda a: np.roll(a, 28, axis=0))][:nm]
+    xs = [f(inp["x" + k]) for k, f in srcs]
+    ds = [f(inp["dout" + k]) for k, f in srcs]
+    m = [net.mb(xs[i], ds[i]) for i in range(nm)]
     acc = M.MOE_ACCUM_DW
-    steps = [net.make(m[0], None, acc), net.make(m[1], m[0], acc), net.make(m[2], m[1], acc),
-             net.make(None, m[2], acc)]
+    steps = [net.make(m[0], None, acc)] + \
+        [net.make(m[i + 1], m[i], acc) for i in range(nm - 1)] + [net.make(None, m[-1], acc)]
+    flag = M.MOE_STEP_PAIR_WGRAD if group == 2 else M.MOE_STEP_GROUP4_WGRAD
     s0, s1 = torch.cuda.current_stream(), torch.cuda.Stream()
-    M.moe_overlap_steps(steps, s0, s1, M.MOE_STEP_MID_WGRAD | M.MOE_STEP_PAIR_WGRAD)
+    M.moe_overlap_steps(steps, s0, s1, M.MOE_STEP_MID_WGRAD | flag)
     torch.cuda.synchronize()
     rng = np.random.default_rng(5)
-    for i in range(3):
+    for i in range(nm):
         log(f"  micro-batch {i}")
         sampled_check(w, dict(inp, x=xs[i], dout=ds[i]), m[i], net, rng, wgrad_prev=True)
     prec, tau = w.dtype, TAU[w.dtype]
@@ -359,8 +365,8 @@ def test_fullsize_paired_steps():
             prev = O.ffn_wgrad(sl(mb.xp), sl(mb.a), sl(mb.dh), sl(mb.dyp), np.array([0, r1 - r0]),
                                dW_gu_prev=None if prev is None else prev[0],
                                dW_down_prev=None if prev is None else prev[1], prec=prec)
-        close(f"dW_gu of three micro-batches (expert {j}, all entries)", host(net.dW_gu[j]),
+        close(f"dW_gu of {nm} micro-batches (expert {j}, all entries)", host(net.dW_gu[j]),
               prev[0][0], tau)
-        close(f"dW_down of three micro-batches (expert {j}, all entries)",
+        close(f"dW_down of {nm} micro-batches (expert {j}, all entries)",
               host(net.dW_down[j]), prev[1][0], tau)
-    log(f"[full size paired] ok: outputs of three micro-batches, dW of experts {experts}")
+    log(f"[full size grouped] ok: outputs of {nm} micro-batches, dW of experts {experts}")

@@ -91,6 +91,49 @@ def test_wgrad_pair_against_oracle(prec, countsA, countsB):
         assert torch.equal(again[0], dW[0]) and torch.equal(again[1], dW[1])
 
 
+@pytest.mark.parametrize("prec", ["bf16", "f32"])
+@pytest.mark.parametrize("counts", [
+    ((700, 0, 1313, 65), (64, 1, 0, 257), (0, 0, 129, 1000)),
+    ((1024,) * 4, (1000, 1100, 900, 1090), (63, 65, 127, 1), (500, 0, 0, 2049)),
+])
+def test_wgrad_multi_against_oracle(prec, counts):
+    """moe_ffn_wgrad_multi over three and four micro-batches against the oracle's
+    sum of their weight gradients, and against single calls within float32
+    rounding; deterministic."""
+    d, F = (256, 128) if prec != "f32" else (64, 64)
+    E_l = len(counts[0])
+    cap = max(sum(c) for c in counts)
+    s = M.make_shape(cap, d, F, E_l, 0, E_l, 1, prec)
+    rng = np.random.default_rng(29)
+    mbs = [_ops(rng, c, d, F, prec, cap) for c in counts]
+    log(f"[wgrad multi] {prec} n={len(counts)} counts={counts}")
+    prior = [torch.full((E_l, 2 * F, d), 0.75, device="cuda"),
+             torch.full((E_l, d, F), -0.5, device="cuda")]
+    ops = [tuple(t) + (dev(off, "i32"),) for off, t in mbs]
+    X = [[host(t, int(off[-1])) for t in T_] for off, T_ in mbs]
+    refs = [O.ffn_wgrad(*x, off, prec="f64") for x, (off, _) in zip(X, mbs)]
+    mags = [O.ffn_wgrad(*[np.abs(t) for t in x], off, prec="f64") for x, (off, _) in zip(X, mbs)]
+    tau = 1e-5
+    for acc in (0, M.MOE_ACCUM_DW):
+        dW = [t.clone() for t in prior]
+        M.moe_ffn_wgrad_multi(s, ops, dW[0], dW[1], acc)
+        base = [host(t) if acc else 0.0 for t in prior]
+        for k, name in ((0, "dW_gu"), (1, "dW_down")):
+            close_reduction(f"{name} multi acc={acc}", host(dW[k]),
+                            base[k] + sum(r[k] for r in refs),
+                            sum(m_[k] for m_ in mags) + np.abs(base[k]), tau)
+        one = [t.clone() for t in prior]
+        for i, o in enumerate(ops):
+            M.moe_ffn_wgrad(s, *o, one[0], one[1], acc if i == 0 else M.MOE_ACCUM_DW)
+        for k in range(2):
+            close_reduction("multi vs single calls", host(dW[k]), host(one[k]),
+                            sum(m_[k] for m_ in mags) + np.abs(base[k] if acc else 0.0), tau)
+        again = [t.clone() for t in prior]
+        M.moe_ffn_wgrad_multi(s, ops, again[0], again[1], acc)
+        torch.cuda.synchronize()
+        assert torch.equal(again[0], dW[0]) and torch.equal(again[1], dW[1])
+
+
 def _steps(s, w, m, W, dW, ws, n, W_r, bias, rot, overwrite=()):
     """n 1F1B steps over buffer sets m: step j forwards m[j % rot] (none in
     the last step) and back-propagates m[(j - 1) % rot] (none in the first);
@@ -102,19 +145,28 @@ def _steps(s, w, m, W, dW, ws, n, W_r, bias, rot, overwrite=()):
             for j in range(n)]
 
 
-@pytest.mark.parametrize("name,n,flags,overwrite", [
-    ("zipf_bf16", 8, M.MOE_STEP_MID_WGRAD, ()),
-    ("zipf_bf16", 7, 0, ()),
-    ("zipf_bf16", 9, M.MOE_STEP_SKIP_WGRAD, ()),
-    ("mid_f32", 6, M.MOE_STEP_MID_WGRAD, ()),
+P2, G4 = M.MOE_STEP_PAIR_WGRAD, M.MOE_STEP_GROUP4_WGRAD
+
+
+@pytest.mark.parametrize("name,n,flags,overwrite,group", [
+    ("zipf_bf16", 8, M.MOE_STEP_MID_WGRAD, (), P2),
+    ("zipf_bf16", 7, 0, (), P2),
+    ("zipf_bf16", 9, M.MOE_STEP_SKIP_WGRAD, (), P2),
+    ("mid_f32", 6, M.MOE_STEP_MID_WGRAD, (), P2),
     # the first backward overwrites: its pair starts from zero
-    ("zipf_bf16", 7, M.MOE_STEP_MID_WGRAD, (1,)),
+    ("zipf_bf16", 7, M.MOE_STEP_MID_WGRAD, (1,), P2),
     # the second overwrites: steps 1 and 2 do not pair (2 discards 1's sums)
-    ("zipf_bf16", 7, 0, (2,)),
+    ("zipf_bf16", 7, 0, (2,), P2),
     # an overwrite in the middle of the run
-    ("mid_f32", 8, M.MOE_STEP_MID_WGRAD, (4,)),
+    ("mid_f32", 8, M.MOE_STEP_MID_WGRAD, (4,), P2),
+    # groups of four: two whole groups and a remainder, with SKIP_WGRAD, with
+    # an overwrite starting a group and one inside a would-be group
+    ("zipf_bf16", 11, M.MOE_STEP_MID_WGRAD, (), G4),
+    ("zipf_bf16", 10, M.MOE_STEP_SKIP_WGRAD, (), G4),
+    ("mid_f32", 10, 0, (1,), G4),
+    ("zipf_bf16", 10, M.MOE_STEP_MID_WGRAD, (3,), G4),
 ])
-def test_pair_steps_pipelined_equals_serialized(name, n, flags, overwrite):
+def test_pair_steps_pipelined_equals_serialized(name, n, flags, overwrite, group):
     w = {
         "zipf_bf16": Workload("zipf_bf16", T=700, d=192, F=320, E=64, e_lo=0, E_l=8, K=6,
                               dtype="bf16", route="topk", zipf_s=1.1),
@@ -122,7 +174,7 @@ def test_pair_steps_pipelined_equals_serialized(name, n, flags, overwrite):
                             dtype="f32", route="topk"),
     }[name]
     prec = w.dtype
-    log(f"[pair steps] {name} n={n} flags={flags} overwrite={overwrite}")
+    log(f"[grouped steps] {name} n={n} flags={flags} overwrite={overwrite} group={group}")
     inp = make_inputs(w, seed=3, microbatches=2)
     s = M.shape_of(w)
     D = lambda a: dev(a, prec)
@@ -130,27 +182,32 @@ def test_pair_steps_pipelined_equals_serialized(name, n, flags, overwrite):
     W_r = D(inp["W_r"])
     bias = dev(inp["bias"], "f32x") if inp["bias"] is not None else None
     s0, s1 = torch.cuda.current_stream(), torch.cuda.Stream()
-    xs = [inp["x"], inp["x_b"], inp["x"][::-1].copy()]
-    ds = [inp["dout"], inp["dout_b"], inp["dout"][::-1].copy()]
+    # a group of G steps keeps G micro-batches until its last step: G + 1
+    # buffer sets rotate
+    rot = 3 if group == P2 else 5
+    xs = [inp["x"], inp["x_b"], inp["x"][::-1].copy(), inp["x_b"][::-1].copy(),
+          np.roll(inp["x"], 7, axis=0)][:rot]
+    ds = [inp["dout"], inp["dout_b"], inp["dout"][::-1].copy(), inp["dout_b"][::-1].copy(),
+          np.roll(inp["dout"], 7, axis=0)][:rot]
     res = {}
-    for tag, fl in (("serial", flags | M.MOE_STEP_PAIR_WGRAD | M.MOE_STEP_SERIALIZE),
-                    ("pipelined", flags | M.MOE_STEP_PAIR_WGRAD),
+    for tag, fl in (("serial", flags | group | M.MOE_STEP_SERIALIZE),
+                    ("pipelined", flags | group),
                     ("unpaired", flags)):
-        m = [M.MicroBatch(s, x=D(xs[i]), dout=D(ds[i])) for i in range(3)]
+        m = [M.MicroBatch(s, x=D(xs[i]), dout=D(ds[i])) for i in range(rot)]
         dW = (torch.full((w.E_l, 2 * w.F, w.d), 0.25, device="cuda"),
               torch.full((w.E_l, w.d, w.F), 0.25, device="cuda"),
               torch.full((w.d, w.E), 0.25, device="cuda"))
         ws = torch.empty(M.moe_step_workspace_bytes(s), dtype=torch.uint8, device="cuda")
-        M.moe_overlap_steps(_steps(s, w, m, W, dW, ws, n, W_r, bias, 3, overwrite), s0, s1,
+        M.moe_overlap_steps(_steps(s, w, m, W, dW, ws, n, W_r, bias, rot, overwrite), s0, s1,
                             fl)
         if flags & M.MOE_STEP_SKIP_WGRAD:  # the caller's delayed wgrad of the last step
-            b = m[(n - 2) % 3]
+            b = m[(n - 2) % rot]
             M.moe_ffn_wgrad(s, b.xp, b.a, b.dh, b.dyp, b.offsets, dW[0], dW[1],
                             M.MOE_ACCUM_DW, stream=s0)
         torch.cuda.synchronize()
         res[tag] = (m, dW)
     (ma, ga), (mb, gb), (mu, gu) = res["serial"], res["pipelined"], res["unpaired"]
-    for i in range(3):
+    for i in range(rot):
         for k in ("out", "dx", "dgates", "dlogits", "idx"):
             assert torch.equal(getattr(mb[i], k), getattr(ma[i], k)), (i, k)
             assert torch.equal(getattr(mu[i], k), getattr(ma[i], k)), ("unpaired", i, k)
@@ -165,7 +222,7 @@ def test_pair_steps_pipelined_equals_serialized(name, n, flags, overwrite):
         ref = gu[k].double()
         err = ((ga[k].double() - ref).abs() / ref.abs().clamp(min=1.0)).max().item()
         assert err <= 1e-5, (k, err)
-    log("[pair steps] pipelined == serialized; unpaired within float32 rounding")
+    log("[grouped steps] pipelined == serialized; ungrouped within float32 rounding")
 
 
 def test_pair_steps_checks():
@@ -193,10 +250,20 @@ def test_pair_steps_checks():
         M.moe_overlap_steps(steps, s0, s1, M.MOE_STEP_PAIR_WGRAD | M.MOE_STEP_FUSED_PERMUTE)
     assert e.value.code == M.MOE_ERR_UNSUPPORTED
     torch.cuda.synchronize()
+    # groups of four need the deferred micro-batches intact for three steps:
+    # three buffer sets are too few
+    m3 = m2 + [M.MicroBatch(s, x=D(inp["x"][::-1].copy()), dout=D(inp["dout"][::-1].copy()))]
+    steps6 = _steps(s, w, m3, W, dW, ws, 6, W_r, None, 3)
+    with pytest.raises(M.MoeError) as e:
+        M.moe_overlap_steps(steps6, s0, s1, M.MOE_STEP_GROUP4_WGRAD)
+    assert e.value.code == M.MOE_ERR_ARG
+    with pytest.raises(M.MoeError) as e:
+        M.moe_overlap_step(steps6[1], s0, s1, M.MOE_STEP_GROUP4_WGRAD)
+    assert e.value.code == M.MOE_ERR_ARG
+    torch.cuda.synchronize()
     # paired steps are issued eagerly only: under stream capture the call
     # returns the error before it issues anything (the graph holds only the
     # fill around it)
-    m3 = m2 + [M.MicroBatch(s, x=D(inp["x"][::-1].copy()), dout=D(inp["dout"][::-1].copy()))]
     steps3 = _steps(s, w, m3, W, dW, ws, 4, W_r, None, 3)
     probe = torch.zeros(64, device="cuda")
     g = torch.cuda.CUDAGraph()
