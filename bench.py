@@ -372,7 +372,8 @@ def overlap_ab(L, G, rounds, graph):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=48,
+                    help="timed steps (default 48: whole groups of four steps in calls of 12)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--tokens", type=int, default=None, help="override T of the workload")
