@@ -1422,8 +1422,11 @@ extern "C" int moe_overlap_steps(const moe_step* steps, int n, hipStream_t s0, h
       bool ok = true;
       for (int k = 0; k < G; ++k) ok = ok && steps[j + k].bwd != nullptr;
       // the later steps must add to what the earlier ones leave (an
-      // overwriting step discards the weight gradients before it)
-      for (int k = 1; k < G; ++k) ok = ok && (steps[j + k].accumulate & MOE_ACCUM_DW) != 0;
+      // overwriting step discards the weight gradients before it), into the
+      // same weight-gradient buffers
+      for (int k = 1; k < G; ++k)
+        ok = ok && (steps[j + k].accumulate & MOE_ACCUM_DW) != 0 &&
+             steps[j + k].dW_gu == steps[j].dW_gu && steps[j + k].dW_down == steps[j].dW_down;
       if (!ok) {
         ++j;
         continue;

@@ -114,7 +114,8 @@ extern "C" {
                                  gradients of steps j and j + 1 in one launch
                                  (moe_ffn_wgrad_pair) in step j + 1, pairs
                                  formed from the first step on where step j + 1
-                                 accumulates (MOE_ACCUM_DW); the launch
+                                 accumulates (MOE_ACCUM_DW) into the same dW
+                                 buffers; the launch
                                  overwrites or accumulates as step j asks.
                                  Step j's backward micro-batch must stay intact
                                  until then (step j + 1 may not forward into

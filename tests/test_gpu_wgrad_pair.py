@@ -250,6 +250,24 @@ def test_pair_steps_checks():
         M.moe_overlap_steps(steps, s0, s1, M.MOE_STEP_PAIR_WGRAD | M.MOE_STEP_FUSED_PERMUTE)
     assert e.value.code == M.MOE_ERR_UNSUPPORTED
     torch.cuda.synchronize()
+    # steps that accumulate into other weight-gradient buffers are not paired:
+    # the same results, bit for bit, as the steps without the flag
+    outs = []
+    for fl in (M.MOE_STEP_PAIR_WGRAD, 0):
+        m3x = [M.MicroBatch(s, x=D(inp["x"]), dout=D(inp["dout"])),
+               M.MicroBatch(s, x=D(inp["x_b"]), dout=D(inp["dout_b"])),
+               M.MicroBatch(s, x=D(inp["x"][::-1].copy()), dout=D(inp["dout"][::-1].copy()))]
+        dWa = [torch.full_like(t, 0.5) for t in dW[:2]]
+        dWb = [torch.full_like(t, -0.5) for t in dW[:2]]
+        st4 = _steps(s, w, m3x, W, dW, ws, 5, W_r, None, 3)
+        for j in range(5):  # odd steps into one pair of buffers, even into another
+            g_ = dWa if j % 2 else dWb
+            st4[j].dW_gu, st4[j].dW_down = g_[0].data_ptr(), g_[1].data_ptr()
+        M.moe_overlap_steps(st4, s0, s1, fl)
+        torch.cuda.synchronize()
+        outs.append(dWa + dWb)
+    for a_, b_ in zip(*outs):
+        assert torch.equal(a_, b_)
     # groups of four need the deferred micro-batches intact for three steps:
     # three buffer sets are too few
     m3 = m2 + [M.MicroBatch(s, x=D(inp["x"][::-1].copy()), dout=D(inp["dout"][::-1].copy()))]
