@@ -203,7 +203,7 @@ def cpu_oracle_baseline(w, inp, target_s=10.0):
 def group_plan(K, G0, unit=2):
     """Steps per captured graph for K timed steps: (G, rem) with G a multiple
     of `unit` (the steps after which the micro-batch buffer sets are back in
-    their roles, times the steps a paired weight gradient spans) and
+    their roles) and
     G * reps + rem == K, rem < unit eager steps; G0 when it divides K - rem,
     else the largest such divisor of K - rem up to 2 G0; (None, K) when K is
     too small for a graph."""
@@ -380,7 +380,7 @@ def main():
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
     ap.add_argument("--graph", choices=("on", "off"), default=None,
                     help="time the overlapped steps as replays of a HIP graph of --group steps "
-                         "(on) or as eager launches (off); default: off with paired weight "
+                         "(on) or as eager launches (off); default: off with grouped weight "
                          "gradients (the library does not capture them), else on")
     ap.add_argument("--fused-permute", choices=("on", "off"), default="off",
                     help="fuse the permute into the expert GEMMs (MOE_STEP_FUSED_PERMUTE): GEMM1 "
@@ -757,7 +757,7 @@ def bench_name(sym):
                 cur += ch
             j += 1
         args.append(cur.strip())
-        # wgrad_kernel<GATHER, element type, ROUTER, ACC, GD, PAIR>
+        # wgrad_kernel<GATHER, element type, ROUTER, ACC, GD, MULTI>
         if len(args) > 2 and args[2] == "true":
             return "dwr_mfma"
         return "wgrad_multi" if len(args) > 5 and args[5] == "true" else "wgrad"

@@ -1306,7 +1306,7 @@ static int bwd_chain(const StepCtx& c, const moe_mb* B, hipStream_t q, bool mid,
     ord.dw = true;
     return MOE_OK;
   };
-  // B's dh is written: the paired weight gradient of the next step may read it
+  // B's dh is written: the grouped weight gradient of a later step may read it
   auto dh_done = [&]() -> int {
     if (rw == kRwDefer) HIPTRY(hipEventRecord(ev->grp[g.slot], q));
     return MOE_OK;
