@@ -938,6 +938,32 @@ def test_multi_step_gapped_chain(name, shared):
     log(f"[multi-step gaps] {name}: bit-identical")
 
 
+@pytest.mark.parametrize("E,K", [(8, 8), (64, 6), (128, 8), (200, 16), (512, 16)])
+def test_topk_ties_and_signed_zeros(E, K):
+    """Top-K from given logits with many exact ties (small integers), signed
+    zeros, subnormals and ordinary values: idx must equal the oracle's stable
+    descending order (ties to the lower expert index, -0 equal to +0) bit for
+    bit, and the gates its softmax over the selection."""
+    T = 1024
+    rng = np.random.default_rng(E * 31 + K)
+    parts = [rng.integers(-3, 4, (T // 4, E)).astype(np.float32),
+             np.where(rng.random((T // 4, E)) < 0.5, np.float32(0.0), np.float32(-0.0)),
+             (rng.standard_normal((T // 4, E)) * 1e-39).astype(np.float32),
+             rng.standard_normal((T // 4, E)).astype(np.float32)]
+    parts[1][np.arange(T // 4), rng.integers(0, E, T // 4)] = 1.0
+    logits = np.concatenate(parts).astype(np.float32)
+    log(f"[top-k ties] T={T} E={E} K={K}")
+    s = M.make_shape(T, 64, 64, E, 0, min(E, 8), K, "bf16")
+    idx = torch.empty(T, K, dtype=torch.int32, device="cuda")
+    gates = torch.empty(T, K, device="cuda")
+    M.moe_route(s, M.MOE_ROUTE_TOPK_FROM_LOGITS, None, None, None, dev(logits, "f32x"), idx,
+                gates, None)
+    torch.cuda.synchronize()
+    i_o, g_o = O.topk_route(logits.astype(np.float64), K, "f32")
+    exact("idx", host(idx), i_o)
+    close("gates", host(gates), g_o, 1e-5)
+
+
 def test_router_weight_grad_split_precision():
     """bf16 dW_r runs on the matrix cores from dlogits split into two bf16 terms.
     Against float64 x^T dlogits computed from the GPU's own float32 dlogits, the
