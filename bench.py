@@ -429,6 +429,11 @@ def main():
                     help="run a few serialized steps and a copy probe of known size, print no "
                          "JSON line: the program to run under rocprofv3 --pmc for the per-kernel "
                          "HBM traffic (FETCH_SIZE / WRITE_SIZE) and MFMA counters")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="time the vendor library's dense bf16 GEMM (torch.matmul) on the "
+                         "shapes of the five expert GEMMs with the workload's dispatched rows "
+                         "as one matrix, print one line per shape and exit (no JSON line): "
+                         "a reference rate for the grouped kernels on the same chip")
     ap.add_argument("--roctx", action="store_true",
                     help="bracket every phase of the step with a roctx range (MOE_ROCTX=1): "
                          "run eagerly (--graph off) under rocprofv3 --marker-trace")
@@ -486,6 +491,8 @@ def main():
         w = w.with_tokens(args.tokens)
     err(f"[bench] workload {w.name}: T={w.T} d={w.d} F={w.F} E={w.E} E_l={w.E_l} K={w.K} "
         f"{w.dtype} route={w.route}")
+    if args.vendor_gemm:
+        return vendor_gemm(w)
     s0 = torch.cuda.current_stream()
     s1 = torch.cuda.Stream()
     L = Layer(w, args, s0, s1)
@@ -733,6 +740,45 @@ _CLASS = [("GateUpOp", "ffn_gate_up"), ("DownOp", "ffn_down"), ("DgradActOp", "d
           ("topk_kernel", "topk"), ("dlogits_kernel", "dlogits"),
           ("dwr_reduce", "dwr_reduce"), ("dwr_partial_kernel", "dwr_partial"),
           ("shared_plan_kernel", "shared_plan")]
+
+
+def vendor_gemm(w, reps=10):
+    """Dense bf16 torch.matmul (hipBLASLt / rocBLAS) on the expert GEMMs' shapes:
+    the N dispatched rows (T*K, times E_l/E for a window, rounded to 256) as one
+    matrix, so the same flops as the grouped kernels without their per-expert
+    tiling; the weight gradients as [M, N] @ [N, K] products over the rows
+    (bf16 output, where the library's kernels accumulate float32)."""
+    import torch
+    N = w.T * w.K * w.E_l // w.E // 256 * 256
+    d, F = w.d, w.F
+    g = torch.Generator(device="cuda").manual_seed(0)
+    r = lambda *sh: torch.randn(*sh, generator=g, device="cuda", dtype=torch.bfloat16)
+    shapes = {"ffn_gate_up": (N, d, 2 * F), "ffn_down": (N, F, d), "dgrad_act": (N, d, F),
+              "dgrad_in": (N, 2 * F, d), "wgrad dW_gu": (2 * F, N, d),
+              "wgrad dW_down": (d, N, F)}
+    try:
+        lib = str(torch.backends.cuda.preferred_blas_library())
+    except Exception:  # noqa: BLE001 - older torch
+        lib = "default"
+    err(f"[vendor] torch {torch.__version__}, preferred BLAS library {lib}, N = {N} rows")
+    for name, (m, k, n) in shapes.items():
+        a, b = r(m, k), r(k, n)
+        for _ in range(3):
+            torch.matmul(a, b)
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            torch.matmul(a, b)
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        t = statistics.median(ts)
+        fl = 2.0 * m * k * n
+        print(f"[vendor] {name:14s} [{m} x {k}] @ [{k} x {n}]: {t * 1e6:8.1f} us, "
+              f"{fl / t / 1e12:7.1f} TFLOP/s = {fl / t / 1e12 / PEAK_BF16_TFLOPS:.3f} of peak",
+              flush=True)
+        del a, b
 
 
 def bench_name(sym):
