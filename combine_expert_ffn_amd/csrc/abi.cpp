@@ -1269,7 +1269,6 @@ struct AccumOrder {
 // and records its own, so the sums happen in step order.  Only events
 // recorded in this call are waited on.
 // skip: leave the weight gradients (routed and shared) to the caller.
-// With PAIR_WGRAD, rw says what the routed experts' weight gradient does:
 // With grouped weight gradients, rw says what the routed experts' weight
 // gradient does: kRwOwn (B's alone), kRwDefer (none: record ev->grp[g.slot]
 // once dh is written; the group's last step takes it) or kRwGroup (B's

@@ -165,11 +165,15 @@ P2, G4 = M.MOE_STEP_PAIR_WGRAD, M.MOE_STEP_GROUP4_WGRAD
     ("zipf_bf16", 10, M.MOE_STEP_SKIP_WGRAD, (), G4),
     ("mid_f32", 10, 0, (1,), G4),
     ("zipf_bf16", 10, M.MOE_STEP_MID_WGRAD, (3,), G4),
+    # fp16 data through the same grouped launch
+    ("zipf_f16", 10, M.MOE_STEP_MID_WGRAD, (), G4),
 ])
 def test_pair_steps_pipelined_equals_serialized(name, n, flags, overwrite, group):
     w = {
         "zipf_bf16": Workload("zipf_bf16", T=700, d=192, F=320, E=64, e_lo=0, E_l=8, K=6,
                               dtype="bf16", route="topk", zipf_s=1.1),
+        "zipf_f16": Workload("zipf_f16", T=700, d=192, F=320, E=64, e_lo=0, E_l=8, K=6,
+                             dtype="f16", route="topk", zipf_s=1.1),
         "mid_f32": Workload("mid_f32", T=150, d=64, F=64, E=16, e_lo=5, E_l=3, K=4,
                             dtype="f32", route="topk"),
     }[name]
