@@ -134,14 +134,15 @@ def test_wgrad_multi_against_oracle(prec, counts):
         assert torch.equal(again[0], dW[0]) and torch.equal(again[1], dW[1])
 
 
-def _steps(s, w, m, W, dW, ws, n, W_r, bias, rot, overwrite=()):
+def _steps(s, w, m, W, dW, ws, n, W_r, bias, rot, overwrite=(), shared=None):
     """n 1F1B steps over buffer sets m: step j forwards m[j % rot] (none in
     the last step) and back-propagates m[(j - 1) % rot] (none in the first);
     the steps in `overwrite` overwrite the weight gradients, the others add."""
     return [M.make_step(s, M.MOE_ROUTE_TOPK, W[0], W[1], dW[0], dW[1], ws,
                         fwd=m[j % rot] if j < n - 1 else None,
                         bwd=m[(j - 1) % rot] if j > 0 else None, W_r=W_r, bias=bias,
-                        dW_r=dW[2], accumulate=0 if j in overwrite else M.MOE_ACCUM_DW)
+                        dW_r=dW[2], accumulate=0 if j in overwrite else M.MOE_ACCUM_DW,
+                        shared=shared)
             for j in range(n)]
 
 
@@ -167,11 +168,16 @@ P2, G4 = M.MOE_STEP_PAIR_WGRAD, M.MOE_STEP_GROUP4_WGRAD
     ("zipf_bf16", 10, M.MOE_STEP_MID_WGRAD, (3,), G4),
     # fp16 data through the same grouped launch
     ("zipf_f16", 10, M.MOE_STEP_MID_WGRAD, (), G4),
+    # with a shared expert (its weight gradients stay per step)
+    ("zipf_bf16_shared", 10, M.MOE_STEP_MID_WGRAD, (), G4),
+    ("zipf_bf16_shared", 9, 0, (2,), P2),
 ])
 def test_pair_steps_pipelined_equals_serialized(name, n, flags, overwrite, group):
     w = {
         "zipf_bf16": Workload("zipf_bf16", T=700, d=192, F=320, E=64, e_lo=0, E_l=8, K=6,
                               dtype="bf16", route="topk", zipf_s=1.1),
+        "zipf_bf16_shared": Workload("zipf_bf16_shared", T=700, d=192, F=320, E=64, e_lo=0,
+                                     E_l=8, K=6, dtype="bf16", route="topk", zipf_s=1.1),
         "zipf_f16": Workload("zipf_f16", T=700, d=192, F=320, E=64, e_lo=0, E_l=8, K=6,
                              dtype="f16", route="topk", zipf_s=1.1),
         "mid_f32": Workload("mid_f32", T=150, d=64, F=64, E=16, e_lo=5, E_l=3, K=4,
@@ -186,6 +192,10 @@ def test_pair_steps_pipelined_equals_serialized(name, n, flags, overwrite, group
     W_r = D(inp["W_r"])
     bias = dev(inp["bias"], "f32x") if inp["bias"] is not None else None
     s0, s1 = torch.cuda.current_stream(), torch.cuda.Stream()
+    Fs = 128 if name.endswith("_shared") else 0
+    rng = np.random.default_rng(17)
+    W_s = (D(O.store(0.05 * rng.standard_normal((2 * Fs, w.d)), prec)),
+           D(O.store(0.05 * rng.standard_normal((w.d, Fs)), prec))) if Fs else None
     # a group of G steps keeps G micro-batches until its last step: G + 1
     # buffer sets rotate
     rot = 3 if group == P2 else 5
@@ -197,22 +207,31 @@ def test_pair_steps_pipelined_equals_serialized(name, n, flags, overwrite, group
     for tag, fl in (("serial", flags | group | M.MOE_STEP_SERIALIZE),
                     ("pipelined", flags | group),
                     ("unpaired", flags)):
-        m = [M.MicroBatch(s, x=D(xs[i]), dout=D(ds[i])) for i in range(rot)]
+        m = [M.MicroBatch(s, x=D(xs[i]), dout=D(ds[i]), F_s=Fs) for i in range(rot)]
         dW = (torch.full((w.E_l, 2 * w.F, w.d), 0.25, device="cuda"),
               torch.full((w.E_l, w.d, w.F), 0.25, device="cuda"),
               torch.full((w.d, w.E), 0.25, device="cuda"))
-        ws = torch.empty(M.moe_step_workspace_bytes(s), dtype=torch.uint8, device="cuda")
-        M.moe_overlap_steps(_steps(s, w, m, W, dW, ws, n, W_r, bias, rot, overwrite), s0, s1,
-                            fl)
+        sh = None
+        if Fs:
+            sh = (W_s[0], W_s[1], torch.full((2 * Fs, w.d), 0.25, device="cuda"),
+                  torch.full((w.d, Fs), 0.25, device="cuda"))
+        ws = torch.empty(M.moe_step_workspace_bytes_shared(s, Fs), dtype=torch.uint8,
+                         device="cuda")
+        M.moe_overlap_steps(_steps(s, w, m, W, dW, ws, n, W_r, bias, rot, overwrite, sh),
+                            s0, s1, fl)
         if flags & M.MOE_STEP_SKIP_WGRAD:  # the caller's delayed wgrad of the last step
             b = m[(n - 2) % rot]
             M.moe_ffn_wgrad(s, b.xp, b.a, b.dh, b.dyp, b.offsets, dW[0], dW[1],
                             M.MOE_ACCUM_DW, stream=s0)
+            assert not Fs, "the shared expert's delayed wgrad is not issued here"
         torch.cuda.synchronize()
-        res[tag] = (m, dW)
-    (ma, ga), (mb, gb), (mu, gu) = res["serial"], res["pipelined"], res["unpaired"]
+        res[tag] = (m, dW, sh)
+    (ma, ga, sa), (mb, gb, sb), (mu, gu, su) = res["serial"], res["pipelined"], res["unpaired"]
+    if Fs:  # the shared expert's weight gradients are not grouped
+        for k in (2, 3):
+            assert torch.equal(sa[k], sb[k]) and torch.equal(sa[k], su[k]), ("shared dW", k)
     for i in range(rot):
-        for k in ("out", "dx", "dgates", "dlogits", "idx"):
+        for k in ("out", "dx", "dgates", "dlogits", "idx") + (("y_s", "dx_s") if Fs else ()):
             assert torch.equal(getattr(mb[i], k), getattr(ma[i], k)), (i, k)
             assert torch.equal(getattr(mu[i], k), getattr(ma[i], k)), ("unpaired", i, k)
         # dh is sized to the cap; rows past N are never written
